@@ -1,0 +1,262 @@
+"""CPU oracle for the Hyena operator -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this module.  The product path (the HIP library and its
+binding) never calls it and shares no code with it.
+
+Everything here is plain NumPy in float64, written for a reader to check against
+the pages by eye.  The pages are cited by title:
+
+  [Hyena note]   "Hyena: 암묵적 장거리 컨볼루션으로 어텐션을 완전 대체한 서브-이차 모델"
+                 (obsidian-dorae222.pages.dev/20.AI/22.SSM/hyena)
+  [EulerStack]   "4. Hyena 상세" (eulerwa.com, EulerStack tutorial, mixers/04_hyena)
+  [HyenaND]      "Native Multi-Dimensional Subquadratic Operators via Input Dependent
+                 Long Convolutions" (gist.science summary, Korean and Italian copies)
+  [SPECTRE news] "FFT의 반격: Self-Attention의 효율적 대안" (news.hada.io digest)
+
+What is computed (y = x_N * (h_N conv (... x_1 * (h_1 conv v)))):
+
+  * positional features phi(t) of the normalised position t/L            [Hyena note, step 2]
+  * filter network g = W2 SiLU(W1 phi + b1) + b2, one per order           [Hyena note, listing
+    ``ImplicitFilter``; EulerStack YAML ``filter_hidden``]
+  * exponential decay window h = g * exp(-alpha t/L)                      [Hyena note, step 2, w(t)]
+  * causal linear convolution over the whole sequence                      [EulerStack, "how it works" 2]
+  * multiplicative gating, innermost gate x_1 with filter h_1              [Hyena note, step 3 equation;
+                                                                           listing ``hyena_operator``]
+  * 3-D: non-causal "same" linear convolution by zero-padding every axis
+    to twice its size                                                      [HyenaND, method: native N-D
+                                                                           convolution; boundary handling]
+
+Readings where the pages are silent (each also listed in the design notes):
+  order N = number of filters = number of gates (listing chunks len(filters)+1);
+  phi(t) = [sin(2 pi f t/L) for f=1..F/2] + [cos(2 pi f t/L) for f=1..F/2];
+  time normalised as t/L for both features and window; one alpha per (order, channel);
+  3-D features: per axis 16 frequencies x {sin, cos} of r/n for signed offsets r in [-(n-1), n-1];
+  3-D window exp(-alpha |r/n|_2).
+
+Pins (each function is checked against something other than itself in
+tests/test_oracle.py): direct sum vs FFT form, numpy.convolve special case,
+first-order-recurrence and geometric-sum closed forms, delta and unit-delay
+filters, linearity, causality, 3-D brute force, separable 3-D products,
+hand-computed worked examples under tests/golden/.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "positional_features_1d", "positional_features_3d", "silu", "filter_network",
+    "implicit_filter_1d", "implicit_filter_3d", "causal_conv_direct", "causal_conv_fft",
+    "linear_conv3d_direct", "linear_conv3d_fft", "hyena_operator_rows", "hyena_operator_3d",
+    "rel_l2_per_row",
+]
+
+
+# --------------------------------------------------------------------------------------------
+# implicit filter  [Hyena note, step 2: h(t) = FFN(pos_enc(t)) * w(t), w(t) = exp(-alpha t)]
+# --------------------------------------------------------------------------------------------
+
+def positional_features_1d(L: int, F: int = 64, t: Optional[np.ndarray] = None) -> np.ndarray:
+    """phi(t) for t = 0..L-1 (or the given t): [L, F] float64.
+
+    Sinusoidal features of the normalised position t/L ([EulerStack] "how it works" 1: a small
+    MLP over sinusoidal features of the position).  Block order: F/2 sines, then F/2 cosines,
+    frequencies 1..F/2 cycles per sequence.
+    """
+    if t is None:
+        t = np.arange(L, dtype=np.float64)
+    t = np.asarray(t, dtype=np.float64)
+    f = np.arange(1, F // 2 + 1, dtype=np.float64)
+    ang = 2.0 * math.pi * np.outer(t, f) / L
+    return np.concatenate([np.sin(ang), np.cos(ang)], axis=1)
+
+
+def positional_features_3d(offsets: np.ndarray, n: int, F: int = 96) -> np.ndarray:
+    """phi(r) for signed integer offsets r [P, 3]: [P, F] float64.
+
+    Per axis (x, y, z in that order): F/6 sines then F/6 cosines of 2 pi f r_a / n, f = 1..F/6.
+    """
+    r = np.asarray(offsets, dtype=np.float64) / n
+    per = F // 6
+    f = np.arange(1, per + 1, dtype=np.float64)
+    cols = []
+    for a in range(3):
+        ang = 2.0 * math.pi * np.outer(r[:, a], f)
+        cols.append(np.sin(ang))
+        cols.append(np.cos(ang))
+    return np.concatenate(cols, axis=1)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z)  ([Hyena note] listing ``nn.SiLU``)."""
+    return z / (1.0 + np.exp(-z))
+
+
+def filter_network(phi: np.ndarray, p: dict, channels: Optional[Sequence[int]] = None) -> np.ndarray:
+    """g = W2 SiLU(W1 phi + b1) + b2 for every row of phi: [P, D_sel] float64.
+
+    W1 [H, F], b1 [H], W2 [D, H], b2 [D] ([Hyena note] listing ``filter_fn``: Linear, SiLU, Linear;
+    [EulerStack] YAML ``filter_hidden: 64``).
+    """
+    W1 = np.asarray(p["W1"], np.float64)
+    b1 = np.asarray(p["b1"], np.float64)
+    W2 = np.asarray(p["W2"], np.float64)
+    b2 = np.asarray(p["b2"], np.float64)
+    if channels is not None:
+        ch = np.asarray(channels, dtype=np.int64)
+        W2, b2 = W2[ch], b2[ch]
+    z = phi @ W1.T + b1
+    a = silu(z)
+    return a @ W2.T + b2
+
+
+def implicit_filter_1d(p: dict, L: int, channels: Optional[Sequence[int]] = None) -> np.ndarray:
+    """h[d, t] = g[d](t) * exp(-alpha_d t / L), t = 0..L-1: [D_sel, L] float64."""
+    F = np.asarray(p["W1"]).shape[1]
+    g = filter_network(positional_features_1d(L, F), p, channels)      # [L, D_sel]
+    alpha = np.asarray(p["alpha"], np.float64)
+    if channels is not None:
+        alpha = alpha[np.asarray(channels, dtype=np.int64)]
+    t = np.arange(L, dtype=np.float64)
+    window = np.exp(-np.outer(alpha, t) / L)                             # [D_sel, L]
+    return g.T * window
+
+
+def filter_offsets_3d(n: int) -> np.ndarray:
+    """All signed offsets r in [-(n-1), n-1]^3, x slowest: [(2n-1)^3, 3] int64."""
+    a = np.arange(-(n - 1), n, dtype=np.int64)
+    X, Y, Z = np.meshgrid(a, a, a, indexing="ij")
+    return np.stack([X.ravel(), Y.ravel(), Z.ravel()], axis=1)
+
+
+def implicit_filter_3d(p: dict, n: int, channels: Optional[Sequence[int]] = None) -> np.ndarray:
+    """h[d, rx, ry, rz] on offsets [-(n-1), n-1]^3: [D_sel, 2n-1, 2n-1, 2n-1] float64.
+
+    h = g(r) * exp(-alpha_d |r/n|_2): a coordinate MLP on the grid offsets times a decaying window
+    ([HyenaND] method, kernel on a continuous coordinate grid; the window shape follows the 1-D
+    exponential of [Hyena note], step 2).
+    """
+    F = np.asarray(p["W1"]).shape[1]
+    r = filter_offsets_3d(n)
+    g = filter_network(positional_features_3d(r, n, F), p, channels)    # [P, D_sel]
+    alpha = np.asarray(p["alpha"], np.float64)
+    if channels is not None:
+        alpha = alpha[np.asarray(channels, dtype=np.int64)]
+    rad = np.sqrt(np.sum((r.astype(np.float64) / n) ** 2, axis=1))      # [P]
+    h = g.T * np.exp(-np.outer(alpha, rad))
+    m = 2 * n - 1
+    return h.reshape(-1, m, m, m)
+
+
+# --------------------------------------------------------------------------------------------
+# long convolution  [EulerStack, "how it works" 2: FFT, pointwise product, inverse FFT = convolution;
+#                    HyenaND, boundary handling: zero-pad to double size to avoid wrap-around]
+# --------------------------------------------------------------------------------------------
+
+def causal_conv_direct(u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """c[t] = sum_{s=0..t} h[t-s] u[s]  (the definition; O(L^2); last axis is time)."""
+    u = np.asarray(u, np.float64)
+    h = np.asarray(h, np.float64)
+    L = u.shape[-1]
+    out = np.zeros(np.broadcast_shapes(u.shape, h.shape), dtype=np.float64)
+    for t in range(L):
+        out[..., t] = np.sum(h[..., t::-1] * u[..., : t + 1], axis=-1)
+    return out
+
+
+def causal_conv_fft(u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """Same result through the convolution theorem on a 2L zero-padded grid, truncated to L."""
+    u = np.asarray(u, np.float64)
+    h = np.asarray(h, np.float64)
+    L = u.shape[-1]
+    n = 2 * L
+    return np.fft.irfft(np.fft.rfft(u, n) * np.fft.rfft(h, n), n)[..., :L]
+
+
+def linear_conv3d_direct(u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """c[p] = sum_{q in [0,n)^3} h[p-q] u[q], p in [0,n)^3 (the definition, brute force).
+
+    u: [n, n, n]; h: [2n-1]^3 indexed by offset + (n-1).
+    """
+    u = np.asarray(u, np.float64)
+    h = np.asarray(h, np.float64)
+    n = u.shape[0]
+    c = np.zeros_like(u)
+    for px in range(n):
+        for py in range(n):
+            for pz in range(n):
+                # offsets p - q for q over the grid, shifted into h's index range
+                hx = slice(px + n - 1, px - 1 if px > 0 else None, -1)
+                hy = slice(py + n - 1, py - 1 if py > 0 else None, -1)
+                hz = slice(pz + n - 1, pz - 1 if pz > 0 else None, -1)
+                c[px, py, pz] = np.sum(h[hx, hy, hz] * u)
+    return c
+
+
+def linear_conv3d_fft(u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """Same result via 3-D real FFTs on a (2n)^3 grid: h[r] placed at r mod 2n, output cropped to [0,n)^3.
+
+    Exact because |p - q| <= n-1 < 2n - (n-1) on every axis, so no wrapped term lands in the crop.
+    Leading axes of u / h are batch axes.
+    """
+    u = np.asarray(u, np.float64)
+    h = np.asarray(h, np.float64)
+    n = u.shape[-1]
+    m = 2 * n
+    hp = np.zeros(h.shape[:-3] + (m, m, m), dtype=np.float64)
+    idx = np.arange(-(n - 1), n) % m
+    hp[..., idx[:, None, None], idx[None, :, None], idx[None, None, :]] = h
+    axes = (-3, -2, -1)
+    U = np.fft.rfftn(u, s=(m, m, m), axes=axes)
+    Hs = np.fft.rfftn(hp, s=(m, m, m), axes=axes)
+    return np.fft.irfftn(U * Hs, s=(m, m, m), axes=axes)[..., :n, :n, :n]
+
+
+# --------------------------------------------------------------------------------------------
+# the operator  [Hyena note, step 3 equation and listing ``hyena_operator``:
+#                v, x_1..x_N chunks; for (h_i, x_i): v <- (h_i conv v) * x_i]
+# --------------------------------------------------------------------------------------------
+
+def hyena_operator_rows(v: np.ndarray, xs: Sequence[np.ndarray], hs: Sequence[np.ndarray],
+                        direct: bool = False) -> np.ndarray:
+    """Order-N recurrence on a batch of independent rows.
+
+    v, xs[i]: [..., R, L] (any float dtype, taken as exact values); hs[i]: [R, L] filter per row
+    (broadcast over leading axes).  Returns y = u_N as float64.
+    """
+    conv = causal_conv_direct if direct else causal_conv_fft
+    u = np.asarray(v, np.float64)
+    for h, x in zip(hs, xs):
+        u = np.asarray(x, np.float64) * conv(u, h)
+    return u
+
+
+def hyena_operator_3d(v: np.ndarray, xs: Sequence[np.ndarray], hs: Sequence[np.ndarray],
+                      direct: bool = False) -> np.ndarray:
+    """Order-N recurrence with non-causal zero-padded 3-D convolutions.
+
+    v, xs[i]: [C, n, n, n]; hs[i]: [C, 2n-1, 2n-1, 2n-1].
+    """
+    u = np.asarray(v, np.float64)
+    for h, x in zip(hs, xs):
+        if direct:
+            c = np.stack([linear_conv3d_direct(u[j], h[j]) for j in range(u.shape[0])])
+        else:
+            c = linear_conv3d_fft(u, h)
+        u = np.asarray(x, np.float64) * c
+    return u
+
+
+def rel_l2_per_row(y: np.ndarray, ref: np.ndarray, point_axes: int = 1) -> np.ndarray:
+    """||y - ref||_2 / ||ref||_2 per row, where a row is the last ``point_axes`` axes (1 for a
+    sequence, 3 for a volume) and every leading index (b, d) names one row."""
+    ref = np.asarray(ref, np.float64)
+    npts = int(np.prod(ref.shape[ref.ndim - point_axes:]))
+    rows = ref.reshape(-1, npts)
+    ys = np.asarray(y, np.float64).reshape(rows.shape)
+    num = np.sqrt(np.sum((ys - rows) ** 2, axis=1))
+    den = np.sqrt(np.sum(rows ** 2, axis=1))
+    return num / np.where(den == 0, 1.0, den)

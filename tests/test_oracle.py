@@ -1,0 +1,312 @@
+"""Pins for the CPU oracle: every function is checked against something other than itself
+(hand-worked examples, closed forms, library routines, brute force, invariants)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.signal
+
+from oracle import hyena_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+@pytest.fixture(scope="module")
+def golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _params(F, H, D, rng, alpha=(0.3, 3.0)):
+    return dict(W1=rng.standard_normal((H, F)) * 0.3, b1=rng.standard_normal(H) * 0.1,
+                W2=rng.standard_normal((D, H)) * 0.3, b2=rng.standard_normal(D) * 0.1,
+                alpha=rng.uniform(*alpha, size=D))
+
+
+# ---------------------------------------------------------------- worked examples (by hand)
+
+def test_golden_causal_conv(golden):
+    g = golden["causal_conv_4"]
+    np.testing.assert_array_equal(orc.causal_conv_direct(g["u"], g["h"]), g["c"])
+    np.testing.assert_allclose(orc.causal_conv_fft(np.array(g["u"], float), np.array(g["h"], float)), g["c"],
+                               rtol=0, atol=1e-13)
+
+
+def test_golden_order2_operator(golden):
+    g = golden["order2_operator_3"]
+    for direct in (True, False):
+        y = orc.hyena_operator_rows(np.array([g["v"]], float), [np.array([g["x1"]], float), np.array([g["x2"]], float)],
+                                    [np.array([g["h1"]], float), np.array([g["h2"]], float)], direct=direct)
+        np.testing.assert_allclose(y[0], g["y"], rtol=0, atol=1e-13)
+
+
+def test_golden_conv3d_point_sources(golden):
+    g = golden["conv3d_point_sources_n2"]
+    n = g["n"]
+    r = np.arange(-(n - 1), n)
+    h = (100 * (r[:, None, None] + 1) + 10 * (r[None, :, None] + 1) + (r[None, None, :] + 1)).astype(float)
+    for key, q in (("delta_at_000", (0, 0, 0)), ("delta_at_111", (1, 1, 1))):
+        u = np.zeros((n, n, n))
+        u[q] = 1.0
+        np.testing.assert_array_equal(orc.linear_conv3d_direct(u, h), g[key])
+        np.testing.assert_allclose(orc.linear_conv3d_fft(u, h), g[key], rtol=0, atol=1e-11)
+
+
+def test_golden_features(golden):
+    g = golden["features_quarter_period"]
+    phi = orc.positional_features_1d(g["L"], 64, t=np.array([g["t"]]))[0]
+    np.testing.assert_allclose(phi[:8], g["sin_first8"], atol=1e-14)
+    np.testing.assert_allclose(phi[32:40], g["cos_first8"], atol=1e-14)
+
+
+# ---------------------------------------------------------------- convolution pins
+
+@pytest.mark.parametrize("L", [1, 2, 3, 17, 64, 257])
+def test_direct_matches_fft(L):
+    rng = np.random.default_rng(L)
+    u = rng.standard_normal((3, L))
+    h = rng.standard_normal((3, L))
+    d = orc.causal_conv_direct(u, h)
+    f = orc.causal_conv_fft(u, h)
+    assert np.max(np.abs(d - f)) <= 1e-12 * max(1.0, np.max(np.abs(d)))
+
+
+@pytest.mark.parametrize("L", [5, 128, 1000])
+def test_order1_equals_numpy_convolve(L):
+    rng = np.random.default_rng(7 + L)
+    u = rng.standard_normal(L)
+    h = rng.standard_normal(L)
+    ref = np.convolve(u, h)[:L]
+    for direct in (True, False):
+        y = orc.hyena_operator_rows(u[None], [np.ones((1, L))], [h[None]], direct=direct)[0]
+        np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-11)
+
+
+def _exp_filter_params(D, alpha, F=64, H=64):
+    """W1 = 0, b1 = 0, W2 = 0, b2 = 1: the network is the constant 1, so h[t] = exp(-alpha t/L)."""
+    return dict(W1=np.zeros((H, F)), b1=np.zeros(H), W2=np.zeros((D, H)), b2=np.ones(D), alpha=np.asarray(alpha, float))
+
+
+@pytest.mark.parametrize("L", [64, 4096, 1 << 16])
+def test_exponential_filter_is_first_order_recurrence(L):
+    """h[t] = a^t, a = exp(-alpha/L): the causal convolution equals y[t] = a y[t-1] + u[t] (scipy lfilter)."""
+    alpha = np.array([0.01, 0.7, 3.0])
+    h = orc.implicit_filter_1d(_exp_filter_params(3, alpha), L)
+    a = np.exp(-alpha / L)
+    np.testing.assert_allclose(h[:, 1], a, rtol=1e-15)
+    rng = np.random.default_rng(L)
+    u = rng.standard_normal((3, L))
+    got = orc.causal_conv_fft(u, h)
+    for d in range(3):
+        ref = scipy.signal.lfilter([1.0], [1.0, -a[d]], u[d])
+        assert np.linalg.norm(got[d] - ref) <= 1e-12 * np.linalg.norm(ref)
+
+
+@pytest.mark.slow
+def test_exponential_filter_full_length_1M():
+    """The same closed form at the 1M-token length of the DNA workload."""
+    L = 1 << 20
+    alpha = np.array([0.01])
+    h = orc.implicit_filter_1d(_exp_filter_params(1, alpha), L)
+    u = np.random.default_rng(3).standard_normal((1, L))
+    got = orc.causal_conv_fft(u, h)[0]
+    ref = scipy.signal.lfilter([1.0], [1.0, -math.exp(-0.01 / L)], u[0])
+    assert np.linalg.norm(got - ref) <= 1e-10 * np.linalg.norm(ref)
+
+
+def test_geometric_sum_closed_form():
+    """Constant input with h[t] = a^t gives (1 - a^(t+1)) / (1 - a)."""
+    L = 2048
+    alpha = np.array([0.5, 2.5])
+    h = orc.implicit_filter_1d(_exp_filter_params(2, alpha), L)
+    got = orc.causal_conv_fft(np.ones((2, L)), h)
+    t = np.arange(L)
+    for d in range(2):
+        a = math.exp(-alpha[d] / L)
+        ref = (1 - a ** (t + 1)) / (1 - a)
+        np.testing.assert_allclose(got[d], ref, rtol=1e-11)
+
+
+def test_delta_filter_gives_product_of_gates():
+    rng = np.random.default_rng(11)
+    L, N = 300, 3
+    v = rng.standard_normal((2, L))
+    xs = [rng.standard_normal((2, L)) for _ in range(N)]
+    delta = np.zeros((2, L))
+    delta[:, 0] = 1
+    for direct in (True, False):
+        y = orc.hyena_operator_rows(v, xs, [delta] * N, direct=direct)
+        np.testing.assert_allclose(y, v * xs[0] * xs[1] * xs[2], rtol=1e-12, atol=1e-12)
+
+
+def test_unit_delay_shifts_by_one():
+    rng = np.random.default_rng(12)
+    L = 100
+    u = rng.standard_normal((1, L))
+    h = np.zeros((1, L))
+    h[0, 1] = 1
+    for conv in (orc.causal_conv_direct, orc.causal_conv_fft):
+        c = conv(u, h)
+        np.testing.assert_allclose(c[0, 1:], u[0, :-1], atol=1e-12)
+        assert abs(c[0, 0]) < 1e-12
+
+
+def test_linearity_and_multilinearity():
+    rng = np.random.default_rng(13)
+    L = 200
+    v1, v2 = rng.standard_normal((2, 1, L))
+    xs = [rng.standard_normal((1, L)) for _ in range(2)]
+    hs = [rng.standard_normal((1, L)) for _ in range(2)]
+    op = orc.hyena_operator_rows
+    np.testing.assert_allclose(op(2 * v1 - 3 * v2, xs, hs), 2 * op(v1, xs, hs) - 3 * op(v2, xs, hs), rtol=1e-10, atol=1e-9)
+    np.testing.assert_allclose(op(v1, [xs[0] * 5, xs[1]], hs), 5 * op(v1, xs, hs), rtol=1e-11, atol=1e-9)
+    np.testing.assert_allclose(op(v1, xs, [hs[0], hs[1] * -2]), -2 * op(v1, xs, hs), rtol=1e-11, atol=1e-9)
+
+
+def test_causality():
+    rng = np.random.default_rng(14)
+    L, t0 = 256, 97
+    v = rng.standard_normal((1, L))
+    xs = [rng.standard_normal((1, L)) for _ in range(2)]
+    hs = [rng.standard_normal((1, L)) for _ in range(2)]
+    v2 = v.copy()
+    v2[0, t0] += 10.0
+    y1 = orc.hyena_operator_rows(v, xs, hs, direct=True)
+    y2 = orc.hyena_operator_rows(v2, xs, hs, direct=True)
+    np.testing.assert_array_equal(y1[0, :t0], y2[0, :t0])
+    assert np.any(y1[0, t0:] != y2[0, t0:])
+    f1 = orc.hyena_operator_rows(v, xs, hs)
+    f2 = orc.hyena_operator_rows(v2, xs, hs)
+    assert np.max(np.abs(f1[0, :t0] - f2[0, :t0])) < 1e-10
+
+
+# ---------------------------------------------------------------- filter pins
+
+def test_features_at_zero_and_period():
+    phi = orc.positional_features_1d(1024, 64)
+    np.testing.assert_array_equal(phi[0], np.r_[np.zeros(32), np.ones(32)])
+    # cos block at t=L/2: cos(pi f) = (-1)^f
+    np.testing.assert_allclose(phi[512, 32:], (-1.0) ** np.arange(1, 33), atol=1e-13)
+    # the features are a function of t/L: t=256 at L=1024 equals t=2 at L=8
+    np.testing.assert_allclose(orc.positional_features_1d(8, 64, t=np.array([2]))[0], phi[256], atol=1e-13)
+
+
+def test_silu_identities():
+    z = np.linspace(-30, 30, 1001)
+    s = orc.silu(z)
+    assert orc.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(s - orc.silu(-z), z, atol=1e-12)      # z*sig(z) + z*sig(-z) = z
+    assert abs(orc.silu(np.array([30.0]))[0] - 30.0) < 1e-10
+    assert abs(orc.silu(np.array([-30.0]))[0]) < 1e-10
+
+
+def test_filter_network_single_path():
+    """W1 with one entry (hidden j <- feature k) and W2 with one entry (channel d <- hidden j):
+    g[d](t) = w2 * SiLU(w1 * phi_k(t)); every other channel is its bias."""
+    F = H = 64
+    D, L = 5, 64
+    j, k, d = 3, 40, 2          # feature 40 = cos of frequency 9
+    W1 = np.zeros((H, F)); W1[j, k] = 1.5
+    W2 = np.zeros((D, H)); W2[d, j] = -2.0
+    b2 = np.arange(D, dtype=float)
+    p = dict(W1=W1, b1=np.zeros(H), W2=W2, b2=b2, alpha=np.zeros(D))
+    h = orc.implicit_filter_1d(p, L)
+    t = np.arange(L)
+    zz = 1.5 * np.cos(2 * np.pi * 9 * t / L)
+    np.testing.assert_allclose(h[d], -2.0 * zz / (1 + np.exp(-zz)) + b2[d], atol=1e-13)
+    for other in range(D):
+        if other != d:
+            np.testing.assert_array_equal(h[other], np.full(L, b2[other]))
+
+
+def test_window_closed_form_and_channel_subset():
+    rng = np.random.default_rng(15)
+    p = _params(64, 64, 6, rng)
+    L = 512
+    h = orc.implicit_filter_1d(p, L)
+    g = orc.filter_network(orc.positional_features_1d(L), p)
+    t = np.arange(L)
+    for d in range(6):
+        np.testing.assert_allclose(h[d], g[:, d] * np.exp(-p["alpha"][d] * t / L), rtol=1e-14)
+    assert h[3, 0] == pytest.approx(g[0, 3], rel=1e-15)         # window is 1 at t = 0
+    np.testing.assert_allclose(orc.implicit_filter_1d(p, L, channels=[4, 1]), h[[4, 1]], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------- 3-D pins
+
+@pytest.mark.parametrize("n", [1, 3, 4])
+def test_conv3d_brute_force_matches_fft(n):
+    rng = np.random.default_rng(20 + n)
+    u = rng.standard_normal((n, n, n))
+    h = rng.standard_normal((2 * n - 1,) * 3)
+    np.testing.assert_allclose(orc.linear_conv3d_fft(u, h), orc.linear_conv3d_direct(u, h), rtol=1e-11, atol=1e-11)
+
+
+def test_conv3d_separable_is_product_of_1d():
+    n = 6
+    rng = np.random.default_rng(31)
+    a, b, c = rng.standard_normal((3, 2 * n - 1))
+    p, q, r = rng.standard_normal((3, n))
+    h = np.einsum("i,j,k->ijk", a, b, c)
+    u = np.einsum("i,j,k->ijk", p, q, r)
+
+    def same1d(sig, ker):  # c[i] = sum_j ker[i-j] sig[j], ker indexed by offset + n-1
+        return np.convolve(sig, ker)[n - 1:2 * n - 1]
+
+    ref = np.einsum("i,j,k->ijk", same1d(p, a), same1d(q, b), same1d(r, c))
+    np.testing.assert_allclose(orc.linear_conv3d_fft(u, h), ref, rtol=1e-11, atol=1e-12)
+
+
+def test_conv3d_point_source_returns_cropped_filter():
+    n = 8
+    rng = np.random.default_rng(32)
+    h = rng.standard_normal((2 * n - 1,) * 3)
+    q = (3, 5, 1)
+    u = np.zeros((n, n, n)); u[q] = 1.0
+    c = orc.linear_conv3d_fft(u, h)
+    P = np.arange(n)
+    ref = h[np.ix_(P - q[0] + n - 1, P - q[1] + n - 1, P - q[2] + n - 1)]
+    np.testing.assert_allclose(c, ref, atol=1e-12)
+
+
+def test_filter3d_features_and_window():
+    n = 4
+    rng = np.random.default_rng(33)
+    p = _params(96, 64, 3, rng)
+    h = orc.implicit_filter_3d(p, n)
+    assert h.shape == (3, 7, 7, 7)
+    phi0 = orc.positional_features_3d(np.zeros((1, 3), int), n)[0]
+    np.testing.assert_array_equal(phi0, np.r_[np.zeros(16), np.ones(16)].tolist() * 3)
+    # offset (n/2, 0, 0): x-sines sin(pi f) = 0, x-cosines (-1)^f; window exp(-alpha/2)
+    phi = orc.positional_features_3d(np.array([[2, 0, 0]]), n)[0]
+    np.testing.assert_allclose(phi[16:32], (-1.0) ** np.arange(1, 17), atol=1e-13)
+    g = orc.filter_network(phi[None], p)[0]
+    np.testing.assert_allclose(h[:, 2 + 3, 3, 3], g * np.exp(-p["alpha"] * 0.5), rtol=1e-14)
+    # W2 = 0, b2 = 1: h = exp(-alpha |r|/n), a radial closed form
+    pe = dict(p, W2=np.zeros_like(p["W2"]), b2=np.ones(3))
+    he = orc.implicit_filter_3d(pe, n)
+    rr = np.arange(-3, 4)
+    rad = np.sqrt(rr[:, None, None] ** 2 + rr[None, :, None] ** 2 + rr[None, None, :] ** 2) / n
+    for d in range(3):
+        np.testing.assert_allclose(he[d], np.exp(-p["alpha"][d] * rad), rtol=1e-14)
+
+
+def test_operator3d_delta_and_direct():
+    n = 3
+    rng = np.random.default_rng(34)
+    v = rng.standard_normal((2, n, n, n))
+    xs = [rng.standard_normal((2, n, n, n)) for _ in range(2)]
+    delta = np.zeros((2,) + (2 * n - 1,) * 3)
+    delta[:, n - 1, n - 1, n - 1] = 1.0
+    np.testing.assert_allclose(orc.hyena_operator_3d(v, xs, [delta, delta]), v * xs[0] * xs[1], atol=1e-12)
+    hs = [rng.standard_normal((2,) + (2 * n - 1,) * 3) for _ in range(2)]
+    np.testing.assert_allclose(orc.hyena_operator_3d(v, xs, hs), orc.hyena_operator_3d(v, xs, hs, direct=True),
+                               rtol=1e-10, atol=1e-10)
+
+
+def test_rel_l2_per_row():
+    ref = np.array([[[3.0, 4.0]], [[1.0, 0.0]]])
+    y = ref + np.array([[[0.3, 0.4]], [[0.0, 0.5]]])
+    np.testing.assert_allclose(orc.rel_l2_per_row(y, ref), [0.1, 0.5])
