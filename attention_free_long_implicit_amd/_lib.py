@@ -1,0 +1,240 @@
+"""ctypes binding of libhyena.so (include/hyena.h).  Argument marshalling only: every step of the
+operator runs in the library's HIP kernels; PyTorch supplies device memory and the current stream.
+
+The library must have been built (``python -m attention_free_long_implicit_amd.build``); loading
+fails loudly otherwise -- there is no fallback path."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libhyena.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "hyena.h")
+
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EALIAS = 0, -1, -2, -3, -4, -5
+F32, BF16 = 0, 1
+CAUSAL, LINEAR, CIRCULAR = 0, 1, 2
+
+
+class HyenaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_str(status)})")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("ndim", ctypes.c_int32), ("n", ctypes.c_int64 * 3)]
+
+
+class FilterParams(ctypes.Structure):
+    _fields_ = [("F", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+                ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("W2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p), ("alpha", ctypes.c_void_p)]
+
+
+_lib = None
+_c = ctypes
+_SIG = {
+    "hyena_version": (_c.c_int, []),
+    "hyena_status_str": (_c.c_char_p, [_c.c_int]),
+    "hyena_spectrum_bytes": (_c.c_int, [Dims, _c.c_int, _c.c_int64, _c.POINTER(_c.c_size_t)]),
+    "hyena_filter_workspace_bytes": (_c.c_int, [Dims, _c.c_int, _c.c_int64, _c.POINTER(_c.c_size_t)]),
+    "hyena_workspace_bytes": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, Dims, _c.c_int, _c.c_int,
+                                         _c.POINTER(_c.c_size_t)]),
+    "hyena_filter_gen": (_c.c_int, [_c.POINTER(FilterParams), Dims, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                    _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "hyena_fftconv": (_c.c_int, [_c.c_int64, _c.c_int64, Dims, _c.c_int, _c.c_int, _c.c_void_p, _c.c_void_p,
+                                 _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "hyena_operator": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, Dims, _c.c_int, _c.c_int, _c.c_void_p,
+                                  _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p,
+                                  _c.c_size_t, _c.c_void_p]),
+    "hyena_spectrum_export": (_c.c_int, [Dims, _c.c_int, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+}
+
+
+def lib():
+    """Load libhyena.so once and attach the C signatures.  Raises if the library is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m attention_free_long_implicit_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def declared_symbols() -> list:
+    """Names of the functions include/hyena.h declares."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(hyena_\w+)\s*\(", text, flags=re.M)))
+
+
+def status_str(status: int) -> str:
+    try:
+        return lib().hyena_status_str(int(status)).decode()
+    except Exception:  # pragma: no cover - used while formatting another error
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise HyenaError(status, what)
+
+
+def dims_of(shape: Sequence[int]) -> Dims:
+    pts = list(shape)
+    d = Dims()
+    d.ndim = len(pts)
+    for i in range(3):
+        d.n[i] = pts[i] if i < len(pts) else 0
+    return d
+
+
+def mode_for(ndim: int) -> int:
+    return CAUSAL if ndim == 1 else LINEAR
+
+
+# ----------------------------------------------------------------------------- torch-facing wrappers
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _stream(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("tensors must be contiguous CUDA (HIP) tensors")
+    return t.data_ptr()
+
+
+def spectrum_bytes(point_shape: Sequence[int], D: int, mode: Optional[int] = None) -> int:
+    n = ctypes.c_size_t()
+    mode = mode_for(len(point_shape)) if mode is None else mode
+    _check(lib().hyena_spectrum_bytes(dims_of(point_shape), mode, D, ctypes.byref(n)), "hyena_spectrum_bytes")
+    return n.value
+
+
+def filter_workspace_bytes(point_shape: Sequence[int], D: int, mode: Optional[int] = None) -> int:
+    n = ctypes.c_size_t()
+    mode = mode_for(len(point_shape)) if mode is None else mode
+    _check(lib().hyena_filter_workspace_bytes(dims_of(point_shape), mode, D, ctypes.byref(n)),
+           "hyena_filter_workspace_bytes")
+    return n.value
+
+
+def workspace_bytes(order: int, B: int, D: int, point_shape: Sequence[int], dtype_code: int,
+                    mode: Optional[int] = None) -> int:
+    n = ctypes.c_size_t()
+    mode = mode_for(len(point_shape)) if mode is None else mode
+    _check(lib().hyena_workspace_bytes(order, B, D, dims_of(point_shape), dtype_code, mode, ctypes.byref(n)),
+           "hyena_workspace_bytes")
+    return n.value
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None
+    torch = _torch()
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def filter_gen(params: dict, point_shape: Sequence[int], h_time=None, spectrum=None, mode: Optional[int] = None):
+    """One order's implicit filter.  params: dict of CUDA float32 tensors W1 [H,F], b1 [H], W2 [D,H],
+    b2 [D], alpha [D].  Returns the spectrum (opaque uint8 tensor); fills h_time when given."""
+    torch = _torch()
+    W1, W2 = params["W1"], params["W2"]
+    H, F = W1.shape
+    D = W2.shape[0]
+    dev = W1.device
+    mode = mode_for(len(point_shape)) if mode is None else mode
+    if spectrum is None:
+        spectrum = torch.empty(spectrum_bytes(point_shape, D, mode), dtype=torch.uint8, device=dev)
+    ws = None
+    if h_time is None:
+        ws = _workspace(filter_workspace_bytes(point_shape, D, mode), dev)
+    p = FilterParams(F, H, D, _ptr(W1), _ptr(params["b1"]), _ptr(W2), _ptr(params["b2"]), _ptr(params["alpha"]))
+    _check(lib().hyena_filter_gen(ctypes.byref(p), dims_of(point_shape), mode, _ptr(h_time), _ptr(spectrum),
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(W1)),
+           "hyena_filter_gen")
+    # ws may be released now: the caching allocator hands it out again only to work ordered after
+    # this call on the same stream.
+    return spectrum
+
+
+def fftconv(u, spectrum, gate=None, y=None, mode: Optional[int] = None):
+    """y = gate * (h conv u) (or h conv u when gate is None); u: [B, D, *points]."""
+    torch = _torch()
+    B, D = u.shape[:2]
+    pts = tuple(u.shape[2:])
+    mode = mode_for(len(pts)) if mode is None else mode
+    if y is None:
+        y = torch.empty_like(u)
+    dt = _dtype_code(u)
+    ws = _workspace(workspace_bytes(1, B, D, pts, dt, mode), u.device)
+    _check(lib().hyena_fftconv(B, D, dims_of(pts), dt, mode, _ptr(u), _ptr(spectrum), _ptr(gate), _ptr(y),
+                               _ptr(ws), 0 if ws is None else ws.numel(), _stream(u)), "hyena_fftconv")
+    return y
+
+
+def operator(v, xs: Sequence, spectra: Sequence, y=None, ws=None, mode: Optional[int] = None):
+    """y = x_N * (h_N conv (... x_1 * (h_1 conv v))); v, xs[i]: [B, D, *points]; spectra from filter_gen."""
+    torch = _torch()
+    B, D = v.shape[:2]
+    pts = tuple(v.shape[2:])
+    order = len(xs)
+    if len(spectra) != order:
+        raise ValueError("need one spectrum per gate")
+    mode = mode_for(len(pts)) if mode is None else mode
+    if y is None:
+        y = torch.empty_like(v)
+    dt = _dtype_code(v)
+    for x in xs:
+        if x.dtype != v.dtype or x.shape != v.shape:
+            raise ValueError("gates must match v in shape and dtype")
+    if ws is None:
+        ws = _workspace(workspace_bytes(order, B, D, pts, dt, mode), v.device)
+    xa = (ctypes.c_void_p * order)(*[_ptr(x) for x in xs])
+    sa = (ctypes.c_void_p * order)(*[_ptr(s) for s in spectra])
+    _check(lib().hyena_operator(order, B, D, dims_of(pts), dt, mode, _ptr(v), xa, sa, _ptr(y), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(v)), "hyena_operator")
+    return y
+
+
+def spectrum_export(spectrum, point_shape: Sequence[int], D: int, mode: Optional[int] = None):
+    """Engine-ordered spectrum -> complex64 tensor of natural-order bins (testing aid)."""
+    torch = _torch()
+    mode = mode_for(len(point_shape)) if mode is None else mode
+    if len(point_shape) == 1:
+        shape = (D, point_shape[0] + 1)
+    else:
+        nx, ny, nz = point_shape
+        shape = (D, 2 * nx, 2 * ny, nz + 1)
+    H = torch.zeros(shape, dtype=torch.complex64, device=spectrum.device)
+    _check(lib().hyena_spectrum_export(dims_of(point_shape), mode, D, _ptr(spectrum), H.data_ptr(),
+                                       _stream(spectrum)), "hyena_spectrum_export")
+    return H

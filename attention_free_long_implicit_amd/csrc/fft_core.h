@@ -1,0 +1,244 @@
+// Device-side building blocks of the FFT engine used by every Hyena kernel (gfx950, wave64).
+//
+// * complex helpers on float2 (x = real, y = imaginary), fp32 arithmetic throughout;
+// * in-register radix-R DFTs (R = 2..32) whose twiddles are compile-time constants, written as
+//   radix-2 decimation-in-frequency stages followed by a register renaming to natural order
+//   (the renaming costs nothing: every index is a compile-time constant after unrolling);
+//   pruned forms for an input whose upper half is zero and for an output whose upper half is
+//   not needed, which is what zero-padding a length-L signal to 2L and keeping the first L
+//   outputs leaves (HyenaND summary, boundary handling: zero-pad to twice the size);
+// * twiddle factors W_N^j = exp(-2 pi i j / N) for N = 2^n <= 2^21 from two small tables that
+//   the host computes in double precision (no recurrences, so accuracy does not drift with L);
+// * bf16 load/store with round-to-nearest-even.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace hyena {
+
+// ------------------------------------------------------------------ complex helpers
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 csub(float2 a, float2 b) { return make_float2(a.x - b.x, a.y - b.y); }
+__device__ __forceinline__ float2 cmul(float2 a, float2 b) {
+  return make_float2(fmaf(a.x, b.x, -a.y * b.y), fmaf(a.x, b.y, a.y * b.x));
+}
+// a * conj(b)
+__device__ __forceinline__ float2 cmulc(float2 a, float2 b) {
+  return make_float2(fmaf(a.x, b.x, a.y * b.y), fmaf(a.y, b.x, -a.x * b.y));
+}
+__device__ __forceinline__ float2 cconj(float2 a) { return make_float2(a.x, -a.y); }
+__device__ __forceinline__ float2 cscale(float2 a, float s) { return make_float2(a.x * s, a.y * s); }
+
+// ------------------------------------------------------------------ compile-time loops
+template <int N, class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<N>(f, std::make_integer_sequence<int, N>{});
+}
+
+// ------------------------------------------------------------------ compile-time trigonometry
+// cos / sin of 2 pi j / n in double, by Taylor series after reduction to [-pi/4, pi/4] with the
+// octant symmetries; used only to fold constant twiddles into the instruction stream.
+constexpr double kPi = 3.14159265358979323846264338327950288;
+constexpr double ce_sin_small(double x) {
+  double term = x, sum = x, x2 = x * x;
+  for (int k = 1; k < 14; ++k) { term *= -x2 / ((2 * k) * (2 * k + 1)); sum += term; }
+  return sum;
+}
+constexpr double ce_cos_small(double x) {
+  double term = 1.0, sum = 1.0, x2 = x * x;
+  for (int k = 1; k < 14; ++k) { term *= -x2 / ((2 * k - 1) * (2 * k)); sum += term; }
+  return sum;
+}
+// returns cos(2 pi j / n) (want_sin = false) or sin(2 pi j / n)
+constexpr double ce_trig(long j, long n, bool want_sin) {
+  j %= n; if (j < 0) j += n;
+  // reduce to the first octant using exact integer arithmetic on 8 j / n
+  long q8 = 8 * j;                 // angle in units of (2 pi / 8n)
+  long oct = q8 / n;               // octant 0..7
+  double r = double(q8 - oct * n) / double(n);   // fraction of an octant in [0, 1)
+  double th = r * (kPi / 4);
+  double c = 0, s = 0;
+  // angle = oct * pi/4 + th
+  switch (oct) {
+    case 0: c = ce_cos_small(th); s = ce_sin_small(th); break;
+    case 1: c = ce_sin_small(kPi / 4 - th); s = ce_cos_small(kPi / 4 - th); break;
+    case 2: c = -ce_sin_small(th); s = ce_cos_small(th); break;
+    case 3: c = -ce_cos_small(kPi / 4 - th); s = ce_sin_small(kPi / 4 - th); break;
+    case 4: c = -ce_cos_small(th); s = -ce_sin_small(th); break;
+    case 5: c = -ce_sin_small(kPi / 4 - th); s = -ce_cos_small(kPi / 4 - th); break;
+    case 6: c = ce_sin_small(th); s = -ce_cos_small(th); break;
+    default: c = ce_cos_small(kPi / 4 - th); s = -ce_sin_small(kPi / 4 - th); break;
+  }
+  return want_sin ? s : c;
+}
+
+// v * W_n^j with W = exp(-2 pi i / n) (forward) or exp(+2 pi i / n) (INV); j, n compile-time.
+template <long J, long N, bool INV>
+__device__ __forceinline__ float2 mul_w(float2 v) {
+  constexpr long j = ((J % N) + N) % N;
+  if constexpr (j == 0) {
+    return v;
+  } else if constexpr (4 * j == N) {          // -i (forward) / +i (inverse)
+    return INV ? make_float2(-v.y, v.x) : make_float2(v.y, -v.x);
+  } else if constexpr (2 * j == N) {
+    return make_float2(-v.x, -v.y);
+  } else if constexpr (4 * j == 3 * N) {      // +i (forward) / -i (inverse)
+    return INV ? make_float2(v.y, -v.x) : make_float2(-v.y, v.x);
+  } else {
+    constexpr float c = (float)ce_trig(j, N, false);
+    constexpr float s0 = (float)ce_trig(j, N, true);
+    constexpr float s = INV ? s0 : -s0;       // W = c + i s
+    return make_float2(fmaf(v.x, c, -v.y * s), fmaf(v.x, s, v.y * c));
+  }
+}
+
+constexpr int ilog2(int n) { return n <= 1 ? 0 : 1 + ilog2(n >> 1); }
+constexpr int bitrev(int x, int bits) {
+  int r = 0;
+  for (int i = 0; i < bits; ++i) r |= ((x >> i) & 1) << (bits - 1 - i);
+  return r;
+}
+
+// ------------------------------------------------------------------ in-register DFT
+// X[k] = sum_m x[m] W_R^{mk}, natural order in and out.
+//   ZERO_UPPER: x[m] = 0 for m >= R/2 (those registers are not read).
+//   HALF_OUT:   only X[k] for k < R/2 is produced (upper registers are left undefined).
+template <int R, bool INV, bool ZERO_UPPER = false, bool HALF_OUT = false>
+__device__ __forceinline__ void dft(float2 (&v)[R]) {
+  static_assert(R >= 2 && (R & (R - 1)) == 0 && R <= 64, "radix must be a power of two <= 64");
+  constexpr int LR = ilog2(R);
+  // radix-2 DIF stages: span R/2, R/4, ..., 1
+  static_for<LR>([&](auto s) {
+    constexpr int span = R >> (s.value + 1);
+    constexpr bool first = (s.value == 0);
+    constexpr bool last = (s.value == LR - 1);
+    static_for<R / (2 * span)>([&](auto bi) {
+      constexpr int blk = bi.value * 2 * span;
+      static_for<span>([&](auto jj) {
+        constexpr int j = jj.value;
+        constexpr int i0 = blk + j, i1 = blk + j + span;
+        if constexpr (first && ZERO_UPPER) {
+          // lower input only: sum = a, difference = a
+          v[i1] = mul_w<j, 2 * span, INV>(v[i0]);
+        } else if constexpr (last && HALF_OUT) {
+          // after all stages position p holds X[bitrev(p)]; the sum (even p) holds k < R/2
+          v[i0] = cadd(v[i0], v[i1]);
+        } else {
+          float2 a = v[i0], b = v[i1];
+          v[i0] = cadd(a, b);
+          v[i1] = mul_w<j, 2 * span, INV>(csub(a, b));
+        }
+      });
+    });
+  });
+  // rename to natural order
+  float2 t[R];
+  static_for<R>([&](auto k) {
+    if constexpr (!HALF_OUT || k.value < R / 2) t[k.value] = v[bitrev(k.value, LR)];
+  });
+  static_for<R>([&](auto k) {
+    if constexpr (!HALF_OUT || k.value < R / 2) v[k.value] = t[k.value];
+  });
+}
+
+// Same on a register sub-array x[OFF + m * STRIDE], m < R, of a larger array.
+template <int R, bool INV, bool ZERO_UPPER, bool HALF_OUT, int OFF, int STRIDE, int N>
+__device__ __forceinline__ void dft_sub(float2 (&x)[N]) {
+  float2 v[R];
+  static_for<R>([&](auto m) {
+    if constexpr (!(ZERO_UPPER && m.value >= R / 2)) v[m.value] = x[OFF + m.value * STRIDE];
+  });
+  dft<R, INV, ZERO_UPPER, HALF_OUT>(v);
+  static_for<R>([&](auto k) {
+    if constexpr (!(HALF_OUT && k.value >= R / 2)) x[OFF + k.value * STRIDE] = v[k.value];
+  });
+}
+
+// ------------------------------------------------------------------ twiddle tables
+// tw_coarse[a] = W_{2^15}^a, a < 2^15;  tw_fine[b] = W_{2^21}^b, b < 2^6  (forward sign).
+constexpr int kTwCoarseLog2 = 15;
+constexpr int kTwCoarse = 1 << kTwCoarseLog2;
+constexpr int kTwFineLog2 = 6;
+constexpr int kTwFine = 1 << kTwFineLog2;
+constexpr int kTwMaxLog2 = kTwCoarseLog2 + kTwFineLog2;   // 21
+
+struct Twiddles {
+  const float2* __restrict__ coarse;   // [kTwCoarse]
+  const float2* __restrict__ fine;     // [kTwFine]
+};
+
+// W_{2^LOG2N}^j (forward sign), j taken mod 2^LOG2N.  LOG2N <= 15: one table read.
+template <int LOG2N>
+__device__ __forceinline__ float2 twiddle(const Twiddles& tw, uint32_t j) {
+  static_assert(LOG2N <= kTwMaxLog2, "twiddle table too small");
+  j &= (1u << LOG2N) - 1u;
+  if constexpr (LOG2N <= kTwCoarseLog2) {
+    return tw.coarse[j << (kTwCoarseLog2 - LOG2N)];
+  } else {
+    const uint32_t jj = j << (kTwMaxLog2 - LOG2N);
+    float2 c = tw.coarse[jj >> kTwFineLog2];
+    const uint32_t b = jj & (kTwFine - 1);
+    return b ? cmul(c, tw.fine[b]) : c;
+  }
+}
+__device__ __forceinline__ float2 twiddle_rt(const Twiddles& tw, uint32_t j, int log2n) {
+  j &= (1u << log2n) - 1u;
+  if (log2n <= kTwCoarseLog2) return tw.coarse[j << (kTwCoarseLog2 - log2n)];
+  const uint32_t jj = j << (kTwMaxLog2 - log2n);
+  float2 c = tw.coarse[jj >> kTwFineLog2];
+  const uint32_t b = jj & (kTwFine - 1);
+  return b ? cmul(c, tw.fine[b]) : c;
+}
+
+// ------------------------------------------------------------------ storage types
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);   // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Two consecutive stored elements (one packed complex sample) <-> float2.
+template <bool BF16> struct Store;
+template <> struct Store<false> {
+  using elem = float;
+  __device__ __forceinline__ static float2 load2(const float* p) { return *reinterpret_cast<const float2*>(p); }
+  __device__ __forceinline__ static void store2(float* p, float2 v) { *reinterpret_cast<float2*>(p) = v; }
+};
+template <> struct Store<true> {
+  using elem = uint16_t;
+  __device__ __forceinline__ static float2 load2(const uint16_t* p) {
+    uint32_t w = *reinterpret_cast<const uint32_t*>(p);
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  }
+  __device__ __forceinline__ static void store2(uint16_t* p, float2 v) {
+    uint32_t w = uint32_t(f32_to_bf16_rne(v.x)) | (uint32_t(f32_to_bf16_rne(v.y)) << 16);
+    *reinterpret_cast<uint32_t*>(p) = w;
+  }
+};
+
+// ------------------------------------------------------------------ LDS padding
+// One float2 of padding after every 16: rows of 16 contiguous elements read by consecutive lanes
+// then fall on distinct banks.
+__device__ __forceinline__ int lds_pad(int p) { return p + (p >> 4); }
+constexpr int lds_padded_size(int n) { return n + (n >> 4); }
+
+// ------------------------------------------------------------------ XCD-aware block order
+// Consecutive workgroups are dealt round-robin to the 8 XCDs; remap so that each XCD receives a
+// contiguous run of logical block ids (rows that share a filter then share that XCD's L2).
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblk) {
+  constexpr int kXcd = 8;
+  const int per = nblk / kXcd;
+  if (bid >= per * kXcd) return bid;        // tail keeps its identity
+  return (bid % kXcd) * per + bid / kXcd;
+}
+
+}  // namespace hyena

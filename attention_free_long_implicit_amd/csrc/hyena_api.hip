@@ -1,0 +1,204 @@
+// C ABI of libhyena.so: argument validation, pass planning and launches on the caller's stream.
+// Declarations and the contract of every entry point are in include/hyena.h.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/hyena.h"
+#include "launch.h"
+
+using namespace hyena;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+Twiddles g_tw[kMaxDevices];
+bool g_tw_ready[kMaxDevices];
+
+// W_N^j = exp(-2 pi i j / N) in double, rounded once to fp32.
+float2 host_twiddle(long j, long n) {
+  const double a = -2.0 * M_PI * (double)j / (double)n;
+  return make_float2((float)cos(a), (float)sin(a));
+}
+
+int get_twiddles(Twiddles* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HYENA_EHIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_tw_ready[dev]) {
+    std::vector<float2> host(kTwCoarse + kTwFine);
+    for (int a = 0; a < kTwCoarse; ++a) host[a] = host_twiddle(a, kTwCoarse);
+    for (int b = 0; b < kTwFine; ++b) host[kTwCoarse + b] = host_twiddle(b, 1L << kTwMaxLog2);
+    float2* d = nullptr;
+    if (hipMalloc(&d, host.size() * sizeof(float2)) != hipSuccess) return HYENA_EHIP;
+    if (hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(d);
+      return HYENA_EHIP;
+    }
+    g_tw[dev].coarse = d;
+    g_tw[dev].fine = d + kTwCoarse;
+    g_tw_ready[dev] = true;
+  }
+  *out = g_tw[dev];
+  return HYENA_OK;
+}
+
+bool is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
+int log2i(int64_t n) { int k = 0; while ((int64_t(1) << k) < n) ++k; return k; }
+
+size_t elem_bytes(int dtype) { return dtype == HYENA_BF16 ? 2 : 4; }
+
+// Shape checks shared by every entry point.  On success *points = elements per (b, d) row.
+int check_dims(hyena_dims dims, int mode, int64_t* points) {
+  if (mode == HYENA_CIRCULAR) return HYENA_EUNSUPPORTED;
+  if (mode == HYENA_CAUSAL) {
+    if (dims.ndim != 1) return HYENA_EINVAL;
+    const int64_t L = dims.n[0];
+    if (L <= 0) return HYENA_EINVAL;
+    if (!is_pow2(L) || L < (1 << 10) || L > (1 << 20)) return HYENA_EUNSUPPORTED;
+    if (!single_pass_supported(log2i(L))) return HYENA_EUNSUPPORTED;   // multi-pass sizes: see below
+    *points = L;
+    return HYENA_OK;
+  }
+  if (mode == HYENA_LINEAR) {
+    if (dims.ndim != 3) return HYENA_EINVAL;
+    if (dims.n[0] <= 0 || dims.n[1] <= 0 || dims.n[2] <= 0) return HYENA_EINVAL;
+    return HYENA_EUNSUPPORTED;
+  }
+  return HYENA_EINVAL;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const char* pa = (const char*)a;
+  const char* pb = (const char*)b;
+  return pa < pb + nb && pb < pa + na;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? HYENA_OK : HYENA_EHIP; }
+
+int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const void* spectrum, const void* gate,
+              void* y, const Twiddles& tw, hipStream_t s) {
+  return hip_status(launch_conv1d_single(log2i(L), dtype == HYENA_BF16, u, gate, y, (const float2*)spectrum,
+                                         (int)B, (int)D, tw, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int hyena_version(void) { return 100; }
+
+const char* hyena_status_str(int status) {
+  switch (status) {
+    case HYENA_OK: return "ok";
+    case HYENA_EINVAL: return "invalid argument";
+    case HYENA_EUNSUPPORTED: return "unsupported size or mode";
+    case HYENA_EWORKSPACE: return "workspace missing or too small";
+    case HYENA_EHIP: return "HIP runtime error";
+    case HYENA_EALIAS: return "output overlaps an input";
+  }
+  return "unknown status";
+}
+
+int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
+  if (!bytes || D <= 0) return HYENA_EINVAL;
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  *bytes = (size_t)D * (size_t)pts * sizeof(float2);
+  return HYENA_OK;
+}
+
+int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
+  if (!bytes || D <= 0) return HYENA_EINVAL;
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  *bytes = (size_t)D * (size_t)pts * sizeof(float);
+  return HYENA_OK;
+}
+
+int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, size_t* bytes) {
+  if (!bytes || order < 1 || B <= 0 || D <= 0 || (dtype != HYENA_F32 && dtype != HYENA_BF16)) return HYENA_EINVAL;
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  *bytes = 0;
+  return HYENA_OK;
+}
+
+int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, float* h_time, void* spectrum,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!p || !spectrum || !p->W1 || !p->b1 || !p->W2 || !p->b2 || !p->alpha || p->D <= 0) return HYENA_EINVAL;
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  if (p->H != 64 || p->F != (mode == HYENA_CAUSAL ? 64 : 96)) return HYENA_EUNSUPPORTED;
+  const size_t hbytes = (size_t)p->D * (size_t)pts * sizeof(float);
+  float* h = h_time;
+  if (!h) {
+    if (!ws || ws_bytes < hbytes) return HYENA_EWORKSPACE;
+    h = (float*)ws;
+  }
+  Twiddles tw;
+  if ((st = get_twiddles(&tw))) return st;
+  FilterArgs a{p->F, p->H, p->D, p->W1, p->b1, p->W2, p->b2, p->alpha};
+  const int64_t L = pts;
+  if ((st = hip_status(launch_filter1d(a, (int)L, h, stream)))) return st;
+  return hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, p->D, tw, stream));
+}
+
+int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void* u, const void* spectrum,
+                  const void* gate, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (B <= 0 || D <= 0 || !u || !spectrum || !y || (dtype != HYENA_F32 && dtype != HYENA_BF16)) return HYENA_EINVAL;
+  if (B * D > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  const size_t tb = (size_t)B * D * pts * elem_bytes(dtype);
+  if (y != u && overlaps(y, tb, u, tb)) return HYENA_EALIAS;
+  if (gate && y != gate && overlaps(y, tb, gate, tb)) return HYENA_EALIAS;
+  (void)ws; (void)ws_bytes;
+  Twiddles tw;
+  if ((st = get_twiddles(&tw))) return st;
+  return conv_once(B, D, pts, dtype, u, spectrum, gate, y, tw, stream);
+}
+
+int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void* v,
+                   const void* const* x, const void* const* spectra, void* y, void* ws, size_t ws_bytes,
+                   hipStream_t stream) {
+  if (order < 1 || B <= 0 || D <= 0 || !v || !x || !spectra || !y || (dtype != HYENA_F32 && dtype != HYENA_BF16))
+    return HYENA_EINVAL;
+  for (int i = 0; i < order; ++i)
+    if (!x[i] || !spectra[i]) return HYENA_EINVAL;
+  if (B * D > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  const size_t tb = (size_t)B * D * pts * elem_bytes(dtype);
+  if (y != v && overlaps(y, tb, v, tb)) return HYENA_EALIAS;
+  for (int i = 0; i < order; ++i)
+    if (overlaps(y, tb, x[i], tb)) return HYENA_EALIAS;
+  (void)ws; (void)ws_bytes;
+  Twiddles tw;
+  if ((st = get_twiddles(&tw))) return st;
+  const void* cur = v;
+  for (int i = 0; i < order; ++i) {
+    if ((st = conv_once(B, D, pts, dtype, cur, spectra[i], x[i], y, tw, stream))) return st;
+    cur = y;
+  }
+  return HYENA_OK;
+}
+
+int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spectrum, void* H, hipStream_t stream) {
+  if (D <= 0 || !spectrum || !H) return HYENA_EINVAL;
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  return hip_status(launch_export1d_single(log2i(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,25 @@
+// Host-side launchers exported by each kernel translation unit to the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "fft_core.h"
+
+namespace hyena {
+
+// ---- 1-D, one workgroup per row (L = 2^log2L, 10 <= log2L <= 14)
+bool single_pass_supported(int log2L);
+hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* gate, void* y, const float2* Hs,
+                                int B, int D, const Twiddles& tw, hipStream_t s);
+hipError_t launch_spectrum1d_single(int log2L, const float* h, float2* Hs, int D, const Twiddles& tw,
+                                    hipStream_t s);
+hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
+
+// ---- implicit filter taps
+struct FilterArgs {
+  int F, H, D;
+  const float *W1, *b1, *W2, *b2, *alpha;
+};
+hipError_t launch_filter1d(const FilterArgs& a, int L, float* h, hipStream_t s);
+
+}  // namespace hyena

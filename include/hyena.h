@@ -1,0 +1,120 @@
+/*
+ * hyena.h -- C ABI of the MI355X (gfx950) Hyena operator library, libhyena.so.
+ *
+ * The operator (Hyena study note, obsidian-dorae222.pages.dev/20.AI/22.SSM/hyena, section
+ * "아키텍처 상세", step 3 equation, and its listing hyena_operator):
+ *
+ *     u_0 = v,   u_i = x_i * (h_i conv u_{i-1})   (i = 1..order),   y = u_order
+ *
+ * with x_1 the innermost gate, paired with h_1.  Each h_i is an implicit filter (same page, step 2:
+ * h(t) = FFN(pos_enc(t)) * exp(-alpha t); EulerStack "4. Hyena 상세", how it works 1: small MLP over
+ * sinusoidal features with an exponential decay window), and "conv" is
+ *   - 1-D (HYENA_CAUSAL): c[t] = sum_{s<=t} h[t-s] u[s], t < L, by FFT on a 2L zero-padded grid
+ *     (EulerStack page, how it works 2; HyenaND summary, boundary handling);
+ *   - 3-D (HYENA_LINEAR): c[p] = sum_{q in grid} h[p-q] u[q] over an n^3 grid, offsets p-q in
+ *     [-(n-1), n-1]^3, by 3-D FFT on a (2n)^3 zero-padded grid ("Native Multi-Dimensional
+ *     Subquadratic Operators via Input Dependent Long Convolutions" summary, method: native N-D
+ *     convolution; boundary handling: zero-pad to twice the size).
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library never frees them.
+ *   - Activations are channel-major and contiguous: [B, D, L] (1-D) or [B, D, nx, ny, nz] (3-D),
+ *     element type given by hyena_dtype (math is always fp32; bf16 stores round to nearest even).
+ *   - Calls are asynchronous on the caller's HIP stream and never synchronise the host, except the
+ *     first call on a device, which uploads the library's constant twiddle tables (about 256 KB) once.
+ *   - The library holds no state across calls besides those immutable tables.
+ *   - Return value: HYENA_OK or a negative status (below); arguments are validated before anything
+ *     is launched, so an error return means nothing was enqueued.  Device faults surface at the
+ *     caller's next synchronisation.  hyena_status_str() names a status.
+ */
+#ifndef HYENA_H_
+#define HYENA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  HYENA_OK = 0,
+  HYENA_EINVAL = -1,        /* null pointer, order < 1, non-positive size, mode/ndim mismatch       */
+  HYENA_EUNSUPPORTED = -2,  /* size not a power of two or outside the supported range; F/H not 64  */
+  HYENA_EWORKSPACE = -3,    /* workspace missing or smaller than the size the query returned      */
+  HYENA_EHIP = -4,          /* a HIP runtime call or launch failed                                   */
+  HYENA_EALIAS = -5         /* the output overlaps an input in a way that is not allowed            */
+};
+
+typedef enum { HYENA_F32 = 0, HYENA_BF16 = 1 } hyena_dtype;
+
+typedef enum {
+  HYENA_CAUSAL = 0,   /* 1-D causal linear convolution (pad to 2L, keep [0, L))                  */
+  HYENA_LINEAR = 1,   /* 3-D non-causal zero-padded "same" convolution (pad each axis to 2n)      */
+  HYENA_CIRCULAR = 2  /* periodic boundary: not implemented, returns HYENA_EUNSUPPORTED           */
+} hyena_mode;
+
+/* Grid shape: 1-D {1, {L, 0, 0}}; 3-D {3, {nx, ny, nz}}.
+ * Supported: 1-D L = 2^k, 2^10 <= L <= 2^20; 3-D nx = ny = nz = 64. */
+typedef struct {
+  int32_t ndim;
+  int64_t n[3];
+} hyena_dims;
+
+/* One order's implicit-filter parameters (device pointers, fp32, row-major):
+ *   W1 [H, F], b1 [H], W2 [D, H], b2 [D], alpha [D] (alpha >= 0 is a precondition, not checked).
+ * Supported: H = 64; F = 64 for 1-D, F = 96 for 3-D (16 frequencies x {sin, cos} per axis). */
+typedef struct {
+  int32_t F, H, D;
+  const float *W1, *b1, *W2, *b2, *alpha;
+} hyena_filter_params;
+
+/* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array). */
+int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
+
+/* Workspace bytes hyena_filter_gen needs when h_time is NULL (it then keeps the taps there). */
+int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
+
+/* Workspace bytes hyena_fftconv / hyena_operator need (0 when the transform fits on chip). */
+int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, size_t *bytes);
+
+/* Implicit filter of one order: writes the taps (1-D: h_time[D, L]; 3-D: h_time[D, 2n-1, 2n-1, 2n-1],
+ * offsets from -(n-1)) when h_time is not NULL, and the filter spectrum into `spectrum`
+ * (hyena_spectrum_bytes bytes).  ws/ws_bytes: scratch of hyena_filter_workspace_bytes (may be NULL/0
+ * when h_time is given).  The spectrum depends only on (params, dims), so callers cache it per length. */
+int hyena_filter_gen(const hyena_filter_params *p, hyena_dims dims, int mode, float *h_time, void *spectrum,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* One long convolution with optional gate: y = gate * (h conv u), or y = h conv u when gate == NULL.
+ * u, gate, y: [B, D, points] of dtype.  spectrum: from hyena_filter_gen for the same dims and D.
+ * y may equal u or gate exactly (in place); any other overlap returns HYENA_EALIAS. */
+int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *u,
+                  const void *spectrum, const void *gate, void *y, void *ws, size_t ws_bytes,
+                  hipStream_t stream);
+
+/* The order-N operator y = x_N * (h_N conv (... x_1 * (h_1 conv v))).
+ * x: host array of `order` device pointers (x[0] = x_1); spectra: host array of `order` spectra
+ * (spectra[i] pairs with x[i]).  y doubles as the buffer between orders; y may equal v exactly but
+ * must not overlap any x_i.  ws: hyena_workspace_bytes bytes. */
+int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *v,
+                   const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,
+                   hipStream_t stream);
+
+/* Testing aid: the engine-ordered spectrum as natural-order DFT bins of the zero-padded filter,
+ * complex64 H[D, L+1] (1-D) or H[D, 2nx, 2ny, nz+1] (3-D). */
+int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void *spectrum, void *H,
+                          hipStream_t stream);
+
+/* Static description of a status code. */
+const char *hyena_status_str(int status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int hyena_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYENA_H_ */

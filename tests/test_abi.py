@@ -1,0 +1,96 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function the
+header declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+import attention_free_long_implicit_amd as hy
+from attention_free_long_implicit_amd import _lib as L
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        from attention_free_long_implicit_amd import build
+        build.build()
+    return hy.lib()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = hy.declared_symbols()
+    assert len(names) >= 8
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_status_strings(lib):
+    assert lib.hyena_status_str(0) == b"ok"
+    for s in (-1, -2, -3, -4, -5):
+        assert lib.hyena_status_str(s) != b"unknown status"
+    assert lib.hyena_version() >= 100
+
+
+def _size(fn, *args):
+    n = ctypes.c_size_t()
+    return fn(*args, ctypes.byref(n)), n.value
+
+
+def test_size_queries(lib):
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([8192]), L.CAUSAL, 768)
+    assert st == 0 and n == 768 * 8192 * 8
+    st, n = _size(lib.hyena_filter_workspace_bytes, L.dims_of([1024]), L.CAUSAL, 16)
+    assert st == 0 and n == 16 * 1024 * 4
+    st, n = _size(lib.hyena_workspace_bytes, 2, 4, 768, L.dims_of([8192]), L.BF16, L.CAUSAL)
+    assert st == 0 and n == 0
+
+
+@pytest.mark.parametrize("shape,mode,status", [
+    ([8191], L.CAUSAL, L.EUNSUPPORTED),      # not a power of two
+    ([512], L.CAUSAL, L.EUNSUPPORTED),       # below the supported range
+    ([1 << 21], L.CAUSAL, L.EUNSUPPORTED),   # above it
+    ([0], L.CAUSAL, L.EINVAL),
+    ([1024], L.LINEAR, L.EINVAL),            # linear mode needs a 3-D grid
+    ([64, 64, 64], L.CAUSAL, L.EINVAL),      # causal mode needs 1-D
+    ([1024], L.CIRCULAR, L.EUNSUPPORTED),
+])
+def test_bad_shapes(lib, shape, mode, status):
+    st, _ = _size(lib.hyena_spectrum_bytes, L.dims_of(shape), mode, 4)
+    assert st == status
+
+
+def test_invalid_arguments_return_before_launch(lib):
+    d = L.dims_of([8192])
+    # null pointers
+    assert lib.hyena_fftconv(4, 768, d, L.BF16, L.CAUSAL, None, 0x2000, None, 0x3000, None, 0, None) == L.EINVAL
+    assert lib.hyena_fftconv(0, 768, d, L.BF16, L.CAUSAL, 0x1000, 0x2000, None, 0x3000, None, 0, None) == L.EINVAL
+    assert lib.hyena_fftconv(4, 768, d, 7, L.CAUSAL, 0x1000, 0x2000, None, 0x3000, None, 0, None) == L.EINVAL
+    # partial overlap of y with u / gate
+    base = 1 << 32
+    assert lib.hyena_fftconv(4, 768, d, L.BF16, L.CAUSAL, base, 0x2000, None, base + 64, None, 0, None) == L.EALIAS
+    assert lib.hyena_fftconv(4, 768, d, L.BF16, L.CAUSAL, 0x10, 0x2000, base, base + 64, None, 0, None) == L.EALIAS
+    # operator: order < 1, null gate, y overlapping a gate
+    xs = (ctypes.c_void_p * 2)(base, base + (1 << 30))
+    sp = (ctypes.c_void_p * 2)(0x100, 0x200)
+    assert lib.hyena_operator(0, 4, 768, d, L.BF16, L.CAUSAL, 0x10, xs, sp, 1 << 40, None, 0, None) == L.EINVAL
+    xs_null = (ctypes.c_void_p * 2)(base, None)
+    assert lib.hyena_operator(2, 4, 768, d, L.BF16, L.CAUSAL, 0x10, xs_null, sp, 1 << 40, None, 0, None) == L.EINVAL
+    assert lib.hyena_operator(2, 4, 768, d, L.BF16, L.CAUSAL, 1 << 40, xs, sp, base + 128, None, 0, None) == L.EALIAS
+    # filter parameters of an unsupported width
+    p = L.FilterParams(32, 64, 16, 1, 2, 3, 4, 5)
+    assert lib.hyena_filter_gen(ctypes.byref(p), L.dims_of([1024]), L.CAUSAL, 0x1000, 0x2000, None, 0, None) \
+        == L.EUNSUPPORTED
+    p = L.FilterParams(64, 64, 16, 1, 2, 3, 4, 5)
+    assert lib.hyena_filter_gen(ctypes.byref(p), L.dims_of([1024]), L.CAUSAL, None, 0x2000, None, 0, None) \
+        == L.EWORKSPACE
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(L, "_lib", None)
+    with pytest.raises(ImportError):
+        L.lib()

@@ -1,0 +1,186 @@
+"""GPU parity of the 1-D path (filter generation, spectrum, convolution, operator) against the
+CPU oracle, through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+import scipy.signal
+
+import hyena_inputs as hi
+from oracle import hyena_oracle as orc
+from gpu_util import (BF16_TOL, FP32_TOL, oracle_rows_1d, params_to_dev, rel_err_rows, run_hip_operator, say,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+SINGLE_PASS_L = [1024, 2048, 4096, 8192, 16384]
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import attention_free_long_implicit_amd as hy
+    hy.lib()
+    return torch
+
+
+def _small(w, **kw):
+    return w.with_(**kw)
+
+
+@pytest.mark.parametrize("L", SINGLE_PASS_L)
+def test_filter_taps_and_spectrum_match_oracle(torch_cuda, L):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = _small(hi.WORKLOADS[0], D=24, dims=(L,))
+    p = hi.draw_filter_params(w, seed=100 + L)[0]
+    say(f"filter_gen L={L} D=24")
+    h = torch.empty((24, L), dtype=torch.float32, device="cuda")
+    spec = hy.filter_gen(params_to_dev(p), (L,), h_time=h)
+    H = hy.spectrum_export(spec, (L,), 24)
+    torch.cuda.synchronize()
+    ref = orc.implicit_filter_1d(p, L)
+    e = rel_err_rows(h.cpu().numpy(), ref)
+    assert e.max() < 1e-5, e.max()
+    Href = np.fft.rfft(ref, 2 * L)
+    Hg = H.cpu().numpy().astype(np.complex128)
+    num = np.linalg.norm(Hg - Href, axis=1)
+    den = np.linalg.norm(Href, axis=1)
+    assert (num / den).max() < 1e-5, (num / den).max()
+
+
+@pytest.mark.parametrize("L", SINGLE_PASS_L)
+@pytest.mark.parametrize("gate", [False, True])
+def test_fftconv_fp32_matches_oracle(torch_cuda, L, gate):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    B, D = 3, 7     # 21 rows: not a multiple of the 8-way block remap
+    w = _small(hi.WORKLOADS[0], B=B, D=D, dims=(L,))
+    rng = np.random.default_rng(L)
+    u = rng.standard_normal((B, D, L)).astype(np.float32)
+    g = rng.standard_normal((B, D, L)).astype(np.float32)
+    p = hi.draw_filter_params(w, seed=L)[0]
+    say(f"fftconv fp32 L={L} gate={gate}")
+    spec = hy.filter_gen(params_to_dev(p), (L,))
+    y = hy.fftconv(to_dev(u, torch.float32), spec, gate=to_dev(g, torch.float32) if gate else None)
+    torch.cuda.synchronize()
+    h = orc.implicit_filter_1d(p, L)
+    ref = orc.causal_conv_fft(u.astype(np.float64), h[None])
+    if gate:
+        ref = ref * g
+    e = rel_err_rows(y.cpu().numpy(), ref)
+    assert e.max() < 2e-5, e.max()
+
+
+def test_exponential_filter_closed_form(torch_cuda):
+    """W2 = 0, b2 = 1 makes h[t] = exp(-alpha t/L): the convolution is y[t] = a y[t-1] + u[t]."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L, D = 8192, 4
+    alpha = np.array([0.01, 0.3, 1.0, 3.0], np.float32)
+    p = dict(W1=np.zeros((64, 64), np.float32), b1=np.zeros(64, np.float32), W2=np.zeros((D, 64), np.float32),
+             b2=np.ones(D, np.float32), alpha=alpha)
+    u = np.random.default_rng(1).standard_normal((1, D, L)).astype(np.float32)
+    say("closed form exp filter")
+    spec = hy.filter_gen(params_to_dev(p), (L,))
+    y = hy.fftconv(to_dev(u, torch.float32), spec).cpu().numpy()[0]
+    for d in range(D):
+        a = math.exp(-float(alpha[d]) / L)
+        ref = scipy.signal.lfilter([1.0], [1.0, -a], u[0, d].astype(np.float64))
+        assert np.linalg.norm(y[d] - ref) / np.linalg.norm(ref) < 2e-6
+
+
+def test_delta_filter_gives_product_of_gates(torch_cuda):
+    """A window so steep that h = b2 * delta: y = b2_1 b2_2 v x_1 x_2."""
+    torch = torch_cuda
+    L, D, B = 2048, 8, 2
+    w = _small(hi.WORKLOADS[0], B=B, D=D, dims=(L,))
+    v, xs = hi.draw_activations(w, seed=5)
+    params = []
+    for i, scale in enumerate((0.5, -2.0)):
+        params.append(dict(W1=np.zeros((64, 64), np.float32), b1=np.zeros(64, np.float32),
+                           W2=np.zeros((D, 64), np.float32), b2=np.full(D, scale, np.float32),
+                           alpha=np.full(D, 200.0 * L, np.float32)))
+    say("delta filter")
+    y = run_hip_operator(w, v, xs, params)
+    ref = -1.0 * v * xs[0] * xs[1]
+    assert np.max(np.abs(y - ref)) < 1e-5 * np.max(np.abs(ref))
+
+
+def test_operator_workload0_all_rows(torch_cuda):
+    w = hi.WORKLOADS[0]
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    say("operator workload 0 (order 2, L=1024, fp32), all rows")
+    y = run_hip_operator(w, v, xs, params)
+    rows = [(b, d) for b in range(w.B) for d in range(w.D)]
+    ref = oracle_rows_1d(w, v, xs, params, rows)
+    got = np.stack([y[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
+    assert e.max() < FP32_TOL
+
+
+def test_operator_workload1_sampled_rows(torch_cuda):
+    w = hi.WORKLOADS[1]
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    say("operator workload 1 (order 2, B=4 D=768 L=8192, bf16), sampled rows")
+    y = run_hip_operator(w, v, xs, params)
+    rows = [tuple(r) for r in hi.sample_rows(w, 24)]
+    ref = oracle_rows_1d(w, v, xs, params, rows)
+    got = np.stack([y[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
+    assert e.max() < BF16_TOL
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_inplace_and_bitwise_determinism(torch_cuda, dtype):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = _small(hi.WORKLOADS[1], B=2, D=16, dims=(4096,), dtype=dtype)
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    say(f"in-place / determinism {dtype}")
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
+    vd = to_dev(v, dt)
+    xd = [to_dev(x, dt) for x in xs]
+    y1 = hy.operator(vd, xd, spectra)
+    y2 = hy.operator(vd, xd, spectra)
+    v_inplace = vd.clone()
+    hy.operator(v_inplace, xd, spectra, y=v_inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(y1, v_inplace)
+
+
+def test_rows_are_independent_and_causal(torch_cuda):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L = 4096
+    w = _small(hi.WORKLOADS[0], B=2, D=8, dims=(L,))
+    v, xs = hi.draw_activations(w, seed=9)
+    params = hi.draw_filter_params(w, seed=9)
+    say("row independence / causality")
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
+    xd = [to_dev(x, torch.float32) for x in xs]
+    base = hy.operator(to_dev(v, torch.float32), xd, spectra).cpu().numpy()
+    vn = v.copy()
+    vn[1, 3, 100] = np.nan
+    yn = hy.operator(to_dev(vn, torch.float32), xd, spectra).cpu().numpy()
+    bad = ~np.isfinite(yn)
+    assert bad[1, 3].any()
+    bad[1, 3] = False
+    assert not bad.any()
+    np.testing.assert_array_equal(np.delete(yn.reshape(16, L), 11, axis=0), np.delete(base.reshape(16, L), 11, axis=0))
+    t0 = 1500
+    vp = v.copy()
+    vp[0, 2, t0] += 50.0
+    yp = hy.operator(to_dev(vp, torch.float32), xd, spectra).cpu().numpy()
+    scale = np.max(np.abs(base[0, 2]))
+    assert np.max(np.abs(yp[0, 2, :t0] - base[0, 2, :t0])) < 1e-5 * scale
+    assert np.max(np.abs(yp[0, 2, t0:] - base[0, 2, t0:])) > 1e-2 * scale
