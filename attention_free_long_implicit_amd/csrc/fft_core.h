@@ -1,14 +1,15 @@
 // Device-side building blocks of the FFT engine used by every Hyena kernel (gfx950, wave64).
 //
 // * complex helpers on float2 (x = real, y = imaginary), fp32 arithmetic throughout;
-// * in-register radix-R DFTs (R = 2..32) whose twiddles are compile-time constants, written as
-//   radix-2 decimation-in-frequency stages followed by a register renaming to natural order
-//   (the renaming costs nothing: every index is a compile-time constant after unrolling);
+// * in-register radix-R DFTs (R = 2..64) whose twiddles are compile-time constants, written as
+//   radix-2 decimation-in-time stages on a register renaming of the input (the renaming costs
+//   nothing: every index is a compile-time constant after unrolling);
 //   pruned forms for an input whose upper half is zero and for an output whose upper half is
 //   not needed, which is what zero-padding a length-L signal to 2L and keeping the first L
 //   outputs leaves (HyenaND summary, boundary handling: zero-pad to twice the size);
-// * twiddle factors W_N^j = exp(-2 pi i j / N) for N = 2^n <= 2^21 from two small tables that
-//   the host computes in double precision (no recurrences, so accuracy does not drift with L);
+// * twiddle factors W_N^j = exp(-2 pi i j / N) for N = 2^n <= 2^21 from tables the host computes
+//   in double precision; within one butterfly the powers w^k of a looked-up w are formed by
+//   squaring (a few roundings deep, independent of L);
 // * bf16 load/store with round-to-nearest-even.
 #pragma once
 
@@ -107,16 +108,57 @@ constexpr int bitrev(int x, int bits) {
 }
 
 // ------------------------------------------------------------------ in-register DFT
-// X[k] = sum_m x[m] W_R^{mk}, natural order in and out.
-//   ZERO_UPPER: x[m] = 0 for m >= R/2 (those registers are not read).
+// X[k] = sum_m x[m] W_R^{mk}, natural order in and out, as radix-2 decimation-in-time stages on
+// the bit-reversed renaming of the input (the renaming is free: all indices are constants).
+// A butterfly with a non-trivial twiddle w costs 6 instructions: a' = a + w b as two chained FMAs
+// per component, b' = 2a - a' as one FMA per component.
+//   ZERO_UPPER: x[m] = 0 for m >= R/2 (those registers are not read; the first stage is a copy).
 //   HALF_OUT:   only X[k] for k < R/2 is produced (upper registers are left undefined).
+template <long J, long N, bool INV>
+__device__ __forceinline__ void bfly_dit(float2& a, float2& b) {
+  constexpr long j = ((J % N) + N) % N;
+  if constexpr (j == 0) {
+    const float2 t = b;
+    b = csub(a, t); a = cadd(a, t);
+  } else if constexpr (4 * j == N) {            // w = -i (forward) / +i (inverse)
+    const float2 t = INV ? make_float2(-b.y, b.x) : make_float2(b.y, -b.x);
+    b = csub(a, t); a = cadd(a, t);
+  } else {
+    constexpr float c = (float)ce_trig(j, N, false);
+    constexpr float s0 = (float)ce_trig(j, N, true);
+    constexpr float s = INV ? s0 : -s0;         // w = c + i s
+    const float ax = fmaf(c, b.x, fmaf(-s, b.y, a.x));
+    const float ay = fmaf(c, b.y, fmaf(s, b.x, a.y));
+    b = make_float2(fmaf(2.0f, a.x, -ax), fmaf(2.0f, a.y, -ay));
+    a = make_float2(ax, ay);
+  }
+}
+template <long J, long N, bool INV>
+__device__ __forceinline__ void bfly_dit_top(float2& a, const float2& b) {   // only a' = a + w b
+  constexpr long j = ((J % N) + N) % N;
+  if constexpr (j == 0) {
+    a = cadd(a, b);
+  } else if constexpr (4 * j == N) {
+    a = cadd(a, INV ? make_float2(-b.y, b.x) : make_float2(b.y, -b.x));
+  } else {
+    constexpr float c = (float)ce_trig(j, N, false);
+    constexpr float s0 = (float)ce_trig(j, N, true);
+    constexpr float s = INV ? s0 : -s0;
+    a = make_float2(fmaf(c, b.x, fmaf(-s, b.y, a.x)), fmaf(c, b.y, fmaf(s, b.x, a.y)));
+  }
+}
+
 template <int R, bool INV, bool ZERO_UPPER = false, bool HALF_OUT = false>
-__device__ __forceinline__ void dft(float2 (&v)[R]) {
+__device__ __forceinline__ void dft(float2 (&x)[R]) {
   static_assert(R >= 2 && (R & (R - 1)) == 0 && R <= 64, "radix must be a power of two <= 64");
   constexpr int LR = ilog2(R);
-  // radix-2 DIF stages: span R/2, R/4, ..., 1
+  float2 v[R];
+  static_for<R>([&](auto i) {
+    constexpr int src = bitrev(i.value, LR);
+    if constexpr (!(ZERO_UPPER && src >= R / 2)) v[i.value] = x[src];
+  });
   static_for<LR>([&](auto s) {
-    constexpr int span = R >> (s.value + 1);
+    constexpr int span = 1 << s.value;
     constexpr bool first = (s.value == 0);
     constexpr bool last = (s.value == LR - 1);
     static_for<R / (2 * span)>([&](auto bi) {
@@ -125,26 +167,17 @@ __device__ __forceinline__ void dft(float2 (&v)[R]) {
         constexpr int j = jj.value;
         constexpr int i0 = blk + j, i1 = blk + j + span;
         if constexpr (first && ZERO_UPPER) {
-          // lower input only: sum = a, difference = a
-          v[i1] = mul_w<j, 2 * span, INV>(v[i0]);
+          v[i1] = v[i0];                       // odd input is zero: both outputs equal the even one
         } else if constexpr (last && HALF_OUT) {
-          // after all stages position p holds X[bitrev(p)]; the sum (even p) holds k < R/2
-          v[i0] = cadd(v[i0], v[i1]);
+          bfly_dit_top<j, 2 * span, INV>(v[i0], v[i1]);
         } else {
-          float2 a = v[i0], b = v[i1];
-          v[i0] = cadd(a, b);
-          v[i1] = mul_w<j, 2 * span, INV>(csub(a, b));
+          bfly_dit<j, 2 * span, INV>(v[i0], v[i1]);
         }
       });
     });
   });
-  // rename to natural order
-  float2 t[R];
   static_for<R>([&](auto k) {
-    if constexpr (!HALF_OUT || k.value < R / 2) t[k.value] = v[bitrev(k.value, LR)];
-  });
-  static_for<R>([&](auto k) {
-    if constexpr (!HALF_OUT || k.value < R / 2) v[k.value] = t[k.value];
+    if constexpr (!HALF_OUT || k.value < R / 2) x[k.value] = v[k.value];
   });
 }
 
@@ -162,39 +195,49 @@ __device__ __forceinline__ void dft_sub(float2 (&x)[N]) {
 }
 
 // ------------------------------------------------------------------ twiddle tables
-// tw_coarse[a] = W_{2^15}^a, a < 2^15;  tw_fine[b] = W_{2^21}^b, b < 2^6  (forward sign).
-constexpr int kTwCoarseLog2 = 15;
-constexpr int kTwCoarse = 1 << kTwCoarseLog2;
+// pow2[2^s + j] = W_{2^s}^j for s <= 15, j < 2^s (each size contiguous, so lanes with consecutive j
+// read consecutive addresses);  fine[b] = W_{2^21}^b, b < 64, for sizes above 2^15:
+//   W_N^j = W_{2^15}^{j >> (n-15)} * W_{2^21}^{(j mod 2^(n-15)) << (21-n)}.
+constexpr int kTwPow2Log2 = 15;
+constexpr int kTwPow2Entries = 2 << kTwPow2Log2;     // offsets 0..2^16 (entry 0 unused)
 constexpr int kTwFineLog2 = 6;
 constexpr int kTwFine = 1 << kTwFineLog2;
-constexpr int kTwMaxLog2 = kTwCoarseLog2 + kTwFineLog2;   // 21
+constexpr int kTwMaxLog2 = kTwPow2Log2 + kTwFineLog2;   // 21
 
 struct Twiddles {
-  const float2* __restrict__ coarse;   // [kTwCoarse]
-  const float2* __restrict__ fine;     // [kTwFine]
+  const float2* __restrict__ pow2;   // [kTwPow2Entries]
+  const float2* __restrict__ fine;   // [kTwFine]
 };
 
-// W_{2^LOG2N}^j (forward sign), j taken mod 2^LOG2N.  LOG2N <= 15: one table read.
+// W_{2^LOG2N}^j (forward sign), j taken mod 2^LOG2N.
 template <int LOG2N>
 __device__ __forceinline__ float2 twiddle(const Twiddles& tw, uint32_t j) {
   static_assert(LOG2N <= kTwMaxLog2, "twiddle table too small");
   j &= (1u << LOG2N) - 1u;
-  if constexpr (LOG2N <= kTwCoarseLog2) {
-    return tw.coarse[j << (kTwCoarseLog2 - LOG2N)];
+  if constexpr (LOG2N <= kTwPow2Log2) {
+    return tw.pow2[(1u << LOG2N) + j];
   } else {
-    const uint32_t jj = j << (kTwMaxLog2 - LOG2N);
-    float2 c = tw.coarse[jj >> kTwFineLog2];
-    const uint32_t b = jj & (kTwFine - 1);
-    return b ? cmul(c, tw.fine[b]) : c;
+    constexpr int sh = LOG2N - kTwPow2Log2;
+    const float2 c = tw.pow2[(1u << kTwPow2Log2) + (j >> sh)];
+    const uint32_t r = j & ((1u << sh) - 1u);
+    return r ? cmul(c, tw.fine[r << (kTwMaxLog2 - LOG2N)]) : c;
   }
 }
-__device__ __forceinline__ float2 twiddle_rt(const Twiddles& tw, uint32_t j, int log2n) {
-  j &= (1u << log2n) - 1u;
-  if (log2n <= kTwCoarseLog2) return tw.coarse[j << (kTwCoarseLog2 - log2n)];
-  const uint32_t jj = j << (kTwMaxLog2 - log2n);
-  float2 c = tw.coarse[jj >> kTwFineLog2];
-  const uint32_t b = jj & (kTwFine - 1);
-  return b ? cmul(c, tw.fine[b]) : c;
+
+__device__ __forceinline__ float2 csq(float2 a) { return make_float2(fmaf(a.x, a.x, -a.y * a.y), 2.0f * a.x * a.y); }
+
+// p[k] = w^k, k < R (p[0] = 1), by repeated squaring / one extra product: depth about 2 log2 k.
+template <int R>
+__device__ __forceinline__ void twiddle_powers(float2 w, float2 (&p)[R]) {
+  p[0] = make_float2(1.f, 0.f);
+  if constexpr (R > 1) p[1] = w;
+  static_for<R>([&](auto kk) {
+    constexpr int k = kk.value;
+    if constexpr (k >= 2) {
+      if constexpr (k % 2 == 0) p[k] = csq(p[k / 2]);
+      else p[k] = cmul(p[k - 1], w);
+    }
+  });
 }
 
 // ------------------------------------------------------------------ storage types

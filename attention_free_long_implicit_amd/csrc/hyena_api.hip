@@ -29,17 +29,19 @@ int get_twiddles(Twiddles* out) {
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HYENA_EHIP;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_tw_ready[dev]) {
-    std::vector<float2> host(kTwCoarse + kTwFine);
-    for (int a = 0; a < kTwCoarse; ++a) host[a] = host_twiddle(a, kTwCoarse);
-    for (int b = 0; b < kTwFine; ++b) host[kTwCoarse + b] = host_twiddle(b, 1L << kTwMaxLog2);
+    std::vector<float2> host(kTwPow2Entries + kTwFine);
+    host[0] = make_float2(1.f, 0.f);
+    for (int sz = 1; sz <= (1 << kTwPow2Log2); sz <<= 1)
+      for (int j = 0; j < sz; ++j) host[sz + j] = host_twiddle(j, sz);
+    for (int b = 0; b < kTwFine; ++b) host[kTwPow2Entries + b] = host_twiddle(b, 1L << kTwMaxLog2);
     float2* d = nullptr;
     if (hipMalloc(&d, host.size() * sizeof(float2)) != hipSuccess) return HYENA_EHIP;
     if (hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
       (void)hipFree(d);
       return HYENA_EHIP;
     }
-    g_tw[dev].coarse = d;
-    g_tw[dev].fine = d + kTwCoarse;
+    g_tw[dev].pow2 = d;
+    g_tw[dev].fine = d + kTwPow2Entries;
     g_tw_ready[dev] = true;
   }
   *out = g_tw[dev];

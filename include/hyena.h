@@ -21,7 +21,7 @@
  *   - Activations are channel-major and contiguous: [B, D, L] (1-D) or [B, D, nx, ny, nz] (3-D),
  *     element type given by hyena_dtype (math is always fp32; bf16 stores round to nearest even).
  *   - Calls are asynchronous on the caller's HIP stream and never synchronise the host, except the
- *     first call on a device, which uploads the library's constant twiddle tables (about 256 KB) once.
+ *     first call on a device, which uploads the library's constant twiddle tables (about 512 KB) once.
  *   - The library holds no state across calls besides those immutable tables.
  *   - Return value: HYENA_OK or a negative status (below); arguments are validated before anything
  *     is launched, so an error return means nothing was enqueued.  Device faults surface at the
