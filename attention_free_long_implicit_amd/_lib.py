@@ -174,9 +174,7 @@ def filter_gen(params: dict, point_shape: Sequence[int], h_time=None, spectrum=N
     mode = mode_for(len(point_shape)) if mode is None else mode
     if spectrum is None:
         spectrum = torch.empty(spectrum_bytes(point_shape, D, mode), dtype=torch.uint8, device=dev)
-    ws = None
-    if h_time is None:
-        ws = _workspace(filter_workspace_bytes(point_shape, D, mode), dev)
+    ws = _workspace(filter_workspace_bytes(point_shape, D, mode), dev)
     p = FilterParams(F, H, D, _ptr(W1), _ptr(params["b1"]), _ptr(W2), _ptr(params["b2"]), _ptr(params["alpha"]))
     _check(lib().hyena_filter_gen(ctypes.byref(p), dims_of(point_shape), mode, _ptr(h_time), _ptr(spectrum),
                                   _ptr(ws), 0 if ws is None else ws.numel(), _stream(W1)),

@@ -253,11 +253,11 @@ struct NegPairs {
   }
 };
 
-// Column engine: NL lines, N = RL::S points per line, element (l, p) at lds[p * LP + l] (+pad).
+// Column engine: NL lines, N = RL::S points per line, element (l, p) at lds[lds_pad(p * LP + l)].
 template <int NL, int LP, int T, class RL>
 struct ColEngine {
   static constexpr int P = RL::P, N = RL::S;
-  __device__ __forceinline__ static int addr(int p, int l) { return p * LP + l; }
+  __device__ __forceinline__ static int addr(int p, int l) { return lds_pad(p * LP + l); }
 
   template <int J, bool INV, bool ZERO_UPPER, bool HALF_OUT>
   __device__ __forceinline__ static void pass(float2* lds, const Twiddles& tw, int t) {

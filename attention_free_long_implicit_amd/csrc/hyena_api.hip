@@ -61,7 +61,7 @@ int check_dims(hyena_dims dims, int mode, int64_t* points) {
     const int64_t L = dims.n[0];
     if (L <= 0) return HYENA_EINVAL;
     if (!is_pow2(L) || L < (1 << 10) || L > (1 << 20)) return HYENA_EUNSUPPORTED;
-    if (!single_pass_supported(log2i(L))) return HYENA_EUNSUPPORTED;   // multi-pass sizes: see below
+    if (!single_pass_supported(log2i(L)) && !fourstep_supported(log2i(L))) return HYENA_EUNSUPPORTED;
     *points = L;
     return HYENA_OK;
   }
@@ -81,10 +81,29 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? HYENA_OK : HYENA_EHIP; }
 
+bool is_multipass(int64_t L) { return !single_pass_supported(log2i(L)); }
+
+// Rows per multi-pass chunk by default: about 96 MB of intermediate, so a chunk's intermediate
+// stays in the 256 MB memory-side cache while the next pass reads it.
+int64_t default_chunk_rows(int64_t L, int64_t rows) {
+  const int64_t per = (int64_t)fourstep_row_bytes(log2i(L));
+  int64_t c = ((int64_t)96 << 20) / per;
+  if (c < 1) c = 1;
+  return c < rows ? c : rows;
+}
+
 int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const void* spectrum, const void* gate,
               void* y, const Twiddles& tw, hipStream_t s) {
   return hip_status(launch_conv1d_single(log2i(L), dtype == HYENA_BF16, u, gate, y, (const float2*)spectrum,
                                          (int)B, (int)D, tw, s));
+}
+
+// Multi-pass chunk rows that fit the caller's workspace (0 when it is too small).
+int chunk_from_ws(int64_t L, int64_t rows, void* ws, size_t ws_bytes) {
+  if (!ws) return 0;
+  if ((size_t)ws & 255u) return 0;
+  const int64_t c = (int64_t)(ws_bytes / fourstep_row_bytes(log2i(L)));
+  return (int)(c < rows ? c : rows);
 }
 
 }  // namespace
@@ -120,6 +139,8 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* b
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   *bytes = (size_t)D * (size_t)pts * sizeof(float);
+  if (mode == HYENA_CAUSAL && is_multipass(pts))
+    *bytes += (size_t)default_chunk_rows(pts, D) * fourstep_row_bytes(log2i(pts));
   return HYENA_OK;
 }
 
@@ -129,6 +150,8 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   *bytes = 0;
+  if (mode == HYENA_CAUSAL && is_multipass(pts))
+    *bytes = (size_t)default_chunk_rows(pts, B * D) * fourstep_row_bytes(log2i(pts));
   return HYENA_OK;
 }
 
@@ -140,16 +163,39 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
   if (st) return st;
   if (p->H != 64 || p->F != (mode == HYENA_CAUSAL ? 64 : 96)) return HYENA_EUNSUPPORTED;
   const size_t hbytes = (size_t)p->D * (size_t)pts * sizeof(float);
+  const int64_t L = pts;
+  const bool multi = is_multipass(L);
+  const size_t row_b = multi ? fourstep_row_bytes(log2i(L)) : 0;
+  char* wsp = (char*)ws;
+  size_t wsn = ws ? ws_bytes : 0;
   float* h = h_time;
   if (!h) {
-    if (!ws || ws_bytes < hbytes) return HYENA_EWORKSPACE;
-    h = (float*)ws;
+    if (wsn < hbytes) return HYENA_EWORKSPACE;
+    h = (float*)wsp;
+    wsp += hbytes;
+    wsn -= hbytes;
+  }
+  int chunk = 0;
+  if (multi) {
+    // 256-byte alignment for the intermediate rows
+    const size_t mis = (size_t)wsp & 255u;
+    if (mis) {
+      const size_t adv = 256 - mis;
+      if (wsn < adv) return HYENA_EWORKSPACE;
+      wsp += adv;
+      wsn -= adv;
+    }
+    const int64_t c = (int64_t)(wsn / row_b);
+    if (c < 1) return HYENA_EWORKSPACE;
+    chunk = (int)(c < p->D ? c : p->D);
   }
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
   FilterArgs a{p->F, p->H, p->D, p->W1, p->b1, p->W2, p->b2, p->alpha};
-  const int64_t L = pts;
   if ((st = hip_status(launch_filter1d(a, (int)L, h, stream)))) return st;
+  if (multi)
+    return hip_status(launch_spectrum1d_fourstep(log2i(L), h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw,
+                                                 stream));
   return hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, p->D, tw, stream));
 }
 
@@ -163,9 +209,21 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   const size_t tb = (size_t)B * D * pts * elem_bytes(dtype);
   if (y != u && overlaps(y, tb, u, tb)) return HYENA_EALIAS;
   if (gate && y != gate && overlaps(y, tb, gate, tb)) return HYENA_EALIAS;
-  (void)ws; (void)ws_bytes;
+  int chunk = 0;
+  if (is_multipass(pts)) {
+    chunk = chunk_from_ws(pts, B * D, ws, ws_bytes);
+    if (chunk < 1) return HYENA_EWORKSPACE;
+    if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, u, tb) || (gate && overlaps(ws, ws_bytes, gate, tb)))
+      return HYENA_EALIAS;
+  }
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
+  if (chunk) {
+    const void* xs[1] = {gate};
+    const void* sp[1] = {spectrum};
+    return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y,
+                                             (float2*)ws, chunk, tw, stream));
+  }
   return conv_once(B, D, pts, dtype, u, spectrum, gate, y, tw, stream);
 }
 
@@ -184,9 +242,19 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   if (y != v && overlaps(y, tb, v, tb)) return HYENA_EALIAS;
   for (int i = 0; i < order; ++i)
     if (overlaps(y, tb, x[i], tb)) return HYENA_EALIAS;
-  (void)ws; (void)ws_bytes;
+  int chunk = 0;
+  if (is_multipass(pts)) {
+    chunk = chunk_from_ws(pts, B * D, ws, ws_bytes);
+    if (chunk < 1) return HYENA_EWORKSPACE;
+    if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
+    for (int i = 0; i < order; ++i)
+      if (overlaps(ws, ws_bytes, x[i], tb)) return HYENA_EALIAS;
+  }
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
+  if (chunk)
+    return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra,
+                                             y, (float2*)ws, chunk, tw, stream));
   const void* cur = v;
   for (int i = 0; i < order; ++i) {
     if ((st = conv_once(B, D, pts, dtype, cur, spectra[i], x[i], y, tw, stream))) return st;
@@ -200,6 +268,8 @@ int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spec
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
+  if (is_multipass(pts))
+    return hip_status(launch_export1d_fourstep(log2i(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
   return hip_status(launch_export1d_single(log2i(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
 }
 

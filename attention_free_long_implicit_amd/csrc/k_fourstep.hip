@@ -1,0 +1,401 @@
+// Multi-pass ("four-step") causal long convolution for 2^15 <= L <= 2^20, where one row's transform
+// does not fit in LDS.  Same operation as the single-pass kernels (Hyena study note, steps 2-3;
+// EulerStack "4. Hyena 상세", how it works 2; HyenaND summary, boundary handling and nSubQ fusion):
+// the packed row z[n] = u[2n] + i u[2n+1] (zero for n >= M/2, M = L) is transformed as an
+// M1 x M2 matrix, n = n2 + M2 n1, bin k = k1 + M1 k2:
+//
+//   pass A  (k_fs_cols)  columns n2: M1-point DFT over n1 (upper half of the input is zero)
+//   pass B  (k_fs_rows)  rows k1 and M1-k1 together: twiddle W_M^{n2 k1}, M2-point DFT over n2,
+//                        mirrored-bin split, product with the filter spectrum, re-pack, inverse
+//                        M2-point DFT, conjugate twiddle
+//   pass C  (k_fs_cols)  columns: inverse M1-point DFT, keep n1 < M1/2 (the causal half), gate;
+//                        for every order but the last the same workgroup then runs the next
+//                        order's pass A on the gated tile, so u_i never goes to HBM
+//
+// The intermediate is one complex fp32 M-vector per row; rows are processed in chunks whose
+// intermediates stay resident in L2 / the memory-side cache.  Rows are visited channel-major
+// (q = d*B + b) so the B rows of a channel read its filter spectrum back to back.
+//
+// Spectrum layout per channel: Hs[g][slot][t'] for row-pair group g < M1/2, slot < 2 RP, thread t'
+// of the pair (see k_fs_rows); g = 0 holds rows k1 = 0 and k1 = M1/2.  Hs = H / (4M).
+#include "engine.h"
+#include "launch.h"
+
+namespace hyena {
+
+template <int LOG2M> struct FourStepPlan;
+// M1 (columns) x M2 (rows); column radices, row radices (last radix 8, 16 elements per thread)
+template <> struct FourStepPlan<15> { using Col = Radices<16, 8>;    using Row = Radices<4, 8, 8>;   static constexpr int G = 4; };
+template <> struct FourStepPlan<16> { using Col = Radices<16, 8>;    using Row = Radices<8, 8, 8>;   static constexpr int G = 2; };
+template <> struct FourStepPlan<17> { using Col = Radices<16, 16>;   using Row = Radices<8, 8, 8>;   static constexpr int G = 2; };
+template <> struct FourStepPlan<18> { using Col = Radices<16, 16>;   using Row = Radices<16, 8, 8>;  static constexpr int G = 1; };
+template <> struct FourStepPlan<19> { using Col = Radices<8, 8, 8>;  using Row = Radices<16, 8, 8>;  static constexpr int G = 1; };
+template <> struct FourStepPlan<20> { using Col = Radices<8, 8, 8>;  using Row = Radices<16, 16, 8>; static constexpr int G = 1; };
+
+template <int LOG2M>
+struct FS {
+  using Plan = FourStepPlan<LOG2M>;
+  using ColRL = typename Plan::Col;
+  using RowRL = typename Plan::Row;
+  static constexpr int M = 1 << LOG2M;
+  static constexpr int M1 = ColRL::S, M2 = RowRL::S;
+  static_assert(M1 * M2 == M, "plan");
+  // column tiles: C columns x M1 positions = 8192 complex in LDS
+  static constexpr int TILE = 8192;
+  static constexpr int C = TILE / M1;
+  static constexpr int TC = 512;
+  using Col = ColEngine<C, C, TC, ColRL>;
+  // row pairs
+  static constexpr int G = Plan::G;
+  using Row = RowEngine<2 * G, RowRL>;
+  static constexpr int RP = RowRL::RP;
+  static constexpr int TP = M2 / RP;              // threads per row pair
+  static constexpr int TR = Row::T;               // = G * TP
+  static_assert(TR == G * TP, "row engine threads");
+};
+
+// ----------------------------------------------------------------------------------------------
+// pass A / pass C (+A of the next order).  MODE: 0 = A from u (load u, forward columns, store I)
+//                                                1 = C (+A): inverse columns, gate, [forward, store I] or store y
+// grid.x = tiles * rows_in_chunk (row fastest); one workgroup = one column tile of one row.
+template <int LOG2M, bool BF16, int MODE, bool GATE, bool CHAIN>
+__global__ void __launch_bounds__(FS<LOG2M>::TC)
+k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* gate,
+          typename Store<BF16>::elem* y, float2* I, int q0, int nq, int B, int D, Twiddles tw) {
+  using F = FS<LOG2M>;
+  using St = Store<BF16>;
+  constexpr int M = F::M, M1 = F::M1, M2 = F::M2, C = F::C, TC = F::TC;
+  constexpr int PER_T = C * M1 / TC;              // tile elements per thread
+  __shared__ float2 lds[lds_padded_size(C * M1)];
+  const int t = threadIdx.x;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int ql = lb % nq, tile = lb / nq;
+  const int q = q0 + ql;
+  const int d = q / B, b = q % B;
+  const size_t row = (size_t)b * D + d;
+  const int c0 = tile * C;
+  float2* Irow = I + (size_t)ql * M;
+  auto tile_addr = [&](int p, int c) { return lds_pad(p * C + c); };
+
+  if constexpr (MODE == 0) {
+    // load the nonzero half of the packed row: positions n1 < M1/2
+    const auto* urow = u + row * M;
+    static_for<PER_T / 2>([&](auto ii) {
+      const int e = t + TC * ii.value;
+      const int p = e / C, c = e % C;
+      lds[tile_addr(p, c)] = St::load2(urow + 2 * ((size_t)(c0 + c) + (size_t)M2 * p));
+    });
+    __syncthreads();
+  } else {
+    static_for<PER_T>([&](auto ii) {
+      const int e = t + TC * ii.value;
+      const int p = e / C, c = e % C;
+      lds[tile_addr(p, c)] = Irow[(size_t)p * M2 + c0 + c];
+    });
+    __syncthreads();
+    F::Col::template inverse<true>(lds, tw, t);
+    // gate the causal half (positions n1 < M1/2 are z'[n2 + M2 n1])
+    const auto* grow = GATE ? gate + row * M : nullptr;
+    auto* yrow = CHAIN ? nullptr : y + row * M;
+    static_for<PER_T / 2>([&](auto ii) {
+      const int e = t + TC * ii.value;
+      const int p = e / C, c = e % C;
+      const size_t j = (size_t)(c0 + c) + (size_t)M2 * p;
+      float2 v = lds[tile_addr(p, c)];
+      if constexpr (GATE) {
+        const float2 g = St::load2(grow + 2 * j);
+        v = make_float2(v.x * g.x, v.y * g.y);
+      }
+      if constexpr (CHAIN) {
+        // the next order consumes the stored (rounded) value, as it would from memory
+        if constexpr (BF16) v = make_float2(bf16_to_f32(f32_to_bf16_rne(v.x)), bf16_to_f32(f32_to_bf16_rne(v.y)));
+        lds[tile_addr(p, c)] = v;
+      } else {
+        St::store2(yrow + 2 * j, v);
+      }
+    });
+    if constexpr (!CHAIN) return;
+    __syncthreads();
+  }
+  F::Col::template forward<true>(lds, tw, t);
+  static_for<PER_T>([&](auto ii) {
+    const int e = t + TC * ii.value;
+    const int p = e / C, c = e % C;
+    Irow[(size_t)p * M2 + c0 + c] = lds[tile_addr(p, c)];
+  });
+}
+
+// Spectrum pass A: fp32 taps h[d, 0:L) (one "row" per channel, B = 1).
+template <int LOG2M>
+__global__ void __launch_bounds__(FS<LOG2M>::TC)
+k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
+  using F = FS<LOG2M>;
+  constexpr int M = F::M, M1 = F::M1, M2 = F::M2, C = F::C, TC = F::TC;
+  constexpr int PER_T = C * M1 / TC;
+  __shared__ float2 lds[lds_padded_size(C * M1)];
+  const int t = threadIdx.x;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int ql = lb % nq, tile = lb / nq;
+  const int d = q0 + ql;
+  const int c0 = tile * C;
+  const float* hrow = h + (size_t)d * M;
+  static_for<PER_T / 2>([&](auto ii) {
+    const int e = t + TC * ii.value;
+    const int p = e / C, c = e % C;
+    lds[lds_pad(p * C + c)] = Store<false>::load2(hrow + 2 * ((size_t)(c0 + c) + (size_t)M2 * p));
+  });
+  __syncthreads();
+  F::Col::template forward<true>(lds, tw, t);
+  float2* Irow = I + (size_t)ql * M;
+  static_for<PER_T>([&](auto ii) {
+    const int e = t + TC * ii.value;
+    const int p = e / C, c = e % C;
+    Irow[(size_t)p * M2 + c0 + c] = lds[lds_pad(p * C + c)];
+  });
+}
+
+// ----------------------------------------------------------------------------------------------
+// pass B.  MODE 0: convolution (spectral product with Hs); MODE 1: write the filter spectrum.
+// Workgroup = G row pairs of one row; pair g_glob = group*G + j covers bin rows k1 = g_glob and
+// M1 - g_glob (g_glob = 0: rows 0 and M1/2).  In the last pass, thread t' < TP of a pair holds block
+// beta_A = t' of the first row and beta_B = NBLK-1-t' of the second (their bins mirror each other:
+// k <-> M-k pairs k1 with M1-k1 and complements every k2 digit); the g_glob = 0 pair instead uses
+// whole-row negation pairing on row 0 (threads < TP/2) and in-row complement pairing on row M1/2.
+template <int LOG2M, int MODE>
+__global__ void __launch_bounds__(FS<LOG2M>::TR)
+k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq, int B,
+          Twiddles tw) {
+  using F = FS<LOG2M>;
+  using Row = typename F::Row;
+  using RL = typename F::RowRL;
+  constexpr int M = F::M, M1 = F::M1, M2 = F::M2, G = F::G, TP = F::TP, TR = F::TR, RP = F::RP;
+  constexpr int E = Row::E, R0 = RL::R[0], PER0 = M2 / R0, NBLK = Row::NBLK;
+  __shared__ float2 lds[Row::LDS_ELEMS];
+  const int t = threadIdx.x;
+  const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
+  const int ql = lb % nq, grp = lb / nq;
+  const int q = q0 + ql;
+  const int d = (MODE == 0) ? q / B : q;
+  float2* Irow = I + (size_t)ql * M;
+
+  // bin row k1 of sub-row s (s = 2j: first of pair j, 2j+1: second)
+  auto k1_of = [&](int s) {
+    const int gg = grp * G + s / 2;
+    if (gg == 0) return (s & 1) ? M1 / 2 : 0;
+    return (s & 1) ? M1 - gg : gg;
+  };
+
+  // load + forward twiddle W_M^{n2 k1}: element m of butterfly i is column n + m * PER0
+  float2 x[E];
+  static_for<E / R0>([&](auto ii) {
+    constexpr int i = ii.value;
+    int s, n;
+    Row::first_input(t, i, s, n);
+    const int k1 = k1_of(s);
+    const float2* src = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
+    const float2 wb = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
+    const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
+    float2 wp[R0];
+    twiddle_powers<R0>(ws, wp);
+    static_for<R0>([&](auto m) {
+      const float2 v = src[n + m.value * PER0];
+      x[i * R0 + m.value] = cmul(v, cmul(wb, wp[m.value]));
+    });
+  });
+  Row::template forward_to_last<false>(x, lds, tw, t);
+
+  // last-pass assignment
+  const int j = t / TP, tp = t % TP;                 // pair within the workgroup, thread within pair
+  const int gg = grp * G + j;
+  int bA, bB, kapA, kapB, k1A;
+  bool selfmirror = false;
+  if (gg != 0) {
+    bA = (2 * j) * NBLK + tp;
+    bB = (2 * j + 1) * NBLK + (NBLK - 1 - tp);
+    kapA = RL::kappa_of_block(tp);
+    kapB = 0;
+    k1A = gg;
+  } else if (tp < TP / 2) {                          // row k1 = 0, negation pairing
+    const auto np = NegPairs<RL>::of(tp);
+    bA = (2 * j) * NBLK + np.betaA;
+    bB = (2 * j) * NBLK + np.betaB;
+    kapA = np.kapA; kapB = np.kapB;
+    selfmirror = np.special;
+    k1A = 0;
+  } else {                                           // row k1 = M1/2, in-row complement pairing
+    const int tq = tp - TP / 2;
+    bA = (2 * j + 1) * NBLK + tq;
+    bB = (2 * j + 1) * NBLK + (NBLK - 1 - tq);
+    kapA = RL::kappa_of_block(tq);
+    kapB = 0;
+    k1A = M1 / 2;
+  }
+  Row::fwd_last(x, lds, bA, bB);
+
+  const size_t hoff = (size_t)d * M + (size_t)gg * (2 * RP * TP) + tp;
+  if (!selfmirror) {
+    const float2 wA = twiddle<LOG2M + 1>(tw, uint32_t(k1A) + uint32_t(M1) * uint32_t(kapA));
+    if constexpr (MODE == 0) spectral_complement<RP, 0>(x, wA, Hs + hoff, TP, nullptr, 0.f);
+    else spectral_complement<RP, 1>(x, wA, nullptr, TP, Hs_out + hoff, 1.0f / (8.0f * M));
+  } else {
+    const float2 wB = twiddle<LOG2M + 1>(tw, uint32_t(M1) * uint32_t(kapB));
+    if constexpr (MODE == 0) spectral_selfmirror<RP, 0>(x, wB, Hs + hoff, TP, nullptr, 0.f);
+    else spectral_selfmirror<RP, 1>(x, wB, nullptr, TP, Hs_out + hoff, 1.0f / (8.0f * M));
+  }
+  if constexpr (MODE == 1) return;
+
+  Row::inv_last(x, lds, bA, bB);
+  Row::template inverse_from_last<false>(x, lds, tw, t);
+  // conjugate twiddle and store back
+  static_for<E / R0>([&](auto ii) {
+    constexpr int i = ii.value;
+    int s, n;
+    Row::first_input(t, i, s, n);
+    const int k1 = k1_of(s);
+    float2* dst = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
+    const float2 wb = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
+    const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
+    float2 wp[R0];
+    twiddle_powers<R0>(ws, wp);
+    static_for<R0>([&](auto m) {
+      dst[n + m.value * PER0] = cmulc(x[i * R0 + m.value], cmul(wb, wp[m.value]));
+    });
+  });
+}
+
+// Engine-order spectrum -> H[d, k], k = 0..L (unscaled 2L-point DFT bins); mirrors k_fs_rows' slots.
+template <int LOG2M>
+__global__ void k_export1d_fs(const float2* __restrict__ Hs, float2* __restrict__ H) {
+  using F = FS<LOG2M>;
+  using RL = typename F::RowRL;
+  constexpr int M = F::M, M1 = F::M1, M2 = F::M2, TP = F::TP, RP = F::RP, NBLK = F::Row::NBLK;
+  const int d = blockIdx.y;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= M) return;
+  const int gg = idx / (2 * RP * TP), rem = idx % (2 * RP * TP);
+  const int slot = rem / TP, tp = rem % TP;
+  const float sc = 4.0f * M;
+  const float2 v = Hs[(size_t)d * M + idx];
+  float2* out = H + (size_t)d * (M + 1);
+  const int m = slot % RP;
+  const bool second = slot >= RP;
+  int k1, kap;
+  if (gg != 0) {
+    k1 = second ? M1 - gg : gg;
+    kap = RL::kappa_of_block(second ? NBLK - 1 - tp : tp);
+  } else if (tp < TP / 2) {
+    const auto np = NegPairs<RL>::of(tp);
+    if (np.special && slot == 0) {
+      out[0] = make_float2(v.x * sc, 0.f);
+      out[M] = make_float2(v.y * sc, 0.f);
+      return;
+    }
+    k1 = 0;
+    kap = second ? np.kapB : np.kapA;
+  } else {
+    const int tq = tp - TP / 2;
+    k1 = M1 / 2;
+    kap = RL::kappa_of_block(second ? NBLK - 1 - tq : tq);
+  }
+  out[k1 + M1 * (kap + (M2 / RP) * m)] = cscale(v, sc);
+}
+
+// ------------------------------------------------------------------ host side
+namespace {
+
+template <int LOG2M>
+size_t fs_row_bytes() { return (size_t)(1 << LOG2M) * sizeof(float2); }
+
+template <int LOG2M, bool BF16>
+hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
+                          void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s) {
+  using F = FS<LOG2M>;
+  using E = typename Store<BF16>::elem;
+  const int rows = B * D;
+  const int tiles = F::M2 / F::C;
+  const int groups = (F::M1 / 2) / F::G;
+  for (int q0 = 0; q0 < rows; q0 += chunk) {
+    const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
+    hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
+                       (const E*)v, (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
+    for (int i = 0; i < order; ++i) {
+      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0>), dim3(groups * nq), dim3(F::TR), 0, s, I,
+                         (const float2*)spectra[i], (float2*)nullptr, q0, nq, B, tw);
+      if (i + 1 < order)
+        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, true>), dim3(tiles * nq), dim3(F::TC), 0, s,
+                           (const E*)nullptr, (const E*)x[i], (E*)nullptr, I, q0, nq, B, D, tw);
+      else if (x[i])
+        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
+                           (const E*)nullptr, (const E*)x[i], (E*)y, I, q0, nq, B, D, tw);
+      else
+        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, false, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
+                           (const E*)nullptr, (const E*)nullptr, (E*)y, I, q0, nq, B, D, tw);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int LOG2M>
+hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
+                              hipStream_t s) {
+  using F = FS<LOG2M>;
+  const int tiles = F::M2 / F::C;
+  const int groups = (F::M1 / 2) / F::G;
+  for (int q0 = 0; q0 < D; q0 += chunk) {
+    const int nq = (D - q0 < chunk) ? D - q0 : chunk;
+    hipLaunchKernelGGL((k_fs_cols_taps<LOG2M>), dim3(tiles * nq), dim3(F::TC), 0, s, h, I, q0, nq, tw);
+    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const float2*)nullptr,
+                       Hs, q0, nq, 1, tw);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+bool fourstep_supported(int log2L) { return log2L >= 15 && log2L <= 20; }
+
+size_t fourstep_row_bytes(int log2L) { return (size_t)1 << log2L << 3; }
+
+#define HYENA_FS_CASES(X) X(15) X(16) X(17) X(18) X(19) X(20)
+
+hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s) {
+  switch (log2L) {
+#define X(n)                                                                                              \
+  case n:                                                                                                 \
+    hipLaunchKernelGGL((k_export1d_fs<n>), dim3(((1 << n) + 255) / 256, D), dim3(256), 0, s, Hs, H);    \
+    return hipGetLastError();
+    HYENA_FS_CASES(X)
+#undef X
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
+                                  const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
+                                  const Twiddles& tw, hipStream_t s) {
+  switch (log2L) {
+#define X(n)                                                                                  \
+  case n:                                                                                     \
+    return bf16 ? fs_conv_launch<n, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s)     \
+                : fs_conv_launch<n, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
+    HYENA_FS_CASES(X)
+#undef X
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
+                                      const Twiddles& tw, hipStream_t s) {
+  switch (log2L) {
+#define X(n) case n: return fs_spectrum_launch<n>(h, Hs, D, I, chunk, tw, s);
+    HYENA_FS_CASES(X)
+#undef X
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hyena

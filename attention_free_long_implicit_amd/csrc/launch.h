@@ -15,6 +15,17 @@ hipError_t launch_spectrum1d_single(int log2L, const float* h, float2* Hs, int D
                                     hipStream_t s);
 hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
 
+// ---- 1-D, multi-pass (2^15 <= L <= 2^20): I is a workspace of `chunk` rows of L complex values.
+// x[i] may be NULL for the last order only (no gate).
+bool fourstep_supported(int log2L);
+size_t fourstep_row_bytes(int log2L);
+hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
+                                  const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
+                                  const Twiddles& tw, hipStream_t s);
+hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
+                                      const Twiddles& tw, hipStream_t s);
+hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
+
 // ---- implicit filter taps
 struct FilterArgs {
   int F, H, D;

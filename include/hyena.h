@@ -74,7 +74,8 @@ typedef struct {
 /* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array). */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
-/* Workspace bytes hyena_filter_gen needs when h_time is NULL (it then keeps the taps there). */
+/* Workspace bytes hyena_filter_gen needs: room for the taps (used when h_time is NULL) plus, for
+ * multi-pass lengths (L > 16384), the transform intermediate of a chunk of channels. */
 int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_fftconv / hyena_operator need (0 when the transform fits on chip). */
@@ -82,8 +83,9 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
 
 /* Implicit filter of one order: writes the taps (1-D: h_time[D, L]; 3-D: h_time[D, 2n-1, 2n-1, 2n-1],
  * offsets from -(n-1)) when h_time is not NULL, and the filter spectrum into `spectrum`
- * (hyena_spectrum_bytes bytes).  ws/ws_bytes: scratch of hyena_filter_workspace_bytes (may be NULL/0
- * when h_time is given).  The spectrum depends only on (params, dims), so callers cache it per length. */
+ * (hyena_spectrum_bytes bytes).  ws/ws_bytes: scratch of hyena_filter_workspace_bytes bytes (may be
+ * NULL/0 when h_time is given and L <= 16384; HYENA_EWORKSPACE when too small).  The spectrum depends
+ * only on (params, dims), so callers cache it per length. */
 int hyena_filter_gen(const hyena_filter_params *p, hyena_dims dims, int mode, float *h_time, void *spectrum,
                      void *ws, size_t ws_bytes, hipStream_t stream);
 

@@ -47,6 +47,11 @@ def test_size_queries(lib):
     assert st == 0 and n == 16 * 1024 * 4
     st, n = _size(lib.hyena_workspace_bytes, 2, 4, 768, L.dims_of([8192]), L.BF16, L.CAUSAL)
     assert st == 0 and n == 0
+    # multi-pass lengths need a workspace of whole rows of L complex fp32 values
+    st, n = _size(lib.hyena_workspace_bytes, 3, 2, 1024, L.dims_of([65536]), L.BF16, L.CAUSAL)
+    assert st == 0 and n > 0 and n % (65536 * 8) == 0
+    st, n = _size(lib.hyena_workspace_bytes, 2, 1, 3, L.dims_of([1 << 20]), L.F32, L.CAUSAL)
+    assert st == 0 and n == 3 * (1 << 20) * 8          # never more rows than there are
 
 
 @pytest.mark.parametrize("shape,mode,status", [
@@ -80,6 +85,12 @@ def test_invalid_arguments_return_before_launch(lib):
     xs_null = (ctypes.c_void_p * 2)(base, None)
     assert lib.hyena_operator(2, 4, 768, d, L.BF16, L.CAUSAL, 0x10, xs_null, sp, 1 << 40, None, 0, None) == L.EINVAL
     assert lib.hyena_operator(2, 4, 768, d, L.BF16, L.CAUSAL, 1 << 40, xs, sp, base + 128, None, 0, None) == L.EALIAS
+    # multi-pass length without a workspace
+    d64 = L.dims_of([65536])
+    assert lib.hyena_operator(2, 4, 768, d64, L.BF16, L.CAUSAL, 1 << 40, xs, sp, 1 << 41, None, 0, None) \
+        == L.EWORKSPACE
+    assert lib.hyena_fftconv(1, 4, d64, L.F32, L.CAUSAL, 1 << 40, 0x10, None, 1 << 41, 1 << 42, 100, None) \
+        == L.EWORKSPACE
     # filter parameters of an unsupported width
     p = L.FilterParams(32, 64, 16, 1, 2, 3, 4, 5)
     assert lib.hyena_filter_gen(ctypes.byref(p), L.dims_of([1024]), L.CAUSAL, 0x1000, 0x2000, None, 0, None) \

@@ -1,0 +1,125 @@
+"""GPU parity of the multi-pass (four-step) 1-D path, 2^15 <= L <= 2^20, against the CPU oracle."""
+import numpy as np
+import pytest
+
+import hyena_inputs as hi
+from oracle import hyena_oracle as orc
+from gpu_util import (BF16_TOL, FP32_TOL, oracle_rows_1d, params_to_dev, rel_err_rows, run_hip_operator, say,
+                      to_dev)
+
+pytestmark = pytest.mark.gpu
+
+MULTI_L = [1 << 15, 1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 20]
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import attention_free_long_implicit_amd as hy
+    hy.lib()
+    return torch
+
+
+@pytest.mark.parametrize("L", [1 << 15, 1 << 16, 1 << 20])
+def test_fourstep_spectrum_matches_numpy(torch_cuda, L):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 3
+    w = hi.WORKLOADS[0].with_(D=D, dims=(L,))
+    p = hi.draw_filter_params(w, seed=L % 997)[0]
+    say(f"four-step spectrum L={L}")
+    h = torch.empty((D, L), dtype=torch.float32, device="cuda")
+    spec = hy.filter_gen(params_to_dev(p), (L,), h_time=h)
+    H = hy.spectrum_export(spec, (L,), D)
+    torch.cuda.synchronize()
+    ref = orc.implicit_filter_1d(p, L)
+    assert rel_err_rows(h.cpu().numpy(), ref).max() < 1e-5
+    Href = np.fft.rfft(ref, 2 * L)
+    Hg = H.cpu().numpy().astype(np.complex128)
+    e = np.linalg.norm(Hg - Href, axis=1) / np.linalg.norm(Href, axis=1)
+    assert e.max() < 2e-5, e.max()
+
+
+@pytest.mark.parametrize("L", MULTI_L)
+def test_fourstep_fftconv_fp32_chunked(torch_cuda, L):
+    """fp32 convolution with a workspace of 3 rows, so B*D = 5 rows take two chunks (one ragged)."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    from attention_free_long_implicit_amd import _lib
+    B, D = 1, 5
+    w = hi.WORKLOADS[0].with_(B=B, D=D, dims=(L,))
+    rng = np.random.default_rng(L % 1009)
+    u = rng.standard_normal((B, D, L)).astype(np.float32)
+    g = rng.standard_normal((B, D, L)).astype(np.float32)
+    p = hi.draw_filter_params(w, seed=3)[0]
+    say(f"four-step fftconv fp32 L={L}")
+    spec = hy.filter_gen(params_to_dev(p), (L,))
+    ws = torch.empty(3 * L * 8, dtype=torch.uint8, device="cuda")
+    y = hy.operator(to_dev(u, torch.float32), [to_dev(g, torch.float32)], [spec], ws=ws)
+    torch.cuda.synchronize()
+    h = orc.implicit_filter_1d(p, L)
+    ref = orc.causal_conv_fft(u.astype(np.float64), h[None]) * g
+    e = rel_err_rows(y.cpu().numpy(), ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < 5e-5, e.max()
+
+
+def test_fourstep_no_gate_and_chunk_invariance(torch_cuda):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L, B, D = 1 << 16, 2, 3
+    w = hi.WORKLOADS[2].with_(B=B, D=D, dims=(L,))
+    v, xs = hi.draw_activations(w, seed=4)
+    params = hi.draw_filter_params(w, seed=4)
+    say("four-step chunk invariance (bf16, order 3)")
+    spectra = [hy.filter_gen(params_to_dev(p), (L,)) for p in params]
+    vd = to_dev(v, torch.bfloat16)
+    xd = [to_dev(x, torch.bfloat16) for x in xs]
+    y_big = hy.operator(vd, xd, spectra)
+    y_one = hy.operator(vd, xd, spectra, ws=torch.empty(L * 8, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(y_big, y_one)
+    # no-gate fftconv of one channel == order-1 oracle convolution
+    p1 = {k: (a[:1] if k in ("W2", "b2", "alpha") else a) for k, a in params[0].items()}
+    spec1 = hy.filter_gen(params_to_dev(p1), (L,))
+    u = np.ascontiguousarray(v[:1, :1]).astype(np.float32)
+    c = hy.fftconv(to_dev(u, torch.float32), spec1)
+    torch.cuda.synchronize()
+    h0 = orc.implicit_filter_1d(params[0], L, channels=[0])
+    ref = orc.causal_conv_fft(u[0].astype(np.float64), h0)
+    assert rel_err_rows(c.cpu().numpy()[0], ref).max() < 5e-5
+
+
+def test_operator_workload2_sampled_rows(torch_cuda):
+    w = hi.WORKLOADS[2]
+    say("operator workload 2 (order 3, B=2 D=1024 L=65536, bf16): drawing inputs")
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    say("  running HIP operator")
+    y = run_hip_operator(w, v, xs, params)
+    rows = [tuple(r) for r in hi.sample_rows(w, 12)]
+    say("  oracle on sampled rows")
+    ref = oracle_rows_1d(w, v, xs, params, rows)
+    got = np.stack([y[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
+    assert e.max() < BF16_TOL
+    assert np.all(np.isfinite(y))
+
+
+def test_operator_workload3_sampled_rows(torch_cuda):
+    w = hi.WORKLOADS[3]
+    say("operator workload 3 (HyenaDNA order 2, B=1 D=256 L=1M, fp32): drawing inputs")
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    say("  running HIP operator")
+    y = run_hip_operator(w, v, xs, params)
+    rows = [tuple(r) for r in hi.sample_rows(w, 6)]
+    say("  oracle on sampled rows")
+    ref = oracle_rows_1d(w, v, xs, params, rows)
+    got = np.stack([y[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
+    assert e.max() < FP32_TOL
+    assert np.all(np.isfinite(y))
