@@ -253,20 +253,27 @@ struct NegPairs {
   }
 };
 
-// Column engine: NL lines, N = RL::S points per line, element (l, p) at lds[lds_pad(p * LP + l)].
-template <int NL, int LP, int T, class RL>
+// Column engine: NL lines of N = RL::S points; element (line l, position p) at
+// lds[addr(p * PS + l * LS)], addr = lds_pad when PAD.  Butterflies are enumerated line-fastest, so
+// consecutive lanes touch consecutive lines (conflict-free when LS == 1, or when LS is odd).
+// NL need not divide the butterfly count evenly among threads (the tail is guarded).
+template <int NL, int PS, int LS, int T, class RL, bool PAD = true>
 struct ColEngine {
   static constexpr int P = RL::P, N = RL::S;
-  __device__ __forceinline__ static int addr(int p, int l) { return lds_pad(p * LP + l); }
+  __device__ __forceinline__ static int addr(int p, int l) {
+    const int a = p * PS + l * LS;
+    return PAD ? lds_pad(a) : a;
+  }
 
   template <int J, bool INV, bool ZERO_UPPER, bool HALF_OUT>
   __device__ __forceinline__ static void pass(float2* lds, const Twiddles& tw, int t) {
     constexpr int R = RL::R[J], SJ = RL::sub(J), Q = SJ / R;
     constexpr int NBF = NL * N / R;                      // butterflies in this pass
-    static_assert(NBF % T == 0, "butterflies must divide evenly among threads");
-    constexpr int NBT = NBF / T;
+    constexpr int NBT = (NBF + T - 1) / T;
+    constexpr bool EVEN = (NBF % T == 0);
     static_for<NBT>([&](auto ii) {
       const int b = t + T * ii.value;
+      if (!EVEN && b >= NBF) return;
       const int l = b % NL, rem = b / NL;
       const int n = rem % Q;
       const int p0 = (rem / Q) * SJ + n;

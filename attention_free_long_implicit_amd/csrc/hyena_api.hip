@@ -68,7 +68,9 @@ int check_dims(hyena_dims dims, int mode, int64_t* points) {
   if (mode == HYENA_LINEAR) {
     if (dims.ndim != 3) return HYENA_EINVAL;
     if (dims.n[0] <= 0 || dims.n[1] <= 0 || dims.n[2] <= 0) return HYENA_EINVAL;
-    return HYENA_EUNSUPPORTED;
+    if (!grid3d_supported(dims.n[0], dims.n[1], dims.n[2])) return HYENA_EUNSUPPORTED;
+    *points = dims.n[0] * dims.n[1] * dims.n[2];
+    return HYENA_OK;
   }
   return HYENA_EINVAL;
 }
@@ -83,10 +85,20 @@ int hip_status(hipError_t e) { return e == hipSuccess ? HYENA_OK : HYENA_EHIP; }
 
 bool is_multipass(int64_t L) { return !single_pass_supported(log2i(L)); }
 
+// Intermediate bytes per (b, d) row / volume for the multi-pass plans (0: single pass).
+size_t row_intermediate_bytes(int mode, int64_t pts) {
+  if (mode == HYENA_LINEAR) return conv3d_volume_bytes();
+  return is_multipass(pts) ? fourstep_row_bytes(log2i(pts)) : 0;
+}
+size_t filter_intermediate_bytes(int mode, int64_t pts) {
+  if (mode == HYENA_LINEAR) return conv3d_filter_volume_bytes();
+  return is_multipass(pts) ? fourstep_row_bytes(log2i(pts)) : 0;
+}
+size_t taps_per_channel(int mode, int64_t pts) { return mode == HYENA_LINEAR ? conv3d_taps_per_channel() : (size_t)pts; }
+
 // Rows per multi-pass chunk by default: about 96 MB of intermediate, so a chunk's intermediate
 // stays in the 256 MB memory-side cache while the next pass reads it.
-int64_t default_chunk_rows(int64_t L, int64_t rows) {
-  const int64_t per = (int64_t)fourstep_row_bytes(log2i(L));
+int64_t default_chunk_rows(int64_t per, int64_t rows) {
   int64_t c = ((int64_t)96 << 20) / per;
   if (c < 1) c = 1;
   return c < rows ? c : rows;
@@ -99,10 +111,10 @@ int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const v
 }
 
 // Multi-pass chunk rows that fit the caller's workspace (0 when it is too small).
-int chunk_from_ws(int64_t L, int64_t rows, void* ws, size_t ws_bytes) {
+int chunk_from_ws(size_t per, int64_t rows, void* ws, size_t ws_bytes) {
   if (!ws) return 0;
   if ((size_t)ws & 255u) return 0;
-  const int64_t c = (int64_t)(ws_bytes / fourstep_row_bytes(log2i(L)));
+  const int64_t c = (int64_t)(ws_bytes / per);
   return (int)(c < rows ? c : rows);
 }
 
@@ -129,7 +141,8 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
-  *bytes = (size_t)D * (size_t)pts * sizeof(float2);
+  if (mode == HYENA_LINEAR) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel();
+  else *bytes = (size_t)D * (size_t)pts * sizeof(float2);
   return HYENA_OK;
 }
 
@@ -138,9 +151,9 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* b
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
-  *bytes = (size_t)D * (size_t)pts * sizeof(float);
-  if (mode == HYENA_CAUSAL && is_multipass(pts))
-    *bytes += (size_t)default_chunk_rows(pts, D) * fourstep_row_bytes(log2i(pts));
+  *bytes = (size_t)D * taps_per_channel(mode, pts) * sizeof(float);
+  const size_t per = filter_intermediate_bytes(mode, pts);
+  if (per) *bytes += 256 + (size_t)default_chunk_rows((int64_t)per, D) * per;
   return HYENA_OK;
 }
 
@@ -150,8 +163,8 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   *bytes = 0;
-  if (mode == HYENA_CAUSAL && is_multipass(pts))
-    *bytes = (size_t)default_chunk_rows(pts, B * D) * fourstep_row_bytes(log2i(pts));
+  const size_t per = row_intermediate_bytes(mode, pts);
+  if (per) *bytes = (size_t)default_chunk_rows((int64_t)per, B * D) * per;
   return HYENA_OK;
 }
 
@@ -162,10 +175,10 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   if (p->H != 64 || p->F != (mode == HYENA_CAUSAL ? 64 : 96)) return HYENA_EUNSUPPORTED;
-  const size_t hbytes = (size_t)p->D * (size_t)pts * sizeof(float);
+  const size_t hbytes = (size_t)p->D * taps_per_channel(mode, pts) * sizeof(float);
   const int64_t L = pts;
-  const bool multi = is_multipass(L);
-  const size_t row_b = multi ? fourstep_row_bytes(log2i(L)) : 0;
+  const size_t row_b = filter_intermediate_bytes(mode, pts);
+  const bool multi = row_b != 0;
   char* wsp = (char*)ws;
   size_t wsn = ws ? ws_bytes : 0;
   float* h = h_time;
@@ -192,6 +205,10 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
   FilterArgs a{p->F, p->H, p->D, p->W1, p->b1, p->W2, p->b2, p->alpha};
+  if (mode == HYENA_LINEAR) {
+    if ((st = hip_status(launch_filter3d(a, h, stream)))) return st;
+    return hip_status(launch_spectrum3d(h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream));
+  }
   if ((st = hip_status(launch_filter1d(a, (int)L, h, stream)))) return st;
   if (multi)
     return hip_status(launch_spectrum1d_fourstep(log2i(L), h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw,
@@ -210,8 +227,9 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   if (y != u && overlaps(y, tb, u, tb)) return HYENA_EALIAS;
   if (gate && y != gate && overlaps(y, tb, gate, tb)) return HYENA_EALIAS;
   int chunk = 0;
-  if (is_multipass(pts)) {
-    chunk = chunk_from_ws(pts, B * D, ws, ws_bytes);
+  const size_t per = row_intermediate_bytes(mode, pts);
+  if (per) {
+    chunk = chunk_from_ws(per, B * D, ws, ws_bytes);
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, u, tb) || (gate && overlaps(ws, ws_bytes, gate, tb)))
       return HYENA_EALIAS;
@@ -221,6 +239,9 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   if (chunk) {
     const void* xs[1] = {gate};
     const void* sp[1] = {spectrum};
+    if (mode == HYENA_LINEAR)
+      return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
+                                      stream));
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y,
                                              (float2*)ws, chunk, tw, stream));
   }
@@ -243,8 +264,9 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   for (int i = 0; i < order; ++i)
     if (overlaps(y, tb, x[i], tb)) return HYENA_EALIAS;
   int chunk = 0;
-  if (is_multipass(pts)) {
-    chunk = chunk_from_ws(pts, B * D, ws, ws_bytes);
+  const size_t per = row_intermediate_bytes(mode, pts);
+  if (per) {
+    chunk = chunk_from_ws(per, B * D, ws, ws_bytes);
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
     for (int i = 0; i < order; ++i)
@@ -252,6 +274,9 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   }
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
+  if (chunk && mode == HYENA_LINEAR)
+    return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws, chunk,
+                                    tw, stream));
   if (chunk)
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra,
                                              y, (float2*)ws, chunk, tw, stream));
@@ -268,6 +293,8 @@ int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spec
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
+  if (mode == HYENA_LINEAR)
+    return hip_status(launch_export3d((const float2*)spectrum, (float2*)H, (int)D, stream));
   if (is_multipass(pts))
     return hip_status(launch_export1d_fourstep(log2i(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
   return hip_status(launch_export1d_single(log2i(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));

@@ -44,7 +44,7 @@ struct FS {
   static constexpr int TILE = 8192;
   static constexpr int C = TILE / M1;
   static constexpr int TC = 512;
-  using Col = ColEngine<C, C, TC, ColRL>;
+  using Col = ColEngine<C, C, 1, TC, ColRL>;
   // row pairs
   static constexpr int G = Plan::G;
   using Row = RowEngine<2 * G, RowRL>;

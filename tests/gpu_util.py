@@ -58,5 +58,5 @@ def oracle_rows_1d(w, v, xs, params, rows):
     return np.stack(out)
 
 
-def rel_err_rows(got_rows, ref_rows):
-    return orc.rel_l2_per_row(got_rows, ref_rows)
+def rel_err_rows(got_rows, ref_rows, point_axes=1):
+    return orc.rel_l2_per_row(got_rows, ref_rows, point_axes=point_axes)

@@ -52,6 +52,11 @@ def test_size_queries(lib):
     assert st == 0 and n > 0 and n % (65536 * 8) == 0
     st, n = _size(lib.hyena_workspace_bytes, 2, 1, 3, L.dims_of([1 << 20]), L.F32, L.CAUSAL)
     assert st == 0 and n == 3 * (1 << 20) * 8          # never more rows than there are
+    # 3-D: spectrum 128 x 128 x 65 bins per channel; intermediate 64 x 128 x 65 per volume
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.LINEAR, 128)
+    assert st == 0 and n == 128 * 128 * 128 * 65 * 8
+    st, n = _size(lib.hyena_workspace_bytes, 2, 1, 2, L.dims_of([64, 64, 64]), L.F32, L.LINEAR)
+    assert st == 0 and n == 2 * 64 * 128 * 65 * 8
 
 
 @pytest.mark.parametrize("shape,mode,status", [
@@ -61,6 +66,7 @@ def test_size_queries(lib):
     ([0], L.CAUSAL, L.EINVAL),
     ([1024], L.LINEAR, L.EINVAL),            # linear mode needs a 3-D grid
     ([64, 64, 64], L.CAUSAL, L.EINVAL),      # causal mode needs 1-D
+    ([32, 32, 32], L.LINEAR, L.EUNSUPPORTED),  # only the 64^3 grid is planned
     ([1024], L.CIRCULAR, L.EUNSUPPORTED),
 ])
 def test_bad_shapes(lib, shape, mode, status):

@@ -1,0 +1,112 @@
+"""GPU parity of the 3-D (HyenaND-style) path: 64^3 grid, zero-padded non-causal convolution."""
+import numpy as np
+import pytest
+
+import hyena_inputs as hi
+from oracle import hyena_oracle as orc
+from gpu_util import FP32_TOL, params_to_dev, rel_err_rows, say, to_dev
+
+pytestmark = pytest.mark.gpu
+N = 64
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    import attention_free_long_implicit_amd as hy
+    hy.lib()
+    return torch
+
+
+def _placed(h, n=N):
+    """Filter offsets [-(n-1), n-1]^3 placed at r mod 2n (index n is zero)."""
+    m = 2 * n
+    hp = np.zeros(h.shape[:-3] + (m, m, m))
+    idx = np.arange(-(n - 1), n) % m
+    hp[..., idx[:, None, None], idx[None, :, None], idx[None, None, :]] = h
+    return hp
+
+
+def test_filter3d_taps_and_spectrum(torch_cuda):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 2
+    w = hi.WORKLOADS[4].with_(D=D)
+    p = hi.draw_filter_params(w, seed=41)[0]
+    say("3-D filter taps + spectrum, D=2")
+    h = torch.empty((D, 127, 127, 127), dtype=torch.float32, device="cuda")
+    spec = hy.filter_gen(params_to_dev(p), (N, N, N), h_time=h)
+    H = hy.spectrum_export(spec, (N, N, N), D)
+    torch.cuda.synchronize()
+    ref = orc.implicit_filter_3d(p, N)
+    e = rel_err_rows(h.cpu().numpy(), ref, point_axes=3)
+    assert e.max() < 1e-5, e.max()
+    Href = np.fft.rfftn(_placed(ref), axes=(-3, -2, -1))
+    Hg = H.cpu().numpy().astype(np.complex128)
+    e = np.sqrt(np.sum(np.abs(Hg - Href) ** 2, axis=(1, 2, 3)) / np.sum(np.abs(Href) ** 2, axis=(1, 2, 3)))
+    assert e.max() < 2e-5, e.max()
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_fftconv3d_fp32_matches_oracle(torch_cuda, gate):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    B, D = 1, 3
+    w = hi.WORKLOADS[4].with_(B=B, D=D)
+    rng = np.random.default_rng(42)
+    u = rng.standard_normal((B, D, N, N, N)).astype(np.float32)
+    g = rng.standard_normal((B, D, N, N, N)).astype(np.float32)
+    p = hi.draw_filter_params(w, seed=42)[0]
+    say(f"3-D fftconv fp32 gate={gate}")
+    spec = hy.filter_gen(params_to_dev(p), (N, N, N))
+    ws = torch.empty(2 * N * 8320 * 8, dtype=torch.uint8, device="cuda")   # two volumes per chunk: 2 chunks
+    y = hy.operator(to_dev(u, torch.float32), [to_dev(g, torch.float32)], [spec], ws=ws) if gate else \
+        hy.fftconv(to_dev(u, torch.float32), spec)
+    torch.cuda.synchronize()
+    h = orc.implicit_filter_3d(p, N)
+    ref = orc.linear_conv3d_fft(u[0].astype(np.float64), h)
+    if gate:
+        ref = ref * g[0]
+    e = rel_err_rows(y.cpu().numpy()[0], ref, point_axes=3)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < 2e-5, e.max()
+
+
+def test_conv3d_delta_filter(torch_cuda):
+    """A window steep enough that h = b2 * delta(r): y = b2_1 b2_2 v x_1 x_2 (bf16 storage)."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 2
+    w = hi.WORKLOADS[4].with_(D=D, dtype="bf16")
+    v, xs = hi.draw_activations(w, seed=7)
+    params = [dict(W1=np.zeros((64, 96), np.float32), b1=np.zeros(64, np.float32), W2=np.zeros((D, 64), np.float32),
+                   b2=np.full(D, s, np.float32), alpha=np.full(D, 1e6, np.float32)) for s in (0.5, 4.0)]
+    say("3-D delta filter")
+    spectra = [hy.filter_gen(params_to_dev(p), (N, N, N)) for p in params]
+    y = hy.operator(to_dev(v, torch.bfloat16), [to_dev(x, torch.bfloat16) for x in xs], spectra)
+    torch.cuda.synchronize()
+    ref = 2.0 * v.astype(np.float64) * xs[0] * xs[1]
+    e = rel_err_rows(y.float().cpu().numpy(), ref, point_axes=3)
+    assert e.max() < 1e-2, e.max()
+
+
+def test_operator_workload4_sampled_channels(torch_cuda):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[4]
+    say("operator workload 4 (HyenaND 3-D order 2, D=128, 64^3, fp32)")
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
+    y = hy.operator(to_dev(v, torch.float32), [to_dev(x, torch.float32) for x in xs], spectra)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    chans = [0, 37, 127]
+    say("  oracle on sampled channels")
+    hs = [orc.implicit_filter_3d(p, N, channels=chans) for p in params]
+    ref = orc.hyena_operator_3d(v[0, chans], [x[0, chans] for x in xs], hs)
+    e = rel_err_rows(y[0, chans], ref, point_axes=3)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < FP32_TOL
+    assert np.all(np.isfinite(y))
