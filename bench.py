@@ -2,12 +2,13 @@
 """Benchmark of the Hyena operator hot path on one MI355X.
 
 A step is one call of the order-N operator (every order: load, zero-padded forward transform,
-product with the cached filter spectrum, inverse transform, causal cut, gate, store) over one batch
-of seeded synthetic input already resident in HBM.  The filter spectra depend only on the filter
-parameters and the length, so they are built once (hyena_filter_gen) before the timed region and
+product with the cached filter spectrum, inverse transform, cut to the output window, gate, store)
+over one batch of seeded synthetic input already resident in HBM.  The filter spectra depend only on
+the filter parameters and the grid, so they are built once (hyena_filter_gen) before the timed region;
 that build is reported separately as ``filter_gen_ms``.
 
-Prints ONE JSON line (rank 0).  Default workload: order 2, B=4, D=768, L=8192, bf16 storage.
+Prints ONE JSON line.  Default workload: order 2, B=4, D=768, L=8192, bf16 storage (workload 1);
+``--workload i`` times another of hyena_inputs.WORKLOADS (parity configurations are not bench lines).
 """
 from __future__ import annotations
 
@@ -26,25 +27,31 @@ import hyena_inputs as hi  # noqa: E402
 
 PEAK_HBM_GBPS = 8000.0
 METRIC = "Hyena op tokens·channels/s + HBM GB/s (% peak), order 2, L=8K..1M, 1 GPU"
-KERNEL_NAME = {1: "k_conv1d<13, bf16, gate>"}
 
 
 def algorithmic_bytes_per_order(w) -> int:
-    """One HBM round trip per order: read u, read x_i, write u_i (s bytes each), plus the filter read
-    once in its smallest exact form (fp32 taps), shared by the B rows of a channel."""
+    """One HBM round trip per order: read u, read x_i, write u_i (s bytes each per token-channel),
+    plus the filter read once in its smallest exact form (fp32 taps), shared by the B rows of a channel."""
     return 3 * w.elem_bytes * w.tokens_channels + 4 * w.D * w.support
 
 
-def load_traffic(kernel_key: str):
+def kernel_key(w) -> str:
+    if w.ndim == 3:
+        return f"conv3d_{w.dims[0]}cubed_{w.dtype}"
+    L = w.dims[0]
+    return f"conv1d_L{L}_{w.dtype}_gate" if L <= 16384 else f"fourstep_L{L}_{w.dtype}"
+
+
+def load_traffic(key: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it was taken on the
-    current kernel source (matched by hash); else None."""
+    current kernel sources (matched by hash); else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     try:
         with open(path) as f:
             data = json.load(f)
-        ent = data.get(kernel_key)
+        ent = data.get(key)
         if not ent:
             return None
         from attention_free_long_implicit_amd.build import source_hash
@@ -56,27 +63,54 @@ def load_traffic(kernel_key: str):
 
 
 def cpu_baseline(w, v, xs, params, budget_s: float):
-    """The oracle as it stands, on whole (b, d) rows of the same workload, until ~budget_s of CPU time;
-    filters for the sampled channels are built before the clock starts (as the GPU's are)."""
+    """The oracle as it stands on whole (b, d) rows (volumes) of the same workload, until about
+    budget_s seconds of oracle time; the filters of the sampled channels are built outside the
+    timed part (as the GPU's spectra are), and building stops once it has taken 3 x budget_s."""
     from oracle import hyena_oracle as orc
-    L = w.dims[0]
     rows = hi.sample_rows(w, 4096, seed=99)
     filt = {}
-    n_done = 0
-    t_used = 0.0
+    n_done, t_used, t_build = 0, 0.0, 0.0
     for b, d in rows:
         if d not in filt:
-            filt[d] = [orc.implicit_filter_1d(p, L, channels=[d]) for p in params]
+            if t_build > 3 * budget_s and n_done > 0:
+                break
+            tb = time.perf_counter()
+            if w.ndim == 1:
+                filt[d] = [orc.implicit_filter_1d(p, w.dims[0], channels=[d]) for p in params]
+            else:
+                filt[d] = [orc.implicit_filter_3d(p, w.dims[0], channels=[d]) for p in params]
+            t_build += time.perf_counter() - tb
+            print(f"cpu baseline: filters for channel {d} built ({t_build:.1f} s so far)", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
-        orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], filt[d])
+        if w.ndim == 1:
+            orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], filt[d])
+        else:
+            orc.hyena_operator_3d(v[b, d][None], [x[b, d][None] for x in xs], filt[d])
         t_used += time.perf_counter() - t0
         n_done += 1
         if t_used >= budget_s:
             break
-    value = n_done * L / t_used
-    return {"value": value, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_done} of {w.B * w.D} (b,d) rows of the same workload, order {w.order}, fp64 numpy FFT "
-                      f"convolution on one core, filters prebuilt; {t_used:.1f} s"}
+    return {"value": n_done * w.points / t_used, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_done} of {w.B * w.D} (b,d) rows of the same workload, order {w.order}, float64 numpy FFT "
+                      f"convolution on one core (numpy.fft is single-threaded), filters prebuilt; {t_used:.1f} s"}
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
+    """Device-to-device copy of nbytes (read + write) as the practical bandwidth ceiling."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return 2 * nbytes / (ms / 1e3) / 1e9
 
 
 def main():
@@ -87,20 +121,20 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="index into hyena_inputs.WORKLOADS")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the device copy-bandwidth probe")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only: the operator's (b, d) rows are independent "
-                                   "and a multi-GPU run would shard channels with no communication; use --gpus 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the operator's (b, d) rows are independent, "
+                                   "so a multi-GPU run would shard channels with no communication; use --gpus 1"}))
         sys.exit(2)
 
     import torch
     import attention_free_long_implicit_amd as hy
+    from attention_free_long_implicit_amd import _lib
 
     w = hi.WORKLOADS[args.workload]
-    if w.ndim != 1:
-        raise SystemExit("bench.py times the 1-D workloads")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     v, xs = hi.draw_activations(w)
     params = hi.draw_filter_params(w)
@@ -110,8 +144,10 @@ def main():
     xd = [torch.from_numpy(x).to(dev).to(dt) for x in xs]
     pd = [{k: torch.from_numpy(a).to(dev) for k, a in p.items()} for p in params]
     y = torch.empty_like(vd)
+    ws_n = _lib.workspace_bytes(w.order, w.B, w.D, w.dims, _lib.BF16 if w.dtype == "bf16" else _lib.F32)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
 
-    # filter spectra (cached per length): timed separately
+    # filter spectra (cached per grid): timed separately
     spectra = [hy.filter_gen(p, w.dims) for p in pd]
     torch.cuda.synchronize()
     fg = []
@@ -124,7 +160,7 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
-        hy.operator(vd, xd, spectra, y=y)
+        hy.operator(vd, xd, spectra, y=y, ws=ws)
     torch.cuda.synchronize()
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -132,7 +168,7 @@ def main():
     t0 = time.perf_counter()
     ev[0].record(stream)
     for k in range(args.steps):
-        hy.operator(vd, xd, spectra, y=y)
+        hy.operator(vd, xd, spectra, y=y, ws=ws)
         ev[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -141,13 +177,7 @@ def main():
     ms_per_step = 1e3 * wall / args.steps
     T = w.tokens_channels
     value = T / (ms_per_step / 1e3)
-    # dominant kernel: the fused per-order convolution kernel, launched `order` times per step
-    launch_ms = float(np.mean(step_ms)) / w.order
-    bytes_launch = algorithmic_bytes_per_order(w)
-    achieved = bytes_launch / (launch_ms / 1e3) / 1e9
-    kernel_key = f"conv1d_L{w.dims[0]}_{w.dtype}_gate"
-    traffic = load_traffic(kernel_key)
-
+    alg_step = algorithmic_bytes_per_order(w) * w.order
     out = {
         "metric": METRIC,
         "value": value,
@@ -160,16 +190,31 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) activations, Xavier-uniform filter networks)",
-        "config": {"workload": w.name, "order": w.order, "B": w.B, "D": w.D, "L": w.dims[0],
+        "data": "synthetic (seeded activations, Xavier-uniform filter networks; see hyena_inputs)",
+        "config": {"workload": w.name, "order": w.order, "B": w.B, "D": w.D, "grid": list(w.dims),
                    "storage": w.dtype, "arithmetic": "fp32"},
-        "hbm_gbps_alg": algorithmic_bytes_per_order(w) * w.order / (ms_per_step / 1e3) / 1e9,
-        "hbm_frac_alg": algorithmic_bytes_per_order(w) * w.order / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "hbm_gbps_alg": alg_step / (ms_per_step / 1e3) / 1e9,
+        "hbm_frac_alg": alg_step / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "event_ms_per_step": float(np.mean(step_ms)),
         "filter_gen_ms": filter_gen_ms,
-        "roofline": {"bound": "hbm", "kernel": kernel_key, "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-                     "launch_ms": launch_ms, "alg_bytes_per_launch": bytes_launch},
     }
+    key = kernel_key(w)
+    if w.ndim == 1 and w.dims[0] <= 16384:
+        # the whole step is `order` launches of one fused kernel: its average launch duration
+        launch_ms = float(np.mean(step_ms)) / w.order
+        bytes_launch = algorithmic_bytes_per_order(w)
+        achieved = bytes_launch / (launch_ms / 1e3) / 1e9
+        out["roofline"] = {"bound": "hbm", "kernel": key, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": load_traffic(key),
+                           "launch_ms": launch_ms, "alg_bytes_per_launch": bytes_launch}
+    else:
+        # several kernels per order: the whole step against the algorithmic bytes of the step
+        achieved = alg_step / (float(np.mean(step_ms)) / 1e3) / 1e9
+        out["roofline"] = {"bound": "hbm", "kernel": key + " (whole step)", "achieved": achieved,
+                           "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                           "traffic": load_traffic(key), "alg_bytes_per_step": alg_step}
+    if not args.no_copy:
+        out["copy_gbps"] = copy_bandwidth(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, v, xs, params, args.cpu_budget)
     print(json.dumps(out), flush=True)
