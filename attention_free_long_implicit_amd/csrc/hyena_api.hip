@@ -16,6 +16,7 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 Twiddles g_tw[kMaxDevices];
+const void* g_mats[kMaxDevices];     // DFT matrices of the matrix-core path (bf16, per lane)
 bool g_tw_ready[kMaxDevices];
 
 // W_N^j = exp(-2 pi i j / N) in double, rounded once to fp32.
@@ -40,12 +41,32 @@ int get_twiddles(Twiddles* out) {
       (void)hipFree(d);
       return HYENA_EHIP;
     }
+    std::vector<uint16_t> mats(mfma_matrices_count());
+    mfma_matrices_host(mats.data());
+    void* dm = nullptr;
+    if (hipMalloc(&dm, mats.size() * sizeof(uint16_t)) != hipSuccess) {
+      (void)hipFree(d);
+      return HYENA_EHIP;
+    }
+    if (hipMemcpy(dm, mats.data(), mats.size() * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess) {
+      (void)hipFree(d);
+      (void)hipFree(dm);
+      return HYENA_EHIP;
+    }
     g_tw[dev].pow2 = d;
     g_tw[dev].fine = d + kTwPow2Entries;
+    g_mats[dev] = dm;
     g_tw_ready[dev] = true;
   }
   *out = g_tw[dev];
   return HYENA_OK;
+}
+
+const void* device_mats() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_tw_ready[dev] ? g_mats[dev] : nullptr;
 }
 
 bool is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
@@ -96,6 +117,10 @@ size_t filter_intermediate_bytes(int mode, int64_t pts) {
 }
 size_t taps_per_channel(int mode, int64_t pts) { return mode == HYENA_LINEAR ? conv3d_taps_per_channel() : (size_t)pts; }
 
+// Lengths whose spectrum also carries the matrix-core (row-pair, bf16) copy after the fp32 one.
+bool has_pair_copy(int64_t L) { return mfma_pair_supported(log2i(L), 2); }
+size_t pair_copy_temp_bytes(int64_t L, int64_t D) { return (size_t)D * (size_t)(L + 1) * sizeof(float2); }
+
 // Rows per multi-pass chunk by default: about 96 MB of intermediate, so a chunk's intermediate
 // stays in the 256 MB memory-side cache while the next pass reads it.
 int64_t default_chunk_rows(int64_t per, int64_t rows) {
@@ -106,6 +131,12 @@ int64_t default_chunk_rows(int64_t per, int64_t rows) {
 
 int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const void* spectrum, const void* gate,
               void* y, const Twiddles& tw, hipStream_t s) {
+  if (dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B)) {
+    const void* mats = device_mats();
+    if (!mats) return HYENA_EHIP;
+    const void* pair = (const char*)spectrum + (size_t)D * (size_t)L * sizeof(float2);
+    return hip_status(launch_conv_mfma(u, gate, y, pair, mats, (int)B, (int)D, tw, s));
+  }
   return hip_status(launch_conv1d_single(log2i(L), dtype == HYENA_BF16, u, gate, y, (const float2*)spectrum,
                                          (int)B, (int)D, tw, s));
 }
@@ -142,7 +173,7 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   if (mode == HYENA_LINEAR) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel();
-  else *bytes = (size_t)D * (size_t)pts * sizeof(float2);
+  else *bytes = (size_t)D * (size_t)pts * sizeof(float2) + (has_pair_copy(pts) ? (size_t)D * mfma_pair_spectrum_bytes_per_channel() : 0);
   return HYENA_OK;
 }
 
@@ -152,6 +183,7 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* b
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   *bytes = (size_t)D * taps_per_channel(mode, pts) * sizeof(float);
+  if (mode == HYENA_CAUSAL && has_pair_copy(pts)) *bytes += 256 + pair_copy_temp_bytes(pts, D);
   const size_t per = filter_intermediate_bytes(mode, pts);
   if (per) *bytes += 256 + (size_t)default_chunk_rows((int64_t)per, D) * per;
   return HYENA_OK;
@@ -213,7 +245,18 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
   if (multi)
     return hip_status(launch_spectrum1d_fourstep(log2i(L), h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw,
                                                  stream));
-  return hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, p->D, tw, stream));
+  if ((st = hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, p->D, tw, stream)))) return st;
+  if (has_pair_copy(L)) {
+    // natural-order bins into the workspace, then the pair-order bf16 copy after the fp32 spectrum
+    const size_t mis = (size_t)wsp & 255u;
+    const size_t adv = mis ? 256 - mis : 0;
+    if (wsn < adv + pair_copy_temp_bytes(L, p->D)) return HYENA_EWORKSPACE;
+    float2* nat = (float2*)(wsp + adv);
+    if ((st = hip_status(launch_export1d_single(log2i(L), (const float2*)spectrum, nat, p->D, stream)))) return st;
+    void* pair = (char*)spectrum + (size_t)p->D * (size_t)L * sizeof(float2);
+    return hip_status(launch_pair_spectrum(nat, pair, p->D, stream));
+  }
+  return HYENA_OK;
 }
 
 int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void* u, const void* spectrum,

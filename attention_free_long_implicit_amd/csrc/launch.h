@@ -38,6 +38,15 @@ hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int c
                              hipStream_t s);
 hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s);
 
+// ---- matrix-core path: bf16 storage, L = 8192, rows in pairs of one channel (B even)
+bool mfma_pair_supported(int log2L, int B);
+size_t mfma_pair_spectrum_bytes_per_channel();
+size_t mfma_matrices_count();                    // bf16 values in the DFT-matrix table
+void mfma_matrices_host(uint16_t* out);
+hipError_t launch_conv_mfma(const void* u, const void* gate, void* y, const void* Hc, const void* mats, int B, int D,
+                            const Twiddles& tw, hipStream_t s);
+hipError_t launch_pair_spectrum(const float2* Hnat, void* Hc, int D, hipStream_t s);
+
 // ---- implicit filter taps
 struct FilterArgs {
   int F, H, D;

@@ -184,3 +184,39 @@ def test_rows_are_independent_and_causal(torch_cuda):
     scale = np.max(np.abs(base[0, 2]))
     assert np.max(np.abs(yp[0, 2, :t0] - base[0, 2, :t0])) < 1e-5 * scale
     assert np.max(np.abs(yp[0, 2, t0:] - base[0, 2, t0:])) > 1e-2 * scale
+
+
+@pytest.mark.parametrize("B", [2, 4])
+def test_matrix_core_path_bf16_L8192(torch_cuda, B):
+    """bf16 storage, L = 8192, even B: the rows of a channel are transformed in pairs on the matrix
+    cores.  All rows against the oracle, plus in-place and bitwise determinism."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[1].with_(B=B, D=6, dims=(8192,))
+    v, xs = hi.draw_activations(w, seed=21)
+    params = hi.draw_filter_params(w, seed=21)
+    say(f"matrix-core path B={B}")
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
+    vd = to_dev(v, torch.bfloat16)
+    xd = [to_dev(x, torch.bfloat16) for x in xs]
+    y1 = hy.operator(vd, xd, spectra)
+    y2 = hy.operator(vd, xd, spectra)
+    vi = vd.clone()
+    hy.operator(vi, xd, spectra, y=vi)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(y1, vi)
+    rows = [(b, d) for b in range(B) for d in range(6)]
+    ref = oracle_rows_1d(w, v, xs, params, rows)
+    got = np.stack([y1.float().cpu().numpy()[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
+    assert e.max() < BF16_TOL
+    # the same data through the fp32-arithmetic path (odd B takes it): one extra row of zeros
+    vz = np.concatenate([v, np.zeros_like(v[:1])])
+    xz = [np.concatenate([x, np.zeros_like(x[:1])]) for x in xs]
+    y3 = hy.operator(to_dev(vz, torch.bfloat16), [to_dev(x, torch.bfloat16) for x in xz], spectra)
+    torch.cuda.synchronize()
+    got3 = np.stack([y3.float().cpu().numpy()[b, d] for b, d in rows])
+    e2 = rel_err_rows(got3, ref)
+    say(f"  odd-B (fp32 engine) max rel err {e2.max():.3e}")
+    assert e2.max() < BF16_TOL
