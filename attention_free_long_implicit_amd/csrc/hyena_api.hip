@@ -131,7 +131,10 @@ int64_t default_chunk_rows(int64_t per, int64_t rows) {
 
 int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const void* spectrum, const void* gate,
               void* y, const Twiddles& tw, hipStream_t s) {
-  if (dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B)) {
+  // the matrix-core kernel moves 16-byte vectors: every activation pointer must be 16-byte aligned
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(u) | reinterpret_cast<uintptr_t>(gate) |
+                           reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
+  if (dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B) && aligned16) {
     const void* mats = device_mats();
     if (!mats) return HYENA_EHIP;
     const void* pair = (const char*)spectrum + (size_t)D * (size_t)L * sizeof(float2);

@@ -18,10 +18,14 @@
 //   pass 2' inverse DFT over k2, conj twiddle W_N^{(n3 + 32 n2) k1}
 //   pass 1' inverse DFT over k1, keep n1 < 8 (the causal half); gate; store
 // A complex radix-R DFT is a real 2R x 2R matrix on (Re, Im); each MFMA (32x32x16) multiplies a 32-row
-// block of it by 32 columns (independent sub-transforms).  Every lane keeps the DFT matrices it needs
-// (44 VGPRs).  LDS rows hold 32 values plus one pad, so lanes reading one element each from 32
-// consecutive rows, or 32 consecutive elements of one row, hit distinct banks.  Passes 2, 3, 3' and
-// 2' of tile k1 touch only slab k1, which one wave owns, so only two barriers are needed.
+// block of it by 32 columns (independent sub-transforms).  Every lane keeps the radix-32 matrices it
+// needs (32 VGPRs).  LDS holds one plane of complex bf16 words (re low, im high); rows hold 32 words plus
+// one pad, so lanes reading one word each from 32 consecutive rows, or 32 consecutive words of one
+// row, hit distinct banks.  Passes 2, 3, 3' and 2' of tile k1 touch only slab k1, which one wave owns,
+// so only two barriers are needed.  Global memory is touched in 16-byte accesses only: pass 1 and
+// pass 1' give each lane 8 tiles whose columns are 8 consecutive samples.  Twiddles come from the
+// tables once per lane and are advanced by complex products (recurrence over tiles, short power
+// chains within a slab), so no table gather sits on the critical path.
 #include <math.h>
 #include <string.h>
 
@@ -76,165 +80,249 @@ __device__ __forceinline__ void dft32(const bf16x8 (&A)[mf::NMAT], int c_lo, int
   di = mfma(A[s_hi], sxr_hi, di);
 }
 
-// Gather 8 bf16 of one plane: base + e * stride, e < 8
-template <int STRIDE>
-__device__ __forceinline__ bf16x8 lds8(const __bf16* p) {
-  bf16x8 r;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// two floats -> one dword of bf16 (round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const bf16x2 v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float2 unpack_c(uint32_t w) { return make_float2(lo_f32(w), hi_f32(w)); }
+
+// 8 complex bf16 words (re low, im high) -> the 8 real parts and the 8 imaginary parts as MFMA operands
+__device__ __forceinline__ void split8(const uint32_t (&c)[8], bf16x8& re, bf16x8& im) {
+  u32x4 r, i;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = p[e * STRIDE];
-  return r;
+  for (int m = 0; m < 4; ++m) {
+    r[m] = __builtin_amdgcn_perm(c[2 * m + 1], c[2 * m], 0x05040100u);
+    i[m] = __builtin_amdgcn_perm(c[2 * m + 1], c[2 * m], 0x07060302u);
+  }
+  re = __builtin_bit_cast(bf16x8, r);
+  im = __builtin_bit_cast(bf16x8, i);
+}
+// element t (compile-time) of each of 8 vectors of 8 bf16 -> one operand
+template <int TT>
+__device__ __forceinline__ bf16x8 column8(const u32x4 (&V)[8]) {
+  constexpr uint32_t sel = (TT & 1) ? 0x07060302u : 0x05040100u;
+  u32x4 r;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) r[m] = __builtin_amdgcn_perm(V[2 * m + 1][TT >> 1], V[2 * m][TT >> 1], sel);
+  return __builtin_bit_cast(bf16x8, r);
+}
+template <int TT>
+__device__ __forceinline__ float elem_f32(const u32x4& g) {
+  return (TT & 1) ? hi_f32(g[TT >> 1]) : lo_f32(g[TT >> 1]);
 }
 
+// LDS: one plane of complex bf16 words, 16 slabs (k1 or n1) x 32 rows x ROW.
+// Pass 1 / pass 1' column mapping: wave w, lane j (= lane % 32), tile t handle column c = 256 w + 8 j + t
+// (n3 = c % 32, n2 = c / 32), so each lane's 8 tiles cover 8 consecutive samples: one 16-byte access per
+// (row, n1) in global memory.
 template <bool GATE>
 __global__ void __launch_bounds__(mf::T, 2)
 k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __restrict__ Hc,
             const bf16x8* __restrict__ mats, int B, int D, Twiddles tw) {
   using namespace mf;
-  __shared__ __bf16 lre[PLANE];
-  __shared__ __bf16 lim[PLANE];
+  __shared__ uint32_t S[PLANE];
   const int t = threadIdx.x, w = t >> 6, l = t & 63, j = l & 31, h = l >> 5;
   const int npair = B >> 1;
   const int r = xcd_logical_block(blockIdx.x, D * npair);
   const int d = r / npair, p = r % npair;
   const size_t row0 = (size_t)(2 * p) * D + d, row1 = (size_t)(2 * p + 1) * D + d;
+  const int c0 = 256 * w + 8 * j;
+  const int n2c = 8 * w + (j >> 2), n3c = 8 * (j & 3);   // tile t: n2 = n2c, n3 = n3c + t
+
+  // ---------------- pass 1 loads: lanes h = 0 / 1 carry row b0 / b1 (real / imaginary input), n1 = e
+  u32x4 V[8];
+  {
+    const __bf16* src = (h == 0 ? u + row0 * L : u + row1 * L) + c0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) V[e] = *reinterpret_cast<const u32x4*>(src + 1024 * e);
+  }
+  const bf16x8 m1f = mats[M1F * 64 + l];
+  // twiddle W_N^{c k1}, k1 = row of accumulator e: W_N^{c0 k1} advanced by W_N^{k1} per tile
+  float2 cur[8], stp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t k1 = acc_row(e, h);
+    cur[e] = twiddle<14>(tw, uint32_t(c0) * k1);
+    stp[e] = twiddle<14>(tw, k1);
+  }
+  static_for<8>([&](auto tt) {
+    constexpr int TT = tt.value;
+    const f32x16 z = {};
+    const f32x16 D1 = mfma(m1f, column8<TT>(V), z);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k1 = acc_row(e, h);
+      const float2 v = cmul(make_float2(D1[e], D1[8 + e]), cur[e]);
+      S[k1 * SLAB + n2c * ROW + n3c + TT] = pack2(v.x, v.y);
+      if (TT < 7) cur[e] = cmul(cur[e], stp[e]);
+    }
+  });
 
   bf16x8 A[NMAT];
 #pragma unroll
-  for (int q = 0; q < NMAT; ++q) A[q] = mats[q * 64 + l];
-
-  // per-lane twiddles: p1[e] = W_N^{j k1(e)}, k1(e) = row of accumulator e (e < 8);
-  //                    p2[v] = W_1024^{j k(v)},  k(v) = row of accumulator v
-  float2 p1[8], p2[16];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) p1[e] = twiddle<14>(tw, uint32_t(j * acc_row(e, h)));
+  for (int q = C_LO; q <= SP_HI; ++q) A[q] = mats[q * 64 + l];
+  // per-lane W_1024^{j k(v)}, k(v) = row of accumulator v
+  float2 p2[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) p2[v] = twiddle<10>(tw, uint32_t(j * acc_row(v, h)));
-
-  // ---------------- pass 1: tiles n2 (8 per wave), columns n3 = j; lanes h = 0 / 1 carry row b0 / b1
-  {
-    const __bf16* src = (h == 0 ? u + row0 * L : u + row1 * L) + j;
-    for (int it = 0; it < 8; ++it) {
-      const int n2 = w * 8 + it;
-      bf16x8 b;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = src[32 * n2 + 1024 * e];
-      f32x16 z = {};
-      const f32x16 D1 = mfma(A[M1F], b, z);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k1 = acc_row(e, h);
-        const float2 q = twiddle<9>(tw, uint32_t(n2 * k1));     // W_512^{n2 k1}, same across the half-wave
-        const float2 tw1 = cmul(p1[e], q);
-        const float2 v = cmul(make_float2(D1[e], D1[8 + e]), tw1);
-        const int a = (k1 * 32 + n2) * ROW + j;
-        lre[a] = tobf(v.x);
-        lim[a] = tobf(v.y);
-      }
-    }
-  }
   __syncthreads();
 
   // ---------------- passes 2, 3, 3', 2' per slab k1 (wave w owns k1 = w, w+4, w+8, w+12)
   for (int it = 0; it < 4; ++it) {
     const int k1 = w + 4 * it;
-    __bf16* sre = lre + k1 * SLAB;
-    __bf16* sim = lim + k1 * SLAB;
+    uint32_t* sl = S + k1 * SLAB;
+    // loads for this slab, consumed after passes 2 and 3
+    uint32_t hw[16];
+    {
+      const uint32_t* hp = Hc + ((size_t)d * 16 + k1) * 16 * 64 + l;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) hw[v] = hp[v * 64];
+    }
+    const float2 a1 = twiddle<14>(tw, uint32_t(j * k1));   // W_N^{j k1}
+    const float2 g1 = twiddle<9>(tw, uint32_t(k1));        // W_512^{k1}
+    uint32_t clo[8], chi[8];
+    bf16x8 xr_lo, xr_hi, xi_lo, xi_hi;
     // pass 2: columns n3 = j, K = n2: element (n2, n3) at n2 * ROW + n3
     {
-      const bf16x8 xr_lo = lds8<ROW>(sre + (8 * h) * ROW + j), xr_hi = lds8<ROW>(sre + (16 + 8 * h) * ROW + j);
-      const bf16x8 xi_lo = lds8<ROW>(sim + (8 * h) * ROW + j), xi_hi = lds8<ROW>(sim + (16 + 8 * h) * ROW + j);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        clo[e] = sl[(8 * h + e) * ROW + j];
+        chi[e] = sl[(16 + 8 * h + e) * ROW + j];
+      }
+      split8(clo, xr_lo, xi_lo);
+      split8(chi, xr_hi, xi_hi);
       f32x16 dr, di;
       dft32<false>(A, C_LO, C_HI, S_LO, S_HI, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
       // twiddle W_1024^{n3 k2} (n3 = j, k2 = row of v), store (k2, n3) at k2 * ROW + n3
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float2 o = cmul(make_float2(dr[v], di[v]), p2[v]);
-        const int a = acc_row(v, h) * ROW + j;
-        sre[a] = tobf(o.x);
-        sim[a] = tobf(o.y);
+        sl[acc_row(v, h) * ROW + j] = pack2(o.x, o.y);
       }
     }
     // pass 3: columns k2 = j, K = n3: element (k2, n3) at k2 * ROW + n3
     f32x16 dr, di;
     {
-      const bf16x8 xr_lo = lds8<1>(sre + j * ROW + 8 * h), xr_hi = lds8<1>(sre + j * ROW + 16 + 8 * h);
-      const bf16x8 xi_lo = lds8<1>(sim + j * ROW + 8 * h), xi_hi = lds8<1>(sim + j * ROW + 16 + 8 * h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        clo[e] = sl[j * ROW + 8 * h + e];
+        chi[e] = sl[j * ROW + 16 + 8 * h + e];
+      }
+      split8(clo, xr_lo, xi_lo);
+      split8(chi, xr_hi, xi_hi);
       dft32<false>(A, C_LO, C_HI, S_LO, S_HI, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
     }
     // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N in this exact order
-    {
-      const uint32_t* hp = Hc + ((size_t)d * 16 + k1) * 16 * 64 + l;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t hw = hp[v * 64];
-        const float2 hv = make_float2(__uint_as_float(hw << 16), __uint_as_float(hw & 0xffff0000u));
-        const float2 o = cmul(make_float2(dr[v], di[v]), hv);
-        dr[v] = o.x;
-        di[v] = o.y;
-      }
-    }
     // pass 3': inverse over k3 from the accumulators (register v is input K' = v of the permuted matrix)
     {
-      bf16x8 yr_lo, yr_hi, yi_lo, yi_hi;
+      u32x4 rlo, rhi, ilo, ihi;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        yr_lo[e] = tobf(dr[e]); yr_hi[e] = tobf(dr[8 + e]);
-        yi_lo[e] = tobf(di[e]); yi_hi[e] = tobf(di[8 + e]);
+      for (int m = 0; m < 4; ++m) {
+        const float2 a0 = cmul(make_float2(dr[2 * m], di[2 * m]), unpack_c(hw[2 * m]));
+        const float2 a1v = cmul(make_float2(dr[2 * m + 1], di[2 * m + 1]), unpack_c(hw[2 * m + 1]));
+        const float2 b0 = cmul(make_float2(dr[8 + 2 * m], di[8 + 2 * m]), unpack_c(hw[8 + 2 * m]));
+        const float2 b1 = cmul(make_float2(dr[9 + 2 * m], di[9 + 2 * m]), unpack_c(hw[9 + 2 * m]));
+        rlo[m] = pack2(a0.x, a1v.x);
+        ilo[m] = pack2(a0.y, a1v.y);
+        rhi[m] = pack2(b0.x, b1.x);
+        ihi[m] = pack2(b0.y, b1.y);
       }
       f32x16 er, ei;
-      dft32<true>(A, CP_LO, CP_HI, SP_LO, SP_HI, yr_lo, yr_hi, yi_lo, yi_hi, er, ei);
+      dft32<true>(A, CP_LO, CP_HI, SP_LO, SP_HI, __builtin_bit_cast(bf16x8, rlo), __builtin_bit_cast(bf16x8, rhi),
+                  __builtin_bit_cast(bf16x8, ilo), __builtin_bit_cast(bf16x8, ihi), er, ei);
       // conj twiddle W_1024^{n3 k2} (k2 = j, n3 = row of v), store (n3, k2) at n3 * ROW + k2
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const float2 o = cmulc(make_float2(er[v], ei[v]), p2[v]);
-        const int a = acc_row(v, h) * ROW + j;
-        sre[a] = tobf(o.x);
-        sim[a] = tobf(o.y);
+        sl[acc_row(v, h) * ROW + j] = pack2(o.x, o.y);
       }
     }
     // pass 2': inverse over k2, columns n3 = j: element (n3, k2) at n3 * ROW + k2
     {
-      const bf16x8 xr_lo = lds8<1>(sre + j * ROW + 8 * h), xr_hi = lds8<1>(sre + j * ROW + 16 + 8 * h);
-      const bf16x8 xi_lo = lds8<1>(sim + j * ROW + 8 * h), xi_hi = lds8<1>(sim + j * ROW + 16 + 8 * h);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        clo[e] = sl[j * ROW + 8 * h + e];
+        chi[e] = sl[j * ROW + 16 + 8 * h + e];
+      }
+      split8(clo, xr_lo, xi_lo);
+      split8(chi, xr_hi, xi_hi);
       f32x16 er, ei;
       dft32<true>(A, C_LO, C_HI, S_LO, S_HI, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
-      // conj twiddle W_N^{(n3 + 32 n2) k1} = conj(W_N^{n3 k1} W_512^{n2 k1}); store (n2, n3) at n2 * ROW + n3
-      const float2 a1 = twiddle<14>(tw, uint32_t(j * k1));
+      // conj twiddle W_N^{(n3 + 32 n2) k1} = conj(a1 g^{n2}), g = W_512^{k1},
+      // n2 = 8 (v >> 2) + 4 h + (v & 3); store (n2, n3) at n2 * ROW + n3
+      const float2 g2 = cmul(g1, g1), g3 = cmul(g2, g1), g4 = cmul(g2, g2), g8 = cmul(g4, g4);
+      float2 bq = h ? cmul(a1, g4) : a1;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int n2 = acc_row(v, h);
-        const float2 b1 = twiddle<9>(tw, uint32_t(n2 * k1));
-        const float2 o = cmulc(make_float2(er[v], ei[v]), cmul(a1, b1));
-        const int a = n2 * ROW + j;
-        sre[a] = tobf(o.x);
-        sim[a] = tobf(o.y);
+      for (int q = 0; q < 4; ++q) {
+        if (q) bq = cmul(bq, g8);
+        const float2 tq[4] = {bq, cmul(bq, g1), cmul(bq, g2), cmul(bq, g3)};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+          const int v = 4 * q + s2;
+          const float2 o = cmulc(make_float2(er[v], ei[v]), tq[s2]);
+          sl[acc_row(v, h) * ROW + j] = pack2(o.x, o.y);
+        }
       }
     }
   }
+
+  // gate for pass 1': lane keeps rows b0 / b1 at n1 = 4h + e (e < 4), 8 consecutive samples each
+  u32x4 G[2][4];
+  if (GATE) {
+    const __bf16* g0 = gate + row0 * L + c0;
+    const __bf16* g1p = gate + row1 * L + c0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      G[0][e] = *reinterpret_cast<const u32x4*>(g0 + 1024 * (4 * h + e));
+      G[1][e] = *reinterpret_cast<const u32x4*>(g1p + 1024 * (4 * h + e));
+    }
+  }
+  const bf16x8 m1r = mats[M1I_R * 64 + l], m1i = mats[M1I_I * 64 + l];
   __syncthreads();
 
-  // ---------------- pass 1': tiles n2 (8 per wave), columns n3 = j, K = k1 (slab index)
+  // ---------------- pass 1': tiles t, column c = c0 + t, K = k1 (slab index), outputs n1 = 4h + e
   {
-    const size_t base0 = row0 * L, base1 = row1 * L;
-    for (int it = 0; it < 8; ++it) {
-      const int n2 = w * 8 + it;
-      const bf16x8 xr = lds8<SLAB>(lre + (8 * h) * SLAB + n2 * ROW + j);
-      const bf16x8 xi = lds8<SLAB>(lim + (8 * h) * SLAB + n2 * ROW + j);
-      f32x16 z = {};
-      f32x16 o = mfma(A[M1I_R], xr, z);
-      o = mfma(A[M1I_I], xi, o);
-      // rows 4h + e (e < 4) are n1 = 4h + e (< 8): real part in o[e], imaginary part in o[8 + e]
+    u32x4 Y[2][4];
+    float pa[4], pb[4];
+    static_for<8>([&](auto tt) {
+      constexpr int TT = tt.value;
+      uint32_t cw[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cw[e] = S[(8 * h + e) * SLAB + n2c * ROW + n3c + TT];
+      bf16x8 xr, xi;
+      split8(cw, xr, xi);
+      const f32x16 z = {};
+      f32x16 o = mfma(m1r, xr, z);
+      o = mfma(m1i, xi, o);
+      // rows 4h + e (e < 4): real part (row b0) in o[e], imaginary part (row b1) in o[8 + e]
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int n = j + 32 * n2 + 1024 * (4 * h + e);
         float a = o[e], b = o[8 + e];
         if (GATE) {
-          a *= (float)gate[base0 + n];
-          b *= (float)gate[base1 + n];
+          a *= elem_f32<TT>(G[0][e]);
+          b *= elem_f32<TT>(G[1][e]);
         }
-        y[base0 + n] = tobf(a);
-        y[base1 + n] = tobf(b);
+        if constexpr (TT % 2 == 0) {
+          pa[e] = a;
+          pb[e] = b;
+        } else {
+          Y[0][e][TT >> 1] = pack2(pa[e], a);
+          Y[1][e][TT >> 1] = pack2(pb[e], b);
+        }
       }
+    });
+    __bf16* y0 = y + row0 * L + c0;
+    __bf16* y1 = y + row1 * L + c0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      *reinterpret_cast<u32x4*>(y0 + 1024 * (4 * h + e)) = Y[0][e];
+      *reinterpret_cast<u32x4*>(y1 + 1024 * (4 * h + e)) = Y[1][e];
     }
   }
 }

@@ -220,3 +220,27 @@ def test_matrix_core_path_bf16_L8192(torch_cuda, B):
     e2 = rel_err_rows(got3, ref)
     say(f"  odd-B (fp32 engine) max rel err {e2.max():.3e}")
     assert e2.max() < BF16_TOL
+
+
+def test_matrix_core_path_misaligned_falls_back(torch_cuda):
+    """Activations that are not 16-byte aligned take the fp32-arithmetic engine; results agree with
+    the aligned (matrix-core) call to the bf16 tolerance."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[1].with_(B=2, D=3, dims=(8192,))
+    v, xs = hi.draw_activations(w, seed=5)
+    params = hi.draw_filter_params(w, seed=5)
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
+    vd = to_dev(v, torch.bfloat16)
+    xd = [to_dev(x, torch.bfloat16) for x in xs]
+    ya = hy.operator(vd, xd, spectra)
+    n = v.size
+    buf = torch.empty(n + 1, dtype=torch.bfloat16, device="cuda")
+    vm = buf[1:].view(v.shape)
+    vm.copy_(vd)
+    assert vm.data_ptr() % 16 != 0
+    ym = hy.operator(vm, xd, spectra)
+    torch.cuda.synchronize()
+    e = rel_err_rows(ym.float().cpu().numpy().reshape(-1, 8192), ya.float().cpu().numpy().reshape(-1, 8192))
+    say(f"misaligned vs aligned max rel diff {e.max():.3e}")
+    assert e.max() < BF16_TOL
