@@ -9,23 +9,25 @@
 //
 // Two rows b0, b1 of one channel (same filter) are transformed together as z = u_b0 + i u_b1:
 // since h is real, IDFT(DFT(z) H) = (h * u_b0) + i (h * u_b1), so no real-input split is needed.
-// N = 2L = 16384 = 16 x 32 x 32, n = n3 + 32 n2 + 1024 n1 (n1 < 8 nonzero), k = k1 + 16 k2 + 512 k3.
-//   pass 1  DFT over n1 (radix 16, half the inputs zero), twiddle W_N^{(n3 + 32 n2) k1}
-//   pass 2  DFT over n2 (radix 32), twiddle W_1024^{n3 k2}
-//   pass 3  DFT over n3 (radix 32) -> Z[k]; times H[k]/N (bf16 spectrum in consumption order)
-//   pass 3' inverse DFT over k3 straight from the accumulators (the matrix's input order is the
+// N = 2L = 16384 = 16 x 32 x 32, n = n3 + 32 n2 + 1024 n1 (n1 < 8 nonzero), k = k1 + 16 k2 + 512 k3, and
+//   W_N^{nk} = W_16^{n1 k1} . W_512^{n2 (16 k2 + k1)} . W_1024^{n3 k2} . W_N^{n3 (512 k3 + k1)}.
+//   pass 1  DFT over n1 (radix 16, half the inputs zero) -> slab k1
+//   pass 2  over n2 with the slab's matrix W_512^{n2 (16 k2 + k1)}, then twiddle W_1024^{n3 k2}
+//   pass 3  over n3 with the slab's matrix W_N^{n3 (512 k3 + k1)} -> Z[k]; times H[k]/N
+//   pass 3' inverse of pass 3 straight from the accumulators (the matrix's input order is the
 //           accumulator row order), conj twiddle W_1024^{n3 k2}
-//   pass 2' inverse DFT over k2, conj twiddle W_N^{(n3 + 32 n2) k1}
+//   pass 2' inverse of pass 2
 //   pass 1' inverse DFT over k1, keep n1 < 8 (the causal half); gate; store
+// Every factor that depends on the slab k1 and on one of a pass's own indices lives in that pass's
+// matrix (16 slabs x 4 matrices, a 256 KB table that stays in L2), so the only elementwise twiddle
+// left is W_1024^{n3 k2}, whose two indices are the row and the column of one product.
 // A complex radix-R DFT is a real 2R x 2R matrix on (Re, Im); each MFMA (32x32x16) multiplies a 32-row
-// block of it by 32 columns (independent sub-transforms).  Every lane keeps the radix-32 matrices it
-// needs (32 VGPRs).  LDS holds one plane of complex bf16 words (re low, im high); rows hold 32 words plus
-// one pad, so lanes reading one word each from 32 consecutive rows, or 32 consecutive words of one
-// row, hit distinct banks.  Passes 2, 3, 3' and 2' of tile k1 touch only slab k1, which one wave owns,
-// so only two barriers are needed.  Global memory is touched in 16-byte accesses only: pass 1 and
-// pass 1' give each lane 8 tiles whose columns are 8 consecutive samples.  Twiddles come from the
-// tables once per lane and are advanced by complex products (recurrence over tiles, short power
-// chains within a slab), so no table gather sits on the critical path.
+// block of it by 32 columns (independent sub-transforms).  LDS holds one plane of complex bf16 words
+// (re low, im high); rows hold 32 words plus one pad, so lanes reading one word each from 32
+// consecutive rows, or 32 consecutive words of one row, hit distinct banks.  Passes 2, 3, 3' and 2'
+// of slab k1 touch only that slab, which one wave owns, so only two barriers are needed.  Global
+// memory is touched in 16-byte accesses only: pass 1 and pass 1' give each lane 8 tiles whose columns
+// are 8 consecutive samples.
 #include <math.h>
 #include <string.h>
 
@@ -36,6 +38,7 @@ namespace hyena {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 namespace mf {
 constexpr int L = 8192, N = 2 * L;
@@ -43,44 +46,45 @@ constexpr int ROW = 33;                     // 32 values + 1 pad
 constexpr int SLAB = 32 * ROW;              // one k1 (or n1-free) slab
 constexpr int PLANE = 16 * SLAB;            // 16 slabs
 constexpr int T = 256;                      // 4 waves
-// DFT matrices, each stored per lane as 8 bf16 (A operand layout): index into the table
-enum { M1F = 0, C_LO, C_HI, S_LO, S_HI, CP_LO, CP_HI, SP_LO, SP_HI, M1I_R, M1I_I, NMAT };
+// Matrix table, per lane 8 bf16 in the A-operand layout (row i = lane % 32, K = 8 (lane / 32) + e).
+// Fixed radix-16 matrices first, then per slab k1 four radix-32 matrices of four blocks each.
+enum { M1F = 0, M1I_R, M1I_I, NFIX };
+enum { MF2 = 0, MF3, MI3, MI2, NSLABMAT };       // pass 2, pass 3, pass 3', pass 2'
+enum { B_CLO = 0, B_CHI, B_SLO, B_SHI, NBLK };   // cos / sin, K < 16 / K >= 16
+constexpr int SLAB_TABLE = NSLABMAT * NBLK;       // bf16x8 per lane per slab
 }  // namespace mf
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ bf16x8 neg8(bf16x8 v) {
-  bf16x8 r;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = -v[e];
-  return r;
+__device__ __forceinline__ bf16x8 neg8(bf16x8 v) {   // flip the 8 sign bits, one XOR per dword
+  u32x4 r = __builtin_bit_cast(u32x4, v);
+  r ^= 0x80008000u;
+  return __builtin_bit_cast(bf16x8, r);
 }
-__device__ __forceinline__ __bf16 tobf(float f) { return (__bf16)f; }
 
 // output row of accumulator register v for lane half h (32x32 MFMA layout)
 __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
-// radix-32 forward / inverse on B blocks (xr_lo, xr_hi, xi_lo, xi_hi); out dr, di
+// Complex radix-32 product with matrix blocks M (cos lo/hi, sin lo/hi) on B blocks (xr_lo, xr_hi, xi_lo,
+// xi_hi).  Forward (W = cos - i sin): Yr = C Xr + S Xi, Yi = C Xi - S Xr;
+// inverse (W = cos + i sin):           Yr = C Xr - S Xi, Yi = C Xi + S Xr.
 template <bool INV>
-__device__ __forceinline__ void dft32(const bf16x8 (&A)[mf::NMAT], int c_lo, int c_hi, int s_lo, int s_hi,
-                                      bf16x8 xr_lo, bf16x8 xr_hi, bf16x8 xi_lo, bf16x8 xi_hi, f32x16& dr,
-                                      f32x16& di) {
-  f32x16 z = {};
-  // forward: Yr = C Xr + S Xi, Yi = C Xi - S Xr;  inverse: Yr = C Xr - S Xi, Yi = C Xi + S Xr
+__device__ __forceinline__ void dft32(const bf16x8 (&M)[mf::NBLK], bf16x8 xr_lo, bf16x8 xr_hi, bf16x8 xi_lo,
+                                      bf16x8 xi_hi, f32x16& dr, f32x16& di) {
+  using namespace mf;
+  const f32x16 z = {};
   const bf16x8 sxi_lo = INV ? neg8(xi_lo) : xi_lo, sxi_hi = INV ? neg8(xi_hi) : xi_hi;
   const bf16x8 sxr_lo = INV ? xr_lo : neg8(xr_lo), sxr_hi = INV ? xr_hi : neg8(xr_hi);
-  dr = mfma(A[c_lo], xr_lo, z);
-  dr = mfma(A[c_hi], xr_hi, dr);
-  dr = mfma(A[s_lo], sxi_lo, dr);
-  dr = mfma(A[s_hi], sxi_hi, dr);
-  di = mfma(A[c_lo], xi_lo, z);
-  di = mfma(A[c_hi], xi_hi, di);
-  di = mfma(A[s_lo], sxr_lo, di);
-  di = mfma(A[s_hi], sxr_hi, di);
+  dr = mfma(M[B_CLO], xr_lo, z);
+  dr = mfma(M[B_CHI], xr_hi, dr);
+  dr = mfma(M[B_SLO], sxi_lo, dr);
+  dr = mfma(M[B_SHI], sxi_hi, dr);
+  di = mfma(M[B_CLO], xi_lo, z);
+  di = mfma(M[B_CHI], xi_hi, di);
+  di = mfma(M[B_SLO], sxr_lo, di);
+  di = mfma(M[B_SHI], sxr_hi, di);
 }
-
-typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
 // two floats -> one dword of bf16 (round to nearest even), a in the low half
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -116,8 +120,11 @@ template <int TT>
 __device__ __forceinline__ float elem_f32(const u32x4& g) {
   return (TT & 1) ? hi_f32(g[TT >> 1]) : lo_f32(g[TT >> 1]);
 }
+__device__ __forceinline__ void load_blocks(const bf16x8* p, bf16x8 (&M)[mf::NBLK]) {
+#pragma unroll
+  for (int b = 0; b < mf::NBLK; ++b) M[b] = p[b * 64];
+}
 
-// LDS: one plane of complex bf16 words, 16 slabs (k1 or n1) x 32 rows x ROW.
 // Pass 1 / pass 1' column mapping: wave w, lane j (= lane % 32), tile t handle column c = 256 w + 8 j + t
 // (n3 = c % 32, n2 = c / 32), so each lane's 8 tiles cover 8 consecutive samples: one 16-byte access per
 // (row, n1) in global memory.
@@ -134,6 +141,7 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
   const size_t row0 = (size_t)(2 * p) * D + d, row1 = (size_t)(2 * p + 1) * D + d;
   const int c0 = 256 * w + 8 * j;
   const int n2c = 8 * w + (j >> 2), n3c = 8 * (j & 3);   // tile t: n2 = n2c, n3 = n3c + t
+  const bf16x8* slab_mats = mats + NFIX * 64 + l;
 
   // ---------------- pass 1 loads: lanes h = 0 / 1 carry row b0 / b1 (real / imaginary input), n1 = e
   u32x4 V[8];
@@ -142,50 +150,54 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
 #pragma unroll
     for (int e = 0; e < 8; ++e) V[e] = *reinterpret_cast<const u32x4*>(src + 1024 * e);
   }
-  const bf16x8 m1f = mats[M1F * 64 + l];
-  // twiddle W_N^{c k1}, k1 = row of accumulator e: W_N^{c0 k1} advanced by W_N^{k1} per tile
-  float2 cur[8], stp[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t k1 = acc_row(e, h);
-    cur[e] = twiddle<14>(tw, uint32_t(c0) * k1);
-    stp[e] = twiddle<14>(tw, k1);
-  }
-  static_for<8>([&](auto tt) {
-    constexpr int TT = tt.value;
-    const f32x16 z = {};
-    const f32x16 D1 = mfma(m1f, column8<TT>(V), z);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k1 = acc_row(e, h);
-      const float2 v = cmul(make_float2(D1[e], D1[8 + e]), cur[e]);
-      S[k1 * SLAB + n2c * ROW + n3c + TT] = pack2(v.x, v.y);
-      if (TT < 7) cur[e] = cmul(cur[e], stp[e]);
-    }
-  });
-
-  bf16x8 A[NMAT];
-#pragma unroll
-  for (int q = C_LO; q <= SP_HI; ++q) A[q] = mats[q * 64 + l];
   // per-lane W_1024^{j k(v)}, k(v) = row of accumulator v
   float2 p2[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) p2[v] = twiddle<10>(tw, uint32_t(j * acc_row(v, h)));
+  {
+    const bf16x8 m1f = mats[M1F * 64 + l];
+    static_for<8>([&](auto tt) {
+      constexpr int TT = tt.value;
+      const f32x16 z = {};
+      const f32x16 D1 = mfma(m1f, column8<TT>(V), z);
+      // rows k1 = acc_row(e, h): real part in D1[e], imaginary part in D1[8 + e]
+#pragma unroll
+      for (int e = 0; e < 8; ++e) S[acc_row(e, h) * SLAB + n2c * ROW + n3c + TT] = pack2(D1[e], D1[8 + e]);
+    });
+  }
   __syncthreads();
 
+  // gate for pass 1', in flight during the middle passes: lane keeps rows b0 / b1 at n1 = 4h + e (e < 4),
+  // 8 consecutive samples each
+  u32x4 G[2][4];
+  if (GATE) {
+    const __bf16* g0 = gate + row0 * L + c0;
+    const __bf16* g1p = gate + row1 * L + c0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      G[0][e] = *reinterpret_cast<const u32x4*>(g0 + 1024 * (4 * h + e));
+      G[1][e] = *reinterpret_cast<const u32x4*>(g1p + 1024 * (4 * h + e));
+    }
+  }
+
   // ---------------- passes 2, 3, 3', 2' per slab k1 (wave w owns k1 = w, w+4, w+8, w+12)
+  // Slab matrices rotate through two buffers, each load issued one pass before its use:
+  // Ma = pass 2, Mb = pass 3, then Ma = pass 3', Mb = pass 2', then the next slab's pass 2 and 3.
+  bf16x8 Ma[NBLK], Mb[NBLK];
+  load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF2 * NBLK * 64, Ma);
+  load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF3 * NBLK * 64, Mb);
   for (int it = 0; it < 4; ++it) {
     const int k1 = w + 4 * it;
     uint32_t* sl = S + k1 * SLAB;
-    // loads for this slab, consumed after passes 2 and 3
+    const bf16x8* ms = slab_mats + (size_t)k1 * SLAB_TABLE * 64;
+    const bf16x8* ms_next = slab_mats + (size_t)(it < 3 ? k1 + 4 : k1) * SLAB_TABLE * 64;
+    // filter spectrum of this slab, consumed after passes 2 and 3
     uint32_t hw[16];
     {
       const uint32_t* hp = Hc + ((size_t)d * 16 + k1) * 16 * 64 + l;
 #pragma unroll
       for (int v = 0; v < 16; ++v) hw[v] = hp[v * 64];
     }
-    const float2 a1 = twiddle<14>(tw, uint32_t(j * k1));   // W_N^{j k1}
-    const float2 g1 = twiddle<9>(tw, uint32_t(k1));        // W_512^{k1}
     uint32_t clo[8], chi[8];
     bf16x8 xr_lo, xr_hi, xi_lo, xi_hi;
     // pass 2: columns n3 = j, K = n2: element (n2, n3) at n2 * ROW + n3
@@ -198,7 +210,8 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
       split8(clo, xr_lo, xi_lo);
       split8(chi, xr_hi, xi_hi);
       f32x16 dr, di;
-      dft32<false>(A, C_LO, C_HI, S_LO, S_HI, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
+      dft32<false>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
+      load_blocks(ms + MI3 * NBLK * 64, Ma);
       // twiddle W_1024^{n3 k2} (n3 = j, k2 = row of v), store (k2, n3) at k2 * ROW + n3
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -216,26 +229,28 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
       }
       split8(clo, xr_lo, xi_lo);
       split8(chi, xr_hi, xi_hi);
-      dft32<false>(A, C_LO, C_HI, S_LO, S_HI, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
+      dft32<false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
+      load_blocks(ms + MI2 * NBLK * 64, Mb);
     }
-    // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N in this exact order
+    // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N in this exact order.
     // pass 3': inverse over k3 from the accumulators (register v is input K' = v of the permuted matrix)
     {
       u32x4 rlo, rhi, ilo, ihi;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const float2 a0 = cmul(make_float2(dr[2 * m], di[2 * m]), unpack_c(hw[2 * m]));
-        const float2 a1v = cmul(make_float2(dr[2 * m + 1], di[2 * m + 1]), unpack_c(hw[2 * m + 1]));
+        const float2 a1 = cmul(make_float2(dr[2 * m + 1], di[2 * m + 1]), unpack_c(hw[2 * m + 1]));
         const float2 b0 = cmul(make_float2(dr[8 + 2 * m], di[8 + 2 * m]), unpack_c(hw[8 + 2 * m]));
         const float2 b1 = cmul(make_float2(dr[9 + 2 * m], di[9 + 2 * m]), unpack_c(hw[9 + 2 * m]));
-        rlo[m] = pack2(a0.x, a1v.x);
-        ilo[m] = pack2(a0.y, a1v.y);
+        rlo[m] = pack2(a0.x, a1.x);
+        ilo[m] = pack2(a0.y, a1.y);
         rhi[m] = pack2(b0.x, b1.x);
         ihi[m] = pack2(b0.y, b1.y);
       }
       f32x16 er, ei;
-      dft32<true>(A, CP_LO, CP_HI, SP_LO, SP_HI, __builtin_bit_cast(bf16x8, rlo), __builtin_bit_cast(bf16x8, rhi),
+      dft32<true>(Ma, __builtin_bit_cast(bf16x8, rlo), __builtin_bit_cast(bf16x8, rhi),
                   __builtin_bit_cast(bf16x8, ilo), __builtin_bit_cast(bf16x8, ihi), er, ei);
+      if (it < 3) load_blocks(ms_next + MF2 * NBLK * 64, Ma);
       // conj twiddle W_1024^{n3 k2} (k2 = j, n3 = row of v), store (n3, k2) at n3 * ROW + k2
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
@@ -243,7 +258,7 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
         sl[acc_row(v, h) * ROW + j] = pack2(o.x, o.y);
       }
     }
-    // pass 2': inverse over k2, columns n3 = j: element (n3, k2) at n3 * ROW + k2
+    // pass 2': inverse over k2, columns n3 = j: element (n3, k2) at n3 * ROW + k2; out (n2, n3)
     {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -253,36 +268,13 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
       split8(clo, xr_lo, xi_lo);
       split8(chi, xr_hi, xi_hi);
       f32x16 er, ei;
-      dft32<true>(A, C_LO, C_HI, S_LO, S_HI, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
-      // conj twiddle W_N^{(n3 + 32 n2) k1} = conj(a1 g^{n2}), g = W_512^{k1},
-      // n2 = 8 (v >> 2) + 4 h + (v & 3); store (n2, n3) at n2 * ROW + n3
-      const float2 g2 = cmul(g1, g1), g3 = cmul(g2, g1), g4 = cmul(g2, g2), g8 = cmul(g4, g4);
-      float2 bq = h ? cmul(a1, g4) : a1;
+      dft32<true>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
+      if (it < 3) load_blocks(ms_next + MF3 * NBLK * 64, Mb);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if (q) bq = cmul(bq, g8);
-        const float2 tq[4] = {bq, cmul(bq, g1), cmul(bq, g2), cmul(bq, g3)};
-#pragma unroll
-        for (int s2 = 0; s2 < 4; ++s2) {
-          const int v = 4 * q + s2;
-          const float2 o = cmulc(make_float2(er[v], ei[v]), tq[s2]);
-          sl[acc_row(v, h) * ROW + j] = pack2(o.x, o.y);
-        }
-      }
+      for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2(er[v], ei[v]);
     }
   }
 
-  // gate for pass 1': lane keeps rows b0 / b1 at n1 = 4h + e (e < 4), 8 consecutive samples each
-  u32x4 G[2][4];
-  if (GATE) {
-    const __bf16* g0 = gate + row0 * L + c0;
-    const __bf16* g1p = gate + row1 * L + c0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      G[0][e] = *reinterpret_cast<const u32x4*>(g0 + 1024 * (4 * h + e));
-      G[1][e] = *reinterpret_cast<const u32x4*>(g1p + 1024 * (4 * h + e));
-    }
-  }
   const bf16x8 m1r = mats[M1I_R * 64 + l], m1i = mats[M1I_I * 64 + l];
   __syncthreads();
 
@@ -345,54 +337,75 @@ __global__ void k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __res
 }
 
 // ------------------------------------------------------------------ host side
-// DFT matrices per lane in the MFMA A-operand layout (row i = lane % 32, K = 8 (lane / 32) + e).
-static float host_mat(int q, int i, int K) {
-  const double tp = 2.0 * 3.14159265358979323846;
-  auto c = [&](int a, int b, int n) { return cos(tp * (double)((a * b) % n) / n); };
-  auto s = [&](int a, int b, int n) { return sin(tp * (double)((a * b) % n) / n); };
-  auto perm = [](int Kp) {   // permuted input order of the pass-3' matrix: K' -> k3
-    const int hh = (Kp >> 3) & 1, e = Kp & 7, hi = Kp >> 4;
-    return 16 * hi + (e < 4 ? 4 * hh + e : 8 + 4 * hh + e - 4);
-  };
+namespace {
+constexpr double kTwoPi = 2.0 * 3.14159265358979323846;
+
+// input order of the pass-3' matrix: K' (accumulator register order of pass 3) -> k3
+int perm_k3(int Kp) {
+  const int hh = (Kp >> 3) & 1, e = Kp & 7, hi = Kp >> 4;
+  return 16 * hi + (e < 4 ? 4 * hh + e : 8 + 4 * hh + e - 4);
+}
+
+// Radix-16 matrices, entry (row i, input K).
+float fixed_entry(int q, int i, int K) {
+  auto c = [](int a, int b) { return cos(kTwoPi * (double)((a * b) % 16) / 16); };
+  auto s = [](int a, int b) { return sin(kTwoPi * (double)((a * b) % 16) / 16); };
   switch (q) {
-    case mf::M1F: {   // radix 16, inputs m < 8: rows (Yr k | Yi k), cols (Xr m | Xi m)
+    case mf::M1F: {   // forward, inputs m < 8: rows (Yr k | Yi k), cols (Xr m | Xi m)
       const int k = i & 15, m = K & 7;
       const bool yi = i >= 16, xi = K >= 8;
-      if (!yi) return (float)(xi ? s(k, m, 16) : c(k, m, 16));
-      return (float)(xi ? c(k, m, 16) : -s(k, m, 16));
+      if (!yi) return (float)(xi ? s(k, m) : c(k, m));
+      return (float)(xi ? c(k, m) : -s(k, m));
     }
-    case mf::C_LO: return (float)c(i, K, 32);
-    case mf::C_HI: return (float)c(i, K + 16, 32);
-    case mf::S_LO: return (float)s(i, K, 32);
-    case mf::S_HI: return (float)s(i, K + 16, 32);
-    case mf::CP_LO: return (float)c(i, perm(K), 32);
-    case mf::CP_HI: return (float)c(i, perm(K + 16), 32);
-    case mf::SP_LO: return (float)s(i, perm(K), 32);
-    case mf::SP_HI: return (float)s(i, perm(K + 16), 32);
-    case mf::M1I_R: {  // inverse radix 16, Xr block: Yr = c, Yi = s
+    case mf::M1I_R: {  // inverse, Xr block: Yr = c, Yi = s
       const int n = i & 15;
-      return (float)(i < 16 ? c(n, K, 16) : s(n, K, 16));
+      return (float)(i < 16 ? c(n, K) : s(n, K));
     }
-    case mf::M1I_I: {  // Xi block: Yr = -s, Yi = c
+    case mf::M1I_I: {  // inverse, Xi block: Yr = -s, Yi = c
       const int n = i & 15;
-      return (float)(i < 16 ? -s(n, K, 16) : c(n, K, 16));
+      return (float)(i < 16 ? -s(n, K) : c(n, K));
     }
   }
   return 0.f;
 }
 
-void mfma_matrices_host(uint16_t* out) {   // [NMAT][64 lanes][8]
-  for (int q = 0; q < mf::NMAT; ++q)
-    for (int l = 0; l < 64; ++l)
-      for (int e = 0; e < 8; ++e) {
-        const float f = host_mat(q, l % 32, 8 * (l / 32) + e);
-        uint32_t u;
-        memcpy(&u, &f, 4);
-        u += 0x7fffu + ((u >> 16) & 1u);
-        out[(q * 64 + l) * 8 + e] = (uint16_t)(u >> 16);
-      }
+// Angle (in turns) of the radix-32 entry (row i, input k) of slab matrix m for slab k1.
+double slab_angle(int m, int k1, int i, int k) {
+  switch (m) {
+    case mf::MF2: return (double)((k * (16 * i + k1)) % 512) / 512;                 // row k2, input n2
+    case mf::MF3: return (double)((k * (512 * i + k1)) % mf::N) / mf::N;            // row k3, input n3
+    case mf::MI3: return (double)((i * (512 * perm_k3(k) + k1)) % mf::N) / mf::N;   // row n3, input k3
+    case mf::MI2: return (double)((i * (16 * k + k1)) % 512) / 512;                 // row n2, input k2
+  }
+  return 0.0;
 }
-size_t mfma_matrices_count() { return (size_t)mf::NMAT * 64 * 8; }
+
+uint16_t bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+}  // namespace
+
+size_t mfma_matrices_count() { return ((size_t)mf::NFIX + 16 * mf::SLAB_TABLE) * 64 * 8; }
+
+void mfma_matrices_host(uint16_t* out) {   // [NFIX][64][8] then [16 slabs][4 mats][4 blocks][64][8]
+  for (int q = 0; q < mf::NFIX; ++q)
+    for (int l = 0; l < 64; ++l)
+      for (int e = 0; e < 8; ++e) out[(q * 64 + l) * 8 + e] = bf16_rne(fixed_entry(q, l % 32, 8 * (l / 32) + e));
+  uint16_t* o = out + (size_t)mf::NFIX * 64 * 8;
+  for (int k1 = 0; k1 < 16; ++k1)
+    for (int m = 0; m < mf::NSLABMAT; ++m)
+      for (int b = 0; b < mf::NBLK; ++b)
+        for (int l = 0; l < 64; ++l)
+          for (int e = 0; e < 8; ++e) {
+            const int i = l % 32, k = 8 * (l / 32) + e + ((b == mf::B_CHI || b == mf::B_SHI) ? 16 : 0);
+            const double a = kTwoPi * slab_angle(m, k1, i, k);
+            const double val = (b == mf::B_CLO || b == mf::B_CHI) ? cos(a) : sin(a);
+            o[((((size_t)k1 * mf::NSLABMAT + m) * mf::NBLK + b) * 64 + l) * 8 + e] = bf16_rne((float)val);
+          }
+}
 
 bool mfma_pair_supported(int log2L, int B) { return log2L == 13 && B % 2 == 0; }
 size_t mfma_pair_spectrum_bytes_per_channel() { return (size_t)16 * 16 * 64 * 4; }
