@@ -66,24 +66,29 @@ __device__ __forceinline__ bf16x8 neg8(bf16x8 v) {   // flip the 8 sign bits, on
 // output row of accumulator register v for lane half h (32x32 MFMA layout)
 __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 
-// Complex radix-32 product with matrix blocks M (cos lo/hi, sin lo/hi) on B blocks (xr_lo, xr_hi, xi_lo,
+// Complex radix-32 product of matrix blocks M (cos lo/hi, sin lo/hi) and data blocks (xr_lo, xr_hi, xi_lo,
 // xi_hi).  Forward (W = cos - i sin): Yr = C Xr + S Xi, Yi = C Xi - S Xr;
 // inverse (W = cos + i sin):           Yr = C Xr - S Xi, Yi = C Xi + S Xr.
-template <bool INV>
+// A and B operands share one register layout (lane % 32 = row or column, K = 8 (lane / 32) + e), so the
+// same registers serve either side.  DATA_A = false: matrix on A, data columns on B -> output row = the
+// matrix row, lane = the data column.  DATA_A = true: data on A -> the transpose (lane = the matrix row,
+// registers = the data column), which puts the next contraction index in registers.
+template <bool INV, bool DATA_A>
 __device__ __forceinline__ void dft32(const bf16x8 (&M)[mf::NBLK], bf16x8 xr_lo, bf16x8 xr_hi, bf16x8 xi_lo,
                                       bf16x8 xi_hi, f32x16& dr, f32x16& di) {
   using namespace mf;
+  auto mm = [](bf16x8 m, bf16x8 x, f32x16 c) { return DATA_A ? mfma(x, m, c) : mfma(m, x, c); };
   const f32x16 z = {};
   const bf16x8 sxi_lo = INV ? neg8(xi_lo) : xi_lo, sxi_hi = INV ? neg8(xi_hi) : xi_hi;
   const bf16x8 sxr_lo = INV ? xr_lo : neg8(xr_lo), sxr_hi = INV ? xr_hi : neg8(xr_hi);
-  dr = mfma(M[B_CLO], xr_lo, z);
-  dr = mfma(M[B_CHI], xr_hi, dr);
-  dr = mfma(M[B_SLO], sxi_lo, dr);
-  dr = mfma(M[B_SHI], sxi_hi, dr);
-  di = mfma(M[B_CLO], xi_lo, z);
-  di = mfma(M[B_CHI], xi_hi, di);
-  di = mfma(M[B_SLO], sxr_lo, di);
-  di = mfma(M[B_SHI], sxr_hi, di);
+  dr = mm(M[B_CLO], xr_lo, z);
+  dr = mm(M[B_CHI], xr_hi, dr);
+  dr = mm(M[B_SLO], sxi_lo, dr);
+  dr = mm(M[B_SHI], sxi_hi, dr);
+  di = mm(M[B_CLO], xi_lo, z);
+  di = mm(M[B_CHI], xi_hi, di);
+  di = mm(M[B_SLO], sxr_lo, di);
+  di = mm(M[B_SHI], sxr_hi, di);
 }
 
 // two floats -> one dword of bf16 (round to nearest even), a in the low half
@@ -95,6 +100,29 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float2 unpack_c(uint32_t w) { return make_float2(lo_f32(w), hi_f32(w)); }
+
+// fp32 accumulators, each multiplied by a complex factor, -> bf16 operands in accumulator order
+// (block lo = registers 0..7, block hi = registers 8..15)
+template <class F>
+__device__ __forceinline__ void pack_operands(const f32x16& xr, const f32x16& xi, F&& factor, bf16x8& r_lo,
+                                              bf16x8& r_hi, bf16x8& i_lo, bf16x8& i_hi) {
+  u32x4 rl, rh, il, ih;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const float2 a0 = factor(2 * m, make_float2(xr[2 * m], xi[2 * m]));
+    const float2 a1 = factor(2 * m + 1, make_float2(xr[2 * m + 1], xi[2 * m + 1]));
+    const float2 b0 = factor(8 + 2 * m, make_float2(xr[8 + 2 * m], xi[8 + 2 * m]));
+    const float2 b1 = factor(9 + 2 * m, make_float2(xr[9 + 2 * m], xi[9 + 2 * m]));
+    rl[m] = pack2(a0.x, a1.x);
+    il[m] = pack2(a0.y, a1.y);
+    rh[m] = pack2(b0.x, b1.x);
+    ih[m] = pack2(b0.y, b1.y);
+  }
+  r_lo = __builtin_bit_cast(bf16x8, rl);
+  r_hi = __builtin_bit_cast(bf16x8, rh);
+  i_lo = __builtin_bit_cast(bf16x8, il);
+  i_hi = __builtin_bit_cast(bf16x8, ih);
+}
 
 // 8 complex bf16 words (re low, im high) -> the 8 real parts and the 8 imaginary parts as MFMA operands
 __device__ __forceinline__ void split8(const uint32_t (&c)[8], bf16x8& re, bf16x8& im) {
@@ -198,10 +226,12 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
 #pragma unroll
       for (int v = 0; v < 16; ++v) hw[v] = hp[v * 64];
     }
-    uint32_t clo[8], chi[8];
     bf16x8 xr_lo, xr_hi, xi_lo, xi_hi;
-    // pass 2: columns n3 = j, K = n2: element (n2, n3) at n2 * ROW + n3
+    f32x16 dr, di;
+    // pass 2: data on A (rows n3 = j, K = n2 from LDS: element (n2, n3) at n2 * ROW + n3), matrix on B
+    //   -> lane = k2, registers = n3 (row of v)
     {
+      uint32_t clo[8], chi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         clo[e] = sl[(8 * h + e) * ROW + j];
@@ -209,70 +239,28 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
       }
       split8(clo, xr_lo, xi_lo);
       split8(chi, xr_hi, xi_hi);
-      f32x16 dr, di;
-      dft32<false>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
+      dft32<false, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
       load_blocks(ms + MI3 * NBLK * 64, Ma);
-      // twiddle W_1024^{n3 k2} (n3 = j, k2 = row of v), store (k2, n3) at k2 * ROW + n3
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float2 o = cmul(make_float2(dr[v], di[v]), p2[v]);
-        sl[acc_row(v, h) * ROW + j] = pack2(o.x, o.y);
-      }
     }
-    // pass 3: columns k2 = j, K = n3: element (k2, n3) at k2 * ROW + n3
-    f32x16 dr, di;
-    {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        clo[e] = sl[j * ROW + 8 * h + e];
-        chi[e] = sl[j * ROW + 16 + 8 * h + e];
-      }
-      split8(clo, xr_lo, xi_lo);
-      split8(chi, xr_hi, xi_hi);
-      dft32<false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
-      load_blocks(ms + MI2 * NBLK * 64, Mb);
-    }
+    // twiddle W_1024^{n3 k2} (k2 = j, n3 = row of v); pass 3: matrix on A (rows k3, input n3 in accumulator
+    // order), data on B -> lane = k2, registers = k3
+    pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, p2[v]); }, xr_lo, xr_hi, xi_lo, xi_hi);
+    dft32<false, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
+    load_blocks(ms + MI2 * NBLK * 64, Mb);
     // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N in this exact order.
-    // pass 3': inverse over k3 from the accumulators (register v is input K' = v of the permuted matrix)
-    {
-      u32x4 rlo, rhi, ilo, ihi;
+    // pass 3': data on A (rows k2 = j, input k3 in accumulator order), matrix on B -> lane = n3,
+    // registers = k2
+    pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, unpack_c(hw[v])); }, xr_lo, xr_hi, xi_lo, xi_hi);
+    f32x16 er, ei;
+    dft32<true, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
+    if (it < 3) load_blocks(ms_next + MF2 * NBLK * 64, Ma);
+    // conj twiddle W_1024^{n3 k2} (n3 = j, k2 = row of v); pass 2': matrix on A (rows n2, input k2 in
+    // accumulator order), data on B -> lane = n3, registers = n2; store (n2, n3) at n2 * ROW + n3
+    pack_operands(er, ei, [&](int v, float2 x) { return cmulc(x, p2[v]); }, xr_lo, xr_hi, xi_lo, xi_hi);
+    dft32<true, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
+    if (it < 3) load_blocks(ms_next + MF3 * NBLK * 64, Mb);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const float2 a0 = cmul(make_float2(dr[2 * m], di[2 * m]), unpack_c(hw[2 * m]));
-        const float2 a1 = cmul(make_float2(dr[2 * m + 1], di[2 * m + 1]), unpack_c(hw[2 * m + 1]));
-        const float2 b0 = cmul(make_float2(dr[8 + 2 * m], di[8 + 2 * m]), unpack_c(hw[8 + 2 * m]));
-        const float2 b1 = cmul(make_float2(dr[9 + 2 * m], di[9 + 2 * m]), unpack_c(hw[9 + 2 * m]));
-        rlo[m] = pack2(a0.x, a1.x);
-        ilo[m] = pack2(a0.y, a1.y);
-        rhi[m] = pack2(b0.x, b1.x);
-        ihi[m] = pack2(b0.y, b1.y);
-      }
-      f32x16 er, ei;
-      dft32<true>(Ma, __builtin_bit_cast(bf16x8, rlo), __builtin_bit_cast(bf16x8, rhi),
-                  __builtin_bit_cast(bf16x8, ilo), __builtin_bit_cast(bf16x8, ihi), er, ei);
-      if (it < 3) load_blocks(ms_next + MF2 * NBLK * 64, Ma);
-      // conj twiddle W_1024^{n3 k2} (k2 = j, n3 = row of v), store (n3, k2) at n3 * ROW + k2
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float2 o = cmulc(make_float2(er[v], ei[v]), p2[v]);
-        sl[acc_row(v, h) * ROW + j] = pack2(o.x, o.y);
-      }
-    }
-    // pass 2': inverse over k2, columns n3 = j: element (n3, k2) at n3 * ROW + k2; out (n2, n3)
-    {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        clo[e] = sl[j * ROW + 8 * h + e];
-        chi[e] = sl[j * ROW + 16 + 8 * h + e];
-      }
-      split8(clo, xr_lo, xi_lo);
-      split8(chi, xr_hi, xi_hi);
-      f32x16 er, ei;
-      dft32<true>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
-      if (it < 3) load_blocks(ms_next + MF3 * NBLK * 64, Mb);
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2(er[v], ei[v]);
-    }
+    for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2(er[v], ei[v]);
   }
 
   const bf16x8 m1r = mats[M1I_R * 64 + l], m1i = mats[M1I_I * 64 + l];
@@ -340,7 +328,8 @@ __global__ void k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __res
 namespace {
 constexpr double kTwoPi = 2.0 * 3.14159265358979323846;
 
-// input order of the pass-3' matrix: K' (accumulator register order of pass 3) -> k3
+// input order of the matrices that read accumulators (passes 3, 3', 2'): K' (register order of the
+// previous product's output rows) -> index
 int perm_k3(int Kp) {
   const int hh = (Kp >> 3) & 1, e = Kp & 7, hi = Kp >> 4;
   return 16 * hi + (e < 4 ? 4 * hh + e : 8 + 4 * hh + e - 4);
@@ -373,9 +362,9 @@ float fixed_entry(int q, int i, int K) {
 double slab_angle(int m, int k1, int i, int k) {
   switch (m) {
     case mf::MF2: return (double)((k * (16 * i + k1)) % 512) / 512;                 // row k2, input n2
-    case mf::MF3: return (double)((k * (512 * i + k1)) % mf::N) / mf::N;            // row k3, input n3
+    case mf::MF3: return (double)((perm_k3(k) * (512 * i + k1)) % mf::N) / mf::N;   // row k3, input n3
     case mf::MI3: return (double)((i * (512 * perm_k3(k) + k1)) % mf::N) / mf::N;   // row n3, input k3
-    case mf::MI2: return (double)((i * (16 * k + k1)) % 512) / 512;                 // row n2, input k2
+    case mf::MI2: return (double)((i * (16 * perm_k3(k) + k1)) % 512) / 512;        // row n2, input k2
   }
   return 0.0;
 }
