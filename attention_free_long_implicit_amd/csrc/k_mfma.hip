@@ -178,6 +178,19 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
 #pragma unroll
     for (int e = 0; e < 8; ++e) V[e] = *reinterpret_cast<const u32x4*>(src + 1024 * e);
   }
+  // Slab matrices rotate through two buffers, each load issued one pass before its use:
+  // Ma = pass 2, Mb = pass 3, then Ma = pass 3', Mb = pass 2', then the next slab's pass 2 and 3.
+  // The first slab's matrices and filter spectrum are in flight during pass 1.
+  bf16x8 Ma[NBLK], Mb[NBLK];
+  load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF2 * NBLK * 64, Ma);
+  load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF3 * NBLK * 64, Mb);
+  uint32_t hw[16];
+  auto load_spectrum = [&](int k1) {
+    const uint32_t* hp = Hc + ((size_t)d * 16 + k1) * 16 * 64 + l;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) hw[v] = hp[v * 64];
+  };
+  load_spectrum(w);
   // per-lane W_1024^{j k(v)}, k(v) = row of accumulator v
   float2 p2[16];
 #pragma unroll
@@ -195,37 +208,12 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
   }
   __syncthreads();
 
-  // gate for pass 1', in flight during the middle passes: lane keeps rows b0 / b1 at n1 = 4h + e (e < 4),
-  // 8 consecutive samples each
-  u32x4 G[2][4];
-  if (GATE) {
-    const __bf16* g0 = gate + row0 * L + c0;
-    const __bf16* g1p = gate + row1 * L + c0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      G[0][e] = *reinterpret_cast<const u32x4*>(g0 + 1024 * (4 * h + e));
-      G[1][e] = *reinterpret_cast<const u32x4*>(g1p + 1024 * (4 * h + e));
-    }
-  }
-
   // ---------------- passes 2, 3, 3', 2' per slab k1 (wave w owns k1 = w, w+4, w+8, w+12)
-  // Slab matrices rotate through two buffers, each load issued one pass before its use:
-  // Ma = pass 2, Mb = pass 3, then Ma = pass 3', Mb = pass 2', then the next slab's pass 2 and 3.
-  bf16x8 Ma[NBLK], Mb[NBLK];
-  load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF2 * NBLK * 64, Ma);
-  load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF3 * NBLK * 64, Mb);
   for (int it = 0; it < 4; ++it) {
     const int k1 = w + 4 * it;
     uint32_t* sl = S + k1 * SLAB;
     const bf16x8* ms = slab_mats + (size_t)k1 * SLAB_TABLE * 64;
     const bf16x8* ms_next = slab_mats + (size_t)(it < 3 ? k1 + 4 : k1) * SLAB_TABLE * 64;
-    // filter spectrum of this slab, consumed after passes 2 and 3
-    uint32_t hw[16];
-    {
-      const uint32_t* hp = Hc + ((size_t)d * 16 + k1) * 16 * 64 + l;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) hw[v] = hp[v * 64];
-    }
     bf16x8 xr_lo, xr_hi, xi_lo, xi_hi;
     f32x16 dr, di;
     // pass 2: data on A (rows n3 = j, K = n2 from LDS: element (n2, n3) at n2 * ROW + n3), matrix on B
@@ -251,6 +239,7 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
     // pass 3': data on A (rows k2 = j, input k3 in accumulator order), matrix on B -> lane = n3,
     // registers = k2
     pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, unpack_c(hw[v])); }, xr_lo, xr_hi, xi_lo, xi_hi);
+    if (it < 3) load_spectrum(k1 + 4);
     f32x16 er, ei;
     dft32<true, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
     if (it < 3) load_blocks(ms_next + MF2 * NBLK * 64, Ma);
@@ -261,6 +250,19 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
     if (it < 3) load_blocks(ms_next + MF3 * NBLK * 64, Mb);
 #pragma unroll
     for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2(er[v], ei[v]);
+  }
+
+  // gate for pass 1' (issued after every slab load, so no slab waits on it): lane keeps rows b0 / b1 at
+  // n1 = 4h + e (e < 4), 8 consecutive samples each
+  u32x4 G[2][4];
+  if (GATE) {
+    const __bf16* g0 = gate + row0 * L + c0;
+    const __bf16* g1p = gate + row1 * L + c0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      G[0][e] = *reinterpret_cast<const u32x4*>(g0 + 1024 * (4 * h + e));
+      G[1][e] = *reinterpret_cast<const u32x4*>(g1p + 1024 * (4 * h + e));
+    }
   }
 
   const bf16x8 m1r = mats[M1I_R * 64 + l], m1i = mats[M1I_I * 64 + l];
