@@ -7,7 +7,8 @@ over one batch of seeded synthetic input already resident in HBM.  The filter sp
 the filter parameters and the grid, so they are built once (hyena_filter_gen) before the timed region;
 that build is reported separately as ``filter_gen_ms``.
 
-Prints ONE JSON line.  Default workload: order 2, B=4, D=768, L=8192, bf16 storage (workload 1);
+Prints ONE JSON line.  Default workload: order 2, B=4, D=768, L=8192, bf16 storage (workload 1), whose
+convolution runs on the matrix cores;
 ``--workload i`` times another of hyena_inputs.WORKLOADS (parity configurations are not bench lines).
 """
 from __future__ import annotations
@@ -35,11 +36,24 @@ def algorithmic_bytes_per_order(w) -> int:
     return 3 * w.elem_bytes * w.tokens_channels + 4 * w.D * w.support
 
 
+def uses_matrix_cores(w) -> bool:
+    """bf16 storage, L = 8192, rows in pairs of one channel: the library's matrix-core kernel."""
+    return w.ndim == 1 and w.dtype == "bf16" and w.dims[0] == 8192 and w.B % 2 == 0
+
+
 def kernel_key(w) -> str:
     if w.ndim == 3:
         return f"conv3d_{w.dims[0]}cubed_{w.dtype}"
     L = w.dims[0]
+    if uses_matrix_cores(w):
+        return f"conv_mfma_L{L}_bf16_pairs"
     return f"conv1d_L{L}_{w.dtype}_gate" if L <= 16384 else f"fourstep_L{L}_{w.dtype}"
+
+
+def arithmetic(w) -> str:
+    if uses_matrix_cores(w):
+        return "bf16 matrix-core products, fp32 accumulation and twiddles"
+    return "fp32"
 
 
 def load_traffic(key: str):
@@ -192,7 +206,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded activations, Xavier-uniform filter networks; see hyena_inputs)",
         "config": {"workload": w.name, "order": w.order, "B": w.B, "D": w.D, "grid": list(w.dims),
-                   "storage": w.dtype, "arithmetic": "fp32"},
+                   "storage": w.dtype, "arithmetic": arithmetic(w)},
         "hbm_gbps_alg": alg_step / (ms_per_step / 1e3) / 1e9,
         "hbm_frac_alg": alg_step / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
         "event_ms_per_step": float(np.mean(step_ms)),
