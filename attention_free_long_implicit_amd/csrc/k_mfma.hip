@@ -20,7 +20,8 @@
 //   pass 1' inverse DFT over k1, keep n1 < 8 (the causal half); gate; store
 // Every factor that depends on the slab k1 and on one of a pass's own indices lives in that pass's
 // matrix (16 slabs x 4 matrices, a 256 KB table that stays in L2), so the only elementwise twiddle
-// left is W_1024^{n3 k2}, whose two indices are the row and the column of one product.
+// left is W_1024^{n3 k2}, whose two indices are the row and the column of one product.  The filter
+// spectrum is stored for slabs 0..8 only (36 KB per channel); conjugate symmetry gives the rest.
 // A complex radix-R DFT is a real 2R x 2R matrix on (Re, Im); each MFMA (32x32x16) multiplies a 32-row
 // block of it by 32 columns (independent sub-transforms).  LDS holds one plane of complex bf16 words
 // (re low, im high); rows hold 32 words plus one pad, so lanes reading one word each from 32
@@ -52,6 +53,7 @@ enum { M1F = 0, M1I_R, M1I_I, NFIX };
 enum { MF2 = 0, MF3, MI3, MI2, NSLABMAT };       // pass 2, pass 3, pass 3', pass 2'
 enum { B_CLO = 0, B_CHI, B_SLO, B_SHI, NBLK };   // cos / sin, K < 16 / K >= 16
 constexpr int SLAB_TABLE = NSLABMAT * NBLK;       // bf16x8 per lane per slab
+constexpr int PAIR_SLABS = 9;                     // filter-spectrum slabs stored per channel (k1 = 0..8)
 }  // namespace mf
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -184,11 +186,16 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
   bf16x8 Ma[NBLK], Mb[NBLK];
   load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF2 * NBLK * 64, Ma);
   load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF3 * NBLK * 64, Mb);
+  // Filter spectrum: only slabs 0..8 are stored.  h is real, so H[N - k] = conj(H[k]); bin N - k of
+  // slab k1 > 8 is register 15 - v of lane 63 - l in slab 16 - k1, read mirrored and conjugated (sign of
+  // the imaginary half flipped).
   uint32_t hw[16];
   auto load_spectrum = [&](int k1) {
-    const uint32_t* hp = Hc + ((size_t)d * 16 + k1) * 16 * 64 + l;
+    const bool mirror = k1 > 8;
+    const uint32_t* hp = Hc + ((size_t)d * PAIR_SLABS + (mirror ? 16 - k1 : k1)) * 16 * 64 + (mirror ? 63 - l : l);
+    const uint32_t flip = mirror ? 0x80000000u : 0u;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) hw[v] = hp[v * 64];
+    for (int v = 0; v < 16; ++v) hw[v] = hp[(mirror ? 15 - v : v) * 64] ^ flip;
   };
   load_spectrum(w);
   // per-lane W_1024^{j k(v)}, k(v) = row of accumulator v
@@ -310,12 +317,13 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
 }
 
 // Pair-order spectrum: Hc[d][k1][v][lane] = H[k]/N as bf16 (re low, im high), k = k1 + 16 (lane%32)
-// + 512 k3(v, lane/32); H from the natural-order bins 0..L (upper bins by conjugate symmetry).
+// + 512 k3(v, lane/32), for k1 = 0..8 (the convolution kernel mirrors slabs 9..15 from slabs 7..1);
+// H from the natural-order bins 0..L (upper bins by conjugate symmetry).
 __global__ void k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc) {
   using namespace mf;
   const int d = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;    // (k1, v, lane)
-  if (idx >= 16 * 16 * 64) return;
+  if (idx >= PAIR_SLABS * 16 * 64) return;
   const int k1 = idx / (16 * 64), v = (idx / 64) % 16, l = idx % 64;
   const int jj = l & 31, h = l >> 5;
   const int k = k1 + 16 * jj + 512 * acc_row(v, h);
@@ -323,7 +331,7 @@ __global__ void k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __res
   float2 hv = k <= L ? hn[k] : cconj(hn[N - k]);
   hv = cscale(hv, 1.0f / N);
   const uint32_t lo = (uint32_t)f32_to_bf16_rne(hv.x), hi = (uint32_t)f32_to_bf16_rne(hv.y);
-  Hc[(size_t)d * 16 * 16 * 64 + idx] = lo | (hi << 16);
+  Hc[(size_t)d * PAIR_SLABS * 16 * 64 + idx] = lo | (hi << 16);
 }
 
 // ------------------------------------------------------------------ host side
@@ -399,7 +407,7 @@ void mfma_matrices_host(uint16_t* out) {   // [NFIX][64][8] then [16 slabs][4 ma
 }
 
 bool mfma_pair_supported(int log2L, int B) { return log2L == 13 && B % 2 == 0; }
-size_t mfma_pair_spectrum_bytes_per_channel() { return (size_t)16 * 16 * 64 * 4; }
+size_t mfma_pair_spectrum_bytes_per_channel() { return (size_t)mf::PAIR_SLABS * 16 * 64 * 4; }
 
 hipError_t launch_conv_mfma(const void* u, const void* gate, void* y, const void* Hc, const void* mats, int B, int D,
                             const Twiddles& tw, hipStream_t s) {
@@ -414,7 +422,8 @@ hipError_t launch_conv_mfma(const void* u, const void* gate, void* y, const void
 }
 
 hipError_t launch_pair_spectrum(const float2* Hnat, void* Hc, int D, hipStream_t s) {
-  hipLaunchKernelGGL(k_pair_spectrum, dim3((16 * 16 * 64 + 255) / 256, D), dim3(256), 0, s, Hnat, (uint32_t*)Hc);
+  hipLaunchKernelGGL(k_pair_spectrum, dim3((mf::PAIR_SLABS * 16 * 64 + 255) / 256, D), dim3(256), 0, s, Hnat,
+                     (uint32_t*)Hc);
   return hipGetLastError();
 }
 

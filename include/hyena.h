@@ -71,7 +71,8 @@ typedef struct {
   const float *W1, *b1, *W2, *b2, *alpha;
 } hyena_filter_params;
 
-/* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array). */
+/* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array).
+ * For L = 8192 it also holds a bf16 copy laid out for the matrix-core kernel (36 KB per channel). */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_filter_gen needs: room for the taps (used when h_time is NULL) plus, for
@@ -91,6 +92,8 @@ int hyena_filter_gen(const hyena_filter_params *p, hyena_dims dims, int mode, fl
 
 /* One long convolution with optional gate: y = gate * (h conv u), or y = h conv u when gate == NULL.
  * u, gate, y: [B, D, points] of dtype.  spectrum: from hyena_filter_gen for the same dims and D.
+ * bf16 storage with L = 8192, even B and 16-byte-aligned u, gate and y runs on the matrix cores (rows
+ * b and b+1 of a channel transformed together); every other case runs the fp32 transform engine.
  * y may equal u or gate exactly (in place); any other overlap returns HYENA_EALIAS. */
 int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *u,
                   const void *spectrum, const void *gate, void *y, void *ws, size_t ws_bytes,

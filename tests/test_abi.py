@@ -42,7 +42,10 @@ def _size(fn, *args):
 
 def test_size_queries(lib):
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([8192]), L.CAUSAL, 768)
-    assert st == 0 and n == 768 * 8192 * 8
+    # L = 8192 adds the matrix-core copy: 9 slabs x 16 registers x 64 lanes of bf16 pairs per channel
+    assert st == 0 and n == 768 * 8192 * 8 + 768 * 9 * 16 * 64 * 4
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([4096]), L.CAUSAL, 768)
+    assert st == 0 and n == 768 * 4096 * 8
     st, n = _size(lib.hyena_filter_workspace_bytes, L.dims_of([1024]), L.CAUSAL, 16)
     assert st == 0 and n == 16 * 1024 * 4
     st, n = _size(lib.hyena_workspace_bytes, 2, 4, 768, L.dims_of([8192]), L.BF16, L.CAUSAL)
