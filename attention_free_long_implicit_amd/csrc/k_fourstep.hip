@@ -12,8 +12,9 @@
 //                        for every order but the last the same workgroup then runs the next
 //                        order's pass A on the gated tile, so u_i never goes to HBM
 //
-// The intermediate is one complex fp32 M-vector per row; rows are processed in chunks whose
-// intermediates stay resident in L2 / the memory-side cache.  Rows are visited channel-major
+// The intermediate is one complex M-vector per row, fp32 for fp32 activations and bf16 words (re low,
+// im high) for bf16 activations (rounded like every stored bf16 value; it halves the pass traffic).
+// Rows are processed in chunks whose intermediates stay resident in L2 / the memory-side cache.  Rows are visited channel-major
 // (q = d*B + b) so the B rows of a channel read its filter spectrum back to back.
 //
 // Spectrum layout per channel: Hs[g][slot][t'] for row-pair group g < M1/2, slot < 2 RP, thread t'
@@ -22,6 +23,26 @@
 #include "launch.h"
 
 namespace hyena {
+
+// Element type of the intermediate.
+template <bool BF16> struct Inter;
+template <> struct Inter<false> {
+  using T = float2;
+  __device__ __forceinline__ static float2 ld(const float2* p) { return *p; }
+  __device__ __forceinline__ static void st(float2* p, float2 v) { *p = v; }
+};
+template <> struct Inter<true> {
+  using T = uint32_t;
+  __device__ __forceinline__ static float2 ld(const uint32_t* p) {
+    const uint32_t w = *p;
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  }
+  __device__ __forceinline__ static void st(uint32_t* p, float2 v) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    const bf16x2 b = {(__bf16)v.x, (__bf16)v.y};
+    *p = __builtin_bit_cast(uint32_t, b);
+  }
+};
 
 template <int LOG2M> struct FourStepPlan;
 // M1 (columns) x M2 (rows); column radices, row radices (last radix 8, 16 elements per thread)
@@ -61,9 +82,10 @@ struct FS {
 template <int LOG2M, bool BF16, int MODE, bool GATE, bool CHAIN>
 __global__ void __launch_bounds__(FS<LOG2M>::TC)
 k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* gate,
-          typename Store<BF16>::elem* y, float2* I, int q0, int nq, int B, int D, Twiddles tw) {
+          typename Store<BF16>::elem* y, typename Inter<BF16>::T* I, int q0, int nq, int B, int D, Twiddles tw) {
   using F = FS<LOG2M>;
   using St = Store<BF16>;
+  using In = Inter<BF16>;
   constexpr int M = F::M, M1 = F::M1, M2 = F::M2, C = F::C, TC = F::TC;
   constexpr int PER_T = C * M1 / TC;              // tile elements per thread
   __shared__ float2 lds[lds_padded_size(C * M1)];
@@ -74,7 +96,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   const int d = q / B, b = q % B;
   const size_t row = (size_t)b * D + d;
   const int c0 = tile * C;
-  float2* Irow = I + (size_t)ql * M;
+  typename In::T* Irow = I + (size_t)ql * M;
   auto tile_addr = [&](int p, int c) { return lds_pad(p * C + c); };
 
   if constexpr (MODE == 0) {
@@ -90,7 +112,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
     static_for<PER_T>([&](auto ii) {
       const int e = t + TC * ii.value;
       const int p = e / C, c = e % C;
-      lds[tile_addr(p, c)] = Irow[(size_t)p * M2 + c0 + c];
+      lds[tile_addr(p, c)] = In::ld(Irow + (size_t)p * M2 + c0 + c);
     });
     __syncthreads();
     F::Col::template inverse<true>(lds, tw, t);
@@ -121,7 +143,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   static_for<PER_T>([&](auto ii) {
     const int e = t + TC * ii.value;
     const int p = e / C, c = e % C;
-    Irow[(size_t)p * M2 + c0 + c] = lds[tile_addr(p, c)];
+    In::st(Irow + (size_t)p * M2 + c0 + c, lds[tile_addr(p, c)]);
   });
 }
 
@@ -161,11 +183,12 @@ k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
 // beta_A = t' of the first row and beta_B = NBLK-1-t' of the second (their bins mirror each other:
 // k <-> M-k pairs k1 with M1-k1 and complements every k2 digit); the g_glob = 0 pair instead uses
 // whole-row negation pairing on row 0 (threads < TP/2) and in-row complement pairing on row M1/2.
-template <int LOG2M, int MODE>
+template <int LOG2M, int MODE, bool IBF16>
 __global__ void __launch_bounds__(FS<LOG2M>::TR)
-k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq, int B,
-          Twiddles tw) {
+k_fs_rows(typename Inter<IBF16>::T* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq,
+          int B, Twiddles tw) {
   using F = FS<LOG2M>;
+  using In = Inter<IBF16>;
   using Row = typename F::Row;
   using RL = typename F::RowRL;
   constexpr int M = F::M, M1 = F::M1, M2 = F::M2, G = F::G, TP = F::TP, TR = F::TR, RP = F::RP;
@@ -176,7 +199,7 @@ k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out,
   const int ql = lb % nq, grp = lb / nq;
   const int q = q0 + ql;
   const int d = (MODE == 0) ? q / B : q;
-  float2* Irow = I + (size_t)ql * M;
+  typename In::T* Irow = I + (size_t)ql * M;
 
   // bin row k1 of sub-row s (s = 2j: first of pair j, 2j+1: second)
   auto k1_of = [&](int s) {
@@ -192,13 +215,13 @@ k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out,
     int s, n;
     Row::first_input(t, i, s, n);
     const int k1 = k1_of(s);
-    const float2* src = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
+    const typename In::T* src = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
     const float2 wb = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
     float2 wp[R0];
     twiddle_powers<R0>(ws, wp);
     static_for<R0>([&](auto m) {
-      const float2 v = src[n + m.value * PER0];
+      const float2 v = In::ld(src + n + m.value * PER0);
       x[i * R0 + m.value] = cmul(v, cmul(wb, wp[m.value]));
     });
   });
@@ -252,13 +275,13 @@ k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out,
     int s, n;
     Row::first_input(t, i, s, n);
     const int k1 = k1_of(s);
-    float2* dst = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
+    typename In::T* dst = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
     const float2 wb = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
     float2 wp[R0];
     twiddle_powers<R0>(ws, wp);
     static_for<R0>([&](auto m) {
-      dst[n + m.value * PER0] = cmulc(x[i * R0 + m.value], cmul(wb, wp[m.value]));
+      In::st(dst + n + m.value * PER0, cmulc(x[i * R0 + m.value], cmul(wb, wp[m.value])));
     });
   });
 }
@@ -311,25 +334,27 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
                           void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s) {
   using F = FS<LOG2M>;
   using E = typename Store<BF16>::elem;
+  using IT = typename Inter<BF16>::T;
+  IT* Ib = reinterpret_cast<IT*>(I);
   const int rows = B * D;
   const int tiles = F::M2 / F::C;
   const int groups = (F::M1 / 2) / F::G;
   for (int q0 = 0; q0 < rows; q0 += chunk) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
     hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                       (const E*)v, (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
+                       (const E*)v, (const E*)nullptr, (E*)nullptr, Ib, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
-      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0>), dim3(groups * nq), dim3(F::TR), 0, s, I,
+      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0, BF16>), dim3(groups * nq), dim3(F::TR), 0, s, Ib,
                          (const float2*)spectra[i], (float2*)nullptr, q0, nq, B, tw);
       if (i + 1 < order)
         hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, true>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                           (const E*)nullptr, (const E*)x[i], (E*)nullptr, I, q0, nq, B, D, tw);
+                           (const E*)nullptr, (const E*)x[i], (E*)nullptr, Ib, q0, nq, B, D, tw);
       else if (x[i])
         hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                           (const E*)nullptr, (const E*)x[i], (E*)y, I, q0, nq, B, D, tw);
+                           (const E*)nullptr, (const E*)x[i], (E*)y, Ib, q0, nq, B, D, tw);
       else
         hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, false, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                           (const E*)nullptr, (const E*)nullptr, (E*)y, I, q0, nq, B, D, tw);
+                           (const E*)nullptr, (const E*)nullptr, (E*)y, Ib, q0, nq, B, D, tw);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -346,7 +371,7 @@ hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int 
   for (int q0 = 0; q0 < D; q0 += chunk) {
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
     hipLaunchKernelGGL((k_fs_cols_taps<LOG2M>), dim3(tiles * nq), dim3(F::TC), 0, s, h, I, q0, nq, tw);
-    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const float2*)nullptr,
+    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1, false>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const float2*)nullptr,
                        Hs, q0, nq, 1, tw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
