@@ -121,10 +121,11 @@ size_t taps_per_channel(int mode, int64_t pts) { return mode == HYENA_LINEAR ? c
 bool has_pair_copy(int64_t L) { return mfma_pair_supported(log2i(L), 2); }
 size_t pair_copy_temp_bytes(int64_t L, int64_t D) { return (size_t)D * (size_t)(L + 1) * sizeof(float2); }
 
-// Rows per multi-pass chunk by default: about 96 MB of intermediate, so a chunk's intermediate
-// stays in the 256 MB memory-side cache while the next pass reads it.
+// Rows per multi-pass chunk by default: about 160 MB of intermediate.  Smaller chunks (24-96 MB,
+// sized for the 256 MB memory-side cache) measured slower, from fewer workgroups per launch; larger
+// ones (up to whole workloads) measured the same.
 int64_t default_chunk_rows(int64_t per, int64_t rows) {
-  int64_t c = ((int64_t)96 << 20) / per;
+  int64_t c = ((int64_t)160 << 20) / per;
   if (c < 1) c = 1;
   return c < rows ? c : rows;
 }
