@@ -130,16 +130,39 @@ int64_t default_chunk_rows(int64_t per, int64_t rows) {
   return c < rows ? c : rows;
 }
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The matrix-core kernel: bf16, L = 8192, rows in pairs, and (16-byte vector accesses) every activation
+// pointer 16-byte aligned.
+bool use_mfma(int dtype, int64_t B, int64_t L) { return dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B); }
+
+// Orders [0, order) through the matrix-core kernel, up to kMfmaMaxChain orders per launch with u_i on chip.
+int conv_mfma_chain(int64_t B, int64_t D, int64_t L, const void* u, const void* const* gates,
+                    const void* const* spectra, int order, void* y, const Twiddles& tw, hipStream_t s) {
+  const void* mats = device_mats();
+  if (!mats) return HYENA_EHIP;
+  const void* cur = u;
+  for (int i0 = 0; i0 < order; i0 += kMfmaMaxChain) {
+    const int n = order - i0 < kMfmaMaxChain ? order - i0 : kMfmaMaxChain;
+    const void* g[kMfmaMaxChain];
+    const void* sp[kMfmaMaxChain];
+    for (int k = 0; k < n; ++k) {
+      g[k] = gates[i0 + k];
+      sp[k] = (const char*)spectra[i0 + k] + (size_t)D * (size_t)L * sizeof(float2);
+    }
+    const int st = hip_status(launch_conv_mfma(cur, g, sp, n, y, mats, (int)B, (int)D, tw, s));
+    if (st) return st;
+    cur = y;
+  }
+  return HYENA_OK;
+}
+
 int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const void* spectrum, const void* gate,
               void* y, const Twiddles& tw, hipStream_t s) {
-  // the matrix-core kernel moves 16-byte vectors: every activation pointer must be 16-byte aligned
-  const bool aligned16 = ((reinterpret_cast<uintptr_t>(u) | reinterpret_cast<uintptr_t>(gate) |
-                           reinterpret_cast<uintptr_t>(y)) & 15u) == 0;
-  if (dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B) && aligned16) {
-    const void* mats = device_mats();
-    if (!mats) return HYENA_EHIP;
-    const void* pair = (const char*)spectrum + (size_t)D * (size_t)L * sizeof(float2);
-    return hip_status(launch_conv_mfma(u, gate, y, pair, mats, (int)B, (int)D, tw, s));
+  if (use_mfma(dtype, B, L) && aligned16(u) && aligned16(gate) && aligned16(y)) {
+    const void* g[1] = {gate};
+    const void* sp[1] = {spectrum};
+    return conv_mfma_chain(B, D, L, u, g, sp, 1, y, tw, s);
   }
   return hip_status(launch_conv1d_single(log2i(L), dtype == HYENA_BF16, u, gate, y, (const float2*)spectrum,
                                          (int)B, (int)D, tw, s));
@@ -327,6 +350,11 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   if (chunk)
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra,
                                              y, (float2*)ws, chunk, tw, stream));
+  if (use_mfma(dtype, B, pts)) {
+    bool aligned = aligned16(v) && aligned16(y);
+    for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);
+    if (aligned) return conv_mfma_chain(B, D, pts, v, x, spectra, order, y, tw, stream);
+  }
   const void* cur = v;
   for (int i = 0; i < order; ++i) {
     if ((st = conv_once(B, D, pts, dtype, cur, spectra[i], x[i], y, tw, stream))) return st;

@@ -56,6 +56,13 @@ constexpr int SLAB_TABLE = NSLABMAT * NBLK;       // bf16x8 per lane per slab
 constexpr int PAIR_SLABS = 9;                     // filter-spectrum slabs stored per channel (k1 = 0..8)
 }  // namespace mf
 
+// Orders run back to back in one launch: gate and matrix-core spectrum copy of each order.
+struct MfmaChain {
+  const __bf16* gate[kMfmaMaxChain];
+  const uint32_t* spectrum[kMfmaMaxChain];
+  int order;
+};
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -160,26 +167,35 @@ __device__ __forceinline__ void load_blocks(const bf16x8* p, bf16x8 (&M)[mf::NBL
 // (row, n1) in global memory.
 template <bool GATE>
 __global__ void __launch_bounds__(mf::T, 2)
-k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __restrict__ Hc,
-            const bf16x8* __restrict__ mats, int B, int D, Twiddles tw) {
+k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__ mats, int B, int D,
+            Twiddles tw) {
   using namespace mf;
   __shared__ uint32_t S[PLANE];
-  const int t = threadIdx.x, w = t >> 6, l = t & 63, j = l & 31, h = l >> 5;
   const int npair = B >> 1;
   const int r = xcd_logical_block(blockIdx.x, D * npair);
   const int d = r / npair, p = r % npair;
   const size_t row0 = (size_t)(2 * p) * D + d, row1 = (size_t)(2 * p + 1) * D + d;
-  const int c0 = 256 * w + 8 * j;
-  const int n2c = 8 * w + (j >> 2), n3c = 8 * (j & 3);   // tile t: n2 = n2c, n3 = n3c + t
-  const bf16x8* slab_mats = mats + NFIX * 64 + l;
 
-  // ---------------- pass 1 loads: lanes h = 0 / 1 carry row b0 / b1 (real / imaginary input), n1 = e
+  // pass 1 input of the first order: lanes h = 0 / 1 carry row b0 / b1 (real / imaginary input), n1 = e
   u32x4 V[8];
   {
-    const __bf16* src = (h == 0 ? u + row0 * L : u + row1 * L) + c0;
+    const int l = threadIdx.x & 63, c0 = 256 * (threadIdx.x >> 6) + 8 * (l & 31);
+    const __bf16* src = ((l >> 5) == 0 ? u + row0 * L : u + row1 * L) + c0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) V[e] = *reinterpret_cast<const u32x4*>(src + 1024 * e);
   }
+
+  for (int ord = 0; ord < ch.order; ++ord) {
+  // lane constants derived from an opaque copy of the thread id, so nothing is hoisted across orders
+  int tq = threadIdx.x;
+  asm volatile("" : "+v"(tq));
+  const int t = tq, w = t >> 6, l = t & 63, j = l & 31, h = l >> 5;
+  const int c0 = 256 * w + 8 * j;
+  const int n2c = 8 * w + (j >> 2), n3c = 8 * (j & 3);   // tile t: n2 = n2c, n3 = n3c + t
+  const bf16x8* slab_mats = mats + NFIX * 64 + l;
+  const uint32_t* __restrict__ Hc = ch.spectrum[ord];
+  const __bf16* gate = ch.gate[ord];
+
   // Slab matrices rotate through two buffers, each load issued one pass before its use:
   // Ma = pass 2, Mb = pass 3, then Ma = pass 3', Mb = pass 2', then the next slab's pass 2 and 3.
   // The first slab's matrices and filter spectrum are in flight during pass 1.
@@ -308,11 +324,29 @@ k_conv_mfma(const __bf16* u, const __bf16* gate, __bf16* y, const uint32_t* __re
     });
     __bf16* y0 = y + row0 * L + c0;
     __bf16* y1 = y + row1 * L + c0;
+    if (ord + 1 == ch.order) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<u32x4*>(y0 + 1024 * (4 * h + e)) = Y[0][e];
-      *reinterpret_cast<u32x4*>(y1 + 1024 * (4 * h + e)) = Y[1][e];
+      for (int e = 0; e < 4; ++e) {
+        *reinterpret_cast<u32x4*>(y0 + 1024 * (4 * h + e)) = Y[0][e];
+        *reinterpret_cast<u32x4*>(y1 + 1024 * (4 * h + e)) = Y[1][e];
+      }
+    } else {
+      // u_i stays on chip, rounded to bf16 exactly as its store would be.  Pass 1' left lane (j, h) with
+      // rows b0, b1 at n1 = 4h + e; the next pass 1 wants row b_h at n1 = 0..7 in lane (j, h): swap the
+      // other row's half with lane l ^ 32 through the LDS crossbar (no LDS memory).
+      const int partner = (l ^ 32) << 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const u32x4 own = h ? Y[1][e] : Y[0][e], snd = h ? Y[0][e] : Y[1][e];
+        u32x4 rcv;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rcv[q] = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)snd[q]);
+        V[e] = h ? rcv : own;
+        V[4 + e] = h ? own : rcv;
+      }
+      __syncthreads();   // every wave is done reading LDS before the next order's pass 1 writes it
     }
+  }
   }
 }
 
@@ -409,15 +443,25 @@ void mfma_matrices_host(uint16_t* out) {   // [NFIX][64][8] then [16 slabs][4 ma
 bool mfma_pair_supported(int log2L, int B) { return log2L == 13 && B % 2 == 0; }
 size_t mfma_pair_spectrum_bytes_per_channel() { return (size_t)mf::PAIR_SLABS * 16 * 64 * 4; }
 
-hipError_t launch_conv_mfma(const void* u, const void* gate, void* y, const void* Hc, const void* mats, int B, int D,
-                            const Twiddles& tw, hipStream_t s) {
+hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void* const* spectra, int order,
+                            void* y, const void* mats, int B, int D, const Twiddles& tw, hipStream_t s) {
+  if (order < 1 || order > kMfmaMaxChain) return hipErrorInvalidValue;
+  MfmaChain ch{};
+  bool gated = true;
+  for (int i = 0; i < order; ++i) {
+    ch.gate[i] = (const __bf16*)gates[i];
+    ch.spectrum[i] = (const uint32_t*)spectra[i];
+    gated = gated && gates[i] != nullptr;
+  }
+  if (!gated && (order != 1 || gates[0])) return hipErrorInvalidValue;   // only a single order may go ungated
+  ch.order = order;
   const dim3 grid(D * (B / 2)), block(mf::T);
-  if (gate)
-    hipLaunchKernelGGL((k_conv_mfma<true>), grid, block, 0, s, (const __bf16*)u, (const __bf16*)gate, (__bf16*)y,
-                       (const uint32_t*)Hc, (const bf16x8*)mats, B, D, tw);
+  if (gated)
+    hipLaunchKernelGGL((k_conv_mfma<true>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch, (const bf16x8*)mats,
+                       B, D, tw);
   else
-    hipLaunchKernelGGL((k_conv_mfma<false>), grid, block, 0, s, (const __bf16*)u, (const __bf16*)nullptr,
-                       (__bf16*)y, (const uint32_t*)Hc, (const bf16x8*)mats, B, D, tw);
+    hipLaunchKernelGGL((k_conv_mfma<false>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch,
+                       (const bf16x8*)mats, B, D, tw);
   return hipGetLastError();
 }
 

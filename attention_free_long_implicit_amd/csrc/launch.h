@@ -43,8 +43,10 @@ bool mfma_pair_supported(int log2L, int B);
 size_t mfma_pair_spectrum_bytes_per_channel();
 size_t mfma_matrices_count();                    // bf16 values in the DFT-matrix table
 void mfma_matrices_host(uint16_t* out);
-hipError_t launch_conv_mfma(const void* u, const void* gate, void* y, const void* Hc, const void* mats, int B, int D,
-                            const Twiddles& tw, hipStream_t s);
+// Orders 1..order back to back in one launch (u_i stays on chip); spectra[i] = matrix-core copies.
+constexpr int kMfmaMaxChain = 8;
+hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void* const* spectra, int order,
+                            void* y, const void* mats, int B, int D, const Twiddles& tw, hipStream_t s);
 hipError_t launch_pair_spectrum(const float2* Hnat, void* Hc, int D, hipStream_t s);
 
 // ---- implicit filter taps

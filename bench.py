@@ -36,6 +36,11 @@ def algorithmic_bytes_per_order(w) -> int:
     return 3 * w.elem_bytes * w.tokens_channels + 4 * w.D * w.support
 
 
+def floor_bytes_per_step(w) -> int:
+    """All orders fused on chip: read v and the N gates, write y, plus the N filters (fp32 taps)."""
+    return (w.order + 2) * w.elem_bytes * w.tokens_channels + 4 * w.order * w.D * w.support
+
+
 def uses_matrix_cores(w) -> bool:
     """bf16 storage, L = 8192, rows in pairs of one channel: the library's matrix-core kernel."""
     return w.ndim == 1 and w.dtype == "bf16" and w.dims[0] == 8192 and w.B % 2 == 0
@@ -213,7 +218,17 @@ def main():
         "filter_gen_ms": filter_gen_ms,
     }
     key = kernel_key(w)
-    if w.ndim == 1 and w.dims[0] <= 16384:
+    if uses_matrix_cores(w) and w.order <= 8:
+        # the whole step is one launch of the matrix-core kernel: all orders, u_i kept on chip
+        launch_ms = float(np.mean(step_ms))
+        achieved = alg_step / (launch_ms / 1e3) / 1e9
+        floor = floor_bytes_per_step(w)
+        out["roofline"] = {"bound": "hbm", "kernel": key, "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                           "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": load_traffic(key),
+                           "launch_ms": launch_ms, "alg_bytes_per_launch": alg_step,
+                           "floor_bytes_per_launch": floor,
+                           "floor_frac": floor / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+    elif w.ndim == 1 and w.dims[0] <= 16384:
         # the whole step is `order` launches of one fused kernel: its average launch duration
         launch_ms = float(np.mean(step_ms)) / w.order
         bytes_launch = algorithmic_bytes_per_order(w)

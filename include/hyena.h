@@ -102,7 +102,9 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
 /* The order-N operator y = x_N * (h_N conv (... x_1 * (h_1 conv v))).
  * x: host array of `order` device pointers (x[0] = x_1); spectra: host array of `order` spectra
  * (spectra[i] pairs with x[i]).  y doubles as the buffer between orders; y may equal v exactly but
- * must not overlap any x_i.  ws: hyena_workspace_bytes bytes. */
+ * must not overlap any x_i.  ws: hyena_workspace_bytes bytes.  On the matrix-core case (see
+ * hyena_fftconv) up to 8 orders run in one launch with u_i kept on chip, rounded to bf16 exactly as a
+ * store would round it, so the result equals `order` separate hyena_fftconv calls bit for bit. */
 int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *v,
                    const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,
                    hipStream_t stream);

@@ -244,3 +244,52 @@ def test_matrix_core_path_misaligned_falls_back(torch_cuda):
     e = rel_err_rows(ym.float().cpu().numpy().reshape(-1, 8192), ya.float().cpu().numpy().reshape(-1, 8192))
     say(f"misaligned vs aligned max rel diff {e.max():.3e}")
     assert e.max() < BF16_TOL
+
+
+def test_matrix_core_orders_fused_order3(torch_cuda):
+    """Order 3 at L = 8192, bf16, B = 2: the orders run back to back in one launch with u_1, u_2 kept
+    on chip.  All rows against the oracle; bitwise equal to the same orders as separate one-order
+    calls (each storing u_i in bf16)."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[2].with_(B=2, D=6, dims=(8192,))
+    assert w.order == 3
+    v, xs = hi.draw_activations(w, seed=31)
+    params = hi.draw_filter_params(w, seed=31)
+    say("fused orders: order 3, B=2, D=6, L=8192, bf16")
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
+    vd = to_dev(v, torch.bfloat16)
+    xd = [to_dev(x, torch.bfloat16) for x in xs]
+    y = hy.operator(vd, xd, spectra)
+    cur = vd
+    for x, sp in zip(xd, spectra):
+        cur = hy.fftconv(cur, sp, gate=x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, cur)
+    rows = [(b, d) for b in range(2) for d in range(6)]
+    ref = oracle_rows_1d(w, v, xs, params, rows)
+    got = np.stack([y.float().cpu().numpy()[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
+    assert e.max() < BF16_TOL
+
+
+def test_matrix_core_orders_beyond_one_launch(torch_cuda):
+    """Nine orders: eight fused in one launch, then one more; equal to nine one-order calls."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[1].with_(B=2, D=3, dims=(8192,))
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((2, 3, 8192)).astype(np.float32)
+    xs = [rng.uniform(0.5, 1.5, (2, 3, 8192)).astype(np.float32) for _ in range(9)]
+    params = hi.draw_filter_params(w, seed=7)[0]
+    sp = hy.filter_gen(params_to_dev(params), w.dims)
+    vd = to_dev(v, torch.bfloat16)
+    xd = [to_dev(x, torch.bfloat16) for x in xs]
+    y = hy.operator(vd, xd, [sp] * 9)
+    cur = vd
+    for x in xd:
+        cur = hy.fftconv(cur, sp, gate=x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, cur)
+    assert torch.isfinite(y.float()).all()
