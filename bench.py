@@ -135,8 +135,10 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU reaches steady-state clocks only under sustained load: 0.1 s of warm-up and timed work
+    # (workload 1) measures that state; 50 steps after 5 read about 15 % slower
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=1, help="index into hyena_inputs.WORKLOADS")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -182,16 +184,18 @@ def main():
         hy.operator(vd, xd, spectra, y=y, ws=ws)
     torch.cuda.synchronize()
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # two events on the launch stream bracket the timed region (an event after every step would add
+    # its own few microseconds to each step)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev[0].record(stream)
+    ev0.record(stream)
     for k in range(args.steps):
         hy.operator(vd, xd, spectra, y=y, ws=ws)
-        ev[k + 1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = np.array([ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)])
+    step_ms = np.full(args.steps, ev0.elapsed_time(ev1) / args.steps)
 
     ms_per_step = 1e3 * wall / args.steps
     T = w.tokens_channels
