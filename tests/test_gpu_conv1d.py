@@ -293,3 +293,44 @@ def test_matrix_core_orders_beyond_one_launch(torch_cuda):
     torch.cuda.synchronize()
     assert torch.equal(y, cur)
     assert torch.isfinite(y.float()).all()
+
+
+@pytest.mark.parametrize("L,B,dtype", [(1024, 1, "f32"), (8192, 1, "bf16"), (8192, 2, "bf16"), (16384, 3, "f32")])
+def test_zero_input_gives_exact_zero(torch_cuda, L, B, dtype):
+    """v = 0 gives y = 0 exactly on every single-pass path (fp32 engine, bf16 engine, matrix cores)."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 4
+    w = hi.WORKLOADS[0].with_(B=B, D=D, dims=(L,))
+    p = hi.draw_filter_params(w, seed=11)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    spectra = [hy.filter_gen(params_to_dev(q), (L,)) for q in p]
+    v = torch.zeros((B, D, L), dtype=tdt, device="cuda")
+    xs = [torch.randn((B, D, L), device="cuda").to(tdt) for _ in p]
+    y = hy.operator(v, xs, spectra)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
+
+
+@pytest.mark.parametrize("L,B,dtype", [(4096, 1, "f32"), (8192, 2, "bf16")])
+def test_no_decay_window(torch_cuda, L, B, dtype):
+    """alpha = 0: the window is 1 over the whole length (the longest-reaching filter the method
+    allows); against the oracle."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 4
+    w = hi.WORKLOADS[1].with_(B=B, D=D, dims=(L,), dtype=dtype)
+    v, xs = hi.draw_activations(w, seed=13)
+    params = hi.draw_filter_params(w, seed=13)
+    for q in params:
+        q["alpha"][:] = 0.0
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    spectra = [hy.filter_gen(params_to_dev(q), (L,)) for q in params]
+    y = hy.operator(to_dev(v, tdt), [to_dev(x, tdt) for x in xs], spectra)
+    torch.cuda.synchronize()
+    rows = [(b, d) for b in range(B) for d in range(D)]
+    ref = oracle_rows_1d(w, v, xs, params, rows)
+    got = np.stack([y.float().cpu().numpy()[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"no decay L={L} {dtype}: max rel err {e.max():.3e}")
+    assert e.max() < (FP32_TOL if dtype == "f32" else BF16_TOL)

@@ -123,3 +123,44 @@ def test_operator_workload3_sampled_rows(torch_cuda):
     say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
     assert e.max() < FP32_TOL
     assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("L", [1 << 15, 1 << 16, 1 << 17, 1 << 20])
+def test_fourstep_fftconv_bf16_chunked(torch_cuda, L):
+    """bf16 storage (the intermediate is bf16 too), two chunks of which one is ragged, every
+    multi-pass plan family; against the oracle on the bf16-rounded inputs."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    B, D = 1, 5
+    w = hi.WORKLOADS[2].with_(B=B, D=D, dims=(L,))
+    rng = np.random.default_rng(L % 1013)
+    u = torch.from_numpy(rng.standard_normal((B, D, L)).astype(np.float32)).to(torch.bfloat16)
+    g = torch.from_numpy(rng.standard_normal((B, D, L)).astype(np.float32)).to(torch.bfloat16)
+    p = hi.draw_filter_params(w, seed=5)[0]
+    say(f"four-step fftconv bf16 L={L}")
+    spec = hy.filter_gen(params_to_dev(p), (L,))
+    ws = torch.empty(3 * L * 8, dtype=torch.uint8, device="cuda")
+    y = hy.operator(u.cuda(), [g.cuda()], [spec], ws=ws)
+    torch.cuda.synchronize()
+    h = orc.implicit_filter_1d(p, L)
+    un, gn = u.float().numpy().astype(np.float64), g.float().numpy().astype(np.float64)
+    ref = orc.causal_conv_fft(un, h[None]) * gn
+    e = rel_err_rows(y.float().cpu().numpy(), ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < BF16_TOL, e.max()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_fourstep_zero_input_gives_exact_zero(torch_cuda, dtype):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L, B, D = 1 << 15, 1, 3
+    w = hi.WORKLOADS[0].with_(B=B, D=D, dims=(L,))
+    p = hi.draw_filter_params(w, seed=9)
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    spectra = [hy.filter_gen(params_to_dev(q), (L,)) for q in p]
+    v = torch.zeros((B, D, L), dtype=tdt, device="cuda")
+    xs = [torch.randn((B, D, L), device="cuda").to(tdt) for _ in p]
+    y = hy.operator(v, xs, spectra)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y).item() == 0
