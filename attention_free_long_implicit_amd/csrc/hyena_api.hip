@@ -313,7 +313,7 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
       return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
                                       stream));
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y,
-                                             (float2*)ws, chunk, tw, stream));
+                                             (float2*)ws, chunk, tw, device_mats(), stream));
   }
   return conv_once(B, D, pts, dtype, u, spectrum, gate, y, tw, stream);
 }
@@ -349,7 +349,7 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
                                     tw, stream));
   if (chunk)
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra,
-                                             y, (float2*)ws, chunk, tw, stream));
+                                             y, (float2*)ws, chunk, tw, device_mats(), stream));
   if (use_mfma(dtype, B, pts)) {
     bool aligned = aligned16(v) && aligned16(y);
     for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);

@@ -331,7 +331,9 @@ size_t fs_row_bytes() { return (size_t)(1 << LOG2M) * sizeof(float2); }
 
 template <int LOG2M, bool BF16>
 hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
-                          void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s) {
+                          void* y, float2* I, int chunk, const Twiddles& tw, const void* mats, hipStream_t s) {
+  // bf16 plans with 128-point columns run their column passes on the matrix cores
+  const bool mc = BF16 && mats && fs_cols_mfma_supported(LOG2M);
   using F = FS<LOG2M>;
   using E = typename Store<BF16>::elem;
   using IT = typename Inter<BF16>::T;
@@ -341,12 +343,18 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
   const int groups = (F::M1 / 2) / F::G;
   for (int q0 = 0; q0 < rows; q0 += chunk) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
-    hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                       (const E*)v, (const E*)nullptr, (E*)nullptr, Ib, q0, nq, B, D, tw);
+    if (mc)
+      (void)launch_fs_cols_mfma(LOG2M, 0, false, false, v, nullptr, nullptr, Ib, q0, nq, B, D, mats, s);
+    else
+      hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
+                         (const E*)v, (const E*)nullptr, (E*)nullptr, Ib, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
       hipLaunchKernelGGL((k_fs_rows<LOG2M, 0, BF16>), dim3(groups * nq), dim3(F::TR), 0, s, Ib,
                          (const float2*)spectra[i], (float2*)nullptr, q0, nq, B, tw);
-      if (i + 1 < order)
+      if (mc)
+        (void)launch_fs_cols_mfma(LOG2M, 1, x[i] != nullptr, i + 1 < order, nullptr, x[i], y, Ib, q0, nq, B, D, mats,
+                                  s);
+      else if (i + 1 < order)
         hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, true>), dim3(tiles * nq), dim3(F::TC), 0, s,
                            (const E*)nullptr, (const E*)x[i], (E*)nullptr, Ib, q0, nq, B, D, tw);
       else if (x[i])
@@ -401,12 +409,12 @@ hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int 
 
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, hipStream_t s) {
+                                  const Twiddles& tw, const void* mats, hipStream_t s) {
   switch (log2L) {
 #define X(n)                                                                                  \
   case n:                                                                                     \
-    return bf16 ? fs_conv_launch<n, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s)     \
-                : fs_conv_launch<n, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
+    return bf16 ? fs_conv_launch<n, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s)     \
+                : fs_conv_launch<n, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s);
     HYENA_FS_CASES(X)
 #undef X
   }

@@ -350,6 +350,136 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   }
 }
 
+
+// ---------------------------------------------------------------------------------------------
+// Matrix-core column passes of the multi-pass plan (bf16 storage, 128-point columns: L = 2^15, 2^16).
+// Same operation and data layout as the fp32-VALU column passes in the four-step kernels: the packed
+// row z[n] = u[2n] + i u[2n+1] is an M1 x M2 matrix, n = n2 + M2 n1; a column is a 128-point DFT over
+// n1 (the upper half of the input is zero) whose bin k1 is stored at intermediate row
+// 8 (k1 mod 16) + k1 / 16 (the VALU plan's digit order, which the row pass reads).  Here each column
+// DFT is a dense complex matrix product on the matrix cores: pass C (inverse, keep n1 < 64, gate) and
+// the next order's pass A (forward) chain through registers -- the inverse's accumulators are the
+// forward's inputs, so the forward matrix takes its inputs in accumulator order.  A persistent
+// workgroup keeps the 64 matrix blocks (64 KB) in LDS; each wave owns 32 columns of one row.
+namespace fc {
+constexpr int M1 = 128;
+constexpr int NBLK = 64;   // forward [ob 4][kb 4][cos, sin], then inverse [rb 2][kb 8][cos, sin]
+constexpr int T = 256;
+__host__ __device__ constexpr int pos_of_bin(int k) { return 8 * (k % 16) + k / 16; }
+__device__ __forceinline__ int fwd_blk(int ob, int kb, int cs) { return (ob * 4 + kb) * 2 + cs; }
+__device__ __forceinline__ int inv_blk(int rb, int kb, int cs) { return 32 + (rb * 8 + kb) * 2 + cs; }
+}  // namespace fc
+
+// MODE 0: pass A from u (forward, store the intermediate).  MODE 1: pass C (inverse, gate), then
+// either store y (CHAIN = false) or run the next order's pass A on the gated, bf16-rounded values.
+// u, gate, y are bf16 rows viewed as words (two samples = one packed complex value).
+template <int LOG2M, int MODE, bool GATE, bool CHAIN>
+__global__ void __launch_bounds__(fc::T, 2)
+k_fs_cols_mfma(const uint32_t* __restrict__ u, const uint32_t* __restrict__ gate, uint32_t* __restrict__ y,
+               uint32_t* I, int q0, int nq, int B, int D, const bf16x8* __restrict__ cmats) {
+  using namespace fc;
+  constexpr int M = 1 << LOG2M, M2 = M / M1, CG = M2 / 128, WPR = M / 2;   // words per bf16 row
+  __shared__ bf16x8 Ms[NBLK * 64];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, j = l & 31, h = l >> 5;
+  for (int i = t; i < NBLK * 64; i += T) Ms[i] = cmats[i];
+  __syncthreads();
+  const int nitems = nq * CG, G = gridDim.x;
+  for (int item = xcd_logical_block(blockIdx.x, G); item < nitems; item += G) {
+    const int ql = item / CG, cg = item % CG;
+    const int q = q0 + ql, d = q / B, b = q % B;
+    const size_t row = (size_t)b * D + d;
+    const int c = cg * 128 + 32 * w + j;   // this lane's column n2
+    uint32_t* Irow = I + (size_t)ql * M;
+    // the matrix blocks are read from LDS at each use: an offset the compiler cannot see through keeps
+    // those reads inside the item loop (hoisted, the 64 blocks would need 256 registers)
+    int lz = l;
+    asm volatile("" : "+v"(lz));
+    const bf16x8* Mw = Ms + lz;
+    bf16x8 fr[4], fi[4];                   // forward inputs, K-block kb (accumulator order of n1)
+    if constexpr (MODE == 0) {
+      const uint32_t* zc = u + row * WPR + c;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        uint32_t wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[e] = zc[(size_t)M2 * (32 * (kb >> 1) + acc_row(8 * (kb & 1) + e, h))];
+        split8(wv, fr[kb], fi[kb]);
+      }
+    } else {
+      // inverse over k1 (natural order, K = 16 kb + 8 h + e), outputs n1 < 64 in two row blocks
+      bf16x8 xr[8], xi[8];
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        uint32_t wv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[e] = Irow[(size_t)pos_of_bin(16 * kb + 8 * h + e) * M2 + c];
+        split8(wv, xr[kb], xi[kb]);
+      }
+      if constexpr (!CHAIN) asm volatile("" ::: "memory");   // gate loads stay in their row block
+      const uint32_t* gc = GATE ? gate + row * WPR + c : nullptr;
+      uint32_t* yc = CHAIN ? nullptr : y + row * WPR + c;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x16 dr = {}, di = {};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+          const bf16x8 Cb = Mw[inv_blk(rb, kb, 0) * 64], Sb = Mw[inv_blk(rb, kb, 1) * 64];
+          dr = mfma(Cb, xr[kb], dr);                 // inverse: Yr = C Xr - S Xi, Yi = C Xi + S Xr
+          dr = mfma(Sb, neg8(xi[kb]), dr);
+          di = mfma(Cb, xi[kb], di);
+          di = mfma(Sb, xr[kb], di);
+        }
+        float o_re[16], o_im[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int n1 = 32 * rb + acc_row(v, h);
+          float a = dr[v], bb = di[v];
+          if constexpr (GATE) {
+            const uint32_t g = gc[(size_t)M2 * n1];
+            a *= lo_f32(g);
+            bb *= hi_f32(g);
+          }
+          if constexpr (!CHAIN) yc[(size_t)M2 * n1] = pack2(a, bb);
+          o_re[v] = a;
+          o_im[v] = bb;
+        }
+        if constexpr (!CHAIN) asm volatile("" ::: "memory");   // one row block at a time (register budget)
+        if constexpr (CHAIN) {   // the next order reads the stored (bf16-rounded) value
+          u32x4 rl, rh, il, ih;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            rl[m] = pack2(o_re[2 * m], o_re[2 * m + 1]);
+            il[m] = pack2(o_im[2 * m], o_im[2 * m + 1]);
+            rh[m] = pack2(o_re[8 + 2 * m], o_re[9 + 2 * m]);
+            ih[m] = pack2(o_im[8 + 2 * m], o_im[9 + 2 * m]);
+          }
+          fr[2 * rb] = __builtin_bit_cast(bf16x8, rl);
+          fr[2 * rb + 1] = __builtin_bit_cast(bf16x8, rh);
+          fi[2 * rb] = __builtin_bit_cast(bf16x8, il);
+          fi[2 * rb + 1] = __builtin_bit_cast(bf16x8, ih);
+        }
+      }
+      if constexpr (!CHAIN) continue;
+    }
+    // forward over n1 (64 nonzero inputs) -> 128 bins; bin k1 goes to intermediate row pos_of_bin(k1)
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) {
+      f32x16 dr = {}, di = {};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 Cb = Mw[fwd_blk(ob, kb, 0) * 64], Sb = Mw[fwd_blk(ob, kb, 1) * 64];
+        dr = mfma(Cb, fr[kb], dr);                   // forward: Yr = C Xr + S Xi, Yi = C Xi - S Xr
+        dr = mfma(Sb, fi[kb], dr);
+        di = mfma(Cb, fi[kb], di);
+        di = mfma(Sb, neg8(fr[kb]), di);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        Irow[(size_t)pos_of_bin(32 * ob + acc_row(v, h)) * M2 + c] = pack2(dr[v], di[v]);
+    }
+  }
+}
+
 // Pair-order spectrum: Hc[d][k1][v][lane] = H[k]/N as bf16 (re low, im high), k = k1 + 16 (lane%32)
 // + 512 k3(v, lane/32), for k1 = 0..8 (the convolution kernel mirrors slabs 9..15 from slabs 7..1);
 // H from the natural-order bins 0..L (upper bins by conjugate symmetry).
@@ -421,9 +551,13 @@ uint16_t bf16_rne(float f) {
 }
 }  // namespace
 
-size_t mfma_matrices_count() { return ((size_t)mf::NFIX + 16 * mf::SLAB_TABLE) * 64 * 8; }
+// bf16x8 blocks before the column-pass matrices
+constexpr size_t kColsOffset = ((size_t)mf::NFIX + 16 * mf::SLAB_TABLE) * 64;
 
-void mfma_matrices_host(uint16_t* out) {   // [NFIX][64][8] then [16 slabs][4 mats][4 blocks][64][8]
+size_t mfma_matrices_count() { return (kColsOffset + (size_t)fc::NBLK * 64) * 8; }
+
+// [NFIX][64][8], [16 slabs][4 mats][4 blocks][64][8], then the 64 column-pass blocks [64][8] (bf16)
+void mfma_matrices_host(uint16_t* out) {
   for (int q = 0; q < mf::NFIX; ++q)
     for (int l = 0; l < 64; ++l)
       for (int e = 0; e < 8; ++e) out[(q * 64 + l) * 8 + e] = bf16_rne(fixed_entry(q, l % 32, 8 * (l / 32) + e));
@@ -438,6 +572,64 @@ void mfma_matrices_host(uint16_t* out) {   // [NFIX][64][8] then [16 slabs][4 ma
             const double val = (b == mf::B_CLO || b == mf::B_CHI) ? cos(a) : sin(a);
             o[((((size_t)k1 * mf::NSLABMAT + m) * mf::NBLK + b) * 64 + l) * 8 + e] = bf16_rne((float)val);
           }
+  // column passes (128 points): entry (row i = lane % 32, K = 8 (lane / 32) + e) of each block
+  uint16_t* oc = out + kColsOffset * 8;
+  for (int blk = 0; blk < fc::NBLK; ++blk)
+    for (int l = 0; l < 64; ++l)
+      for (int e = 0; e < 8; ++e) {
+        const int i = l % 32, K = 8 * (l / 32) + e;
+        int k1, n1, cs;
+        if (blk < 32) {   // forward: rows k1, inputs n1 in the inverse's accumulator order
+          const int ob = blk / 8, kb = (blk / 2) % 4;
+          cs = blk % 2;
+          k1 = 32 * ob + i;
+          n1 = 32 * (kb >> 1) + perm_k3(16 * (kb & 1) + K);
+        } else {          // inverse: rows n1 < 64, inputs k1 in natural order
+          const int rb = (blk - 32) / 16, kb = ((blk - 32) / 2) % 8;
+          cs = blk % 2;
+          n1 = 32 * rb + i;
+          k1 = 16 * kb + K;
+        }
+        const double a = kTwoPi * (double)((k1 * n1) % fc::M1) / fc::M1;
+        oc[((size_t)blk * 64 + l) * 8 + e] = bf16_rne((float)(cs == 0 ? cos(a) : sin(a)));
+      }
+}
+
+bool fs_cols_mfma_supported(int log2L) { return log2L == 15 || log2L == 16; }
+
+hipError_t launch_fs_cols_mfma(int log2L, int mode, bool gated, bool chain, const void* u, const void* gate, void* y,
+                               void* I, int q0, int nq, int B, int D, const void* mats, hipStream_t s) {
+  static int n_cu = 0;
+  if (n_cu <= 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+      n_cu = 256;
+  }
+  const bf16x8* cm = (const bf16x8*)mats + kColsOffset;
+  const int items = nq * ((1 << log2L) / fc::M1 / 128);
+  const dim3 grid(items < 2 * n_cu ? items : 2 * n_cu), block(fc::T);
+  const uint32_t* uw = (const uint32_t*)u;
+  const uint32_t* gw = (const uint32_t*)gate;
+  uint32_t* yw = (uint32_t*)y;
+  uint32_t* Iw = (uint32_t*)I;
+#define HYENA_FC(LG, MODE, GT, CH) \
+  hipLaunchKernelGGL((k_fs_cols_mfma<LG, MODE, GT, CH>), grid, block, 0, s, uw, gw, yw, Iw, q0, nq, B, D, cm)
+#define HYENA_FC_ALL(LG)                                  \
+  if (mode == 0) HYENA_FC(LG, 0, false, false);           \
+  else if (chain) HYENA_FC(LG, 1, true, true);            \
+  else if (gated) HYENA_FC(LG, 1, true, false);           \
+  else HYENA_FC(LG, 1, false, false);
+  if (log2L == 15) {
+    HYENA_FC_ALL(15)
+  } else if (log2L == 16) {
+    HYENA_FC_ALL(16)
+  } else {
+    return hipErrorInvalidValue;
+  }
+#undef HYENA_FC_ALL
+#undef HYENA_FC
+  return hipGetLastError();
 }
 
 bool mfma_pair_supported(int log2L, int B) { return log2L == 13 && B % 2 == 0; }

@@ -19,9 +19,10 @@ hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D,
 // x[i] may be NULL for the last order only (no gate).
 bool fourstep_supported(int log2L);
 size_t fourstep_row_bytes(int log2L);
+// mats: the matrix-core table (bf16 L = 2^15, 2^16 run their column passes on the matrix cores), or NULL.
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, hipStream_t s);
+                                  const Twiddles& tw, const void* mats, hipStream_t s);
 hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
                                       const Twiddles& tw, hipStream_t s);
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
@@ -48,6 +49,11 @@ constexpr int kMfmaMaxChain = 8;
 hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void* const* spectra, int order,
                             void* y, const void* mats, int B, int D, const Twiddles& tw, hipStream_t s);
 hipError_t launch_pair_spectrum(const float2* Hnat, void* Hc, int D, hipStream_t s);
+// Matrix-core column passes of the multi-pass plan (bf16, L = 2^15, 2^16).  mode 0: pass A from u;
+// mode 1: pass C with gate (gated) then either the next order's pass A (chain) or the store of y.
+bool fs_cols_mfma_supported(int log2L);
+hipError_t launch_fs_cols_mfma(int log2L, int mode, bool gated, bool chain, const void* u, const void* gate, void* y,
+                               void* I, int q0, int nq, int B, int D, const void* mats, hipStream_t s);
 
 // ---- implicit filter taps
 struct FilterArgs {
