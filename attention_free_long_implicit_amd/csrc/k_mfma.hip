@@ -184,6 +184,14 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
 #pragma unroll
     for (int e = 0; e < 8; ++e) V[e] = *reinterpret_cast<const u32x4*>(src + 1024 * e);
   }
+  // Order-independent operands, loaded once right behind the first input (inside the order loop they
+  // would queue behind that order's spectrum loads): the fixed radix-16 matrices and the per-lane
+  // twiddles W_1024^{j k(v)}, k(v) = row of accumulator v.
+  const int l0 = threadIdx.x & 63;
+  const bf16x8 m1f = mats[M1F * 64 + l0], m1r = mats[M1I_R * 64 + l0], m1i = mats[M1I_I * 64 + l0];
+  float2 p2[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) p2[v] = twiddle<10>(tw, uint32_t((l0 & 31) * acc_row(v, l0 >> 5)));
 
   for (int ord = 0; ord < ch.order; ++ord) {
   // lane constants derived from an opaque copy of the thread id, so nothing is hoisted across orders
@@ -203,23 +211,17 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF2 * NBLK * 64, Ma);
   load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF3 * NBLK * 64, Mb);
   // Filter spectrum: only slabs 0..8 are stored.  h is real, so H[N - k] = conj(H[k]); bin N - k of
-  // slab k1 > 8 is register 15 - v of lane 63 - l in slab 16 - k1, read mirrored and conjugated (sign of
-  // the imaginary half flipped).
+  // slab k1 > 8 is register 15 - v of lane 63 - l in slab 16 - k1, read mirrored; the conjugation (sign
+  // of the imaginary half) is applied where the value is used, so the load stays in flight until then.
   uint32_t hw[16];
   auto load_spectrum = [&](int k1) {
     const bool mirror = k1 > 8;
     const uint32_t* hp = Hc + ((size_t)d * PAIR_SLABS + (mirror ? 16 - k1 : k1)) * 16 * 64 + (mirror ? 63 - l : l);
-    const uint32_t flip = mirror ? 0x80000000u : 0u;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) hw[v] = hp[(mirror ? 15 - v : v) * 64] ^ flip;
+    for (int v = 0; v < 16; ++v) hw[v] = hp[(mirror ? 15 - v : v) * 64];
   };
   load_spectrum(w);
-  // per-lane W_1024^{j k(v)}, k(v) = row of accumulator v
-  float2 p2[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) p2[v] = twiddle<10>(tw, uint32_t(j * acc_row(v, h)));
   {
-    const bf16x8 m1f = mats[M1F * 64 + l];
     static_for<8>([&](auto tt) {
       constexpr int TT = tt.value;
       const f32x16 z = {};
@@ -261,7 +263,9 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
     // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N in this exact order.
     // pass 3': data on A (rows k2 = j, input k3 in accumulator order), matrix on B -> lane = n3,
     // registers = k2
-    pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, unpack_c(hw[v])); }, xr_lo, xr_hi, xi_lo, xi_hi);
+    const uint32_t flip = k1 > 8 ? 0x80000000u : 0u;
+    pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, unpack_c(hw[v] ^ flip)); }, xr_lo, xr_hi, xi_lo,
+                  xi_hi);
     if (it < 3) load_spectrum(k1 + 4);
     f32x16 er, ei;
     dft32<true, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
@@ -288,7 +292,6 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
     }
   }
 
-  const bf16x8 m1r = mats[M1I_R * 64 + l], m1i = mats[M1I_I * 64 + l];
   __syncthreads();
 
   // ---------------- pass 1': tiles t, column c = c0 + t, K = k1 (slab index), outputs n1 = 4h + e

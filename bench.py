@@ -143,6 +143,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device copy-bandwidth probe")
+    ap.add_argument("--cold-steps", type=int, default=50,
+                    help="after the timed region, this many more steps, each after a scratch write that evicts the "
+                         "256 MB memory-side cache, timed one by one (reported as cold_cache; 0 skips them)")
+    ap.add_argument("--evict-mb", type=int, default=1024, help="size of that scratch write")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -196,8 +200,29 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = np.full(args.steps, ev0.elapsed_time(ev1) / args.steps)
-
     ms_per_step = 1e3 * wall / args.steps
+
+    # Back-to-back steps reread the same buffers, part of which the memory-side cache still holds.  The
+    # cold figure evicts it before every step (a scratch write several times its size) and times each
+    # step by its own events (which add a few microseconds per step).
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(args.evict_mb << 18, dtype=torch.float32, device=dev)
+        marks = []
+        torch.cuda.synchronize()
+        for k in range(args.cold_steps):
+            scratch.fill_(float(k))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            hy.operator(vd, xd, spectra, y=y, ws=ws)
+            e1.record(stream)
+            marks.append((e0, e1))
+        torch.cuda.synchronize()
+        cold_ms = float(np.median([a.elapsed_time(b) for a, b in marks]))
+        del scratch
+        cold = {"ms_per_step": cold_ms, "steps": args.cold_steps, "evict_mb": args.evict_mb,
+                "value": w.tokens_channels / (cold_ms / 1e3),
+                "hbm_frac_alg": algorithmic_bytes_per_order(w) * w.order / (cold_ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
     T = w.tokens_channels
     value = T / (ms_per_step / 1e3)
     alg_step = algorithmic_bytes_per_order(w) * w.order
@@ -221,6 +246,8 @@ def main():
         "event_ms_per_step": float(np.mean(step_ms)),
         "filter_gen_ms": filter_gen_ms,
     }
+    if cold is not None:
+        out["cold_cache"] = cold
     key = kernel_key(w)
     if uses_matrix_cores(w) and w.order <= 8:
         # the whole step is one launch of the matrix-core kernel: all orders, u_i kept on chip
