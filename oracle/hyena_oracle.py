@@ -26,19 +26,27 @@ What is computed (y = x_N * (h_N conv (... x_1 * (h_1 conv v)))):
   * 3-D: non-causal "same" linear convolution by zero-padding every axis
     to twice its size                                                      [HyenaND, method: native N-D
                                                                            convolution; boundary handling]
+  * circular (periodic) convolution, no padding, 1-D and 3-D              [HyenaND, boundary handling:
+                                                                           circular convolutions for
+                                                                           periodic physical systems]
 
 Readings where the pages are silent (each also listed in the design notes):
   order N = number of filters = number of gates (listing chunks len(filters)+1);
   phi(t) = [sin(2 pi f t/L) for f=1..F/2] + [cos(2 pi f t/L) for f=1..F/2];
   time normalised as t/L for both features and window; one alpha per (order, channel);
   3-D features: per axis 16 frequencies x {sin, cos} of r/n for signed offsets r in [-(n-1), n-1];
-  3-D window exp(-alpha |r/n|_2).
+  3-D window exp(-alpha |r/n|_2);
+  circular mode: indices taken modulo the grid, no padding; 1-D keeps the causal taps t = 0..L-1
+  (one period), 3-D evaluates the filter on the centred offsets r in [-n/2, n/2)^3, placed at r mod n.
 
 Pins (each function is checked against something other than itself in
 tests/test_oracle.py): direct sum vs FFT form, numpy.convolve special case,
 first-order-recurrence and geometric-sum closed forms, delta and unit-delay
 filters, linearity, causality, 3-D brute force, separable 3-D products,
-hand-computed worked examples under tests/golden/.
+hand-computed worked examples under tests/golden/; circular mode: direct sum vs
+FFT, cyclic shifts by delta filters, numpy.convolve when nothing wraps, the
+geometric-filter eigenvalue closed form, 3-D brute force and separable products,
+and the circular 3-D filter against the linear one at shared offsets.
 """
 from __future__ import annotations
 
@@ -51,7 +59,8 @@ __all__ = [
     "positional_features_1d", "positional_features_3d", "silu", "filter_network",
     "implicit_filter_1d", "implicit_filter_3d", "causal_conv_direct", "causal_conv_fft",
     "linear_conv3d_direct", "linear_conv3d_fft", "hyena_operator_rows", "hyena_operator_3d",
-    "rel_l2_per_row",
+    "rel_l2_per_row", "filter_offsets_3d_circular", "implicit_filter_3d_circular", "circular_conv_direct",
+    "circular_conv_fft", "circular_conv3d_direct", "circular_conv3d_fft",
 ]
 
 
@@ -151,6 +160,30 @@ def implicit_filter_3d(p: dict, n: int, channels: Optional[Sequence[int]] = None
     return h.reshape(-1, m, m, m)
 
 
+def filter_offsets_3d_circular(n: int) -> np.ndarray:
+    """One period of signed offsets, centred: r in [-n/2, n/2)^3, x slowest: [n^3, 3] int64."""
+    a = np.arange(-(n // 2), n - n // 2, dtype=np.int64)
+    X, Y, Z = np.meshgrid(a, a, a, indexing="ij")
+    return np.stack([X.ravel(), Y.ravel(), Z.ravel()], axis=1)
+
+
+def implicit_filter_3d_circular(p: dict, n: int, channels: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Periodic 3-D filter: h[d, i, j, k] = g(r) exp(-alpha_d |r/n|_2) at the centred offset r with
+    r = (i, j, k) mod n: [D_sel, n, n, n] float64 (same network and window as the zero-padded mode)."""
+    F = np.asarray(p["W1"]).shape[1]
+    r = filter_offsets_3d_circular(n)
+    g = filter_network(positional_features_3d(r, n, F), p, channels)    # [n^3, D_sel]
+    alpha = np.asarray(p["alpha"], np.float64)
+    if channels is not None:
+        alpha = alpha[np.asarray(channels, dtype=np.int64)]
+    rad = np.sqrt(np.sum((r.astype(np.float64) / n) ** 2, axis=1))
+    vals = g.T * np.exp(-np.outer(alpha, rad))                          # [D_sel, n^3]
+    h = np.zeros((vals.shape[0], n, n, n), dtype=np.float64)
+    ri = r % n
+    h[:, ri[:, 0], ri[:, 1], ri[:, 2]] = vals
+    return h
+
+
 # --------------------------------------------------------------------------------------------
 # long convolution  [EulerStack, "how it works" 2: FFT, pointwise product, inverse FFT = convolution;
 #                    HyenaND, boundary handling: zero-pad to double size to avoid wrap-around]
@@ -215,19 +248,71 @@ def linear_conv3d_fft(u: np.ndarray, h: np.ndarray) -> np.ndarray:
     return np.fft.irfftn(U * Hs, s=(m, m, m), axes=axes)[..., :n, :n, :n]
 
 
+def circular_conv_direct(u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """c[t] = sum_{s=0..L-1} h[(t-s) mod L] u[s]  (periodic boundary, the definition; O(L^2))."""
+    u = np.asarray(u, np.float64)
+    h = np.asarray(h, np.float64)
+    L = u.shape[-1]
+    s = np.arange(L)
+    out = np.zeros(np.broadcast_shapes(u.shape, h.shape), dtype=np.float64)
+    for t in range(L):
+        out[..., t] = np.sum(h[..., (t - s) % L] * u, axis=-1)
+    return out
+
+
+def circular_conv_fft(u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """Same result through the convolution theorem on the L-point grid itself (no padding)."""
+    u = np.asarray(u, np.float64)
+    h = np.asarray(h, np.float64)
+    L = u.shape[-1]
+    return np.fft.irfft(np.fft.rfft(u) * np.fft.rfft(h), L)
+
+
+def circular_conv3d_direct(u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """c[p] = sum_{q in [0,n)^3} h[(p-q) mod n] u[q] (periodic on every axis; brute force).
+
+    u, h: [n, n, n]; h indexed by offset mod n.
+    """
+    u = np.asarray(u, np.float64)
+    h = np.asarray(h, np.float64)
+    n = u.shape[0]
+    q = np.arange(n)
+    c = np.zeros_like(u)
+    for px in range(n):
+        for py in range(n):
+            for pz in range(n):
+                hx = (px - q) % n
+                hy = (py - q) % n
+                hz = (pz - q) % n
+                c[px, py, pz] = np.sum(h[hx[:, None, None], hy[None, :, None], hz[None, None, :]] * u)
+    return c
+
+
+def circular_conv3d_fft(u: np.ndarray, h: np.ndarray) -> np.ndarray:
+    """Same result via 3-D real FFTs on the n^3 grid itself; leading axes are batch axes."""
+    u = np.asarray(u, np.float64)
+    h = np.asarray(h, np.float64)
+    n = u.shape[-1]
+    axes = (-3, -2, -1)
+    return np.fft.irfftn(np.fft.rfftn(u, axes=axes) * np.fft.rfftn(h, axes=axes), s=(n, n, n), axes=axes)
+
+
 # --------------------------------------------------------------------------------------------
 # the operator  [Hyena note, step 3 equation and listing ``hyena_operator``:
 #                v, x_1..x_N chunks; for (h_i, x_i): v <- (h_i conv v) * x_i]
 # --------------------------------------------------------------------------------------------
 
 def hyena_operator_rows(v: np.ndarray, xs: Sequence[np.ndarray], hs: Sequence[np.ndarray],
-                        direct: bool = False) -> np.ndarray:
-    """Order-N recurrence on a batch of independent rows.
+                        direct: bool = False, circular: bool = False) -> np.ndarray:
+    """Order-N recurrence on a batch of independent rows (causal, or periodic with ``circular``).
 
     v, xs[i]: [..., R, L] (any float dtype, taken as exact values); hs[i]: [R, L] filter per row
     (broadcast over leading axes).  Returns y = u_N as float64.
     """
-    conv = causal_conv_direct if direct else causal_conv_fft
+    if circular:
+        conv = circular_conv_direct if direct else circular_conv_fft
+    else:
+        conv = causal_conv_direct if direct else causal_conv_fft
     u = np.asarray(v, np.float64)
     for h, x in zip(hs, xs):
         u = np.asarray(x, np.float64) * conv(u, h)
@@ -235,17 +320,19 @@ def hyena_operator_rows(v: np.ndarray, xs: Sequence[np.ndarray], hs: Sequence[np
 
 
 def hyena_operator_3d(v: np.ndarray, xs: Sequence[np.ndarray], hs: Sequence[np.ndarray],
-                      direct: bool = False) -> np.ndarray:
-    """Order-N recurrence with non-causal zero-padded 3-D convolutions.
+                      direct: bool = False, circular: bool = False) -> np.ndarray:
+    """Order-N recurrence with non-causal 3-D convolutions: zero-padded, or periodic with ``circular``.
 
-    v, xs[i]: [C, n, n, n]; hs[i]: [C, 2n-1, 2n-1, 2n-1].
+    v, xs[i]: [C, n, n, n]; hs[i]: [C, 2n-1, 2n-1, 2n-1] (zero-padded) or [C, n, n, n] (periodic).
     """
     u = np.asarray(v, np.float64)
+    direct_fn = circular_conv3d_direct if circular else linear_conv3d_direct
+    fft_fn = circular_conv3d_fft if circular else linear_conv3d_fft
     for h, x in zip(hs, xs):
         if direct:
-            c = np.stack([linear_conv3d_direct(u[j], h[j]) for j in range(u.shape[0])])
+            c = np.stack([direct_fn(u[j], h[j]) for j in range(u.shape[0])])
         else:
-            c = linear_conv3d_fft(u, h)
+            c = fft_fn(u, h)
         u = np.asarray(x, np.float64) * c
     return u
 

@@ -310,3 +310,139 @@ def test_rel_l2_per_row():
     ref = np.array([[[3.0, 4.0]], [[1.0, 0.0]]])
     y = ref + np.array([[[0.3, 0.4]], [[0.0, 0.5]]])
     np.testing.assert_allclose(orc.rel_l2_per_row(y, ref), [0.1, 0.5])
+
+
+# ---------------------------------------------------------------- circular (periodic) mode
+
+def test_golden_circular_conv(golden):
+    g = golden["circular_conv_4"]
+    np.testing.assert_array_equal(orc.circular_conv_direct(g["u"], g["h"]), g["c"])
+    np.testing.assert_allclose(orc.circular_conv_fft(np.array(g["u"], float), np.array(g["h"], float)), g["c"],
+                               rtol=0, atol=1e-13)
+
+
+def test_golden_conv3d_circular_point_sources(golden):
+    g = golden["conv3d_circular_point_sources_n2"]
+    n = g["n"]
+    digit = np.array([2.0, 1.0])          # index 0 <-> offset 0, index 1 <-> offset -1
+    h = 100 * digit[:, None, None] + 10 * digit[None, :, None] + digit[None, None, :]
+    for key, q in (("delta_at_000", (0, 0, 0)), ("delta_at_111", (1, 1, 1))):
+        u = np.zeros((n, n, n))
+        u[q] = 1.0
+        np.testing.assert_array_equal(orc.circular_conv3d_direct(u, h), g[key])
+        np.testing.assert_allclose(orc.circular_conv3d_fft(u, h), g[key], rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("L", [5, 16, 64])
+def test_circular_direct_matches_fft(L):
+    rng = np.random.default_rng(L)
+    u = rng.standard_normal((3, L))
+    h = rng.standard_normal((3, L))
+    np.testing.assert_allclose(orc.circular_conv_fft(u, h), orc.circular_conv_direct(u, h), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("k", [0, 1, 7, 31])
+def test_circular_delta_filter_is_cyclic_shift(k):
+    L = 32
+    u = np.random.default_rng(k).standard_normal(L)
+    h = np.zeros(L)
+    h[k] = 1.0
+    want = np.roll(u, k)                     # c[t] = u[(t - k) mod L]
+    np.testing.assert_array_equal(orc.circular_conv_direct(u, h), want)
+    np.testing.assert_allclose(orc.circular_conv_fft(u, h), want, rtol=0, atol=1e-13)
+
+
+def test_circular_equals_linear_when_nothing_wraps():
+    # u and h supported on [0, L/2): no product lands beyond L-1, so the periodic sum is the plain one
+    L = 64
+    rng = np.random.default_rng(3)
+    u = np.zeros(L)
+    h = np.zeros(L)
+    u[: L // 2] = rng.standard_normal(L // 2)
+    h[: L // 2] = rng.standard_normal(L // 2)
+    want = np.convolve(u[: L // 2], h[: L // 2])             # length L - 1
+    got = orc.circular_conv_direct(u, h)
+    np.testing.assert_allclose(got[: L - 1], want, rtol=0, atol=1e-12)
+    assert abs(got[L - 1]) < 1e-12
+
+
+@pytest.mark.parametrize("k", [0, 3, 10])
+def test_circular_geometric_filter_eigenvalue(k):
+    # h[t] = r^t on one period: a sinusoid of frequency k is an eigenvector of the periodic convolution with
+    # eigenvalue H_k = sum_t r^t w^t = (1 - r^L) / (1 - r w), w = exp(-2 pi i k / L) (geometric sum).
+    L, r, phase = 24, 0.8, 0.4
+    t = np.arange(L)
+    h = r ** t
+    u = np.cos(2 * math.pi * k * t / L + phase)
+    w = np.exp(-2j * math.pi * k / L)
+    Hk = (1 - r ** L) / (1 - r * w)
+    want = np.real(Hk * np.exp(1j * (2 * math.pi * k * t / L + phase)))
+    np.testing.assert_allclose(orc.circular_conv_direct(u, h), want, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(orc.circular_conv_fft(u, h), want, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [3, 4])
+def test_circular3d_brute_force_matches_fft(n):
+    rng = np.random.default_rng(n)
+    u = rng.standard_normal((n, n, n))
+    h = rng.standard_normal((n, n, n))
+    np.testing.assert_allclose(orc.circular_conv3d_fft(u, h), orc.circular_conv3d_direct(u, h), rtol=0, atol=1e-12)
+
+
+def test_circular3d_delta_is_roll():
+    n = 4
+    u = np.random.default_rng(9).standard_normal((n, n, n))
+    h = np.zeros((n, n, n))
+    h[1, 3, 2] = 1.0
+    want = np.roll(u, (1, 3, 2), axis=(0, 1, 2))
+    np.testing.assert_array_equal(orc.circular_conv3d_direct(u, h), want)
+    np.testing.assert_allclose(orc.circular_conv3d_fft(u, h), want, rtol=0, atol=1e-13)
+
+
+def test_circular3d_separable_is_product_of_1d():
+    n = 4
+    rng = np.random.default_rng(11)
+    a, b, c = (rng.standard_normal(n) for _ in range(3))
+    f, g, k = (rng.standard_normal(n) for _ in range(3))
+    u = np.einsum("i,j,k->ijk", a, b, c)
+    h = np.einsum("i,j,k->ijk", f, g, k)
+    want = np.einsum("i,j,k->ijk", orc.circular_conv_direct(a, f), orc.circular_conv_direct(b, g),
+                     orc.circular_conv_direct(c, k))
+    np.testing.assert_allclose(orc.circular_conv3d_direct(u, h), want, rtol=0, atol=1e-12)
+
+
+def test_filter3d_circular_matches_linear_at_shared_offsets():
+    # the periodic filter is the same network and window, evaluated on one centred period of offsets
+    n = 6
+    rng = np.random.default_rng(5)
+    p = _params(96, 64, 3, rng)
+    hc = orc.implicit_filter_3d_circular(p, n)
+    hl = orc.implicit_filter_3d(p, n)                       # offsets [-(n-1), n-1]^3 at index r + n - 1
+    for r in [(0, 0, 0), (-3, 2, 1), (2, -1, -3), (-3, -3, -3), (1, 2, 2)]:
+        ci = tuple(x % n for x in r)
+        li = tuple(x + n - 1 for x in r)
+        np.testing.assert_allclose(hc[(slice(None),) + ci], hl[(slice(None),) + li], rtol=1e-13, atol=0)
+    offs = orc.filter_offsets_3d_circular(n)
+    assert offs.shape == (n ** 3, 3) and offs.min() == -(n // 2) and offs.max() == n - n // 2 - 1
+    assert len({tuple(x % n) for x in offs}) == n ** 3
+
+
+def test_operator_circular_direct_vs_fft_and_delta():
+    rng = np.random.default_rng(21)
+    L = 32
+    v = rng.standard_normal((2, L))
+    xs = [rng.standard_normal((2, L)) for _ in range(2)]
+    hs = [rng.standard_normal((2, L)) for _ in range(2)]
+    y_d = orc.hyena_operator_rows(v, xs, hs, direct=True, circular=True)
+    y_f = orc.hyena_operator_rows(v, xs, hs, circular=True)
+    np.testing.assert_allclose(y_f, y_d, rtol=0, atol=1e-12)
+    delta = np.zeros((2, L))
+    delta[:, 0] = 1.0
+    np.testing.assert_allclose(orc.hyena_operator_rows(v, xs, [delta, delta], circular=True), xs[1] * xs[0] * v,
+                               rtol=0, atol=1e-14)
+    n = 3
+    v3 = rng.standard_normal((2, n, n, n))
+    x3 = [rng.standard_normal((2, n, n, n)) for _ in range(2)]
+    h3 = [rng.standard_normal((2, n, n, n)) for _ in range(2)]
+    np.testing.assert_allclose(orc.hyena_operator_3d(v3, x3, h3, circular=True),
+                               orc.hyena_operator_3d(v3, x3, h3, direct=True, circular=True), rtol=0, atol=1e-12)
