@@ -228,7 +228,7 @@ def spectrum_export(spectrum, point_shape: Sequence[int], D: int, mode: Optional
     torch = _torch()
     mode = mode_for(len(point_shape)) if mode is None else mode
     if len(point_shape) == 1:
-        shape = (D, point_shape[0] + 1)
+        shape = (D, (point_shape[0] // 2 if mode == CIRCULAR else point_shape[0]) + 1)
     else:
         nx, ny, nz = point_shape
         shape = (D, 2 * nx, 2 * ny, nz + 1)

@@ -76,7 +76,17 @@ size_t elem_bytes(int dtype) { return dtype == HYENA_BF16 ? 2 : 4; }
 
 // Shape checks shared by every entry point.  On success *points = elements per (b, d) row.
 int check_dims(hyena_dims dims, int mode, int64_t* points) {
-  if (mode == HYENA_CIRCULAR) return HYENA_EUNSUPPORTED;
+  if (mode == HYENA_CIRCULAR) {
+    // periodic boundary: 1-D rows of L = 2^11 .. 2^15 samples (one packed L/2-point transform in LDS)
+    if (dims.ndim != 1 && dims.ndim != 3) return HYENA_EINVAL;
+    for (int a = 0; a < dims.ndim; ++a)
+      if (dims.n[a] <= 0) return HYENA_EINVAL;
+    if (dims.ndim == 3) return HYENA_EUNSUPPORTED;
+    const int64_t L = dims.n[0];
+    if (!is_pow2(L) || L < (1 << 11) || !single_pass_supported(log2i(L) - 1)) return HYENA_EUNSUPPORTED;
+    *points = L;
+    return HYENA_OK;
+  }
   if (mode == HYENA_CAUSAL) {
     if (dims.ndim != 1) return HYENA_EINVAL;
     const int64_t L = dims.n[0];
@@ -106,13 +116,19 @@ int hip_status(hipError_t e) { return e == hipSuccess ? HYENA_OK : HYENA_EHIP; }
 
 bool is_multipass(int64_t L) { return !single_pass_supported(log2i(L)); }
 
+// 1-D periodic rows of L samples run the single-pass engine on L/2 packed points.
+bool circular1d(int mode) { return mode == HYENA_CIRCULAR; }
+int circular_log2(int64_t L) { return log2i(L) - 1; }
+
 // Intermediate bytes per (b, d) row / volume for the multi-pass plans (0: single pass).
 size_t row_intermediate_bytes(int mode, int64_t pts) {
   if (mode == HYENA_LINEAR) return conv3d_volume_bytes();
+  if (circular1d(mode)) return 0;
   return is_multipass(pts) ? fourstep_row_bytes(log2i(pts)) : 0;
 }
 size_t filter_intermediate_bytes(int mode, int64_t pts) {
   if (mode == HYENA_LINEAR) return conv3d_filter_volume_bytes();
+  if (circular1d(mode)) return 0;
   return is_multipass(pts) ? fourstep_row_bytes(log2i(pts)) : 0;
 }
 size_t taps_per_channel(int mode, int64_t pts) { return mode == HYENA_LINEAR ? conv3d_taps_per_channel() : (size_t)pts; }
@@ -200,6 +216,7 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   if (mode == HYENA_LINEAR) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel();
+  else if (circular1d(mode)) *bytes = (size_t)D * (size_t)(pts / 2) * sizeof(float2);
   else *bytes = (size_t)D * (size_t)pts * sizeof(float2) + (has_pair_copy(pts) ? (size_t)D * mfma_pair_spectrum_bytes_per_channel() : 0);
   return HYENA_OK;
 }
@@ -233,7 +250,7 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
-  if (p->H != 64 || p->F != (mode == HYENA_CAUSAL ? 64 : 96)) return HYENA_EUNSUPPORTED;
+  if (p->H != 64 || p->F != (dims.ndim == 1 ? 64 : 96)) return HYENA_EUNSUPPORTED;
   const size_t hbytes = (size_t)p->D * taps_per_channel(mode, pts) * sizeof(float);
   const int64_t L = pts;
   const size_t row_b = filter_intermediate_bytes(mode, pts);
@@ -269,6 +286,8 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
     return hip_status(launch_spectrum3d(h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream));
   }
   if ((st = hip_status(launch_filter1d(a, (int)L, h, stream)))) return st;
+  if (circular1d(mode))
+    return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, p->D, tw, stream, 1));
   if (multi)
     return hip_status(launch_spectrum1d_fourstep(log2i(L), h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw,
                                                  stream));
@@ -315,6 +334,9 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y,
                                              (float2*)ws, chunk, tw, device_mats(), stream));
   }
+  if (circular1d(mode))
+    return hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, u, gate, y,
+                                           (const float2*)spectrum, (int)B, (int)D, tw, stream, 1));
   return conv_once(B, D, pts, dtype, u, spectrum, gate, y, tw, stream);
 }
 
@@ -350,6 +372,16 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   if (chunk)
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra,
                                              y, (float2*)ws, chunk, tw, device_mats(), stream));
+  if (circular1d(mode)) {
+    const void* cur = v;
+    for (int i = 0; i < order; ++i) {
+      if ((st = hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, cur, x[i], y,
+                                                (const float2*)spectra[i], (int)B, (int)D, tw, stream, 1))))
+        return st;
+      cur = y;
+    }
+    return HYENA_OK;
+  }
   if (use_mfma(dtype, B, pts)) {
     bool aligned = aligned16(v) && aligned16(y);
     for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);
@@ -370,6 +402,8 @@ int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spec
   if (st) return st;
   if (mode == HYENA_LINEAR)
     return hip_status(launch_export3d((const float2*)spectrum, (float2*)H, (int)D, stream));
+  if (circular1d(mode))
+    return hip_status(launch_export1d_single(circular_log2(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
   if (is_multipass(pts))
     return hip_status(launch_export1d_fourstep(log2i(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
   return hip_status(launch_export1d_single(log2i(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));

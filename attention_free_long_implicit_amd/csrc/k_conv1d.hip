@@ -1,4 +1,5 @@
-// Single-pass kernels for 1-D causal long convolution, L <= 16384 (the transform lives in LDS):
+// Single-pass kernels for 1-D long convolution whose transform lives in LDS: causal for L <= 16384,
+// periodic (circular) for L <= 32768:
 //   k_conv1d       y = gate * (h conv u)[0:L) for every (b, d) row, one workgroup per row
 //   k_spectrum1d   filter spectrum in engine order from time-domain taps h[d, 0:L)
 //   k_export1d     engine-order spectrum -> natural-order bins H[d, 0..L] (testing aid)
@@ -12,6 +13,11 @@
 // z[n] = u[2n] + i u[2n+1] (n < L/2; zero above), so the M = L point complex transform of z gives
 // the 2L-point real transform after the mirrored-bin split (spectral_pair).  The product of the
 // zero-padded spectra is the linear convolution; keeping outputs [0, L) makes it causal.
+//
+// Periodic boundary (FULL = true; HyenaND summary, boundary handling: circular convolution for
+// periodic systems, no padding): a row of L = 2M samples fills all M packed values, so the same
+// M-point transform and split give the L-point real transform; the product is the circular
+// convolution and every output is kept.  The filter spectrum is that of the L taps, unpadded.
 //
 // Spectrum layout ("engine order"), per channel: Hs[slot * T + t], slot < 2 RP, holding Hs = H/(4L)
 // at the bin of register `slot` of thread t in the fused pass; thread T-1, slot 0 holds the two
@@ -38,7 +44,7 @@ struct Single {
   static_assert(RL::S == M && NP::TN == T, "plan");
 };
 
-template <int LOG2M, bool BF16, bool GATE>
+template <int LOG2M, bool BF16, bool GATE, bool FULL>
 __global__ void __launch_bounds__(Single<LOG2M>::T, 4)
 k_conv1d(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* gate,
          typename Store<BF16>::elem* y, const float2* __restrict__ Hs, int B, int D, Twiddles tw) {
@@ -51,13 +57,15 @@ k_conv1d(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* 
   const int r = xcd_logical_block(blockIdx.x, B * D);
   const int d = r / B, b = r % B;
   const size_t row = (size_t)b * D + d;
-  const auto* urow = u + row * M;
+  constexpr int RS = FULL ? 2 * M : M;        // samples per row
+  constexpr int NIN = FULL ? R0 : R0 / 2;     // nonzero inputs (and kept outputs) per first-pass butterfly
+  const auto* urow = u + row * RS;
   float2 x[E];
   static_for<C::NB0>([&](auto ii) {
     constexpr int i = ii.value;
-    static_for<R0 / 2>([&](auto m) { x[i * R0 + m.value] = St::load2(urow + 2 * (t + T * i + m.value * Q0)); });
+    static_for<NIN>([&](auto m) { x[i * R0 + m.value] = St::load2(urow + 2 * (t + T * i + m.value * Q0)); });
   });
-  En::template forward_to_last<true>(x, lds, tw, t);
+  En::template forward_to_last<!FULL>(x, lds, tw, t);
   const auto P = C::NP::of(t);
   En::fwd_last(x, lds, P.betaA, P.betaB);
 
@@ -69,13 +77,13 @@ k_conv1d(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* 
   }
 
   En::inv_last(x, lds, P.betaA, P.betaB);
-  En::template inverse_from_last<true>(x, lds, tw, t);
+  En::template inverse_from_last<!FULL>(x, lds, tw, t);
 
-  auto* yrow = y + row * M;
-  const auto* grow = GATE ? gate + row * M : nullptr;
+  auto* yrow = y + row * RS;
+  const auto* grow = GATE ? gate + row * RS : nullptr;
   static_for<C::NB0>([&](auto ii) {
     constexpr int i = ii.value;
-    static_for<R0 / 2>([&](auto m) {
+    static_for<NIN>([&](auto m) {
       const int j = t + T * i + m.value * Q0;
       float2 v = x[i * R0 + m.value];
       if constexpr (GATE) {
@@ -87,8 +95,9 @@ k_conv1d(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* 
   });
 }
 
-// Filter spectrum in engine order: Hs = DFT_{2L}(h || 0) / (4L).
-template <int LOG2M>
+// Filter spectrum in engine order: Hs = DFT_{2M}(h || 0) / (4M) from M taps, or (FULL) Hs = DFT_{2M}(h) / (4M)
+// from 2M taps (periodic boundary).
+template <int LOG2M, bool FULL>
 __global__ void __launch_bounds__(Single<LOG2M>::T)
 k_spectrum1d(const float* __restrict__ h, float2* __restrict__ Hs, Twiddles tw) {
   using C = Single<LOG2M>;
@@ -97,15 +106,15 @@ k_spectrum1d(const float* __restrict__ h, float2* __restrict__ Hs, Twiddles tw) 
   __shared__ float2 lds[En::LDS_ELEMS];
   const int t = threadIdx.x;
   const int d = blockIdx.x;
-  const float* hrow = h + (size_t)d * M;
+  const float* hrow = h + (size_t)d * (FULL ? 2 * M : M);
   float2 x[E];
   static_for<C::NB0>([&](auto ii) {
     constexpr int i = ii.value;
-    static_for<R0 / 2>([&](auto m) {
+    static_for<FULL ? R0 : R0 / 2>([&](auto m) {
       x[i * R0 + m.value] = Store<false>::load2(hrow + 2 * (t + T * i + m.value * Q0));
     });
   });
-  En::template forward_to_last<true>(x, lds, tw, t);
+  En::template forward_to_last<!FULL>(x, lds, tw, t);
   const auto P = C::NP::of(t);
   En::fwd_last(x, lds, P.betaA, P.betaB);
   const float sc = 1.0f / (8.0f * M);
@@ -140,28 +149,35 @@ __global__ void k_export1d(const float2* __restrict__ Hs, float2* __restrict__ H
 
 // ------------------------------------------------------------------ host launchers
 namespace {
-template <int LOG2M>
-hipError_t conv1d_launch(int bf16, bool gate, const void* u, const void* g, void* y, const float2* Hs, int B,
-                         int D, const Twiddles& tw, hipStream_t s) {
+template <int LOG2M, bool BF16, bool FULL>
+void conv1d_launch_t(bool gate, const void* u, const void* g, void* y, const float2* Hs, int B, int D,
+                     const Twiddles& tw, hipStream_t s) {
+  using E = typename Store<BF16>::elem;
   dim3 grid(B * D), block(Single<LOG2M>::T);
-  if (bf16) {
-    using E = uint16_t;
-    if (gate)
-      hipLaunchKernelGGL((k_conv1d<LOG2M, true, true>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs, B, D, tw);
-    else
-      hipLaunchKernelGGL((k_conv1d<LOG2M, true, false>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs, B, D, tw);
-  } else {
-    using E = float;
-    if (gate)
-      hipLaunchKernelGGL((k_conv1d<LOG2M, false, true>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs, B, D, tw);
-    else
-      hipLaunchKernelGGL((k_conv1d<LOG2M, false, false>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs, B, D, tw);
-  }
+  if (gate)
+    hipLaunchKernelGGL((k_conv1d<LOG2M, BF16, true, FULL>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs,
+                       B, D, tw);
+  else
+    hipLaunchKernelGGL((k_conv1d<LOG2M, BF16, false, FULL>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs,
+                       B, D, tw);
+}
+template <int LOG2M>
+hipError_t conv1d_launch(int bf16, bool gate, bool full, const void* u, const void* g, void* y, const float2* Hs,
+                         int B, int D, const Twiddles& tw, hipStream_t s) {
+  if (bf16)
+    full ? conv1d_launch_t<LOG2M, true, true>(gate, u, g, y, Hs, B, D, tw, s)
+         : conv1d_launch_t<LOG2M, true, false>(gate, u, g, y, Hs, B, D, tw, s);
+  else
+    full ? conv1d_launch_t<LOG2M, false, true>(gate, u, g, y, Hs, B, D, tw, s)
+         : conv1d_launch_t<LOG2M, false, false>(gate, u, g, y, Hs, B, D, tw, s);
   return hipGetLastError();
 }
 template <int LOG2M>
-hipError_t spectrum1d_launch(const float* h, float2* Hs, int D, const Twiddles& tw, hipStream_t s) {
-  hipLaunchKernelGGL((k_spectrum1d<LOG2M>), dim3(D), dim3(Single<LOG2M>::T), 0, s, h, Hs, tw);
+hipError_t spectrum1d_launch(const float* h, float2* Hs, int D, bool full, const Twiddles& tw, hipStream_t s) {
+  if (full)
+    hipLaunchKernelGGL((k_spectrum1d<LOG2M, true>), dim3(D), dim3(Single<LOG2M>::T), 0, s, h, Hs, tw);
+  else
+    hipLaunchKernelGGL((k_spectrum1d<LOG2M, false>), dim3(D), dim3(Single<LOG2M>::T), 0, s, h, Hs, tw);
   return hipGetLastError();
 }
 template <int LOG2M>
@@ -177,10 +193,10 @@ bool single_pass_supported(int log2L) { return log2L >= 10 && log2L <= 14; }
 #define HYENA_SINGLE_CASES(X) X(10) X(11) X(12) X(13) X(14)
 
 hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* gate, void* y, const float2* Hs,
-                                int B, int D, const Twiddles& tw, hipStream_t s) {
+                                int B, int D, const Twiddles& tw, hipStream_t s, int full) {
   const bool g = gate != nullptr;
   switch (log2L) {
-#define X(n) case n: return conv1d_launch<n>(bf16, g, u, gate, y, Hs, B, D, tw, s);
+#define X(n) case n: return conv1d_launch<n>(bf16, g, full != 0, u, gate, y, Hs, B, D, tw, s);
     HYENA_SINGLE_CASES(X)
 #undef X
   }
@@ -188,9 +204,9 @@ hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* 
 }
 
 hipError_t launch_spectrum1d_single(int log2L, const float* h, float2* Hs, int D, const Twiddles& tw,
-                                    hipStream_t s) {
+                                    hipStream_t s, int full) {
   switch (log2L) {
-#define X(n) case n: return spectrum1d_launch<n>(h, Hs, D, tw, s);
+#define X(n) case n: return spectrum1d_launch<n>(h, Hs, D, full != 0, tw, s);
     HYENA_SINGLE_CASES(X)
 #undef X
   }

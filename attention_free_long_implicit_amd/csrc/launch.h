@@ -7,12 +7,13 @@
 
 namespace hyena {
 
-// ---- 1-D, one workgroup per row (L = 2^log2L, 10 <= log2L <= 14)
+// ---- 1-D, one workgroup per row: an M = 2^log2L point packed transform, 10 <= log2L <= 14.
+// full = 0: causal, rows of M samples (zero-padded to 2M); full = 1: periodic, rows of 2M samples.
 bool single_pass_supported(int log2L);
 hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* gate, void* y, const float2* Hs,
-                                int B, int D, const Twiddles& tw, hipStream_t s);
+                                int B, int D, const Twiddles& tw, hipStream_t s, int full = 0);
 hipError_t launch_spectrum1d_single(int log2L, const float* h, float2* Hs, int D, const Twiddles& tw,
-                                    hipStream_t s);
+                                    hipStream_t s, int full = 0);
 hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
 
 // ---- 1-D, multi-pass (2^15 <= L <= 2^20): I is a workspace of `chunk` rows of L complex values.

@@ -14,7 +14,10 @@
  *   - 3-D (HYENA_LINEAR): c[p] = sum_{q in grid} h[p-q] u[q] over an n^3 grid, offsets p-q in
  *     [-(n-1), n-1]^3, by 3-D FFT on a (2n)^3 zero-padded grid ("Native Multi-Dimensional
  *     Subquadratic Operators via Input Dependent Long Convolutions" summary, method: native N-D
- *     convolution; boundary handling: zero-pad to twice the size).
+ *     convolution; boundary handling: zero-pad to twice the size);
+ *   - 1-D periodic (HYENA_CIRCULAR): c[t] = sum_{s<L} h[(t-s) mod L] u[s], by FFT on the L-point grid
+ *     itself, no padding (same summary, boundary handling: circular convolutions for periodic
+ *     systems).  The filter is the 1-D one, taps t = 0..L-1 (one period).
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library never frees them.
@@ -53,11 +56,12 @@ typedef enum { HYENA_F32 = 0, HYENA_BF16 = 1 } hyena_dtype;
 typedef enum {
   HYENA_CAUSAL = 0,   /* 1-D causal linear convolution (pad to 2L, keep [0, L))                  */
   HYENA_LINEAR = 1,   /* 3-D non-causal zero-padded "same" convolution (pad each axis to 2n)      */
-  HYENA_CIRCULAR = 2  /* periodic boundary: not implemented, returns HYENA_EUNSUPPORTED           */
+  HYENA_CIRCULAR = 2  /* periodic boundary, no padding: 1-D rows (3-D returns HYENA_EUNSUPPORTED)   */
 } hyena_mode;
 
 /* Grid shape: 1-D {1, {L, 0, 0}}; 3-D {3, {nx, ny, nz}}.
- * Supported: 1-D L = 2^k, 2^10 <= L <= 2^20; 3-D nx = ny = nz = 64. */
+ * Supported: HYENA_CAUSAL L = 2^k, 2^10 <= L <= 2^20; HYENA_CIRCULAR L = 2^k, 2^11 <= L <= 2^15;
+ * HYENA_LINEAR nx = ny = nz = 64. */
 typedef struct {
   int32_t ndim;
   int64_t n[3];
@@ -71,8 +75,9 @@ typedef struct {
   const float *W1, *b1, *W2, *b2, *alpha;
 } hyena_filter_params;
 
-/* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array).
- * For L = 8192 it also holds a bf16 copy laid out for the matrix-core kernel (36 KB per channel). */
+/* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array):
+ * causal 8L bytes per channel (for L = 8192 followed by a bf16 copy laid out for the matrix-core
+ * kernel, 36 KB per channel); periodic 4L bytes per channel. */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_filter_gen needs: room for the taps (used when h_time is NULL) plus, for
@@ -109,8 +114,9 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
                    const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,
                    hipStream_t stream);
 
-/* Testing aid: the engine-ordered spectrum as natural-order DFT bins of the zero-padded filter,
- * complex64 H[D, L+1] (1-D) or H[D, 2nx, 2ny, nz+1] (3-D). */
+/* Testing aid: the engine-ordered spectrum as natural-order DFT bins of the filter, complex64:
+ * causal H[D, L+1] (bins of the 2L-point transform of the zero-padded taps), periodic H[D, L/2+1]
+ * (bins of the L-point transform of the taps), 3-D H[D, 2nx, 2ny, nz+1]. */
 int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void *spectrum, void *H,
                           hipStream_t stream);
 

@@ -31,21 +31,21 @@ def params_to_dev(p):
     return {k: torch.from_numpy(np.ascontiguousarray(v)).to("cuda") for k, v in p.items()}
 
 
-def run_hip_operator(w, v, xs, params):
+def run_hip_operator(w, v, xs, params, mode=None):
     """Filter spectra + operator through the C ABI; returns y on the host as float64."""
     import torch
     import attention_free_long_implicit_amd as hy
     dt = torch_dtype(w)
     vd = to_dev(v, dt)
     xd = [to_dev(x, dt) for x in xs]
-    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
-    y = hy.operator(vd, xd, spectra)
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims, mode=mode) for p in params]
+    y = hy.operator(vd, xd, spectra, mode=mode)
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64)
 
 
-def oracle_rows_1d(w, v, xs, params, rows):
-    """Oracle output for the given (b, d) rows: [len(rows), L] float64."""
+def oracle_rows_1d(w, v, xs, params, rows, circular=False):
+    """Oracle output for the given (b, d) rows: [len(rows), L] float64 (periodic with ``circular``)."""
     L = w.dims[0]
     out = []
     cache = {}
@@ -53,7 +53,7 @@ def oracle_rows_1d(w, v, xs, params, rows):
         if d not in cache:
             cache[d] = [orc.implicit_filter_1d(p, L, channels=[d]) for p in params]
         hs = cache[d]
-        y = orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], hs)
+        y = orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], hs, circular=circular)
         out.append(y[0])
     return np.stack(out)
 

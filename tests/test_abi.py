@@ -60,6 +60,14 @@ def test_size_queries(lib):
     assert st == 0 and n == 128 * 128 * 128 * 65 * 8
     st, n = _size(lib.hyena_workspace_bytes, 2, 1, 2, L.dims_of([64, 64, 64]), L.F32, L.LINEAR)
     assert st == 0 and n == 2 * 64 * 128 * 65 * 8
+    # periodic 1-D: L/2 packed bins per channel, no workspace, taps only for the filter
+    for Lc in (2048, 8192, 32768):
+        st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([Lc]), L.CIRCULAR, 16)
+        assert st == 0 and n == 16 * (Lc // 2) * 8
+        st, n = _size(lib.hyena_workspace_bytes, 2, 4, 16, L.dims_of([Lc]), L.F32, L.CIRCULAR)
+        assert st == 0 and n == 0
+        st, n = _size(lib.hyena_filter_workspace_bytes, L.dims_of([Lc]), L.CIRCULAR, 16)
+        assert st == 0 and n == 16 * Lc * 4
 
 
 @pytest.mark.parametrize("shape,mode,status", [
@@ -70,7 +78,11 @@ def test_size_queries(lib):
     ([1024], L.LINEAR, L.EINVAL),            # linear mode needs a 3-D grid
     ([64, 64, 64], L.CAUSAL, L.EINVAL),      # causal mode needs 1-D
     ([32, 32, 32], L.LINEAR, L.EUNSUPPORTED),  # only the 64^3 grid is planned
-    ([1024], L.CIRCULAR, L.EUNSUPPORTED),
+    ([1024], L.CIRCULAR, L.EUNSUPPORTED),    # periodic rows: 2^11 .. 2^15
+    ([1 << 16], L.CIRCULAR, L.EUNSUPPORTED),
+    ([6144], L.CIRCULAR, L.EUNSUPPORTED),
+    ([0], L.CIRCULAR, L.EINVAL),
+    ([64, 64, 64], L.CIRCULAR, L.EUNSUPPORTED),   # periodic 3-D is not planned
 ])
 def test_bad_shapes(lib, shape, mode, status):
     st, _ = _size(lib.hyena_spectrum_bytes, L.dims_of(shape), mode, 4)
