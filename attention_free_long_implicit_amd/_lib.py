@@ -231,7 +231,7 @@ def spectrum_export(spectrum, point_shape: Sequence[int], D: int, mode: Optional
         shape = (D, (point_shape[0] // 2 if mode == CIRCULAR else point_shape[0]) + 1)
     else:
         nx, ny, nz = point_shape
-        shape = (D, 2 * nx, 2 * ny, nz + 1)
+        shape = (D, nx, ny, nz // 2 + 1) if mode == CIRCULAR else (D, 2 * nx, 2 * ny, nz + 1)
     H = torch.zeros(shape, dtype=torch.complex64, device=spectrum.device)
     _check(lib().hyena_spectrum_export(dims_of(point_shape), mode, D, _ptr(spectrum), H.data_ptr(),
                                        _stream(spectrum)), "hyena_spectrum_export")

@@ -77,11 +77,16 @@ size_t elem_bytes(int dtype) { return dtype == HYENA_BF16 ? 2 : 4; }
 // Shape checks shared by every entry point.  On success *points = elements per (b, d) row.
 int check_dims(hyena_dims dims, int mode, int64_t* points) {
   if (mode == HYENA_CIRCULAR) {
-    // periodic boundary: 1-D rows of L = 2^11 .. 2^15 samples (one packed L/2-point transform in LDS)
+    // periodic boundary: 1-D rows of L = 2^11 .. 2^15 samples (one packed L/2-point transform in LDS),
+    // or the 64^3 grid
     if (dims.ndim != 1 && dims.ndim != 3) return HYENA_EINVAL;
     for (int a = 0; a < dims.ndim; ++a)
       if (dims.n[a] <= 0) return HYENA_EINVAL;
-    if (dims.ndim == 3) return HYENA_EUNSUPPORTED;
+    if (dims.ndim == 3) {
+      if (!grid3d_supported(dims.n[0], dims.n[1], dims.n[2])) return HYENA_EUNSUPPORTED;
+      *points = dims.n[0] * dims.n[1] * dims.n[2];
+      return HYENA_OK;
+    }
     const int64_t L = dims.n[0];
     if (!is_pow2(L) || L < (1 << 11) || !single_pass_supported(log2i(L) - 1)) return HYENA_EUNSUPPORTED;
     *points = L;
@@ -116,22 +121,30 @@ int hip_status(hipError_t e) { return e == hipSuccess ? HYENA_OK : HYENA_EHIP; }
 
 bool is_multipass(int64_t L) { return !single_pass_supported(log2i(L)); }
 
+// What a (mode, grid) pair runs: 1-D causal, 1-D periodic, 3-D zero-padded or 3-D periodic.
+enum Kind { K_CAUSAL, K_CIRC1, K_LIN3, K_CIRC3 };
+int kind_of(int mode, hyena_dims dims) {
+  if (mode == HYENA_CAUSAL) return K_CAUSAL;
+  if (mode == HYENA_LINEAR) return K_LIN3;
+  return dims.ndim == 1 ? K_CIRC1 : K_CIRC3;
+}
+bool is3d(int kind) { return kind == K_LIN3 || kind == K_CIRC3; }
+int circ3(int kind) { return kind == K_CIRC3 ? 1 : 0; }
 // 1-D periodic rows of L samples run the single-pass engine on L/2 packed points.
-bool circular1d(int mode) { return mode == HYENA_CIRCULAR; }
 int circular_log2(int64_t L) { return log2i(L) - 1; }
 
 // Intermediate bytes per (b, d) row / volume for the multi-pass plans (0: single pass).
-size_t row_intermediate_bytes(int mode, int64_t pts) {
-  if (mode == HYENA_LINEAR) return conv3d_volume_bytes();
-  if (circular1d(mode)) return 0;
+size_t row_intermediate_bytes(int kind, int64_t pts) {
+  if (is3d(kind)) return conv3d_volume_bytes(circ3(kind));
+  if (kind == K_CIRC1) return 0;
   return is_multipass(pts) ? fourstep_row_bytes(log2i(pts)) : 0;
 }
-size_t filter_intermediate_bytes(int mode, int64_t pts) {
-  if (mode == HYENA_LINEAR) return conv3d_filter_volume_bytes();
-  if (circular1d(mode)) return 0;
+size_t filter_intermediate_bytes(int kind, int64_t pts) {
+  if (is3d(kind)) return conv3d_filter_volume_bytes(circ3(kind));
+  if (kind == K_CIRC1) return 0;
   return is_multipass(pts) ? fourstep_row_bytes(log2i(pts)) : 0;
 }
-size_t taps_per_channel(int mode, int64_t pts) { return mode == HYENA_LINEAR ? conv3d_taps_per_channel() : (size_t)pts; }
+size_t taps_per_channel(int kind, int64_t pts) { return is3d(kind) ? conv3d_taps_per_channel(circ3(kind)) : (size_t)pts; }
 
 // Lengths whose spectrum also carries the matrix-core (row-pair, bf16) copy after the fp32 one.
 bool has_pair_copy(int64_t L) { return mfma_pair_supported(log2i(L), 2); }
@@ -215,8 +228,9 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
-  if (mode == HYENA_LINEAR) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel();
-  else if (circular1d(mode)) *bytes = (size_t)D * (size_t)(pts / 2) * sizeof(float2);
+  const int kind = kind_of(mode, dims);
+  if (is3d(kind)) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel(circ3(kind));
+  else if (kind == K_CIRC1) *bytes = (size_t)D * (size_t)(pts / 2) * sizeof(float2);
   else *bytes = (size_t)D * (size_t)pts * sizeof(float2) + (has_pair_copy(pts) ? (size_t)D * mfma_pair_spectrum_bytes_per_channel() : 0);
   return HYENA_OK;
 }
@@ -226,9 +240,10 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* b
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
-  *bytes = (size_t)D * taps_per_channel(mode, pts) * sizeof(float);
-  if (mode == HYENA_CAUSAL && has_pair_copy(pts)) *bytes += 256 + pair_copy_temp_bytes(pts, D);
-  const size_t per = filter_intermediate_bytes(mode, pts);
+  const int kind = kind_of(mode, dims);
+  *bytes = (size_t)D * taps_per_channel(kind, pts) * sizeof(float);
+  if (kind == K_CAUSAL && has_pair_copy(pts)) *bytes += 256 + pair_copy_temp_bytes(pts, D);
+  const size_t per = filter_intermediate_bytes(kind, pts);
   if (per) *bytes += 256 + (size_t)default_chunk_rows((int64_t)per, D) * per;
   return HYENA_OK;
 }
@@ -238,8 +253,9 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
+  const int kind = kind_of(mode, dims);
   *bytes = 0;
-  const size_t per = row_intermediate_bytes(mode, pts);
+  const size_t per = row_intermediate_bytes(kind, pts);
   if (per) *bytes = (size_t)default_chunk_rows((int64_t)per, B * D) * per;
   return HYENA_OK;
 }
@@ -250,10 +266,11 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
+  const int kind = kind_of(mode, dims);
   if (p->H != 64 || p->F != (dims.ndim == 1 ? 64 : 96)) return HYENA_EUNSUPPORTED;
-  const size_t hbytes = (size_t)p->D * taps_per_channel(mode, pts) * sizeof(float);
+  const size_t hbytes = (size_t)p->D * taps_per_channel(kind, pts) * sizeof(float);
   const int64_t L = pts;
-  const size_t row_b = filter_intermediate_bytes(mode, pts);
+  const size_t row_b = filter_intermediate_bytes(kind, pts);
   const bool multi = row_b != 0;
   char* wsp = (char*)ws;
   size_t wsn = ws ? ws_bytes : 0;
@@ -281,12 +298,12 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
   FilterArgs a{p->F, p->H, p->D, p->W1, p->b1, p->W2, p->b2, p->alpha};
-  if (mode == HYENA_LINEAR) {
-    if ((st = hip_status(launch_filter3d(a, h, stream)))) return st;
-    return hip_status(launch_spectrum3d(h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream));
+  if (is3d(kind)) {
+    if ((st = hip_status(launch_filter3d(a, h, stream, circ3(kind))))) return st;
+    return hip_status(launch_spectrum3d(h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream, circ3(kind)));
   }
   if ((st = hip_status(launch_filter1d(a, (int)L, h, stream)))) return st;
-  if (circular1d(mode))
+  if (kind == K_CIRC1)
     return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, p->D, tw, stream, 1));
   if (multi)
     return hip_status(launch_spectrum1d_fourstep(log2i(L), h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw,
@@ -312,11 +329,12 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
+  const int kind = kind_of(mode, dims);
   const size_t tb = (size_t)B * D * pts * elem_bytes(dtype);
   if (y != u && overlaps(y, tb, u, tb)) return HYENA_EALIAS;
   if (gate && y != gate && overlaps(y, tb, gate, tb)) return HYENA_EALIAS;
   int chunk = 0;
-  const size_t per = row_intermediate_bytes(mode, pts);
+  const size_t per = row_intermediate_bytes(kind, pts);
   if (per) {
     chunk = chunk_from_ws(per, B * D, ws, ws_bytes);
     if (chunk < 1) return HYENA_EWORKSPACE;
@@ -328,13 +346,13 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   if (chunk) {
     const void* xs[1] = {gate};
     const void* sp[1] = {spectrum};
-    if (mode == HYENA_LINEAR)
+    if (is3d(kind))
       return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
-                                      stream));
+                                      stream, circ3(kind)));
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y,
                                              (float2*)ws, chunk, tw, device_mats(), stream));
   }
-  if (circular1d(mode))
+  if (kind == K_CIRC1)
     return hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, u, gate, y,
                                            (const float2*)spectrum, (int)B, (int)D, tw, stream, 1));
   return conv_once(B, D, pts, dtype, u, spectrum, gate, y, tw, stream);
@@ -351,12 +369,13 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
+  const int kind = kind_of(mode, dims);
   const size_t tb = (size_t)B * D * pts * elem_bytes(dtype);
   if (y != v && overlaps(y, tb, v, tb)) return HYENA_EALIAS;
   for (int i = 0; i < order; ++i)
     if (overlaps(y, tb, x[i], tb)) return HYENA_EALIAS;
   int chunk = 0;
-  const size_t per = row_intermediate_bytes(mode, pts);
+  const size_t per = row_intermediate_bytes(kind, pts);
   if (per) {
     chunk = chunk_from_ws(per, B * D, ws, ws_bytes);
     if (chunk < 1) return HYENA_EWORKSPACE;
@@ -366,13 +385,13 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   }
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
-  if (chunk && mode == HYENA_LINEAR)
+  if (chunk && is3d(kind))
     return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws, chunk,
-                                    tw, stream));
+                                    tw, stream, circ3(kind)));
   if (chunk)
     return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra,
                                              y, (float2*)ws, chunk, tw, device_mats(), stream));
-  if (circular1d(mode)) {
+  if (kind == K_CIRC1) {
     const void* cur = v;
     for (int i = 0; i < order; ++i) {
       if ((st = hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, cur, x[i], y,
@@ -400,9 +419,10 @@ int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spec
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
-  if (mode == HYENA_LINEAR)
-    return hip_status(launch_export3d((const float2*)spectrum, (float2*)H, (int)D, stream));
-  if (circular1d(mode))
+  const int kind = kind_of(mode, dims);
+  if (is3d(kind))
+    return hip_status(launch_export3d((const float2*)spectrum, (float2*)H, (int)D, stream, circ3(kind)));
+  if (kind == K_CIRC1)
     return hip_status(launch_export1d_single(circular_log2(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
   if (is_multipass(pts))
     return hip_status(launch_export1d_fourstep(log2i(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));

@@ -1,8 +1,16 @@
-// 3-D non-causal ("same") long convolution on a 64^3 grid, zero-padded to 128^3 (HyenaND summary,
-// method: native N-D convolution evaluated by an N-D FFT; boundary handling: zero-pad to twice the
-// size so nothing wraps), with the Hyena gate (Hyena study note, step 3).
+// 3-D non-causal long convolution on a 64^3 grid (HyenaND summary, method: native N-D convolution
+// evaluated by an N-D FFT; boundary handling), with the Hyena gate (Hyena study note, step 3), for two
+// boundaries (template geometry G):
 //
-//   c[p] = sum_{q in [0,64)^3} h[p-q] u[q],  p in [0,64)^3,  h on offsets [-63, 63]^3 placed at r mod 128
+//   zero-padded "same" (Geo3<false>): c[p] = sum_{q in [0,64)^3} h[p-q] u[q], p in [0,64)^3, h on
+//     offsets [-63, 63]^3 placed at r mod 128, transforms on the 128^3 grid (padding to twice the size
+//     so nothing wraps);
+//   periodic (Geo3<true>): c[p] = sum_q h[(p-q) mod 64] u[q], h on the centred offsets [-32, 31]^3
+//     placed at r mod 64, transforms on the 64^3 grid itself (circular convolution for periodic
+//     systems).
+//
+// The description below is for the zero-padded geometry; the periodic one has 32 packed points and
+// 33 bins per z-line, 64-point y and x transforms, full inputs and outputs everywhere.
 //
 // Layout of the transform: every z-line (128 reals, upper half zero) is packed two samples per
 // complex value and transformed with 64 points, then split into its 65 real-transform bins; y and x
@@ -21,39 +29,72 @@ namespace hyena {
 
 namespace k3 {
 constexpr int N = 64;              // grid points per axis
-constexpr int MP = 128;            // padded length per axis
-constexpr int NZC = 64;            // packed complex points per z-line
-constexpr int NKZ = 65;            // real-transform bins per z-line
-constexpr int PLANE = MP * NKZ;    // 8320 complex per x-slab
-constexpr int COLS = 64;           // columns per pass-B workgroup
-constexpr int TILES = PLANE / COLS;  // 130
 constexpr int T = 512;
-using ZRL = Radices<8, 8>;
-using YRL = Radices<16, 8>;
-using XRL = Radices<16, 8>;
-template <int NL>
-using ZEng = ColEngine<NL, 1, NKZ, T, ZRL, false>;       // lines = y, positions = packed z
-using YEng = ColEngine<NKZ, NKZ, 1, T, YRL, false>;      // lines = kz, positions = y
-using XEng = ColEngine<COLS, COLS, 1, T, XRL, true>;     // lines = columns, positions = x
-constexpr float kSpecScale = 1.0f / 8388608.0f;          // 2^-23 (the split contributes a factor 2)
+constexpr int COLS = 64;           // columns per pass-B workgroup
 }  // namespace k3
 
-// z-line split / re-pack on the plane.  Split: Z (digit-reversed positions 0..63 of each line) ->
-// 2 X[kz] at natural columns 0..64.  Re-pack: Y at natural columns 0..64 -> Z'' at digit-reversed
-// positions 0..63.  All reads happen before the barrier, all writes after.
-template <int NLINES, bool SPLIT>
+template <bool CIRC> struct Geo3;
+template <> struct Geo3<false> {   // zero-padded to 128^3
+  static constexpr bool PAD = true;
+  static constexpr int MP = 128;   // transform length per axis
+  using ZRL = Radices<8, 8>;       // 64 packed points per z-line
+  using YRL = Radices<16, 8>;
+  using XRL = Radices<16, 8>;
+};
+template <> struct Geo3<true> {    // periodic, 64^3
+  static constexpr bool PAD = false;
+  static constexpr int MP = 64;
+  using ZRL = Radices<8, 4>;       // 32 packed points per z-line
+  using YRL = Radices<8, 8>;
+  using XRL = Radices<8, 8>;
+};
+
+template <class G>
+struct K3 {
+  static constexpr int N = k3::N, T = k3::T, COLS = k3::COLS, MP = G::MP;
+  static constexpr bool PAD = G::PAD;
+  static constexpr int NZC = MP / 2;            // packed complex points per z-line
+  static constexpr int NKZ = NZC + 1;           // real-transform bins per z-line
+  static constexpr int PLANE = MP * NKZ;        // complex per x-slab
+  static constexpr int TILES = PLANE / COLS;
+  static constexpr int NZIN = PAD ? NZC / 2 : NZC;   // packed z values of the activations per line
+  static_assert(PLANE % COLS == 0, "tiles");
+  using ZRL = typename G::ZRL;
+  using YRL = typename G::YRL;
+  using XRL = typename G::XRL;
+  static_assert(ZRL::S == NZC && YRL::S == MP && XRL::S == MP, "plans");
+  template <int NL>
+  using ZEng = ColEngine<NL, 1, NKZ, T, ZRL, false>;       // lines = y, positions = packed z
+  using YEng = ColEngine<NKZ, NKZ, 1, T, YRL, false>;      // lines = kz, positions = y
+  using XEng = ColEngine<COLS, COLS, 1, T, XRL, true>;     // lines = columns, positions = x
+  // Hs = H / (2 MP^3); the filter's own z split contributes a factor 2 (2^-23 for 128^3, 2^-20 for 64^3)
+  static constexpr float kSpecScale = 1.0f / (4.0f * MP * MP * MP);
+  // signed offset of transform index i on the MP-torus, and whether the filter holds it
+  __device__ __forceinline__ static int offset(int i) { return PAD ? (i < N ? i : i - MP) : (i < MP / 2 ? i : i - MP); }
+  __device__ __forceinline__ static bool in_filter(int i) { return !PAD || i != N; }
+  // filter taps per axis and the tap index of a signed offset
+  static constexpr int W = PAD ? 2 * N - 1 : N;
+  __device__ __forceinline__ static int tap(int r) { return PAD ? r + N - 1 : r + N / 2; }
+};
+
+// z-line split / re-pack on the plane.  Split: Z (digit-reversed positions 0..NZC-1 of each line) ->
+// 2 X[kz] at natural columns 0..NZC.  Re-pack: Y at natural columns 0..NZC -> Z'' at digit-reversed
+// positions 0..NZC-1.  All reads happen before the barrier, all writes after.
+template <class G, int NLINES, bool SPLIT>
 __device__ __forceinline__ void k3_zline_pairs(float2* plane, const Twiddles& tw, int t) {
-  using namespace k3;
-  constexpr int ITEMS = NLINES * 33;
+  using C = K3<G>;
+  constexpr int NZC = C::NZC, NKZ = C::NKZ, T = C::T, HZ = NZC / 2;
+  using ZRL = typename C::ZRL;
+  constexpr int ITEMS = NLINES * (HZ + 1);
   constexpr int PER = (ITEMS + T - 1) / T;
   float2 a[PER], b[PER];
   static_for<PER>([&](auto ii) {
     const int it = t + T * ii.value;
     if (it >= ITEMS) return;
-    const int y = it / 33, k = it % 33;
+    const int y = it / (HZ + 1), k = it % (HZ + 1);
     const int kp = (NZC - k) % NZC;
     float2* line = plane + y * NKZ;
-    const float2 w = twiddle<7>(tw, uint32_t(k));
+    const float2 w = twiddle<ilog2(2 * NZC)>(tw, uint32_t(k));
     if constexpr (SPLIT) {
       const float2 A = line[ZRL::position_of_bin(k)];
       const float2 B = line[ZRL::position_of_bin(kp)];
@@ -71,37 +112,38 @@ __device__ __forceinline__ void k3_zline_pairs(float2* plane, const Twiddles& tw
   static_for<PER>([&](auto ii) {
     const int it = t + T * ii.value;
     if (it >= ITEMS) return;
-    const int y = it / 33, k = it % 33;
+    const int y = it / (HZ + 1), k = it % (HZ + 1);
     float2* line = plane + y * NKZ;
     if constexpr (SPLIT) {
       line[k] = a[ii.value];
-      if (k != 0 && k != 32) line[NZC - k] = b[ii.value];
+      if (k != 0 && k != HZ) line[NZC - k] = b[ii.value];
       if (k == 0) line[NZC] = b[ii.value];
     } else {
       line[ZRL::position_of_bin(k)] = a[ii.value];
-      if (k != 0 && k != 32) line[ZRL::position_of_bin(NZC - k)] = b[ii.value];
+      if (k != 0 && k != HZ) line[ZRL::position_of_bin(NZC - k)] = b[ii.value];
     }
   });
   __syncthreads();
 }
 
 // forward half of pass A on a plane whose packed z-lines are in place (lines y < NLINES nonzero)
-template <int NLINES>
+template <class G, int NLINES>
 __device__ __forceinline__ void k3_plane_forward(float2* plane, const Twiddles& tw, int t) {
-  using namespace k3;
-  constexpr bool HALF = NLINES == N;      // activation slabs: y >= 64 and z >= 64 are zero
-  ZEng<NLINES>::template forward<HALF>(plane, tw, t);
-  k3_zline_pairs<NLINES, true>(plane, tw, t);
-  YEng::template forward<HALF>(plane, tw, t);
+  using C = K3<G>;
+  constexpr bool HALF = C::PAD && NLINES == C::N;   // zero-padded activation slabs: y, z >= 64 are zero
+  C::template ZEng<NLINES>::template forward<HALF>(plane, tw, t);
+  k3_zline_pairs<G, NLINES, true>(plane, tw, t);
+  C::YEng::template forward<HALF>(plane, tw, t);
 }
 
 // Pass A (MODE 0, from activations) or pass C (MODE 1, inverse + gate [+ chained pass A]).
 // grid.x = 64 slabs * nq (volume fastest).
-template <bool BF16, int MODE, bool GATE, bool CHAIN>
+template <class G, bool BF16, int MODE, bool GATE, bool CHAIN>
 __global__ void __launch_bounds__(k3::T)
 k3_planes(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* gate,
           typename Store<BF16>::elem* y, float2* I, int q0, int nq, int B, int D, Twiddles tw) {
-  using namespace k3;
+  using C = K3<G>;
+  constexpr int N = C::N, T = C::T, PLANE = C::PLANE, NKZ = C::NKZ, NZIN = C::NZIN;
   using St = Store<BF16>;
   __shared__ float2 plane[PLANE];
   const int t = threadIdx.x;
@@ -113,23 +155,23 @@ k3_planes(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   float2* slab = I + ((size_t)ql * N + x) * PLANE;
   if constexpr (MODE == 0) {
     const auto* src = u + vol + (size_t)x * N * N;
-    static_for<(N * NZC / 2) / T>([&](auto ii) {
+    static_for<(N * NZIN) / T>([&](auto ii) {
       const int e = t + T * ii.value;
-      const int yy = e / (NZC / 2), m = e % (NZC / 2);
+      const int yy = e / NZIN, m = e % NZIN;
       plane[yy * NKZ + m] = St::load2(src + yy * N + 2 * m);
     });
     __syncthreads();
   } else {
     for (int j = t; j < PLANE; j += T) plane[j] = slab[j];
     __syncthreads();
-    YEng::template inverse<true>(plane, tw, t);
-    k3_zline_pairs<N, false>(plane, tw, t);
-    ZEng<N>::template inverse<true>(plane, tw, t);
+    C::YEng::template inverse<C::PAD>(plane, tw, t);
+    k3_zline_pairs<G, N, false>(plane, tw, t);
+    C::template ZEng<N>::template inverse<C::PAD>(plane, tw, t);
     const auto* g = GATE ? gate + vol + (size_t)x * N * N : nullptr;
     auto* dst = CHAIN ? nullptr : y + vol + (size_t)x * N * N;
-    static_for<(N * NZC / 2) / T>([&](auto ii) {
+    static_for<(N * NZIN) / T>([&](auto ii) {
       const int e = t + T * ii.value;
-      const int yy = e / (NZC / 2), m = e % (NZC / 2);
+      const int yy = e / NZIN, m = e % NZIN;
       float2 v = plane[yy * NKZ + m];
       if constexpr (GATE) {
         const float2 gv = St::load2(g + yy * N + 2 * m);
@@ -145,49 +187,53 @@ k3_planes(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
     if constexpr (!CHAIN) return;
     __syncthreads();
   }
-  k3_plane_forward<N>(plane, tw, t);
+  k3_plane_forward<G, N>(plane, tw, t);
   for (int j = t; j < PLANE; j += T) slab[j] = plane[j];
 }
 
-// Pass A for the filter: taps h[d, 127, 127, 127] (offset + 63) placed at r mod 128; all 128 slabs.
+// Pass A for the filter: taps h[d, W, W, W] (tap index of a signed offset: K3::tap) placed at r mod MP;
+// all MP slabs.  Zero-padded: W = 127, offsets [-63, 63], index 64 of each axis empty.  Periodic:
+// W = 64, offsets [-32, 31].
+template <class G>
 __global__ void __launch_bounds__(k3::T)
 k3_planes_taps(const float* __restrict__ h, float2* I, int q0, int nq, Twiddles tw) {
-  using namespace k3;
-  constexpr int W = 2 * N - 1;     // 127
+  using C = K3<G>;
+  constexpr int T = C::T, MP = C::MP, NZC = C::NZC, NKZ = C::NKZ, PLANE = C::PLANE, W = C::W;
   __shared__ float2 plane[PLANE];
   const int t = threadIdx.x;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int ql = lb % nq, x = lb / nq;
   const int d = q0 + ql;
   const float* hd = h + (size_t)d * W * W * W;
-  auto off = [](int i) { return i < N ? i : i - MP; };    // index on the 128-torus -> signed offset
-  const int rx = off(x);
+  const int rx = C::offset(x);
   static_for<(MP * NZC) / T>([&](auto ii) {
     const int e = t + T * ii.value;
     const int yy = e / NZC, m = e % NZC;
-    const int ry = off(yy);
+    const int ry = C::offset(yy);
     float2 v = make_float2(0.f, 0.f);
-    if (x != N && yy != N) {
-      const float* line = hd + ((size_t)(rx + N - 1) * W + (ry + N - 1)) * W;
+    if (C::in_filter(x) && C::in_filter(yy)) {
+      const float* line = hd + ((size_t)C::tap(rx) * W + C::tap(ry)) * W;
       const int z0 = 2 * m, z1 = 2 * m + 1;
-      if (z0 != N) v.x = line[off(z0) + N - 1];
-      if (z1 != N) v.y = line[off(z1) + N - 1];
+      if (C::in_filter(z0)) v.x = line[C::tap(C::offset(z0))];
+      if (C::in_filter(z1)) v.y = line[C::tap(C::offset(z1))];
     }
     plane[yy * NKZ + m] = v;
   });
   __syncthreads();
-  k3_plane_forward<MP>(plane, tw, t);
+  k3_plane_forward<G, MP>(plane, tw, t);
   float2* slab = I + ((size_t)ql * MP + x) * PLANE;
   for (int j = t; j < PLANE; j += T) slab[j] = plane[j];
 }
 
-// Pass B.  MODE 0: x-transform (x >= 64 zero), product with Hs, inverse, keep x < 64 (in place).
-//          MODE 1: x-transform of a full filter slab stack, write the scaled spectrum.
-// grid.x = 130 tiles * nq (volume fastest).
-template <int MODE>
+// Pass B.  MODE 0: x-transform (zero-padded: x >= 64 zero), product with Hs, inverse, keep x < 64
+//          (in place).  MODE 1: x-transform of a full filter slab stack, write the scaled spectrum.
+// grid.x = TILES * nq (volume fastest).
+template <class G, int MODE>
 __global__ void __launch_bounds__(k3::T)
 k3_cols(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq, int B, Twiddles tw) {
-  using namespace k3;
+  using C = K3<G>;
+  constexpr int N = C::N, T = C::T, MP = C::MP, COLS = C::COLS, PLANE = C::PLANE, TILES = C::TILES;
+  using XEng = typename C::XEng;
   constexpr int NX = (MODE == 0) ? N : MP;    // slabs present in the intermediate
   __shared__ float2 lds[lds_padded_size(COLS * MP)];
   const int t = threadIdx.x;
@@ -203,13 +249,13 @@ k3_cols(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, i
     lds[XEng::addr(xx, l)] = base[(size_t)xx * PLANE + l];
   });
   __syncthreads();
-  XEng::template forward<MODE == 0>(lds, tw, t);
+  XEng::template forward<MODE == 0 && C::PAD>(lds, tw, t);
   const size_t hoff = ((size_t)d * TILES + tile) * (MP * COLS);
   if constexpr (MODE == 1) {
     static_for<(MP * COLS) / T>([&](auto ii) {
       const int e = t + T * ii.value;
       const int p = e / COLS, l = e % COLS;
-      Hs_out[hoff + e] = cscale(lds[XEng::addr(p, l)], kSpecScale);
+      Hs_out[hoff + e] = cscale(lds[XEng::addr(p, l)], C::kSpecScale);
     });
     return;
   }
@@ -220,7 +266,7 @@ k3_cols(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, i
     lds[a] = cmul(lds[a], Hs[hoff + e]);
   });
   __syncthreads();
-  XEng::template inverse<true>(lds, tw, t);
+  XEng::template inverse<C::PAD>(lds, tw, t);
   static_for<(N * COLS) / T>([&](auto ii) {
     const int e = t + T * ii.value;
     const int xx = e / COLS, l = e % COLS;
@@ -228,9 +274,13 @@ k3_cols(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, i
   });
 }
 
-// Engine-order spectrum -> H[d, kx, ky, kz] (128 x 128 x 65, unscaled real-input DFT bins).
+// Engine-order spectrum -> H[d, kx, ky, kz] (MP x MP x (MP/2+1), unscaled real-input DFT bins).
+template <class G>
 __global__ void k3_export(const float2* __restrict__ Hs, float2* __restrict__ H) {
-  using namespace k3;
+  using C = K3<G>;
+  constexpr int MP = C::MP, COLS = C::COLS, TILES = C::TILES, NKZ = C::NKZ;
+  using XRL = typename C::XRL;
+  using YRL = typename C::YRL;
   const int d = blockIdx.y;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= TILES * MP * COLS) return;
@@ -239,17 +289,20 @@ __global__ void k3_export(const float2* __restrict__ Hs, float2* __restrict__ H)
   const int j = tile * COLS + l;
   const int ypos = j / NKZ, kz = j % NKZ;
   const int kx = XRL::bin_of_position(p), ky = YRL::bin_of_position(ypos);
-  H[(((size_t)d * MP + kx) * MP + ky) * NKZ + kz] = cscale(Hs[(size_t)d * TILES * MP * COLS + idx], 4194304.0f);
+  H[(((size_t)d * MP + kx) * MP + ky) * NKZ + kz] =
+      cscale(Hs[(size_t)d * TILES * MP * COLS + idx], 0.5f / C::kSpecScale);
 }
 
 // ------------------------------------------------------------------ 3-D filter taps
-// h[d, rx, ry, rz] = (W2 SiLU(W1 phi(r) + b1) + b2)_d * exp(-alpha_d |r| / n) on offsets [-(n-1), n-1]^3;
+// h[d, rx, ry, rz] = (W2 SiLU(W1 phi(r) + b1) + b2)_d * exp(-alpha_d |r| / n) on offsets [-(n-1), n-1]^3
+// (zero-padded geometry) or [-n/2, n/2)^3 (periodic), tap index K3::tap(r) per axis;
 // phi(r): per axis (x, y, z) 16 sines then 16 cosines of 2 pi f r_a / n, f = 1..16 (phases reduced mod n).
-template <int F, int H>
+template <class G, int F, int H>
 __global__ void __launch_bounds__(256)
 k_filter3d(FilterArgs a, float* __restrict__ h) {
-  using namespace k3;
-  constexpr int W = 2 * N - 1, NP = W * W * W, TP = 64, PER_AX = F / 6;
+  using C = K3<G>;
+  constexpr int N = C::N, W = C::W, NP = W * W * W, TP = 64, PER_AX = F / 6;
+  constexpr int R0 = C::PAD ? N - 1 : N / 2;    // tap index of offset 0
   __shared__ float phi[TP][F + 1];
   __shared__ float w1t[F][H + 1];
   __shared__ float act[TP][H + 1];
@@ -264,7 +317,7 @@ k_filter3d(FilterArgs a, float* __restrict__ h) {
     const int pp = i / (3 * PER_AX), rem = i % (3 * PER_AX);
     const int ax = rem / PER_AX, f = rem % PER_AX;
     const int pos = min(p0 + pp, NP - 1);
-    const int r3[3] = {pos / (W * W) - (N - 1), (pos / W) % W - (N - 1), pos % W - (N - 1)};
+    const int r3[3] = {pos / (W * W) - R0, (pos / W) % W - R0, pos % W - R0};
     const int ph = (((f + 1) * r3[ax]) % N + N) % N;
     float s, c;
     sincospif(2.0f * (float)ph / (float)N, &s, &c);
@@ -302,33 +355,47 @@ k_filter3d(FilterArgs a, float* __restrict__ h) {
 
 // ------------------------------------------------------------------ host side
 bool grid3d_supported(int64_t nx, int64_t ny, int64_t nz) { return nx == k3::N && ny == k3::N && nz == k3::N; }
-size_t conv3d_volume_bytes() { return (size_t)k3::N * k3::PLANE * sizeof(float2); }
-size_t conv3d_filter_volume_bytes() { return (size_t)k3::MP * k3::PLANE * sizeof(float2); }
-size_t conv3d_spectrum_bytes_per_channel() { return (size_t)k3::TILES * k3::MP * k3::COLS * sizeof(float2); }
-size_t conv3d_taps_per_channel() { return (size_t)(2 * k3::N - 1) * (2 * k3::N - 1) * (2 * k3::N - 1); }
+size_t conv3d_volume_bytes(int circ) {
+  return circ ? (size_t)k3::N * K3<Geo3<true>>::PLANE * sizeof(float2)
+              : (size_t)k3::N * K3<Geo3<false>>::PLANE * sizeof(float2);
+}
+size_t conv3d_filter_volume_bytes(int circ) {
+  return circ ? (size_t)K3<Geo3<true>>::MP * K3<Geo3<true>>::PLANE * sizeof(float2)
+              : (size_t)K3<Geo3<false>>::MP * K3<Geo3<false>>::PLANE * sizeof(float2);
+}
+size_t conv3d_spectrum_bytes_per_channel(int circ) {
+  using A = K3<Geo3<true>>;
+  using B = K3<Geo3<false>>;
+  return circ ? (size_t)A::TILES * A::MP * A::COLS * sizeof(float2) : (size_t)B::TILES * B::MP * B::COLS * sizeof(float2);
+}
+size_t conv3d_taps_per_channel(int circ) {
+  return circ ? (size_t)K3<Geo3<true>>::W * K3<Geo3<true>>::W * K3<Geo3<true>>::W
+              : (size_t)K3<Geo3<false>>::W * K3<Geo3<false>>::W * K3<Geo3<false>>::W;
+}
 
 namespace {
-template <bool BF16>
+template <class G, bool BF16>
 hipError_t conv3d_launch_t(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
                            void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s) {
-  using namespace k3;
+  using C = K3<G>;
+  constexpr int N = C::N, T = C::T, TILES = C::TILES;
   using E = typename Store<BF16>::elem;
   const int rows = B * D;
   for (int q0 = 0; q0 < rows; q0 += chunk) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
-    hipLaunchKernelGGL((k3_planes<BF16, 0, false, false>), dim3(N * nq), dim3(T), 0, s, (const E*)v,
+    hipLaunchKernelGGL((k3_planes<G, BF16, 0, false, false>), dim3(N * nq), dim3(T), 0, s, (const E*)v,
                        (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
-      hipLaunchKernelGGL((k3_cols<0>), dim3(TILES * nq), dim3(T), 0, s, I, (const float2*)spectra[i],
+      hipLaunchKernelGGL((k3_cols<G, 0>), dim3(TILES * nq), dim3(T), 0, s, I, (const float2*)spectra[i],
                          (float2*)nullptr, q0, nq, B, tw);
       if (i + 1 < order)
-        hipLaunchKernelGGL((k3_planes<BF16, 1, true, true>), dim3(N * nq), dim3(T), 0, s, (const E*)nullptr,
+        hipLaunchKernelGGL((k3_planes<G, BF16, 1, true, true>), dim3(N * nq), dim3(T), 0, s, (const E*)nullptr,
                            (const E*)x[i], (E*)nullptr, I, q0, nq, B, D, tw);
       else if (x[i])
-        hipLaunchKernelGGL((k3_planes<BF16, 1, true, false>), dim3(N * nq), dim3(T), 0, s, (const E*)nullptr,
+        hipLaunchKernelGGL((k3_planes<G, BF16, 1, true, false>), dim3(N * nq), dim3(T), 0, s, (const E*)nullptr,
                            (const E*)x[i], (E*)y, I, q0, nq, B, D, tw);
       else
-        hipLaunchKernelGGL((k3_planes<BF16, 1, false, false>), dim3(N * nq), dim3(T), 0, s, (const E*)nullptr,
+        hipLaunchKernelGGL((k3_planes<G, BF16, 1, false, false>), dim3(N * nq), dim3(T), 0, s, (const E*)nullptr,
                            (const E*)nullptr, (E*)y, I, q0, nq, B, D, tw);
     }
     hipError_t e = hipGetLastError();
@@ -336,40 +403,59 @@ hipError_t conv3d_launch_t(int order, int B, int D, const void* v, const void* c
   }
   return hipSuccess;
 }
-}  // namespace
 
-hipError_t launch_conv3d(int bf16, int order, int B, int D, const void* v, const void* const* x,
-                         const void* const* spectra, void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s) {
-  return bf16 ? conv3d_launch_t<true>(order, B, D, v, x, spectra, y, I, chunk, tw, s)
-              : conv3d_launch_t<false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
-}
-
-hipError_t launch_filter3d(const FilterArgs& a, float* h, hipStream_t s) {
-  if (a.F != 96 || a.H != 64) return hipErrorInvalidValue;
-  const int np = (int)conv3d_taps_per_channel();
-  hipLaunchKernelGGL((k_filter3d<96, 64>), dim3((np + 63) / 64), dim3(256), 0, s, a, h);
-  return hipGetLastError();
-}
-
-hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
-                             hipStream_t s) {
-  using namespace k3;
+template <class G>
+hipError_t spectrum3d_launch_t(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
+                               hipStream_t s) {
+  using C = K3<G>;
   for (int q0 = 0; q0 < D; q0 += chunk) {
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
-    hipLaunchKernelGGL(k3_planes_taps, dim3(MP * nq), dim3(T), 0, s, h, I, q0, nq, tw);
-    hipLaunchKernelGGL((k3_cols<1>), dim3(TILES * nq), dim3(T), 0, s, I, (const float2*)nullptr, Hs, q0, nq, 1,
-                       tw);
+    hipLaunchKernelGGL((k3_planes_taps<G>), dim3(C::MP * nq), dim3(C::T), 0, s, h, I, q0, nq, tw);
+    hipLaunchKernelGGL((k3_cols<G, 1>), dim3(C::TILES * nq), dim3(C::T), 0, s, I, (const float2*)nullptr, Hs, q0,
+                       nq, 1, tw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s) {
-  using namespace k3;
-  const int n = TILES * MP * COLS;
-  hipLaunchKernelGGL(k3_export, dim3((n + 255) / 256, D), dim3(256), 0, s, Hs, H);
+template <class G>
+hipError_t export3d_launch_t(const float2* Hs, float2* H, int D, hipStream_t s) {
+  using C = K3<G>;
+  const int n = C::TILES * C::MP * C::COLS;
+  hipLaunchKernelGGL((k3_export<G>), dim3((n + 255) / 256, D), dim3(256), 0, s, Hs, H);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_conv3d(int bf16, int order, int B, int D, const void* v, const void* const* x,
+                         const void* const* spectra, void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s,
+                         int circ) {
+  if (circ)
+    return bf16 ? conv3d_launch_t<Geo3<true>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s)
+                : conv3d_launch_t<Geo3<true>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
+  return bf16 ? conv3d_launch_t<Geo3<false>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s)
+              : conv3d_launch_t<Geo3<false>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
+}
+
+hipError_t launch_filter3d(const FilterArgs& a, float* h, hipStream_t s, int circ) {
+  if (a.F != 96 || a.H != 64) return hipErrorInvalidValue;
+  const int np = (int)conv3d_taps_per_channel(circ);
+  if (circ)
+    hipLaunchKernelGGL((k_filter3d<Geo3<true>, 96, 64>), dim3((np + 63) / 64), dim3(256), 0, s, a, h);
+  else
+    hipLaunchKernelGGL((k_filter3d<Geo3<false>, 96, 64>), dim3((np + 63) / 64), dim3(256), 0, s, a, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
+                             hipStream_t s, int circ) {
+  return circ ? spectrum3d_launch_t<Geo3<true>>(h, Hs, D, I, chunk, tw, s)
+              : spectrum3d_launch_t<Geo3<false>>(h, Hs, D, I, chunk, tw, s);
+}
+
+hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s, int circ) {
+  return circ ? export3d_launch_t<Geo3<true>>(Hs, H, D, s) : export3d_launch_t<Geo3<false>>(Hs, H, D, s);
 }
 
 }  // namespace hyena

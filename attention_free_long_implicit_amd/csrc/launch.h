@@ -28,17 +28,19 @@ hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int
                                       const Twiddles& tw, hipStream_t s);
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
 
-// ---- 3-D, 64^3 grid zero-padded to 128^3 (non-causal "same" convolution)
+// ---- 3-D, 64^3 grid: circ = 0 zero-padded to 128^3 (non-causal "same" convolution),
+//      circ = 1 periodic on the 64^3 grid itself
 bool grid3d_supported(int64_t nx, int64_t ny, int64_t nz);
-size_t conv3d_volume_bytes();                 // intermediate per (b, d) volume
-size_t conv3d_filter_volume_bytes();          // intermediate per channel while building a spectrum
-size_t conv3d_spectrum_bytes_per_channel();
-size_t conv3d_taps_per_channel();             // (2n-1)^3
+size_t conv3d_volume_bytes(int circ);                 // intermediate per (b, d) volume
+size_t conv3d_filter_volume_bytes(int circ);          // intermediate per channel while building a spectrum
+size_t conv3d_spectrum_bytes_per_channel(int circ);
+size_t conv3d_taps_per_channel(int circ);             // (2n-1)^3 or n^3
 hipError_t launch_conv3d(int bf16, int order, int B, int D, const void* v, const void* const* x,
-                         const void* const* spectra, void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s);
+                         const void* const* spectra, void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s,
+                         int circ);
 hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
-                             hipStream_t s);
-hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s);
+                             hipStream_t s, int circ);
+hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s, int circ);
 
 // ---- matrix-core path: bf16 storage, L = 8192, rows in pairs of one channel (B even)
 bool mfma_pair_supported(int log2L, int B);
@@ -62,6 +64,6 @@ struct FilterArgs {
   const float *W1, *b1, *W2, *b2, *alpha;
 };
 hipError_t launch_filter1d(const FilterArgs& a, int L, float* h, hipStream_t s);
-hipError_t launch_filter3d(const FilterArgs& a, float* h, hipStream_t s);
+hipError_t launch_filter3d(const FilterArgs& a, float* h, hipStream_t s, int circ);
 
 }  // namespace hyena

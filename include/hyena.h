@@ -15,9 +15,10 @@
  *     [-(n-1), n-1]^3, by 3-D FFT on a (2n)^3 zero-padded grid ("Native Multi-Dimensional
  *     Subquadratic Operators via Input Dependent Long Convolutions" summary, method: native N-D
  *     convolution; boundary handling: zero-pad to twice the size);
- *   - 1-D periodic (HYENA_CIRCULAR): c[t] = sum_{s<L} h[(t-s) mod L] u[s], by FFT on the L-point grid
- *     itself, no padding (same summary, boundary handling: circular convolutions for periodic
- *     systems).  The filter is the 1-D one, taps t = 0..L-1 (one period).
+ *   - periodic (HYENA_CIRCULAR), by FFT on the grid itself, no padding (same summary, boundary
+ *     handling: circular convolutions for periodic systems): 1-D c[t] = sum_{s<L} h[(t-s) mod L] u[s]
+ *     with the 1-D filter's taps t = 0..L-1 (one period); 3-D c[p] = sum_q h[(p-q) mod n] u[q] with
+ *     the 3-D filter on the centred offsets [-n/2, n/2)^3 (one period).
  *
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library never frees them.
@@ -56,12 +57,12 @@ typedef enum { HYENA_F32 = 0, HYENA_BF16 = 1 } hyena_dtype;
 typedef enum {
   HYENA_CAUSAL = 0,   /* 1-D causal linear convolution (pad to 2L, keep [0, L))                  */
   HYENA_LINEAR = 1,   /* 3-D non-causal zero-padded "same" convolution (pad each axis to 2n)      */
-  HYENA_CIRCULAR = 2  /* periodic boundary, no padding: 1-D rows (3-D returns HYENA_EUNSUPPORTED)   */
+  HYENA_CIRCULAR = 2  /* periodic boundary, no padding: 1-D rows or the 3-D grid                    */
 } hyena_mode;
 
 /* Grid shape: 1-D {1, {L, 0, 0}}; 3-D {3, {nx, ny, nz}}.
- * Supported: HYENA_CAUSAL L = 2^k, 2^10 <= L <= 2^20; HYENA_CIRCULAR L = 2^k, 2^11 <= L <= 2^15;
- * HYENA_LINEAR nx = ny = nz = 64. */
+ * Supported: HYENA_CAUSAL L = 2^k, 2^10 <= L <= 2^20; HYENA_CIRCULAR 1-D L = 2^k, 2^11 <= L <= 2^15,
+ * or nx = ny = nz = 64; HYENA_LINEAR nx = ny = nz = 64. */
 typedef struct {
   int32_t ndim;
   int64_t n[3];
@@ -77,7 +78,8 @@ typedef struct {
 
 /* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array):
  * causal 8L bytes per channel (for L = 8192 followed by a bf16 copy laid out for the matrix-core
- * kernel, 36 KB per channel); periodic 4L bytes per channel. */
+ * kernel, 36 KB per channel); periodic 1-D 4L bytes per channel; 3-D 128*128*65*8 bytes per channel
+ * (zero-padded) or 64*64*33*8 (periodic). */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_filter_gen needs: room for the taps (used when h_time is NULL) plus, for
@@ -87,8 +89,9 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t *b
 /* Workspace bytes hyena_fftconv / hyena_operator need (0 when the transform fits on chip). */
 int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, size_t *bytes);
 
-/* Implicit filter of one order: writes the taps (1-D: h_time[D, L]; 3-D: h_time[D, 2n-1, 2n-1, 2n-1],
- * offsets from -(n-1)) when h_time is not NULL, and the filter spectrum into `spectrum`
+/* Implicit filter of one order: writes the taps (1-D: h_time[D, L]; 3-D zero-padded:
+ * h_time[D, 2n-1, 2n-1, 2n-1], index = offset + n-1; 3-D periodic: h_time[D, n, n, n], index =
+ * offset + n/2) when h_time is not NULL, and the filter spectrum into `spectrum`
  * (hyena_spectrum_bytes bytes).  ws/ws_bytes: scratch of hyena_filter_workspace_bytes bytes (may be
  * NULL/0 when h_time is given and L <= 16384; HYENA_EWORKSPACE when too small).  The spectrum depends
  * only on (params, dims), so callers cache it per length. */
@@ -116,7 +119,8 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
 
 /* Testing aid: the engine-ordered spectrum as natural-order DFT bins of the filter, complex64:
  * causal H[D, L+1] (bins of the 2L-point transform of the zero-padded taps), periodic H[D, L/2+1]
- * (bins of the L-point transform of the taps), 3-D H[D, 2nx, 2ny, nz+1]. */
+ * (bins of the L-point transform of the taps), 3-D H[D, 2nx, 2ny, nz+1] (zero-padded) or
+ * H[D, nx, ny, nz/2+1] (periodic). */
 int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void *spectrum, void *H,
                           hipStream_t stream);
 

@@ -68,6 +68,13 @@ def test_size_queries(lib):
         assert st == 0 and n == 0
         st, n = _size(lib.hyena_filter_workspace_bytes, L.dims_of([Lc]), L.CIRCULAR, 16)
         assert st == 0 and n == 16 * Lc * 4
+    # periodic 3-D: 64 x 64 x 33 bins per channel, intermediate 64 x-slabs of 64 x 33 per volume
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.CIRCULAR, 128)
+    assert st == 0 and n == 128 * 64 * 64 * 33 * 8
+    st, n = _size(lib.hyena_workspace_bytes, 2, 1, 2, L.dims_of([64, 64, 64]), L.F32, L.CIRCULAR)
+    assert st == 0 and n == 2 * 64 * 64 * 33 * 8
+    st, n = _size(lib.hyena_filter_workspace_bytes, L.dims_of([64, 64, 64]), L.CIRCULAR, 3)
+    assert st == 0 and n == 3 * 64 ** 3 * 4 + 256 + 3 * 64 * 64 * 33 * 8
 
 
 @pytest.mark.parametrize("shape,mode,status", [
@@ -82,7 +89,8 @@ def test_size_queries(lib):
     ([1 << 16], L.CIRCULAR, L.EUNSUPPORTED),
     ([6144], L.CIRCULAR, L.EUNSUPPORTED),
     ([0], L.CIRCULAR, L.EINVAL),
-    ([64, 64, 64], L.CIRCULAR, L.EUNSUPPORTED),   # periodic 3-D is not planned
+    ([32, 32, 32], L.CIRCULAR, L.EUNSUPPORTED),   # periodic 3-D: the 64^3 grid only
+    ([64, 64], L.CIRCULAR, L.EINVAL),
 ])
 def test_bad_shapes(lib, shape, mode, status):
     st, _ = _size(lib.hyena_spectrum_bytes, L.dims_of(shape), mode, 4)

@@ -105,3 +105,99 @@ def test_circular_operator_order2(torch_cuda, L, dtype):
     e = rel_err_rows(got, ref)
     say(f"  max rel err {e.max():.3e}")
     assert e.max() < (BF16_TOL if dtype == "bf16" else FP32_TOL), e.max()
+
+
+# ---------------------------------------------------------------- periodic 3-D (64^3)
+N3 = 64
+
+
+def _w3(B=1, D=3, dtype="f32", order=2):
+    return hi.WORKLOADS[4].with_(B=B, D=D, dtype=dtype, order=order, mode="circular")
+
+
+def test_circular3d_filter_taps_and_spectrum(torch_cuda):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 2
+    w = _w3(D=D)
+    p = hi.draw_filter_params(w, seed=51)[0]
+    say("periodic 3-D filter taps + spectrum, D=2")
+    h = torch.empty((D, N3, N3, N3), dtype=torch.float32, device="cuda")   # offsets from -32 (index - 32)
+    spec = hy.filter_gen(params_to_dev(p), (N3, N3, N3), h_time=h, mode=hy.CIRCULAR)
+    assert spec.numel() == D * N3 * N3 * 33 * 8
+    H = hy.spectrum_export(spec, (N3, N3, N3), D, mode=hy.CIRCULAR)
+    torch.cuda.synchronize()
+    ref = orc.implicit_filter_3d_circular(p, N3)                             # index r mod 64
+    centred = np.roll(ref, N3 // 2, axis=(1, 2, 3))                          # index r + 32
+    e = rel_err_rows(h.cpu().numpy(), centred, point_axes=3)
+    assert e.max() < 1e-5, e.max()
+    Href = np.fft.rfftn(ref, axes=(-3, -2, -1))
+    Hg = H.cpu().numpy().astype(np.complex128)
+    assert Hg.shape == Href.shape
+    e = np.sqrt(np.sum(np.abs(Hg - Href) ** 2, axis=(1, 2, 3)) / np.sum(np.abs(Href) ** 2, axis=(1, 2, 3)))
+    assert e.max() < 2e-5, e.max()
+
+
+@pytest.mark.parametrize("gate", [False, True])
+def test_circular3d_fftconv_fp32(torch_cuda, gate):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    B, D = 1, 3
+    w = _w3(B=B, D=D)
+    rng = np.random.default_rng(52)
+    u = rng.standard_normal(w.shape).astype(np.float32)
+    g = rng.standard_normal(w.shape).astype(np.float32)
+    p = hi.draw_filter_params(w, seed=52)[0]
+    say(f"periodic 3-D fftconv fp32 gate={gate}")
+    spec = hy.filter_gen(params_to_dev(p), (N3, N3, N3), mode=hy.CIRCULAR)
+    ws = torch.empty(2 * N3 * N3 * 33 * 8, dtype=torch.uint8, device="cuda")   # two volumes per chunk: 2 chunks
+    y = hy.operator(to_dev(u, torch.float32), [to_dev(g, torch.float32)], [spec], ws=ws, mode=hy.CIRCULAR) \
+        if gate else hy.fftconv(to_dev(u, torch.float32), spec, mode=hy.CIRCULAR)
+    torch.cuda.synchronize()
+    h = orc.implicit_filter_3d_circular(p, N3)
+    ref = orc.circular_conv3d_fft(u[0].astype(np.float64), h)
+    if gate:
+        ref = ref * g[0]
+    e = rel_err_rows(y.cpu().numpy()[0], ref, point_axes=3)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < 2e-5, e.max()
+
+
+def test_circular3d_wraps_around(torch_cuda):
+    # impulse at the last voxel: c[p] = h[(p + 1) mod 64] on every axis
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 2
+    w = _w3(D=D)
+    p = hi.draw_filter_params(w, seed=53)[0]
+    spec = hy.filter_gen(params_to_dev(p), (N3, N3, N3), mode=hy.CIRCULAR)
+    u = np.zeros(w.shape, np.float32)
+    u[:, :, -1, -1, -1] = 1.0
+    say("periodic 3-D impulse at the last voxel")
+    y = hy.fftconv(to_dev(u, torch.float32), spec, mode=hy.CIRCULAR)
+    torch.cuda.synchronize()
+    want = np.roll(orc.implicit_filter_3d_circular(p, N3), -1, axis=(1, 2, 3))
+    e = rel_err_rows(y.cpu().numpy()[0], want, point_axes=3)
+    assert e.max() < 2e-5, e.max()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_circular3d_operator_order2(torch_cuda, dtype):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = _w3(B=2, D=3, dtype=dtype)
+    v, xs = hi.draw_activations(w, seed=54)
+    params = hi.draw_filter_params(w, seed=55)
+    say(f"periodic 3-D operator order 2 {dtype}")
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims, mode=hy.CIRCULAR) for p in params]
+    y = hy.operator(to_dev(v, dt), [to_dev(x, dt) for x in xs], spectra, mode=hy.CIRCULAR)
+    torch.cuda.synchronize()
+    y = y.float().cpu().numpy().reshape((-1,) + w.dims)
+    hs = [orc.implicit_filter_3d_circular(p, N3) for p in params]
+    vv = v.reshape((-1,) + w.dims)
+    ref = orc.hyena_operator_3d(vv, [x.reshape((-1,) + w.dims) for x in xs],
+                                [np.tile(h, (w.B, 1, 1, 1)) for h in hs], circular=True)
+    e = rel_err_rows(y, ref, point_axes=3)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < (BF16_TOL if dtype == "bf16" else FP32_TOL), e.max()
