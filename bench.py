@@ -42,17 +42,23 @@ def floor_bytes_per_step(w) -> int:
 
 
 def uses_matrix_cores(w) -> bool:
-    """bf16 storage, L = 8192, rows in pairs of one channel: the library's matrix-core kernel."""
-    return w.ndim == 1 and w.dtype == "bf16" and w.dims[0] == 8192 and w.B % 2 == 0
+    """Causal, bf16 storage, L = 8192, rows in pairs of one channel: the library's matrix-core kernel."""
+    return w.mode == "causal" and w.dtype == "bf16" and w.dims[0] == 8192 and w.B % 2 == 0
+
+
+def single_launch_per_order(w) -> bool:
+    """1-D lengths whose transform fits one workgroup: one fused kernel per order."""
+    return w.ndim == 1 and (w.dims[0] <= 16384 or w.mode == "circular")
 
 
 def kernel_key(w) -> str:
+    circ = "_periodic" if w.mode == "circular" else ""
     if w.ndim == 3:
-        return f"conv3d_{w.dims[0]}cubed_{w.dtype}"
+        return f"conv3d_{w.dims[0]}cubed_{w.dtype}{circ}"
     L = w.dims[0]
     if uses_matrix_cores(w):
         return f"conv_mfma_L{L}_bf16_pairs"
-    return f"conv1d_L{L}_{w.dtype}_gate" if L <= 16384 else f"fourstep_L{L}_{w.dtype}"
+    return f"conv1d_L{L}_{w.dtype}_gate{circ}" if single_launch_per_order(w) else f"fourstep_L{L}_{w.dtype}"
 
 
 def arithmetic(w) -> str:
@@ -87,6 +93,7 @@ def cpu_baseline(w, v, xs, params, budget_s: float):
     timed part (as the GPU's spectra are), and building stops once it has taken 3 x budget_s."""
     from oracle import hyena_oracle as orc
     rows = hi.sample_rows(w, 4096, seed=99)
+    circ = w.mode == "circular"
     filt = {}
     n_done, t_used, t_build = 0, 0.0, 0.0
     for b, d in rows:
@@ -96,15 +103,17 @@ def cpu_baseline(w, v, xs, params, budget_s: float):
             tb = time.perf_counter()
             if w.ndim == 1:
                 filt[d] = [orc.implicit_filter_1d(p, w.dims[0], channels=[d]) for p in params]
+            elif circ:
+                filt[d] = [orc.implicit_filter_3d_circular(p, w.dims[0], channels=[d]) for p in params]
             else:
                 filt[d] = [orc.implicit_filter_3d(p, w.dims[0], channels=[d]) for p in params]
             t_build += time.perf_counter() - tb
             print(f"cpu baseline: filters for channel {d} built ({t_build:.1f} s so far)", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
         if w.ndim == 1:
-            orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], filt[d])
+            orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], filt[d], circular=circ)
         else:
-            orc.hyena_operator_3d(v[b, d][None], [x[b, d][None] for x in xs], filt[d])
+            orc.hyena_operator_3d(v[b, d][None], [x[b, d][None] for x in xs], filt[d], circular=circ)
         t_used += time.perf_counter() - t0
         n_done += 1
         if t_used >= budget_s:
@@ -169,23 +178,24 @@ def main():
     xd = [torch.from_numpy(x).to(dev).to(dt) for x in xs]
     pd = [{k: torch.from_numpy(a).to(dev) for k, a in p.items()} for p in params]
     y = torch.empty_like(vd)
-    ws_n = _lib.workspace_bytes(w.order, w.B, w.D, w.dims, _lib.BF16 if w.dtype == "bf16" else _lib.F32)
+    mode = {"causal": _lib.CAUSAL, "linear": _lib.LINEAR, "circular": _lib.CIRCULAR}[w.mode]
+    ws_n = _lib.workspace_bytes(w.order, w.B, w.D, w.dims, _lib.BF16 if w.dtype == "bf16" else _lib.F32, mode)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
 
     # filter spectra (cached per grid): timed separately
-    spectra = [hy.filter_gen(p, w.dims) for p in pd]
+    spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
     torch.cuda.synchronize()
     fg = []
     for _ in range(3):
         t0 = time.perf_counter()
-        spectra = [hy.filter_gen(p, w.dims) for p in pd]
+        spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
         torch.cuda.synchronize()
         fg.append(time.perf_counter() - t0)
     filter_gen_ms = 1e3 * min(fg)
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
-        hy.operator(vd, xd, spectra, y=y, ws=ws)
+        hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
     torch.cuda.synchronize()
 
     # two events on the launch stream bracket the timed region (an event after every step would add
@@ -195,7 +205,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for k in range(args.steps):
-        hy.operator(vd, xd, spectra, y=y, ws=ws)
+        hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -214,7 +224,7 @@ def main():
             scratch.fill_(float(k))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            hy.operator(vd, xd, spectra, y=y, ws=ws)
+            hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
             e1.record(stream)
             marks.append((e0, e1))
         torch.cuda.synchronize()
@@ -259,7 +269,7 @@ def main():
                            "launch_ms": launch_ms, "alg_bytes_per_launch": alg_step,
                            "floor_bytes_per_launch": floor,
                            "floor_frac": floor / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
-    elif w.ndim == 1 and w.dims[0] <= 16384:
+    elif single_launch_per_order(w):
         # the whole step is `order` launches of one fused kernel: its average launch duration
         launch_ms = float(np.mean(step_ms)) / w.order
         bytes_launch = algorithmic_bytes_per_order(w)

@@ -12,6 +12,8 @@ Workloads (the five shapes the Hyena operator is exercised on):
   2  order 3, B=2, D=1024, L=65536,    bf16 storage, v, x_i ~ N(0,1)
   3  order 2, B=1, D=256, L=1048576,   fp32, DNA tokens through a 4x768 embedding
   4  order 2, B=1, D=128, grid 64^3,   fp32, non-causal 3-D (padded to 128^3)
+  5  order 2, B=4, D=768, L=8192,      fp32, periodic 1-D (no padding)
+  6  order 2, B=1, D=128, grid 64^3,   fp32, periodic 3-D (no padding)
 
 Random streams: ``numpy.random.default_rng([seed, stream])``.  Stream 0 draws
 the activations (v, x_1 .. x_N in that order, or tokens then the embedding for
@@ -40,7 +42,7 @@ class Workload:
     D: int
     dims: tuple            # (L,) for 1-D, (nx, ny, nz) for 3-D
     dtype: str             # storage of v, x_i, y: "f32" or "bf16"
-    mode: str              # "causal" (1-D) or "linear" (3-D, zero-padded "same")
+    mode: str              # "causal" (1-D), "linear" (3-D, zero-padded "same") or "circular" (periodic)
     alpha_lo: float
     alpha_hi: float
     features: int          # width of the positional-feature vector
@@ -72,9 +74,9 @@ class Workload:
 
     @property
     def support(self) -> int:
-        """Number of filter taps per channel (L in 1-D; (2n-1)^3 offsets in 3-D)."""
-        if self.ndim == 1:
-            return self.dims[0]
+        """Number of filter taps per channel (L in 1-D; (2n-1)^3 offsets in 3-D, n^3 when periodic)."""
+        if self.ndim == 1 or self.mode == "circular":
+            return self.points
         p = 1
         for n in self.dims:
             p *= 2 * n - 1
@@ -91,6 +93,9 @@ WORKLOADS: List[Workload] = [
     Workload(3, "hyenadna_order2_B1_D256_L1M_f32", 2, 1, 256, (1 << 20,), "f32", "causal", 0.01, 1.0, 64, 64,
              activations="dna"),
     Workload(4, "hyenand3d_order2_B1_D128_64cubed_f32", 2, 1, 128, (64, 64, 64), "f32", "linear", 0.3, 3.0, 96, 64),
+    Workload(5, "periodic_order2_B4_D768_L8192_f32", 2, 4, 768, (8192,), "f32", "circular", 0.3, 3.0, 64, 64),
+    Workload(6, "hyenand3d_periodic_order2_B1_D128_64cubed_f32", 2, 1, 128, (64, 64, 64), "f32", "circular",
+             0.3, 3.0, 96, 64),
 ]
 
 

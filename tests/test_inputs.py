@@ -39,10 +39,12 @@ def test_bf16_matches_torch_conversion():
 
 
 def test_workloads_table():
-    assert [w.order for w in hi.WORKLOADS] == [2, 2, 3, 2, 2]
+    assert [w.order for w in hi.WORKLOADS] == [2, 2, 3, 2, 2, 2, 2]
+    assert [w.mode for w in hi.WORKLOADS] == ["causal"] * 4 + ["linear", "circular", "circular"]
     assert hi.WORKLOADS[1].tokens_channels == 4 * 768 * 8192
     assert hi.WORKLOADS[3].dims == (1 << 20,)
     assert hi.WORKLOADS[4].support == 127 ** 3
+    assert hi.WORKLOADS[5].support == 8192 and hi.WORKLOADS[6].support == 64 ** 3
 
 
 def test_draws_are_seeded_and_shaped():
