@@ -201,3 +201,41 @@ def test_circular3d_operator_order2(torch_cuda, dtype):
     e = rel_err_rows(y, ref, point_axes=3)
     say(f"  max rel err {e.max():.3e}")
     assert e.max() < (BF16_TOL if dtype == "bf16" else FP32_TOL), e.max()
+
+
+def test_operator_workload5_sampled_rows(torch_cuda):
+    # the periodic 1-D workload at full size (B=4, D=768, L=8192, fp32), as the bench runs it
+    w = hi.WORKLOADS[5]
+    import attention_free_long_implicit_amd as hy
+    say("operator workload 5 (periodic 1-D, full size)")
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    y = run_hip_operator(w, v, xs, params, mode=hy.CIRCULAR)
+    rows = hi.sample_rows(w, 12)
+    ref = oracle_rows_1d(w, v, xs, params, rows, circular=True)
+    got = np.stack([y[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < FP32_TOL, e.max()
+    assert np.all(np.isfinite(y))
+
+
+def test_operator_workload6_sampled_channels(torch_cuda):
+    # the periodic 3-D workload at full size (B=1, D=128, 64^3, fp32)
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[6]
+    say("operator workload 6 (periodic 3-D, full size)")
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims, mode=hy.CIRCULAR) for p in params]
+    y = hy.operator(to_dev(v, torch.float32), [to_dev(x, torch.float32) for x in xs], spectra, mode=hy.CIRCULAR)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy()
+    chans = [0, 61, 127]
+    hs = [orc.implicit_filter_3d_circular(p, N3, channels=chans) for p in params]
+    ref = orc.hyena_operator_3d(v[0, chans], [x[0, chans] for x in xs], hs, circular=True)
+    e = rel_err_rows(y[0, chans], ref, point_axes=3)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < FP32_TOL, e.max()
+    assert np.all(np.isfinite(y))
