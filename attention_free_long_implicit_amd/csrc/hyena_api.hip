@@ -77,8 +77,8 @@ size_t elem_bytes(int dtype) { return dtype == HYENA_BF16 ? 2 : 4; }
 // Shape checks shared by every entry point.  On success *points = elements per (b, d) row.
 int check_dims(hyena_dims dims, int mode, int64_t* points) {
   if (mode == HYENA_CIRCULAR) {
-    // periodic boundary: 1-D rows of L = 2^11 .. 2^15 samples (one packed L/2-point transform in LDS),
-    // or the 64^3 grid
+    // periodic boundary: 1-D rows of L = 2^11 .. 2^21 samples (a packed L/2-point transform: in LDS up to
+    // 2^15, multi-pass above), or the 64^3 grid
     if (dims.ndim != 1 && dims.ndim != 3) return HYENA_EINVAL;
     for (int a = 0; a < dims.ndim; ++a)
       if (dims.n[a] <= 0) return HYENA_EINVAL;
@@ -88,7 +88,9 @@ int check_dims(hyena_dims dims, int mode, int64_t* points) {
       return HYENA_OK;
     }
     const int64_t L = dims.n[0];
-    if (!is_pow2(L) || L < (1 << 11) || !single_pass_supported(log2i(L) - 1)) return HYENA_EUNSUPPORTED;
+    if (!is_pow2(L) || L < (1 << 11) ||
+        (!single_pass_supported(log2i(L) - 1) && !fourstep_supported(log2i(L) - 1)))
+      return HYENA_EUNSUPPORTED;
     *points = L;
     return HYENA_OK;
   }
@@ -130,19 +132,20 @@ int kind_of(int mode, hyena_dims dims) {
 }
 bool is3d(int kind) { return kind == K_LIN3 || kind == K_CIRC3; }
 int circ3(int kind) { return kind == K_CIRC3 ? 1 : 0; }
-// 1-D periodic rows of L samples run the single-pass engine on L/2 packed points.
+// 1-D periodic rows of L samples run the 1-D engines on L/2 packed points (all of them filled).
 int circular_log2(int64_t L) { return log2i(L) - 1; }
+// log2 of the packed transform length of a 1-D plan
+int engine_log2(int kind, int64_t L) { return kind == K_CIRC1 ? circular_log2(L) : log2i(L); }
+bool multipass1d(int kind, int64_t L) { return !single_pass_supported(engine_log2(kind, L)); }
 
 // Intermediate bytes per (b, d) row / volume for the multi-pass plans (0: single pass).
 size_t row_intermediate_bytes(int kind, int64_t pts) {
   if (is3d(kind)) return conv3d_volume_bytes(circ3(kind));
-  if (kind == K_CIRC1) return 0;
-  return is_multipass(pts) ? fourstep_row_bytes(log2i(pts)) : 0;
+  return multipass1d(kind, pts) ? fourstep_row_bytes(engine_log2(kind, pts)) : 0;
 }
 size_t filter_intermediate_bytes(int kind, int64_t pts) {
   if (is3d(kind)) return conv3d_filter_volume_bytes(circ3(kind));
-  if (kind == K_CIRC1) return 0;
-  return is_multipass(pts) ? fourstep_row_bytes(log2i(pts)) : 0;
+  return multipass1d(kind, pts) ? fourstep_row_bytes(engine_log2(kind, pts)) : 0;
 }
 size_t taps_per_channel(int kind, int64_t pts) { return is3d(kind) ? conv3d_taps_per_channel(circ3(kind)) : (size_t)pts; }
 
@@ -303,6 +306,9 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
     return hip_status(launch_spectrum3d(h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream, circ3(kind)));
   }
   if ((st = hip_status(launch_filter1d(a, (int)L, h, stream)))) return st;
+  if (kind == K_CIRC1 && multi)
+    return hip_status(launch_spectrum1d_fourstep(circular_log2(L), h, (float2*)spectrum, p->D, (float2*)wsp, chunk,
+                                                 tw, stream, 1));
   if (kind == K_CIRC1)
     return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, p->D, tw, stream, 1));
   if (multi)
@@ -349,8 +355,9 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
     if (is3d(kind))
       return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
                                       stream, circ3(kind)));
-    return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y,
-                                             (float2*)ws, chunk, tw, device_mats(), stream));
+    return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs,
+                                             sp, y, (float2*)ws, chunk, tw, device_mats(), stream,
+                                             kind == K_CIRC1 ? 1 : 0));
   }
   if (kind == K_CIRC1)
     return hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, u, gate, y,
@@ -389,8 +396,9 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
     return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws, chunk,
                                     tw, stream, circ3(kind)));
   if (chunk)
-    return hip_status(launch_conv1d_fourstep(log2i(pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra,
-                                             y, (float2*)ws, chunk, tw, device_mats(), stream));
+    return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
+                                             spectra, y, (float2*)ws, chunk, tw, device_mats(), stream,
+                                             kind == K_CIRC1 ? 1 : 0));
   if (kind == K_CIRC1) {
     const void* cur = v;
     for (int i = 0; i < order; ++i) {
@@ -422,6 +430,8 @@ int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spec
   const int kind = kind_of(mode, dims);
   if (is3d(kind))
     return hip_status(launch_export3d((const float2*)spectrum, (float2*)H, (int)D, stream, circ3(kind)));
+  if (kind == K_CIRC1 && multipass1d(kind, pts))
+    return hip_status(launch_export1d_fourstep(circular_log2(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
   if (kind == K_CIRC1)
     return hip_status(launch_export1d_single(circular_log2(pts), (const float2*)spectrum, (float2*)H, (int)D, stream));
   if (is_multipass(pts))

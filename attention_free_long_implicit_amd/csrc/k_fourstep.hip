@@ -12,6 +12,10 @@
 //                        for every order but the last the same workgroup then runs the next
 //                        order's pass A on the gated tile, so u_i never goes to HBM
 //
+// Periodic boundary (FULL; HyenaND summary, boundary handling: circular convolution, no padding): a
+// row of L = 2M samples fills all M packed values, pass A loads every n1 and pass C keeps every n1,
+// so the same passes compute the L-point circular convolution (the row pass is unchanged).
+//
 // The intermediate is one complex M-vector per row, fp32 for fp32 activations and bf16 words (re low,
 // im high) for bf16 activations (rounded like every stored bf16 value; it halves the pass traffic).
 // Rows are processed in chunks whose intermediates stay resident in L2 / the memory-side cache.  Rows are visited channel-major
@@ -79,7 +83,7 @@ struct FS {
 // pass A / pass C (+A of the next order).  MODE: 0 = A from u (load u, forward columns, store I)
 //                                                1 = C (+A): inverse columns, gate, [forward, store I] or store y
 // grid.x = tiles * rows_in_chunk (row fastest); one workgroup = one column tile of one row.
-template <int LOG2M, bool BF16, int MODE, bool GATE, bool CHAIN>
+template <int LOG2M, bool BF16, int MODE, bool GATE, bool CHAIN, bool FULL>
 __global__ void __launch_bounds__(FS<LOG2M>::TC)
 k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* gate,
           typename Store<BF16>::elem* y, typename Inter<BF16>::T* I, int q0, int nq, int B, int D, Twiddles tw) {
@@ -88,6 +92,8 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   using In = Inter<BF16>;
   constexpr int M = F::M, M1 = F::M1, M2 = F::M2, C = F::C, TC = F::TC;
   constexpr int PER_T = C * M1 / TC;              // tile elements per thread
+  constexpr int PER_IO = FULL ? PER_T : PER_T / 2;  // of them loaded from u / stored to y
+  constexpr int RS = FULL ? 2 * M : M;            // samples per row
   __shared__ float2 lds[lds_padded_size(C * M1)];
   const int t = threadIdx.x;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
@@ -100,9 +106,9 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   auto tile_addr = [&](int p, int c) { return lds_pad(p * C + c); };
 
   if constexpr (MODE == 0) {
-    // load the nonzero half of the packed row: positions n1 < M1/2
-    const auto* urow = u + row * M;
-    static_for<PER_T / 2>([&](auto ii) {
+    // load the packed row: positions n1 < M1/2 (the rest is the zero padding), or all of them (FULL)
+    const auto* urow = u + row * RS;
+    static_for<PER_IO>([&](auto ii) {
       const int e = t + TC * ii.value;
       const int p = e / C, c = e % C;
       lds[tile_addr(p, c)] = St::load2(urow + 2 * ((size_t)(c0 + c) + (size_t)M2 * p));
@@ -115,11 +121,11 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
       lds[tile_addr(p, c)] = In::ld(Irow + (size_t)p * M2 + c0 + c);
     });
     __syncthreads();
-    F::Col::template inverse<true>(lds, tw, t);
-    // gate the causal half (positions n1 < M1/2 are z'[n2 + M2 n1])
-    const auto* grow = GATE ? gate + row * M : nullptr;
-    auto* yrow = CHAIN ? nullptr : y + row * M;
-    static_for<PER_T / 2>([&](auto ii) {
+    F::Col::template inverse<!FULL>(lds, tw, t);
+    // gate the causal half (positions n1 < M1/2 are z'[n2 + M2 n1]), or every position (FULL)
+    const auto* grow = GATE ? gate + row * RS : nullptr;
+    auto* yrow = CHAIN ? nullptr : y + row * RS;
+    static_for<PER_IO>([&](auto ii) {
       const int e = t + TC * ii.value;
       const int p = e / C, c = e % C;
       const size_t j = (size_t)(c0 + c) + (size_t)M2 * p;
@@ -139,7 +145,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
     if constexpr (!CHAIN) return;
     __syncthreads();
   }
-  F::Col::template forward<true>(lds, tw, t);
+  F::Col::template forward<!FULL>(lds, tw, t);
   static_for<PER_T>([&](auto ii) {
     const int e = t + TC * ii.value;
     const int p = e / C, c = e % C;
@@ -147,8 +153,8 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   });
 }
 
-// Spectrum pass A: fp32 taps h[d, 0:L) (one "row" per channel, B = 1).
-template <int LOG2M>
+// Spectrum pass A: fp32 taps h[d, 0:M) zero-padded, or h[d, 0:2M) (FULL; one "row" per channel, B = 1).
+template <int LOG2M, bool FULL>
 __global__ void __launch_bounds__(FS<LOG2M>::TC)
 k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
   using F = FS<LOG2M>;
@@ -160,14 +166,14 @@ k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
   const int ql = lb % nq, tile = lb / nq;
   const int d = q0 + ql;
   const int c0 = tile * C;
-  const float* hrow = h + (size_t)d * M;
-  static_for<PER_T / 2>([&](auto ii) {
+  const float* hrow = h + (size_t)d * (FULL ? 2 * M : M);
+  static_for<FULL ? PER_T : PER_T / 2>([&](auto ii) {
     const int e = t + TC * ii.value;
     const int p = e / C, c = e % C;
     lds[lds_pad(p * C + c)] = Store<false>::load2(hrow + 2 * ((size_t)(c0 + c) + (size_t)M2 * p));
   });
   __syncthreads();
-  F::Col::template forward<true>(lds, tw, t);
+  F::Col::template forward<!FULL>(lds, tw, t);
   float2* Irow = I + (size_t)ql * M;
   static_for<PER_T>([&](auto ii) {
     const int e = t + TC * ii.value;
@@ -329,11 +335,11 @@ namespace {
 template <int LOG2M>
 size_t fs_row_bytes() { return (size_t)(1 << LOG2M) * sizeof(float2); }
 
-template <int LOG2M, bool BF16>
+template <int LOG2M, bool BF16, bool FULL>
 hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
                           void* y, float2* I, int chunk, const Twiddles& tw, const void* mats, hipStream_t s) {
-  // bf16 plans with 128-point columns run their column passes on the matrix cores
-  const bool mc = BF16 && mats && fs_cols_mfma_supported(LOG2M);
+  // bf16 causal plans with 128-point columns run their column passes on the matrix cores
+  const bool mc = BF16 && !FULL && mats && fs_cols_mfma_supported(LOG2M);
   using F = FS<LOG2M>;
   using E = typename Store<BF16>::elem;
   using IT = typename Inter<BF16>::T;
@@ -346,7 +352,7 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
     if (mc)
       (void)launch_fs_cols_mfma(LOG2M, 0, false, false, v, nullptr, nullptr, Ib, q0, nq, B, D, mats, s);
     else
-      hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
+      hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
                          (const E*)v, (const E*)nullptr, (E*)nullptr, Ib, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
       hipLaunchKernelGGL((k_fs_rows<LOG2M, 0, BF16>), dim3(groups * nq), dim3(F::TR), 0, s, Ib,
@@ -355,13 +361,13 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
         (void)launch_fs_cols_mfma(LOG2M, 1, x[i] != nullptr, i + 1 < order, nullptr, x[i], y, Ib, q0, nq, B, D, mats,
                                   s);
       else if (i + 1 < order)
-        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, true>), dim3(tiles * nq), dim3(F::TC), 0, s,
+        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, true, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
                            (const E*)nullptr, (const E*)x[i], (E*)nullptr, Ib, q0, nq, B, D, tw);
       else if (x[i])
-        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
+        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
                            (const E*)nullptr, (const E*)x[i], (E*)y, Ib, q0, nq, B, D, tw);
       else
-        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, false, false>), dim3(tiles * nq), dim3(F::TC), 0, s,
+        hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
                            (const E*)nullptr, (const E*)nullptr, (E*)y, Ib, q0, nq, B, D, tw);
     }
     hipError_t e = hipGetLastError();
@@ -370,7 +376,7 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
   return hipSuccess;
 }
 
-template <int LOG2M>
+template <int LOG2M, bool FULL>
 hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
                               hipStream_t s) {
   using F = FS<LOG2M>;
@@ -378,7 +384,7 @@ hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int 
   const int groups = (F::M1 / 2) / F::G;
   for (int q0 = 0; q0 < D; q0 += chunk) {
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
-    hipLaunchKernelGGL((k_fs_cols_taps<LOG2M>), dim3(tiles * nq), dim3(F::TC), 0, s, h, I, q0, nq, tw);
+    hipLaunchKernelGGL((k_fs_cols_taps<LOG2M, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s, h, I, q0, nq, tw);
     hipLaunchKernelGGL((k_fs_rows<LOG2M, 1, false>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const float2*)nullptr,
                        Hs, q0, nq, 1, tw);
     hipError_t e = hipGetLastError();
@@ -409,12 +415,15 @@ hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int 
 
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, const void* mats, hipStream_t s) {
+                                  const Twiddles& tw, const void* mats, hipStream_t s, int full) {
   switch (log2L) {
-#define X(n)                                                                                  \
-  case n:                                                                                     \
-    return bf16 ? fs_conv_launch<n, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s)     \
-                : fs_conv_launch<n, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s);
+#define X(n)                                                                                              \
+  case n:                                                                                                 \
+    if (full)                                                                                             \
+      return bf16 ? fs_conv_launch<n, true, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s)   \
+                  : fs_conv_launch<n, false, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s); \
+    return bf16 ? fs_conv_launch<n, true, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s)    \
+                : fs_conv_launch<n, false, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s);
     HYENA_FS_CASES(X)
 #undef X
   }
@@ -422,9 +431,12 @@ hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, 
 }
 
 hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
-                                      const Twiddles& tw, hipStream_t s) {
+                                      const Twiddles& tw, hipStream_t s, int full) {
   switch (log2L) {
-#define X(n) case n: return fs_spectrum_launch<n>(h, Hs, D, I, chunk, tw, s);
+#define X(n)                                                                           \
+  case n:                                                                              \
+    return full ? fs_spectrum_launch<n, true>(h, Hs, D, I, chunk, tw, s)               \
+                : fs_spectrum_launch<n, false>(h, Hs, D, I, chunk, tw, s);
     HYENA_FS_CASES(X)
 #undef X
   }

@@ -16,16 +16,17 @@ hipError_t launch_spectrum1d_single(int log2L, const float* h, float2* Hs, int D
                                     hipStream_t s, int full = 0);
 hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
 
-// ---- 1-D, multi-pass (2^15 <= L <= 2^20): I is a workspace of `chunk` rows of L complex values.
-// x[i] may be NULL for the last order only (no gate).
+// ---- 1-D, multi-pass: an M = 2^log2L point packed transform, 15 <= log2L <= 20; I is a workspace of
+// `chunk` rows of M complex values.  full = 0: causal, rows of M samples; full = 1: periodic, rows of
+// 2M samples.  x[i] may be NULL for the last order only (no gate).
 bool fourstep_supported(int log2L);
 size_t fourstep_row_bytes(int log2L);
 // mats: the matrix-core table (bf16 L = 2^15, 2^16 run their column passes on the matrix cores), or NULL.
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, const void* mats, hipStream_t s);
+                                  const Twiddles& tw, const void* mats, hipStream_t s, int full = 0);
 hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
-                                      const Twiddles& tw, hipStream_t s);
+                                      const Twiddles& tw, hipStream_t s, int full = 0);
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
 
 // ---- 3-D, 64^3 grid: circ = 0 zero-padded to 128^3 (non-causal "same" convolution),

@@ -61,7 +61,7 @@ typedef enum {
 } hyena_mode;
 
 /* Grid shape: 1-D {1, {L, 0, 0}}; 3-D {3, {nx, ny, nz}}.
- * Supported: HYENA_CAUSAL L = 2^k, 2^10 <= L <= 2^20; HYENA_CIRCULAR 1-D L = 2^k, 2^11 <= L <= 2^15,
+ * Supported: HYENA_CAUSAL L = 2^k, 2^10 <= L <= 2^20; HYENA_CIRCULAR 1-D L = 2^k, 2^11 <= L <= 2^21,
  * or nx = ny = nz = 64; HYENA_LINEAR nx = ny = nz = 64. */
 typedef struct {
   int32_t ndim;
@@ -83,7 +83,8 @@ typedef struct {
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_filter_gen needs: room for the taps (used when h_time is NULL) plus, for
- * multi-pass lengths (L > 16384), the transform intermediate of a chunk of channels. */
+ * multi-pass lengths (causal L > 16384, periodic L > 32768, 3-D), the transform intermediate of a
+ * chunk of channels. */
 int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_fftconv / hyena_operator need (0 when the transform fits on chip). */

@@ -68,6 +68,11 @@ def test_size_queries(lib):
         assert st == 0 and n == 0
         st, n = _size(lib.hyena_filter_workspace_bytes, L.dims_of([Lc]), L.CIRCULAR, 16)
         assert st == 0 and n == 16 * Lc * 4
+    # long periodic rows: multi-pass on L/2 packed points, rows of L/2 complex fp32 values
+    st, n = _size(lib.hyena_workspace_bytes, 2, 1, 3, L.dims_of([1 << 21]), L.F32, L.CIRCULAR)
+    assert st == 0 and n == 3 * (1 << 20) * 8
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([1 << 16]), L.CIRCULAR, 2)
+    assert st == 0 and n == 2 * (1 << 15) * 8
     # periodic 3-D: 64 x 64 x 33 bins per channel, intermediate 64 x-slabs of 64 x 33 per volume
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.CIRCULAR, 128)
     assert st == 0 and n == 128 * 64 * 64 * 33 * 8
@@ -86,7 +91,7 @@ def test_size_queries(lib):
     ([64, 64, 64], L.CAUSAL, L.EINVAL),      # causal mode needs 1-D
     ([32, 32, 32], L.LINEAR, L.EUNSUPPORTED),  # only the 64^3 grid is planned
     ([1024], L.CIRCULAR, L.EUNSUPPORTED),    # periodic rows: 2^11 .. 2^15
-    ([1 << 16], L.CIRCULAR, L.EUNSUPPORTED),
+    ([1 << 22], L.CIRCULAR, L.EUNSUPPORTED),
     ([6144], L.CIRCULAR, L.EUNSUPPORTED),
     ([0], L.CIRCULAR, L.EINVAL),
     ([32, 32, 32], L.CIRCULAR, L.EUNSUPPORTED),   # periodic 3-D: the 64^3 grid only

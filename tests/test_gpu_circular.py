@@ -239,3 +239,79 @@ def test_operator_workload6_sampled_channels(torch_cuda):
     say(f"  max rel err {e.max():.3e}")
     assert e.max() < FP32_TOL, e.max()
     assert np.all(np.isfinite(y))
+
+
+# ---------------------------------------------------------------- long periodic rows (multi-pass)
+LONG_L = [1 << 16, 1 << 17, 1 << 21]
+
+
+@pytest.mark.parametrize("L", [1 << 16, 1 << 21])
+def test_circular_long_filter_spectrum(torch_cuda, L):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 3
+    w = _w(L, D=D)
+    p = hi.draw_filter_params(w, seed=400 + L % 97)[0]
+    say(f"periodic multi-pass filter_gen L={L}")
+    spec = hy.filter_gen(params_to_dev(p), (L,), mode=hy.CIRCULAR)
+    H = hy.spectrum_export(spec, (L,), D, mode=hy.CIRCULAR)
+    torch.cuda.synchronize()
+    Href = np.fft.rfft(orc.implicit_filter_1d(p, L))
+    Hg = H.cpu().numpy().astype(np.complex128)
+    e = np.linalg.norm(Hg - Href, axis=1) / np.linalg.norm(Href, axis=1)
+    assert e.max() < 1e-5, e.max()
+
+
+@pytest.mark.parametrize("L", LONG_L)
+def test_circular_long_operator_fp32_chunked(torch_cuda, L):
+    # B*D = 3 rows through a workspace of two rows: chunks of 2 and 1
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = _w(L, B=1, D=3)
+    v, xs = hi.draw_activations(w, seed=L % 1009)
+    params = hi.draw_filter_params(w, seed=L % 1013)
+    say(f"periodic multi-pass operator fp32 L={L}")
+    spectra = [hy.filter_gen(params_to_dev(p), (L,), mode=hy.CIRCULAR) for p in params]
+    ws = torch.empty(2 * (L // 2) * 8, dtype=torch.uint8, device="cuda")
+    y = hy.operator(to_dev(v, torch.float32), [to_dev(x, torch.float32) for x in xs], spectra, ws=ws,
+                    mode=hy.CIRCULAR)
+    torch.cuda.synchronize()
+    rows = [(0, d) for d in range(w.D)]
+    ref = oracle_rows_1d(w, v, xs, params, rows, circular=True)
+    e = rel_err_rows(y.cpu().numpy()[0], ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < FP32_TOL, e.max()
+
+
+@pytest.mark.parametrize("L", [1 << 16, 1 << 17])
+def test_circular_long_operator_bf16(torch_cuda, L):
+    w = _w(L, B=2, D=2, dtype="bf16")
+    v, xs = hi.draw_activations(w, seed=L % 1019)
+    params = hi.draw_filter_params(w, seed=L % 1021)
+    import attention_free_long_implicit_amd as hy
+    say(f"periodic multi-pass operator bf16 L={L}")
+    y = run_hip_operator(w, v, xs, params, mode=hy.CIRCULAR)
+    rows = [(b, d) for b in range(w.B) for d in range(w.D)]
+    ref = oracle_rows_1d(w, v, xs, params, rows, circular=True)
+    got = np.stack([y[b, d] for b, d in rows])
+    e = rel_err_rows(got, ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < BF16_TOL, e.max()
+
+
+def test_circular_long_wraps_around(torch_cuda):
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L, D = 1 << 16, 2
+    w = _w(L, B=1, D=D)
+    p = hi.draw_filter_params(w, seed=78)[0]
+    h = torch.empty((D, L), dtype=torch.float32, device="cuda")
+    spec = hy.filter_gen(params_to_dev(p), (L,), h_time=h, mode=hy.CIRCULAR)
+    u = np.zeros(w.shape, np.float32)
+    u[:, :, L - 1] = 1.0
+    say("periodic multi-pass impulse at the last sample")
+    y = hy.fftconv(to_dev(u, torch.float32), spec, None, mode=hy.CIRCULAR)
+    torch.cuda.synchronize()
+    want = np.roll(h.cpu().numpy().astype(np.float64), -1, axis=1)[None]
+    e = rel_err_rows(y.cpu().numpy(), want)
+    assert e.max() < FP32_TOL, e.max()
