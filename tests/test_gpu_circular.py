@@ -203,7 +203,7 @@ def test_circular3d_operator_order2(torch_cuda, dtype):
     assert e.max() < (BF16_TOL if dtype == "bf16" else FP32_TOL), e.max()
 
 
-def test_operator_workload5_sampled_rows(torch_cuda):
+def test_operator_periodic_f32_B4_D768_L8192_sampled_rows(torch_cuda):
     # the periodic 1-D workload at full size (B=4, D=768, L=8192, fp32), as the bench runs it
     w = hi.WORKLOADS[5]
     import attention_free_long_implicit_amd as hy
@@ -220,7 +220,7 @@ def test_operator_workload5_sampled_rows(torch_cuda):
     assert np.all(np.isfinite(y))
 
 
-def test_operator_workload6_sampled_channels(torch_cuda):
+def test_operator3d_periodic_f32_D128_64cubed_sampled_channels(torch_cuda):
     # the periodic 3-D workload at full size (B=1, D=128, 64^3, fp32)
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy

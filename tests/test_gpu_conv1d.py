@@ -108,7 +108,7 @@ def test_delta_filter_gives_product_of_gates(torch_cuda):
     assert np.max(np.abs(y - ref)) < 1e-5 * np.max(np.abs(ref))
 
 
-def test_operator_workload0_all_rows(torch_cuda):
+def test_operator_f32_B1_D16_L1024_all_rows(torch_cuda):
     w = hi.WORKLOADS[0]
     v, xs = hi.draw_activations(w)
     params = hi.draw_filter_params(w)
@@ -122,7 +122,7 @@ def test_operator_workload0_all_rows(torch_cuda):
     assert e.max() < FP32_TOL
 
 
-def test_operator_workload1_sampled_rows(torch_cuda):
+def test_operator_bf16_B4_D768_L8192_sampled_rows(torch_cuda):
     w = hi.WORKLOADS[1]
     v, xs = hi.draw_activations(w)
     params = hi.draw_filter_params(w)

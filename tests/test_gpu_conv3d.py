@@ -91,7 +91,7 @@ def test_conv3d_delta_filter(torch_cuda):
     assert e.max() < 1e-2, e.max()
 
 
-def test_operator_workload4_sampled_channels(torch_cuda):
+def test_operator3d_f32_D128_64cubed_sampled_channels(torch_cuda):
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
     w = hi.WORKLOADS[4]

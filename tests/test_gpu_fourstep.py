@@ -91,7 +91,7 @@ def test_fourstep_no_gate_and_chunk_invariance(torch_cuda):
     assert rel_err_rows(c.cpu().numpy()[0], ref).max() < 5e-5
 
 
-def test_operator_workload2_sampled_rows(torch_cuda):
+def test_operator_bf16_order3_B2_D1024_L65536_sampled_rows(torch_cuda):
     w = hi.WORKLOADS[2]
     say("operator workload 2 (order 3, B=2 D=1024 L=65536, bf16): drawing inputs")
     v, xs = hi.draw_activations(w)
@@ -108,7 +108,7 @@ def test_operator_workload2_sampled_rows(torch_cuda):
     assert np.all(np.isfinite(y))
 
 
-def test_operator_workload3_sampled_rows(torch_cuda):
+def test_operator_f32_B1_D256_L1M_dna_sampled_rows(torch_cuda):
     w = hi.WORKLOADS[3]
     say("operator workload 3 (HyenaDNA order 2, B=1 D=256 L=1M, fp32): drawing inputs")
     v, xs = hi.draw_activations(w)
