@@ -63,6 +63,10 @@ struct MfmaChain {
   int order;
 };
 
+// Word 3 of a raw buffer descriptor on this architecture family: DATA_FORMAT = 32-bit (bits 15..18 = 4),
+// no swizzle, no index stride; offsets beyond the record count read zero.
+constexpr int kRawBufferWord3 = 0x00020000;
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -157,10 +161,6 @@ template <int TT>
 __device__ __forceinline__ float elem_f32(const u32x4& g) {
   return (TT & 1) ? hi_f32(g[TT >> 1]) : lo_f32(g[TT >> 1]);
 }
-__device__ __forceinline__ void load_blocks(const bf16x8* p, bf16x8 (&M)[mf::NBLK]) {
-#pragma unroll
-  for (int b = 0; b < mf::NBLK; ++b) M[b] = p[b * 64];
-}
 
 // Pass 1 / pass 1' column mapping: wave w, lane j (= lane % 32), tile t handle column c = 256 w + 8 j + t
 // (n3 = c % 32, n2 = c / 32), so each lane's 8 tiles cover 8 consecutive samples: one 16-byte access per
@@ -200,7 +200,6 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   const int t = tq, w = t >> 6, l = t & 63, j = l & 31, h = l >> 5;
   const int c0 = 256 * w + 8 * j;
   const int n2c = 8 * w + (j >> 2), n3c = 8 * (j & 3);   // tile t: n2 = n2c, n3 = n3c + t
-  const bf16x8* slab_mats = mats + NFIX * 64 + l;
   const uint32_t* __restrict__ Hc = ch.spectrum[ord];
   const __bf16* gate = ch.gate[ord];
 
@@ -208,19 +207,37 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   // Ma = pass 2, Mb = pass 3, then Ma = pass 3', Mb = pass 2', then the next slab's pass 2 and 3.
   // The first slab's matrices and filter spectrum are in flight during pass 1.
   bf16x8 Ma[NBLK], Mb[NBLK];
-  load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF2 * NBLK * 64, Ma);
-  load_blocks(slab_mats + (size_t)w * SLAB_TABLE * 64 + MF3 * NBLK * 64, Mb);
+  // The matrix table and the spectrum are read through buffer descriptors: the per-lane part of the
+  // offset is fixed, the block / register part (and the mirror choice, uniform per wave) stays in
+  // scalar registers, so a slab's 32 loads cost no vector instructions for their addresses.
+  const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(mats + NFIX * 64), (short)0, 16 * SLAB_TABLE * 64 * 16, kRawBufferWord3);
+  const int mvo = l * 16;
+  // blocks of matrix `which` of slab k1s (scalar) into M
+  auto load_mat = [&](int k1s_, int which, bf16x8 (&M)[NBLK]) {
+#pragma unroll
+    for (int b = 0; b < NBLK; ++b)
+      M[b] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                            mrs, mvo, ((k1s_ * SLAB_TABLE + which * NBLK + b) * 64) * 16, 0));
+  };
   // Filter spectrum: only slabs 0..8 are stored.  h is real, so H[N - k] = conj(H[k]); bin N - k of
   // slab k1 > 8 is register 15 - v of lane 63 - l in slab 16 - k1, read mirrored; the conjugation (sign
   // of the imaginary half) is applied where the value is used, so the load stays in flight until then.
   uint32_t hw[16];
+  const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Hc + (size_t)d * PAIR_SLABS * 16 * 64), (short)0, PAIR_SLABS * 16 * 64 * 4, kRawBufferWord3);
+  const int ws = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto load_spectrum = [&](int k1) {
     const bool mirror = k1 > 8;
-    const uint32_t* hp = Hc + ((size_t)d * PAIR_SLABS + (mirror ? 16 - k1 : k1)) * 16 * 64 + (mirror ? 63 - l : l);
+    const int slab = (mirror ? 16 - k1 : k1) * (16 * 64 * 4);
+    const int vo = (mirror ? 63 - l : l) * 4;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) hw[v] = hp[(mirror ? 15 - v : v) * 64];
+    for (int v = 0; v < 16; ++v)
+      hw[v] = __builtin_amdgcn_raw_buffer_load_b32(hrs, vo, slab + (mirror ? 15 - v : v) * 256, 0);
   };
-  load_spectrum(w);
+  load_mat(ws, MF2, Ma);
+  load_mat(ws, MF3, Mb);
+  load_spectrum(ws);
   {
     static_for<8>([&](auto tt) {
       constexpr int TT = tt.value;
@@ -236,9 +253,8 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   // ---------------- passes 2, 3, 3', 2' per slab k1 (wave w owns k1 = w, w+4, w+8, w+12)
   for (int it = 0; it < 4; ++it) {
     const int k1 = w + 4 * it;
+    const int k1s = ws + 4 * it;   // the same slab index, in a scalar register
     uint32_t* sl = S + k1 * SLAB;
-    const bf16x8* ms = slab_mats + (size_t)k1 * SLAB_TABLE * 64;
-    const bf16x8* ms_next = slab_mats + (size_t)(it < 3 ? k1 + 4 : k1) * SLAB_TABLE * 64;
     bf16x8 xr_lo, xr_hi, xi_lo, xi_hi;
     f32x16 dr, di;
     // pass 2: data on A (rows n3 = j, K = n2 from LDS: element (n2, n3) at n2 * ROW + n3), matrix on B
@@ -253,28 +269,28 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
       split8(clo, xr_lo, xi_lo);
       split8(chi, xr_hi, xi_hi);
       dft32<false, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
-      load_blocks(ms + MI3 * NBLK * 64, Ma);
+      load_mat(k1s, MI3, Ma);
     }
     // twiddle W_1024^{n3 k2} (k2 = j, n3 = row of v); pass 3: matrix on A (rows k3, input n3 in accumulator
     // order), data on B -> lane = k2, registers = k3
     pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, p2[v]); }, xr_lo, xr_hi, xi_lo, xi_hi);
     dft32<false, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
-    load_blocks(ms + MI2 * NBLK * 64, Mb);
+    load_mat(k1s, MI2, Mb);
     // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N in this exact order.
     // pass 3': data on A (rows k2 = j, input k3 in accumulator order), matrix on B -> lane = n3,
     // registers = k2
-    const uint32_t flip = k1 > 8 ? 0x80000000u : 0u;
+    const uint32_t flip = k1s > 8 ? 0x80000000u : 0u;
     pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, unpack_c(hw[v] ^ flip)); }, xr_lo, xr_hi, xi_lo,
                   xi_hi);
-    if (it < 3) load_spectrum(k1 + 4);
+    if (it < 3) load_spectrum(k1s + 4);
     f32x16 er, ei;
     dft32<true, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
-    if (it < 3) load_blocks(ms_next + MF2 * NBLK * 64, Ma);
+    if (it < 3) load_mat(k1s + 4, MF2, Ma);
     // conj twiddle W_1024^{n3 k2} (n3 = j, k2 = row of v); pass 2': matrix on A (rows n2, input k2 in
     // accumulator order), data on B -> lane = n3, registers = n2; store (n2, n3) at n2 * ROW + n3
     pack_operands(er, ei, [&](int v, float2 x) { return cmulc(x, p2[v]); }, xr_lo, xr_hi, xi_lo, xi_hi);
     dft32<true, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
-    if (it < 3) load_blocks(ms_next + MF3 * NBLK * 64, Mb);
+    if (it < 3) load_mat(k1s + 4, MF3, Mb);
 #pragma unroll
     for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2(er[v], ei[v]);
   }
