@@ -293,66 +293,6 @@ __global__ void k3_export(const float2* __restrict__ Hs, float2* __restrict__ H)
       cscale(Hs[(size_t)d * TILES * MP * COLS + idx], 0.5f / C::kSpecScale);
 }
 
-// ------------------------------------------------------------------ 3-D filter taps
-// h[d, rx, ry, rz] = (W2 SiLU(W1 phi(r) + b1) + b2)_d * exp(-alpha_d |r| / n) on offsets [-(n-1), n-1]^3
-// (zero-padded geometry) or [-n/2, n/2)^3 (periodic), tap index K3::tap(r) per axis;
-// phi(r): per axis (x, y, z) 16 sines then 16 cosines of 2 pi f r_a / n, f = 1..16 (phases reduced mod n).
-template <class G, int F, int H>
-__global__ void __launch_bounds__(256)
-k_filter3d(FilterArgs a, float* __restrict__ h) {
-  using C = K3<G>;
-  constexpr int N = C::N, W = C::W, NP = W * W * W, TP = 64, PER_AX = F / 6;
-  constexpr int R0 = C::PAD ? N - 1 : N / 2;    // tap index of offset 0
-  __shared__ float phi[TP][F + 1];
-  __shared__ float w1t[F][H + 1];
-  __shared__ float act[TP][H + 1];
-  __shared__ float rad[TP];
-  const int tid = threadIdx.x;
-  const int p0 = blockIdx.x * TP;
-  for (int i = tid; i < F * H; i += 256) {
-    const int j = i / F, f = i % F;
-    w1t[f][j] = a.W1[i];
-  }
-  for (int i = tid; i < TP * 3 * PER_AX; i += 256) {
-    const int pp = i / (3 * PER_AX), rem = i % (3 * PER_AX);
-    const int ax = rem / PER_AX, f = rem % PER_AX;
-    const int pos = min(p0 + pp, NP - 1);
-    const int r3[3] = {pos / (W * W) - R0, (pos / W) % W - R0, pos % W - R0};
-    const int ph = (((f + 1) * r3[ax]) % N + N) % N;
-    float s, c;
-    sincospif(2.0f * (float)ph / (float)N, &s, &c);
-    phi[pp][ax * 2 * PER_AX + f] = s;
-    phi[pp][ax * 2 * PER_AX + PER_AX + f] = c;
-    if (ax == 0 && f == 0) {
-      const float fx = (float)r3[0] / N, fy = (float)r3[1] / N, fz = (float)r3[2] / N;
-      rad[pp] = sqrtf(fx * fx + fy * fy + fz * fz);
-    }
-  }
-  __syncthreads();
-  for (int i = tid; i < TP * H; i += 256) {
-    const int pp = i / H, j = i % H;
-    float z = a.b1[j];
-#pragma unroll 8
-    for (int f = 0; f < F; ++f) z = fmaf(w1t[f][j], phi[pp][f], z);
-    act[pp][j] = z / (1.0f + expf(-z));
-  }
-  __syncthreads();
-  const int pp = tid % TP, wv = tid / TP;
-  float av[H];
-#pragma unroll
-  for (int j = 0; j < H; ++j) av[j] = act[pp][j];
-  const int pos = p0 + pp;
-  if (pos >= NP) return;
-  const float rr = rad[pp];
-  for (int dd = wv; dd < a.D; dd += 4) {
-    const float* w2 = a.W2 + (size_t)dd * H;
-    float g = a.b2[dd];
-#pragma unroll
-    for (int j = 0; j < H; ++j) g = fmaf(w2[j], av[j], g);
-    h[(size_t)dd * NP + pos] = g * expf(-a.alpha[dd] * rr);
-  }
-}
-
 // ------------------------------------------------------------------ host side
 bool grid3d_supported(int64_t nx, int64_t ny, int64_t nz) { return nx == k3::N && ny == k3::N && nz == k3::N; }
 size_t conv3d_volume_bytes(int circ) {
@@ -436,16 +376,6 @@ hipError_t launch_conv3d(int bf16, int order, int B, int D, const void* v, const
                 : conv3d_launch_t<Geo3<true>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
   return bf16 ? conv3d_launch_t<Geo3<false>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s)
               : conv3d_launch_t<Geo3<false>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
-}
-
-hipError_t launch_filter3d(const FilterArgs& a, float* h, hipStream_t s, int circ) {
-  if (a.F != 96 || a.H != 64) return hipErrorInvalidValue;
-  const int np = (int)conv3d_taps_per_channel(circ);
-  if (circ)
-    hipLaunchKernelGGL((k_filter3d<Geo3<true>, 96, 64>), dim3((np + 63) / 64), dim3(256), 0, s, a, h);
-  else
-    hipLaunchKernelGGL((k_filter3d<Geo3<false>, 96, 64>), dim3((np + 63) / 64), dim3(256), 0, s, a, h);
-  return hipGetLastError();
 }
 
 hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
