@@ -258,6 +258,11 @@ def main():
     }
     if cold is not None:
         out["cold_cache"] = cold
+    # filter network (a GEMM pair per position) for all orders; the time includes the spectrum build
+    net_flop = 2.0 * w.order * w.support * w.hidden * (w.features + w.D)
+    out["filter_gen"] = {"ms": filter_gen_ms, "network_gflop": net_flop / 1e9,
+                         "achieved_tflops": net_flop / (filter_gen_ms / 1e3) / 1e12, "peak_tflops": 157.3,
+                         "note": "all orders; network flops over the whole filter build (spectra included)"}
     key = kernel_key(w)
     if uses_matrix_cores(w) and w.order <= 8:
         # the whole step is one launch of the matrix-core kernel: all orders, u_i kept on chip
