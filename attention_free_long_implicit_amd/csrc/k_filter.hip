@@ -11,8 +11,9 @@
 //
 // Phases f t (f r) are reduced modulo L (n) in integers before the sine, so every angle is exact.
 // A workgroup owns a tile of 64 positions x 128 channels: the hidden layer of its 64 positions is
-// formed once, then the second layer runs as a small GEMM from LDS with a 4 x 8 register tile per
-// thread.  W1 and the features, then W2 and the hidden activations, share one LDS region.
+// formed once (a 4 positions x 4 units register tile per thread), then the second layer runs as a
+// small GEMM from LDS with a 4 x 8 register tile per thread; both read their operands as 16-byte
+// LDS vectors.  W1 and the features, then W2 and the hidden activations, share one LDS region.
 #include "launch.h"
 
 namespace hyena {
@@ -66,16 +67,16 @@ __global__ void __launch_bounds__(flt::T)
 k_filter_tiles(FilterArgs a, G geo, float* __restrict__ h) {
   using namespace flt;
   static_assert(H == 64 && (TP * H) % T == 0, "tile shape");
-  constexpr int PHASE1 = F * H + TP * (F + 1);          // w1t[F][H], phi[TP][F+1]
+  constexpr int PHASE1 = F * H + F * (TP + 4);          // w1t[F][H], phiT[F][TP+4]
   constexpr int PHASE2 = H * CB + H * (TP + 4);         // w2t[H][CB], actT[H][TP+4]
   __shared__ __align__(16) float lds[PHASE1 > PHASE2 ? PHASE1 : PHASE2];
   const int tid = threadIdx.x;
   const int npos = geo.count();
   const int p0 = blockIdx.x * TP, c0 = blockIdx.y * CB;
 
-  // phase 1: W1 transposed and the features of the tile's positions
+  // phase 1: W1 transposed and the features of the tile's positions (feature-major)
   float* w1t = lds;
-  float* phi = lds + F * H;
+  float* phiT = lds + F * H;
   for (int i = tid; i < F * H; i += T) {
     const int j = i / F, f = i % F;
     w1t[f * H + j] = a.W1[i];
@@ -86,24 +87,34 @@ k_filter_tiles(FilterArgs a, G geo, float* __restrict__ h) {
     int cs, cc;
     float s, c;
     geo.template pair<F>(pos, q, cs, cc, s, c);
-    phi[p * (F + 1) + cs] = s;
-    phi[p * (F + 1) + cc] = c;
+    phiT[cs * (TP + 4) + p] = s;
+    phiT[cc * (TP + 4) + p] = c;
   }
   __syncthreads();
-  // hidden layer: thread owns unit j = tid % H for positions p = tid / H + 4 k
-  constexpr int NA = TP * H / T;
-  float act[NA];
+  // hidden layer: thread owns positions 4 hp .. 4 hp + 3 and units 4 hj .. 4 hj + 3
+  const int hp = tid % (TP / 4), hj = tid / (TP / 4);
+  float act[4][4];
   {
-    const int j = tid % H;
-    const float b1 = a.b1[j];
+    const float bj[4] = {a.b1[4 * hj], a.b1[4 * hj + 1], a.b1[4 * hj + 2], a.b1[4 * hj + 3]};
 #pragma unroll
-    for (int k = 0; k < NA; ++k) {
-      const int p = tid / H + (T / H) * k;
-      float z = b1;
-#pragma unroll 8
-      for (int f = 0; f < F; ++f) z = fmaf(w1t[f * H + j], phi[p * (F + 1) + f], z);
-      act[k] = z / (1.0f + expf(-z));
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) act[i][k] = bj[k];
+#pragma unroll 4
+    for (int f = 0; f < F; ++f) {
+      const float4 pv = *reinterpret_cast<const float4*>(phiT + f * (TP + 4) + 4 * hp);
+      const float4 wv = *reinterpret_cast<const float4*>(w1t + f * H + 4 * hj);
+      const float x[4] = {pv.x, pv.y, pv.z, pv.w};
+      const float y[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) act[i][k] = fmaf(x[i], y[k], act[i][k]);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) act[i][k] = __fdividef(act[i][k], 1.0f + __expf(-act[i][k]));   // SiLU
   }
   __syncthreads();
 
@@ -114,11 +125,10 @@ k_filter_tiles(FilterArgs a, G geo, float* __restrict__ h) {
     const int j = i / CB, c = i % CB;
     w2t[i] = (c0 + c < a.D) ? a.W2[(size_t)(c0 + c) * H + j] : 0.0f;
   }
-  {
-    const int j = tid % H;
 #pragma unroll
-    for (int k = 0; k < NA; ++k) actT[j * (TP + 4) + tid / H + (T / H) * k] = act[k];
-  }
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<float4*>(actT + (4 * hj + k) * (TP + 4) + 4 * hp) =
+        make_float4(act[0][k], act[1][k], act[2][k], act[3][k]);
   __syncthreads();
 
   // second layer: positions 4 pg .. 4 pg + 3, channels 8 cg .. 8 cg + 7 of the tile
@@ -154,7 +164,7 @@ k_filter_tiles(FilterArgs a, G geo, float* __restrict__ h) {
     const float b2 = a.b2[d], al = a.alpha[d];
     float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (acc[i][c] + b2) * expf(-al * wa[i]);
+    for (int i = 0; i < 4; ++i) v[i] = (acc[i][c] + b2) * __expf(-al * wa[i]);
     float* dst = h + (size_t)d * npos + pos0;
     if (full) {
       *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
