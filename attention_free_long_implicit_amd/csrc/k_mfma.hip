@@ -251,7 +251,19 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   __syncthreads();
 
   // ---------------- passes 2, 3, 3', 2' per slab k1 (wave w owns k1 = w, w+4, w+8, w+12)
-  for (int it = 0; it < 4; ++it) {
+  u32x4 G[2][4];
+  auto load_gate = [&]() {
+    if (GATE) {
+      const __bf16* g0 = gate + row0 * L + c0;
+      const __bf16* g1p = gate + row1 * L + c0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        G[0][e] = *reinterpret_cast<const u32x4*>(g0 + 1024 * (4 * h + e));
+        G[1][e] = *reinterpret_cast<const u32x4*>(g1p + 1024 * (4 * h + e));
+      }
+    }
+  };
+  auto slab_step = [&](int it) {
     const int k1 = w + 4 * it;
     const int k1s = ws + 4 * it;   // the same slab index, in a scalar register
     uint32_t* sl = S + k1 * SLAB;
@@ -293,20 +305,13 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
     if (it < 3) load_mat(k1s + 4, MF3, Mb);
 #pragma unroll
     for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2(er[v], ei[v]);
-  }
-
-  // gate for pass 1' (issued after every slab load, so no slab waits on it): lane keeps rows b0 / b1 at
-  // n1 = 4h + e (e < 4), 8 consecutive samples each
-  u32x4 G[2][4];
-  if (GATE) {
-    const __bf16* g0 = gate + row0 * L + c0;
-    const __bf16* g1p = gate + row1 * L + c0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      G[0][e] = *reinterpret_cast<const u32x4*>(g0 + 1024 * (4 * h + e));
-      G[1][e] = *reinterpret_cast<const u32x4*>(g1p + 1024 * (4 * h + e));
-    }
-  }
+  };
+  // The gate for pass 1' is issued before the last slab, behind that slab's matrix and spectrum loads
+  // (the vector-memory counter retires in order, so no earlier slab waits on it): lane keeps rows
+  // b0 / b1 at n1 = 4h + e (e < 4), 8 consecutive samples each.
+  for (int it = 0; it < 3; ++it) slab_step(it);
+  load_gate();
+  slab_step(3);
 
   __syncthreads();
 
