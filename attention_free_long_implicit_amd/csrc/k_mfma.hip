@@ -408,12 +408,20 @@ k_fs_cols_mfma(const uint32_t* __restrict__ u, const uint32_t* __restrict__ gate
   for (int i = t; i < NBLK * 64; i += T) Ms[i] = cmats[i];
   __syncthreads();
   const int nitems = nq * CG, G = gridDim.x;
+  // Global accesses go through buffer descriptors based at this item's 128 columns: the lane's part of
+  // the offset (column, and the h-dependent rows) is one vector register per access kind; the row part
+  // is a compile-time constant times M2, kept in scalar registers.
+  const int lc = 32 * w + j;
+  const int vo_a = (4 * h * M2 + lc) * 4;    // rows n1 = ... + 4h (pass A input, gate, y)
+  const int vo_i = (64 * h * M2 + lc) * 4;   // intermediate rows pos_of_bin(16 kb + 8h + e) = 64h + 8e + kb
+  const int vo_f = (32 * h * M2 + lc) * 4;   // intermediate rows of the forward output: ... + 32h
   for (int item = xcd_logical_block(blockIdx.x, G); item < nitems; item += G) {
     const int ql = item / CG, cg = item % CG;
     const int q = q0 + ql, d = q / B, b = q % B;
     const size_t row = (size_t)b * D + d;
-    const int c = cg * 128 + 32 * w + j;   // this lane's column n2
-    uint32_t* Irow = I + (size_t)ql * M;
+    const int cb = cg * 128;
+    const __amdgpu_buffer_rsrc_t irs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(I + (size_t)ql * M + cb), (short)0, (M - cb) * 4, kRawBufferWord3);
     // the matrix blocks are read from LDS at each use: an offset the compiler cannot see through keeps
     // those reads inside the item loop (hoisted, the 64 blocks would need 256 registers)
     int lz = l;
@@ -421,12 +429,15 @@ k_fs_cols_mfma(const uint32_t* __restrict__ u, const uint32_t* __restrict__ gate
     const bf16x8* Mw = Ms + lz;
     bf16x8 fr[4], fi[4];                   // forward inputs, K-block kb (accumulator order of n1)
     if constexpr (MODE == 0) {
-      const uint32_t* zc = u + row * WPR + c;
+      const __amdgpu_buffer_rsrc_t urs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(u + row * WPR + cb), (short)0, (WPR - cb) * 4, kRawBufferWord3);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         uint32_t wv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wv[e] = zc[(size_t)M2 * (32 * (kb >> 1) + acc_row(8 * (kb & 1) + e, h))];
+        for (int e = 0; e < 8; ++e)   // n1 = 32 (kb >> 1) + acc_row(8 (kb & 1) + e, h)
+          wv[e] = __builtin_amdgcn_raw_buffer_load_b32(
+              urs, vo_a, (32 * (kb >> 1) + 16 * (kb & 1) + 8 * (e >> 2) + (e & 3)) * M2 * 4, 0);
         split8(wv, fr[kb], fi[kb]);
       }
     } else {
@@ -436,12 +447,15 @@ k_fs_cols_mfma(const uint32_t* __restrict__ u, const uint32_t* __restrict__ gate
       for (int kb = 0; kb < 8; ++kb) {
         uint32_t wv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wv[e] = Irow[(size_t)pos_of_bin(16 * kb + 8 * h + e) * M2 + c];
+        for (int e = 0; e < 8; ++e) wv[e] = __builtin_amdgcn_raw_buffer_load_b32(irs, vo_i, (8 * e + kb) * M2 * 4, 0);
         split8(wv, xr[kb], xi[kb]);
       }
       if constexpr (!CHAIN) asm volatile("" ::: "memory");   // gate loads stay in their row block
-      const uint32_t* gc = GATE ? gate + row * WPR + c : nullptr;
-      uint32_t* yc = CHAIN ? nullptr : y + row * WPR + c;
+      // (a descriptor that is not used points at the intermediate, never dereferenced)
+      const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+          GATE ? (void*)(gate + row * WPR + cb) : (void*)I, (short)0, (WPR - cb) * 4, kRawBufferWord3);
+      const __amdgpu_buffer_rsrc_t yrs = __builtin_amdgcn_make_buffer_rsrc(
+          CHAIN ? (void*)I : (void*)(y + row * WPR + cb), (short)0, (WPR - cb) * 4, kRawBufferWord3);
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         f32x16 dr = {}, di = {};
@@ -456,14 +470,15 @@ k_fs_cols_mfma(const uint32_t* __restrict__ u, const uint32_t* __restrict__ gate
         float o_re[16], o_im[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const int n1 = 32 * rb + acc_row(v, h);
+          // n1 = 32 rb + acc_row(v, h) = 32 rb + 8 (v >> 2) + (v & 3) + 4h
+          const int so = (32 * rb + 8 * (v >> 2) + (v & 3)) * M2 * 4;
           float a = dr[v], bb = di[v];
           if constexpr (GATE) {
-            const uint32_t g = gc[(size_t)M2 * n1];
+            const uint32_t g = __builtin_amdgcn_raw_buffer_load_b32(grs, vo_a, so, 0);
             a *= lo_f32(g);
             bb *= hi_f32(g);
           }
-          if constexpr (!CHAIN) yc[(size_t)M2 * n1] = pack2(a, bb);
+          if constexpr (!CHAIN) __builtin_amdgcn_raw_buffer_store_b32(pack2(a, bb), yrs, vo_a, so, 0);
           o_re[v] = a;
           o_im[v] = bb;
         }
@@ -498,8 +513,9 @@ k_fs_cols_mfma(const uint32_t* __restrict__ u, const uint32_t* __restrict__ gate
         di = mfma(Sb, neg8(fr[kb]), di);
       }
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        Irow[(size_t)pos_of_bin(32 * ob + acc_row(v, h)) * M2 + c] = pack2(dr[v], di[v]);
+      for (int v = 0; v < 16; ++v)   // pos_of_bin(32 ob + acc_row(v, h)) = 64 ((v >> 2) & 1) + 32h + 8 (v & 3) + 2 ob + (v >> 3)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            pack2(dr[v], di[v]), irs, vo_f, (64 * ((v >> 2) & 1) + 8 * (v & 3) + 2 * ob + (v >> 3)) * M2 * 4, 0);
     }
   }
 }
