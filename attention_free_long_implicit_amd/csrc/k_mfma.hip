@@ -356,17 +356,18 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
       }
     } else {
       // u_i stays on chip, rounded to bf16 exactly as its store would be.  Pass 1' left lane (j, h) with
-      // rows b0, b1 at n1 = 4h + e; the next pass 1 wants row b_h at n1 = 0..7 in lane (j, h): swap the
-      // other row's half with lane l ^ 32 through the LDS crossbar (no LDS memory).
-      const int partner = (l ^ 32) << 2;
+      // rows b0, b1 at n1 = 4h + e; the next pass 1 wants row b_h at n1 = 0..7 in lane (j, h).  One
+      // cross-half swap per register does it: swapping the upper half of the row-b0 register with the
+      // lower half of the row-b1 register leaves [b0 from lanes 0..31, b1 from lanes 0..31] (n1 = e) in
+      // the first and [b0 from lanes 32..63, b1 from lanes 32..63] (n1 = 4 + e) in the second.
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const u32x4 own = h ? Y[1][e] : Y[0][e], snd = h ? Y[0][e] : Y[1][e];
-        u32x4 rcv;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rcv[q] = (uint32_t)__builtin_amdgcn_ds_bpermute(partner, (int)snd[q]);
-        V[e] = h ? rcv : own;
-        V[4 + e] = h ? own : rcv;
+        for (int q = 0; q < 4; ++q) {
+          const auto r = __builtin_amdgcn_permlane32_swap(Y[0][e][q], Y[1][e][q], false, false);
+          V[e][q] = r[0];
+          V[4 + e][q] = r[1];
+        }
       }
       __syncthreads();   // every wave is done reading LDS before the next order's pass 1 writes it
     }
