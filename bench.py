@@ -250,7 +250,9 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded activations, Xavier-uniform filter networks; see hyena_inputs)",
         "config": {"workload": w.name, "order": w.order, "B": w.B, "D": w.D, "grid": list(w.dims),
-                   "storage": w.dtype, "arithmetic": arithmetic(w)},
+                   "boundary": w.mode, "storage": w.dtype, "arithmetic": arithmetic(w),
+                   "alpha_range": [w.alpha_lo, w.alpha_hi],
+                   "inputs": f"numpy default_rng([{w.index}, stream]): stream 0 activations, stream 1 filter parameters"},
         "hbm_gbps_alg": alg_step / (ms_per_step / 1e3) / 1e9,
         "hbm_frac_alg": alg_step / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
         "event_ms_per_step": float(np.mean(step_ms)),

@@ -446,3 +446,42 @@ def test_operator_circular_direct_vs_fft_and_delta():
     h3 = [rng.standard_normal((2, n, n, n)) for _ in range(2)]
     np.testing.assert_allclose(orc.hyena_operator_3d(v3, x3, h3, circular=True),
                                orc.hyena_operator_3d(v3, x3, h3, direct=True, circular=True), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- spot checks and equivariance
+
+def test_fft_form_spot_checked_by_direct_sums_at_1M():
+    # the FFT form at the 1M-token length against O(L) direct dot products at 64 random positions
+    L = 1 << 20
+    rng = np.random.default_rng(20)
+    u = rng.standard_normal(L)
+    t = np.arange(L)
+    h = np.exp(-0.7 * t / L) * np.cos(2 * math.pi * 5 * t / L)
+    c = orc.causal_conv_fft(u, h)
+    for t0 in rng.integers(0, L, size=64):
+        want = np.dot(h[t0::-1], u[: t0 + 1])
+        assert abs(c[t0] - want) <= 1e-9 * (1 + abs(want)), (t0, c[t0], want)
+
+
+def test_causal_shift_equivariance():
+    # delaying the input by s (zero history) delays the causal output by s
+    L, s = 256, 37
+    rng = np.random.default_rng(22)
+    u = rng.standard_normal(L)
+    h = rng.standard_normal(L)
+    us = np.concatenate([np.zeros(s), u[: L - s]])
+    c = orc.causal_conv_direct(u, h)
+    cs = orc.causal_conv_direct(us, h)
+    np.testing.assert_allclose(cs[s:], c[: L - s], rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(cs[:s], np.zeros(s))
+
+
+def test_circular_shift_equivariance():
+    L, s = 64, 23
+    rng = np.random.default_rng(23)
+    u = rng.standard_normal(L)
+    h = rng.standard_normal(L)
+    np.testing.assert_allclose(orc.circular_conv_direct(np.roll(u, s), h), np.roll(orc.circular_conv_direct(u, h), s),
+                               rtol=0, atol=1e-12)
+    np.testing.assert_allclose(orc.circular_conv_fft(np.roll(u, s), h), np.roll(orc.circular_conv_fft(u, h), s),
+                               rtol=0, atol=1e-12)
