@@ -343,6 +343,13 @@ __device__ __forceinline__ void spectral_pair(float2& A, float2& B, float2 w, fl
   B = make_float2(Ye.x + Yo.y, Yo.x - Ye.y);
 }
 
+// Spectrum element: fp32 complex, or one word of two bf16 (real part low, imaginary part high).
+__device__ __forceinline__ float2 hload(const float2* p) { return *p; }
+__device__ __forceinline__ float2 hload(const uint32_t* p) {
+  const uint32_t w = *p;
+  return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+
 // Real-input split only: returns 2 X[k] and 2 X[M-k] (used to build filter spectra).
 __device__ __forceinline__ void split_pair(float2 A, float2 B, float2 w, float2& Xk, float2& Xp) {
   const float2 Bc = cconj(B);
@@ -358,14 +365,14 @@ __device__ __forceinline__ void split_pair(float2 A, float2 B, float2 w, float2&
 // ("complement" pairing: block B holds the mirrors of block A in reverse order).
 // wA = W_{2M}^{bin of x[0]}; bins of x[m] advance by `step` = M*? via the constant W_{2RP}^m.
 // MODE 0: multiply by the spectrum (h from slots), MODE 1: write the split spectrum to `hs_out`.
-template <int RP, int MODE>
-__device__ __forceinline__ void spectral_complement(float2 (&x)[2 * RP], float2 wA, const float2* hs, int stride,
+template <int RP, int MODE, class HT = float2>
+__device__ __forceinline__ void spectral_complement(float2 (&x)[2 * RP], float2 wA, const HT* hs, int stride,
                                                     float2* hs_out, float sc) {
   static_for<RP>([&](auto mm) {
     constexpr int m = mm.value, mp = 2 * RP - 1 - m;
     const float2 w = mul_w<m, 2 * RP, false>(wA);
     if constexpr (MODE == 0) {
-      spectral_pair(x[m], x[mp], w, hs[m * stride], hs[mp * stride]);
+      spectral_pair(x[m], x[mp], w, hload(hs + m * stride), hload(hs + mp * stride));
     } else {
       float2 Xk, Xp;
       split_pair(x[m], x[mp], w, Xk, Xp);
@@ -379,23 +386,23 @@ __device__ __forceinline__ void spectral_complement(float2 (&x)[2 * RP], float2 
 // block A (x[0..RP)) has bins (S/RP) m, mirrored as m <-> RP-m (m = 0: bins 0 and M; m = RP/2: M/2);
 // block B (x[RP..2RP)) has bins kB + (S/RP) m mirrored as m <-> RP-1-m.  Slot 0 carries the real
 // pair (Hs[0], Hs[M]) as (x, y).  w0 = W_{2M}^{0} = 1, wB = W_{2M}^{kB}.
-template <int RP, int MODE>
-__device__ __forceinline__ void spectral_selfmirror(float2 (&x)[2 * RP], float2 wB, const float2* hs, int stride,
+template <int RP, int MODE, class HT = float2>
+__device__ __forceinline__ void spectral_selfmirror(float2 (&x)[2 * RP], float2 wB, const HT* hs, int stride,
                                                     float2* hs_out, float sc) {
   static_for<RP / 2 + 1>([&](auto mm) {
     constexpr int m = mm.value, mp = (RP - m) % RP;
     const float2 w = mul_w<m, 2 * RP, false>(make_float2(1.f, 0.f));
     if constexpr (MODE == 0) {
       if constexpr (m == 0) {
-        const float2 s = hs[0];
+        const float2 s = hload(hs);
         float2 bb = x[0];
         spectral_pair(x[0], bb, w, make_float2(s.x, 0.f), make_float2(s.y, 0.f));
       } else if constexpr (m == RP / 2) {
         float2 bb = x[m];
-        const float2 h = hs[m * stride];
+        const float2 h = hload(hs + m * stride);
         spectral_pair(x[m], bb, w, h, h);
       } else {
-        spectral_pair(x[m], x[mp], w, hs[m * stride], hs[mp * stride]);
+        spectral_pair(x[m], x[mp], w, hload(hs + m * stride), hload(hs + mp * stride));
       }
     } else {
       float2 Xk, Xp;
@@ -412,7 +419,7 @@ __device__ __forceinline__ void spectral_selfmirror(float2 (&x)[2 * RP], float2 
     constexpr int m = RP + mm.value, mp = 2 * RP - 1 - mm.value;
     const float2 w = mul_w<mm.value, 2 * RP, false>(wB);
     if constexpr (MODE == 0) {
-      spectral_pair(x[m], x[mp], w, hs[m * stride], hs[mp * stride]);
+      spectral_pair(x[m], x[mp], w, hload(hs + m * stride), hload(hs + mp * stride));
     } else {
       float2 Xk, Xp;
       split_pair(x[m], x[mp], w, Xk, Xp);

@@ -232,8 +232,11 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   const int kind = kind_of(mode, dims);
+  // multi-pass 1-D spectra carry a bf16 copy (one word per value) after the fp32 one
+  const size_t mp_copy = multipass1d(kind, pts) ? sizeof(uint32_t) : 0;
   if (is3d(kind)) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel(circ3(kind));
-  else if (kind == K_CIRC1) *bytes = (size_t)D * (size_t)(pts / 2) * sizeof(float2);
+  else if (kind == K_CIRC1) *bytes = (size_t)D * (size_t)(pts / 2) * (sizeof(float2) + mp_copy);
+  else if (mp_copy) *bytes = (size_t)D * (size_t)pts * (sizeof(float2) + mp_copy);
   else *bytes = (size_t)D * (size_t)pts * sizeof(float2) + (has_pair_copy(pts) ? (size_t)D * mfma_pair_spectrum_bytes_per_channel() : 0);
   return HYENA_OK;
 }
@@ -306,14 +309,17 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
     return hip_status(launch_spectrum3d(h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream, circ3(kind)));
   }
   if ((st = hip_status(launch_filter1d(a, (int)L, h, stream)))) return st;
-  if (kind == K_CIRC1 && multi)
-    return hip_status(launch_spectrum1d_fourstep(circular_log2(L), h, (float2*)spectrum, p->D, (float2*)wsp, chunk,
-                                                 tw, stream, 1));
+  if (multi) {
+    // fp32 spectrum, then its bf16 copy for the bf16 plans' row pass
+    const int lg = engine_log2(kind, L);
+    if ((st = hip_status(launch_spectrum1d_fourstep(lg, h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream,
+                                                    kind == K_CIRC1 ? 1 : 0))))
+      return st;
+    const size_t n = (size_t)p->D << lg;
+    return hip_status(launch_spectrum_bf16_copy((const float2*)spectrum, (char*)spectrum + n * sizeof(float2), n, stream));
+  }
   if (kind == K_CIRC1)
     return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, p->D, tw, stream, 1));
-  if (multi)
-    return hip_status(launch_spectrum1d_fourstep(log2i(L), h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw,
-                                                 stream));
   if ((st = hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, p->D, tw, stream)))) return st;
   if (has_pair_copy(L)) {
     // natural-order bins into the workspace, then the pair-order bf16 copy after the fp32 spectrum

@@ -120,9 +120,9 @@ k_spectrum1d(const float* __restrict__ h, float2* __restrict__ Hs, Twiddles tw) 
   const float sc = 1.0f / (8.0f * M);
   float2* out = Hs + (size_t)d * M + t;
   if (!P.special)
-    spectral_complement<RP, 1>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapA)), nullptr, T, out, sc);
+    spectral_complement<RP, 1, float2>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapA)), nullptr, T, out, sc);
   else
-    spectral_selfmirror<RP, 1>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapB)), nullptr, T, out, sc);
+    spectral_selfmirror<RP, 1, float2>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapB)), nullptr, T, out, sc);
 }
 
 // Engine-order spectrum -> H[d, k], k = 0..L (unscaled 2L-point DFT bins).

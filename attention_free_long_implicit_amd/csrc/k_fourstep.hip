@@ -22,7 +22,9 @@
 // (q = d*B + b) so the B rows of a channel read its filter spectrum back to back.
 //
 // Spectrum layout per channel: Hs[g][slot][t'] for row-pair group g < M1/2, slot < 2 RP, thread t'
-// of the pair (see k_fs_rows); g = 0 holds rows k1 = 0 and k1 = M1/2.  Hs = H / (4M).
+// of the pair (see k_fs_rows); g = 0 holds rows k1 = 0 and k1 = M1/2.  Hs = H / (4M).  The bf16 plans
+// read a bf16 copy of it (one word per value, real part low) stored after the fp32 spectrum: their
+// intermediate and products are bf16 already, and it halves the spectrum traffic of the row pass.
 #include "engine.h"
 #include "launch.h"
 
@@ -191,8 +193,10 @@ k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
 // whole-row negation pairing on row 0 (threads < TP/2) and in-row complement pairing on row M1/2.
 template <int LOG2M, int MODE, bool IBF16>
 __global__ void __launch_bounds__(FS<LOG2M>::TR)
-k_fs_rows(typename Inter<IBF16>::T* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq,
+k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __restrict__ Hs_out, int q0, int nq,
           int B, Twiddles tw) {
+  using HT = typename Inter<IBF16>::T;   // spectrum element: fp32 complex, or a bf16 pair word
+  const HT* __restrict__ Hs = static_cast<const HT*>(Hsv);
   using F = FS<LOG2M>;
   using In = Inter<IBF16>;
   using Row = typename F::Row;
@@ -265,11 +269,11 @@ k_fs_rows(typename Inter<IBF16>::T* I, const float2* __restrict__ Hs, float2* __
   if (!selfmirror) {
     const float2 wA = twiddle<LOG2M + 1>(tw, uint32_t(k1A) + uint32_t(M1) * uint32_t(kapA));
     if constexpr (MODE == 0) spectral_complement<RP, 0>(x, wA, Hs + hoff, TP, nullptr, 0.f);
-    else spectral_complement<RP, 1>(x, wA, nullptr, TP, Hs_out + hoff, 1.0f / (8.0f * M));
+    else spectral_complement<RP, 1, float2>(x, wA, nullptr, TP, Hs_out + hoff, 1.0f / (8.0f * M));
   } else {
     const float2 wB = twiddle<LOG2M + 1>(tw, uint32_t(M1) * uint32_t(kapB));
     if constexpr (MODE == 0) spectral_selfmirror<RP, 0>(x, wB, Hs + hoff, TP, nullptr, 0.f);
-    else spectral_selfmirror<RP, 1>(x, wB, nullptr, TP, Hs_out + hoff, 1.0f / (8.0f * M));
+    else spectral_selfmirror<RP, 1, float2>(x, wB, nullptr, TP, Hs_out + hoff, 1.0f / (8.0f * M));
   }
   if constexpr (MODE == 1) return;
 
@@ -329,6 +333,12 @@ __global__ void k_export1d_fs(const float2* __restrict__ Hs, float2* __restrict_
   out[k1 + M1 * (kap + (M2 / RP) * m)] = cscale(v, sc);
 }
 
+// fp32 spectrum -> bf16 copy (round to nearest even), one word per complex value
+__global__ void k_spectrum_bf16(const float2* __restrict__ Hs, uint32_t* __restrict__ Hb, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) Inter<true>::st(Hb + i, Hs[i]);
+}
+
 // ------------------------------------------------------------------ host side
 namespace {
 
@@ -355,8 +365,10 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
       hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
                          (const E*)v, (const E*)nullptr, (E*)nullptr, Ib, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
-      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0, BF16>), dim3(groups * nq), dim3(F::TR), 0, s, Ib,
-                         (const float2*)spectra[i], (float2*)nullptr, q0, nq, B, tw);
+      // bf16 plans read the bf16 copy stored after the fp32 spectrum
+      const void* hs = BF16 ? (const void*)((const char*)spectra[i] + (size_t)D * F::M * sizeof(float2)) : spectra[i];
+      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0, BF16>), dim3(groups * nq), dim3(F::TR), 0, s, Ib, hs,
+                         (float2*)nullptr, q0, nq, B, tw);
       if (mc)
         (void)launch_fs_cols_mfma(LOG2M, 1, x[i] != nullptr, i + 1 < order, nullptr, x[i], y, Ib, q0, nq, B, D, mats,
                                   s);
@@ -385,7 +397,7 @@ hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int 
   for (int q0 = 0; q0 < D; q0 += chunk) {
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
     hipLaunchKernelGGL((k_fs_cols_taps<LOG2M, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s, h, I, q0, nq, tw);
-    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1, false>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const float2*)nullptr,
+    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1, false>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const void*)nullptr,
                        Hs, q0, nq, 1, tw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -400,6 +412,11 @@ bool fourstep_supported(int log2L) { return log2L >= 15 && log2L <= 20; }
 size_t fourstep_row_bytes(int log2L) { return (size_t)1 << log2L << 3; }
 
 #define HYENA_FS_CASES(X) X(15) X(16) X(17) X(18) X(19) X(20)
+
+hipError_t launch_spectrum_bf16_copy(const float2* Hs, void* Hb, size_t n, hipStream_t s) {
+  hipLaunchKernelGGL(k_spectrum_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Hs, (uint32_t*)Hb, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s) {
   switch (log2L) {

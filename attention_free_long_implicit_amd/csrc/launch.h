@@ -28,6 +28,8 @@ hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, 
 hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
                                       const Twiddles& tw, hipStream_t s, int full = 0);
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
+// bf16 copy of a multi-pass spectrum (n complex values), read by the bf16 plans' row pass
+hipError_t launch_spectrum_bf16_copy(const float2* Hs, void* Hb, size_t n, hipStream_t s);
 
 // ---- 3-D, 64^3 grid: circ = 0 zero-padded to 128^3 (non-causal "same" convolution),
 //      circ = 1 periodic on the 64^3 grid itself

@@ -78,8 +78,9 @@ typedef struct {
 
 /* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array):
  * causal 8L bytes per channel (for L = 8192 followed by a bf16 copy laid out for the matrix-core
- * kernel, 36 KB per channel); periodic 1-D 4L bytes per channel; 3-D 128*128*65*8 bytes per channel
- * (zero-padded) or 64*64*33*8 (periodic). */
+ * kernel, 36 KB per channel; for L > 16384, 12L: a bf16 copy for the bf16 plans follows); periodic
+ * 1-D 4L bytes per channel (6L for L > 32768); 3-D 128*128*65*8 bytes per channel (zero-padded) or
+ * 64*64*33*8 (periodic). */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_filter_gen needs: room for the taps (used when h_time is NULL) plus, for

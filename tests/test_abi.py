@@ -72,7 +72,9 @@ def test_size_queries(lib):
     st, n = _size(lib.hyena_workspace_bytes, 2, 1, 3, L.dims_of([1 << 21]), L.F32, L.CIRCULAR)
     assert st == 0 and n == 3 * (1 << 20) * 8
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([1 << 16]), L.CIRCULAR, 2)
-    assert st == 0 and n == 2 * (1 << 15) * 8
+    assert st == 0 and n == 2 * (1 << 15) * (8 + 4)        # fp32 spectrum + bf16 copy for the bf16 plans
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([65536]), L.CAUSAL, 3)
+    assert st == 0 and n == 3 * 65536 * (8 + 4)
     # periodic 3-D: 64 x 64 x 33 bins per channel, intermediate 64 x-slabs of 64 x 33 per volume
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.CIRCULAR, 128)
     assert st == 0 and n == 128 * 64 * 64 * 33 * 8
