@@ -14,11 +14,15 @@ Workloads (the five shapes the Hyena operator is exercised on):
   4  order 2, B=1, D=128, grid 64^3,   fp32, non-causal 3-D (padded to 128^3)
   5  order 2, B=4, D=768, L=8192,      fp32, periodic 1-D (no padding)
   6  order 2, B=1, D=128, grid 64^3,   fp32, periodic 3-D (no padding)
+  7  order 2, B=2, D=128, grid 64^3,   fp32, non-causal 3-D with input-dependent filters: 8 register
+     tokens per sample, a FiLM-modulated SIREN (64 units) and a Gaussian window, one filter per (b, d)
 
 Random streams: ``numpy.random.default_rng([seed, stream])``.  Stream 0 draws
 the activations (v, x_1 .. x_N in that order, or tokens then the embedding for
 the DNA workload); stream 1 draws the filter parameters (per order: W1, W2,
 alpha).  Biases are zero.  Xavier-uniform bounds use sqrt(6/(fan_in+fan_out)).
+For input-dependent filters stream 1 draws, per order, the SIREN and FiLM parameters (see
+``draw_film_params``) and stream 2 the register activations [B, R, D] ~ N(0,1).
 """
 from __future__ import annotations
 
@@ -29,7 +33,8 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "draw_activations", "draw_filter_params",
-    "bf16_bits_rne", "bf16_bits_to_f32", "seeded_rng",
+    "bf16_bits_rne", "bf16_bits_to_f32", "seeded_rng", "draw_film_params", "draw_registers",
+    "FILM_OMEGA0_BLOCKS",
 ]
 
 
@@ -48,6 +53,10 @@ class Workload:
     features: int          # width of the positional-feature vector
     hidden: int            # width of the filter network's hidden layer
     activations: str = "normal"   # "normal" or "dna"
+    filter: str = "exp"           # "exp": FFN x exponential window; "film": input-dependent (per sample)
+    registers: int = 0            # register tokens per sample (input-dependent filters)
+    sigma_lo: float = 0.2         # Gaussian window widths (input-dependent filters)
+    sigma_hi: float = 0.8
 
     @property
     def ndim(self) -> int:
@@ -96,6 +105,8 @@ WORKLOADS: List[Workload] = [
     Workload(5, "periodic_order2_B4_D768_L8192_f32", 2, 4, 768, (8192,), "f32", "circular", 0.3, 3.0, 64, 64),
     Workload(6, "hyenand3d_periodic_order2_B1_D128_64cubed_f32", 2, 1, 128, (64, 64, 64), "f32", "circular",
              0.3, 3.0, 96, 64),
+    Workload(7, "hyenand3d_film_order2_B2_D128_64cubed_f32", 2, 2, 128, (64, 64, 64), "f32", "linear",
+             0.0, 0.0, 3, 64, filter="film", registers=8),
 ]
 
 
@@ -181,6 +192,46 @@ def draw_filter_params(w: Workload, seed: Optional[int] = None) -> List[dict]:
         alpha = rng.uniform(w.alpha_lo, w.alpha_hi, size=D).astype(np.float32)
         out.append(dict(W1=W1, b1=np.zeros(H, np.float32), W2=W2, b2=np.zeros(D, np.float32), alpha=alpha))
     return out
+
+
+FILM_OMEGA0_BLOCKS = (1.0, 3.0, 10.0, 30.0)
+
+
+def draw_film_params(w: Workload, seed: Optional[int] = None) -> List[dict]:
+    """Per-order input-dependent filter parameters as float32 arrays (H = w.hidden units, n = w.ndim
+    coordinates, E = D register width):
+
+    q [E] ~ N(0, 1/E); A1 [H, n], a1 [H] ~ U(-1/n, 1/n); omega0 [H]: the units in equal blocks at the
+    scales FILM_OMEGA0_BLOCKS; A2 [H, H] ~ U(+-sqrt(6/H)), a2 [H] ~ U(+-1/sqrt(H)); A3 [D, H] Xavier
+    uniform, a3 [D] zeros; FiLM maps G1, P1, G2, P2 [H, E] ~ N(0, 0.25/E), g1 = g2 = 1, p1 = p2 = 0;
+    sigma [D] ~ U[sigma_lo, sigma_hi).
+    """
+    seed = w.index if seed is None else seed
+    rng = seeded_rng(seed, 1)
+    H, D, n, E = w.hidden, w.D, w.ndim, w.D
+    f32 = lambda a: np.asarray(a, dtype=np.float32)
+    uni = lambda shape, b: f32((rng.random(shape) * 2 - 1) * b)
+    nb = len(FILM_OMEGA0_BLOCKS)
+    omega0 = f32(np.repeat(FILM_OMEGA0_BLOCKS, -(-H // nb))[:H])
+    out = []
+    for _ in range(w.order):
+        p = dict(q=f32(rng.standard_normal(E) / np.sqrt(E)), A1=uni((H, n), 1.0 / n), a1=uni(H, 1.0 / n),
+                 omega0=omega0.copy(), A2=uni((H, H), np.sqrt(6.0 / H)), a2=uni(H, 1.0 / np.sqrt(H)),
+                 A3=uni((D, H), np.sqrt(6.0 / (H + D))), a3=np.zeros(D, np.float32))
+        for l in (1, 2):
+            p[f"G{l}"] = f32(rng.standard_normal((H, E)) * (0.5 / np.sqrt(E)))
+            p[f"g{l}"] = np.ones(H, np.float32)
+            p[f"P{l}"] = f32(rng.standard_normal((H, E)) * (0.5 / np.sqrt(E)))
+            p[f"p{l}"] = np.zeros(H, np.float32)
+        p["sigma"] = f32(rng.uniform(w.sigma_lo, w.sigma_hi, size=D))
+        out.append(p)
+    return out
+
+
+def draw_registers(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """Register activations [B, R, D] ~ N(0,1) as float32 (random stream 2)."""
+    seed = w.index if seed is None else seed
+    return seeded_rng(seed, 2).standard_normal((w.B, w.registers, w.D), dtype=np.float32)
 
 
 def sample_rows(w: Workload, count: int, seed: int = 1234) -> np.ndarray:

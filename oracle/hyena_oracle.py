@@ -29,6 +29,11 @@ What is computed (y = x_N * (h_N conv (... x_1 * (h_1 conv v)))):
   * circular (periodic) convolution, no padding, 1-D and 3-D              [HyenaND, boundary handling:
                                                                            circular convolutions for
                                                                            periodic physical systems]
+  * input-dependent (per-sample) filters: z(x) = softmax-weighted mean of
+    the register activations; K = w(c) * f(c; z) with a FiLM-modulated
+    SIREN f and a Gaussian window w                                        [HyenaND, method: registers,
+                                                                           FiLM conditioning, kernel
+                                                                           synthesis, parameterisation]
 
 Readings where the pages are silent (each also listed in the design notes):
   order N = number of filters = number of gates (listing chunks len(filters)+1);
@@ -38,6 +43,11 @@ Readings where the pages are silent (each also listed in the design notes):
   3-D window exp(-alpha |r/n|_2);
   circular mode: indices taken modulo the grid, no padding; 1-D keeps the causal taps t = 0..L-1
   (one period), 3-D evaluates the filter on the centred offsets r in [-n/2, n/2)^3, placed at r mod n.
+  input-dependent filters: the register activations arrive as an input [B, R, E]; softmax weights
+  from a learned score vector q (a[b, r] = softmax_r(q . reg[b, r])); two FiLM-modulated sine layers
+  (gamma = G z + g scales the pre-activation omega0 * (A1 c + a1) or A2 h1 + a2, beta = P z + p is
+  added) and a linear read-out; omega0 one scale per first-layer unit; window exp(-|c|^2 / (2 sigma_d^2));
+  coordinates c = t/L (1-D) or r/n per axis (3-D), as for the exponential filter.
 
 Pins (each function is checked against something other than itself in
 tests/test_oracle.py): direct sum vs FFT form, numpy.convolve special case,
@@ -46,7 +56,11 @@ filters, linearity, causality, 3-D brute force, separable 3-D products,
 hand-computed worked examples under tests/golden/; circular mode: direct sum vs
 FFT, cyclic shifts by delta filters, numpy.convolve when nothing wraps, the
 geometric-filter eigenvalue closed form, 3-D brute force and separable products,
-and the circular 3-D filter against the linear one at shared offsets.
+and the circular 3-D filter against the linear one at shared offsets; input-dependent filters: the
+plain mean and the two-register logistic closed form of the softmax summary, permutation invariance,
+closed-form SIREN outputs with and without FiLM terms, the Gaussian window against the normal density
+and its separability, kernels that follow the registers sample by sample, axis order of the 3-D taps,
+and per-(b, d) filters in the operator against row-by-row direct sums.
 """
 from __future__ import annotations
 
@@ -60,7 +74,8 @@ __all__ = [
     "implicit_filter_1d", "implicit_filter_3d", "causal_conv_direct", "causal_conv_fft",
     "linear_conv3d_direct", "linear_conv3d_fft", "hyena_operator_rows", "hyena_operator_3d",
     "rel_l2_per_row", "filter_offsets_3d_circular", "implicit_filter_3d_circular", "circular_conv_direct",
-    "circular_conv_fft", "circular_conv3d_direct", "circular_conv3d_fft",
+    "circular_conv_fft", "circular_conv3d_direct", "circular_conv3d_fft", "register_summary", "film_siren",
+    "gaussian_window", "input_dependent_filter_1d", "input_dependent_filter_3d",
 ]
 
 
@@ -295,6 +310,81 @@ def circular_conv3d_fft(u: np.ndarray, h: np.ndarray) -> np.ndarray:
     n = u.shape[-1]
     axes = (-3, -2, -1)
     return np.fft.irfftn(np.fft.rfftn(u, axes=axes) * np.fft.rfftn(h, axes=axes), s=(n, n, n), axes=axes)
+
+
+# --------------------------------------------------------------------------------------------
+# input-dependent filters  [HyenaND, method: registers and FiLM; kernel synthesis K(x) = w(c) f(c; z(x));
+#                           kernel parameterisation: coordinate SIREN with multi-frequency omega_0]
+# --------------------------------------------------------------------------------------------
+
+def register_summary(registers: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """z(x) per sample: the softmax-weighted mean of the R register activations: [B, E] float64.
+
+    registers [B, R, E] (the register tokens after the layers that processed them together with the
+    grid), q [E] a learned score vector; weights a[b, r] = softmax over r of q . registers[b, r].
+    """
+    reg = np.asarray(registers, np.float64)
+    s = reg @ np.asarray(q, np.float64)                                  # [B, R] scores
+    s = s - s.max(axis=1, keepdims=True)
+    a = np.exp(s)
+    a = a / a.sum(axis=1, keepdims=True)
+    return np.einsum("br,bre->be", a, reg)
+
+
+def film_siren(coords: np.ndarray, z: np.ndarray, p: dict) -> np.ndarray:
+    """f(c; z) for every coordinate row c of coords [P, n] and one sample's z [E]: [P, D] float64.
+
+    Two sine layers, each modulated feature-wise by z (gamma = G z + g scales the pre-activation,
+    beta = P z + p shifts it), then a linear read-out to the D channels:
+        s1 = omega0 * (A1 c + a1);   h1 = sin(gamma1 * s1 + beta1)
+        s2 = A2 h1 + a2;             h2 = sin(gamma2 * s2 + beta2)
+        f  = A3 h2 + a3
+    omega0 [H] is one frequency scale per first-layer unit (blocks of units at different scales).
+    """
+    f64 = lambda k: np.asarray(p[k], np.float64)
+    z = np.asarray(z, np.float64)
+    c = np.asarray(coords, np.float64)
+    g1, b1 = f64("G1") @ z + f64("g1"), f64("P1") @ z + f64("p1")
+    g2, b2 = f64("G2") @ z + f64("g2"), f64("P2") @ z + f64("p2")
+    s1 = f64("omega0") * (c @ f64("A1").T + f64("a1"))
+    h1 = np.sin(g1 * s1 + b1)
+    s2 = h1 @ f64("A2").T + f64("a2")
+    h2 = np.sin(g2 * s2 + b2)
+    return h2 @ f64("A3").T + f64("a3")
+
+
+def gaussian_window(coords: np.ndarray, sigma: np.ndarray) -> np.ndarray:
+    """w[d, c] = exp(-|c|^2 / (2 sigma_d^2)) for coords [P, n]: [D, P] float64."""
+    r2 = np.sum(np.asarray(coords, np.float64) ** 2, axis=1)
+    sig = np.asarray(sigma, np.float64)
+    return np.exp(-np.outer(1.0 / (2.0 * sig * sig), r2))
+
+
+def _input_dependent(p: dict, registers: np.ndarray, coords: np.ndarray) -> np.ndarray:
+    z = register_summary(registers, p["q"])
+    w = gaussian_window(coords, p["sigma"])                              # [D, P]
+    return np.stack([film_siren(coords, z[b], p).T * w for b in range(z.shape[0])])
+
+
+def input_dependent_filter_1d(p: dict, registers: np.ndarray, L: int) -> np.ndarray:
+    """K[b, d, t] = w_d(t/L) f_d(t/L; z_b), t = 0..L-1: [B, D, L] float64 (taps of the causal or
+    periodic 1-D convolution; coordinate normalised as t/L like the exponential filter)."""
+    c = (np.arange(L, dtype=np.float64) / L)[:, None]
+    return _input_dependent(p, registers, c)
+
+
+def input_dependent_filter_3d(p: dict, registers: np.ndarray, n: int, circular: bool = False) -> np.ndarray:
+    """K[b, d, ...] on the 3-D offsets, coordinate r/n per axis: zero-padded [B, D, 2n-1, 2n-1, 2n-1]
+    (index = offset + n-1), or periodic [B, D, n, n, n] (centred offsets placed at r mod n)."""
+    r = filter_offsets_3d_circular(n) if circular else filter_offsets_3d(n)
+    vals = _input_dependent(p, registers, r.astype(np.float64) / n)      # [B, D, P]
+    if not circular:
+        m = 2 * n - 1
+        return vals.reshape(vals.shape[0], vals.shape[1], m, m, m)
+    h = np.zeros(vals.shape[:2] + (n, n, n), dtype=np.float64)
+    ri = r % n
+    h[:, :, ri[:, 0], ri[:, 1], ri[:, 2]] = vals
+    return h
 
 
 # --------------------------------------------------------------------------------------------

@@ -39,8 +39,9 @@ def test_bf16_matches_torch_conversion():
 
 
 def test_workloads_table():
-    assert [w.order for w in hi.WORKLOADS] == [2, 2, 3, 2, 2, 2, 2]
-    assert [w.mode for w in hi.WORKLOADS] == ["causal"] * 4 + ["linear", "circular", "circular"]
+    assert [w.order for w in hi.WORKLOADS] == [2, 2, 3, 2, 2, 2, 2, 2]
+    assert [w.mode for w in hi.WORKLOADS] == ["causal"] * 4 + ["linear", "circular", "circular", "linear"]
+    assert [w.filter for w in hi.WORKLOADS] == ["exp"] * 7 + ["film"]
     assert hi.WORKLOADS[1].tokens_channels == 4 * 768 * 8192
     assert hi.WORKLOADS[3].dims == (1 << 20,)
     assert hi.WORKLOADS[4].support == 127 ** 3
@@ -76,3 +77,19 @@ def test_dna_activations_take_four_values_per_channel():
             assert len(np.unique(a[0, d])) <= 4
     # the three streams come from different embedding columns
     assert not np.array_equal(v, xs[0])
+
+
+def test_film_draws_are_seeded_and_shaped():
+    w = hi.WORKLOADS[7]
+    p1, p2 = hi.draw_film_params(w), hi.draw_film_params(w)
+    assert len(p1) == 2
+    for k in p1[0]:
+        np.testing.assert_array_equal(p1[0][k], p2[0][k])
+        assert p1[0][k].dtype == np.float32
+    assert p1[0]["A1"].shape == (64, 3) and p1[0]["G2"].shape == (64, 128) and p1[0]["A3"].shape == (128, 64)
+    assert sorted(set(p1[0]["omega0"].tolist())) == list(hi.FILM_OMEGA0_BLOCKS)
+    assert np.all(p1[1]["sigma"] >= 0.2) and np.all(p1[1]["sigma"] < 0.8)
+    assert not np.array_equal(p1[0]["A2"], p1[1]["A2"])
+    r = hi.draw_registers(w)
+    assert r.shape == (2, 8, 128) and r.dtype == np.float32
+    np.testing.assert_array_equal(r, hi.draw_registers(w))

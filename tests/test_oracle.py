@@ -485,3 +485,173 @@ def test_circular_shift_equivariance():
                                rtol=0, atol=1e-12)
     np.testing.assert_allclose(orc.circular_conv_fft(np.roll(u, s), h), np.roll(orc.circular_conv_fft(u, h), s),
                                rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- input-dependent filters (HyenaND registers,
+# FiLM-modulated SIREN, Gaussian window)
+
+def test_register_summary_equal_scores_is_plain_mean():
+    rng = np.random.default_rng(40)
+    reg = rng.standard_normal((3, 5, 4))
+    np.testing.assert_allclose(orc.register_summary(reg, np.zeros(4)), reg.mean(axis=1), rtol=0, atol=1e-15)
+
+
+def test_register_summary_two_registers_logistic_weights():
+    # two registers: the softmax weights are the logistic function of the score difference
+    reg = np.array([[[1.0, 0.0, 2.0], [0.0, 1.0, -1.0]]])
+    q = np.array([0.5, -0.25, 1.0])
+    s1, s2 = 0.5 + 2.0, -0.25 - 1.0
+    a1 = 1.0 / (1.0 + math.exp(-(s1 - s2)))
+    want = a1 * reg[0, 0] + (1.0 - a1) * reg[0, 1]
+    np.testing.assert_allclose(orc.register_summary(reg, q)[0], want, rtol=0, atol=1e-15)
+
+
+def test_register_summary_permutation_invariant_and_dominant_register():
+    rng = np.random.default_rng(41)
+    reg = rng.standard_normal((2, 6, 8))
+    q = rng.standard_normal(8)
+    perm = rng.permutation(6)
+    np.testing.assert_allclose(orc.register_summary(reg[:, perm], q), orc.register_summary(reg, q), rtol=0, atol=1e-14)
+    # one register with a score far above the others takes all the weight
+    big = reg.copy()
+    big[:, 2] = 50.0 * q / np.linalg.norm(q)
+    np.testing.assert_allclose(orc.register_summary(big, q), big[:, 2], rtol=0, atol=1e-12)
+
+
+def _siren_closed_form_params(w):
+    # H = 2 units, one coordinate, D = 3 channels, FiLM switched off (gamma = 1, beta = 0)
+    return dict(A1=np.array([[1.0], [0.0]]), a1=np.array([0.0, 0.5]), omega0=np.array([w, 1.0]),
+                A2=np.eye(2), a2=np.zeros(2), A3=np.array([[1.0, 0.0], [0.0, 1.0], [1.0, 1.0]]),
+                a3=np.array([0.0, 0.0, 0.25]), G1=np.zeros((2, 2)), g1=np.ones(2), P1=np.zeros((2, 2)),
+                p1=np.zeros(2), G2=np.zeros((2, 2)), g2=np.ones(2), P2=np.zeros((2, 2)), p2=np.zeros(2),
+                q=np.zeros(2), sigma=np.array([0.3, 0.5, 1.0]))
+
+
+def test_siren_without_modulation_closed_form():
+    w = 7.0
+    p = _siren_closed_form_params(w)
+    c = np.linspace(-1, 1, 9)[:, None]
+    f = orc.film_siren(c, np.array([0.3, -0.2]), p)
+    u = np.sin(np.sin(w * c[:, 0]))
+    k = math.sin(math.sin(0.5))
+    np.testing.assert_allclose(f, np.stack([u, np.full(9, k), u + k + 0.25], axis=1), rtol=0, atol=1e-15)
+
+
+def test_film_scales_preactivation_and_shifts_it():
+    # gamma multiplies omega0 * (A1 c + a1) (bias included), beta is added after the scaling
+    w = 3.0
+    p = _siren_closed_form_params(w)
+    p.update(omega0=np.array([w, 2.0]), G1=np.array([[1.0, 0.0], [0.0, 0.0]]), g1=np.array([0.0, 1.0]),
+             P1=np.array([[0.0, 0.0], [0.0, 2.0]]), p1=np.array([0.0, 0.1]),
+             g2=np.array([3.0, 1.0]), P2=np.array([[0.0, 1.0], [0.0, 0.0]]),
+             A3=np.eye(2), a3=np.zeros(2), sigma=np.array([1.0, 1.0]))
+    z = np.array([2.0, -0.5])                 # gamma1 = (2, 1), beta1 = (0, -0.9), beta2 = (-0.5, 0)
+    c = np.linspace(0, 1, 5)[:, None]
+    f = orc.film_siren(c, z, p)
+    h1a = np.sin(2.0 * w * c[:, 0])
+    h1b = math.sin(1.0 * 2.0 * 0.5 - 0.9)
+    np.testing.assert_allclose(f[:, 0], np.sin(3.0 * h1a - 0.5), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(f[:, 1], np.full(5, math.sin(h1b)), rtol=0, atol=1e-15)
+
+
+def test_gaussian_window_against_normal_density():
+    import scipy.stats
+    rng = np.random.default_rng(42)
+    c = rng.uniform(-1, 1, size=(50, 3))
+    sigma = np.array([0.2, 0.5, 1.5])
+    w = orc.gaussian_window(c, sigma)
+    r = np.linalg.norm(c, axis=1)
+    for d, s in enumerate(sigma):
+        np.testing.assert_allclose(w[d], scipy.stats.norm.pdf(r, scale=s) / scipy.stats.norm.pdf(0.0, scale=s),
+                                   rtol=1e-13, atol=0)
+        # separable over the axes; one sigma away from the origin the window is exp(-1/2)
+        prod = np.prod(np.exp(-c ** 2 / (2 * s * s)), axis=1)
+        np.testing.assert_allclose(w[d], prod, rtol=1e-13, atol=0)
+    assert abs(orc.gaussian_window(np.array([[0.0, 0.6, 0.8]]), np.array([1.0]))[0, 0] - math.exp(-0.5)) < 1e-15
+
+
+def test_input_dependent_filter_1d_closed_form_without_conditioning():
+    # G = P = 0: every sample gets the same kernel, window(t/L) * closed-form SIREN(t/L)
+    w, L = 5.0, 16
+    p = _siren_closed_form_params(w)
+    reg = np.random.default_rng(43).standard_normal((3, 4, 2))
+    K = orc.input_dependent_filter_1d(p, reg, L)
+    assert K.shape == (3, 3, L)
+    c = np.arange(L) / L
+    u, k = np.sin(np.sin(w * c)), math.sin(math.sin(0.5))
+    f = np.stack([u, np.full(L, k), u + k + 0.25])
+    want = f * np.exp(-c[None, :] ** 2 / (2 * p["sigma"][:, None] ** 2))
+    for b in range(3):
+        np.testing.assert_allclose(K[b], want, rtol=0, atol=1e-15)
+
+
+def test_input_dependent_filter_follows_registers():
+    rng = np.random.default_rng(44)
+    H, E, D = 8, 6, 5
+    p = dict(A1=rng.uniform(-1, 1, (H, 1)), a1=rng.uniform(-1, 1, H), omega0=np.full(H, 4.0),
+             A2=rng.standard_normal((H, H)) * 0.3, a2=rng.standard_normal(H) * 0.1,
+             A3=rng.standard_normal((D, H)) * 0.3, a3=rng.standard_normal(D) * 0.1,
+             G1=rng.standard_normal((H, E)) * 0.2, g1=np.ones(H), P1=rng.standard_normal((H, E)) * 0.2,
+             p1=np.zeros(H), G2=rng.standard_normal((H, E)) * 0.2, g2=np.ones(H),
+             P2=rng.standard_normal((H, E)) * 0.2, p2=np.zeros(H), q=rng.standard_normal(E),
+             sigma=rng.uniform(0.2, 0.6, D))
+    reg = rng.standard_normal((3, 4, E))
+    reg[2] = reg[0]                          # samples 0 and 2 carry the same registers
+    K = orc.input_dependent_filter_1d(p, reg, 32)
+    np.testing.assert_array_equal(K[0], K[2])
+    assert np.max(np.abs(K[0] - K[1])) > 1e-3
+    # each sample's kernel is the FiLM-SIREN at that sample's z, times the window
+    z1 = orc.register_summary(reg, p["q"])[1]
+    c = (np.arange(32) / 32.0)[:, None]
+    np.testing.assert_allclose(K[1], orc.film_siren(c, z1, p).T * orc.gaussian_window(c, p["sigma"]), rtol=0,
+                               atol=1e-15)
+
+
+def test_input_dependent_filter_3d_axes_and_periodic_offsets():
+    # a network that sees only the x coordinate gives taps that vary along x alone (x is the slowest
+    # tap axis); the periodic filter equals the zero-padded one at every shared offset
+    rng = np.random.default_rng(45)
+    H, E, D, n = 4, 3, 2, 4
+    A1 = np.zeros((H, 3))
+    A1[:, 0] = rng.uniform(-1, 1, H)
+    p = dict(A1=A1, a1=rng.uniform(-1, 1, H), omega0=np.full(H, 3.0), A2=rng.standard_normal((H, H)) * 0.3,
+             a2=np.zeros(H), A3=rng.standard_normal((D, H)), a3=np.zeros(D), G1=rng.standard_normal((H, E)) * 0.1,
+             g1=np.ones(H), P1=np.zeros((H, E)), p1=np.zeros(H), G2=np.zeros((H, E)), g2=np.ones(H),
+             P2=np.zeros((H, E)), p2=np.zeros(H), q=np.zeros(E), sigma=np.array([1e6, 1e6]))
+    reg = rng.standard_normal((2, 2, E))
+    K = orc.input_dependent_filter_3d(p, reg, n)
+    assert K.shape == (2, D, 7, 7, 7)
+    np.testing.assert_allclose(K, np.broadcast_to(K[:, :, :, :1, :1], K.shape), rtol=0, atol=1e-9)
+    assert np.max(np.abs(K[:, :, 0] - K[:, :, 6])) > 1e-3
+    p["sigma"] = np.array([0.4, 0.7])
+    p["A1"] = rng.uniform(-1, 1, (H, 3))
+    Kl = orc.input_dependent_filter_3d(p, reg, n)
+    Kc = orc.input_dependent_filter_3d(p, reg, n, circular=True)
+    for r in orc.filter_offsets_3d_circular(n):
+        np.testing.assert_allclose(Kc[:, :, r[0] % n, r[1] % n, r[2] % n], Kl[:, :, r[0] + n - 1, r[1] + n - 1,
+                                   r[2] + n - 1], rtol=0, atol=0)
+
+
+def test_per_sample_filters_in_the_operator_match_row_by_row_sums():
+    # one filter per (b, d): the operator with [B, D, L] filters equals the definition applied row by row
+    rng = np.random.default_rng(46)
+    B, D, L = 2, 3, 12
+    v = rng.standard_normal((B, D, L))
+    xs = [rng.standard_normal((B, D, L)) for _ in range(2)]
+    hs = [rng.standard_normal((B, D, L)) for _ in range(2)]
+    y = orc.hyena_operator_rows(v, xs, hs)
+    for b in range(B):
+        for d in range(D):
+            u = v[b, d]
+            for h, x in zip(hs, xs):
+                u = x[b, d] * np.array([sum(h[b, d, t - s] * u[s] for s in range(t + 1)) for t in range(L)])
+            np.testing.assert_allclose(y[b, d], u, rtol=1e-12, atol=1e-12)
+    # 3-D periodic with per-sample filters, against the brute-force definition per volume
+    n = 3
+    v3 = rng.standard_normal((B * D, n, n, n))
+    x3 = [rng.standard_normal((B * D, n, n, n))]
+    h3 = [rng.standard_normal((B * D, n, n, n))]
+    y3 = orc.hyena_operator_3d(v3, x3, h3, circular=True)
+    for j in range(B * D):
+        np.testing.assert_allclose(y3[j], x3[0][j] * orc.circular_conv3d_direct(v3[j], h3[0][j]), rtol=1e-12,
+                                   atol=1e-12)
