@@ -17,6 +17,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "hyena.h")
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP, EALIAS = 0, -1, -2, -3, -4, -5
 F32, BF16 = 0, 1
 CAUSAL, LINEAR, CIRCULAR = 0, 1, 2
+PER_SAMPLE = 8          # mode flag: one filter per (b, d) (input-dependent filters)
 
 
 class HyenaError(RuntimeError):
@@ -33,6 +34,12 @@ class FilterParams(ctypes.Structure):
     _fields_ = [("F", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
                 ("W1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("W2", ctypes.c_void_p),
                 ("b2", ctypes.c_void_p), ("alpha", ctypes.c_void_p)]
+
+
+class FilmParams(ctypes.Structure):
+    _fields_ = [("E", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32)] + [
+        (k, ctypes.c_void_p) for k in ("q", "A1", "a1", "omega0", "A2", "a2", "A3", "a3", "G1", "g1", "P1", "p1",
+                                       "G2", "g2", "P2", "p2", "sigma")]
 
 
 _lib = None
@@ -52,6 +59,11 @@ _SIG = {
                                   _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p,
                                   _c.c_size_t, _c.c_void_p]),
     "hyena_spectrum_export": (_c.c_int, [Dims, _c.c_int, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "hyena_film_filter_workspace_bytes": (_c.c_int, [_c.c_int64, Dims, _c.c_int, _c.c_int64,
+                                                     _c.POINTER(_c.c_size_t)]),
+    "hyena_film_filter_gen": (_c.c_int, [_c.POINTER(FilmParams), _c.c_int64, _c.c_int32, _c.c_void_p, Dims,
+                                         _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
+                                         _c.c_void_p]),
 }
 
 
@@ -184,6 +196,39 @@ def filter_gen(params: dict, point_shape: Sequence[int], h_time=None, spectrum=N
     return spectrum
 
 
+def film_filter_workspace_bytes(B: int, point_shape: Sequence[int], D: int, mode: Optional[int] = None) -> int:
+    n = ctypes.c_size_t()
+    mode = mode_for(len(point_shape)) if mode is None else mode
+    _check(lib().hyena_film_filter_workspace_bytes(B, dims_of(point_shape), mode, D, ctypes.byref(n)),
+           "hyena_film_filter_workspace_bytes")
+    return n.value
+
+
+FILM_KEYS = ("q", "A1", "a1", "omega0", "A2", "a2", "A3", "a3", "G1", "g1", "P1", "p1", "G2", "g2", "P2", "p2",
+             "sigma")
+
+
+def film_filter_gen(params: dict, registers, point_shape: Sequence[int], h_time=None, spectrum=None,
+                    mode: Optional[int] = None):
+    """Input-dependent filters of one order for every sample.  params: dict of CUDA float32 tensors
+    (FILM_KEYS; A3 [D, H], G1 [H, E], ...); registers: [B, R, E] CUDA float32.  Returns the spectra of
+    the B*D filters (opaque uint8 tensor, for mode | PER_SAMPLE); fills h_time [B, D, taps] when given."""
+    torch = _torch()
+    B, R, E = registers.shape
+    H = params["A2"].shape[0]
+    D = params["A3"].shape[0]
+    dev = registers.device
+    mode = mode_for(len(point_shape)) if mode is None else mode
+    if spectrum is None:
+        spectrum = torch.empty(spectrum_bytes(point_shape, B * D, mode | PER_SAMPLE), dtype=torch.uint8, device=dev)
+    ws = _workspace(film_filter_workspace_bytes(B, point_shape, D, mode), dev)
+    p = FilmParams(E, H, D, *[_ptr(params[k]) for k in FILM_KEYS])
+    _check(lib().hyena_film_filter_gen(ctypes.byref(p), B, R, _ptr(registers), dims_of(point_shape), mode,
+                                       _ptr(h_time), _ptr(spectrum), _ptr(ws), ws.numel(), _stream(registers)),
+           "hyena_film_filter_gen")
+    return spectrum
+
+
 def fftconv(u, spectrum, gate=None, y=None, mode: Optional[int] = None):
     """y = gate * (h conv u) (or h conv u when gate is None); u: [B, D, *points]."""
     torch = _torch()
@@ -227,11 +272,12 @@ def spectrum_export(spectrum, point_shape: Sequence[int], D: int, mode: Optional
     """Engine-ordered spectrum -> complex64 tensor of natural-order bins (testing aid)."""
     torch = _torch()
     mode = mode_for(len(point_shape)) if mode is None else mode
+    circ = (mode & ~PER_SAMPLE) == CIRCULAR
     if len(point_shape) == 1:
-        shape = (D, (point_shape[0] // 2 if mode == CIRCULAR else point_shape[0]) + 1)
+        shape = (D, (point_shape[0] // 2 if circ else point_shape[0]) + 1)
     else:
         nx, ny, nz = point_shape
-        shape = (D, nx, ny, nz // 2 + 1) if mode == CIRCULAR else (D, 2 * nx, 2 * ny, nz + 1)
+        shape = (D, nx, ny, nz // 2 + 1) if circ else (D, 2 * nx, 2 * ny, nz + 1)
     H = torch.zeros(shape, dtype=torch.complex64, device=spectrum.device)
     _check(lib().hyena_spectrum_export(dims_of(point_shape), mode, D, _ptr(spectrum), H.data_ptr(),
                                        _stream(spectrum)), "hyena_spectrum_export")

@@ -190,14 +190,14 @@ int conv_mfma_chain(int64_t B, int64_t D, int64_t L, const void* u, const void* 
 }
 
 int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const void* spectrum, const void* gate,
-              void* y, const Twiddles& tw, hipStream_t s) {
-  if (use_mfma(dtype, B, L) && aligned16(u) && aligned16(gate) && aligned16(y)) {
+              void* y, const Twiddles& tw, hipStream_t s, int hsb) {
+  if (!hsb && use_mfma(dtype, B, L) && aligned16(u) && aligned16(gate) && aligned16(y)) {
     const void* g[1] = {gate};
     const void* sp[1] = {spectrum};
     return conv_mfma_chain(B, D, L, u, g, sp, 1, y, tw, s);
   }
   return hip_status(launch_conv1d_single(log2i(L), dtype == HYENA_BF16, u, gate, y, (const float2*)spectrum,
-                                         (int)B, (int)D, tw, s));
+                                         (int)B, (int)D, tw, s, 0, hsb));
 }
 
 // Multi-pass chunk rows that fit the caller's workspace (0 when it is too small).
@@ -206,6 +206,71 @@ int chunk_from_ws(size_t per, int64_t rows, void* ws, size_t ws_bytes) {
   if ((size_t)ws & 255u) return 0;
   const int64_t c = (int64_t)(ws_bytes / per);
   return (int)(c < rows ? c : rows);
+}
+
+// Align a workspace cursor to 256 bytes; false when the remaining room is too small.
+bool ws_align256(char*& p, size_t& n) {
+  const size_t mis = (size_t)p & 255u;
+  if (!mis) return true;
+  const size_t adv = 256 - mis;
+  if (n < adv) return false;
+  p += adv;
+  n -= adv;
+  return true;
+}
+
+// Filter spectra of `nch` channels from their taps h [nch, taps] (the workspace [wsp, wsp + wsn) holds the
+// multi-pass intermediate or the matrix-core copy's staging).  pair_copy: also write the bf16 row-pair
+// copy (L = 8192 causal, one filter per channel).
+int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* spectrum, char* wsp, size_t wsn,
+                      bool pair_copy, const Twiddles& tw, hipStream_t stream) {
+  int st;
+  const size_t row_b = filter_intermediate_bytes(kind, L);
+  int chunk = 0;
+  if (row_b) {
+    if (!ws_align256(wsp, wsn)) return HYENA_EWORKSPACE;
+    const int64_t c = (int64_t)(wsn / row_b);
+    if (c < 1) return HYENA_EWORKSPACE;
+    chunk = (int)(c < nch ? c : nch);
+  }
+  if (is3d(kind))
+    return hip_status(launch_spectrum3d(h, (float2*)spectrum, (int)nch, (float2*)wsp, chunk, tw, stream, circ3(kind)));
+  if (row_b) {
+    // fp32 spectrum, then its bf16 copy for the bf16 plans' row pass
+    const int lg = engine_log2(kind, L);
+    if ((st = hip_status(launch_spectrum1d_fourstep(lg, h, (float2*)spectrum, (int)nch, (float2*)wsp, chunk, tw,
+                                                    stream, kind == K_CIRC1 ? 1 : 0))))
+      return st;
+    const size_t n = (size_t)nch << lg;
+    return hip_status(launch_spectrum_bf16_copy((const float2*)spectrum, (char*)spectrum + n * sizeof(float2), n, stream));
+  }
+  if (kind == K_CIRC1)
+    return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, (int)nch, tw, stream, 1));
+  if ((st = hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, (int)nch, tw, stream)))) return st;
+  if (pair_copy && has_pair_copy(L)) {
+    // natural-order bins into the workspace, then the pair-order bf16 copy after the fp32 spectrum
+    if (!ws_align256(wsp, wsn) || wsn < pair_copy_temp_bytes(L, nch)) return HYENA_EWORKSPACE;
+    float2* nat = (float2*)wsp;
+    if ((st = hip_status(launch_export1d_single(log2i(L), (const float2*)spectrum, nat, (int)nch, stream)))) return st;
+    void* pair = (char*)spectrum + (size_t)nch * (size_t)L * sizeof(float2);
+    return hip_status(launch_pair_spectrum(nat, pair, (int)nch, stream));
+  }
+  return HYENA_OK;
+}
+
+// Whether spectra_from_taps finds the room it needs in [wsp, wsp + wsn) (checked before any launch).
+bool spectra_ws_ok(int kind, int64_t L, int64_t nch, char* wsp, size_t wsn, bool pair_copy) {
+  const size_t row_b = filter_intermediate_bytes(kind, L);
+  if (row_b) return ws_align256(wsp, wsn) && wsn >= row_b;
+  if (pair_copy && kind == K_CAUSAL && has_pair_copy(L))
+    return ws_align256(wsp, wsn) && wsn >= pair_copy_temp_bytes(L, nch);
+  return true;
+}
+
+// Split the per-sample flag off a mode argument.
+int split_mode(int mode, bool* per_sample) {
+  *per_sample = (mode & HYENA_PER_SAMPLE) != 0;
+  return mode & ~HYENA_PER_SAMPLE;
 }
 
 }  // namespace
@@ -228,6 +293,8 @@ const char* hyena_status_str(int status) {
 
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   if (!bytes || D <= 0) return HYENA_EINVAL;
+  bool ps = false;
+  mode = split_mode(mode, &ps);
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
@@ -237,7 +304,8 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   if (is3d(kind)) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel(circ3(kind));
   else if (kind == K_CIRC1) *bytes = (size_t)D * (size_t)(pts / 2) * (sizeof(float2) + mp_copy);
   else if (mp_copy) *bytes = (size_t)D * (size_t)pts * (sizeof(float2) + mp_copy);
-  else *bytes = (size_t)D * (size_t)pts * sizeof(float2) + (has_pair_copy(pts) ? (size_t)D * mfma_pair_spectrum_bytes_per_channel() : 0);
+  else *bytes = (size_t)D * (size_t)pts * sizeof(float2) +
+                (has_pair_copy(pts) && !ps ? (size_t)D * mfma_pair_spectrum_bytes_per_channel() : 0);
   return HYENA_OK;
 }
 
@@ -256,6 +324,8 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* b
 
 int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, size_t* bytes) {
   if (!bytes || order < 1 || B <= 0 || D <= 0 || (dtype != HYENA_F32 && dtype != HYENA_BF16)) return HYENA_EINVAL;
+  bool ps = false;
+  mode = split_mode(mode, &ps);
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
@@ -275,9 +345,6 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
   const int kind = kind_of(mode, dims);
   if (p->H != 64 || p->F != (dims.ndim == 1 ? 64 : 96)) return HYENA_EUNSUPPORTED;
   const size_t hbytes = (size_t)p->D * taps_per_channel(kind, pts) * sizeof(float);
-  const int64_t L = pts;
-  const size_t row_b = filter_intermediate_bytes(kind, pts);
-  const bool multi = row_b != 0;
   char* wsp = (char*)ws;
   size_t wsn = ws ? ws_bytes : 0;
   float* h = h_time;
@@ -287,57 +354,82 @@ int hyena_filter_gen(const hyena_filter_params* p, hyena_dims dims, int mode, fl
     wsp += hbytes;
     wsn -= hbytes;
   }
-  int chunk = 0;
-  if (multi) {
-    // 256-byte alignment for the intermediate rows
-    const size_t mis = (size_t)wsp & 255u;
-    if (mis) {
-      const size_t adv = 256 - mis;
-      if (wsn < adv) return HYENA_EWORKSPACE;
-      wsp += adv;
-      wsn -= adv;
-    }
-    const int64_t c = (int64_t)(wsn / row_b);
-    if (c < 1) return HYENA_EWORKSPACE;
-    chunk = (int)(c < p->D ? c : p->D);
-  }
+  if (!spectra_ws_ok(kind, pts, p->D, wsp, wsn, true)) return HYENA_EWORKSPACE;
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
   FilterArgs a{p->F, p->H, p->D, p->W1, p->b1, p->W2, p->b2, p->alpha};
-  if (is3d(kind)) {
-    if ((st = hip_status(launch_filter3d(a, h, stream, circ3(kind))))) return st;
-    return hip_status(launch_spectrum3d(h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream, circ3(kind)));
-  }
-  if ((st = hip_status(launch_filter1d(a, (int)L, h, stream)))) return st;
-  if (multi) {
-    // fp32 spectrum, then its bf16 copy for the bf16 plans' row pass
-    const int lg = engine_log2(kind, L);
-    if ((st = hip_status(launch_spectrum1d_fourstep(lg, h, (float2*)spectrum, p->D, (float2*)wsp, chunk, tw, stream,
-                                                    kind == K_CIRC1 ? 1 : 0))))
-      return st;
-    const size_t n = (size_t)p->D << lg;
-    return hip_status(launch_spectrum_bf16_copy((const float2*)spectrum, (char*)spectrum + n * sizeof(float2), n, stream));
-  }
-  if (kind == K_CIRC1)
-    return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, p->D, tw, stream, 1));
-  if ((st = hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, p->D, tw, stream)))) return st;
-  if (has_pair_copy(L)) {
-    // natural-order bins into the workspace, then the pair-order bf16 copy after the fp32 spectrum
-    const size_t mis = (size_t)wsp & 255u;
-    const size_t adv = mis ? 256 - mis : 0;
-    if (wsn < adv + pair_copy_temp_bytes(L, p->D)) return HYENA_EWORKSPACE;
-    float2* nat = (float2*)(wsp + adv);
-    if ((st = hip_status(launch_export1d_single(log2i(L), (const float2*)spectrum, nat, p->D, stream)))) return st;
-    void* pair = (char*)spectrum + (size_t)p->D * (size_t)L * sizeof(float2);
-    return hip_status(launch_pair_spectrum(nat, pair, p->D, stream));
-  }
+  if (is3d(kind)) st = hip_status(launch_filter3d(a, h, stream, circ3(kind)));
+  else st = hip_status(launch_filter1d(a, (int)pts, h, stream));
+  if (st) return st;
+  return spectra_from_taps(kind, pts, h, p->D, spectrum, wsp, wsn, true, tw, stream);
+}
+
+int hyena_film_filter_workspace_bytes(int64_t B, hyena_dims dims, int mode, int64_t D, size_t* bytes) {
+  if (!bytes || B <= 0 || D <= 0) return HYENA_EINVAL;
+  bool ps = false;
+  mode = split_mode(mode, &ps);
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  const int kind = kind_of(mode, dims);
+  const int64_t nch = B * D;
+  *bytes = (size_t)B * 4 * kFilmHidden * sizeof(float);
+  *bytes = (*bytes + 255) / 256 * 256 + (size_t)nch * taps_per_channel(kind, pts) * sizeof(float);
+  const size_t per = filter_intermediate_bytes(kind, pts);
+  if (per) *bytes += 256 + (size_t)default_chunk_rows((int64_t)per, nch) * per;
   return HYENA_OK;
+}
+
+int hyena_film_filter_gen(const hyena_film_params* p, int64_t B, int32_t R, const float* registers, hyena_dims dims,
+                          int mode, float* h_time, void* spectrum, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!p || !registers || !spectrum || !ws || B <= 0 || R <= 0 || p->D <= 0 || p->E <= 0) return HYENA_EINVAL;
+  const float* need[] = {p->q, p->A1, p->a1, p->omega0, p->A2, p->a2, p->A3, p->a3, p->G1, p->g1,
+                         p->P1, p->p1, p->G2, p->g2, p->P2, p->p2, p->sigma};
+  for (const float* q : need)
+    if (!q) return HYENA_EINVAL;
+  bool ps = false;
+  mode = split_mode(mode, &ps);
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  const int kind = kind_of(mode, dims);
+  if (p->H != kFilmHidden || p->E > kFilmMaxE || R > kFilmMaxR || B > 65535) return HYENA_EUNSUPPORTED;
+  const int64_t nch = B * p->D;
+  if (nch > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
+  char* wsp = (char*)ws;
+  size_t wsn = ws_bytes;
+  const size_t mod_b = (size_t)B * 4 * kFilmHidden * sizeof(float);
+  if (!ws_align256(wsp, wsn) || wsn < mod_b) return HYENA_EWORKSPACE;
+  float* mod = (float*)wsp;
+  wsp += mod_b;
+  wsn -= mod_b;
+  float* h = h_time;
+  if (!h) {
+    const size_t hbytes = (size_t)nch * taps_per_channel(kind, pts) * sizeof(float);
+    if (!ws_align256(wsp, wsn) || wsn < hbytes) return HYENA_EWORKSPACE;
+    h = (float*)wsp;
+    wsp += hbytes;
+    wsn -= hbytes;
+  }
+  if (!spectra_ws_ok(kind, pts, nch, wsp, wsn, false)) return HYENA_EWORKSPACE;
+  Twiddles tw;
+  if ((st = get_twiddles(&tw))) return st;
+  FilmArgs a{p->E, p->H, p->D, dims.ndim, p->q, p->A1, p->a1, p->omega0, p->A2, p->a2, p->A3, p->a3,
+             p->G1, p->g1, p->P1, p->p1, p->G2, p->g2, p->P2, p->p2, p->sigma};
+  if ((st = hip_status(launch_film_prep(a, registers, (int)B, R, mod, stream)))) return st;
+  if (is3d(kind)) st = hip_status(launch_film_filter3d(a, mod, (int)B, h, stream, circ3(kind)));
+  else st = hip_status(launch_film_filter1d(a, mod, (int)B, (int)pts, h, stream));
+  if (st) return st;
+  return spectra_from_taps(kind, pts, h, nch, spectrum, wsp, wsn, false, tw, stream);
 }
 
 int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void* u, const void* spectrum,
                   const void* gate, void* y, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (B <= 0 || D <= 0 || !u || !spectrum || !y || (dtype != HYENA_F32 && dtype != HYENA_BF16)) return HYENA_EINVAL;
   if (B * D > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
+  bool ps = false;
+  mode = split_mode(mode, &ps);
+  const int hsb = ps ? (int)D : 0;
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
@@ -360,15 +452,15 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
     const void* sp[1] = {spectrum};
     if (is3d(kind))
       return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
-                                      stream, circ3(kind)));
+                                      stream, circ3(kind), hsb));
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs,
                                              sp, y, (float2*)ws, chunk, tw, device_mats(), stream,
-                                             kind == K_CIRC1 ? 1 : 0));
+                                             kind == K_CIRC1 ? 1 : 0, hsb));
   }
   if (kind == K_CIRC1)
     return hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, u, gate, y,
-                                           (const float2*)spectrum, (int)B, (int)D, tw, stream, 1));
-  return conv_once(B, D, pts, dtype, u, spectrum, gate, y, tw, stream);
+                                           (const float2*)spectrum, (int)B, (int)D, tw, stream, 1, hsb));
+  return conv_once(B, D, pts, dtype, u, spectrum, gate, y, tw, stream, hsb);
 }
 
 int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void* v,
@@ -379,6 +471,9 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   for (int i = 0; i < order; ++i)
     if (!x[i] || !spectra[i]) return HYENA_EINVAL;
   if (B * D > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
+  bool ps = false;
+  mode = split_mode(mode, &ps);
+  const int hsb = ps ? (int)D : 0;
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
@@ -400,29 +495,29 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   if ((st = get_twiddles(&tw))) return st;
   if (chunk && is3d(kind))
     return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws, chunk,
-                                    tw, stream, circ3(kind)));
+                                    tw, stream, circ3(kind), hsb));
   if (chunk)
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
                                              spectra, y, (float2*)ws, chunk, tw, device_mats(), stream,
-                                             kind == K_CIRC1 ? 1 : 0));
+                                             kind == K_CIRC1 ? 1 : 0, hsb));
   if (kind == K_CIRC1) {
     const void* cur = v;
     for (int i = 0; i < order; ++i) {
       if ((st = hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, cur, x[i], y,
-                                                (const float2*)spectra[i], (int)B, (int)D, tw, stream, 1))))
+                                                (const float2*)spectra[i], (int)B, (int)D, tw, stream, 1, hsb))))
         return st;
       cur = y;
     }
     return HYENA_OK;
   }
-  if (use_mfma(dtype, B, pts)) {
+  if (!hsb && use_mfma(dtype, B, pts)) {
     bool aligned = aligned16(v) && aligned16(y);
     for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);
     if (aligned) return conv_mfma_chain(B, D, pts, v, x, spectra, order, y, tw, stream);
   }
   const void* cur = v;
   for (int i = 0; i < order; ++i) {
-    if ((st = conv_once(B, D, pts, dtype, cur, spectra[i], x[i], y, tw, stream))) return st;
+    if ((st = conv_once(B, D, pts, dtype, cur, spectra[i], x[i], y, tw, stream, hsb))) return st;
     cur = y;
   }
   return HYENA_OK;
@@ -430,6 +525,9 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
 
 int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spectrum, void* H, hipStream_t stream) {
   if (D <= 0 || !spectrum || !H) return HYENA_EINVAL;
+  bool ps = false;
+  mode = split_mode(mode, &ps);
+  if (D > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
   int64_t pts = 0;
   int st = check_dims(dims, mode, &pts);
   if (st) return st;

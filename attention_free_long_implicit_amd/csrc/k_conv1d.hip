@@ -47,7 +47,7 @@ struct Single {
 template <int LOG2M, bool BF16, bool GATE, bool FULL>
 __global__ void __launch_bounds__(Single<LOG2M>::T, 4)
 k_conv1d(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* gate,
-         typename Store<BF16>::elem* y, const float2* __restrict__ Hs, int B, int D, Twiddles tw) {
+         typename Store<BF16>::elem* y, const float2* __restrict__ Hs, int B, int D, int hsb, Twiddles tw) {
   using C = Single<LOG2M>;
   using En = typename C::En;
   using St = Store<BF16>;
@@ -69,7 +69,7 @@ k_conv1d(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* 
   const auto P = C::NP::of(t);
   En::fwd_last(x, lds, P.betaA, P.betaB);
 
-  const float2* hs = Hs + (size_t)d * M + t;
+  const float2* hs = Hs + (size_t)(d + b * hsb) * M + t;     // hsb = 0: one filter per channel; D: per (b, d)
   if (!P.special) {
     spectral_complement<RP, 0>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapA)), hs, T, nullptr, 0.f);
   } else {
@@ -150,26 +150,26 @@ __global__ void k_export1d(const float2* __restrict__ Hs, float2* __restrict__ H
 // ------------------------------------------------------------------ host launchers
 namespace {
 template <int LOG2M, bool BF16, bool FULL>
-void conv1d_launch_t(bool gate, const void* u, const void* g, void* y, const float2* Hs, int B, int D,
+void conv1d_launch_t(bool gate, const void* u, const void* g, void* y, const float2* Hs, int B, int D, int hsb,
                      const Twiddles& tw, hipStream_t s) {
   using E = typename Store<BF16>::elem;
   dim3 grid(B * D), block(Single<LOG2M>::T);
   if (gate)
     hipLaunchKernelGGL((k_conv1d<LOG2M, BF16, true, FULL>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs,
-                       B, D, tw);
+                       B, D, hsb, tw);
   else
     hipLaunchKernelGGL((k_conv1d<LOG2M, BF16, false, FULL>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs,
-                       B, D, tw);
+                       B, D, hsb, tw);
 }
 template <int LOG2M>
 hipError_t conv1d_launch(int bf16, bool gate, bool full, const void* u, const void* g, void* y, const float2* Hs,
-                         int B, int D, const Twiddles& tw, hipStream_t s) {
+                         int B, int D, int hsb, const Twiddles& tw, hipStream_t s) {
   if (bf16)
-    full ? conv1d_launch_t<LOG2M, true, true>(gate, u, g, y, Hs, B, D, tw, s)
-         : conv1d_launch_t<LOG2M, true, false>(gate, u, g, y, Hs, B, D, tw, s);
+    full ? conv1d_launch_t<LOG2M, true, true>(gate, u, g, y, Hs, B, D, hsb, tw, s)
+         : conv1d_launch_t<LOG2M, true, false>(gate, u, g, y, Hs, B, D, hsb, tw, s);
   else
-    full ? conv1d_launch_t<LOG2M, false, true>(gate, u, g, y, Hs, B, D, tw, s)
-         : conv1d_launch_t<LOG2M, false, false>(gate, u, g, y, Hs, B, D, tw, s);
+    full ? conv1d_launch_t<LOG2M, false, true>(gate, u, g, y, Hs, B, D, hsb, tw, s)
+         : conv1d_launch_t<LOG2M, false, false>(gate, u, g, y, Hs, B, D, hsb, tw, s);
   return hipGetLastError();
 }
 template <int LOG2M>
@@ -193,10 +193,10 @@ bool single_pass_supported(int log2L) { return log2L >= 10 && log2L <= 14; }
 #define HYENA_SINGLE_CASES(X) X(10) X(11) X(12) X(13) X(14)
 
 hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* gate, void* y, const float2* Hs,
-                                int B, int D, const Twiddles& tw, hipStream_t s, int full) {
+                                int B, int D, const Twiddles& tw, hipStream_t s, int full, int hsb) {
   const bool g = gate != nullptr;
   switch (log2L) {
-#define X(n) case n: return conv1d_launch<n>(bf16, g, full != 0, u, gate, y, Hs, B, D, tw, s);
+#define X(n) case n: return conv1d_launch<n>(bf16, g, full != 0, u, gate, y, Hs, B, D, hsb, tw, s);
     HYENA_SINGLE_CASES(X)
 #undef X
   }

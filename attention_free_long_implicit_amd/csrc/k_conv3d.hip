@@ -230,7 +230,8 @@ k3_planes_taps(const float* __restrict__ h, float2* I, int q0, int nq, Twiddles 
 // grid.x = TILES * nq (volume fastest).
 template <class G, int MODE>
 __global__ void __launch_bounds__(k3::T)
-k3_cols(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq, int B, Twiddles tw) {
+k3_cols(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq, int B, int hsb,
+        Twiddles tw) {
   using C = K3<G>;
   constexpr int N = C::N, T = C::T, MP = C::MP, COLS = C::COLS, PLANE = C::PLANE, TILES = C::TILES;
   using XEng = typename C::XEng;
@@ -240,7 +241,8 @@ k3_cols(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, i
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int ql = lb % nq, tile = lb / nq;
   const int q = q0 + ql;
-  const int d = (MODE == 0) ? q / B : q;
+  // spectrum channel: d (one filter per channel, hsb = 0) or b * D + d (one per (b, d), hsb = D)
+  const int d = (MODE == 0) ? q / B + (q % B) * hsb : q;
   const int j0 = tile * COLS;
   float2* base = I + (size_t)ql * NX * PLANE + j0;
   static_for<(NX * COLS) / T>([&](auto ii) {
@@ -316,7 +318,7 @@ size_t conv3d_taps_per_channel(int circ) {
 namespace {
 template <class G, bool BF16>
 hipError_t conv3d_launch_t(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
-                           void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s) {
+                           void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s, int hsb) {
   using C = K3<G>;
   constexpr int N = C::N, T = C::T, TILES = C::TILES;
   using E = typename Store<BF16>::elem;
@@ -327,7 +329,7 @@ hipError_t conv3d_launch_t(int order, int B, int D, const void* v, const void* c
                        (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
       hipLaunchKernelGGL((k3_cols<G, 0>), dim3(TILES * nq), dim3(T), 0, s, I, (const float2*)spectra[i],
-                         (float2*)nullptr, q0, nq, B, tw);
+                         (float2*)nullptr, q0, nq, B, hsb, tw);
       if (i + 1 < order)
         hipLaunchKernelGGL((k3_planes<G, BF16, 1, true, true>), dim3(N * nq), dim3(T), 0, s, (const E*)nullptr,
                            (const E*)x[i], (E*)nullptr, I, q0, nq, B, D, tw);
@@ -352,7 +354,7 @@ hipError_t spectrum3d_launch_t(const float* h, float2* Hs, int D, float2* I, int
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
     hipLaunchKernelGGL((k3_planes_taps<G>), dim3(C::MP * nq), dim3(C::T), 0, s, h, I, q0, nq, tw);
     hipLaunchKernelGGL((k3_cols<G, 1>), dim3(C::TILES * nq), dim3(C::T), 0, s, I, (const float2*)nullptr, Hs, q0,
-                       nq, 1, tw);
+                       nq, 1, 0, tw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -370,12 +372,12 @@ hipError_t export3d_launch_t(const float2* Hs, float2* H, int D, hipStream_t s) 
 
 hipError_t launch_conv3d(int bf16, int order, int B, int D, const void* v, const void* const* x,
                          const void* const* spectra, void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s,
-                         int circ) {
+                         int circ, int hsb) {
   if (circ)
-    return bf16 ? conv3d_launch_t<Geo3<true>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s)
-                : conv3d_launch_t<Geo3<true>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
-  return bf16 ? conv3d_launch_t<Geo3<false>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s)
-              : conv3d_launch_t<Geo3<false>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s);
+    return bf16 ? conv3d_launch_t<Geo3<true>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb)
+                : conv3d_launch_t<Geo3<true>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb);
+  return bf16 ? conv3d_launch_t<Geo3<false>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb)
+              : conv3d_launch_t<Geo3<false>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb);
 }
 
 hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,

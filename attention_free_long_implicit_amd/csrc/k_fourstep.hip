@@ -194,7 +194,7 @@ k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
 template <int LOG2M, int MODE, bool IBF16>
 __global__ void __launch_bounds__(FS<LOG2M>::TR)
 k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __restrict__ Hs_out, int q0, int nq,
-          int B, Twiddles tw) {
+          int B, int hsb, Twiddles tw) {
   using HT = typename Inter<IBF16>::T;   // spectrum element: fp32 complex, or a bf16 pair word
   const HT* __restrict__ Hs = static_cast<const HT*>(Hsv);
   using F = FS<LOG2M>;
@@ -208,7 +208,8 @@ k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __r
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int ql = lb % nq, grp = lb / nq;
   const int q = q0 + ql;
-  const int d = (MODE == 0) ? q / B : q;
+  // spectrum channel: d (one filter per channel, hsb = 0) or b * D + d (one per (b, d), hsb = D)
+  const int d = (MODE == 0) ? q / B + (q % B) * hsb : q;
   typename In::T* Irow = I + (size_t)ql * M;
 
   // bin row k1 of sub-row s (s = 2j: first of pair j, 2j+1: second)
@@ -347,7 +348,7 @@ size_t fs_row_bytes() { return (size_t)(1 << LOG2M) * sizeof(float2); }
 
 template <int LOG2M, bool BF16, bool FULL>
 hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
-                          void* y, float2* I, int chunk, const Twiddles& tw, const void* mats, hipStream_t s) {
+                          void* y, float2* I, int chunk, const Twiddles& tw, const void* mats, hipStream_t s, int hsb) {
   // bf16 causal plans with 128-point columns run their column passes on the matrix cores
   const bool mc = BF16 && !FULL && mats && fs_cols_mfma_supported(LOG2M);
   using F = FS<LOG2M>;
@@ -366,9 +367,10 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
                          (const E*)v, (const E*)nullptr, (E*)nullptr, Ib, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
       // bf16 plans read the bf16 copy stored after the fp32 spectrum
-      const void* hs = BF16 ? (const void*)((const char*)spectra[i] + (size_t)D * F::M * sizeof(float2)) : spectra[i];
+      const size_t nch = hsb ? (size_t)B * D : (size_t)D;       // filters in the spectrum
+      const void* hs = BF16 ? (const void*)((const char*)spectra[i] + nch * F::M * sizeof(float2)) : spectra[i];
       hipLaunchKernelGGL((k_fs_rows<LOG2M, 0, BF16>), dim3(groups * nq), dim3(F::TR), 0, s, Ib, hs,
-                         (float2*)nullptr, q0, nq, B, tw);
+                         (float2*)nullptr, q0, nq, B, hsb, tw);
       if (mc)
         (void)launch_fs_cols_mfma(LOG2M, 1, x[i] != nullptr, i + 1 < order, nullptr, x[i], y, Ib, q0, nq, B, D, mats,
                                   s);
@@ -398,7 +400,7 @@ hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int 
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
     hipLaunchKernelGGL((k_fs_cols_taps<LOG2M, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s, h, I, q0, nq, tw);
     hipLaunchKernelGGL((k_fs_rows<LOG2M, 1, false>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const void*)nullptr,
-                       Hs, q0, nq, 1, tw);
+                       Hs, q0, nq, 1, 0, tw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -432,15 +434,15 @@ hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int 
 
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, const void* mats, hipStream_t s, int full) {
+                                  const Twiddles& tw, const void* mats, hipStream_t s, int full, int hsb) {
   switch (log2L) {
-#define X(n)                                                                                              \
-  case n:                                                                                                 \
-    if (full)                                                                                             \
-      return bf16 ? fs_conv_launch<n, true, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s)   \
-                  : fs_conv_launch<n, false, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s); \
-    return bf16 ? fs_conv_launch<n, true, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s)    \
-                : fs_conv_launch<n, false, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s);
+#define X(n)                                                                                                   \
+  case n:                                                                                                      \
+    if (full)                                                                                                  \
+      return bf16 ? fs_conv_launch<n, true, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s, hsb)   \
+                  : fs_conv_launch<n, false, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s, hsb); \
+    return bf16 ? fs_conv_launch<n, true, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s, hsb)    \
+                : fs_conv_launch<n, false, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s, hsb);
     HYENA_FS_CASES(X)
 #undef X
   }

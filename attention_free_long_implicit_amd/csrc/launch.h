@@ -10,8 +10,10 @@ namespace hyena {
 // ---- 1-D, one workgroup per row: an M = 2^log2L point packed transform, 10 <= log2L <= 14.
 // full = 0: causal, rows of M samples (zero-padded to 2M); full = 1: periodic, rows of 2M samples.
 bool single_pass_supported(int log2L);
+// hsb (every conv launcher): 0 when the spectrum holds one filter per channel d, D when it holds one per
+// (b, d) in [B, D] order (input-dependent filters).
 hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* gate, void* y, const float2* Hs,
-                                int B, int D, const Twiddles& tw, hipStream_t s, int full = 0);
+                                int B, int D, const Twiddles& tw, hipStream_t s, int full = 0, int hsb = 0);
 hipError_t launch_spectrum1d_single(int log2L, const float* h, float2* Hs, int D, const Twiddles& tw,
                                     hipStream_t s, int full = 0);
 hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
@@ -24,7 +26,7 @@ size_t fourstep_row_bytes(int log2L);
 // mats: the matrix-core table (bf16 L = 2^15, 2^16 run their column passes on the matrix cores), or NULL.
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, const void* mats, hipStream_t s, int full = 0);
+                                  const Twiddles& tw, const void* mats, hipStream_t s, int full = 0, int hsb = 0);
 hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
                                       const Twiddles& tw, hipStream_t s, int full = 0);
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
@@ -40,7 +42,7 @@ size_t conv3d_spectrum_bytes_per_channel(int circ);
 size_t conv3d_taps_per_channel(int circ);             // (2n-1)^3 or n^3
 hipError_t launch_conv3d(int bf16, int order, int B, int D, const void* v, const void* const* x,
                          const void* const* spectra, void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s,
-                         int circ);
+                         int circ, int hsb = 0);
 hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
                              hipStream_t s, int circ);
 hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s, int circ);
@@ -68,5 +70,19 @@ struct FilterArgs {
 };
 hipError_t launch_filter1d(const FilterArgs& a, int L, float* h, hipStream_t s);
 hipError_t launch_filter3d(const FilterArgs& a, float* h, hipStream_t s, int circ);
+
+// ---- input-dependent filters: FiLM-modulated SIREN with a Gaussian window, one filter per (b, d)
+constexpr int kFilmHidden = 64;     // SIREN units per layer
+constexpr int kFilmMaxE = 4096;     // register width
+constexpr int kFilmMaxR = 1024;     // register tokens per sample
+struct FilmArgs {
+  int E, H, D, NC;                  // register width, hidden units, channels, coordinates (1 or 3)
+  const float *q, *A1, *a1, *omega0, *A2, *a2, *A3, *a3, *G1, *g1, *P1, *p1, *G2, *g2, *P2, *p2, *sigma;
+};
+// mod: [B, 4, H] FiLM vectors (gamma_1, beta_1, gamma_2, beta_2) from the registers reg [B, R, E]
+hipError_t launch_film_prep(const FilmArgs& a, const float* reg, int B, int R, float* mod, hipStream_t s);
+// taps h[B, D, points] (1-D t = 0..L-1; 3-D offsets as launch_filter3d)
+hipError_t launch_film_filter1d(const FilmArgs& a, const float* mod, int B, int L, float* h, hipStream_t s);
+hipError_t launch_film_filter3d(const FilmArgs& a, const float* mod, int B, float* h, hipStream_t s, int circ);
 
 }  // namespace hyena

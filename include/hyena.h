@@ -60,6 +60,12 @@ typedef enum {
   HYENA_CIRCULAR = 2  /* periodic boundary, no padding: 1-D rows or the 3-D grid                    */
 } hyena_mode;
 
+/* Flag OR'ed into a mode: the spectra hold one filter per (b, d) in [B, D] order -- the input-dependent
+ * filters of hyena_film_filter_gen -- instead of one per channel.  Accepted by every entry point that
+ * takes a mode; hyena_fftconv / hyena_operator then read filter b*D + d for row (b, d) (always on the
+ * fp32 transform engine), and hyena_spectrum_bytes / hyena_spectrum_export take D = B * channels. */
+#define HYENA_PER_SAMPLE 8
+
 /* Grid shape: 1-D {1, {L, 0, 0}}; 3-D {3, {nx, ny, nz}}.
  * Supported: HYENA_CAUSAL L = 2^k, 2^10 <= L <= 2^20; HYENA_CIRCULAR 1-D L = 2^k, 2^11 <= L <= 2^21,
  * or nx = ny = nz = 64; HYENA_LINEAR nx = ny = nz = 64. */
@@ -78,9 +84,9 @@ typedef struct {
 
 /* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array):
  * causal 8L bytes per channel (for L = 8192 followed by a bf16 copy laid out for the matrix-core
- * kernel, 36 KB per channel; for L > 16384, 12L: a bf16 copy for the bf16 plans follows); periodic
- * 1-D 4L bytes per channel (6L for L > 32768); 3-D 128*128*65*8 bytes per channel (zero-padded) or
- * 64*64*33*8 (periodic). */
+ * kernel, 36 KB per channel, except with HYENA_PER_SAMPLE; for L > 16384, 12L: a bf16 copy for the
+ * bf16 plans follows); periodic 1-D 4L bytes per channel (6L for L > 32768); 3-D 128*128*65*8 bytes
+ * per channel (zero-padded) or 64*64*33*8 (periodic).  With HYENA_PER_SAMPLE, D counts filters (B*D). */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_filter_gen needs: room for the taps (used when h_time is NULL) plus, for
@@ -95,10 +101,39 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
  * h_time[D, 2n-1, 2n-1, 2n-1], index = offset + n-1; 3-D periodic: h_time[D, n, n, n], index =
  * offset + n/2) when h_time is not NULL, and the filter spectrum into `spectrum`
  * (hyena_spectrum_bytes bytes).  ws/ws_bytes: scratch of hyena_filter_workspace_bytes bytes (may be
- * NULL/0 when h_time is given and L <= 16384; HYENA_EWORKSPACE when too small).  The spectrum depends
+ * NULL/0 when h_time is given and the length runs in one pass, L <= 16384, except causal L = 8192,
+ * whose matrix-core copy is staged there; HYENA_EWORKSPACE when too small).  The spectrum depends
  * only on (params, dims), so callers cache it per length. */
 int hyena_filter_gen(const hyena_filter_params *p, hyena_dims dims, int mode, float *h_time, void *spectrum,
                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Input-dependent filter parameters of one order (HyenaND summary, method: registers, FiLM conditioning,
+ * kernel synthesis K(x) = w(c) f(c; z(x)) and the SIREN parameterisation with multi-frequency omega_0).
+ * Device pointers, fp32, row-major; n = dims.ndim coordinates (c = t/L in 1-D, r/n per axis in 3-D):
+ *   z = sum_r a_r reg[b, r],  a = softmax_r(q . reg[b, r])               q [E]
+ *   h1 = sin(gamma1 * omega0 * (A1 c + a1) + beta1)                     A1 [H, n], a1 [H], omega0 [H]
+ *   h2 = sin(gamma2 * (A2 h1 + a2) + beta2)                             A2 [H, H], a2 [H]
+ *   gamma_l = G_l z + g_l,  beta_l = P_l z + p_l                        G_l, P_l [H, E], g_l, p_l [H]
+ *   K[b, d, c] = (A3 h2 + a3)_d * exp(-|c|^2 / (2 sigma_d^2))          A3 [D, H], a3 [D], sigma [D] > 0
+ * Supported: H = 64, E <= 4096. */
+typedef struct {
+  int32_t E, H, D;
+  const float *q, *A1, *a1, *omega0, *A2, *a2, *A3, *a3;
+  const float *G1, *g1, *P1, *p1, *G2, *g2, *P2, *p2, *sigma;
+} hyena_film_params;
+
+/* Workspace bytes hyena_film_filter_gen needs: the FiLM vectors (4*H floats per sample), the taps of B*D
+ * filters (used when h_time is NULL) and, for multi-pass lengths and 3-D, a transform chunk. */
+int hyena_film_filter_workspace_bytes(int64_t B, hyena_dims dims, int mode, int64_t D, size_t *bytes);
+
+/* Input-dependent filters of one order for B samples: registers [B, R, E] (device, fp32; the R register
+ * tokens' activations, R <= 1024) -> taps h_time [B, D, points as hyena_filter_gen] when not NULL, and
+ * the spectra of the B*D filters into `spectrum` (hyena_spectrum_bytes(dims, mode | HYENA_PER_SAMPLE,
+ * B*D) bytes), for hyena_fftconv / hyena_operator with mode | HYENA_PER_SAMPLE.  ws (required):
+ * hyena_film_filter_workspace_bytes bytes.  B <= 65535. */
+int hyena_film_filter_gen(const hyena_film_params *p, int64_t B, int32_t R, const float *registers,
+                          hyena_dims dims, int mode, float *h_time, void *spectrum, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
 
 /* One long convolution with optional gate: y = gate * (h conv u), or y = h conv u when gate == NULL.
  * u, gate, y: [B, D, points] of dtype.  spectrum: from hyena_filter_gen for the same dims and D.

@@ -141,3 +141,50 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(L, "_lib", None)
     with pytest.raises(ImportError):
         L.lib()
+
+
+def test_per_sample_sizes(lib):
+    # one filter per (b, d): the spectrum of B*D filters, without the matrix-core copy at L = 8192
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([8192]), L.CAUSAL | L.PER_SAMPLE, 4 * 768)
+    assert st == 0 and n == 4 * 768 * 8192 * 8
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.LINEAR | L.PER_SAMPLE, 2 * 128)
+    assert st == 0 and n == 2 * 128 * 128 * 128 * 65 * 8
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([65536]), L.CAUSAL | L.PER_SAMPLE, 6)
+    assert st == 0 and n == 6 * 65536 * (8 + 4)
+    # workspace: FiLM vectors (B x 4 x 64 floats, 256-byte rounded), taps of B*D filters, transform chunk
+    st, n = _size(lib.hyena_film_filter_workspace_bytes, 2, L.dims_of([1024]), L.CAUSAL, 16)
+    assert st == 0 and n == 2048 + 2 * 16 * 1024 * 4
+    st, n = _size(lib.hyena_film_filter_workspace_bytes, 2, L.dims_of([64, 64, 64]), L.LINEAR, 3)
+    assert st == 0 and n == 2048 + 6 * 127 ** 3 * 4 + 256 + 6 * 128 * 128 * 65 * 8
+    st, n = _size(lib.hyena_film_filter_workspace_bytes, 0, L.dims_of([1024]), L.CAUSAL, 16)
+    assert st == L.EINVAL
+    # the flag leaves the conv workspace unchanged
+    for mode in (L.CAUSAL, L.CAUSAL | L.PER_SAMPLE):
+        st, n = _size(lib.hyena_workspace_bytes, 2, 1, 3, L.dims_of([1 << 20]), L.F32, mode)
+        assert st == 0 and n == 3 * (1 << 20) * 8
+
+
+def test_film_filter_gen_rejects_before_launch(lib):
+    ptrs = [0x1000 + 64 * i for i in range(17)]
+    d = L.dims_of([1024])
+    ws = 1 << 40
+    p = L.FilmParams(16, 64, 8, *ptrs)
+    # null registers, workspace or parameter
+    assert lib.hyena_film_filter_gen(ctypes.byref(p), 2, 4, None, d, L.CAUSAL, None, 0x2000, ws, 1 << 30, None) \
+        == L.EINVAL
+    assert lib.hyena_film_filter_gen(ctypes.byref(p), 2, 4, 0x3000, d, L.CAUSAL, None, 0x2000, None, 0, None) \
+        == L.EINVAL
+    q = L.FilmParams(16, 64, 8, *(ptrs[:5] + [None] + ptrs[6:]))
+    assert lib.hyena_film_filter_gen(ctypes.byref(q), 2, 4, 0x3000, d, L.CAUSAL, None, 0x2000, ws, 1 << 30, None) \
+        == L.EINVAL
+    # unsupported widths and counts
+    for bad in (L.FilmParams(16, 32, 8, *ptrs), L.FilmParams(5000, 64, 8, *ptrs)):
+        assert lib.hyena_film_filter_gen(ctypes.byref(bad), 2, 4, 0x3000, d, L.CAUSAL, None, 0x2000, ws, 1 << 30,
+                                         None) == L.EUNSUPPORTED
+    assert lib.hyena_film_filter_gen(ctypes.byref(p), 2, 2000, 0x3000, d, L.CAUSAL, None, 0x2000, ws, 1 << 30,
+                                     None) == L.EUNSUPPORTED
+    assert lib.hyena_film_filter_gen(ctypes.byref(p), 2, 4, 0x3000, L.dims_of([1000]), L.CAUSAL, None, 0x2000, ws,
+                                     1 << 30, None) == L.EUNSUPPORTED
+    # workspace too small for the taps of B*D filters
+    assert lib.hyena_film_filter_gen(ctypes.byref(p), 2, 4, 0x3000, d, L.CAUSAL, None, 0x2000, ws, 4096, None) \
+        == L.EWORKSPACE
