@@ -209,19 +209,25 @@ FILM_KEYS = ("q", "A1", "a1", "omega0", "A2", "a2", "A3", "a3", "G1", "g1", "P1"
 
 
 def film_filter_gen(params: dict, registers, point_shape: Sequence[int], h_time=None, spectrum=None,
-                    mode: Optional[int] = None):
+                    mode: Optional[int] = None, ws=None, taps_only: bool = False):
     """Input-dependent filters of one order for every sample.  params: dict of CUDA float32 tensors
     (FILM_KEYS; A3 [D, H], G1 [H, E], ...); registers: [B, R, E] CUDA float32.  Returns the spectra of
-    the B*D filters (opaque uint8 tensor, for mode | PER_SAMPLE); fills h_time [B, D, taps] when given."""
+    the B*D filters (opaque uint8 tensor, for mode | PER_SAMPLE); fills h_time [B, D, taps] when given.
+    taps_only (with h_time): no spectrum is built and None is returned."""
     torch = _torch()
     B, R, E = registers.shape
     H = params["A2"].shape[0]
     D = params["A3"].shape[0]
     dev = registers.device
     mode = mode_for(len(point_shape)) if mode is None else mode
-    if spectrum is None:
+    if taps_only:
+        if h_time is None:
+            raise ValueError("taps_only needs h_time")
+        spectrum = None
+    elif spectrum is None:
         spectrum = torch.empty(spectrum_bytes(point_shape, B * D, mode | PER_SAMPLE), dtype=torch.uint8, device=dev)
-    ws = _workspace(film_filter_workspace_bytes(B, point_shape, D, mode), dev)
+    if ws is None:
+        ws = _workspace(film_filter_workspace_bytes(B, point_shape, D, mode), dev)
     p = FilmParams(E, H, D, *[_ptr(params[k]) for k in FILM_KEYS])
     _check(lib().hyena_film_filter_gen(ctypes.byref(p), B, R, _ptr(registers), dims_of(point_shape), mode,
                                        _ptr(h_time), _ptr(spectrum), _ptr(ws), ws.numel(), _stream(registers)),

@@ -382,7 +382,8 @@ int hyena_film_filter_workspace_bytes(int64_t B, hyena_dims dims, int mode, int6
 
 int hyena_film_filter_gen(const hyena_film_params* p, int64_t B, int32_t R, const float* registers, hyena_dims dims,
                           int mode, float* h_time, void* spectrum, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!p || !registers || !spectrum || !ws || B <= 0 || R <= 0 || p->D <= 0 || p->E <= 0) return HYENA_EINVAL;
+  if (!p || !registers || (!spectrum && !h_time) || !ws || B <= 0 || R <= 0 || p->D <= 0 || p->E <= 0)
+    return HYENA_EINVAL;
   const float* need[] = {p->q, p->A1, p->a1, p->omega0, p->A2, p->a2, p->A3, p->a3, p->G1, p->g1,
                          p->P1, p->p1, p->G2, p->g2, p->P2, p->p2, p->sigma};
   for (const float* q : need)
@@ -411,7 +412,7 @@ int hyena_film_filter_gen(const hyena_film_params* p, int64_t B, int32_t R, cons
     wsp += hbytes;
     wsn -= hbytes;
   }
-  if (!spectra_ws_ok(kind, pts, nch, wsp, wsn, false)) return HYENA_EWORKSPACE;
+  if (spectrum && !spectra_ws_ok(kind, pts, nch, wsp, wsn, false)) return HYENA_EWORKSPACE;
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
   FilmArgs a{p->E, p->H, p->D, dims.ndim, p->q, p->A1, p->a1, p->omega0, p->A2, p->a2, p->A3, p->a3,
@@ -419,7 +420,7 @@ int hyena_film_filter_gen(const hyena_film_params* p, int64_t B, int32_t R, cons
   if ((st = hip_status(launch_film_prep(a, registers, (int)B, R, mod, stream)))) return st;
   if (is3d(kind)) st = hip_status(launch_film_filter3d(a, mod, (int)B, h, stream, circ3(kind)));
   else st = hip_status(launch_film_filter1d(a, mod, (int)B, (int)pts, h, stream));
-  if (st) return st;
+  if (st || !spectrum) return st;
   return spectra_from_taps(kind, pts, h, nch, spectrum, wsp, wsn, false, tw, stream);
 }
 

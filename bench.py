@@ -5,7 +5,10 @@ A step is one call of the order-N operator (every order: load, zero-padded forwa
 product with the cached filter spectrum, inverse transform, cut to the output window, gate, store)
 over one batch of seeded synthetic input already resident in HBM.  The filter spectra depend only on
 the filter parameters and the grid, so they are built once (hyena_filter_gen) before the timed region;
-that build is reported separately as ``filter_gen_ms``.
+that build is reported separately as ``filter_gen_ms``.  Input-dependent (per-sample) filters change with
+every batch, so for those workloads the step also builds them: per order, the register summary, the
+FiLM-modulated SIREN taps of every (b, d) and their spectra, then the operator reading one filter per
+(b, d); the filter network is then the dominant kernel and the roofline object reports it.
 
 Prints ONE JSON line.  Default workload: order 2, B=4, D=768, L=8192, bf16 storage (workload 1), whose
 convolution runs on the matrix cores;
@@ -32,18 +35,22 @@ METRIC = "Hyena op tokens·channels/s + HBM GB/s (% peak), order 2, L=8K..1M, 1 
 
 def algorithmic_bytes_per_order(w) -> int:
     """One HBM round trip per order: read u, read x_i, write u_i (s bytes each per token-channel),
-    plus the filter read once in its smallest exact form (fp32 taps), shared by the B rows of a channel."""
-    return 3 * w.elem_bytes * w.tokens_channels + 4 * w.D * w.support
+    plus the filter read once in its smallest exact form (fp32 taps), shared by the B rows of a channel
+    (one filter per row for input-dependent filters)."""
+    filters = w.B * w.D if w.filter == "film" else w.D
+    return 3 * w.elem_bytes * w.tokens_channels + 4 * filters * w.support
 
 
 def floor_bytes_per_step(w) -> int:
     """All orders fused on chip: read v and the N gates, write y, plus the N filters (fp32 taps)."""
-    return (w.order + 2) * w.elem_bytes * w.tokens_channels + 4 * w.order * w.D * w.support
+    filters = w.B * w.D if w.filter == "film" else w.D
+    return (w.order + 2) * w.elem_bytes * w.tokens_channels + 4 * w.order * filters * w.support
 
 
 def uses_matrix_cores(w) -> bool:
     """Causal, bf16 storage, L = 8192, rows in pairs of one channel: the library's matrix-core kernel."""
-    return w.mode == "causal" and w.dtype == "bf16" and w.dims[0] == 8192 and w.B % 2 == 0
+    return (w.mode == "causal" and w.dtype == "bf16" and w.dims[0] == 8192 and w.B % 2 == 0
+            and w.filter != "film")
 
 
 def single_launch_per_order(w) -> bool:
@@ -85,6 +92,65 @@ def load_traffic(key: str):
         return ent.get("bytes_per_launch")
     except Exception:
         return None
+
+
+def film_network_flops(w) -> float:
+    """Algorithmic flops of one input-dependent filter launch (one order, every sample): per sample and
+    tap, layer 1 (n coordinates -> H), layer 2 (H -> H) and the read-out (H -> D), two flops per
+    multiply-add; the sines, the FiLM affine maps and the window are not counted."""
+    return 2.0 * w.B * w.support * w.hidden * (w.ndim + w.hidden + w.D)
+
+
+def cpu_baseline_film(w, v, xs, fparams, reg, budget_s: float):
+    """The oracle on whole (b, d) volumes/rows of the input-dependent workload: per row, both orders'
+    filters for that (b, d) (register summary, FiLM-SIREN on every tap, window) and then the operator,
+    all inside the timed part, as the GPU step builds its filters per call."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):                  # one core: the matrix products would use every BLAS thread
+        return _cpu_baseline_film(w, v, xs, fparams, reg, budget_s)
+
+
+def _cpu_baseline_film(w, v, xs, fparams, reg, budget_s: float):
+    from oracle import hyena_oracle as orc
+    rows = hi.sample_rows(w, 4096, seed=99)
+    circ = w.mode == "circular"
+    if w.ndim == 1:
+        offs = np.arange(w.dims[0])[:, None]
+        c = offs / w.dims[0]
+        shape = (1, w.dims[0])
+    else:
+        n = w.dims[0]
+        offs = orc.filter_offsets_3d_circular(n) if circ else orc.filter_offsets_3d(n)
+        c = offs.astype(np.float64) / n
+        m = n if circ else 2 * n - 1
+        shape = (1, m, m, m)
+    n_done, t_used = 0, 0.0
+    for b, d in rows:
+        t0 = time.perf_counter()
+        hs = []
+        for p in fparams:
+            z = orc.register_summary(reg[b:b + 1], p["q"])[0]
+            pd = dict(p, A3=p["A3"][d:d + 1], a3=p["a3"][d:d + 1], sigma=p["sigma"][d:d + 1])
+            k = (orc.film_siren(c, z, pd).T * orc.gaussian_window(c, pd["sigma"]))[0]
+            if w.ndim == 3 and circ:
+                hc = np.zeros((n, n, n))
+                ri = offs % n
+                hc[ri[:, 0], ri[:, 1], ri[:, 2]] = k
+                k = hc
+            hs.append(k.reshape(shape))
+        if w.ndim == 1:
+            orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], hs, circular=circ)
+        else:
+            orc.hyena_operator_3d(v[b, d][None], [x[b, d][None] for x in xs], hs, circular=circ)
+        t_used += time.perf_counter() - t0
+        n_done += 1
+        print(f"cpu baseline: row {n_done} done ({t_used:.1f} s)", file=sys.stderr, flush=True)
+        if t_used >= budget_s:
+            break
+    return {"value": n_done * w.points / t_used, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_done} of {w.B * w.D} (b,d) rows of the same workload, order {w.order}, each with its "
+                      f"own input-dependent filters built inside the timed part (float64 numpy, FFT "
+                      f"convolution, BLAS limited to one thread); {t_used:.1f} s"}
 
 
 def cpu_baseline(w, v, xs, params, budget_s: float):
@@ -169,9 +235,11 @@ def main():
     from attention_free_long_implicit_amd import _lib
 
     w = hi.WORKLOADS[args.workload]
+    film = w.filter == "film"
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     v, xs = hi.draw_activations(w)
-    params = hi.draw_filter_params(w)
+    params = hi.draw_film_params(w) if film else hi.draw_filter_params(w)
+    reg = hi.draw_registers(w) if film else None
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     vd = torch.from_numpy(v).to(dev).to(dt)
@@ -181,21 +249,38 @@ def main():
     mode = {"causal": _lib.CAUSAL, "linear": _lib.LINEAR, "circular": _lib.CIRCULAR}[w.mode]
     ws_n = _lib.workspace_bytes(w.order, w.B, w.D, w.dims, _lib.BF16 if w.dtype == "bf16" else _lib.F32, mode)
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    stream = torch.cuda.current_stream(dev)
 
-    # filter spectra (cached per grid): timed separately
-    spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
-    torch.cuda.synchronize()
-    fg = []
-    for _ in range(3):
-        t0 = time.perf_counter()
+    if film:
+        # per-sample filters: rebuilt inside every step into preallocated spectra and workspace
+        regd = torch.from_numpy(reg).to(dev)
+        op_mode = mode | _lib.PER_SAMPLE
+        spectra = [torch.empty(_lib.spectrum_bytes(w.dims, w.B * w.D, op_mode), dtype=torch.uint8, device=dev)
+                   for _ in pd]
+        fws = torch.empty(_lib.film_filter_workspace_bytes(w.B, w.dims, w.D, mode), dtype=torch.uint8, device=dev)
+
+        def step():
+            for p, sp in zip(pd, spectra):
+                hy.film_filter_gen(p, regd, w.dims, spectrum=sp, mode=mode, ws=fws)
+            hy.operator(vd, xd, spectra, y=y, ws=ws, mode=op_mode)
+        filter_gen_ms = None
+    else:
+        # filter spectra (cached per grid): timed separately
         spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
         torch.cuda.synchronize()
-        fg.append(time.perf_counter() - t0)
-    filter_gen_ms = 1e3 * min(fg)
+        fg = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
+            torch.cuda.synchronize()
+            fg.append(time.perf_counter() - t0)
+        filter_gen_ms = 1e3 * min(fg)
 
-    stream = torch.cuda.current_stream(dev)
+        def step():
+            hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
+
     for _ in range(args.warmup):
-        hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
+        step()
     torch.cuda.synchronize()
 
     # two events on the launch stream bracket the timed region (an event after every step would add
@@ -205,7 +290,7 @@ def main():
     t0 = time.perf_counter()
     ev0.record(stream)
     for k in range(args.steps):
-        hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
+        step()
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -224,7 +309,7 @@ def main():
             scratch.fill_(float(k))
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
+            step()
             e1.record(stream)
             marks.append((e0, e1))
         torch.cuda.synchronize()
@@ -258,15 +343,53 @@ def main():
         "event_ms_per_step": float(np.mean(step_ms)),
         "filter_gen_ms": filter_gen_ms,
     }
+    if film:
+        out["data"] = ("synthetic (seeded activations and register activations, SIREN/FiLM parameters drawn as in "
+                       "hyena_inputs.draw_film_params)")
+        out["config"].pop("alpha_range")
+        out["config"].update({"filters": "input-dependent: one FiLM-SIREN filter per (b, d), rebuilt every step",
+                              "registers": w.registers, "hidden": w.hidden,
+                              "sigma_range": [w.sigma_lo, w.sigma_hi],
+                              "inputs": f"numpy default_rng([{w.index}, stream]): stream 0 activations, stream 1 "
+                                        f"filter parameters, stream 2 register activations"})
     if cold is not None:
         out["cold_cache"] = cold
-    # filter network (a GEMM pair per position) for all orders; the time includes the spectrum build
-    net_flop = 2.0 * w.order * w.support * w.hidden * (w.features + w.D)
-    out["filter_gen"] = {"ms": filter_gen_ms, "network_gflop": net_flop / 1e9,
-                         "achieved_tflops": net_flop / (filter_gen_ms / 1e3) / 1e12, "peak_tflops": 157.3,
-                         "note": "all orders; network flops over the whole filter build (spectra included)"}
     key = kernel_key(w)
-    if uses_matrix_cores(w) and w.order <= 8:
+    if film:
+        # dominant kernel: the filter network, timed alone (taps only: register summary + taps launch)
+        taps = torch.empty((w.B, w.D, w.support), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            hy.film_filter_gen(pd[0], regd, w.dims, h_time=taps, mode=mode, ws=fws, taps_only=True)
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            hy.film_filter_gen(pd[0], regd, w.dims, h_time=taps, mode=mode, ws=fws, taps_only=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        del taps
+        launch_ms = e0.elapsed_time(e1) / reps
+        flops = film_network_flops(w)
+        tf = flops / (launch_ms / 1e3) / 1e12
+        out["roofline"] = {"bound": "alu", "kernel": f"k_film_tiles ({'3-D' if w.ndim == 3 else '1-D'} taps, "
+                                                     f"input-dependent filter network)",
+                           "achieved": tf, "peak": 157.3, "unit": "TFLOP/s", "frac": tf / 157.3, "traffic": None,
+                           "launch_ms": launch_ms, "alg_flops_per_launch": flops,
+                           "frac_unpacked_fma": tf / 78.6,
+                           "note": "peak: fp32 vector 157.3 TFLOP/s (packed); the library is built without packed "
+                                   "fp32 instructions, whose FMA peak is 78.6 TFLOP/s (frac_unpacked_fma); the "
+                                   "launch time includes the register-summary kernel"}
+        out["filter_share_of_step"] = w.order * launch_ms / float(np.mean(step_ms))
+    else:
+        # filter network (a GEMM pair per position) for all orders; the time includes the spectrum build
+        net_flop = 2.0 * w.order * w.support * w.hidden * (w.features + w.D)
+        out["filter_gen"] = {"ms": filter_gen_ms, "network_gflop": net_flop / 1e9,
+                             "achieved_tflops": net_flop / (filter_gen_ms / 1e3) / 1e12, "peak_tflops": 157.3,
+                             "note": "all orders; network flops over the whole filter build (spectra included)"}
+    if film:
+        pass                                # the roofline object above
+    elif uses_matrix_cores(w) and w.order <= 8:
         # the whole step is one launch of the matrix-core kernel: all orders, u_i kept on chip
         launch_ms = float(np.mean(step_ms))
         achieved = alg_step / (launch_ms / 1e3) / 1e9
@@ -293,7 +416,8 @@ def main():
     if not args.no_copy:
         out["copy_gbps"] = copy_bandwidth(torch, dev)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, v, xs, params, args.cpu_budget)
+        out["cpu_baseline"] = (cpu_baseline_film(w, v, xs, params, reg, args.cpu_budget) if film else
+                               cpu_baseline(w, v, xs, params, args.cpu_budget))
     print(json.dumps(out), flush=True)
 
 

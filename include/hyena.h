@@ -129,8 +129,9 @@ int hyena_film_filter_workspace_bytes(int64_t B, hyena_dims dims, int mode, int6
 /* Input-dependent filters of one order for B samples: registers [B, R, E] (device, fp32; the R register
  * tokens' activations, R <= 1024) -> taps h_time [B, D, points as hyena_filter_gen] when not NULL, and
  * the spectra of the B*D filters into `spectrum` (hyena_spectrum_bytes(dims, mode | HYENA_PER_SAMPLE,
- * B*D) bytes), for hyena_fftconv / hyena_operator with mode | HYENA_PER_SAMPLE.  ws (required):
- * hyena_film_filter_workspace_bytes bytes.  B <= 65535. */
+ * B*D) bytes), for hyena_fftconv / hyena_operator with mode | HYENA_PER_SAMPLE.  spectrum may be NULL
+ * when h_time is given (taps only).  ws (required): hyena_film_filter_workspace_bytes bytes.
+ * B <= 65535. */
 int hyena_film_filter_gen(const hyena_film_params *p, int64_t B, int32_t R, const float *registers,
                           hyena_dims dims, int mode, float *h_time, void *spectrum, void *ws, size_t ws_bytes,
                           hipStream_t stream);
