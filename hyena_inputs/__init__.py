@@ -16,13 +16,17 @@ Workloads (the five shapes the Hyena operator is exercised on):
   6  order 2, B=1, D=128, grid 64^3,   fp32, periodic 3-D (no padding)
   7  order 2, B=2, D=128, grid 64^3,   fp32, non-causal 3-D with input-dependent filters: 8 register
      tokens per sample, a FiLM-modulated SIREN (64 units) and a Gaussian window, one filter per (b, d)
+  8  order 2, B=4, D=768, L=8192,      bf16 storage, from token-major inputs x [B, L, 768] through the
+     input projection (W_proj [3 * 768, 768]) to v, x_1, x_2, then the operator
 
 Random streams: ``numpy.random.default_rng([seed, stream])``.  Stream 0 draws
 the activations (v, x_1 .. x_N in that order, or tokens then the embedding for
 the DNA workload); stream 1 draws the filter parameters (per order: W1, W2,
 alpha).  Biases are zero.  Xavier-uniform bounds use sqrt(6/(fan_in+fan_out)).
 For input-dependent filters stream 1 draws, per order, the SIREN and FiLM parameters (see
-``draw_film_params``) and stream 2 the register activations [B, R, D] ~ N(0,1).
+``draw_film_params``) and stream 2 the register activations [B, R, D] ~ N(0,1).  For workloads that
+start from the input projection, stream 3 draws the token-major inputs x [B, L, d_model] ~ N(0,1), then
+W_proj [(N+1) D, d_model] (Xavier uniform); its bias is zero.
 """
 from __future__ import annotations
 
@@ -34,7 +38,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "draw_activations", "draw_filter_params",
     "bf16_bits_rne", "bf16_bits_to_f32", "seeded_rng", "draw_film_params", "draw_registers",
-    "FILM_OMEGA0_BLOCKS",
+    "FILM_OMEGA0_BLOCKS", "draw_projection",
 ]
 
 
@@ -57,6 +61,7 @@ class Workload:
     registers: int = 0            # register tokens per sample (input-dependent filters)
     sigma_lo: float = 0.2         # Gaussian window widths (input-dependent filters)
     sigma_hi: float = 0.8
+    d_model: int = 0              # width of the token-major input of the projection (0: none)
 
     @property
     def ndim(self) -> int:
@@ -107,6 +112,8 @@ WORKLOADS: List[Workload] = [
              0.3, 3.0, 96, 64),
     Workload(7, "hyenand3d_film_order2_B2_D128_64cubed_f32", 2, 2, 128, (64, 64, 64), "f32", "linear",
              0.0, 0.0, 3, 64, filter="film", registers=8),
+    Workload(8, "proj_order2_B4_D768_L8192_bf16", 2, 4, 768, (8192,), "bf16", "causal", 0.3, 3.0, 64, 64,
+             d_model=768),
 ]
 
 
@@ -232,6 +239,20 @@ def draw_registers(w: Workload, seed: Optional[int] = None) -> np.ndarray:
     """Register activations [B, R, D] ~ N(0,1) as float32 (random stream 2)."""
     seed = w.index if seed is None else seed
     return seeded_rng(seed, 2).standard_normal((w.B, w.registers, w.D), dtype=np.float32)
+
+
+def draw_projection(w: Workload, seed: Optional[int] = None):
+    """(x [B, L, d_model], W_proj [(N+1) D, d_model], bias [(N+1) D]) as float32 (stream 3); x and W are
+    rounded to bf16 for bf16 workloads, the bias is zero."""
+    seed = w.index if seed is None else seed
+    rng = seeded_rng(seed, 3)
+    M, K = (w.order + 1) * w.D, w.d_model
+    x = rng.standard_normal((w.B, w.points, K), dtype=np.float32)
+    W = ((rng.random((M, K), dtype=np.float32) * 2 - 1) * np.float32(np.sqrt(6.0 / (M + K)))).astype(np.float32)
+    if w.dtype == "bf16":
+        x = bf16_bits_to_f32(bf16_bits_rne(x))
+        W = bf16_bits_to_f32(bf16_bits_rne(W))
+    return x, W, np.zeros(M, np.float32)
 
 
 def sample_rows(w: Workload, count: int, seed: int = 1234) -> np.ndarray:

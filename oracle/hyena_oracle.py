@@ -29,6 +29,8 @@ What is computed (y = x_N * (h_N conv (... x_1 * (h_1 conv v)))):
   * circular (periodic) convolution, no padding, 1-D and 3-D              [HyenaND, boundary handling:
                                                                            circular convolutions for
                                                                            periodic physical systems]
+  * the input projection v, x_1..x_N = split(W_proj x), v first           [Hyena note, step 1 equation;
+                                                                           listing x.chunk]
   * input-dependent (per-sample) filters: z(x) = softmax-weighted mean of
     the register activations; K = w(c) * f(c; z) with a FiLM-modulated
     SIREN f and a Gaussian window w                                        [HyenaND, method: registers,
@@ -60,7 +62,8 @@ and the circular 3-D filter against the linear one at shared offsets; input-depe
 plain mean and the two-register logistic closed form of the softmax summary, permutation invariance,
 closed-form SIREN outputs with and without FiLM terms, the Gaussian window against the normal density
 and its separability, kernels that follow the registers sample by sample, axis order of the 3-D taps,
-and per-(b, d) filters in the operator against row-by-row direct sums.
+and per-(b, d) filters in the operator against row-by-row direct sums; the projection: a pure-Python
+triple loop on tiny shapes and block-identity weights that return the input transposed and scaled.
 """
 from __future__ import annotations
 
@@ -75,7 +78,7 @@ __all__ = [
     "linear_conv3d_direct", "linear_conv3d_fft", "hyena_operator_rows", "hyena_operator_3d",
     "rel_l2_per_row", "filter_offsets_3d_circular", "implicit_filter_3d_circular", "circular_conv_direct",
     "circular_conv_fft", "circular_conv3d_direct", "circular_conv3d_fft", "register_summary", "film_siren",
-    "gaussian_window", "input_dependent_filter_1d", "input_dependent_filter_3d",
+    "gaussian_window", "input_dependent_filter_1d", "input_dependent_filter_3d", "input_projection",
 ]
 
 
@@ -310,6 +313,23 @@ def circular_conv3d_fft(u: np.ndarray, h: np.ndarray) -> np.ndarray:
     n = u.shape[-1]
     axes = (-3, -2, -1)
     return np.fft.irfftn(np.fft.rfftn(u, axes=axes) * np.fft.rfftn(h, axes=axes), s=(n, n, n), axes=axes)
+
+
+# --------------------------------------------------------------------------------------------
+# input projection  [Hyena note, step 1: v, x_1, ..., x_N = split(W_proj x); listing: x.chunk(N + 1)]
+# --------------------------------------------------------------------------------------------
+
+def input_projection(x: np.ndarray, W: np.ndarray, bias: Optional[np.ndarray], order: int) -> List[np.ndarray]:
+    """[v, x_1, ..., x_N] from token-major inputs x [B, L, Dm]: u = x W^T (+ bias), u [B, L, (N+1) D],
+    split along the channel axis into N + 1 chunks of D in that order (v first), each returned
+    channel-major [B, D, L] float64.  W [(N+1) D, Dm] (a learned linear map, weight rows = outputs)."""
+    x = np.asarray(x, np.float64)
+    W = np.asarray(W, np.float64)
+    u = x @ W.T
+    if bias is not None:
+        u = u + np.asarray(bias, np.float64)
+    D = W.shape[0] // (order + 1)
+    return [np.ascontiguousarray(np.swapaxes(u[..., j * D:(j + 1) * D], -1, -2)) for j in range(order + 1)]
 
 
 # --------------------------------------------------------------------------------------------

@@ -39,9 +39,10 @@ def test_bf16_matches_torch_conversion():
 
 
 def test_workloads_table():
-    assert [w.order for w in hi.WORKLOADS] == [2, 2, 3, 2, 2, 2, 2, 2]
-    assert [w.mode for w in hi.WORKLOADS] == ["causal"] * 4 + ["linear", "circular", "circular", "linear"]
-    assert [w.filter for w in hi.WORKLOADS] == ["exp"] * 7 + ["film"]
+    assert [w.order for w in hi.WORKLOADS] == [2, 2, 3, 2, 2, 2, 2, 2, 2]
+    assert [w.mode for w in hi.WORKLOADS] == ["causal"] * 4 + ["linear", "circular", "circular", "linear", "causal"]
+    assert [w.filter for w in hi.WORKLOADS] == ["exp"] * 7 + ["film", "exp"]
+    assert [w.d_model for w in hi.WORKLOADS] == [0] * 8 + [768]
     assert hi.WORKLOADS[1].tokens_channels == 4 * 768 * 8192
     assert hi.WORKLOADS[3].dims == (1 << 20,)
     assert hi.WORKLOADS[4].support == 127 ** 3
@@ -93,3 +94,14 @@ def test_film_draws_are_seeded_and_shaped():
     r = hi.draw_registers(w)
     assert r.shape == (2, 8, 128) and r.dtype == np.float32
     np.testing.assert_array_equal(r, hi.draw_registers(w))
+
+
+def test_projection_draws():
+    w = hi.WORKLOADS[8].with_(B=2, dims=(256,))
+    x, W, b = hi.draw_projection(w)
+    assert x.shape == (2, 256, 768) and W.shape == (3 * 768, 768) and b.shape == (3 * 768,)
+    np.testing.assert_array_equal(hi.bf16_bits_to_f32(hi.bf16_bits_rne(x)), x)
+    np.testing.assert_array_equal(hi.bf16_bits_to_f32(hi.bf16_bits_rne(W)), W)
+    x2, W2, _ = hi.draw_projection(w)
+    np.testing.assert_array_equal(x, x2)
+    assert np.max(np.abs(W)) <= np.sqrt(6.0 / (4 * 768)) and not np.any(b)

@@ -655,3 +655,32 @@ def test_per_sample_filters_in_the_operator_match_row_by_row_sums():
     for j in range(B * D):
         np.testing.assert_allclose(y3[j], x3[0][j] * orc.circular_conv3d_direct(v3[j], h3[0][j]), rtol=1e-12,
                                    atol=1e-12)
+
+
+# ---------------------------------------------------------------- input projection
+
+def test_projection_against_triple_loop():
+    rng = np.random.default_rng(50)
+    B, L, Dm, D, order = 2, 3, 4, 2, 2
+    x = rng.standard_normal((B, L, Dm))
+    W = rng.standard_normal(((order + 1) * D, Dm))
+    bias = rng.standard_normal((order + 1) * D)
+    outs = orc.input_projection(x, W, bias, order)
+    assert len(outs) == order + 1 and all(o.shape == (B, D, L) for o in outs)
+    for j in range(order + 1):
+        for b in range(B):
+            for d in range(D):
+                for t in range(L):
+                    want = bias[j * D + d] + sum(W[j * D + d, k] * x[b, t, k] for k in range(Dm))
+                    assert abs(outs[j][b, d, t] - want) < 1e-12
+
+
+def test_projection_block_identity_splits_in_order():
+    # W = [I; 2I; 3I]: v is x transposed, x_1 twice it, x_2 three times (v comes first)
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((2, 5, 3))
+    W = np.concatenate([np.eye(3), 2 * np.eye(3), 3 * np.eye(3)])
+    v, x1, x2 = orc.input_projection(x, W, None, 2)
+    np.testing.assert_array_equal(v, np.swapaxes(x, 1, 2))
+    np.testing.assert_array_equal(x1, 2 * np.swapaxes(x, 1, 2))
+    np.testing.assert_array_equal(x2, 3 * np.swapaxes(x, 1, 2))
