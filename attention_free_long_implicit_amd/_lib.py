@@ -59,6 +59,8 @@ _SIG = {
                                   _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p,
                                   _c.c_size_t, _c.c_void_p]),
     "hyena_spectrum_export": (_c.c_int, [Dims, _c.c_int, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
+    "hyena_projection": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p,
+                                    _c.c_void_p, _c.c_void_p, _c.POINTER(_c.c_void_p), _c.c_void_p]),
     "hyena_film_filter_workspace_bytes": (_c.c_int, [_c.c_int64, Dims, _c.c_int, _c.c_int64,
                                                      _c.POINTER(_c.c_size_t)]),
     "hyena_film_filter_gen": (_c.c_int, [_c.POINTER(FilmParams), _c.c_int64, _c.c_int32, _c.c_void_p, Dims,
@@ -233,6 +235,23 @@ def film_filter_gen(params: dict, registers, point_shape: Sequence[int], h_time=
                                        _ptr(h_time), _ptr(spectrum), _ptr(ws), ws.numel(), _stream(registers)),
            "hyena_film_filter_gen")
     return spectrum
+
+
+def projection(x, W, order: int, bias=None, outs: Optional[Sequence] = None):
+    """[v, x_1, ..., x_N] (channel-major [B, D, L] each) = split(x W^T + bias); x: [B, L, d_model] token-major,
+    W: [(order+1) D, d_model], both CUDA tensors of one dtype (float32 or bfloat16); bias: float32 or None."""
+    torch = _torch()
+    B, L, K = x.shape
+    M = W.shape[0]
+    if W.shape[1] != K or M % (order + 1) or W.dtype != x.dtype:
+        raise ValueError("W must be [(order+1)*D, d_model] of x's dtype")
+    D = M // (order + 1)
+    if outs is None:
+        outs = [torch.empty((B, D, L), dtype=x.dtype, device=x.device) for _ in range(order + 1)]
+    oa = (ctypes.c_void_p * (order + 1))(*[_ptr(o) for o in outs])
+    _check(lib().hyena_projection(order, B, L, K, D, _dtype_code(x), _ptr(x), _ptr(W), _ptr(bias), oa, _stream(x)),
+           "hyena_projection")
+    return list(outs)
 
 
 def fftconv(u, spectrum, gate=None, y=None, mode: Optional[int] = None):

@@ -524,6 +524,31 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
   return HYENA_OK;
 }
 
+int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D, int dtype, const void* x,
+                     const void* W, const float* bias, void* const* out, hipStream_t stream) {
+  if (order < 1 || B <= 0 || L <= 0 || d_model <= 0 || D <= 0 || !x || !W || !out ||
+      (dtype != HYENA_F32 && dtype != HYENA_BF16))
+    return HYENA_EINVAL;
+  const int nout = order + 1;
+  if (nout > kProjMaxOut) return HYENA_EUNSUPPORTED;
+  for (int j = 0; j < nout; ++j)
+    if (!out[j]) return HYENA_EINVAL;
+  const int es = (int)elem_bytes(dtype);
+  const int64_t M = nout * D;
+  if (B > INT32_MAX || L > INT32_MAX || M > INT32_MAX || !projection_supported(B, L, d_model, M, es))
+    return HYENA_EUNSUPPORTED;
+  const size_t ob = (size_t)B * D * L * es;
+  const size_t xb = (size_t)B * L * d_model * es, wb = (size_t)M * d_model * es;
+  for (int j = 0; j < nout; ++j) {
+    if (overlaps(out[j], ob, x, xb) || overlaps(out[j], ob, W, wb) || (bias && overlaps(out[j], ob, bias, M * 4)))
+      return HYENA_EALIAS;
+    for (int i = 0; i < j; ++i)
+      if (overlaps(out[j], ob, out[i], ob)) return HYENA_EALIAS;
+  }
+  return hip_status(launch_projection(dtype == HYENA_BF16, x, W, bias, out, nout, (int)B, (int)L, (int)d_model,
+                                      (int)D, stream));
+}
+
 int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spectrum, void* H, hipStream_t stream) {
   if (D <= 0 || !spectrum || !H) return HYENA_EINVAL;
   bool ps = false;

@@ -71,6 +71,12 @@ struct FilterArgs {
 hipError_t launch_filter1d(const FilterArgs& a, int L, float* h, hipStream_t s);
 hipError_t launch_filter3d(const FilterArgs& a, float* h, hipStream_t s, int circ);
 
+// ---- input projection: x [B, L, K] token-major, W [nout * D, K] -> nout channel-major outputs [B, D, L]
+constexpr int kProjMaxOut = 9;      // v and up to 8 gates
+bool projection_supported(int64_t B, int64_t L, int64_t K, int64_t M, int es);
+hipError_t launch_projection(int bf16, const void* x, const void* W, const float* bias, void* const* outs, int nout,
+                             int B, int L, int K, int D, hipStream_t s);
+
 // ---- input-dependent filters: FiLM-modulated SIREN with a Gaussian window, one filter per (b, d)
 constexpr int kFilmHidden = 64;     // SIREN units per layer
 constexpr int kFilmMaxE = 4096;     // register width

@@ -155,6 +155,18 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
                    const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,
                    hipStream_t stream);
 
+/* The input projection (Hyena study note, step 1: v, x_1, ..., x_N = split(W_proj x); the listing
+ * chunks the projected channels into N + 1 equal parts, v first):
+ *   out[j][b, d, t] = sum_k W[j*D + d, k] * x[b, t, k] + bias[j*D + d],   j = 0..order
+ * x: token-major [B, L, d_model]; W: [(order+1)*D, d_model] row-major (one row per output channel);
+ * both of dtype (bf16: matrix-core products, fp32 accumulation; fp32: fp32 matrix-core products).
+ * bias: fp32 [(order+1)*D] or NULL.  out: host array of order+1 device pointers, each [B, D, L] of dtype
+ * (channel-major, the layout hyena_operator takes: out[0] = v, out[j] = x_j), written with bf16 rounding
+ * to nearest even.  Supported: d_model a multiple of 32, order <= 8, (order+1)*D*d_model and
+ * L*d_model elements below 2^31 bytes.  Outputs must not overlap x, W, bias or each other. */
+int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D, int dtype, const void *x,
+                     const void *W, const float *bias, void *const *out, hipStream_t stream);
+
 /* Testing aid: the engine-ordered spectrum as natural-order DFT bins of the filter, complex64:
  * causal H[D, L+1] (bins of the 2L-point transform of the zero-padded taps), periodic H[D, L/2+1]
  * (bins of the L-point transform of the taps), 3-D H[D, 2nx, 2ny, nz+1] (zero-padded) or

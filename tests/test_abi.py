@@ -188,3 +188,20 @@ def test_film_filter_gen_rejects_before_launch(lib):
     # workspace too small for the taps of B*D filters
     assert lib.hyena_film_filter_gen(ctypes.byref(p), 2, 4, 0x3000, d, L.CAUSAL, None, 0x2000, ws, 4096, None) \
         == L.EWORKSPACE
+
+
+def test_projection_rejects_before_launch(lib):
+    outs = (ctypes.c_void_p * 3)(1 << 40, 1 << 41, 1 << 42)
+    x, W = 1 << 43, 1 << 44
+    assert lib.hyena_projection(0, 2, 256, 64, 32, L.BF16, x, W, None, outs, None) == L.EINVAL
+    assert lib.hyena_projection(2, 2, 256, 64, 32, 5, x, W, None, outs, None) == L.EINVAL
+    assert lib.hyena_projection(2, 2, 256, 100, 32, L.BF16, x, W, None, outs, None) == L.EUNSUPPORTED   # d_model % 32
+    assert lib.hyena_projection(9, 2, 256, 64, 32, L.BF16, x, W, None,
+                                (ctypes.c_void_p * 10)(*[(i + 1) << 36 for i in range(10)]), None) == L.EUNSUPPORTED
+    nul = (ctypes.c_void_p * 3)(1 << 40, None, 1 << 42)
+    assert lib.hyena_projection(2, 2, 256, 64, 32, L.BF16, x, W, None, nul, None) == L.EINVAL
+    # outputs overlapping each other or the input
+    ov = (ctypes.c_void_p * 3)(1 << 40, (1 << 40) + 64, 1 << 42)
+    assert lib.hyena_projection(2, 2, 256, 64, 32, L.BF16, x, W, None, ov, None) == L.EALIAS
+    ox = (ctypes.c_void_p * 3)(1 << 40, x + 128, 1 << 42)
+    assert lib.hyena_projection(2, 2, 256, 64, 32, L.BF16, x, W, None, ox, None) == L.EALIAS
