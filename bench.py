@@ -8,7 +8,9 @@ the filter parameters and the grid, so they are built once (hyena_filter_gen) be
 that build is reported separately as ``filter_gen_ms``.  Input-dependent (per-sample) filters change with
 every batch, so for those workloads the step also builds them: per order, the register summary, the
 FiLM-modulated SIREN taps of every (b, d) and their spectra, then the operator reading one filter per
-(b, d); the filter network is then the dominant kernel and the roofline object reports it.
+(b, d); the filter network is then the dominant kernel and the roofline object reports it.  Workloads
+that start from token-major inputs run the input projection (a matrix-core GEMM that writes v, x_1..x_N
+channel-major) before the operator in every step; the roofline object then reports the projection.
 
 Prints ONE JSON line.  Default workload: order 2, B=4, D=768, L=8192, bf16 storage (workload 1), whose
 convolution runs on the matrix cores;
@@ -153,10 +155,18 @@ def _cpu_baseline_film(w, v, xs, fparams, reg, budget_s: float):
                       f"convolution, BLAS limited to one thread); {t_used:.1f} s"}
 
 
-def cpu_baseline(w, v, xs, params, budget_s: float):
+def cpu_baseline(w, v, xs, params, budget_s: float, proj_inputs=None):
     """The oracle as it stands on whole (b, d) rows (volumes) of the same workload, until about
     budget_s seconds of oracle time; the filters of the sampled channels are built outside the
-    timed part (as the GPU's spectra are), and building stops once it has taken 3 x budget_s."""
+    timed part (as the GPU's spectra are), and building stops once it has taken 3 x budget_s.
+    With proj_inputs (x, W_proj, bias) each row's v, x_1..x_N come from the oracle's projection of the
+    token-major input, inside the timed part."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1):                  # one core, also for the projection's matrix products
+        return _cpu_baseline(w, v, xs, params, budget_s, proj_inputs)
+
+
+def _cpu_baseline(w, v, xs, params, budget_s: float, proj_inputs):
     from oracle import hyena_oracle as orc
     rows = hi.sample_rows(w, 4096, seed=99)
     circ = w.mode == "circular"
@@ -176,7 +186,12 @@ def cpu_baseline(w, v, xs, params, budget_s: float):
             t_build += time.perf_counter() - tb
             print(f"cpu baseline: filters for channel {d} built ({t_build:.1f} s so far)", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
-        if w.ndim == 1:
+        if proj_inputs is not None:
+            xt, Wp, bp = proj_inputs
+            sel = [j * w.D + d for j in range(w.order + 1)]
+            rows_p = orc.input_projection(xt[b:b + 1], Wp[sel], bp[sel], w.order)     # each [1, 1, L]
+            orc.hyena_operator_rows(rows_p[0][0], [r[0] for r in rows_p[1:]], filt[d], circular=circ)
+        elif w.ndim == 1:
             orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], filt[d], circular=circ)
         else:
             orc.hyena_operator_3d(v[b, d][None], [x[b, d][None] for x in xs], filt[d], circular=circ)
@@ -186,7 +201,9 @@ def cpu_baseline(w, v, xs, params, budget_s: float):
             break
     return {"value": n_done * w.points / t_used, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
             "sample": f"{n_done} of {w.B * w.D} (b,d) rows of the same workload, order {w.order}, float64 numpy FFT "
-                      f"convolution on one core (numpy.fft is single-threaded), filters prebuilt; {t_used:.1f} s"}
+                      f"convolution on one core (numpy.fft is single-threaded, BLAS limited to one thread)"
+                      f"{', each row projected from the token-major input' if proj_inputs is not None else ''}"
+                      f", filters prebuilt; {t_used:.1f} s"}
 
 
 def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
@@ -251,6 +268,14 @@ def main():
     ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
     stream = torch.cuda.current_stream(dev)
 
+    proj = w.d_model > 0
+    if proj:
+        xtok, Wp, bp = hi.draw_projection(w)
+        xtd = torch.from_numpy(xtok).to(dev).to(dt)
+        Wpd = torch.from_numpy(Wp).to(dev).to(dt)
+        bpd = torch.from_numpy(bp).to(dev)
+        pouts = [vd] + xd                       # the projection writes v, x_1..x_N in place of the drawn ones
+
     if film:
         # per-sample filters: rebuilt inside every step into preallocated spectra and workspace
         regd = torch.from_numpy(reg).to(dev)
@@ -277,6 +302,8 @@ def main():
         filter_gen_ms = 1e3 * min(fg)
 
         def step():
+            if proj:
+                hy.projection(xtd, Wpd, w.order, bias=bpd, outs=pouts)
             hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
 
     for _ in range(args.warmup):
@@ -387,7 +414,31 @@ def main():
         out["filter_gen"] = {"ms": filter_gen_ms, "network_gflop": net_flop / 1e9,
                              "achieved_tflops": net_flop / (filter_gen_ms / 1e3) / 1e12, "peak_tflops": 157.3,
                              "note": "all orders; network flops over the whole filter build (spectra included)"}
-    if film:
+    if proj:
+        # dominant kernel of the new step part: the projection GEMM, timed alone
+        for _ in range(3):
+            hy.projection(xtd, Wpd, w.order, bias=bpd, outs=pouts)
+        reps = 50
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            hy.projection(xtd, Wpd, w.order, bias=bpd, outs=pouts)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        proj_ms = e0.elapsed_time(e1) / reps
+        flops = 2.0 * w.B * w.points * w.d_model * (w.order + 1) * w.D
+        peak = 2500.0 if w.dtype == "bf16" else 157.3
+        tf = flops / (proj_ms / 1e3) / 1e12
+        out["roofline"] = {"bound": "mfma", "kernel": f"k_proj<{'bf16' if w.dtype == 'bf16' else 'fp32'}> "
+                                                      f"(input projection, channel-major outputs)",
+                           "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak, "traffic": None,
+                           "launch_ms": proj_ms, "alg_flops_per_launch": flops,
+                           "note": f"dense {'bf16' if w.dtype == 'bf16' else 'fp32'} matrix-core peak"}
+        out["projection_share_of_step"] = proj_ms / float(np.mean(step_ms))
+        out["config"]["d_model"] = w.d_model
+        out["config"]["inputs"] += ", stream 3 token-major inputs and W_proj"
+    if film or proj:
         pass                                # the roofline object above
     elif uses_matrix_cores(w) and w.order <= 8:
         # the whole step is one launch of the matrix-core kernel: all orders, u_i kept on chip
@@ -417,7 +468,8 @@ def main():
         out["copy_gbps"] = copy_bandwidth(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = (cpu_baseline_film(w, v, xs, params, reg, args.cpu_budget) if film else
-                               cpu_baseline(w, v, xs, params, args.cpu_budget))
+                               cpu_baseline(w, v, xs, params, args.cpu_budget,
+                                            proj_inputs=(xtok, Wp, bp) if proj else None))
     print(json.dumps(out), flush=True)
 
 
