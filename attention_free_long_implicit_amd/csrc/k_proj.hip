@@ -7,10 +7,10 @@
 // of layout that the convolution needs costs no pass of its own.  Both operands are contiguous in k,
 // which is the order the matrix-core operands want (lane l holds 8 consecutive k of row l mod 32).
 //
-// A workgroup owns 128 channels x 128 tokens of one sample; its 4 waves own 64 x 64 each (2 x 2 blocks
-// of 32 x 32 accumulators).  k advances in tiles of 32, staged through LDS and double-buffered through
-// registers (the next tile's global loads are in flight while the current one is multiplied).  Global
-// loads go through raw buffer descriptors: rows past the last channel or token read zero.
+// A workgroup owns a tile of channels x tokens of one sample, split among its waves in blocks of 32 x 32
+// accumulators.  k advances in tiles, staged through LDS and double-buffered through registers (the
+// next tile's global loads are in flight while the current one is multiplied).  Global loads go through
+// raw buffer descriptors: rows past the last channel or token read zero.
 #include "launch.h"
 
 namespace hyena {
@@ -22,41 +22,48 @@ typedef __attribute__((ext_vector_type(4))) uint32_t pj_u32x4;
 // raw buffer descriptor word 3: 32-bit data format, offsets beyond the record count read zero
 constexpr int kProjRsrcWord3 = 0x00020000;
 
-namespace pj {
-constexpr int BM = 128, BN = 128, BK = 32, T = 256;
-}
-
 template <bool BF16> struct ProjT;
 template <> struct ProjT<true> {
   using E = uint16_t;                         // bf16 storage
-  static constexpr int ES = 2;
-  static constexpr int LDK = pj::BK + 8;      // LDS row stride (80 bytes: 16-byte rows, no read conflicts)
+  static constexpr int ES = 2, PAD = 8;       // LDS rows padded by 16 bytes: conflict-free 16-byte reads
 };
 template <> struct ProjT<false> {
   using E = float;
-  static constexpr int ES = 4;
-  static constexpr int LDK = pj::BK + 4;      // 144 bytes
+  static constexpr int ES = 4, PAD = 4;
 };
+
+// Tile shape: WM x WN waves, each owning FM x FN blocks of 32 x 32 accumulators; k tiles of BK.
+template <int WM_, int WN_, int FM_, int FN_, int BK_>
+struct ProjCfg {
+  static constexpr int WM = WM_, WN = WN_, FM = FM_, FN = FN_, BK = BK_;
+  static constexpr int T = WM * WN * 64, BM = WM * FM * 32, BN = WN * FN * 32;
+};
+// 256 channels x 256 tokens per workgroup, 8 waves of 64 x 128 (measured against 128 x 128 and 256 x 128
+// tiles, 4 to 16 waves, 1 or 2 waves per SIMD: this shape ran fastest on the layer's shapes)
+using PCB = ProjCfg<4, 2, 2, 4, 64>;          // bf16 operands
+using PCF = ProjCfg<4, 2, 2, 4, 32>;          // fp32 operands (k tile halved: LDS)
 
 struct ProjOut {
   void* p[kProjMaxOut];
 };
 
-template <bool BF16>
-__global__ void __launch_bounds__(pj::T, 2)
+template <bool BF16, class C>
+__global__ void __launch_bounds__(C::T)
 k_proj(const void* __restrict__ x, const void* __restrict__ W, const float* __restrict__ bias, ProjOut out,
-       int L, int K, int M, int D, int tiles_c, int tiles_t) {
-  using namespace pj;
+       int L, int K, int M, int D, int tiles_c, int tiles_t, int vec_store) {
   using P = ProjT<BF16>;
   using E = typename P::E;
-  constexpr int ES = P::ES, LDK = P::LDK;
+  constexpr int T = C::T, BM = C::BM, BN = C::BN, BK = C::BK, FM = C::FM, FN = C::FN, WM = C::WM;
+  constexpr int ES = P::ES, LDK = BK + P::PAD;
   constexpr int CPR = BK * ES / 16;           // 16-byte chunks per tile row
-  constexpr int CH = BM * CPR / T;            // chunks per thread per operand
-  static_assert(BM == BN && (BM * CPR) % T == 0, "tile");
-  __shared__ __align__(16) E As[2][BM * LDK];
-  __shared__ __align__(16) E Bs[2][BN * LDK];
+  constexpr int CHA = BM * CPR / T, CHB = BN * CPR / T;
+  static_assert((BM * CPR) % T == 0 && (BN * CPR) % T == 0, "tile");
+  // one LDS array: two k-tile buffers of each operand, reused by the epilogue's staging
+  __shared__ __align__(16) E lds[2 * (BM + BN) * LDK];
+  E* const As = lds;                          // buffer q at As + q * BM * LDK
+  E* const Bs = lds + 2 * BM * LDK;           // buffer q at Bs + q * BN * LDK
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
   const int ct = lb % tiles_c, rest = lb / tiles_c;
   const int tt = rest % tiles_t, b = rest / tiles_t;
@@ -66,73 +73,86 @@ k_proj(const void* __restrict__ x, const void* __restrict__ W, const float* __re
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(W), (short)0, M * K * ES, kProjRsrcWord3);
   const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)((const char*)x + (size_t)b * L * K * ES), (short)0, L * K * ES, kProjRsrcWord3);
-  int voa[CH], vob[CH], lofs[CH];
+  // chunk r of this thread: tile row, k offset within the tile (elements), LDS offset
+  int voa[CHA], loa[CHA], koa[CHA], vob[CHB], lob[CHB], kob[CHB];
 #pragma unroll
-  for (int r = 0; r < CH; ++r) {
+  for (int r = 0; r < CHA; ++r) {
     const int i = tid + T * r, row = i / CPR, cc = i % CPR;
     voa[r] = (c0 + row) * K * ES + cc * 16;
-    vob[r] = (t0 + row) * K * ES + cc * 16;
-    lofs[r] = row * LDK + cc * (16 / ES);
+    koa[r] = cc * (16 / ES);
+    loa[r] = row * LDK + koa[r];
   }
-  pj_u32x4 ra[CH], rb[CH];
+#pragma unroll
+  for (int r = 0; r < CHB; ++r) {
+    const int i = tid + T * r, row = i / CPR, cc = i % CPR;
+    vob[r] = (t0 + row) * K * ES + cc * 16;
+    kob[r] = cc * (16 / ES);
+    lob[r] = row * LDK + kob[r];
+  }
+  pj_u32x4 ra[CHA], rb[CHB];
+  // a chunk past the last k of a row would read the next row: it is zero instead (k tail)
   auto gload = [&](int k0) {
 #pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      ra[r] = __builtin_bit_cast(pj_u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, voa[r], k0 * ES, 0));
-      rb[r] = __builtin_bit_cast(pj_u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, vob[r], k0 * ES, 0));
-    }
+    for (int r = 0; r < CHA; ++r)
+      ra[r] = k0 + koa[r] < K
+                  ? __builtin_bit_cast(pj_u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, voa[r], k0 * ES, 0))
+                  : pj_u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int r = 0; r < CHB; ++r)
+      rb[r] = k0 + kob[r] < K
+                  ? __builtin_bit_cast(pj_u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, vob[r], k0 * ES, 0))
+                  : pj_u32x4{0u, 0u, 0u, 0u};
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < CH; ++r) {
-      *reinterpret_cast<pj_u32x4*>(&As[buf][lofs[r]]) = ra[r];
-      *reinterpret_cast<pj_u32x4*>(&Bs[buf][lofs[r]]) = rb[r];
-    }
+    for (int r = 0; r < CHA; ++r) *reinterpret_cast<pj_u32x4*>(As + buf * BM * LDK + loa[r]) = ra[r];
+#pragma unroll
+    for (int r = 0; r < CHB; ++r) *reinterpret_cast<pj_u32x4*>(Bs + buf * BN * LDK + lob[r]) = rb[r];
   };
 
-  pj_f32x16 acc[2][2];
+  pj_f32x16 acc[FM][FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int ra_row = wm * 64 + (lane & 31), rb_row = wn * 64 + (lane & 31), hk = lane >> 5;
+  const int ra_row = wm * FM * 32 + (lane & 31), rb_row = wn * FN * 32 + (lane & 31), hk = lane >> 5;
   auto compute = [&](int buf) {
     if constexpr (BF16) {
 #pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
-        pj_bf16x8 a[2], bb[2];
+        pj_bf16x8 a[FM], bb[FN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          a[i] = *reinterpret_cast<const pj_bf16x8*>(&As[buf][(ra_row + 32 * i) * LDK + 16 * s + 8 * hk]);
-          bb[i] = *reinterpret_cast<const pj_bf16x8*>(&Bs[buf][(rb_row + 32 * i) * LDK + 16 * s + 8 * hk]);
-        }
+        for (int i = 0; i < FM; ++i)
+          a[i] = *reinterpret_cast<const pj_bf16x8*>(As + buf * BM * LDK + (ra_row + 32 * i) * LDK + 16 * s + 8 * hk);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < FN; ++j)
+          bb[j] = *reinterpret_cast<const pj_bf16x8*>(Bs + buf * BN * LDK + (rb_row + 32 * j) * LDK + 16 * s + 8 * hk);
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bb[j], acc[i][j], 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int s = 0; s < BK / 2; ++s) {
-        float a[2], bb[2];
+        float a[FM], bb[FN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          a[i] = As[buf][(ra_row + 32 * i) * LDK + 2 * s + hk];
-          bb[i] = Bs[buf][(rb_row + 32 * i) * LDK + 2 * s + hk];
-        }
+        for (int i = 0; i < FM; ++i) a[i] = As[buf * BM * LDK + (ra_row + 32 * i) * LDK + 2 * s + hk];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < FN; ++j) bb[j] = Bs[buf * BN * LDK + (rb_row + 32 * j) * LDK + 2 * s + hk];
 #pragma unroll
-          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], bb[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], bb[j], acc[i][j], 0, 0, 0);
       }
     }
   };
 
-  const int nk = K / BK;
+  const int nk = (K + BK - 1) / BK;
   gload(0);
   lstore(0);
   __syncthreads();
@@ -147,18 +167,50 @@ k_proj(const void* __restrict__ x, const void* __restrict__ W, const float* __re
 
   // epilogue: accumulator register v of lane (col, h) holds row 8 (v / 4) + 4 h + (v mod 4), column col
   const int h = lane >> 5, col = lane & 31;
+  const int wc0 = c0 + wm * FM * 32, wt0 = t0 + wn * FN * 32;
+  if constexpr (BF16) {
+    if (vec_store) {
+      // through LDS: the wave's 64 x 128 block as bf16 rows, then 16-byte stores of 8 tokens each
+      constexpr int RW = FN * 32 + 8;                      // LDS row stride of the block (elements)
+      static_assert(WM * C::WN * FM * 32 * RW <= 2 * (BM + BN) * LDK, "epilogue staging fits the tiles");
+      E* st = lds + wave * (FM * 32 * RW);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          const int c = wc0 + r;
+          const float bc = (bias && c < M) ? bias[c] : 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj) st[r * RW + 32 * jj + col] = f32_to_bf16_rne(acc[i][jj][v] + bc);
+        }
+      __syncthreads();
+      constexpr int CPRW = FN * 32 / 8;                    // 16-byte chunks per block row
+      constexpr int ITER = FM * 32 * CPRW / 64;
+#pragma unroll
+      for (int it = 0; it < ITER; ++it) {
+        const int e = lane + 64 * it, r = e / CPRW, ch = e % CPRW;
+        const int c = wc0 + r, t = wt0 + 8 * ch;
+        if (c >= M || t >= L) continue;
+        const int j = c / D, d = c - j * D;
+        E* dst = static_cast<E*>(out.p[j]) + ((size_t)b * D + d) * L + t;
+        *reinterpret_cast<pj_u32x4*>(dst) = *reinterpret_cast<const pj_u32x4*>(&st[r * RW + 8 * ch]);
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const int c = c0 + wm * 64 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+      const int c = wc0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
       if (c >= M) continue;
       const int j = c / D, d = c - j * D;
       const float bc = bias ? bias[c] : 0.0f;
       E* orow = static_cast<E*>(out.p[j]) + ((size_t)b * D + d) * L;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int t = t0 + wn * 64 + 32 * jj + col;
+      for (int jj = 0; jj < FN; ++jj) {
+        const int t = wt0 + 32 * jj + col;
         if (t >= L) continue;
         const float val = acc[i][jj][v] + bc;
         if constexpr (BF16) orow[t] = f32_to_bf16_rne(val);
@@ -170,11 +222,26 @@ k_proj(const void* __restrict__ x, const void* __restrict__ W, const float* __re
 }  // namespace
 
 bool projection_supported(int64_t B, int64_t L, int64_t K, int64_t M, int es) {
-  if (K % pj::BK) return false;
-  if ((M + pj::BM) * K * es >= ((int64_t)1 << 31) || (L + pj::BN) * K * es >= ((int64_t)1 << 31)) return false;
-  const int64_t tiles = ((M + pj::BM - 1) / pj::BM) * ((L + pj::BN - 1) / pj::BN) * B;
+  const int BM = es == 2 ? PCB::BM : PCF::BM, BN = es == 2 ? PCB::BN : PCF::BN;
+  if (K % (16 / es)) return false;            // whole 16-byte chunks per row
+  if ((M + BM) * K * es >= ((int64_t)1 << 31) || (L + BN) * K * es >= ((int64_t)1 << 31)) return false;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((L + BN - 1) / BN) * B;
   return tiles < ((int64_t)1 << 31);
 }
+
+namespace {
+template <bool BF16, class C>
+hipError_t proj_launch(const void* x, const void* W, const float* bias, const ProjOut& o, int nout, int B, int L,
+                       int K, int M, int D, hipStream_t s) {
+  const int tiles_c = (M + C::BM - 1) / C::BM, tiles_t = (L + C::BN - 1) / C::BN;
+  const dim3 grid((unsigned)(tiles_c * tiles_t * B));
+  // 16-byte stores of 8 bf16 tokens when every output row starts 16-byte aligned
+  int vec = BF16 && L % 8 == 0;
+  for (int j = 0; j < nout; ++j) vec = vec && (reinterpret_cast<uintptr_t>(o.p[j]) & 15u) == 0;
+  hipLaunchKernelGGL((k_proj<BF16, C>), grid, dim3(C::T), 0, s, x, W, bias, o, L, K, M, D, tiles_c, tiles_t, vec);
+  return hipGetLastError();
+}
+}  // namespace
 
 hipError_t launch_projection(int bf16, const void* x, const void* W, const float* bias, void* const* outs, int nout,
                              int B, int L, int K, int D, hipStream_t s) {
@@ -182,13 +249,8 @@ hipError_t launch_projection(int bf16, const void* x, const void* W, const float
   ProjOut o{};
   for (int j = 0; j < nout; ++j) o.p[j] = outs[j];
   const int M = nout * D;
-  const int tiles_c = (M + pj::BM - 1) / pj::BM, tiles_t = (L + pj::BN - 1) / pj::BN;
-  const dim3 grid((unsigned)(tiles_c * tiles_t * B));
-  if (bf16)
-    hipLaunchKernelGGL(k_proj<true>, grid, dim3(pj::T), 0, s, x, W, bias, o, L, K, M, D, tiles_c, tiles_t);
-  else
-    hipLaunchKernelGGL(k_proj<false>, grid, dim3(pj::T), 0, s, x, W, bias, o, L, K, M, D, tiles_c, tiles_t);
-  return hipGetLastError();
+  return bf16 ? proj_launch<true, PCB>(x, W, bias, o, nout, B, L, K, M, D, s)
+              : proj_launch<false, PCF>(x, W, bias, o, nout, B, L, K, M, D, s);
 }
 
 }  // namespace hyena

@@ -162,8 +162,8 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
  * both of dtype (bf16: matrix-core products, fp32 accumulation; fp32: fp32 matrix-core products).
  * bias: fp32 [(order+1)*D] or NULL.  out: host array of order+1 device pointers, each [B, D, L] of dtype
  * (channel-major, the layout hyena_operator takes: out[0] = v, out[j] = x_j), written with bf16 rounding
- * to nearest even.  Supported: d_model a multiple of 32, order <= 8, (order+1)*D*d_model and
- * L*d_model elements below 2^31 bytes.  Outputs must not overlap x, W, bias or each other. */
+ * to nearest even.  Supported: d_model a multiple of 8 (bf16) or 4 (fp32), order <= 8, W and one
+ * sample of x below 2^31 bytes.  Outputs must not overlap x, W, bias or each other. */
 int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D, int dtype, const void *x,
                      const void *W, const float *bias, void *const *out, hipStream_t stream);
 

@@ -195,7 +195,7 @@ def test_projection_rejects_before_launch(lib):
     x, W = 1 << 43, 1 << 44
     assert lib.hyena_projection(0, 2, 256, 64, 32, L.BF16, x, W, None, outs, None) == L.EINVAL
     assert lib.hyena_projection(2, 2, 256, 64, 32, 5, x, W, None, outs, None) == L.EINVAL
-    assert lib.hyena_projection(2, 2, 256, 100, 32, L.BF16, x, W, None, outs, None) == L.EUNSUPPORTED   # d_model % 32
+    assert lib.hyena_projection(2, 2, 256, 100, 32, L.BF16, x, W, None, outs, None) == L.EUNSUPPORTED   # d_model % 8
     assert lib.hyena_projection(9, 2, 256, 64, 32, L.BF16, x, W, None,
                                 (ctypes.c_void_p * 10)(*[(i + 1) << 36 for i in range(10)]), None) == L.EUNSUPPORTED
     nul = (ctypes.c_void_p * 3)(1 << 40, None, 1 << 42)

@@ -27,7 +27,9 @@ def _round(a, dtype):
 @pytest.mark.parametrize("B,L,Dm,D,order", [
     (2, 300, 64, 80, 2),       # ragged tokens (300 = 2 tiles + 44) and channels (240 = 128 + 112)
     (1, 128, 32, 128, 1),      # exactly one tile each way, one k-tile
-    (3, 1000, 96, 40, 3),      # four outputs, channel tiles cutting across chunks
+    (3, 1000, 96, 40, 3),      # four outputs, channel tiles cutting across chunks, a k tail
+    (2, 264, 200, 300, 2),     # k tail of 8 (bf16) / 8 (fp32) past whole k tiles; 900 channels
+    (1, 100, 40, 16, 1),       # L not a multiple of 8: element stores
 ])
 def test_projection_matches_oracle(torch_cuda, dtype, B, L, Dm, D, order):
     torch = torch_cuda
