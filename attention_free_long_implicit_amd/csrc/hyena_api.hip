@@ -373,7 +373,7 @@ int hyena_film_filter_workspace_bytes(int64_t B, hyena_dims dims, int mode, int6
   if (st) return st;
   const int kind = kind_of(mode, dims);
   const int64_t nch = B * D;
-  *bytes = (size_t)B * 4 * kFilmHidden * sizeof(float);
+  *bytes = film_scratch_floats((int)B, (int)D) * sizeof(float);
   *bytes = (*bytes + 255) / 256 * 256 + (size_t)nch * taps_per_channel(kind, pts) * sizeof(float);
   const size_t per = filter_intermediate_bytes(kind, pts);
   if (per) *bytes += 256 + (size_t)default_chunk_rows((int64_t)per, nch) * per;
@@ -399,7 +399,7 @@ int hyena_film_filter_gen(const hyena_film_params* p, int64_t B, int32_t R, cons
   if (nch > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
   char* wsp = (char*)ws;
   size_t wsn = ws_bytes;
-  const size_t mod_b = (size_t)B * 4 * kFilmHidden * sizeof(float);
+  const size_t mod_b = film_scratch_floats((int)B, p->D) * sizeof(float);
   if (!ws_align256(wsp, wsn) || wsn < mod_b) return HYENA_EWORKSPACE;
   float* mod = (float*)wsp;
   wsp += mod_b;

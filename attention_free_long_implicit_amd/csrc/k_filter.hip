@@ -14,7 +14,8 @@
 // formed once (a 4 positions x 4 units register tile per thread), then the second layer runs as a
 // small GEMM from LDS with a 4 x 8 register tile per thread; both read their operands as 16-byte
 // LDS vectors.  W1 and the features, then W2 and the hidden activations, share one LDS region.
-// The input-dependent filters (one per sample) follow the same tiling; see k_film_tiles below.
+// The input-dependent filters (one per sample) use the same 64 x 128 tiles with their two dense layers on
+// the matrix cores; see k_film_tiles below.
 #include "launch.h"
 
 namespace hyena {
@@ -29,6 +30,7 @@ constexpr int T = 256;
 struct FilterGrid1D {
   int L;
   __device__ __forceinline__ int count() const { return L; }
+  int count_host() const { return L; }
   // feature pair q (frequency q + 1): sine at column q, cosine at column F/2 + q
   template <int F>
   __device__ __forceinline__ void pair(int pos, int q, int& col_s, int& col_c, float& s, float& c) const {
@@ -46,6 +48,7 @@ struct FilterGrid1D {
 struct FilterGrid3D {
   int W, R0, n;
   __device__ __forceinline__ int count() const { return W * W * W; }
+  int count_host() const { return W * W * W; }
   __device__ __forceinline__ int off(int pos, int ax) const {
     const int i = ax == 0 ? pos / (W * W) : (ax == 1 ? (pos / W) % W : pos % W);
     return i - R0;
@@ -201,13 +204,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 }  // namespace
 
 // One workgroup per sample: scores, softmax weights, z, then the four FiLM vectors
-// mod[b] = {gamma_1, beta_1, gamma_2, beta_2} (H floats each).
+// mod[b] = {gamma_1, beta_1, gamma_2, beta_2} (H floats each).  Workgroup B writes the transposed
+// weights A2t [H][H] and A3t [H][D] that the tile kernel stages row by row.
 __global__ void __launch_bounds__(256)
-k_film_prep(FilmArgs a, const float* __restrict__ reg, int R, float* __restrict__ mod) {
+k_film_prep(FilmArgs a, const float* __restrict__ reg, int B, int R, float* __restrict__ mod,
+            float* __restrict__ a2t, float* __restrict__ a3t) {
   __shared__ float z[kFilmMaxE];
   __shared__ float wr[kFilmMaxR];
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int E = a.E, H = a.H;
+  if (b == B) {
+    for (int i = tid; i < H * H; i += 256) a2t[i] = a.A2[(i % H) * H + i / H];
+    for (int i = tid; i < H * a.D; i += 256) a3t[i] = a.A3[(size_t)(i % a.D) * H + i / a.D];
+    return;
+  }
   const float* rb = reg + (size_t)b * R * E;
   for (int r = wv; r < R; r += 4) {
     float acc = 0.0f;
@@ -229,171 +239,200 @@ k_film_prep(FilmArgs a, const float* __restrict__ reg, int R, float* __restrict_
     z[e] = acc;
   }
   __syncthreads();
+  // one output per thread (4 H = 256): independent row reads, so the loads of a thread overlap
   const float* Ms[4] = {a.G1, a.P1, a.G2, a.P2};
   const float* vs[4] = {a.g1, a.p1, a.g2, a.p2};
-  for (int o = wv; o < 4 * H; o += 4) {
+  for (int o = tid; o < 4 * H; o += 256) {
     const float* row = Ms[o / H] + (size_t)(o % H) * E;
-    float acc = 0.0f;
-    for (int e = lane; e < E; e += 64) acc = fmaf(row[e], z[e], acc);
-    acc = wave_sum(acc);
-    if (lane == 0) mod[(size_t)b * 4 * H + o] = acc + vs[o / H][o % H];
+    float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+    int e = 0;
+    for (; e + 4 <= E; e += 4) {
+      acc0 = fmaf(row[e], z[e], acc0);
+      acc1 = fmaf(row[e + 1], z[e + 1], acc1);
+      acc2 = fmaf(row[e + 2], z[e + 2], acc2);
+      acc3 = fmaf(row[e + 3], z[e + 3], acc3);
+    }
+    for (; e < E; ++e) acc0 = fmaf(row[e], z[e], acc0);
+    mod[(size_t)b * 4 * H + o] = (acc0 + acc1) + (acc2 + acc3) + vs[o / H][o % H];
   }
 }
 
-// Taps of sample blockIdx.z: a tile of 64 positions x 128 channels per workgroup.  Layer 1 (NC inputs)
-// is evaluated directly into LDS; layer 2 (H x H) and the read-out (H -> D) run as small GEMMs from LDS
-// with 4 x 4 and 4 x 8 register tiles, as in the exponential filter's network.
-template <int H, class G>
-__global__ void __launch_bounds__(flt::T)
-k_film_tiles(FilmArgs a, const float* __restrict__ mod, G geo, float* __restrict__ h) {
-  using namespace flt;
+namespace film {
+constexpr int H = 64, TP = 64, CB = 128, T = 256;
+constexpr int SK = TP + 4;        // row stride of the [k][position] and [k][unit] tiles
+constexpr int SC = CB + 4;        // row stride of the [k][channel] read-out tile
+constexpr int SH = H + 1;         // row stride of the [position][unit] layer-2 output
+constexpr int SP = TP + 1;        // row stride of the [channel][position] output staging
+}  // namespace film
+
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float film_f32x16;
+
+// Taps of sample blockIdx.z: 64 positions x 128 channels per workgroup, four waves.  Layer 1 (n inputs)
+// is evaluated directly into LDS; layer 2 (64 x 64 x 64) and the read-out (64 x 128 x 64) run on the
+// matrix cores in fp32 (v_mfma_f32_32x32x2f32): layer 2 one 32 x 32 block per wave (two accumulators
+// over alternate k), the read-out two.  The read-out weights are staged at the start, so their loads
+// overlap layers 1 and 2; the output tile leaves through LDS as [channel][position] rows, so the
+// stores run along positions.
+template <class G>
+__global__ void __launch_bounds__(film::T)
+k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict__ a2t_g,
+             const float* __restrict__ a3t_g, G geo, float* __restrict__ h) {
+  using namespace film;
   constexpr int NC = G::NC;
-  static_assert(H == 64 && 4 * H == T, "tile shape");
-  constexpr int PHASE1 = H * H + H * (TP + 4);          // a2t[H][H], h1T[H][TP+4]
-  constexpr int PHASE2 = H * CB + H * (TP + 4);         // a3t[H][CB], h2T[H][TP+4]
-  __shared__ __align__(16) float lds[PHASE1 > PHASE2 ? PHASE1 : PHASE2];
+  constexpr int R0 = H * SC;                            // a3t [k][c]; later the output staging [c][p]
+  constexpr int R1 = 2 * H * SK;                        // a2t [k][j], h1T [k][p]; later h2 [p][j]
+  static_assert(CB * SP <= R0 && TP * SH <= R1, "LDS regions");
+  __shared__ __align__(16) float lds[R0 + R1];
   __shared__ float gm[4 * H];                           // gamma_1, beta_1, gamma_2, beta_2
+  __shared__ float w1[H][NC + 2];                       // A1 row, a1, omega0 of each first-layer unit
   __shared__ float crd[NC][TP];
   __shared__ float rsq[TP];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hk = lane >> 5;
   const int b = blockIdx.z;
   const int npos = geo.count();
   const int p0 = blockIdx.x * TP, c0 = blockIdx.y * CB;
 
-  float* a2t = lds;
-  float* h1T = lds + H * H;
-  for (int i = tid; i < H * H; i += T) {
-    const int j = i / H, k = i % H;
-    a2t[k * H + j] = a.A2[i];
+  float* a3t = lds;
+  float* a2t = lds + R0;
+  float* h1T = a2t + H * SK;
+  for (int i = tid; i < H * CB; i += T) {
+    const int k = i / CB, c = i % CB;
+    a3t[k * SC + c] = (c0 + c < a.D) ? a3t_g[(size_t)k * a.D + c0 + c] : 0.0f;
   }
+  for (int i = tid; i < H * H; i += T) a2t[(i / H) * SK + i % H] = a2t_g[i];
   gm[tid] = mod[(size_t)b * 4 * H + tid];
-  if (tid < TP) {
+  if (tid < H) {
+#pragma unroll
+    for (int ax = 0; ax < NC; ++ax) w1[tid][ax] = a.A1[tid * NC + ax];
+    w1[tid][NC] = a.a1[tid];
+    w1[tid][NC + 1] = a.omega0[tid];
+  } else if (tid < H + TP) {
+    const int p = tid - H;
     float c[NC];
-    geo.coords(min(p0 + tid, npos - 1), c);
+    geo.coords(min(p0 + p, npos - 1), c);
     float r2 = 0.0f;
 #pragma unroll
     for (int ax = 0; ax < NC; ++ax) {
-      crd[ax][tid] = c[ax];
+      crd[ax][p] = c[ax];
       r2 = fmaf(c[ax], c[ax], r2);
     }
-    rsq[tid] = r2;
+    rsq[p] = r2;
   }
   __syncthreads();
   // layer 1: unit k of position p, positions fastest
   for (int i = tid; i < TP * H; i += T) {
     const int k = i / TP, p = i % TP;
-    float s = a.a1[k];
+    float s = w1[k][NC];
 #pragma unroll
-    for (int ax = 0; ax < NC; ++ax) s = fmaf(a.A1[k * NC + ax], crd[ax][p], s);
-    h1T[k * (TP + 4) + p] = sinf(fmaf(gm[k], a.omega0[k] * s, gm[H + k]));
+    for (int ax = 0; ax < NC; ++ax) s = fmaf(w1[k][ax], crd[ax][p], s);
+    h1T[k * SK + p] = sinf(fmaf(gm[k], w1[k][NC + 1] * s, gm[H + k]));
   }
   __syncthreads();
-  // layer 2: positions 4 hp .. 4 hp + 3, units 4 hj .. 4 hj + 3
-  const int hp = tid % (TP / 4), hj = tid / (TP / 4);
-  float act[4][4];
+
+  // layer 2: wave owns positions 32 pb .. + 31 x units 32 jb .. + 31 (A: h1[p][k], B: A2^T[k][j])
+  const int pb = wave & 1, jb = wave >> 1;
+  film_f32x16 acc2[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc2[u][v] = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < H / 2; ++s) {
+    const int k = 2 * s + hk;
+    acc2[s & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(h1T[k * SK + 32 * pb + l32], a2t[k * SK + 32 * jb + l32],
+                                                       acc2[s & 1], 0, 0, 0);
+  }
+  // register v holds position 32 pb + 8 (v / 4) + 4 hk + (v mod 4) of unit j = 32 jb + l32
+  float h2v[16];
   {
+    const int j = 32 * jb + l32;
+    const float bj = a.a2[j], g2 = gm[2 * H + j], be2 = gm[3 * H + j];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float bj = a.a2[4 * hj + k];
+    for (int v = 0; v < 16; ++v) h2v[v] = sinf(fmaf(g2, acc2[0][v] + acc2[1][v] + bj, be2));
+  }
+  __syncthreads();                                      // every wave is done with a2t and h1T
+
+  float* h2 = lds + R0;
+  {
+    const int j = 32 * jb + l32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) act[i][k] = bj;
-    }
-#pragma unroll 4
-    for (int k = 0; k < H; ++k) {
-      const float4 pv = *reinterpret_cast<const float4*>(h1T + k * (TP + 4) + 4 * hp);
-      const float4 wv = *reinterpret_cast<const float4*>(a2t + k * H + 4 * hj);
-      const float x[4] = {pv.x, pv.y, pv.z, pv.w};
-      const float y[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) act[i][c] = fmaf(x[i], y[c], act[i][c]);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float g2 = gm[2 * H + 4 * hj + k], b2 = gm[3 * H + 4 * hj + k];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) act[i][k] = sinf(fmaf(g2, act[i][k], b2));
-    }
+    for (int v = 0; v < 16; ++v) h2[(32 * pb + 8 * (v >> 2) + 4 * hk + (v & 3)) * SH + j] = h2v[v];
   }
   __syncthreads();
 
-  // read-out: A3 block transposed (zero past D) and the layer-2 activations, positions contiguous
-  float* a3t = lds;
-  float* h2T = lds + H * CB;
-  for (int i = tid; i < H * CB; i += T) {
-    const int k = i / CB, c = i % CB;
-    a3t[i] = (c0 + c < a.D) ? a.A3[(size_t)(c0 + c) * H + k] : 0.0f;
-  }
+  // read-out: wave owns positions 32 pb .. + 31 x channels 64 cq .. + 63 (two 32-column blocks)
+  const int cq = wave >> 1;
+  film_f32x16 acc3[2];
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    *reinterpret_cast<float4*>(h2T + (4 * hj + k) * (TP + 4) + 4 * hp) =
-        make_float4(act[0][k], act[1][k], act[2][k], act[3][k]);
-  __syncthreads();
-
-  const int pg = tid % (TP / 4), cg = tid / (TP / 4);
-  float acc[4][8];
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+    for (int v = 0; v < 16; ++v) acc3[u][v] = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < H / 2; ++s) {
+    const int k = 2 * s + hk;
+    const float av = h2[(32 * pb + l32) * SH + k];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[i][c] = 0.0f;
-#pragma unroll 4
-  for (int k = 0; k < H; ++k) {
-    const float4 av = *reinterpret_cast<const float4*>(h2T + k * (TP + 4) + 4 * pg);
-    const float4 wa = *reinterpret_cast<const float4*>(a3t + k * CB + 8 * cg);
-    const float4 wb = *reinterpret_cast<const float4*>(a3t + k * CB + 8 * cg + 4);
-    const float x[4] = {av.x, av.y, av.z, av.w};
-    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[i][c] = fmaf(x[i], wv[c], acc[i][c]);
+    for (int u = 0; u < 2; ++u)
+      acc3[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, a3t[k * SC + 64 * cq + 32 * u + l32], acc3[u], 0, 0, 0);
   }
 
-  const int pos0 = p0 + 4 * pg;
-  float* hb = h + (size_t)b * a.D * npos;
-  const bool full = pos0 + 3 < npos && (npos & 3) == 0 && (reinterpret_cast<uintptr_t>(h) & 15) == 0;
+  // bias and window; register v holds position 32 pb + 8 (v / 4) + 4 hk + (v mod 4) of channel d
+  __syncthreads();                                      // every wave is done with a3t and h2
+  float* st = lds;                                      // [CB][SP]
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int d = c0 + 8 * cg + c;
-    if (d >= a.D) break;
-    const float a3 = a.a3[d], sg = a.sigma[d];
+  for (int u = 0; u < 2; ++u) {
+    const int cl = 64 * cq + 32 * u + l32, d = c0 + cl;
+    const float a3 = d < a.D ? a.a3[d] : 0.0f, sg = d < a.D ? a.sigma[d] : 1.0f;
     const float k2 = -0.5f / (sg * sg);
-    float v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (acc[i][c] + a3) * expf(k2 * rsq[4 * pg + i]);
-    float* dst = hb + (size_t)d * npos + pos0;
-    if (full) {
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (pos0 + i < npos) dst[i] = v[i];
+    for (int v = 0; v < 16; ++v) {
+      const int pl = 32 * pb + 8 * (v >> 2) + 4 * hk + (v & 3);
+      st[cl * SP + pl] = (acc3[u][v] + a3) * expf(k2 * rsq[pl]);
     }
+  }
+  __syncthreads();
+  float* hb = h + (size_t)b * a.D * npos;
+  for (int i = tid; i < CB * TP; i += T) {
+    const int cl = i / TP, pl = i % TP;
+    const int d = c0 + cl, pos = p0 + pl;
+    if (d < a.D && pos < npos) hb[(size_t)d * npos + pos] = st[cl * SP + pl];
   }
 }
 
-hipError_t launch_film_prep(const FilmArgs& a, const float* reg, int B, int R, float* mod, hipStream_t s) {
+size_t film_scratch_floats(int B, int D) { return (size_t)B * 4 * kFilmHidden + (size_t)kFilmHidden * (kFilmHidden + D); }
+
+hipError_t launch_film_prep(const FilmArgs& a, const float* reg, int B, int R, float* scratch, hipStream_t s) {
   if (a.H != 64 || a.E < 1 || a.E > kFilmMaxE || R < 1 || R > kFilmMaxR || B < 1) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_film_prep, dim3(B), dim3(256), 0, s, a, reg, R, mod);
+  float* mod = scratch;
+  float* a2t = scratch + (size_t)B * 4 * kFilmHidden;
+  float* a3t = a2t + kFilmHidden * kFilmHidden;
+  hipLaunchKernelGGL(k_film_prep, dim3(B + 1), dim3(256), 0, s, a, reg, B, R, mod, a2t, a3t);
   return hipGetLastError();
 }
 
-hipError_t launch_film_filter1d(const FilmArgs& a, const float* mod, int B, int L, float* h, hipStream_t s) {
+namespace {
+template <class G>
+hipError_t film_tiles_launch(const FilmArgs& a, const float* scratch, int B, const G& geo, float* h, hipStream_t s) {
+  const float* a2t = scratch + (size_t)B * 4 * kFilmHidden;
+  const float* a3t = a2t + kFilmHidden * kFilmHidden;
+  const int np = geo.count_host();
+  const dim3 grid((np + film::TP - 1) / film::TP, (a.D + film::CB - 1) / film::CB, B);
+  hipLaunchKernelGGL((k_film_tiles<G>), grid, dim3(film::T), 0, s, a, scratch, a2t, a3t, geo, h);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_film_filter1d(const FilmArgs& a, const float* scratch, int B, int L, float* h, hipStream_t s) {
   if (a.H != 64 || a.NC != 1 || L <= 0 || B < 1) return hipErrorInvalidValue;
-  const dim3 grid((L + flt::TP - 1) / flt::TP, (a.D + flt::CB - 1) / flt::CB, B);
-  hipLaunchKernelGGL((k_film_tiles<64, FilterGrid1D>), grid, dim3(flt::T), 0, s, a, mod, FilterGrid1D{L}, h);
-  return hipGetLastError();
+  return film_tiles_launch(a, scratch, B, FilterGrid1D{L}, h, s);
 }
 
-hipError_t launch_film_filter3d(const FilmArgs& a, const float* mod, int B, float* h, hipStream_t s, int circ) {
+hipError_t launch_film_filter3d(const FilmArgs& a, const float* scratch, int B, float* h, hipStream_t s, int circ) {
   if (a.H != 64 || a.NC != 3 || B < 1) return hipErrorInvalidValue;
   constexpr int n = 64;
   const FilterGrid3D geo = circ ? FilterGrid3D{n, n / 2, n} : FilterGrid3D{2 * n - 1, n - 1, n};
-  const int np = geo.W * geo.W * geo.W;
-  const dim3 grid((np + flt::TP - 1) / flt::TP, (a.D + flt::CB - 1) / flt::CB, B);
-  hipLaunchKernelGGL((k_film_tiles<64, FilterGrid3D>), grid, dim3(flt::T), 0, s, a, mod, geo, h);
-  return hipGetLastError();
+  return film_tiles_launch(a, scratch, B, geo, h, s);
 }
 
 hipError_t launch_filter1d(const FilterArgs& a, int L, float* h, hipStream_t s) {

@@ -85,10 +85,12 @@ struct FilmArgs {
   int E, H, D, NC;                  // register width, hidden units, channels, coordinates (1 or 3)
   const float *q, *A1, *a1, *omega0, *A2, *a2, *A3, *a3, *G1, *g1, *P1, *p1, *G2, *g2, *P2, *p2, *sigma;
 };
-// mod: [B, 4, H] FiLM vectors (gamma_1, beta_1, gamma_2, beta_2) from the registers reg [B, R, E]
-hipError_t launch_film_prep(const FilmArgs& a, const float* reg, int B, int R, float* mod, hipStream_t s);
-// taps h[B, D, points] (1-D t = 0..L-1; 3-D offsets as launch_filter3d)
-hipError_t launch_film_filter1d(const FilmArgs& a, const float* mod, int B, int L, float* h, hipStream_t s);
-hipError_t launch_film_filter3d(const FilmArgs& a, const float* mod, int B, float* h, hipStream_t s, int circ);
+// scratch (film_scratch_floats floats): [B, 4, H] FiLM vectors (gamma_1, beta_1, gamma_2, beta_2) from the
+// registers reg [B, R, E], then A2 and A3 transposed ([H][H], [H][D])
+size_t film_scratch_floats(int B, int D);
+hipError_t launch_film_prep(const FilmArgs& a, const float* reg, int B, int R, float* scratch, hipStream_t s);
+// taps h[B, D, points] (1-D t = 0..L-1; 3-D offsets as launch_filter3d), after launch_film_prep
+hipError_t launch_film_filter1d(const FilmArgs& a, const float* scratch, int B, int L, float* h, hipStream_t s);
+hipError_t launch_film_filter3d(const FilmArgs& a, const float* scratch, int B, float* h, hipStream_t s, int circ);
 
 }  // namespace hyena

@@ -151,11 +151,13 @@ def test_per_sample_sizes(lib):
     assert st == 0 and n == 2 * 128 * 128 * 128 * 65 * 8
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([65536]), L.CAUSAL | L.PER_SAMPLE, 6)
     assert st == 0 and n == 6 * 65536 * (8 + 4)
-    # workspace: FiLM vectors (B x 4 x 64 floats, 256-byte rounded), taps of B*D filters, transform chunk
+    # workspace: FiLM vectors (B x 4 x 64 floats) and the transposed 64 x 64 and D x 64 weights (256-byte
+    # rounded), taps of B*D filters, transform chunk
+    scratch = lambda B, D: -(-(B * 4 * 64 + 64 * (64 + D)) * 4 // 256) * 256
     st, n = _size(lib.hyena_film_filter_workspace_bytes, 2, L.dims_of([1024]), L.CAUSAL, 16)
-    assert st == 0 and n == 2048 + 2 * 16 * 1024 * 4
+    assert st == 0 and n == scratch(2, 16) + 2 * 16 * 1024 * 4
     st, n = _size(lib.hyena_film_filter_workspace_bytes, 2, L.dims_of([64, 64, 64]), L.LINEAR, 3)
-    assert st == 0 and n == 2048 + 6 * 127 ** 3 * 4 + 256 + 6 * 128 * 128 * 65 * 8
+    assert st == 0 and n == scratch(2, 3) + 6 * 127 ** 3 * 4 + 256 + 6 * 128 * 128 * 65 * 8
     st, n = _size(lib.hyena_film_filter_workspace_bytes, 0, L.dims_of([1024]), L.CAUSAL, 16)
     assert st == L.EINVAL
     # the flag leaves the conv workspace unchanged
