@@ -267,6 +267,19 @@ constexpr int SP = TP + 1;        // row stride of the [channel][position] outpu
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float film_f32x16;
 
+// sin x for the SIREN layers (|x| up to a few hundred): x is reduced by the nearest multiple of 2 pi,
+// with 2 pi split into its fp32 value and the remainder (so the reduced argument keeps fp32 accuracy),
+// then the hardware sine takes the reduced angle in revolutions (|r / 2 pi| <= 1/2).
+__device__ __forceinline__ float siren_sin(float x) {
+  constexpr float kInv2Pi = 0.15915493667125702f;          // fp32(1 / 2 pi)
+  constexpr float k2PiHi = 6.2831854820251465f;            // fp32(2 pi)
+  constexpr float k2PiLo = -1.7484555314695172e-07f;       // 2 pi - fp32(2 pi)
+  const float k = rintf(x * kInv2Pi);
+  float r = fmaf(-k, k2PiHi, x);
+  r = fmaf(-k, k2PiLo, r);
+  return __builtin_amdgcn_sinf(r * kInv2Pi);
+}
+
 // Taps of sample blockIdx.z: 64 positions x 128 channels per workgroup, four waves.  Layer 1 (n inputs)
 // is evaluated directly into LDS; layer 2 (64 x 64 x 64) and the read-out (64 x 128 x 64) run on the
 // matrix cores in fp32 (v_mfma_f32_32x32x2f32): layer 2 one 32 x 32 block per wave (two accumulators
@@ -326,7 +339,7 @@ k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict_
     float s = w1[k][NC];
 #pragma unroll
     for (int ax = 0; ax < NC; ++ax) s = fmaf(w1[k][ax], crd[ax][p], s);
-    h1T[k * SK + p] = sinf(fmaf(gm[k], w1[k][NC + 1] * s, gm[H + k]));
+    h1T[k * SK + p] = siren_sin(fmaf(gm[k], w1[k][NC + 1] * s, gm[H + k]));
   }
   __syncthreads();
 
@@ -349,7 +362,7 @@ k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict_
     const int j = 32 * jb + l32;
     const float bj = a.a2[j], g2 = gm[2 * H + j], be2 = gm[3 * H + j];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) h2v[v] = sinf(fmaf(g2, acc2[0][v] + acc2[1][v] + bj, be2));
+    for (int v = 0; v < 16; ++v) h2v[v] = siren_sin(fmaf(g2, acc2[0][v] + acc2[1][v] + bj, be2));
   }
   __syncthreads();                                      // every wave is done with a2t and h1T
 
