@@ -90,16 +90,16 @@ k_proj(const void* __restrict__ x, const void* __restrict__ W, const float* __re
     lob[r] = row * LDK + kob[r];
   }
   pj_u32x4 ra[CHA], rb[CHB];
-  // a chunk past the last k of a row would read the next row: it is zero instead (k tail)
-  auto gload = [&](int k0) {
+  // in the last, partial k tile a chunk past the last k of a row would read the next row: it is zero
+  auto gload = [&](int k0, bool tail) {
 #pragma unroll
     for (int r = 0; r < CHA; ++r)
-      ra[r] = k0 + koa[r] < K
+      ra[r] = !tail || k0 + koa[r] < K
                   ? __builtin_bit_cast(pj_u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrs, voa[r], k0 * ES, 0))
                   : pj_u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int r = 0; r < CHB; ++r)
-      rb[r] = k0 + kob[r] < K
+      rb[r] = !tail || k0 + kob[r] < K
                   ? __builtin_bit_cast(pj_u32x4, __builtin_amdgcn_raw_buffer_load_b128(xrs, vob[r], k0 * ES, 0))
                   : pj_u32x4{0u, 0u, 0u, 0u};
   };
@@ -152,13 +152,15 @@ k_proj(const void* __restrict__ x, const void* __restrict__ W, const float* __re
     }
   };
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
+  const int nk = (K + BK - 1) / BK, nfull = K / BK;
+  if (nfull > 0) gload(0, false);
+  else gload(0, true);
   lstore(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    if (kt + 1 < nfull) gload((kt + 1) * BK, false);
+    else if (kt + 1 < nk) gload((kt + 1) * BK, true);
     compute(cur);
     // buffer cur ^ 1 was last read in the previous iteration, before the barrier that ended it
     if (kt + 1 < nk) lstore(cur ^ 1);
@@ -173,7 +175,7 @@ k_proj(const void* __restrict__ x, const void* __restrict__ W, const float* __re
       // through LDS: the wave's 64 x 128 block as bf16 rows, then 16-byte stores of 8 tokens each
       constexpr int RW = FN * 32 + 8;                      // LDS row stride of the block (elements)
       static_assert(WM * C::WN * FM * 32 * RW <= 2 * (BM + BN) * LDK, "epilogue staging fits the tiles");
-      E* st = lds + wave * (FM * 32 * RW);
+      __bf16* st = reinterpret_cast<__bf16*>(lds) + wave * (FM * 32 * RW);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -182,19 +184,28 @@ k_proj(const void* __restrict__ x, const void* __restrict__ W, const float* __re
           const int c = wc0 + r;
           const float bc = (bias && c < M) ? bias[c] : 0.0f;
 #pragma unroll
-          for (int jj = 0; jj < FN; ++jj) st[r * RW + 32 * jj + col] = f32_to_bf16_rne(acc[i][jj][v] + bc);
+          for (int jj = 0; jj < FN; ++jj) st[r * RW + 32 * jj + col] = (__bf16)(acc[i][jj][v] + bc);   // RNE
         }
       __syncthreads();
       constexpr int CPRW = FN * 32 / 8;                    // 16-byte chunks per block row
       constexpr int ITER = FM * 32 * CPRW / 64;
+      constexpr int RSTEP = 64 / CPRW;                     // rows advanced per iteration
+      // output chunk and channel of this lane's first row (wc0 is wave-uniform), then stepped by RSTEP
+      int r = lane / CPRW;
+      int j = (wc0 + r) / D, d = wc0 + r - j * D;
+      const int ch = lane % CPRW, t = wt0 + 8 * ch;
 #pragma unroll
       for (int it = 0; it < ITER; ++it) {
-        const int e = lane + 64 * it, r = e / CPRW, ch = e % CPRW;
-        const int c = wc0 + r, t = wt0 + 8 * ch;
-        if (c >= M || t >= L) continue;
-        const int j = c / D, d = c - j * D;
-        E* dst = static_cast<E*>(out.p[j]) + ((size_t)b * D + d) * L + t;
-        *reinterpret_cast<pj_u32x4*>(dst) = *reinterpret_cast<const pj_u32x4*>(&st[r * RW + 8 * ch]);
+        if (wc0 + r < M && t < L) {
+          E* dst = static_cast<E*>(out.p[j]) + ((size_t)b * D + d) * L + t;
+          *reinterpret_cast<pj_u32x4*>(dst) = *reinterpret_cast<const pj_u32x4*>(&st[r * RW + 8 * ch]);
+        }
+        r += RSTEP;
+        d += RSTEP;
+        while (d >= D) {
+          d -= D;
+          ++j;
+        }
       }
       return;
     }
