@@ -242,11 +242,12 @@ __device__ __forceinline__ void twiddle_powers(float2 w, float2 (&p)[R]) {
 
 // ------------------------------------------------------------------ storage types
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);   // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return uint16_t(u >> 16);
+// bf16 rounding to nearest even (the hardware conversion; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+  const bf16x2_t b = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, b);
 }
 
 // Two consecutive stored elements (one packed complex sample) <-> float2.
@@ -263,8 +264,7 @@ template <> struct Store<true> {
     return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
   }
   __device__ __forceinline__ static void store2(uint16_t* p, float2 v) {
-    uint32_t w = uint32_t(f32_to_bf16_rne(v.x)) | (uint32_t(f32_to_bf16_rne(v.y)) << 16);
-    *reinterpret_cast<uint32_t*>(p) = w;
+    *reinterpret_cast<uint32_t*>(p) = f32x2_to_bf16x2_rne(v.x, v.y);
   }
 };
 
