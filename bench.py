@@ -399,14 +399,13 @@ def main():
         launch_ms = e0.elapsed_time(e1) / reps
         flops = film_network_flops(w)
         tf = flops / (launch_ms / 1e3) / 1e12
-        out["roofline"] = {"bound": "alu", "kernel": f"k_film_tiles ({'3-D' if w.ndim == 3 else '1-D'} taps, "
-                                                     f"input-dependent filter network)",
+        out["roofline"] = {"bound": "mfma", "kernel": f"k_film_tiles ({'3-D' if w.ndim == 3 else '1-D'} taps, "
+                                                      f"input-dependent filter network)",
                            "achieved": tf, "peak": 157.3, "unit": "TFLOP/s", "frac": tf / 157.3, "traffic": None,
                            "launch_ms": launch_ms, "alg_flops_per_launch": flops,
-                           "frac_unpacked_fma": tf / 78.6,
-                           "note": "peak: fp32 vector 157.3 TFLOP/s (packed); the library is built without packed "
-                                   "fp32 instructions, whose FMA peak is 78.6 TFLOP/s (frac_unpacked_fma); the "
-                                   "launch time includes the register-summary kernel"}
+                           "note": "peak: dense fp32 matrix-core 157.3 TFLOP/s (layer 2 and the read-out run on "
+                                   "fp32 matrix cores; layer 1, the sines and the window on the vector units); "
+                                   "the launch time includes the register-summary kernel"}
         out["filter_share_of_step"] = w.order * launch_ms / float(np.mean(step_ms))
     else:
         # filter network (a GEMM pair per position) for all orders; the time includes the spectrum build
