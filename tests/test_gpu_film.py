@@ -173,3 +173,26 @@ def test_per_sample_full_workload_sampled_volumes(torch_cuda):
         say(f"  (b={b}, d={d}) rel err {e:.3e}")
         worst = max(worst, e)
     assert worst < FP32_TOL, worst
+
+
+@pytest.mark.parametrize("mode,dims", [("causal", (8192,)), ("causal", (65536,)), ("linear", (64, 64, 64))])
+def test_per_sample_with_equal_registers_matches_shared_filters_bitwise(torch_cuda, mode, dims):
+    """Every sample given the same registers: the per-(b, d) path must reproduce, bit for bit, the shared
+    path fed with one sample's spectra (same kernels, filter index b*D + d against d)."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    B, D = 2, 4
+    w = hi.WORKLOADS[7].with_(B=B, D=D, dims=dims, mode=mode)
+    params, reg = _film(w, seed=31)
+    reg[1] = reg[0]
+    v, xs = hi.draw_activations(w, seed=31)
+    md = _mode(w)
+    say(f"per-sample vs shared, {mode} {dims}")
+    pdev = [{k: _dev(a) for k, a in p.items()} for p in params]
+    sp_ps = [hy.film_filter_gen(p, _dev(reg), dims, mode=md) for p in pdev]
+    sp_one = [hy.film_filter_gen(p, _dev(reg[:1]), dims, mode=md) for p in pdev]
+    vd, xd = to_dev(v, torch.float32), [to_dev(x, torch.float32) for x in xs]
+    y_ps = hy.operator(vd, xd, sp_ps, mode=md | hy.PER_SAMPLE)
+    y_sh = hy.operator(vd, xd, sp_one, mode=md)
+    torch.cuda.synchronize()
+    assert torch.equal(y_ps, y_sh)

@@ -109,3 +109,19 @@ def test_layer_from_token_major_inputs(torch_cuda, dtype):
     e = rel_err_rows(y.float().cpu().numpy(), ref)
     say(f"  max rel err {e.max():.3e}")
     assert e.max() < (BF16_TOL if dtype == "bf16" else FP32_TOL), e.max()
+
+
+def test_projection_nine_outputs(torch_cuda):
+    """order 8: nine output chunks (the largest the entry point takes)."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    B, L, Dm, D, order = 1, 384, 64, 24, 8
+    rng = np.random.default_rng(9)
+    x = _round(rng.standard_normal((B, L, Dm)).astype(np.float32), "bf16")
+    W = _round((rng.standard_normal(((order + 1) * D, Dm)) / 8).astype(np.float32), "bf16")
+    say("projection, nine outputs")
+    outs = hy.projection(to_dev(x, torch.bfloat16), to_dev(W, torch.bfloat16), order)
+    torch.cuda.synchronize()
+    assert len(outs) == 9
+    worst = max(rel_err_rows(o.float().cpu().numpy(), r).max() for o, r in zip(outs, orc.input_projection(x, W, None, order)))
+    assert worst < BF16_TOL / 4, worst
