@@ -162,6 +162,15 @@ int64_t default_chunk_rows(int64_t per, int64_t rows) {
   return c < rows ? c : rows;
 }
 
+// Channels per chunk while building spectra from taps: about 1 GB of intermediate.  Nothing is reused
+// across channels there, and fewer, larger launches lose less to the partly filled last round of
+// workgroups than the 160 MB chunks of the convolution.
+int64_t filter_chunk_rows(int64_t per, int64_t rows) {
+  int64_t c = ((int64_t)1 << 30) / per;
+  if (c < 1) c = 1;
+  return c < rows ? c : rows;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // The matrix-core kernel: bf16, L = 8192, rows in pairs, and (16-byte vector accesses) every activation
@@ -318,7 +327,7 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* b
   *bytes = (size_t)D * taps_per_channel(kind, pts) * sizeof(float);
   if (kind == K_CAUSAL && has_pair_copy(pts)) *bytes += 256 + pair_copy_temp_bytes(pts, D);
   const size_t per = filter_intermediate_bytes(kind, pts);
-  if (per) *bytes += 256 + (size_t)default_chunk_rows((int64_t)per, D) * per;
+  if (per) *bytes += 256 + (size_t)filter_chunk_rows((int64_t)per, D) * per;
   return HYENA_OK;
 }
 
@@ -376,7 +385,7 @@ int hyena_film_filter_workspace_bytes(int64_t B, hyena_dims dims, int mode, int6
   *bytes = film_scratch_floats((int)B, (int)D) * sizeof(float);
   *bytes = (*bytes + 255) / 256 * 256 + (size_t)nch * taps_per_channel(kind, pts) * sizeof(float);
   const size_t per = filter_intermediate_bytes(kind, pts);
-  if (per) *bytes += 256 + (size_t)default_chunk_rows((int64_t)per, nch) * per;
+  if (per) *bytes += 256 + (size_t)filter_chunk_rows((int64_t)per, nch) * per;
   return HYENA_OK;
 }
 
