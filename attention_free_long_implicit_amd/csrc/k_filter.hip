@@ -10,12 +10,9 @@
 //   g = W2 SiLU(W1 phi + b1) + b2,  W1 [H, F], W2 [D, H];  h[d, pos] = g_d(pos) * window_d(pos)
 //
 // Phases f t (f r) are reduced modulo L (n) in integers before the sine, so every angle is exact.
-// A workgroup owns a tile of 64 positions x 128 channels: the hidden layer of its 64 positions is
-// formed once (a 4 positions x 4 units register tile per thread), then the second layer runs as a
-// small GEMM from LDS with a 4 x 8 register tile per thread; both read their operands as 16-byte
-// LDS vectors.  W1 and the features, then W2 and the hidden activations, share one LDS region.
-// The input-dependent filters (one per sample) use the same 64 x 128 tiles with their two dense layers on
-// the matrix cores; see k_film_tiles below.
+// A workgroup owns a tile of 64 positions x 128 channels: the features are formed once per tile, the
+// hidden layer and the read-out run as small fp32 matrix-core GEMMs from LDS.  The input-dependent
+// filters (one per sample) use the same tiling; see k_film_tiles below.
 #include "launch.h"
 
 namespace hyena {
@@ -72,117 +69,128 @@ struct FilterGrid3D {
   }
 };
 
-template <int F, int H, class G>
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float flt_f32x16;
+
+// One tile: 64 positions x 128 channels, four waves.  The features go to LDS feature-major; the hidden
+// layer (64 positions x 64 units x F) and the read-out (64 positions x 128 channels x 64) run on the fp32
+// matrix cores (v_mfma_f32_32x32x2f32): the hidden layer one 32 x 32 block per wave (two accumulators
+// over alternate k), the read-out two.  The read-out weights are fetched into registers before the
+// hidden layer, so their latency overlaps it; the tile leaves through LDS as [channel][position] rows,
+// so the stores run along positions.
+template <int F, class G>
 __global__ void __launch_bounds__(flt::T)
 k_filter_tiles(FilterArgs a, G geo, float* __restrict__ h) {
   using namespace flt;
-  static_assert(H == 64 && (TP * H) % T == 0, "tile shape");
-  constexpr int PHASE1 = F * H + F * (TP + 4);          // w1t[F][H], phiT[F][TP+4]
-  constexpr int PHASE2 = H * CB + H * (TP + 4);         // w2t[H][CB], actT[H][TP+4]
-  __shared__ __align__(16) float lds[PHASE1 > PHASE2 ? PHASE1 : PHASE2];
-  const int tid = threadIdx.x;
+  constexpr int H = 64;
+  constexpr int SK = TP + 4, SC = CB + 4, SH = H + 1, SP = TP + 1;
+  constexpr int PHASE1 = 2 * F * SK;                    // w1t [f][j], phiT [f][p]
+  constexpr int PHASE2 = H * SC + TP * SH;              // w2t [k][c], act [p][k]
+  constexpr int LDSN = PHASE1 > PHASE2 ? PHASE1 : PHASE2;
+  static_assert(CB * SP <= LDSN && T == 4 * 64, "tile shape");
+  __shared__ __align__(16) float lds[LDSN];
+  __shared__ float rarg[TP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hk = lane >> 5;
   const int npos = geo.count();
   const int p0 = blockIdx.x * TP, c0 = blockIdx.y * CB;
 
-  // phase 1: W1 transposed and the features of the tile's positions (feature-major)
+  // read-out weights of this channel block, transposed on the way: w2[k][c] = W2[c0 + c][k]
+  constexpr int NW2 = H * CB / T;
+  float w2r[NW2];
+#pragma unroll
+  for (int r = 0; r < NW2; ++r) {
+    const int i = tid + T * r, k = i / CB, c = i % CB;
+    w2r[r] = (c0 + c < a.D) ? a.W2[(size_t)(c0 + c) * H + k] : 0.0f;
+  }
+
   float* w1t = lds;
-  float* phiT = lds + F * H;
+  float* phiT = lds + F * SK;
   for (int i = tid; i < F * H; i += T) {
     const int j = i / F, f = i % F;
-    w1t[f * H + j] = a.W1[i];
+    w1t[f * SK + j] = a.W1[i];
   }
   for (int i = tid; i < TP * (F / 2); i += T) {
     const int p = i / (F / 2), q = i % (F / 2);
     const int pos = min(p0 + p, npos - 1);
     int cs, cc;
-    float s, c;
-    geo.template pair<F>(pos, q, cs, cc, s, c);
-    phiT[cs * (TP + 4) + p] = s;
-    phiT[cc * (TP + 4) + p] = c;
+    float sv, cv;
+    geo.template pair<F>(pos, q, cs, cc, sv, cv);
+    phiT[cs * SK + p] = sv;
+    phiT[cc * SK + p] = cv;
   }
+  if (tid < TP) rarg[tid] = geo.window_arg(min(p0 + tid, npos - 1));
   __syncthreads();
-  // hidden layer: thread owns positions 4 hp .. 4 hp + 3 and units 4 hj .. 4 hj + 3
-  const int hp = tid % (TP / 4), hj = tid / (TP / 4);
-  float act[4][4];
+
+  // hidden layer: wave owns positions 32 pb .. + 31 x units 32 jb .. + 31 (A: phi[p][f], B: W1^T[f][j])
+  const int pb = wave & 1, jb = wave >> 1;
+  flt_f32x16 acc1[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc1[u][v] = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < F / 2; ++s) {
+    const int f = 2 * s + hk;
+    acc1[s & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(phiT[f * SK + 32 * pb + l32], w1t[f * SK + 32 * jb + l32],
+                                                       acc1[s & 1], 0, 0, 0);
+  }
+  // register v holds position 32 pb + 8 (v / 4) + 4 hk + (v mod 4) of unit j = 32 jb + l32; SiLU
+  float hv[16];
   {
-    const float bj[4] = {a.b1[4 * hj], a.b1[4 * hj + 1], a.b1[4 * hj + 2], a.b1[4 * hj + 3]};
+    const float bj = a.b1[32 * jb + l32];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) act[i][k] = bj[k];
-#pragma unroll 4
-    for (int f = 0; f < F; ++f) {
-      const float4 pv = *reinterpret_cast<const float4*>(phiT + f * (TP + 4) + 4 * hp);
-      const float4 wv = *reinterpret_cast<const float4*>(w1t + f * H + 4 * hj);
-      const float x[4] = {pv.x, pv.y, pv.z, pv.w};
-      const float y[4] = {wv.x, wv.y, wv.z, wv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) act[i][k] = fmaf(x[i], y[k], act[i][k]);
+    for (int v = 0; v < 16; ++v) {
+      const float z = acc1[0][v] + acc1[1][v] + bj;
+      hv[v] = __fdividef(z, 1.0f + __expf(-z));
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) act[i][k] = __fdividef(act[i][k], 1.0f + __expf(-act[i][k]));   // SiLU
   }
-  __syncthreads();
+  __syncthreads();                                      // every wave is done with w1t and phiT
 
-  // phase 2: W2 block transposed (zero past D) and the activations, positions contiguous
   float* w2t = lds;
-  float* actT = lds + H * CB;
-  for (int i = tid; i < H * CB; i += T) {
-    const int j = i / CB, c = i % CB;
-    w2t[i] = (c0 + c < a.D) ? a.W2[(size_t)(c0 + c) * H + j] : 0.0f;
+  float* act = lds + H * SC;
+#pragma unroll
+  for (int r = 0; r < NW2; ++r) {
+    const int i = tid + T * r;
+    w2t[(i / CB) * SC + i % CB] = w2r[r];
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k)
-    *reinterpret_cast<float4*>(actT + (4 * hj + k) * (TP + 4) + 4 * hp) =
-        make_float4(act[0][k], act[1][k], act[2][k], act[3][k]);
+  for (int v = 0; v < 16; ++v) act[(32 * pb + 8 * (v >> 2) + 4 * hk + (v & 3)) * SH + 32 * jb + l32] = hv[v];
   __syncthreads();
 
-  // second layer: positions 4 pg .. 4 pg + 3, channels 8 cg .. 8 cg + 7 of the tile
-  const int pg = tid % (TP / 4), cg = tid / (TP / 4);
-  float acc[4][8];
+  // read-out: wave owns positions 32 pb .. + 31 x channels 64 cq .. + 63 (two 32-column blocks)
+  const int cq = wave >> 1;
+  flt_f32x16 acc2[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[i][c] = 0.0f;
-#pragma unroll 4
-  for (int j = 0; j < H; ++j) {
-    const float4 av = *reinterpret_cast<const float4*>(actT + j * (TP + 4) + 4 * pg);
-    const float4 wa = *reinterpret_cast<const float4*>(w2t + j * CB + 8 * cg);
-    const float4 wb = *reinterpret_cast<const float4*>(w2t + j * CB + 8 * cg + 4);
-    const float x[4] = {av.x, av.y, av.z, av.w};
-    const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+    for (int v = 0; v < 16; ++v) acc2[u][v] = 0.0f;
+#pragma unroll 8
+  for (int s = 0; s < H / 2; ++s) {
+    const int k = 2 * s + hk;
+    const float av = act[(32 * pb + l32) * SH + k];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc[i][c] = fmaf(x[i], wv[c], acc[i][c]);
+    for (int u = 0; u < 2; ++u)
+      acc2[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, w2t[k * SC + 64 * cq + 32 * u + l32], acc2[u], 0, 0, 0);
   }
+  __syncthreads();                                      // every wave is done with w2t and act
 
-  // bias and window; four consecutive positions per channel as one 16-byte store when in range
-  const int pos0 = p0 + 4 * pg;
-  float wa[4];
+  // bias and window, staged as [channel][position]
+  float* st = lds;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) wa[i] = geo.window_arg(min(pos0 + i, npos - 1));
-  const bool full = pos0 + 3 < npos && (npos & 3) == 0 && (reinterpret_cast<uintptr_t>(h) & 15) == 0;
+  for (int u = 0; u < 2; ++u) {
+    const int cl = 64 * cq + 32 * u + l32, d = c0 + cl;
+    const float b2 = d < a.D ? a.b2[d] : 0.0f, al = d < a.D ? a.alpha[d] : 0.0f;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int d = c0 + 8 * cg + c;
-    if (d >= a.D) break;
-    const float b2 = a.b2[d], al = a.alpha[d];
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (acc[i][c] + b2) * __expf(-al * wa[i]);
-    float* dst = h + (size_t)d * npos + pos0;
-    if (full) {
-      *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (pos0 + i < npos) dst[i] = v[i];
+    for (int v = 0; v < 16; ++v) {
+      const int pl = 32 * pb + 8 * (v >> 2) + 4 * hk + (v & 3);
+      st[cl * SP + pl] = (acc2[u][v] + b2) * __expf(-al * rarg[pl]);
     }
+  }
+  __syncthreads();
+  for (int i = tid; i < CB * TP; i += T) {
+    const int cl = i / TP, pl = i % TP;
+    const int d = c0 + cl, pos = p0 + pl;
+    if (d < a.D && pos < npos) h[(size_t)d * npos + pos] = st[cl * SP + pl];
   }
 }
 
@@ -451,7 +459,7 @@ hipError_t launch_film_filter3d(const FilmArgs& a, const float* scratch, int B, 
 hipError_t launch_filter1d(const FilterArgs& a, int L, float* h, hipStream_t s) {
   if (a.F != 64 || a.H != 64 || L <= 0) return hipErrorInvalidValue;
   const dim3 grid((L + flt::TP - 1) / flt::TP, (a.D + flt::CB - 1) / flt::CB);
-  hipLaunchKernelGGL((k_filter_tiles<64, 64, FilterGrid1D>), grid, dim3(flt::T), 0, s, a, FilterGrid1D{L}, h);
+  hipLaunchKernelGGL((k_filter_tiles<64, FilterGrid1D>), grid, dim3(flt::T), 0, s, a, FilterGrid1D{L}, h);
   return hipGetLastError();
 }
 
@@ -463,7 +471,7 @@ hipError_t launch_filter3d(const FilterArgs& a, float* h, hipStream_t s, int cir
   const FilterGrid3D geo = circ ? FilterGrid3D{n, n / 2, n} : FilterGrid3D{2 * n - 1, n - 1, n};
   const int np = geo.W * geo.W * geo.W;
   const dim3 grid((np + flt::TP - 1) / flt::TP, (a.D + flt::CB - 1) / flt::CB);
-  hipLaunchKernelGGL((k_filter_tiles<96, 64, FilterGrid3D>), grid, dim3(flt::T), 0, s, a, geo, h);
+  hipLaunchKernelGGL((k_filter_tiles<96, FilterGrid3D>), grid, dim3(flt::T), 0, s, a, geo, h);
   return hipGetLastError();
 }
 
