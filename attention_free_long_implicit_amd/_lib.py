@@ -184,6 +184,7 @@ def filter_gen(params: dict, point_shape: Sequence[int], h_time=None, spectrum=N
     W1, W2 = params["W1"], params["W2"]
     H, F = W1.shape
     D = W2.shape[0]
+    _require_f32("filter parameters and h_time", h_time, *[params[k] for k in ("W1", "b1", "W2", "b2", "alpha")])
     dev = W1.device
     mode = mode_for(len(point_shape)) if mode is None else mode
     if spectrum is None:
@@ -210,6 +211,13 @@ FILM_KEYS = ("q", "A1", "a1", "omega0", "A2", "a2", "A3", "a3", "G1", "g1", "P1"
              "sigma")
 
 
+def _require_f32(what: str, *tensors):
+    torch = _torch()
+    for t in tensors:
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{what} must be float32, got {t.dtype}")
+
+
 def film_filter_gen(params: dict, registers, point_shape: Sequence[int], h_time=None, spectrum=None,
                     mode: Optional[int] = None, ws=None, taps_only: bool = False):
     """Input-dependent filters of one order for every sample.  params: dict of CUDA float32 tensors
@@ -220,6 +228,9 @@ def film_filter_gen(params: dict, registers, point_shape: Sequence[int], h_time=
     B, R, E = registers.shape
     H = params["A2"].shape[0]
     D = params["A3"].shape[0]
+    _require_f32("registers, FiLM-SIREN parameters and h_time", registers, h_time, *[params[k] for k in FILM_KEYS])
+    if params["A1"].shape[1] != len(point_shape) or params["q"].shape[0] != E:
+        raise ValueError("A1 needs one column per grid axis and q one entry per register feature")
     dev = registers.device
     mode = mode_for(len(point_shape)) if mode is None else mode
     if taps_only:
@@ -245,6 +256,9 @@ def projection(x, W, order: int, bias=None, outs: Optional[Sequence] = None):
     M = W.shape[0]
     if W.shape[1] != K or M % (order + 1) or W.dtype != x.dtype:
         raise ValueError("W must be [(order+1)*D, d_model] of x's dtype")
+    _require_f32("bias", bias)
+    if bias is not None and bias.numel() != M:
+        raise ValueError("bias must hold one value per projected channel")
     D = M // (order + 1)
     if outs is None:
         outs = [torch.empty((B, D, L), dtype=x.dtype, device=x.device) for _ in range(order + 1)]

@@ -207,3 +207,18 @@ def test_projection_rejects_before_launch(lib):
     assert lib.hyena_projection(2, 2, 256, 64, 32, L.BF16, x, W, None, ov, None) == L.EALIAS
     ox = (ctypes.c_void_p * 3)(1 << 40, x + 128, 1 << 42)
     assert lib.hyena_projection(2, 2, 256, 64, 32, L.BF16, x, W, None, ox, None) == L.EALIAS
+
+
+def test_binding_rejects_wrong_dtypes_before_calling():
+    import torch
+    p = {k: torch.zeros(4, dtype=torch.float64) for k in ("W1", "b1", "W2", "b2", "alpha")}
+    p["W1"] = torch.zeros(64, 64, dtype=torch.float64)
+    p["W2"] = torch.zeros(8, 64, dtype=torch.float64)
+    with pytest.raises(TypeError):
+        hy.filter_gen(p, (1024,))
+    x = torch.zeros(1, 128, 32, dtype=torch.bfloat16)
+    W = torch.zeros(64, 32, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        hy.projection(x, W, 1, bias=torch.zeros(64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        hy.projection(x, torch.zeros(64, 32, dtype=torch.float32), 1)
