@@ -257,11 +257,18 @@ struct NegPairs {
 // lds[addr(p * PS + l * LS)], addr = lds_pad when PAD.  Butterflies are enumerated line-fastest, so
 // consecutive lanes touch consecutive lines (conflict-free when LS == 1, or when LS is odd).
 // NL need not divide the butterfly count evenly among threads (the tail is guarded).
-template <int NL, int PS, int LS, int T, class RL, bool PAD = true>
+// SWZ16 (16 contiguous lines, LS == 1, no padding): bit 4 of the element index is flipped with bit 7,
+// i.e. position rows 8..15 of every 16 store their two half-rows of 8 complex swapped.  A 64-bit access
+// serves 32 lanes at once, which here are 16 lines of two rows: rows p and p + 1 (p even) or p and
+// p + 8 (the radix-8 passes with unit stride).  Padded rows put one bank pair of the second row on the
+// first's; with the swap both pairs of rows fill the 64 banks exactly once.
+template <int NL, int PS, int LS, int T, class RL, bool PAD = true, bool SWZ16 = false>
 struct ColEngine {
   static constexpr int P = RL::P, N = RL::S;
+  static_assert(!SWZ16 || (NL == 16 && PS == 16 && LS == 1 && !PAD), "swizzle layout");
   __device__ __forceinline__ static int addr(int p, int l) {
     const int a = p * PS + l * LS;
+    if constexpr (SWZ16) return a ^ ((a >> 3) & 16);
     return PAD ? lds_pad(a) : a;
   }
 

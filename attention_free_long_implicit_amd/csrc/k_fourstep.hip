@@ -71,7 +71,8 @@ struct FS {
   static constexpr int TILE = 8192;
   static constexpr int C = TILE / M1;
   static constexpr int TC = 512;
-  using Col = ColEngine<C, C, 1, TC, ColRL>;
+  // 16-column tiles take the swizzled unpadded layout (conflict-free 64-bit accesses), wider ones padding
+  using Col = ColEngine<C, C, 1, TC, ColRL, C != 16, C == 16>;
   // row pairs
   static constexpr int G = Plan::G;
   using Row = RowEngine<2 * G, RowRL>;
@@ -105,7 +106,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   const size_t row = (size_t)b * D + d;
   const int c0 = tile * C;
   typename In::T* Irow = I + (size_t)ql * M;
-  auto tile_addr = [&](int p, int c) { return lds_pad(p * C + c); };
+  auto tile_addr = [&](int p, int c) { return F::Col::addr(p, c); };
 
   if constexpr (MODE == 0) {
     // load the packed row: positions n1 < M1/2 (the rest is the zero padding), or all of them (FULL)
@@ -172,7 +173,7 @@ k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
   static_for<FULL ? PER_T : PER_T / 2>([&](auto ii) {
     const int e = t + TC * ii.value;
     const int p = e / C, c = e % C;
-    lds[lds_pad(p * C + c)] = Store<false>::load2(hrow + 2 * ((size_t)(c0 + c) + (size_t)M2 * p));
+    lds[F::Col::addr(p, c)] = Store<false>::load2(hrow + 2 * ((size_t)(c0 + c) + (size_t)M2 * p));
   });
   __syncthreads();
   F::Col::template forward<!FULL>(lds, tw, t);
@@ -180,7 +181,7 @@ k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
   static_for<PER_T>([&](auto ii) {
     const int e = t + TC * ii.value;
     const int p = e / C, c = e % C;
-    Irow[(size_t)p * M2 + c0 + c] = lds[lds_pad(p * C + c)];
+    Irow[(size_t)p * M2 + c0 + c] = lds[F::Col::addr(p, c)];
   });
 }
 
