@@ -66,7 +66,9 @@ struct K3 {
   template <int NL>
   using ZEng = ColEngine<NL, 1, NKZ, T, ZRL, false>;       // lines = y, positions = packed z
   using YEng = ColEngine<NKZ, NKZ, 1, T, YRL, false>;      // lines = kz, positions = y
-  using XEng = ColEngine<COLS, COLS, 1, T, XRL, true>;     // lines = columns, positions = x
+  // lines = columns, positions = x; unpadded: a wave's 64 lanes always touch the 64 consecutive
+  // columns of one position, which fill the banks exactly (a padded row spilled one bank pair over)
+  using XEng = ColEngine<COLS, COLS, 1, T, XRL, false>;
   // Hs = H / (2 MP^3); the filter's own z split contributes a factor 2 (2^-23 for 128^3, 2^-20 for 64^3)
   static constexpr float kSpecScale = 1.0f / (4.0f * MP * MP * MP);
   // signed offset of transform index i on the MP-torus, and whether the filter holds it
