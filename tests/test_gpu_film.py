@@ -196,3 +196,31 @@ def test_per_sample_with_equal_registers_matches_shared_filters_bitwise(torch_cu
     y_sh = hy.operator(vd, xd, sp_one, mode=md)
     torch.cuda.synchronize()
     assert torch.equal(y_ps, y_sh)
+
+
+@pytest.mark.parametrize("mode,L,dtype,B,D,gate", [
+    ("causal", 4096, "bf16", 3, 4, True),       # odd B with bf16 storage
+    ("causal", 1 << 20, "f32", 2, 2, True),     # the longest causal rows, multi-pass
+    ("circular", 8192, "f32", 2, 3, False),     # no gate
+])
+def test_per_sample_fftconv(torch_cuda, mode, L, dtype, B, D, gate):
+    """hyena_fftconv with one filter per (b, d): y = gate * (h_{b,d} conv u) row by row."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[7].with_(B=B, D=D, dims=(L,), mode=mode, dtype=dtype, order=1, registers=3)
+    params, reg = _film(w, seed=L + D)
+    v, xs = hi.draw_activations(w, seed=L + D)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    md = _mode(w)
+    say(f"per-sample fftconv {mode} L={L} {dtype} B={B} D={D} gate={gate}")
+    sp = hy.film_filter_gen({k: _dev(a) for k, a in params[0].items()}, _dev(reg), (L,), mode=md)
+    y = hy.fftconv(to_dev(v, dt), sp, gate=to_dev(xs[0], dt) if gate else None, mode=md | hy.PER_SAMPLE)
+    torch.cuda.synchronize()
+    h = _oracle_filters(w, params, reg)[0]
+    conv = orc.circular_conv_fft if mode == "circular" else orc.causal_conv_fft
+    ref = conv(v.astype(np.float64), h)
+    if gate:
+        ref = ref * xs[0]
+    e = rel_err_rows(y.float().cpu().numpy().astype(np.float64), ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < (BF16_TOL if dtype == "bf16" else FP32_TOL), e.max()
