@@ -286,7 +286,7 @@ int split_mode(int mode, bool* per_sample) {
 
 extern "C" {
 
-int hyena_version(void) { return 100; }
+int hyena_version(void) { return 200; }   // 0.2.0: input-dependent filters, projection
 
 const char* hyena_status_str(int status) {
   switch (status) {

@@ -122,8 +122,9 @@ typedef struct {
   const float *G1, *g1, *P1, *p1, *G2, *g2, *P2, *p2, *sigma;
 } hyena_film_params;
 
-/* Workspace bytes hyena_film_filter_gen needs: the FiLM vectors (4*H floats per sample), the taps of B*D
- * filters (used when h_time is NULL) and, for multi-pass lengths and 3-D, a transform chunk. */
+/* Workspace bytes hyena_film_filter_gen needs: the FiLM vectors (4*H floats per sample) and A2, A3
+ * transposed (H*(H + D) floats), the taps of B*D filters (used when h_time is NULL) and, for multi-pass
+ * lengths and 3-D, a transform chunk. */
 int hyena_film_filter_workspace_bytes(int64_t B, hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Input-dependent filters of one order for B samples: registers [B, R, E] (device, fp32; the R register
