@@ -31,6 +31,10 @@ What is computed (y = x_N * (h_N conv (... x_1 * (h_1 conv v)))):
                                                                            periodic physical systems]
   * the input projection v, x_1..x_N = split(W_proj x), v first           [Hyena note, step 1 equation;
                                                                            listing x.chunk]
+  * streaming decode: the same causal operator evaluated token by token,
+    every order advancing one position at a time                          [Hyena note, step 3 equation;
+                                                                           SPECTRE news, generation
+                                                                           support]
   * input-dependent (per-sample) filters: z(x) = softmax-weighted mean of
     the register activations; K = w(c) * f(c; z) with a FiLM-modulated
     SIREN f and a Gaussian window w                                        [HyenaND, method: registers,
@@ -63,7 +67,10 @@ plain mean and the two-register logistic closed form of the softmax summary, per
 closed-form SIREN outputs with and without FiLM terms, the Gaussian window against the normal density
 and its separability, kernels that follow the registers sample by sample, axis order of the 3-D taps,
 and per-(b, d) filters in the operator against row-by-row direct sums; the projection: a pure-Python
-triple loop on tiny shapes and block-identity weights that return the input transposed and scaled.
+triple loop on tiny shapes and block-identity weights that return the input transposed and scaled;
+streaming decode: the whole-sequence operator (FFT form), unit-delay filters that shift each order by one
+token, delta filters (a pointwise product), and prefix stability (outputs before t do not move when
+later inputs change).
 """
 from __future__ import annotations
 
@@ -79,6 +86,7 @@ __all__ = [
     "rel_l2_per_row", "filter_offsets_3d_circular", "implicit_filter_3d_circular", "circular_conv_direct",
     "circular_conv_fft", "circular_conv3d_direct", "circular_conv3d_fft", "register_summary", "film_siren",
     "gaussian_window", "input_dependent_filter_1d", "input_dependent_filter_3d", "input_projection",
+    "hyena_decode_stream",
 ]
 
 
@@ -427,6 +435,33 @@ def hyena_operator_rows(v: np.ndarray, xs: Sequence[np.ndarray], hs: Sequence[np
     for h, x in zip(hs, xs):
         u = np.asarray(x, np.float64) * conv(u, h)
     return u
+
+
+def hyena_decode_stream(v: np.ndarray, xs: Sequence[np.ndarray], hs: Sequence[np.ndarray]) -> np.ndarray:
+    """Streaming (token-by-token) evaluation of the causal operator: at each position t, in increasing
+    t, every order advances by one token using only positions <= t,
+
+        u_0[t] = v[t],  u_i[t] = x_i[t] * sum_{s=0..t} h_i[t-s] u_{i-1}[s],  y[t] = u_N[t]
+
+    ([Hyena note] step 3 equation, evaluated in generation order; [SPECTRE news] generation support:
+    a spectral mixer that decodes one token at a time).  How a decoder caches the prefix changes only
+    the rounding order, so this is the plain per-token definition.  v, xs[i]: [R, L]; hs[i]: [R, L]
+    (broadcast like hyena_operator_rows).  Returns y [R, L] float64.
+    """
+    v = np.asarray(v, np.float64)
+    xs = [np.asarray(x, np.float64) for x in xs]
+    hs = [np.broadcast_to(np.asarray(h, np.float64), v.shape) for h in hs]
+    L = v.shape[-1]
+    hist = [np.zeros_like(v) for _ in xs]          # hist[i][..., s] = u_i's input u_{i-1}[s]
+    y = np.zeros_like(v)
+    for t in range(L):
+        u = v[..., t]
+        for i, (h, x) in enumerate(zip(hs, xs)):
+            hist[i][..., t] = u
+            c = np.sum(h[..., t::-1] * hist[i][..., : t + 1], axis=-1)
+            u = x[..., t] * c
+        y[..., t] = u
+    return y
 
 
 def hyena_operator_3d(v: np.ndarray, xs: Sequence[np.ndarray], hs: Sequence[np.ndarray],

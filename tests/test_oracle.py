@@ -684,3 +684,57 @@ def test_projection_block_identity_splits_in_order():
     np.testing.assert_array_equal(v, np.swapaxes(x, 1, 2))
     np.testing.assert_array_equal(x1, 2 * np.swapaxes(x, 1, 2))
     np.testing.assert_array_equal(x2, 3 * np.swapaxes(x, 1, 2))
+
+
+# ---------------------------------------------------------------- streaming decode
+
+def test_decode_stream_matches_whole_sequence_operator():
+    # token-by-token evaluation (all orders advancing together) against the order-by-order FFT form
+    rng = np.random.default_rng(61)
+    R, L = 5, 96
+    v = rng.standard_normal((R, L))
+    xs = [rng.standard_normal((R, L)) for _ in range(3)]
+    hs = [rng.standard_normal((R, L)) * np.exp(-np.arange(L) / 20.0) for _ in range(3)]
+    y = orc.hyena_decode_stream(v, xs, hs)
+    np.testing.assert_allclose(y, orc.hyena_operator_rows(v, xs, hs), rtol=1e-10, atol=1e-12)
+
+
+def test_decode_stream_unit_delay_filters_shift_each_order():
+    # h_i = delta(t - 1): u_1[t] = x_1[t] v[t-1], y[t] = x_2[t] x_1[t-1] v[t-2] (zero history)
+    rng = np.random.default_rng(62)
+    L = 12
+    v, x1, x2 = (rng.standard_normal(L) for _ in range(3))
+    h = np.zeros(L)
+    h[1] = 1.0
+    y = orc.hyena_decode_stream(v[None], [x1[None], x2[None]], [h[None], h[None]])[0]
+    want = np.zeros(L)
+    want[2:] = x2[2:] * (x1[1:-1] * v[:-2])
+    np.testing.assert_array_equal(y, want)
+
+
+def test_decode_stream_delta_filters_are_pointwise():
+    rng = np.random.default_rng(63)
+    R, L = 3, 10
+    v = rng.standard_normal((R, L))
+    xs = [rng.standard_normal((R, L)) for _ in range(2)]
+    h = np.zeros((R, L))
+    h[:, 0] = [2.0, -1.0, 0.5]
+    y = orc.hyena_decode_stream(v, xs, [h, h])
+    np.testing.assert_allclose(y, v * xs[0] * xs[1] * (h[:, :1] ** 2), rtol=1e-14)
+
+
+def test_decode_stream_prefix_is_stable():
+    # outputs before t0 depend on inputs before t0 only (what lets a decoder emit them early)
+    rng = np.random.default_rng(64)
+    R, L, t0 = 2, 40, 23
+    v = rng.standard_normal((R, L))
+    xs = [rng.standard_normal((R, L)) for _ in range(2)]
+    hs = [rng.standard_normal((R, L)) for _ in range(2)]
+    y = orc.hyena_decode_stream(v, xs, hs)
+    v2, xs2 = v.copy(), [x.copy() for x in xs]
+    v2[:, t0:] = rng.standard_normal((R, L - t0))
+    for x in xs2:
+        x[:, t0:] = rng.standard_normal((R, L - t0))
+    y2 = orc.hyena_decode_stream(v2, xs2, hs)
+    np.testing.assert_array_equal(y2[:, :t0], y[:, :t0])
+    assert np.abs(y2[:, t0:] - y[:, t0:]).max() > 1e-3
