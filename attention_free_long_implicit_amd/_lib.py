@@ -66,6 +66,12 @@ _SIG = {
     "hyena_film_filter_gen": (_c.c_int, [_c.POINTER(FilmParams), _c.c_int64, _c.c_int32, _c.c_void_p, Dims,
                                          _c.c_int, _c.c_void_p, _c.c_void_p, _c.c_void_p, _c.c_size_t,
                                          _c.c_void_p]),
+    "hyena_decode_state_bytes": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.POINTER(_c.c_size_t)]),
+    "hyena_decode_reset": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_size_t,
+                                      _c.c_void_p]),
+    "hyena_decode_step": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                     _c.c_void_p, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p),
+                                     _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
 }
 
 
@@ -321,3 +327,33 @@ def spectrum_export(spectrum, point_shape: Sequence[int], D: int, mode: Optional
     _check(lib().hyena_spectrum_export(dims_of(point_shape), mode, D, _ptr(spectrum), H.data_ptr(),
                                        _stream(spectrum)), "hyena_spectrum_export")
     return H
+
+
+def decode_state_bytes(order: int, B: int, D: int, L: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().hyena_decode_state_bytes(order, B, D, L, ctypes.byref(n)), "hyena_decode_state_bytes")
+    return n.value
+
+
+def decode_reset(state, order: int, B: int, D: int, L: int):
+    """Clear a decode state (uint8 CUDA tensor of decode_state_bytes bytes) before a new sequence."""
+    _check(lib().hyena_decode_reset(order, B, D, L, _ptr(state), state.numel(), _stream(state)), "hyena_decode_reset")
+
+
+def decode_step(t: int, v_t, x_t: Sequence, taps: Sequence, spectra: Sequence, state, L: int, block: int, y_t=None):
+    """Token t of every (b, d) row: y_t [B, D] from v_t, x_t[i] [B, D] (float32); taps[i]: float32 [D, L]
+    (filter_gen's h_time), spectra[i] from filter_gen; state from decode_state_bytes / decode_reset."""
+    torch = _torch()
+    B, D = v_t.shape
+    order = len(x_t)
+    if len(taps) != order or len(spectra) != order:
+        raise ValueError("need one tap row set and one spectrum per gate")
+    _require_f32("decode activations and taps", v_t, *x_t, *taps)
+    if y_t is None:
+        y_t = torch.empty_like(v_t)
+    xa = (ctypes.c_void_p * order)(*[_ptr(x) for x in x_t])
+    ta = (ctypes.c_void_p * order)(*[_ptr(h) for h in taps])
+    sa = (ctypes.c_void_p * order)(*[_ptr(sp) for sp in spectra])
+    _check(lib().hyena_decode_step(order, B, D, L, block, t, _ptr(v_t), xa, ta, sa, _ptr(y_t), _ptr(state),
+                                   state.numel(), _stream(v_t)), "hyena_decode_step")
+    return y_t

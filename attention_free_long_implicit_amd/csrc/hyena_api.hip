@@ -286,7 +286,7 @@ int split_mode(int mode, bool* per_sample) {
 
 extern "C" {
 
-int hyena_version(void) { return 200; }   // 0.2.0: input-dependent filters, projection
+int hyena_version(void) { return 300; }   // 0.3.0: streaming decode
 
 const char* hyena_status_str(int status) {
   switch (status) {
@@ -556,6 +556,102 @@ int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D
   }
   return hip_status(launch_projection(dtype == HYENA_BF16, x, W, bias, out, nout, (int)B, (int)L, (int)d_model,
                                       (int)D, stream));
+}
+
+// ---- streaming decode.  State: hist [order][B*D][L] fp32, fut [order][B*D][L] fp32, then the multi-pass
+// workspace of one order's convolution (long L only).
+namespace {
+int decode_check(int order, int64_t B, int64_t D, int64_t L, int64_t* rows) {
+  if (order < 1 || B <= 0 || D <= 0 || L <= 0) return HYENA_EINVAL;
+  if (order > kDecodeMaxOrder) return HYENA_EUNSUPPORTED;
+  if (B * D > (int64_t)INT32_MAX / 64) return HYENA_EUNSUPPORTED;
+  hyena_dims dims{};
+  dims.ndim = 1;
+  dims.n[0] = L;
+  int64_t pts = 0;
+  const int st = check_dims(dims, HYENA_CAUSAL, &pts);
+  if (st) return st;
+  *rows = B * D;
+  return HYENA_OK;
+}
+size_t decode_plane_bytes(int64_t rows, int64_t L) { return (size_t)rows * (size_t)L * sizeof(float); }
+size_t decode_ws_bytes(int64_t rows, int64_t L) {
+  const size_t per = row_intermediate_bytes(K_CAUSAL, L);
+  return per ? (size_t)default_chunk_rows((int64_t)per, rows) * per : 0;
+}
+}  // namespace
+
+int hyena_decode_state_bytes(int order, int64_t B, int64_t D, int64_t L, size_t* bytes) {
+  if (!bytes) return HYENA_EINVAL;
+  int64_t rows = 0;
+  const int st = decode_check(order, B, D, L, &rows);
+  if (st) return st;
+  *bytes = 2 * (size_t)order * decode_plane_bytes(rows, L) + decode_ws_bytes(rows, L);
+  return HYENA_OK;
+}
+
+int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void* state, size_t state_bytes,
+                       hipStream_t stream) {
+  int64_t rows = 0;
+  int st = decode_check(order, B, D, L, &rows);
+  if (st) return st;
+  if (!state) return HYENA_EINVAL;
+  size_t need = 0;
+  hyena_decode_state_bytes(order, B, D, L, &need);
+  if (((size_t)state & 255u) || state_bytes < need) return HYENA_EWORKSPACE;
+  // the prefix convolutions read whole history rows: everything past the last token must be zero
+  return hip_status(hipMemsetAsync(state, 0, (size_t)order * decode_plane_bytes(rows, L), stream));
+}
+
+int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, const float* v_t,
+                      const float* const* x_t, const float* const* taps, const void* const* spectra, float* y_t,
+                      void* state, size_t state_bytes, hipStream_t stream) {
+  int64_t rows = 0;
+  int st = decode_check(order, B, D, L, &rows);
+  if (st) return st;
+  if (!v_t || !x_t || !taps || !spectra || !y_t || !state) return HYENA_EINVAL;
+  for (int i = 0; i < order; ++i)
+    if (!x_t[i] || !taps[i] || !spectra[i]) return HYENA_EINVAL;
+  if (t < 0 || t >= L) return HYENA_EINVAL;
+  if (!is_pow2(block) || block > L) return HYENA_EUNSUPPORTED;
+  size_t need = 0;
+  hyena_decode_state_bytes(order, B, D, L, &need);
+  if (((size_t)state & 255u) || state_bytes < need) return HYENA_EWORKSPACE;
+  const size_t tok = (size_t)rows * sizeof(float);
+  if (overlaps(y_t, tok, state, need) || overlaps(y_t, tok, v_t, tok) || overlaps(v_t, tok, state, need))
+    return HYENA_EALIAS;
+  for (int i = 0; i < order; ++i)
+    if (overlaps(y_t, tok, x_t[i], tok) || overlaps(x_t[i], tok, state, need)) return HYENA_EALIAS;
+  Twiddles tw;
+  if ((st = get_twiddles(&tw))) return st;
+  float* hist = (float*)state;
+  const size_t plane = (size_t)rows * (size_t)L;
+  float* fut = hist + (size_t)order * plane;
+  const int64_t t0 = t - t % block;
+  if (t > 0 && t0 == t) {
+    // block boundary: the contribution of the whole stored prefix to every later position, by the FFT
+    // convolution of each order's history row with that order's cached spectrum (no gate)
+    const int lg = log2i(L);
+    const size_t per = row_intermediate_bytes(K_CAUSAL, L);
+    const int chunk = per ? (int)default_chunk_rows((int64_t)per, rows) : 0;
+    for (int i = 0; i < order; ++i) {
+      float* h_i = hist + (size_t)i * plane;
+      float* f_i = fut + (size_t)i * plane;
+      if (chunk) {
+        const void* xs[1] = {nullptr};
+        const void* sp[1] = {spectra[i]};
+        st = hip_status(launch_conv1d_fourstep(lg, 0, 1, (int)B, (int)D, h_i, xs, sp, f_i,
+                                               (float2*)(fut + (size_t)order * plane), chunk, tw, device_mats(),
+                                               stream, 0, 0));
+      } else {
+        st = hip_status(launch_conv1d_single(lg, 0, h_i, nullptr, f_i, (const float2*)spectra[i], (int)B, (int)D, tw,
+                                             stream, 0, 0));
+      }
+      if (st) return st;
+    }
+  }
+  return hip_status(launch_decode_step(order, v_t, x_t, taps, hist, fut, y_t, (int)rows, (int)D, (int)L, (int)t,
+                                       (int)t0, stream));
 }
 
 int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spectrum, void* H, hipStream_t stream) {

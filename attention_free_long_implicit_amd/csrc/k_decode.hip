@@ -1,0 +1,93 @@
+// Streaming (token-by-token) evaluation of the causal operator with a prefix-spectrum cache: the
+// decode-time counterpart of the whole-sequence kernels (SPECTRE digest, token mixer and generation
+// support: a cache that plays the role of the KV cache, so that generating a token does not redo the
+// transform of the whole prefix; Hyena study note, step 3 equation for what each token computes).
+//
+// For each (b, d) row and order i the causal sum at position t splits at the start T0 of t's block:
+//
+//   (h_i conv u_{i-1})[t] = F_i[t] + sum_{j=0..t-T0} h_i[j] u_{i-1}[t-j],
+//   F_i[t] = sum_{s<T0} h_i[t-s] u_{i-1}[s],
+//
+// F_i is produced once per block by the FFT convolution of the whole stored prefix (the cached filter
+// spectrum against the history row, zero past T0), and the in-block part is a direct sum of at most
+// one block of taps.  Every term with j >= 1 reads history written by earlier tokens, so the sums of all
+// orders are formed together and only the j = 0 terms chain the orders within the token:
+//
+//   u_i[t] = x_i[t] * (S_i + h_i[0] u_{i-1}[t]),   S_i = F_i[t] + sum_{j=1..t-T0} h_i[j] u_{i-1}[t-j].
+//
+// One wave per (b, d) row; its lanes split the in-block taps (consecutive j, so the tap and history
+// reads are coalesced) and the partial sums are reduced across the wave.
+#include "launch.h"
+
+namespace hyena {
+
+namespace {
+
+struct DecodePtrs {
+  const float* p[kDecodeMaxOrder];
+};
+
+__device__ __forceinline__ float dec_wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// hist, fut: [N][rows][L] fp32 (history of u_{i-1}, prefix contributions); taps[i]: [D][L] fp32.
+template <int N>
+__global__ void __launch_bounds__(256)
+k_decode_step(const float* __restrict__ v_t, DecodePtrs x_t, DecodePtrs taps, float* hist,
+              const float* __restrict__ fut, float* __restrict__ y_t, int rows, int D, int L, int t, int t0) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;                                  // uniform per wave
+  const int d = r % D;
+  const int n = t - t0;                                   // earlier positions of this block
+  const size_t rowL = (size_t)r * L;
+  const size_t plane = (size_t)rows * L;
+
+  float acc[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+  for (int j = 1 + lane; j <= n; j += 64) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      acc[i] = fmaf(taps.p[i][(size_t)d * L + j], hist[i * plane + rowL + (t - j)], acc[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    acc[i] = dec_wave_sum(acc[i]);
+    if (t0 > 0) acc[i] += fut[i * plane + rowL + t];
+  }
+  // the chain through the orders: u_0 = v, u_i = x_i (S_i + h_i[0] u_{i-1})
+  float u = v_t[r];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if (lane == 0) hist[i * plane + rowL + t] = u;        // u_{i-1}[t] joins order i's history
+    u = x_t.p[i][r] * fmaf(taps.p[i][(size_t)d * L], u, acc[i]);
+  }
+  if (lane == 0) y_t[r] = u;
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(int order, const float* v_t, const float* const* x_t, const float* const* taps,
+                              float* hist, const float* fut, float* y_t, int rows, int D, int L, int t, int t0,
+                              hipStream_t s) {
+  DecodePtrs xp{}, tp{};
+  for (int i = 0; i < order; ++i) {
+    xp.p[i] = x_t[i];
+    tp.p[i] = taps[i];
+  }
+  const dim3 grid((rows + 3) / 4), block(256);
+  switch (order) {
+#define X(n) \
+  case n: hipLaunchKernelGGL(k_decode_step<n>, grid, block, 0, s, v_t, xp, tp, hist, fut, y_t, rows, D, L, t, t0); break;
+    X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
+#undef X
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hyena

@@ -77,6 +77,14 @@ bool projection_supported(int64_t B, int64_t L, int64_t K, int64_t M, int es);
 hipError_t launch_projection(int bf16, const void* x, const void* W, const float* bias, void* const* outs, int nout,
                              int B, int L, int K, int D, hipStream_t s);
 
+// ---- streaming decode: one token of every (b, d) row through all orders.  hist, fut: [order][rows][L]
+// fp32 (history of each order's input; contributions of the positions before t0, the start of t's
+// block); taps[i]: [D][L] fp32 (only the first t - t0 + 1 taps of a row are read); v_t, x_t[i], y_t: [rows].
+constexpr int kDecodeMaxOrder = 8;
+hipError_t launch_decode_step(int order, const float* v_t, const float* const* x_t, const float* const* taps,
+                              float* hist, const float* fut, float* y_t, int rows, int D, int L, int t, int t0,
+                              hipStream_t s);
+
 // ---- input-dependent filters: FiLM-modulated SIREN with a Gaussian window, one filter per (b, d)
 constexpr int kFilmHidden = 64;     // SIREN units per layer
 constexpr int kFilmMaxE = 4096;     // register width

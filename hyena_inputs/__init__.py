@@ -18,6 +18,8 @@ Workloads (the five shapes the Hyena operator is exercised on):
      tokens per sample, a FiLM-modulated SIREN (64 units) and a Gaussian window, one filter per (b, d)
   8  order 2, B=4, D=768, L=8192,      bf16 storage, from token-major inputs x [B, L, 768] through the
      input projection (W_proj [3 * 768, 768]) to v, x_1, x_2, then the operator
+  9  order 2, B=4, D=768, L=8192,      fp32, streaming decode: the sequence fed one token at a time
+     (prefix blocks of 256 tokens), v, x_i ~ N(0,1)
 
 Random streams: ``numpy.random.default_rng([seed, stream])``.  Stream 0 draws
 the activations (v, x_1 .. x_N in that order, or tokens then the embedding for
@@ -62,6 +64,7 @@ class Workload:
     sigma_lo: float = 0.2         # Gaussian window widths (input-dependent filters)
     sigma_hi: float = 0.8
     d_model: int = 0              # width of the token-major input of the projection (0: none)
+    decode_block: int = 0         # streaming decode: tokens per prefix block (0: whole-sequence workload)
 
     @property
     def ndim(self) -> int:
@@ -114,6 +117,8 @@ WORKLOADS: List[Workload] = [
              0.0, 0.0, 3, 64, filter="film", registers=8),
     Workload(8, "proj_order2_B4_D768_L8192_bf16", 2, 4, 768, (8192,), "bf16", "causal", 0.3, 3.0, 64, 64,
              d_model=768),
+    Workload(9, "decode_order2_B4_D768_L8192_f32", 2, 4, 768, (8192,), "f32", "causal", 0.3, 3.0, 64, 64,
+             decode_block=256),
 ]
 
 

@@ -168,6 +168,44 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
 int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D, int dtype, const void *x,
                      const void *W, const float *bias, void *const *out, hipStream_t stream);
 
+/* Streaming decode of the causal 1-D operator, one token at a time, with a prefix-spectrum cache (SPECTRE
+ * digest, token mixer and generation support: a cache in the role of the KV cache lets a spectral mixer
+ * generate without transforming the whole prefix again at every step; the operator itself is the Hyena
+ * study note's step 3 equation).  After the tokens t = 0..L-1 of a sequence have gone through
+ * hyena_decode_step in order, y_t holds exactly what hyena_operator computes at position t (up to fp32
+ * rounding order):  u_0[t] = v[t],  u_i[t] = x_i[t] * sum_{s<=t} h_i[t-s] u_{i-1}[s],  y[t] = u_order[t].
+ *
+ * How: the positions are grouped in blocks of `block` tokens.  At each block start the library convolves
+ * every order's stored history (the tokens so far, zero after them) with that order's cached spectrum by
+ * FFT, once, which gives the whole prefix's contribution to every later position; within the block each
+ * token adds a direct sum over at most `block` taps.  A larger block means fewer prefix convolutions and
+ * longer direct sums.
+ *
+ * State: one caller-owned device buffer of hyena_decode_state_bytes bytes, 256-byte aligned, holding
+ * fp32 [order][B*D][L] histories, fp32 [order][B*D][L] prefix contributions and (L >= 32768) the multi-pass
+ * workspace.  It belongs to one sequence: call hyena_decode_reset before the first token of each sequence,
+ * then hyena_decode_step for t = 0, 1, 2, ... in order on one stream (the library cannot check the order;
+ * skipped or repeated positions give wrong results, not an error).  Calls that share a state buffer must
+ * not run concurrently.
+ *
+ * Sizes: 1 <= order <= 8; L a power of two with 1024 <= L <= 2^20 (the causal sizes of hyena_operator);
+ * block a power of two, 1 <= block <= L (block == L: no prefix convolution at all).  Activations are fp32. */
+int hyena_decode_state_bytes(int order, int64_t B, int64_t D, int64_t L, size_t *bytes);
+
+/* Clears the histories of a state buffer (enqueued on `stream`). */
+int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void *state, size_t state_bytes,
+                       hipStream_t stream);
+
+/* Token t of the sequence for every (b, d) row.  v_t, x_t[i] (i = 0..order-1, x_t[0] = x_1) and y_t: fp32
+ * [B, D] (index b*D + d).  taps[i]: fp32 [D, L], the time-domain filter of order i as hyena_filter_gen's
+ * h_time (only its first `block` taps per channel are read); spectra[i]: that order's spectrum from
+ * hyena_filter_gen (causal, same L and D).  y_t must not overlap the inputs or the state; the inputs
+ * must not overlap the state.  HYENA_EINVAL for t outside [0, L); HYENA_EWORKSPACE for a state that is
+ * too small or misaligned. */
+int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, const float *v_t,
+                      const float *const *x_t, const float *const *taps, const void *const *spectra, float *y_t,
+                      void *state, size_t state_bytes, hipStream_t stream);
+
 /* Testing aid: the engine-ordered spectrum as natural-order DFT bins of the filter, complex64:
  * causal H[D, L+1] (bins of the 2L-point transform of the zero-padded taps), periodic H[D, L/2+1]
  * (bins of the L-point transform of the taps), 3-D H[D, 2nx, 2ny, nz+1] (zero-padded) or

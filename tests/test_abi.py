@@ -209,6 +209,42 @@ def test_projection_rejects_before_launch(lib):
     assert lib.hyena_projection(2, 2, 256, 64, 32, L.BF16, x, W, None, ox, None) == L.EALIAS
 
 
+def test_decode_sizes_and_rejects_before_launch(lib):
+    n = ctypes.c_size_t()
+    # histories and prefix contributions, fp32, two planes per order; no workspace below 32768 points
+    assert lib.hyena_decode_state_bytes(2, 4, 768, 8192, ctypes.byref(n)) == L.OK
+    assert n.value == 2 * 2 * 4 * 768 * 8192 * 4
+    assert lib.hyena_decode_state_bytes(2, 1, 256, 1 << 20, ctypes.byref(n)) == L.OK
+    assert n.value > 2 * 2 * 256 * (1 << 20) * 4            # plus the multi-pass workspace
+    assert lib.hyena_decode_state_bytes(0, 1, 8, 8192, ctypes.byref(n)) == L.EINVAL
+    assert lib.hyena_decode_state_bytes(9, 1, 8, 8192, ctypes.byref(n)) == L.EUNSUPPORTED
+    assert lib.hyena_decode_state_bytes(2, 1, 8, 3000, ctypes.byref(n)) == L.EUNSUPPORTED
+    assert lib.hyena_decode_state_bytes(2, 1, 8, 512, ctypes.byref(n)) == L.EUNSUPPORTED
+    assert lib.hyena_decode_state_bytes(2, 1, 8, 8192, None) == L.EINVAL
+    B, D, Lq, order = 2, 8, 1024, 2
+    assert lib.hyena_decode_state_bytes(order, B, D, Lq, ctypes.byref(n)) == L.OK
+    need = n.value
+    state = 1 << 40
+    v, y = 1 << 41, 1 << 42
+    xs = (ctypes.c_void_p * 2)(1 << 43, 1 << 44)
+    taps = (ctypes.c_void_p * 2)(1 << 45, 1 << 46)
+    sp = (ctypes.c_void_p * 2)(1 << 47, 3 << 46)
+
+    def step(t=5, block=64, st=state, nbytes=need, yy=y, vv=v, x=xs):
+        return lib.hyena_decode_step(order, B, D, Lq, block, t, vv, x, taps, sp, yy, st, nbytes, None)
+    assert step(t=-1) == L.EINVAL and step(t=Lq) == L.EINVAL
+    assert step(block=48) == L.EUNSUPPORTED and step(block=2 * Lq) == L.EUNSUPPORTED
+    assert step(nbytes=need - 1) == L.EWORKSPACE
+    assert step(st=state + 16) == L.EWORKSPACE                 # not 256-byte aligned
+    assert step(st=None) == L.EINVAL and step(yy=None) == L.EINVAL
+    assert step(x=(ctypes.c_void_p * 2)(1 << 43, None)) == L.EINVAL
+    assert step(yy=state + 4096) == L.EALIAS                    # output inside the state
+    assert step(yy=v + 4) == L.EALIAS                           # output overlapping an input
+    assert step(vv=state + 256) == L.EALIAS                     # input inside the state
+    assert lib.hyena_decode_reset(order, B, D, Lq, state, need - 1, None) == L.EWORKSPACE
+    assert lib.hyena_decode_reset(order, B, D, Lq, None, need, None) == L.EINVAL
+
+
 def test_binding_rejects_wrong_dtypes_before_calling():
     import torch
     p = {k: torch.zeros(4, dtype=torch.float64) for k in ("W1", "b1", "W2", "b2", "alpha")}

@@ -39,10 +39,11 @@ def test_bf16_matches_torch_conversion():
 
 
 def test_workloads_table():
-    assert [w.order for w in hi.WORKLOADS] == [2, 2, 3, 2, 2, 2, 2, 2, 2]
-    assert [w.mode for w in hi.WORKLOADS] == ["causal"] * 4 + ["linear", "circular", "circular", "linear", "causal"]
-    assert [w.filter for w in hi.WORKLOADS] == ["exp"] * 7 + ["film", "exp"]
-    assert [w.d_model for w in hi.WORKLOADS] == [0] * 8 + [768]
+    assert [w.order for w in hi.WORKLOADS] == [2, 2, 3, 2, 2, 2, 2, 2, 2, 2]
+    assert [w.mode for w in hi.WORKLOADS] == ["causal"] * 4 + ["linear", "circular", "circular", "linear", "causal", "causal"]
+    assert [w.filter for w in hi.WORKLOADS] == ["exp"] * 7 + ["film", "exp", "exp"]
+    assert [w.d_model for w in hi.WORKLOADS] == [0] * 8 + [768, 0]
+    assert [w.decode_block for w in hi.WORKLOADS] == [0] * 9 + [256]
     assert hi.WORKLOADS[1].tokens_channels == 4 * 768 * 8192
     assert hi.WORKLOADS[3].dims == (1 << 20,)
     assert hi.WORKLOADS[4].support == 127 ** 3
