@@ -622,8 +622,6 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
     return HYENA_EALIAS;
   for (int i = 0; i < order; ++i)
     if (overlaps(y_t, tok, x_t[i], tok) || overlaps(x_t[i], tok, state, need)) return HYENA_EALIAS;
-  Twiddles tw;
-  if ((st = get_twiddles(&tw))) return st;
   float* hist = (float*)state;
   const size_t plane = (size_t)rows * (size_t)L;
   float* fut = hist + (size_t)order * plane;
@@ -631,6 +629,8 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
   if (t > 0 && t0 == t) {
     // block boundary: the contribution of the whole stored prefix to every later position, by the FFT
     // convolution of each order's history row with that order's cached spectrum (no gate)
+    Twiddles tw;
+    if ((st = get_twiddles(&tw))) return st;
     const int lg = log2i(L);
     const size_t per = row_intermediate_bytes(K_CAUSAL, L);
     const int chunk = per ? (int)default_chunk_rows((int64_t)per, rows) : 0;

@@ -46,25 +46,32 @@ k_decode_step(const float* __restrict__ v_t, DecodePtrs x_t, DecodePtrs taps, fl
   const size_t rowL = (size_t)r * L;
   const size_t plane = (size_t)rows * L;
 
+  // everything the token needs besides the in-block history, requested before the sums
+  float xg[N], h0[N], pre[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    xg[i] = x_t.p[i][r];
+    h0[i] = taps.p[i][(size_t)d * L];
+    pre[i] = t0 > 0 ? fut[i * plane + rowL + t] : 0.0f;
+  }
+  float u = v_t[r];
+
   float acc[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+#pragma unroll 4
   for (int j = 1 + lane; j <= n; j += 64) {
 #pragma unroll
     for (int i = 0; i < N; ++i)
       acc[i] = fmaf(taps.p[i][(size_t)d * L + j], hist[i * plane + rowL + (t - j)], acc[i]);
   }
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    acc[i] = dec_wave_sum(acc[i]);
-    if (t0 > 0) acc[i] += fut[i * plane + rowL + t];
-  }
+  for (int i = 0; i < N; ++i) acc[i] = dec_wave_sum(acc[i]) + pre[i];
   // the chain through the orders: u_0 = v, u_i = x_i (S_i + h_i[0] u_{i-1})
-  float u = v_t[r];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     if (lane == 0) hist[i * plane + rowL + t] = u;        // u_{i-1}[t] joins order i's history
-    u = x_t.p[i][r] * fmaf(taps.p[i][(size_t)d * L], u, acc[i]);
+    u = xg[i] * fmaf(h0[i], u, acc[i]);
   }
   if (lane == 0) y_t[r] = u;
 }

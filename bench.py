@@ -12,6 +12,9 @@ FiLM-modulated SIREN taps of every (b, d) and their spectra, then the operator r
 that start from token-major inputs run the input projection (a matrix-core GEMM that writes v, x_1..x_N
 channel-major) before the operator in every step; the roofline object then reports the projection.
 
+The streaming-decode workload times one token of every (b, d) row per step (hyena_decode_step, with the
+FFT convolution of the stored prefix at each block start), over a whole sequence by default.
+
 Prints ONE JSON line.  Default workload: order 2, B=4, D=768, L=8192, bf16 storage (workload 1), whose
 convolution runs on the matrix cores;
 ``--workload i`` times another of hyena_inputs.WORKLOADS (parity configurations are not bench lines).
@@ -224,13 +227,163 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
     return 2 * nbytes / (ms / 1e3) / 1e9
 
 
+DECODE_METRIC = "Hyena streaming decode tokens·channels/s (one token of every (b, d) row per step), 1 GPU"
+
+
+def decode_bytes_per_launch(w, n_avg: float) -> float:
+    """Algorithmic bytes of one token-step launch: per row read v_t and the N gates, write y_t, append the
+    N inputs to the histories, read the N prefix contributions, and read n in-block history values per order;
+    per channel read n taps per order (shared by the B rows)."""
+    rows, N = w.B * w.D, w.order
+    return 4.0 * (rows * ((N + 1) + 1 + N + N) + N * n_avg * (rows + w.D))
+
+
+def cpu_baseline_decode(w, v, xs, params, budget_s: float):
+    """The oracle's token-by-token evaluation on whole rows of the same workload (batches of 8 rows, all L
+    tokens each), filters built outside the timed part, until about budget_s seconds of oracle time."""
+    from threadpoolctl import threadpool_limits
+    from oracle import hyena_oracle as orc
+    L = w.dims[0]
+    rows = hi.sample_rows(w, 4096, seed=99)
+    n_done, t_used = 0, 0.0
+    with threadpool_limits(1):
+        for k in range(0, len(rows), 8):
+            sel = rows[k:k + 8]
+            ds = [d for _, d in sel]
+            hs = [orc.implicit_filter_1d(p, L, channels=ds) for p in params]
+            t0 = time.perf_counter()
+            orc.hyena_decode_stream(np.stack([v[b, d] for b, d in sel]),
+                                    [np.stack([x[b, d] for b, d in sel]) for x in xs], hs)
+            t_used += time.perf_counter() - t0
+            n_done += len(sel)
+            print(f"cpu baseline (decode): {n_done} rows, {t_used:.1f} s", file=sys.stderr, flush=True)
+            if t_used >= budget_s:
+                break
+    return {"value": n_done * L / t_used, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_done} of {w.B * w.D} (b,d) rows of the same workload decoded token by token over all "
+                      f"{L} positions (float64 numpy, direct causal sums, one core), filters prebuilt; "
+                      f"{t_used:.1f} s"}
+
+
+def run_decode(args, w, torch, hy, _lib):
+    """Streaming decode: a step is one token of every (b, d) row through hyena_decode_step, the prefix
+    convolutions of block starts included; step k decodes position k mod L of a sequence that restarts
+    (hyena_decode_reset, inside the step) at position 0."""
+    import ctypes
+    L, B, D, N = w.dims[0], w.B, w.D, w.order
+    block = args.decode_block or w.decode_block
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    pd = [{k: torch.from_numpy(a).to(dev) for k, a in p.items()} for p in params]
+    taps = [torch.empty((D, L), dtype=torch.float32, device=dev) for _ in pd]
+    spectra = [hy.filter_gen(p, (L,), h_time=h) for p, h in zip(pd, taps)]
+    # token-major inputs [L, B, D] resident in HBM; outputs likewise
+    vt = torch.from_numpy(np.ascontiguousarray(np.moveaxis(v, -1, 0))).to(dev)
+    xt = [torch.from_numpy(np.ascontiguousarray(np.moveaxis(x, -1, 0))).to(dev) for x in xs]
+    yt = torch.empty_like(vt)
+    nbytes = _lib.decode_state_bytes(N, B, D, L)
+    state = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    # argument marshalling done once: per-position pointer tables for the C call
+    lib = _lib.lib()
+    P = ctypes.c_void_p
+    tok = B * D * 4
+    ta = (P * N)(*[h.data_ptr() for h in taps])
+    sa = (P * N)(*[sp.data_ptr() for sp in spectra])
+    xa = [(P * N)(*[x.data_ptr() + t * tok for x in xt]) for t in range(L)]
+    vb, yb, sb, hs = vt.data_ptr(), yt.data_ptr(), state.data_ptr(), stream.cuda_stream
+
+    def step(k):
+        t = k % L
+        if t == 0:
+            st = lib.hyena_decode_reset(N, B, D, L, sb, nbytes, hs)
+            if st:
+                raise _lib.HyenaError(st, "hyena_decode_reset")
+        st = lib.hyena_decode_step(N, B, D, L, block, t, vb + t * tok, xa[t], ta, sa, yb + t * tok, sb, nbytes, hs)
+        if st:
+            raise _lib.HyenaError(st, "hyena_decode_step")
+
+    k = 0
+    for _ in range(args.warmup):
+        step(k)
+        k += 1
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step(k)
+        k += 1
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+    event_ms = ev0.elapsed_time(ev1) / args.steps
+
+    # the token kernel alone: the positions of one block after its start (no prefix convolution), launched
+    # back to back; and the prefix convolutions of one block start
+    kb = (k // L + 1) * L + block             # a block start of the next sequence, past position 0
+    while k < kb:
+        step(k)
+        k += 1
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
+    step(k)                                   # block start: prefix convolutions + token kernel
+    k += 1
+    e1.record(stream)
+    for _ in range(block - 1):
+        step(k)
+        k += 1
+    e2.record(stream)
+    torch.cuda.synchronize()
+    token_ms = e1.elapsed_time(e2) / (block - 1)
+    boundary_ms = e0.elapsed_time(e1)
+    n_avg = block / 2.0                       # in-block positions summed, averaged over the block
+    bytes_launch = decode_bytes_per_launch(w, n_avg)
+    achieved = bytes_launch / (token_ms / 1e3) / 1e9
+    rows = B * D
+    out = {
+        "metric": DECODE_METRIC,
+        "value": rows / (ms_per_step / 1e3),
+        "unit": "tokens·channels/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded activations, Xavier-uniform filter networks; see hyena_inputs)",
+        "config": {"workload": w.name, "order": N, "B": B, "D": D, "grid": [L], "boundary": "causal",
+                   "storage": "f32", "arithmetic": "fp32", "decode_block": block, "alpha_range": [w.alpha_lo, w.alpha_hi],
+                   "inputs": f"numpy default_rng([{w.index}, stream]): stream 0 activations, stream 1 filter parameters"},
+        "us_per_token_step": 1e3 * ms_per_step,
+        "event_ms_per_step": event_ms,
+        "token_kernel_ms": token_ms,
+        "block_start_ms": boundary_ms,
+        "state_bytes": nbytes,
+        "roofline": {"bound": "hbm", "kernel": f"k_decode_step<{N}> (one token of every row, launched back to back)",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None, "launch_ms": token_ms, "alg_bytes_per_launch": bytes_launch,
+                     "note": "a few MB per launch: the step is bound by launch and memory latency, not bandwidth"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w, v, xs, params, args.cpu_budget)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     # the GPU reaches steady-state clocks only under sustained load: 0.1 s of warm-up and timed work
     # (workload 1) measures that state; 50 steps after 5 read about 15 % slower
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=None, help="default 1000 (decode: one whole sequence, L tokens)")
+    ap.add_argument("--warmup", type=int, default=None, help="default 100 (decode: 512 tokens)")
     ap.add_argument("--workload", type=int, default=1, help="index into hyena_inputs.WORKLOADS")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -239,6 +392,8 @@ def main():
                     help="after the timed region, this many more steps, each after a scratch write that evicts the "
                          "256 MB memory-side cache, timed one by one (reported as cold_cache; 0 skips them)")
     ap.add_argument("--evict-mb", type=int, default=1024, help="size of that scratch write")
+    ap.add_argument("--decode-block", type=int, default=0, help="decode workloads: tokens per prefix block "
+                                                               "(0: the workload's own)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -252,6 +407,14 @@ def main():
     from attention_free_long_implicit_amd import _lib
 
     w = hi.WORKLOADS[args.workload]
+    if args.steps is None:
+        args.steps = w.dims[0] if w.decode_block else 1000
+    if args.warmup is None:
+        args.warmup = 512 if w.decode_block else 100
+    if w.decode_block:
+        out = run_decode(args, w, torch, hy, _lib)
+        print(json.dumps(out), flush=True)
+        return
     film = w.filter == "film"
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     v, xs = hi.draw_activations(w)
