@@ -69,7 +69,7 @@ _SIG = {
     "hyena_decode_state_bytes": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.POINTER(_c.c_size_t)]),
     "hyena_decode_reset": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_size_t,
                                       _c.c_void_p]),
-    "hyena_decode_step": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+    "hyena_decode_step": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                      _c.c_void_p, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p),
                                      _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
 }
@@ -341,19 +341,23 @@ def decode_reset(state, order: int, B: int, D: int, L: int):
 
 
 def decode_step(t: int, v_t, x_t: Sequence, taps: Sequence, spectra: Sequence, state, L: int, block: int, y_t=None):
-    """Token t of every (b, d) row: y_t [B, D] from v_t, x_t[i] [B, D] (float32); taps[i]: float32 [D, L]
-    (filter_gen's h_time), spectra[i] from filter_gen; state from decode_state_bytes / decode_reset."""
+    """Token t of every (b, d) row: y_t [B, D] from v_t, x_t[i] [B, D] (float32 or bfloat16, one dtype);
+    taps[i]: float32 [D, L] (filter_gen's h_time), spectra[i] from filter_gen; state from
+    decode_state_bytes / decode_reset."""
     torch = _torch()
     B, D = v_t.shape
     order = len(x_t)
     if len(taps) != order or len(spectra) != order:
         raise ValueError("need one tap row set and one spectrum per gate")
-    _require_f32("decode activations and taps", v_t, *x_t, *taps)
+    _require_f32("decode taps", *taps)
+    dt = _dtype_code(v_t)
     if y_t is None:
         y_t = torch.empty_like(v_t)
+    if any(x.dtype != v_t.dtype for x in x_t) or y_t.dtype != v_t.dtype:
+        raise ValueError("v_t, x_t and y_t must share one dtype")
     xa = (ctypes.c_void_p * order)(*[_ptr(x) for x in x_t])
     ta = (ctypes.c_void_p * order)(*[_ptr(h) for h in taps])
     sa = (ctypes.c_void_p * order)(*[_ptr(sp) for sp in spectra])
-    _check(lib().hyena_decode_step(order, B, D, L, block, t, _ptr(v_t), xa, ta, sa, _ptr(y_t), _ptr(state),
+    _check(lib().hyena_decode_step(order, B, D, L, block, t, dt, _ptr(v_t), xa, ta, sa, _ptr(y_t), _ptr(state),
                                    state.numel(), _stream(v_t)), "hyena_decode_step")
     return y_t

@@ -603,13 +603,14 @@ int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void* state, 
   return hip_status(hipMemsetAsync(state, 0, (size_t)order * decode_plane_bytes(rows, L), stream));
 }
 
-int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, const float* v_t,
-                      const float* const* x_t, const float* const* taps, const void* const* spectra, float* y_t,
-                      void* state, size_t state_bytes, hipStream_t stream) {
+int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, int dtype,
+                      const void* v_t, const void* const* x_t, const float* const* taps, const void* const* spectra,
+                      void* y_t, void* state, size_t state_bytes, hipStream_t stream) {
   int64_t rows = 0;
   int st = decode_check(order, B, D, L, &rows);
   if (st) return st;
   if (!v_t || !x_t || !taps || !spectra || !y_t || !state) return HYENA_EINVAL;
+  if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_EINVAL;
   for (int i = 0; i < order; ++i)
     if (!x_t[i] || !taps[i] || !spectra[i]) return HYENA_EINVAL;
   if (t < 0 || t >= L) return HYENA_EINVAL;
@@ -617,7 +618,7 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
   size_t need = 0;
   hyena_decode_state_bytes(order, B, D, L, &need);
   if (((size_t)state & 255u) || state_bytes < need) return HYENA_EWORKSPACE;
-  const size_t tok = (size_t)rows * sizeof(float);
+  const size_t tok = (size_t)rows * elem_bytes(dtype);
   if (overlaps(y_t, tok, state, need) || overlaps(y_t, tok, v_t, tok) || overlaps(v_t, tok, state, need))
     return HYENA_EALIAS;
   for (int i = 0; i < order; ++i)
@@ -650,8 +651,8 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
       if (st) return st;
     }
   }
-  return hip_status(launch_decode_step(order, v_t, x_t, taps, hist, fut, y_t, (int)rows, (int)D, (int)L, (int)t,
-                                       (int)t0, stream));
+  return hip_status(launch_decode_step(order, dtype == HYENA_BF16, v_t, x_t, taps, hist, fut, y_t, (int)rows, (int)D,
+                                       (int)L, (int)t, (int)t0, stream));
 }
 
 int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spectrum, void* H, hipStream_t stream) {

@@ -26,6 +26,16 @@ namespace {
 struct DecodePtrs {
   const float* p[kDecodeMaxOrder];
 };
+struct DecodeTok {
+  const void* p[kDecodeMaxOrder];
+};
+
+// one token value of row r: fp32, or bf16 widened exactly
+template <bool BF16>
+__device__ __forceinline__ float dec_load(const void* p, int r) {
+  if constexpr (BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[r]);
+  else return static_cast<const float*>(p)[r];
+}
 
 __device__ __forceinline__ float dec_wave_sum(float v) {
 #pragma unroll
@@ -33,11 +43,12 @@ __device__ __forceinline__ float dec_wave_sum(float v) {
   return v;
 }
 
-// hist, fut: [N][rows][L] fp32 (history of u_{i-1}, prefix contributions); taps[i]: [D][L] fp32.
-template <int N>
+// hist, fut: [N][rows][L] fp32 (history of u_{i-1}, prefix contributions); taps[i]: [D][L] fp32.  With bf16
+// tokens the intermediate u_i (i < N) is rounded to bf16 before it is used, as a stored intermediate is.
+template <int N, bool BF16>
 __global__ void __launch_bounds__(256)
-k_decode_step(const float* __restrict__ v_t, DecodePtrs x_t, DecodePtrs taps, float* hist,
-              const float* __restrict__ fut, float* __restrict__ y_t, int rows, int D, int L, int t, int t0) {
+k_decode_step(const void* __restrict__ v_t, DecodeTok x_t, DecodePtrs taps, float* hist,
+              const float* __restrict__ fut, void* __restrict__ y_t, int rows, int D, int L, int t, int t0) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;                                  // uniform per wave
@@ -50,11 +61,11 @@ k_decode_step(const float* __restrict__ v_t, DecodePtrs x_t, DecodePtrs taps, fl
   float xg[N], h0[N], pre[N];
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    xg[i] = x_t.p[i][r];
+    xg[i] = dec_load<BF16>(x_t.p[i], r);
     h0[i] = taps.p[i][(size_t)d * L];
     pre[i] = t0 > 0 ? fut[i * plane + rowL + t] : 0.0f;
   }
-  float u = v_t[r];
+  float u = dec_load<BF16>(v_t, r);
 
   float acc[N];
 #pragma unroll
@@ -72,24 +83,35 @@ k_decode_step(const float* __restrict__ v_t, DecodePtrs x_t, DecodePtrs taps, fl
   for (int i = 0; i < N; ++i) {
     if (lane == 0) hist[i * plane + rowL + t] = u;        // u_{i-1}[t] joins order i's history
     u = xg[i] * fmaf(h0[i], u, acc[i]);
+    if constexpr (BF16)
+      if (i + 1 < N) u = bf16_to_f32(f32_to_bf16_rne(u));
   }
-  if (lane == 0) y_t[r] = u;
+  if (lane == 0) {
+    if constexpr (BF16) static_cast<uint16_t*>(y_t)[r] = f32_to_bf16_rne(u);
+    else static_cast<float*>(y_t)[r] = u;
+  }
 }
 
 }  // namespace
 
-hipError_t launch_decode_step(int order, const float* v_t, const float* const* x_t, const float* const* taps,
-                              float* hist, const float* fut, float* y_t, int rows, int D, int L, int t, int t0,
-                              hipStream_t s) {
-  DecodePtrs xp{}, tp{};
+hipError_t launch_decode_step(int order, int bf16, const void* v_t, const void* const* x_t,
+                              const float* const* taps, float* hist, const float* fut, void* y_t, int rows, int D,
+                              int L, int t, int t0, hipStream_t s) {
+  DecodeTok xp{};
+  DecodePtrs tp{};
   for (int i = 0; i < order; ++i) {
     xp.p[i] = x_t[i];
     tp.p[i] = taps[i];
   }
   const dim3 grid((rows + 3) / 4), block(256);
   switch (order) {
-#define X(n) \
-  case n: hipLaunchKernelGGL(k_decode_step<n>, grid, block, 0, s, v_t, xp, tp, hist, fut, y_t, rows, D, L, t, t0); break;
+#define X(n)                                                                                                     \
+  case n:                                                                                                        \
+    if (bf16) hipLaunchKernelGGL((k_decode_step<n, true>), grid, block, 0, s, v_t, xp, tp, hist, fut, y_t, rows, D, L, \
+                                 t, t0);                                                                        \
+    else hipLaunchKernelGGL((k_decode_step<n, false>), grid, block, 0, s, v_t, xp, tp, hist, fut, y_t, rows, D, L, \
+                            t, t0);                                                                            \
+    break;
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
 #undef X
     default: return hipErrorInvalidValue;

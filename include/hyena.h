@@ -189,22 +189,24 @@ int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D
  * not run concurrently.
  *
  * Sizes: 1 <= order <= 8; L a power of two with 1024 <= L <= 2^20 (the causal sizes of hyena_operator);
- * block a power of two, 1 <= block <= L (block == L: no prefix convolution at all).  Activations are fp32. */
+ * block a power of two, 1 <= block <= L (block == L: no prefix convolution at all).  Tokens are fp32 or bf16
+ * (dtype); the state is fp32 either way.  With bf16 tokens each intermediate u_i (i < order) is rounded to
+ * bf16 before it is used, as hyena_operator rounds a stored intermediate. */
 int hyena_decode_state_bytes(int order, int64_t B, int64_t D, int64_t L, size_t *bytes);
 
 /* Clears the histories of a state buffer (enqueued on `stream`). */
 int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void *state, size_t state_bytes,
                        hipStream_t stream);
 
-/* Token t of the sequence for every (b, d) row.  v_t, x_t[i] (i = 0..order-1, x_t[0] = x_1) and y_t: fp32
- * [B, D] (index b*D + d).  taps[i]: fp32 [D, L], the time-domain filter of order i as hyena_filter_gen's
+/* Token t of the sequence for every (b, d) row.  v_t, x_t[i] (i = 0..order-1, x_t[0] = x_1) and y_t: [B, D]
+ * of dtype (index b*D + d; bf16 stores round to nearest even).  taps[i]: fp32 [D, L], the time-domain filter of order i as hyena_filter_gen's
  * h_time (only its first `block` taps per channel are read); spectra[i]: that order's spectrum from
  * hyena_filter_gen (causal, same L and D).  y_t must not overlap the inputs or the state; the inputs
  * must not overlap the state.  HYENA_EINVAL for t outside [0, L); HYENA_EWORKSPACE for a state that is
  * too small or misaligned. */
-int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, const float *v_t,
-                      const float *const *x_t, const float *const *taps, const void *const *spectra, float *y_t,
-                      void *state, size_t state_bytes, hipStream_t stream);
+int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, int dtype,
+                      const void *v_t, const void *const *x_t, const float *const *taps, const void *const *spectra,
+                      void *y_t, void *state, size_t state_bytes, hipStream_t stream);
 
 /* Testing aid: the engine-ordered spectrum as natural-order DFT bins of the filter, complex64:
  * causal H[D, L+1] (bins of the 2L-point transform of the zero-padded taps), periodic H[D, L/2+1]

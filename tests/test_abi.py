@@ -230,9 +230,9 @@ def test_decode_sizes_and_rejects_before_launch(lib):
     taps = (ctypes.c_void_p * 2)(1 << 45, 1 << 46)
     sp = (ctypes.c_void_p * 2)(1 << 47, 3 << 46)
 
-    def step(t=5, block=64, st=state, nbytes=need, yy=y, vv=v, x=xs):
-        return lib.hyena_decode_step(order, B, D, Lq, block, t, vv, x, taps, sp, yy, st, nbytes, None)
-    assert step(t=-1) == L.EINVAL and step(t=Lq) == L.EINVAL
+    def step(t=5, block=64, st=state, nbytes=need, yy=y, vv=v, x=xs, dtype=L.F32):
+        return lib.hyena_decode_step(order, B, D, Lq, block, t, dtype, vv, x, taps, sp, yy, st, nbytes, None)
+    assert step(t=-1) == L.EINVAL and step(t=Lq) == L.EINVAL and step(dtype=7) == L.EINVAL
     assert step(block=48) == L.EUNSUPPORTED and step(block=2 * Lq) == L.EUNSUPPORTED
     assert step(nbytes=need - 1) == L.EWORKSPACE
     assert step(st=state + 16) == L.EWORKSPACE                 # not 256-byte aligned
@@ -240,6 +240,7 @@ def test_decode_sizes_and_rejects_before_launch(lib):
     assert step(x=(ctypes.c_void_p * 2)(1 << 43, None)) == L.EINVAL
     assert step(yy=state + 4096) == L.EALIAS                    # output inside the state
     assert step(yy=v + 4) == L.EALIAS                           # output overlapping an input
+    assert step(yy=v + 2 * B * D - 2, dtype=L.BF16) == L.EALIAS  # bf16 tokens: 2 bytes per row
     assert step(vv=state + 256) == L.EALIAS                     # input inside the state
     assert lib.hyena_decode_reset(order, B, D, Lq, state, need - 1, None) == L.EWORKSPACE
     assert lib.hyena_decode_reset(order, B, D, Lq, None, need, None) == L.EINVAL

@@ -6,7 +6,7 @@ import pytest
 
 import hyena_inputs as hi
 from oracle import hyena_oracle as orc
-from gpu_util import FP32_TOL, params_to_dev, rel_err_rows, say, to_dev
+from gpu_util import BF16_TOL, FP32_TOL, params_to_dev, rel_err_rows, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -32,8 +32,9 @@ def _decode(torch, w, v, xs, taps, spectra, block, state=None):
     """All L tokens of [B, D, L] inputs through the decode entry points; y as float64 [B, D, L]."""
     import attention_free_long_implicit_amd as hy
     B, D, L, order = w.B, w.D, w.dims[0], len(xs)
-    vt = to_dev(np.moveaxis(v, -1, 0), torch.float32)                 # token-major [L, B, D]
-    xt = [to_dev(np.moveaxis(x, -1, 0), torch.float32) for x in xs]
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    vt = to_dev(np.moveaxis(v, -1, 0), dt)                            # token-major [L, B, D]
+    xt = [to_dev(np.moveaxis(x, -1, 0), dt) for x in xs]
     yt = torch.empty_like(vt)
     if state is None:
         state = torch.empty(hy.decode_state_bytes(order, B, D, L), dtype=torch.uint8, device="cuda")
@@ -41,7 +42,7 @@ def _decode(torch, w, v, xs, taps, spectra, block, state=None):
     for t in range(L):
         hy.decode_step(t, vt[t], [x[t] for x in xt], taps, spectra, state, L, block, y_t=yt[t])
     torch.cuda.synchronize()
-    return np.moveaxis(yt.cpu().numpy().astype(np.float64), 0, -1)
+    return np.moveaxis(yt.float().cpu().numpy().astype(np.float64), 0, -1)
 
 
 def _rows(a):
@@ -125,3 +126,49 @@ def test_decode_state_reuse_after_reset(torch_cuda):
     again = _decode(torch, w, v2, xs2, taps, spectra, 128, state=state)
     fresh = _decode(torch, w, v2, xs2, taps, spectra, 128)
     np.testing.assert_array_equal(again, fresh)
+
+
+@pytest.mark.parametrize("order,B,D,L,block", [(2, 2, 8, 1024, 64), (3, 1, 4, 2048, 128)])
+def test_decode_bf16_tokens_match_oracle(torch_cuda, order, B, D, L, block):
+    """bf16 tokens (inputs rounded to bf16 once, as both sides see them; intermediates rounded like
+    stored ones on the GPU, not in the oracle)."""
+    torch = torch_cuda
+    w = hi.WORKLOADS[9].with_(order=order, B=B, D=D, dims=(L,), dtype="bf16")
+    v, xs = hi.draw_activations(w, seed=L + block + 1)
+    params = hi.draw_filter_params(w, seed=L + block + 1)
+    say(f"decode bf16 order={order} B={B} D={D} L={L} block={block}")
+    taps, spectra = _filters(torch, w, params)
+    y = _decode(torch, w, v, xs, taps, spectra, block)
+    hs = [np.tile(orc.implicit_filter_1d(p, L), (B, 1)) for p in params]
+    ref = orc.hyena_decode_stream(_rows(v), [_rows(x) for x in xs], hs)
+    e = rel_err_rows(_rows(y), ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < BF16_TOL, e.max()
+
+
+def test_decode_bf16_layer_of_workload_1(torch_cuda):
+    """The layer of workload 1 (B = 4, D = 768, L = 8192, bf16) decoded token by token: sampled rows against
+    the oracle, every row against the whole-sequence bf16 operator (matrix-core path)."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[1].with_(decode_block=256)
+    L = w.dims[0]
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    say(f"decode bf16 {w.name}")
+    taps, spectra = _filters(torch, w, params)
+    y = _decode(torch, w, v, xs, taps, spectra, w.decode_block)
+    rows = [(0, 0), (1, 77), (3, 767)]
+    sel = [b * w.D + d for b, d in rows]
+    hs = [orc.implicit_filter_1d(p, L, channels=[d for _, d in rows]) for p in params]
+    ref = orc.hyena_decode_stream(_rows(v)[sel], [_rows(x)[sel] for x in xs], hs)
+    e = rel_err_rows(_rows(y)[sel], ref)
+    say(f"  sampled rows: max rel err {e.max():.3e}")
+    assert e.max() < BF16_TOL, e.max()
+    whole = hy.operator(to_dev(v, torch.bfloat16), [to_dev(x, torch.bfloat16) for x in xs], spectra)
+    torch.cuda.synchronize()
+    e2 = rel_err_rows(_rows(y), _rows(whole.float().cpu().numpy().astype(np.float64)))
+    say(f"  every row vs the whole-sequence operator: max rel diff {e2.max():.3e}")
+    # each path is held to BF16_TOL against the oracle (the operator's matrix-core transforms round their
+    # operands to bf16 and carry most of it), so their difference is bounded by the sum
+    assert e2.max() < 2 * BF16_TOL, e2.max()
