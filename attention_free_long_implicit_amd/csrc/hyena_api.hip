@@ -621,8 +621,16 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
   const size_t tok = (size_t)rows * elem_bytes(dtype);
   if (overlaps(y_t, tok, state, need) || overlaps(y_t, tok, v_t, tok) || overlaps(v_t, tok, state, need))
     return HYENA_EALIAS;
+  hyena_dims dims{};
+  dims.ndim = 1;
+  dims.n[0] = L;
+  size_t spb = 0;
+  if ((st = hyena_spectrum_bytes(dims, HYENA_CAUSAL, D, &spb))) return st;
+  const size_t tapb = (size_t)D * (size_t)L * sizeof(float);
   for (int i = 0; i < order; ++i)
-    if (overlaps(y_t, tok, x_t[i], tok) || overlaps(x_t[i], tok, state, need)) return HYENA_EALIAS;
+    if (overlaps(y_t, tok, x_t[i], tok) || overlaps(x_t[i], tok, state, need) || overlaps(taps[i], tapb, state, need) ||
+        overlaps(spectra[i], spb, state, need) || overlaps(y_t, tok, taps[i], tapb) || overlaps(y_t, tok, spectra[i], spb))
+      return HYENA_EALIAS;
   float* hist = (float*)state;
   const size_t plane = (size_t)rows * (size_t)L;
   float* fut = hist + (size_t)order * plane;

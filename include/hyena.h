@@ -201,8 +201,8 @@ int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void *state, 
 /* Token t of the sequence for every (b, d) row.  v_t, x_t[i] (i = 0..order-1, x_t[0] = x_1) and y_t: [B, D]
  * of dtype (index b*D + d; bf16 stores round to nearest even).  taps[i]: fp32 [D, L], the time-domain filter of order i as hyena_filter_gen's
  * h_time (only its first `block` taps per channel are read); spectra[i]: that order's spectrum from
- * hyena_filter_gen (causal, same L and D).  y_t must not overlap the inputs or the state; the inputs
- * must not overlap the state.  HYENA_EINVAL for t outside [0, L); HYENA_EWORKSPACE for a state that is
+ * hyena_filter_gen (causal, same L and D).  y_t must not overlap the inputs, taps, spectra or the state;
+ * none of those may overlap the state.  HYENA_EINVAL for t outside [0, L); HYENA_EWORKSPACE for a state that is
  * too small or misaligned. */
 int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, int dtype,
                       const void *v_t, const void *const *x_t, const float *const *taps, const void *const *spectra,

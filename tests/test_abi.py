@@ -242,6 +242,10 @@ def test_decode_sizes_and_rejects_before_launch(lib):
     assert step(yy=v + 4) == L.EALIAS                           # output overlapping an input
     assert step(yy=v + 2 * B * D - 2, dtype=L.BF16) == L.EALIAS  # bf16 tokens: 2 bytes per row
     assert step(vv=state + 256) == L.EALIAS                     # input inside the state
+    assert lib.hyena_decode_step(order, B, D, Lq, 64, 5, L.F32, v, xs, (ctypes.c_void_p * 2)(state + 512, 1 << 46),
+                                 sp, y, state, need, None) == L.EALIAS          # taps inside the state
+    assert lib.hyena_decode_step(order, B, D, Lq, 64, 5, L.F32, v, xs, taps, (ctypes.c_void_p * 2)(1 << 47, y - 64),
+                                 y, state, need, None) == L.EALIAS              # output inside a spectrum
     assert lib.hyena_decode_reset(order, B, D, Lq, state, need - 1, None) == L.EWORKSPACE
     assert lib.hyena_decode_reset(order, B, D, Lq, None, need, None) == L.EINVAL
 
