@@ -1,0 +1,45 @@
+"""Host logic of bench.py (no GPU): the one-GPU refusal and the byte and flop models behind its roofline
+objects, checked against hand-counted values."""
+import json
+import os
+import subprocess
+import sys
+
+import hyena_inputs as hi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_algorithmic_bytes_of_the_headline_workload():
+    w = hi.WORKLOADS[1]
+    T = 4 * 768 * 8192
+    # one round trip per order (read u, read x_i, write u_i at 2 bytes) plus the fp32 taps of 768 channels
+    assert bench.algorithmic_bytes_per_order(w) == 3 * 2 * T + 4 * 768 * 8192
+    assert bench.algorithmic_bytes_per_order(w) * w.order == 352_321_536
+    # all orders fused: read v, x_1, x_2, write y, plus both orders' taps
+    assert bench.floor_bytes_per_step(w) == 4 * 2 * T + 2 * 4 * 768 * 8192
+    assert bench.uses_matrix_cores(w) and not bench.uses_matrix_cores(hi.WORKLOADS[5])
+
+
+def test_input_dependent_filters_count_one_filter_per_row():
+    w = hi.WORKLOADS[7]
+    assert bench.algorithmic_bytes_per_order(w) == 3 * 4 * 2 * 128 * 64 ** 3 + 4 * 2 * 128 * 127 ** 3
+
+
+def test_decode_bytes_per_launch():
+    w = hi.WORKLOADS[9]
+    rows, N, D = 4 * 768, 2, 768
+    # per row: v_t, x_1, x_2 (3 reads), y_t (1 write), 2 history appends, 2 prefix values; per order n
+    # history values per row and n taps per channel
+    want = 4 * (rows * (3 + 1 + 2 + 2) + N * 128 * (rows + D))
+    assert bench.decode_bytes_per_launch(w, 128) == want == 4_030_464
