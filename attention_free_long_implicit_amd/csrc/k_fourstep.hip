@@ -228,13 +228,13 @@ k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __r
     Row::first_input(t, i, s, n);
     const int k1 = k1_of(s);
     const typename In::T* src = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
-    const float2 wb = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
+    // W_M^{(n + m PER0) k1} for m = 0..R0-1 as a running product from W_M^{n k1} by W_M^{PER0 k1}
     const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
-    float2 wp[R0];
-    twiddle_powers<R0>(ws, wp);
+    float2 w = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     static_for<R0>([&](auto m) {
       const float2 v = In::ld(src + n + m.value * PER0);
-      x[i * R0 + m.value] = cmul(v, cmul(wb, wp[m.value]));
+      x[i * R0 + m.value] = cmul(v, w);
+      if constexpr (m.value + 1 < R0) w = cmul(w, ws);
     });
   });
   Row::template forward_to_last<false>(x, lds, tw, t);
@@ -288,12 +288,11 @@ k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __r
     Row::first_input(t, i, s, n);
     const int k1 = k1_of(s);
     typename In::T* dst = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
-    const float2 wb = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
-    float2 wp[R0];
-    twiddle_powers<R0>(ws, wp);
+    float2 w = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     static_for<R0>([&](auto m) {
-      In::st(dst + n + m.value * PER0, cmulc(x[i * R0 + m.value], cmul(wb, wp[m.value])));
+      In::st(dst + n + m.value * PER0, cmulc(x[i * R0 + m.value], w));
+      if constexpr (m.value + 1 < R0) w = cmul(w, ws);
     });
   });
 }
