@@ -4,11 +4,11 @@
     from attention_free_long_implicit_amd import filter_gen, fftconv, operator
 """
 from ._lib import (BF16, CAUSAL, CIRCULAR, F32, LINEAR, PER_SAMPLE, HyenaError, declared_symbols,  # noqa: F401
-                   decode_reset, decode_state_bytes, decode_step, fftconv, film_filter_gen,
+                   decode_prefill, decode_reset, decode_state_bytes, decode_step, fftconv, film_filter_gen,
                    film_filter_workspace_bytes, filter_gen, filter_workspace_bytes, lib, operator, projection,
                    spectrum_bytes, spectrum_export, status_str, workspace_bytes)
 
 __all__ = ["filter_gen", "fftconv", "operator", "spectrum_bytes", "workspace_bytes", "filter_workspace_bytes",
            "spectrum_export", "HyenaError", "lib", "declared_symbols", "F32", "BF16", "CAUSAL", "LINEAR",
            "CIRCULAR", "status_str", "film_filter_gen", "film_filter_workspace_bytes", "PER_SAMPLE", "projection",
-           "decode_state_bytes", "decode_reset", "decode_step"]
+           "decode_state_bytes", "decode_reset", "decode_step", "decode_prefill"]

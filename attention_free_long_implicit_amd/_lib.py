@@ -69,6 +69,9 @@ _SIG = {
     "hyena_decode_state_bytes": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.POINTER(_c.c_size_t)]),
     "hyena_decode_reset": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_size_t,
                                       _c.c_void_p]),
+    "hyena_decode_prefill": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
+                                        _c.c_int, _c.c_void_p, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p),
+                                        _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "hyena_decode_step": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
                                      _c.c_void_p, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p),
                                      _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -361,3 +364,23 @@ def decode_step(t: int, v_t, x_t: Sequence, taps: Sequence, spectra: Sequence, s
     _check(lib().hyena_decode_step(order, B, D, L, block, t, dt, _ptr(v_t), xa, ta, sa, _ptr(y_t), _ptr(state),
                                    state.numel(), _stream(v_t)), "hyena_decode_step")
     return y_t
+
+
+def decode_prefill(v, xs: Sequence, spectra: Sequence, state, L: int, block: int, y=None):
+    """The first P tokens at once (v, xs[i]: [B, D, P], P a multiple of block); returns y [B, D, P].  The next
+    call is decode_step at t = P."""
+    torch = _torch()
+    B, D, P = v.shape
+    order = len(xs)
+    if len(spectra) != order:
+        raise ValueError("need one spectrum per gate")
+    dt = _dtype_code(v)
+    if y is None:
+        y = torch.empty_like(v)
+    if any(x.dtype != v.dtype or x.shape != v.shape for x in xs) or y.dtype != v.dtype:
+        raise ValueError("v, xs and y must share one shape and dtype")
+    xa = (ctypes.c_void_p * order)(*[_ptr(x) for x in xs])
+    sa = (ctypes.c_void_p * order)(*[_ptr(sp) for sp in spectra])
+    _check(lib().hyena_decode_prefill(order, B, D, L, block, P, dt, _ptr(v), xa, sa, _ptr(y), _ptr(state),
+                                      state.numel(), _stream(v)), "hyena_decode_prefill")
+    return y

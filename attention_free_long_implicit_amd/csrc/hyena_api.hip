@@ -663,6 +663,59 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
                                        (int)L, (int)t, (int)t0, stream));
 }
 
+int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t P, int dtype,
+                         const void* v, const void* const* x, const void* const* spectra, void* y, void* state,
+                         size_t state_bytes, hipStream_t stream) {
+  int64_t rows = 0;
+  int st = decode_check(order, B, D, L, &rows);
+  if (st) return st;
+  if (!v || !x || !spectra || !y || !state) return HYENA_EINVAL;
+  for (int i = 0; i < order; ++i)
+    if (!x[i] || !spectra[i]) return HYENA_EINVAL;
+  if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_EINVAL;
+  if (!is_pow2(block) || block > L) return HYENA_EUNSUPPORTED;
+  if (P < 1 || P > L || P % block) return HYENA_EINVAL;
+  size_t need = 0;
+  hyena_decode_state_bytes(order, B, D, L, &need);
+  if (((size_t)state & 255u) || state_bytes < need) return HYENA_EWORKSPACE;
+  const size_t pb = (size_t)rows * (size_t)P * elem_bytes(dtype);
+  if (overlaps(y, pb, v, pb) || overlaps(y, pb, state, need) || overlaps(v, pb, state, need)) return HYENA_EALIAS;
+  for (int i = 0; i < order; ++i)
+    if (overlaps(y, pb, x[i], pb) || overlaps(x[i], pb, state, need)) return HYENA_EALIAS;
+  Twiddles tw;
+  if ((st = get_twiddles(&tw))) return st;
+  float* hist = (float*)state;
+  const size_t plane = (size_t)rows * (size_t)L;
+  float* fut = hist + (size_t)order * plane;
+  const int bf = dtype == HYENA_BF16;
+  const int lg = log2i(L);
+  const size_t per = row_intermediate_bytes(K_CAUSAL, L);
+  const int chunk = per ? (int)default_chunk_rows((int64_t)per, rows) : 0;
+  // the prompt through the orders on the whole-row FFT path, each order's input kept as its history
+  if ((st = hip_status(launch_decode_prefill(0, bf, v, nullptr, hist, nullptr, (int)rows, (int)L, (int)P, stream))))
+    return st;
+  for (int i = 0; i < order; ++i) {
+    float* h_i = hist + (size_t)i * plane;
+    const bool last = i + 1 == order;
+    float* c = last ? fut : hist + (size_t)(i + 1) * plane;   // the prefix contributions are rebuilt at t = P
+    if (chunk) {
+      const void* xs[1] = {nullptr};
+      const void* sp[1] = {spectra[i]};
+      st = hip_status(launch_conv1d_fourstep(lg, 0, 1, (int)B, (int)D, h_i, xs, sp, c,
+                                             (float2*)(fut + (size_t)order * plane), chunk, tw, device_mats(), stream,
+                                             0, 0));
+    } else {
+      st = hip_status(launch_conv1d_single(lg, 0, h_i, nullptr, c, (const float2*)spectra[i], (int)B, (int)D, tw,
+                                           stream, 0, 0));
+    }
+    if (st) return st;
+    if ((st = hip_status(launch_decode_prefill(1, bf, x[i], c, c, last ? y : nullptr, (int)rows, (int)L, (int)P,
+                                               stream))))
+      return st;
+  }
+  return HYENA_OK;
+}
+
 int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void* spectrum, void* H, hipStream_t stream) {
   if (D <= 0 || !spectrum || !H) return HYENA_EINVAL;
   bool ps = false;

@@ -92,7 +92,50 @@ k_decode_step(const void* __restrict__ v_t, DecodeTok x_t, DecodePtrs taps, floa
   }
 }
 
+// Prompt (prefill) staging, one element of a row per thread, rows of L: position t < P takes the prompt
+// value, t >= P is zero (the history past the last token is zero).  MODE 0: dst = v (the input of order
+// 1).  MODE 1: c holds the convolution of order i over its history; dst = x_i * c (the input of order
+// i + 1, rounded to bf16 with bf16 tokens), or, with y (the last order), y[b, d, t < P] = x_N * c.
+// a (v or x_i) and y: [rows][P] of the token type.
+template <int MODE, bool BF16>
+__global__ void __launch_bounds__(256)
+k_decode_prefill(const void* __restrict__ a, const float* c, float* dst, void* __restrict__ y, int L, int P) {
+  const int r = blockIdx.x;
+  const int t = blockIdx.y * 256 + threadIdx.x;
+  if (t >= L) return;
+  const size_t at = (size_t)r * L + t;
+  const size_t ap = (size_t)r * P + t;
+  float u = 0.0f;
+  if (t < P) {
+    const float in = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a)[ap]) : static_cast<const float*>(a)[ap];
+    u = MODE == 0 ? in : in * c[at];
+    if constexpr (BF16)
+      if (MODE == 1 && !y) u = bf16_to_f32(f32_to_bf16_rne(u));
+  }
+  if (MODE == 1 && y) {
+    if (t < P) {
+      if constexpr (BF16) static_cast<uint16_t*>(y)[ap] = f32_to_bf16_rne(u);
+      else static_cast<float*>(y)[ap] = u;
+    }
+    return;
+  }
+  dst[at] = u;
+}
+
 }  // namespace
+
+hipError_t launch_decode_prefill(int mode, int bf16, const void* a, const float* c, float* dst, void* y, int rows,
+                                 int L, int P, hipStream_t s) {
+  const dim3 grid(rows, (L + 255) / 256), block(256);
+  if (mode == 0) {
+    if (bf16) hipLaunchKernelGGL((k_decode_prefill<0, true>), grid, block, 0, s, a, c, dst, y, L, P);
+    else hipLaunchKernelGGL((k_decode_prefill<0, false>), grid, block, 0, s, a, c, dst, y, L, P);
+  } else {
+    if (bf16) hipLaunchKernelGGL((k_decode_prefill<1, true>), grid, block, 0, s, a, c, dst, y, L, P);
+    else hipLaunchKernelGGL((k_decode_prefill<1, false>), grid, block, 0, s, a, c, dst, y, L, P);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_decode_step(int order, int bf16, const void* v_t, const void* const* x_t,
                               const float* const* taps, float* hist, const float* fut, void* y_t, int rows, int D,

@@ -85,6 +85,10 @@ constexpr int kDecodeMaxOrder = 8;
 hipError_t launch_decode_step(int order, int bf16, const void* v_t, const void* const* x_t,
                               const float* const* taps, float* hist, const float* fut, void* y_t, int rows, int D,
                               int L, int t, int t0, hipStream_t s);
+// prompt staging for rows of L (positions >= P zero): mode 0 dst = v; mode 1 dst = x * c, or y = x * c when y
+// is not NULL (a and y: [rows][P] tokens; c, dst: [rows][L] fp32)
+hipError_t launch_decode_prefill(int mode, int bf16, const void* a, const float* c, float* dst, void* y, int rows,
+                                 int L, int P, hipStream_t s);
 
 // ---- input-dependent filters: FiLM-modulated SIREN with a Gaussian window, one filter per (b, d)
 constexpr int kFilmHidden = 64;     // SIREN units per layer

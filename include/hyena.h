@@ -208,6 +208,16 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
                       const void *v_t, const void *const *x_t, const float *const *taps, const void *const *spectra,
                       void *y_t, void *state, size_t state_bytes, hipStream_t stream);
 
+/* A prompt of P tokens in one pass (P a multiple of block, 1 <= P <= L), in place of hyena_decode_reset and
+ * the steps t = 0..P-1: v, x[i]: [B, D, P] of dtype (channel-major, like hyena_operator's inputs); y: [B, D, P]
+ * receives the operator's output on the prompt.  Each order runs the whole-row FFT convolution of its
+ * history (the prompt, zero after it) and stores its gated output as the next order's history, so the next
+ * call is hyena_decode_step at t = P, which starts a block.  spectra as for hyena_decode_step (no taps
+ * needed).  y must not overlap the inputs or the state; the inputs must not overlap the state. */
+int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t P, int dtype,
+                         const void *v, const void *const *x, const void *const *spectra, void *y, void *state,
+                         size_t state_bytes, hipStream_t stream);
+
 /* Testing aid: the engine-ordered spectrum as natural-order DFT bins of the filter, complex64:
  * causal H[D, L+1] (bins of the 2L-point transform of the zero-padded taps), periodic H[D, L/2+1]
  * (bins of the L-point transform of the taps), 3-D H[D, 2nx, 2ny, nz+1] (zero-padded) or

@@ -246,6 +246,12 @@ def test_decode_sizes_and_rejects_before_launch(lib):
                                  sp, y, state, need, None) == L.EALIAS          # taps inside the state
     assert lib.hyena_decode_step(order, B, D, Lq, 64, 5, L.F32, v, xs, taps, (ctypes.c_void_p * 2)(1 << 47, y - 64),
                                  y, state, need, None) == L.EALIAS              # output inside a spectrum
+    def prefill(P=128, block=64, st=state, yy=y, dtype=L.F32):
+        return lib.hyena_decode_prefill(order, B, D, Lq, block, P, dtype, v, xs, sp, yy, st, need, None)
+    assert prefill(P=100) == L.EINVAL and prefill(P=0) == L.EINVAL and prefill(P=2 * Lq) == L.EINVAL
+    assert prefill(block=3) == L.EUNSUPPORTED and prefill(dtype=9) == L.EINVAL
+    assert prefill(st=state + 8) == L.EWORKSPACE
+    assert prefill(yy=state + 1024) == L.EALIAS and prefill(yy=v + 8) == L.EALIAS
     assert lib.hyena_decode_reset(order, B, D, Lq, state, need - 1, None) == L.EWORKSPACE
     assert lib.hyena_decode_reset(order, B, D, Lq, None, need, None) == L.EINVAL
 

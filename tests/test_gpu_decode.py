@@ -172,3 +172,64 @@ def test_decode_bf16_layer_of_workload_1(torch_cuda):
     # each path is held to BF16_TOL against the oracle (the operator's matrix-core transforms round their
     # operands to bf16 and carry most of it), so their difference is bounded by the sum
     assert e2.max() < 2 * BF16_TOL, e2.max()
+
+
+@pytest.mark.parametrize("order,B,D,L,block,P,dtype", [
+    (2, 2, 8, 1024, 64, 512, "f32"),        # half the sequence as a prompt, the rest token by token
+    (3, 1, 4, 2048, 128, 384, "f32"),
+    (2, 2, 8, 1024, 64, 256, "bf16"),
+    (2, 1, 3, 1024, 256, 1024, "f32"),      # the whole sequence as a prompt
+])
+def test_decode_after_prefill_matches_oracle(torch_cuda, order, B, D, L, block, P, dtype):
+    """hyena_decode_prefill on the first P tokens, then hyena_decode_step for t = P..L-1: the joined outputs
+    against the oracle's token-by-token evaluation of the whole sequence."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[9].with_(order=order, B=B, D=D, dims=(L,), dtype=dtype)
+    v, xs = hi.draw_activations(w, seed=P + block)
+    params = hi.draw_filter_params(w, seed=P + block)
+    say(f"decode after prefill order={order} B={B} D={D} L={L} block={block} P={P} {dtype}")
+    taps, spectra = _filters(torch, w, params)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    state = torch.empty(hy.decode_state_bytes(order, B, D, L), dtype=torch.uint8, device="cuda")
+    state.fill_(255)                                   # prefill needs no reset: every history row is written
+    y_pre = hy.decode_prefill(to_dev(v[..., :P], dt), [to_dev(x[..., :P], dt) for x in xs], spectra, state, L, block)
+    vt = to_dev(np.moveaxis(v, -1, 0), dt)
+    xt = [to_dev(np.moveaxis(x, -1, 0), dt) for x in xs]
+    yt = torch.empty_like(vt)
+    for t in range(P, L):
+        hy.decode_step(t, vt[t], [x[t] for x in xt], taps, spectra, state, L, block, y_t=yt[t])
+    torch.cuda.synchronize()
+    y = np.concatenate([y_pre.float().cpu().numpy(), np.moveaxis(yt.float().cpu().numpy(), 0, -1)[..., P:]], axis=-1)
+    hs = [np.tile(orc.implicit_filter_1d(p, L), (B, 1)) for p in params]
+    ref = orc.hyena_decode_stream(_rows(v), [_rows(x) for x in xs], hs)
+    e = rel_err_rows(_rows(y.astype(np.float64)), ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < (BF16_TOL if dtype == "bf16" else FP32_TOL), e.max()
+
+
+def test_decode_after_prefill_multipass(torch_cuda):
+    """L = 32768: the prompt's convolutions and the later prefix convolutions on the multi-pass plan."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L, P, block = 32768, 28672, 4096
+    w = hi.WORKLOADS[9].with_(B=1, D=2, dims=(L,))
+    v, xs = hi.draw_activations(w, seed=21)
+    params = hi.draw_filter_params(w, seed=21)
+    say("decode after prefill L=32768 P=28672 block=4096")
+    taps, spectra = _filters(torch, w, params)
+    state = torch.empty(hy.decode_state_bytes(2, 1, 2, L), dtype=torch.uint8, device="cuda")
+    y_pre = hy.decode_prefill(to_dev(v[..., :P], torch.float32), [to_dev(x[..., :P], torch.float32) for x in xs],
+                              spectra, state, L, block)
+    vt = to_dev(np.moveaxis(v, -1, 0), torch.float32)
+    xt = [to_dev(np.moveaxis(x, -1, 0), torch.float32) for x in xs]
+    yt = torch.empty_like(vt)
+    for t in range(P, L):
+        hy.decode_step(t, vt[t], [x[t] for x in xt], taps, spectra, state, L, block, y_t=yt[t])
+    torch.cuda.synchronize()
+    y = np.concatenate([y_pre.cpu().numpy(), np.moveaxis(yt.cpu().numpy(), 0, -1)[..., P:]], axis=-1)
+    hs = [orc.implicit_filter_1d(p, L) for p in params]
+    ref = orc.hyena_operator_rows(_rows(v), [_rows(x) for x in xs], hs)      # pinned to the streaming form
+    e = rel_err_rows(_rows(y.astype(np.float64)), ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < FP32_TOL, e.max()
