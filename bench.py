@@ -343,6 +343,21 @@ def run_decode(args, w, torch, hy, _lib):
     torch.cuda.synchronize()
     token_ms = e1.elapsed_time(e2) / (block - 1)
     boundary_ms = e0.elapsed_time(e1)
+    # the prompt path for context: the whole sequence as one prompt (hyena_decode_prefill, P = L)
+    yp = torch.empty((B, D, L), dtype=torch.float32, device=dev)
+    vd = torch.from_numpy(v).to(dev)
+    xd = [torch.from_numpy(x).to(dev) for x in xs]
+    for _ in range(2):
+        hy.decode_prefill(vd, xd, spectra, state, L, block, y=yp)
+    e3, e4 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e3.record(stream)
+    for _ in range(5):
+        hy.decode_prefill(vd, xd, spectra, state, L, block, y=yp)
+    e4.record(stream)
+    torch.cuda.synchronize()
+    prefill_ms = e3.elapsed_time(e4) / 5
+    del yp, vd, xd
     n_avg = block / 2.0                       # in-block positions summed, averaged over the block
     bytes_launch = decode_bytes_per_launch(w, n_avg)
     achieved = bytes_launch / (token_ms / 1e3) / 1e9
@@ -367,6 +382,7 @@ def run_decode(args, w, torch, hy, _lib):
         "event_ms_per_step": event_ms,
         "token_kernel_ms": token_ms,
         "block_start_ms": boundary_ms,
+        "prefill_whole_sequence_ms": prefill_ms,
         "state_bytes": nbytes,
         "roofline": {"bound": "hbm", "kernel": f"k_decode_step<{N}> (one token of every row, launched back to back)",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
