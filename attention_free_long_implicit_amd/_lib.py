@@ -70,10 +70,10 @@ _SIG = {
     "hyena_decode_reset": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_void_p, _c.c_size_t,
                                       _c.c_void_p]),
     "hyena_decode_prefill": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64,
-                                        _c.c_int, _c.c_void_p, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p),
+                                        _c.c_int, _c.c_int, _c.c_void_p, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p),
                                         _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "hyena_decode_step": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int,
-                                     _c.c_void_p, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p),
+                                     _c.c_int, _c.c_void_p, _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p),
                                      _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_void_p]),
 }
 
@@ -343,10 +343,12 @@ def decode_reset(state, order: int, B: int, D: int, L: int):
     _check(lib().hyena_decode_reset(order, B, D, L, _ptr(state), state.numel(), _stream(state)), "hyena_decode_reset")
 
 
-def decode_step(t: int, v_t, x_t: Sequence, taps: Sequence, spectra: Sequence, state, L: int, block: int, y_t=None):
+def decode_step(t: int, v_t, x_t: Sequence, taps: Sequence, spectra: Sequence, state, L: int, block: int, y_t=None,
+                mode: int = CAUSAL):
     """Token t of every (b, d) row: y_t [B, D] from v_t, x_t[i] [B, D] (float32 or bfloat16, one dtype);
     taps[i]: float32 [D, L] (filter_gen's h_time), spectra[i] from filter_gen; state from
-    decode_state_bytes / decode_reset."""
+    decode_state_bytes / decode_reset.  mode CAUSAL | PER_SAMPLE: taps [B, D, L] and spectra from
+    film_filter_gen."""
     torch = _torch()
     B, D = v_t.shape
     order = len(x_t)
@@ -361,12 +363,12 @@ def decode_step(t: int, v_t, x_t: Sequence, taps: Sequence, spectra: Sequence, s
     xa = (ctypes.c_void_p * order)(*[_ptr(x) for x in x_t])
     ta = (ctypes.c_void_p * order)(*[_ptr(h) for h in taps])
     sa = (ctypes.c_void_p * order)(*[_ptr(sp) for sp in spectra])
-    _check(lib().hyena_decode_step(order, B, D, L, block, t, dt, _ptr(v_t), xa, ta, sa, _ptr(y_t), _ptr(state),
+    _check(lib().hyena_decode_step(order, B, D, L, block, t, dt, mode, _ptr(v_t), xa, ta, sa, _ptr(y_t), _ptr(state),
                                    state.numel(), _stream(v_t)), "hyena_decode_step")
     return y_t
 
 
-def decode_prefill(v, xs: Sequence, spectra: Sequence, state, L: int, block: int, y=None):
+def decode_prefill(v, xs: Sequence, spectra: Sequence, state, L: int, block: int, y=None, mode: int = CAUSAL):
     """The first P tokens at once (v, xs[i]: [B, D, P], P a multiple of block); returns y [B, D, P].  The next
     call is decode_step at t = P."""
     torch = _torch()
@@ -381,6 +383,6 @@ def decode_prefill(v, xs: Sequence, spectra: Sequence, state, L: int, block: int
         raise ValueError("v, xs and y must share one shape and dtype")
     xa = (ctypes.c_void_p * order)(*[_ptr(x) for x in xs])
     sa = (ctypes.c_void_p * order)(*[_ptr(sp) for sp in spectra])
-    _check(lib().hyena_decode_prefill(order, B, D, L, block, P, dt, _ptr(v), xa, sa, _ptr(y), _ptr(state),
+    _check(lib().hyena_decode_prefill(order, B, D, L, block, P, dt, mode, _ptr(v), xa, sa, _ptr(y), _ptr(state),
                                       state.numel(), _stream(v)), "hyena_decode_prefill")
     return y

@@ -603,12 +603,15 @@ int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void* state, 
   return hip_status(hipMemsetAsync(state, 0, (size_t)order * decode_plane_bytes(rows, L), stream));
 }
 
-int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, int dtype,
+int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, int dtype, int mode,
                       const void* v_t, const void* const* x_t, const float* const* taps, const void* const* spectra,
                       void* y_t, void* state, size_t state_bytes, hipStream_t stream) {
   int64_t rows = 0;
   int st = decode_check(order, B, D, L, &rows);
   if (st) return st;
+  bool ps = false;
+  if (split_mode(mode, &ps) != HYENA_CAUSAL) return HYENA_EUNSUPPORTED;
+  const int hsb = ps ? (int)D : 0;
   if (!v_t || !x_t || !taps || !spectra || !y_t || !state) return HYENA_EINVAL;
   if (dtype != HYENA_F32 && dtype != HYENA_BF16) return HYENA_EINVAL;
   for (int i = 0; i < order; ++i)
@@ -625,8 +628,8 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
   dims.ndim = 1;
   dims.n[0] = L;
   size_t spb = 0;
-  if ((st = hyena_spectrum_bytes(dims, HYENA_CAUSAL, D, &spb))) return st;
-  const size_t tapb = (size_t)D * (size_t)L * sizeof(float);
+  if ((st = hyena_spectrum_bytes(dims, mode, ps ? rows : D, &spb))) return st;
+  const size_t tapb = (size_t)(ps ? rows : D) * (size_t)L * sizeof(float);
   for (int i = 0; i < order; ++i)
     if (overlaps(y_t, tok, x_t[i], tok) || overlaps(x_t[i], tok, state, need) || overlaps(taps[i], tapb, state, need) ||
         overlaps(spectra[i], spb, state, need) || overlaps(y_t, tok, taps[i], tapb) || overlaps(y_t, tok, spectra[i], spb))
@@ -651,24 +654,27 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
         const void* sp[1] = {spectra[i]};
         st = hip_status(launch_conv1d_fourstep(lg, 0, 1, (int)B, (int)D, h_i, xs, sp, f_i,
                                                (float2*)(fut + (size_t)order * plane), chunk, tw, device_mats(),
-                                               stream, 0, 0));
+                                               stream, 0, hsb));
       } else {
         st = hip_status(launch_conv1d_single(lg, 0, h_i, nullptr, f_i, (const float2*)spectra[i], (int)B, (int)D, tw,
-                                             stream, 0, 0));
+                                             stream, 0, hsb));
       }
       if (st) return st;
     }
   }
   return hip_status(launch_decode_step(order, dtype == HYENA_BF16, v_t, x_t, taps, hist, fut, y_t, (int)rows, (int)D,
-                                       (int)L, (int)t, (int)t0, stream));
+                                       (int)L, (int)t, (int)t0, ps ? 1 : 0, stream));
 }
 
-int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t P, int dtype,
+int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t P, int dtype, int mode,
                          const void* v, const void* const* x, const void* const* spectra, void* y, void* state,
                          size_t state_bytes, hipStream_t stream) {
   int64_t rows = 0;
   int st = decode_check(order, B, D, L, &rows);
   if (st) return st;
+  bool ps = false;
+  if (split_mode(mode, &ps) != HYENA_CAUSAL) return HYENA_EUNSUPPORTED;
+  const int hsb = ps ? (int)D : 0;
   if (!v || !x || !spectra || !y || !state) return HYENA_EINVAL;
   for (int i = 0; i < order; ++i)
     if (!x[i] || !spectra[i]) return HYENA_EINVAL;
@@ -703,10 +709,10 @@ int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t blo
       const void* sp[1] = {spectra[i]};
       st = hip_status(launch_conv1d_fourstep(lg, 0, 1, (int)B, (int)D, h_i, xs, sp, c,
                                              (float2*)(fut + (size_t)order * plane), chunk, tw, device_mats(), stream,
-                                             0, 0));
+                                             0, hsb));
     } else {
       st = hip_status(launch_conv1d_single(lg, 0, h_i, nullptr, c, (const float2*)spectra[i], (int)B, (int)D, tw,
-                                           stream, 0, 0));
+                                           stream, 0, hsb));
     }
     if (st) return st;
     if ((st = hip_status(launch_decode_prefill(1, bf, x[i], c, c, last ? y : nullptr, (int)rows, (int)L, (int)P,

@@ -43,16 +43,18 @@ __device__ __forceinline__ float dec_wave_sum(float v) {
   return v;
 }
 
-// hist, fut: [N][rows][L] fp32 (history of u_{i-1}, prefix contributions); taps[i]: [D][L] fp32.  With bf16
+// hist, fut: [N][rows][L] fp32 (history of u_{i-1}, prefix contributions); taps[i]: [D][L] fp32, or
+// [rows][L] with per-sample filters.  With bf16
 // tokens the intermediate u_i (i < N) is rounded to bf16 before it is used, as a stored intermediate is.
 template <int N, bool BF16>
 __global__ void __launch_bounds__(256)
 k_decode_step(const void* __restrict__ v_t, DecodeTok x_t, DecodePtrs taps, float* hist,
-              const float* __restrict__ fut, void* __restrict__ y_t, int rows, int D, int L, int t, int t0) {
+              const float* __restrict__ fut, void* __restrict__ y_t, int rows, int D, int L, int t, int t0,
+              int per_sample) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;                                  // uniform per wave
-  const int d = r % D;
+  const int d = per_sample ? r : r % D;                   // tap row: one filter per channel, or per (b, d)
   const int n = t - t0;                                   // earlier positions of this block
   const size_t rowL = (size_t)r * L;
   const size_t plane = (size_t)rows * L;
@@ -139,7 +141,7 @@ hipError_t launch_decode_prefill(int mode, int bf16, const void* a, const float*
 
 hipError_t launch_decode_step(int order, int bf16, const void* v_t, const void* const* x_t,
                               const float* const* taps, float* hist, const float* fut, void* y_t, int rows, int D,
-                              int L, int t, int t0, hipStream_t s) {
+                              int L, int t, int t0, int per_sample, hipStream_t s) {
   DecodeTok xp{};
   DecodePtrs tp{};
   for (int i = 0; i < order; ++i) {
@@ -151,9 +153,9 @@ hipError_t launch_decode_step(int order, int bf16, const void* v_t, const void* 
 #define X(n)                                                                                                     \
   case n:                                                                                                        \
     if (bf16) hipLaunchKernelGGL((k_decode_step<n, true>), grid, block, 0, s, v_t, xp, tp, hist, fut, y_t, rows, D, L, \
-                                 t, t0);                                                                        \
+                                 t, t0, per_sample);                                                                        \
     else hipLaunchKernelGGL((k_decode_step<n, false>), grid, block, 0, s, v_t, xp, tp, hist, fut, y_t, rows, D, L, \
-                            t, t0);                                                                            \
+                            t, t0, per_sample);                                                                            \
     break;
     X(1) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
 #undef X

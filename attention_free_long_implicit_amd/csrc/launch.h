@@ -79,12 +79,12 @@ hipError_t launch_projection(int bf16, const void* x, const void* W, const float
 
 // ---- streaming decode: one token of every (b, d) row through all orders.  hist, fut: [order][rows][L]
 // fp32 (history of each order's input; contributions of the positions before t0, the start of t's
-// block); taps[i]: [D][L] fp32 (only the first t - t0 + 1 taps of a row are read); v_t, x_t[i], y_t: [rows]
-// of fp32 or (bf16 = 1) bf16.
+// block); taps[i]: [D][L] fp32, or [rows][L] with per_sample (only the first t - t0 + 1 taps of a row are
+// read); v_t, x_t[i], y_t: [rows] of fp32 or (bf16 = 1) bf16.
 constexpr int kDecodeMaxOrder = 8;
 hipError_t launch_decode_step(int order, int bf16, const void* v_t, const void* const* x_t,
                               const float* const* taps, float* hist, const float* fut, void* y_t, int rows, int D,
-                              int L, int t, int t0, hipStream_t s);
+                              int L, int t, int t0, int per_sample, hipStream_t s);
 // prompt staging for rows of L (positions >= P zero): mode 0 dst = v; mode 1 dst = x * c, or y = x * c when y
 // is not NULL (a and y: [rows][P] tokens; c, dst: [rows][L] fp32)
 hipError_t launch_decode_prefill(int mode, int bf16, const void* a, const float* c, float* dst, void* y, int rows,

@@ -302,7 +302,7 @@ def run_decode(args, w, torch, hy, _lib):
             st = lib.hyena_decode_reset(N, B, D, L, sb, nbytes, hs)
             if st:
                 raise _lib.HyenaError(st, "hyena_decode_reset")
-        st = lib.hyena_decode_step(N, B, D, L, block, t, _lib.F32, vb + t * tok, xa[t], ta, sa, yb + t * tok, sb,
+        st = lib.hyena_decode_step(N, B, D, L, block, t, _lib.F32, _lib.CAUSAL, vb + t * tok, xa[t], ta, sa, yb + t * tok, sb,
                                    nbytes, hs)
         if st:
             raise _lib.HyenaError(st, "hyena_decode_step")

@@ -190,7 +190,9 @@ int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D
  *
  * Sizes: 1 <= order <= 8; L a power of two with 1024 <= L <= 2^20 (the causal sizes of hyena_operator);
  * block a power of two, 1 <= block <= L (block == L: no prefix convolution at all).  Tokens are fp32 or bf16
- * (dtype); the state is fp32 either way.  With bf16 tokens each intermediate u_i (i < order) is rounded to
+ * (dtype); the state is fp32 either way.  mode: HYENA_CAUSAL, or HYENA_CAUSAL | HYENA_PER_SAMPLE for input-dependent
+ * filters (one per (b, d) from hyena_film_filter_gen: taps [B, D, L], spectra of B*D filters); other modes
+ * return HYENA_EUNSUPPORTED.  With bf16 tokens each intermediate u_i (i < order) is rounded to
  * bf16 before it is used, as hyena_operator rounds a stored intermediate. */
 int hyena_decode_state_bytes(int order, int64_t B, int64_t D, int64_t L, size_t *bytes);
 
@@ -199,12 +201,12 @@ int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void *state, 
                        hipStream_t stream);
 
 /* Token t of the sequence for every (b, d) row.  v_t, x_t[i] (i = 0..order-1, x_t[0] = x_1) and y_t: [B, D]
- * of dtype (index b*D + d; bf16 stores round to nearest even).  taps[i]: fp32 [D, L], the time-domain filter of order i as hyena_filter_gen's
- * h_time (only its first `block` taps per channel are read); spectra[i]: that order's spectrum from
- * hyena_filter_gen (causal, same L and D).  y_t must not overlap the inputs, taps, spectra or the state;
- * none of those may overlap the state.  HYENA_EINVAL for t outside [0, L); HYENA_EWORKSPACE for a state that is
- * too small or misaligned. */
-int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, int dtype,
+ * of dtype (index b*D + d; bf16 stores round to nearest even).  taps[i]: fp32 [D, L] (per sample: [B, D, L]),
+ * the time-domain filter of order i as the filter generator's h_time (only the first `block` taps of a
+ * row are read); spectra[i]: that order's spectrum from the same generator (causal, same L).  y_t must not
+ * overlap the inputs, taps, spectra or the state; none of those may overlap the state.  HYENA_EINVAL for t
+ * outside [0, L); HYENA_EWORKSPACE for a state that is too small or misaligned. */
+int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, int dtype, int mode,
                       const void *v_t, const void *const *x_t, const float *const *taps, const void *const *spectra,
                       void *y_t, void *state, size_t state_bytes, hipStream_t stream);
 
@@ -214,7 +216,7 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
  * history (the prompt, zero after it) and stores its gated output as the next order's history, so the next
  * call is hyena_decode_step at t = P, which starts a block.  spectra as for hyena_decode_step (no taps
  * needed).  y must not overlap the inputs or the state; the inputs must not overlap the state. */
-int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t P, int dtype,
+int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t P, int dtype, int mode,
                          const void *v, const void *const *x, const void *const *spectra, void *y, void *state,
                          size_t state_bytes, hipStream_t stream);
 

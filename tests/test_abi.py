@@ -230,9 +230,10 @@ def test_decode_sizes_and_rejects_before_launch(lib):
     taps = (ctypes.c_void_p * 2)(1 << 45, 1 << 46)
     sp = (ctypes.c_void_p * 2)(1 << 47, 3 << 46)
 
-    def step(t=5, block=64, st=state, nbytes=need, yy=y, vv=v, x=xs, dtype=L.F32):
-        return lib.hyena_decode_step(order, B, D, Lq, block, t, dtype, vv, x, taps, sp, yy, st, nbytes, None)
+    def step(t=5, block=64, st=state, nbytes=need, yy=y, vv=v, x=xs, dtype=L.F32, mode=L.CAUSAL):
+        return lib.hyena_decode_step(order, B, D, Lq, block, t, dtype, mode, vv, x, taps, sp, yy, st, nbytes, None)
     assert step(t=-1) == L.EINVAL and step(t=Lq) == L.EINVAL and step(dtype=7) == L.EINVAL
+    assert step(mode=L.CIRCULAR) == L.EUNSUPPORTED and step(mode=L.LINEAR | L.PER_SAMPLE) == L.EUNSUPPORTED
     assert step(block=48) == L.EUNSUPPORTED and step(block=2 * Lq) == L.EUNSUPPORTED
     assert step(nbytes=need - 1) == L.EWORKSPACE
     assert step(st=state + 16) == L.EWORKSPACE                 # not 256-byte aligned
@@ -242,12 +243,12 @@ def test_decode_sizes_and_rejects_before_launch(lib):
     assert step(yy=v + 4) == L.EALIAS                           # output overlapping an input
     assert step(yy=v + 2 * B * D - 2, dtype=L.BF16) == L.EALIAS  # bf16 tokens: 2 bytes per row
     assert step(vv=state + 256) == L.EALIAS                     # input inside the state
-    assert lib.hyena_decode_step(order, B, D, Lq, 64, 5, L.F32, v, xs, (ctypes.c_void_p * 2)(state + 512, 1 << 46),
+    assert lib.hyena_decode_step(order, B, D, Lq, 64, 5, L.F32, L.CAUSAL, v, xs, (ctypes.c_void_p * 2)(state + 512, 1 << 46),
                                  sp, y, state, need, None) == L.EALIAS          # taps inside the state
-    assert lib.hyena_decode_step(order, B, D, Lq, 64, 5, L.F32, v, xs, taps, (ctypes.c_void_p * 2)(1 << 47, y - 64),
+    assert lib.hyena_decode_step(order, B, D, Lq, 64, 5, L.F32, L.CAUSAL, v, xs, taps, (ctypes.c_void_p * 2)(1 << 47, y - 64),
                                  y, state, need, None) == L.EALIAS              # output inside a spectrum
     def prefill(P=128, block=64, st=state, yy=y, dtype=L.F32):
-        return lib.hyena_decode_prefill(order, B, D, Lq, block, P, dtype, v, xs, sp, yy, st, need, None)
+        return lib.hyena_decode_prefill(order, B, D, Lq, block, P, dtype, L.CAUSAL, v, xs, sp, yy, st, need, None)
     assert prefill(P=100) == L.EINVAL and prefill(P=0) == L.EINVAL and prefill(P=2 * Lq) == L.EINVAL
     assert prefill(block=3) == L.EUNSUPPORTED and prefill(dtype=9) == L.EINVAL
     assert prefill(st=state + 8) == L.EWORKSPACE

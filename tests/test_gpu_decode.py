@@ -233,3 +233,34 @@ def test_decode_after_prefill_multipass(torch_cuda):
     e = rel_err_rows(_rows(y.astype(np.float64)), ref)
     say(f"  max rel err {e.max():.3e}")
     assert e.max() < FP32_TOL, e.max()
+
+
+def test_decode_per_sample_filters(torch_cuda):
+    """Input-dependent (per (b, d)) filters: FiLM-SIREN taps [B, D, L] and spectra of B*D filters, decoded with
+    HYENA_PER_SAMPLE (a prompt through the prefill, then token steps), against the oracle."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    B, D, L, block, P = 2, 6, 1024, 64, 320
+    w = hi.WORKLOADS[7].with_(B=B, D=D, dims=(L,), mode="causal", registers=4)
+    params, reg = hi.draw_film_params(w, seed=31), hi.draw_registers(w, seed=31)
+    v, xs = hi.draw_activations(w, seed=31)
+    say(f"decode per-sample filters B={B} D={D} L={L} block={block} P={P}")
+    mode = hy.CAUSAL | hy.PER_SAMPLE
+    taps = [torch.empty((B, D, L), dtype=torch.float32, device="cuda") for _ in params]
+    spectra = [hy.film_filter_gen(params_to_dev(p), to_dev(reg, torch.float32), (L,), h_time=h)
+               for p, h in zip(params, taps)]
+    state = torch.empty(hy.decode_state_bytes(2, B, D, L), dtype=torch.uint8, device="cuda")
+    y_pre = hy.decode_prefill(to_dev(v[..., :P], torch.float32), [to_dev(x[..., :P], torch.float32) for x in xs],
+                              spectra, state, L, block, mode=mode)
+    vt = to_dev(np.moveaxis(v, -1, 0), torch.float32)
+    xt = [to_dev(np.moveaxis(x, -1, 0), torch.float32) for x in xs]
+    yt = torch.empty_like(vt)
+    for t in range(P, L):
+        hy.decode_step(t, vt[t], [x[t] for x in xt], taps, spectra, state, L, block, y_t=yt[t], mode=mode)
+    torch.cuda.synchronize()
+    y = np.concatenate([y_pre.cpu().numpy(), np.moveaxis(yt.cpu().numpy(), 0, -1)[..., P:]], axis=-1)
+    hs = [_rows(orc.input_dependent_filter_1d(p, reg, L)) for p in params]
+    ref = orc.hyena_decode_stream(_rows(v), [_rows(x) for x in xs], hs)
+    e = rel_err_rows(_rows(y.astype(np.float64)), ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < FP32_TOL, e.max()
