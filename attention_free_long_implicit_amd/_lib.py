@@ -46,6 +46,7 @@ _lib = None
 _c = ctypes
 _SIG = {
     "hyena_version": (_c.c_int, []),
+    "hyena_init": (_c.c_int, []),
     "hyena_status_str": (_c.c_char_p, [_c.c_int]),
     "hyena_spectrum_bytes": (_c.c_int, [Dims, _c.c_int, _c.c_int64, _c.POINTER(_c.c_size_t)]),
     "hyena_filter_workspace_bytes": (_c.c_int, [Dims, _c.c_int, _c.c_int64, _c.POINTER(_c.c_size_t)]),

@@ -11,13 +11,23 @@
 
 using namespace hyena;
 
+// Constant tables: file-scope device arrays, so every device the library runs on holds its own copy from the
+// moment the code object is loaded (nothing is allocated).  Host code never passes these names to a kernel:
+// it takes each array's address on the device once (hipGetSymbolAddress, with that device current) and
+// uses that address.
+static __device__ __align__(256) float2 g_twiddle_table[kTwPow2Entries + kTwFine];
+static __device__ __align__(256) uint16_t g_matrix_table[kMfmaMatrixCount];
+
 namespace {
 
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
-Twiddles g_tw[kMaxDevices];
-const void* g_mats[kMaxDevices];     // DFT matrices of the matrix-core path (bf16, per lane)
-bool g_tw_ready[kMaxDevices];
+struct DeviceTables {
+  Twiddles tw;
+  const void* mats;       // DFT matrices of the matrix-core path (bf16, per lane)
+  bool ready;
+};
+DeviceTables g_dev[kMaxDevices];
 
 // W_N^j = exp(-2 pi i j / N) in double, rounded once to fp32.
 float2 host_twiddle(long j, long n) {
@@ -25,48 +35,48 @@ float2 host_twiddle(long j, long n) {
   return make_float2((float)cos(a), (float)sin(a));
 }
 
-int get_twiddles(Twiddles* out) {
+// Fill the tables of the current device once (a blocking upload) and record the arrays' device addresses.
+int init_current_device(DeviceTables** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return HYENA_EHIP;
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_tw_ready[dev]) {
+  DeviceTables& t = g_dev[dev];
+  if (!t.ready) {
+    void* tw = nullptr;
+    void* mats = nullptr;
+    if (hipGetSymbolAddress(&tw, HIP_SYMBOL(g_twiddle_table)) != hipSuccess || !tw) return HYENA_EHIP;
+    if (hipGetSymbolAddress(&mats, HIP_SYMBOL(g_matrix_table)) != hipSuccess || !mats) return HYENA_EHIP;
     std::vector<float2> host(kTwPow2Entries + kTwFine);
     host[0] = make_float2(1.f, 0.f);
     for (int sz = 1; sz <= (1 << kTwPow2Log2); sz <<= 1)
       for (int j = 0; j < sz; ++j) host[sz + j] = host_twiddle(j, sz);
     for (int b = 0; b < kTwFine; ++b) host[kTwPow2Entries + b] = host_twiddle(b, 1L << kTwMaxLog2);
-    float2* d = nullptr;
-    if (hipMalloc(&d, host.size() * sizeof(float2)) != hipSuccess) return HYENA_EHIP;
-    if (hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
-      (void)hipFree(d);
+    std::vector<uint16_t> m(kMfmaMatrixCount);
+    mfma_matrices_host(m.data());
+    if (hipMemcpy(tw, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess)
       return HYENA_EHIP;
-    }
-    std::vector<uint16_t> mats(mfma_matrices_count());
-    mfma_matrices_host(mats.data());
-    void* dm = nullptr;
-    if (hipMalloc(&dm, mats.size() * sizeof(uint16_t)) != hipSuccess) {
-      (void)hipFree(d);
+    if (hipMemcpy(mats, m.data(), m.size() * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess)
       return HYENA_EHIP;
-    }
-    if (hipMemcpy(dm, mats.data(), mats.size() * sizeof(uint16_t), hipMemcpyHostToDevice) != hipSuccess) {
-      (void)hipFree(d);
-      (void)hipFree(dm);
-      return HYENA_EHIP;
-    }
-    g_tw[dev].pow2 = d;
-    g_tw[dev].fine = d + kTwPow2Entries;
-    g_mats[dev] = dm;
-    g_tw_ready[dev] = true;
+    t.tw.pow2 = (const float2*)tw;
+    t.tw.fine = (const float2*)tw + kTwPow2Entries;
+    t.mats = mats;
+    t.ready = true;
   }
-  *out = g_tw[dev];
+  *out = &t;
+  return HYENA_OK;
+}
+
+int get_twiddles(Twiddles* out) {
+  DeviceTables* t = nullptr;
+  const int st = init_current_device(&t);
+  if (st) return st;
+  *out = t->tw;
   return HYENA_OK;
 }
 
 const void* device_mats() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  std::lock_guard<std::mutex> lk(g_mu);
-  return g_tw_ready[dev] ? g_mats[dev] : nullptr;
+  DeviceTables* t = nullptr;
+  return init_current_device(&t) ? nullptr : t->mats;
 }
 
 bool is_pow2(int64_t n) { return n > 0 && (n & (n - 1)) == 0; }
@@ -177,6 +187,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // pointer 16-byte aligned.
 bool use_mfma(int dtype, int64_t B, int64_t L) { return dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B); }
 
+// Highest operator order sent to the matrix-core kernel.  Its bf16 transform operands cost about 5e-3 of
+// relative error per order, and later orders amplify what earlier ones leave: measured against the oracle
+// (max over rows) 1.7e-2 at order 2, but 3.4e-2 at order 3 with slowly decaying filters and 5.5e-2 at
+// order 4 with none -- beyond the 2e-2 that bf16 storage allows.  Higher orders take the fp32 engine, whose
+// only roundings are the bf16 stores.
+constexpr int kMfmaMaxOrder = 2;
+
 // Orders [0, order) through the matrix-core kernel, up to kMfmaMaxChain orders per launch with u_i on chip.
 int conv_mfma_chain(int64_t B, int64_t D, int64_t L, const void* u, const void* const* gates,
                     const void* const* spectra, int order, void* y, const Twiddles& tw, hipStream_t s) {
@@ -244,15 +261,9 @@ int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* sp
   }
   if (is3d(kind))
     return hip_status(launch_spectrum3d(h, (float2*)spectrum, (int)nch, (float2*)wsp, chunk, tw, stream, circ3(kind)));
-  if (row_b) {
-    // fp32 spectrum, then its bf16 copy for the bf16 plans' row pass
-    const int lg = engine_log2(kind, L);
-    if ((st = hip_status(launch_spectrum1d_fourstep(lg, h, (float2*)spectrum, (int)nch, (float2*)wsp, chunk, tw,
-                                                    stream, kind == K_CIRC1 ? 1 : 0))))
-      return st;
-    const size_t n = (size_t)nch << lg;
-    return hip_status(launch_spectrum_bf16_copy((const float2*)spectrum, (char*)spectrum + n * sizeof(float2), n, stream));
-  }
+  if (row_b)
+    return hip_status(launch_spectrum1d_fourstep(engine_log2(kind, L), h, (float2*)spectrum, (int)nch, (float2*)wsp,
+                                                 chunk, tw, stream, kind == K_CIRC1 ? 1 : 0));
   if (kind == K_CIRC1)
     return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, (int)nch, tw, stream, 1));
   if ((st = hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, (int)nch, tw, stream)))) return st;
@@ -286,7 +297,12 @@ int split_mode(int mode, bool* per_sample) {
 
 extern "C" {
 
-int hyena_version(void) { return 300; }   // 0.3.0: streaming decode
+int hyena_version(void) { return 400; }   // 0.4.0: fp32 intermediates on every bf16 path, hyena_init
+
+int hyena_init(void) {
+  DeviceTables* t = nullptr;
+  return init_current_device(&t);
+}
 
 const char* hyena_status_str(int status) {
   switch (status) {
@@ -308,11 +324,8 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   int st = check_dims(dims, mode, &pts);
   if (st) return st;
   const int kind = kind_of(mode, dims);
-  // multi-pass 1-D spectra carry a bf16 copy (one word per value) after the fp32 one
-  const size_t mp_copy = multipass1d(kind, pts) ? sizeof(uint32_t) : 0;
   if (is3d(kind)) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel(circ3(kind));
-  else if (kind == K_CIRC1) *bytes = (size_t)D * (size_t)(pts / 2) * (sizeof(float2) + mp_copy);
-  else if (mp_copy) *bytes = (size_t)D * (size_t)pts * (sizeof(float2) + mp_copy);
+  else if (kind == K_CIRC1) *bytes = (size_t)D * (size_t)(pts / 2) * sizeof(float2);
   else *bytes = (size_t)D * (size_t)pts * sizeof(float2) +
                 (has_pair_copy(pts) && !ps ? (size_t)D * mfma_pair_spectrum_bytes_per_channel() : 0);
   return HYENA_OK;
@@ -464,7 +477,7 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
       return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
                                       stream, circ3(kind), hsb));
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs,
-                                             sp, y, (float2*)ws, chunk, tw, device_mats(), stream,
+                                             sp, y, (float2*)ws, chunk, tw, stream,
                                              kind == K_CIRC1 ? 1 : 0, hsb));
   }
   if (kind == K_CIRC1)
@@ -508,26 +521,23 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
                                     tw, stream, circ3(kind), hsb));
   if (chunk)
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
-                                             spectra, y, (float2*)ws, chunk, tw, device_mats(), stream,
+                                             spectra, y, (float2*)ws, chunk, tw, stream,
                                              kind == K_CIRC1 ? 1 : 0, hsb));
-  if (kind == K_CIRC1) {
-    const void* cur = v;
-    for (int i = 0; i < order; ++i) {
-      if ((st = hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, cur, x[i], y,
-                                                (const float2*)spectra[i], (int)B, (int)D, tw, stream, 1, hsb))))
-        return st;
-      cur = y;
-    }
-    return HYENA_OK;
-  }
-  if (!hsb && use_mfma(dtype, B, pts)) {
+  if (kind == K_CAUSAL && !hsb && order <= kMfmaMaxOrder && use_mfma(dtype, B, pts)) {
     bool aligned = aligned16(v) && aligned16(y);
     for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);
     if (aligned) return conv_mfma_chain(B, D, pts, v, x, spectra, order, y, tw, stream);
   }
+  // the single-pass fp32 engine: up to kConvMaxChain orders per launch with u_i on chip
+  const int lg = kind == K_CIRC1 ? circular_log2(pts) : log2i(pts);
   const void* cur = v;
-  for (int i = 0; i < order; ++i) {
-    if ((st = conv_once(B, D, pts, dtype, cur, spectra[i], x[i], y, tw, stream, hsb))) return st;
+  for (int i0 = 0; i0 < order; i0 += kConvMaxChain) {
+    const int n = order - i0 < kConvMaxChain ? order - i0 : kConvMaxChain;
+    const float2* sp[kConvMaxChain];
+    for (int k = 0; k < n; ++k) sp[k] = (const float2*)spectra[i0 + k];
+    if ((st = hip_status(launch_conv1d_chain(lg, dtype == HYENA_BF16, cur, x + i0, sp, n, y, (int)B, (int)D, tw,
+                                             stream, kind == K_CIRC1 ? 1 : 0, hsb))))
+      return st;
     cur = y;
   }
   return HYENA_OK;
@@ -599,8 +609,9 @@ int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void* state, 
   size_t need = 0;
   hyena_decode_state_bytes(order, B, D, L, &need);
   if (((size_t)state & 255u) || state_bytes < need) return HYENA_EWORKSPACE;
-  // the prefix convolutions read whole history rows: everything past the last token must be zero
-  return hip_status(hipMemsetAsync(state, 0, (size_t)order * decode_plane_bytes(rows, L), stream));
+  // the prefix convolutions read whole history rows: everything past the last token must be zero; the
+  // prefix contributions are cleared too, so that a state holds no values of an earlier sequence
+  return hip_status(hipMemsetAsync(state, 0, 2 * (size_t)order * decode_plane_bytes(rows, L), stream));
 }
 
 int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t t, int dtype, int mode,
@@ -653,8 +664,7 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
         const void* xs[1] = {nullptr};
         const void* sp[1] = {spectra[i]};
         st = hip_status(launch_conv1d_fourstep(lg, 0, 1, (int)B, (int)D, h_i, xs, sp, f_i,
-                                               (float2*)(fut + (size_t)order * plane), chunk, tw, device_mats(),
-                                               stream, 0, hsb));
+                                               (float2*)(fut + (size_t)order * plane), chunk, tw, stream, 0, hsb));
       } else {
         st = hip_status(launch_conv1d_single(lg, 0, h_i, nullptr, f_i, (const float2*)spectra[i], (int)B, (int)D, tw,
                                              stream, 0, hsb));
@@ -686,8 +696,15 @@ int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t blo
   if (((size_t)state & 255u) || state_bytes < need) return HYENA_EWORKSPACE;
   const size_t pb = (size_t)rows * (size_t)P * elem_bytes(dtype);
   if (overlaps(y, pb, v, pb) || overlaps(y, pb, state, need) || overlaps(v, pb, state, need)) return HYENA_EALIAS;
+  hyena_dims dims{};
+  dims.ndim = 1;
+  dims.n[0] = L;
+  size_t spb = 0;
+  if ((st = hyena_spectrum_bytes(dims, mode, ps ? rows : D, &spb))) return st;
   for (int i = 0; i < order; ++i)
-    if (overlaps(y, pb, x[i], pb) || overlaps(x[i], pb, state, need)) return HYENA_EALIAS;
+    if (overlaps(y, pb, x[i], pb) || overlaps(x[i], pb, state, need) || overlaps(spectra[i], spb, state, need) ||
+        overlaps(y, pb, spectra[i], spb))
+      return HYENA_EALIAS;
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
   float* hist = (float*)state;
@@ -708,8 +725,7 @@ int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t blo
       const void* xs[1] = {nullptr};
       const void* sp[1] = {spectra[i]};
       st = hip_status(launch_conv1d_fourstep(lg, 0, 1, (int)B, (int)D, h_i, xs, sp, c,
-                                             (float2*)(fut + (size_t)order * plane), chunk, tw, device_mats(), stream,
-                                             0, hsb));
+                                             (float2*)(fut + (size_t)order * plane), chunk, tw, stream, 0, hsb));
     } else {
       st = hip_status(launch_conv1d_single(lg, 0, h_i, nullptr, c, (const float2*)spectra[i], (int)B, (int)D, tw,
                                            stream, 0, hsb));

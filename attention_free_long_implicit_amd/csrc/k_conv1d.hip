@@ -44,13 +44,18 @@ struct Single {
   static_assert(RL::S == M && NP::TN == T, "plan");
 };
 
+// Orders i = 0..order-1 back to back in one launch (the cross-order fusion of the nSubQ pattern: one
+// HBM read of the row and of each gate, one store of the result).  Between orders u_i stays in registers
+// in fp32 -- also for bf16 storage, where only v, the gates and y are bf16 -- so for fp32 storage a chain
+// equals `order` one-order launches bit for bit.  GATE = false only for a single order without a gate.
 template <int LOG2M, bool BF16, bool GATE, bool FULL>
 __global__ void __launch_bounds__(Single<LOG2M>::T, 4)
-k_conv1d(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* gate,
-         typename Store<BF16>::elem* y, const float2* __restrict__ Hs, int B, int D, int hsb, Twiddles tw) {
+k_conv1d(const typename Store<BF16>::elem* u, ConvChain ch, int order, typename Store<BF16>::elem* y, int B,
+         int D, int hsb, Twiddles tw0) {
   using C = Single<LOG2M>;
   using En = typename C::En;
   using St = Store<BF16>;
+  using Elem = typename St::elem;
   constexpr int M = C::M, T = C::T, E = C::E, R0 = C::R0, RP = C::RP, Q0 = C::Q0;
   __shared__ float2 lds[En::LDS_ELEMS];
   const int t = threadIdx.x;
@@ -65,34 +70,44 @@ k_conv1d(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* 
     constexpr int i = ii.value;
     static_for<NIN>([&](auto m) { x[i * R0 + m.value] = St::load2(urow + 2 * (t + T * i + m.value * Q0)); });
   });
-  En::template forward_to_last<!FULL>(x, lds, tw, t);
-  const auto P = C::NP::of(t);
-  En::fwd_last(x, lds, P.betaA, P.betaB);
+  const size_t hrow = (size_t)(d + b * hsb) * M;             // hsb = 0: one filter per channel; D: per (b, d)
+  for (int o = 0; o < order; ++o) {
+    if (o > 0) __syncthreads();               // the previous order's last inverse pass read the LDS
+    // Everything derived from the thread index and the twiddle tables is recomputed per order: kept live
+    // across the loop it would not fit the register budget next to the row.
+    int t = threadIdx.x;
+    Twiddles tw = tw0;
+    asm volatile("" : "+v"(t));
+    asm volatile("" : "+s"(tw.pow2), "+s"(tw.fine));
+    const auto P = C::NP::of(t);
+    En::template forward_to_last<!FULL>(x, lds, tw, t);
+    En::fwd_last(x, lds, P.betaA, P.betaB);
+    const float2* hs = ch.spectrum[o] + hrow + t;
+    if (!P.special) {
+      spectral_complement<RP, 0>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapA)), hs, T, nullptr, 0.f);
+    } else {
+      spectral_selfmirror<RP, 0>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapB)), hs, T, nullptr, 0.f);
+    }
+    En::inv_last(x, lds, P.betaA, P.betaB);
+    En::template inverse_from_last<!FULL>(x, lds, tw, t);
 
-  const float2* hs = Hs + (size_t)(d + b * hsb) * M + t;     // hsb = 0: one filter per channel; D: per (b, d)
-  if (!P.special) {
-    spectral_complement<RP, 0>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapA)), hs, T, nullptr, 0.f);
-  } else {
-    spectral_selfmirror<RP, 0>(x, twiddle<LOG2M + 1>(tw, uint32_t(P.kapB)), hs, T, nullptr, 0.f);
-  }
-
-  En::inv_last(x, lds, P.betaA, P.betaB);
-  En::template inverse_from_last<!FULL>(x, lds, tw, t);
-
-  auto* yrow = y + row * RS;
-  const auto* grow = GATE ? gate + row * RS : nullptr;
-  static_for<C::NB0>([&](auto ii) {
-    constexpr int i = ii.value;
-    static_for<NIN>([&](auto m) {
-      const int j = t + T * i + m.value * Q0;
-      float2 v = x[i * R0 + m.value];
-      if constexpr (GATE) {
-        const float2 g = St::load2(grow + 2 * j);
-        v = make_float2(v.x * g.x, v.y * g.y);
-      }
-      St::store2(yrow + 2 * j, v);
+    const bool last = o + 1 == order;
+    const auto* grow = GATE ? static_cast<const Elem*>(ch.gate[o]) + row * RS : nullptr;
+    auto* yrow = y + row * RS;
+    static_for<C::NB0>([&](auto ii) {
+      constexpr int i = ii.value;
+      static_for<NIN>([&](auto m) {
+        const int j = t + T * i + m.value * Q0;
+        float2 v = x[i * R0 + m.value];
+        if constexpr (GATE) {
+          const float2 g = St::load2(grow + 2 * j);
+          v = make_float2(v.x * g.x, v.y * g.y);
+        }
+        if (last) St::store2(yrow + 2 * j, v);
+        else x[i * R0 + m.value] = v;
+      });
     });
-  });
+  }
 }
 
 // Filter spectrum in engine order: Hs = DFT_{2M}(h || 0) / (4M) from M taps, or (FULL) Hs = DFT_{2M}(h) / (4M)
@@ -150,26 +165,26 @@ __global__ void k_export1d(const float2* __restrict__ Hs, float2* __restrict__ H
 // ------------------------------------------------------------------ host launchers
 namespace {
 template <int LOG2M, bool BF16, bool FULL>
-void conv1d_launch_t(bool gate, const void* u, const void* g, void* y, const float2* Hs, int B, int D, int hsb,
+void conv1d_launch_t(bool gate, const void* u, const ConvChain& ch, int order, void* y, int B, int D, int hsb,
                      const Twiddles& tw, hipStream_t s) {
   using E = typename Store<BF16>::elem;
   dim3 grid(B * D), block(Single<LOG2M>::T);
   if (gate)
-    hipLaunchKernelGGL((k_conv1d<LOG2M, BF16, true, FULL>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs,
-                       B, D, hsb, tw);
+    hipLaunchKernelGGL((k_conv1d<LOG2M, BF16, true, FULL>), grid, block, 0, s, (const E*)u, ch, order, (E*)y, B, D,
+                       hsb, tw);
   else
-    hipLaunchKernelGGL((k_conv1d<LOG2M, BF16, false, FULL>), grid, block, 0, s, (const E*)u, (const E*)g, (E*)y, Hs,
-                       B, D, hsb, tw);
+    hipLaunchKernelGGL((k_conv1d<LOG2M, BF16, false, FULL>), grid, block, 0, s, (const E*)u, ch, order, (E*)y, B, D,
+                       hsb, tw);
 }
 template <int LOG2M>
-hipError_t conv1d_launch(int bf16, bool gate, bool full, const void* u, const void* g, void* y, const float2* Hs,
+hipError_t conv1d_launch(int bf16, bool gate, bool full, const void* u, const ConvChain& ch, int order, void* y,
                          int B, int D, int hsb, const Twiddles& tw, hipStream_t s) {
   if (bf16)
-    full ? conv1d_launch_t<LOG2M, true, true>(gate, u, g, y, Hs, B, D, hsb, tw, s)
-         : conv1d_launch_t<LOG2M, true, false>(gate, u, g, y, Hs, B, D, hsb, tw, s);
+    full ? conv1d_launch_t<LOG2M, true, true>(gate, u, ch, order, y, B, D, hsb, tw, s)
+         : conv1d_launch_t<LOG2M, true, false>(gate, u, ch, order, y, B, D, hsb, tw, s);
   else
-    full ? conv1d_launch_t<LOG2M, false, true>(gate, u, g, y, Hs, B, D, hsb, tw, s)
-         : conv1d_launch_t<LOG2M, false, false>(gate, u, g, y, Hs, B, D, hsb, tw, s);
+    full ? conv1d_launch_t<LOG2M, false, true>(gate, u, ch, order, y, B, D, hsb, tw, s)
+         : conv1d_launch_t<LOG2M, false, false>(gate, u, ch, order, y, B, D, hsb, tw, s);
   return hipGetLastError();
 }
 template <int LOG2M>
@@ -192,15 +207,31 @@ bool single_pass_supported(int log2L) { return log2L >= 10 && log2L <= 14; }
 
 #define HYENA_SINGLE_CASES(X) X(10) X(11) X(12) X(13) X(14)
 
-hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* gate, void* y, const float2* Hs,
-                                int B, int D, const Twiddles& tw, hipStream_t s, int full, int hsb) {
-  const bool g = gate != nullptr;
+hipError_t launch_conv1d_chain(int log2L, int bf16, const void* u, const void* const* gates,
+                               const float2* const* spectra, int order, void* y, int B, int D, const Twiddles& tw,
+                               hipStream_t s, int full, int hsb) {
+  if (order < 1 || order > kConvMaxChain) return hipErrorInvalidValue;
+  ConvChain ch{};
+  bool g = true;
+  for (int i = 0; i < order; ++i) {
+    ch.gate[i] = gates[i];
+    ch.spectrum[i] = spectra[i];
+    g = g && gates[i] != nullptr;
+  }
+  if (!g && order != 1) return hipErrorInvalidValue;   // only a single order may run without a gate
   switch (log2L) {
-#define X(n) case n: return conv1d_launch<n>(bf16, g, full != 0, u, gate, y, Hs, B, D, hsb, tw, s);
+#define X(n) case n: return conv1d_launch<n>(bf16, g, full != 0, u, ch, order, y, B, D, hsb, tw, s);
     HYENA_SINGLE_CASES(X)
 #undef X
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* gate, void* y, const float2* Hs,
+                                int B, int D, const Twiddles& tw, hipStream_t s, int full, int hsb) {
+  const void* g[1] = {gate};
+  const float2* h[1] = {Hs};
+  return launch_conv1d_chain(log2L, bf16, u, g, h, 1, y, B, D, tw, s, full, hsb);
 }
 
 hipError_t launch_spectrum1d_single(int log2L, const float* h, float2* Hs, int D, const Twiddles& tw,

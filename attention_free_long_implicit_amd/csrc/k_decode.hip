@@ -44,8 +44,8 @@ __device__ __forceinline__ float dec_wave_sum(float v) {
 }
 
 // hist, fut: [N][rows][L] fp32 (history of u_{i-1}, prefix contributions); taps[i]: [D][L] fp32, or
-// [rows][L] with per-sample filters.  With bf16
-// tokens the intermediate u_i (i < N) is rounded to bf16 before it is used, as a stored intermediate is.
+// [rows][L] with per-sample filters.  With bf16 tokens only v_t, the gates and y_t are bf16: the
+// intermediates u_i stay fp32, as in the whole-sequence operator.
 template <int N, bool BF16>
 __global__ void __launch_bounds__(256)
 k_decode_step(const void* __restrict__ v_t, DecodeTok x_t, DecodePtrs taps, float* hist,
@@ -85,8 +85,6 @@ k_decode_step(const void* __restrict__ v_t, DecodeTok x_t, DecodePtrs taps, floa
   for (int i = 0; i < N; ++i) {
     if (lane == 0) hist[i * plane + rowL + t] = u;        // u_{i-1}[t] joins order i's history
     u = xg[i] * fmaf(h0[i], u, acc[i]);
-    if constexpr (BF16)
-      if (i + 1 < N) u = bf16_to_f32(f32_to_bf16_rne(u));
   }
   if (lane == 0) {
     if constexpr (BF16) static_cast<uint16_t*>(y_t)[r] = f32_to_bf16_rne(u);
@@ -97,7 +95,7 @@ k_decode_step(const void* __restrict__ v_t, DecodeTok x_t, DecodePtrs taps, floa
 // Prompt (prefill) staging, one element of a row per thread, rows of L: position t < P takes the prompt
 // value, t >= P is zero (the history past the last token is zero).  MODE 0: dst = v (the input of order
 // 1).  MODE 1: c holds the convolution of order i over its history; dst = x_i * c (the input of order
-// i + 1, rounded to bf16 with bf16 tokens), or, with y (the last order), y[b, d, t < P] = x_N * c.
+// i + 1, fp32), or, with y (the last order), y[b, d, t < P] = x_N * c.
 // a (v or x_i) and y: [rows][P] of the token type.
 template <int MODE, bool BF16>
 __global__ void __launch_bounds__(256)
@@ -111,8 +109,6 @@ k_decode_prefill(const void* __restrict__ a, const float* c, float* dst, void* _
   if (t < P) {
     const float in = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(a)[ap]) : static_cast<const float*>(a)[ap];
     u = MODE == 0 ? in : in * c[at];
-    if constexpr (BF16)
-      if (MODE == 1 && !y) u = bf16_to_f32(f32_to_bf16_rne(u));
   }
   if (MODE == 1 && y) {
     if (t < P) {

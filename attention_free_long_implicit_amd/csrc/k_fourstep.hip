@@ -16,39 +16,18 @@
 // row of L = 2M samples fills all M packed values, pass A loads every n1 and pass C keeps every n1,
 // so the same passes compute the L-point circular convolution (the row pass is unchanged).
 //
-// The intermediate is one complex M-vector per row, fp32 for fp32 activations and bf16 words (re low,
-// im high) for bf16 activations (rounded like every stored bf16 value; it halves the pass traffic).
-// Rows are processed in chunks whose intermediates stay resident in L2 / the memory-side cache.  Rows are visited channel-major
+// The intermediate is one complex fp32 M-vector per row, for either storage type: with bf16 activations only
+// v, the gates and y are bf16, and u_i stays fp32 from one order to the next (rounding the intermediate or
+// u_i to bf16 compounds across orders into errors beyond what bf16 storage is allowed).  Rows are processed
+// in chunks whose intermediates stay resident in L2 / the memory-side cache.  Rows are visited channel-major
 // (q = d*B + b) so the B rows of a channel read its filter spectrum back to back.
 //
 // Spectrum layout per channel: Hs[g][slot][t'] for row-pair group g < M1/2, slot < 2 RP, thread t'
-// of the pair (see k_fs_rows); g = 0 holds rows k1 = 0 and k1 = M1/2.  Hs = H / (4M).  The bf16 plans
-// read a bf16 copy of it (one word per value, real part low) stored after the fp32 spectrum: their
-// intermediate and products are bf16 already, and it halves the spectrum traffic of the row pass.
+// of the pair (see k_fs_rows); g = 0 holds rows k1 = 0 and k1 = M1/2.  Hs = H / (4M).
 #include "engine.h"
 #include "launch.h"
 
 namespace hyena {
-
-// Element type of the intermediate.
-template <bool BF16> struct Inter;
-template <> struct Inter<false> {
-  using T = float2;
-  __device__ __forceinline__ static float2 ld(const float2* p) { return *p; }
-  __device__ __forceinline__ static void st(float2* p, float2 v) { *p = v; }
-};
-template <> struct Inter<true> {
-  using T = uint32_t;
-  __device__ __forceinline__ static float2 ld(const uint32_t* p) {
-    const uint32_t w = *p;
-    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-  }
-  __device__ __forceinline__ static void st(uint32_t* p, float2 v) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    const bf16x2 b = {(__bf16)v.x, (__bf16)v.y};
-    *p = __builtin_bit_cast(uint32_t, b);
-  }
-};
 
 template <int LOG2M> struct FourStepPlan;
 // M1 (columns) x M2 (rows); column radices, row radices (last radix 8, 16 elements per thread)
@@ -89,10 +68,9 @@ struct FS {
 template <int LOG2M, bool BF16, int MODE, bool GATE, bool CHAIN, bool FULL>
 __global__ void __launch_bounds__(FS<LOG2M>::TC)
 k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem* gate,
-          typename Store<BF16>::elem* y, typename Inter<BF16>::T* I, int q0, int nq, int B, int D, Twiddles tw) {
+          typename Store<BF16>::elem* y, float2* I, int q0, int nq, int B, int D, Twiddles tw) {
   using F = FS<LOG2M>;
   using St = Store<BF16>;
-  using In = Inter<BF16>;
   constexpr int M = F::M, M1 = F::M1, M2 = F::M2, C = F::C, TC = F::TC;
   constexpr int PER_T = C * M1 / TC;              // tile elements per thread
   constexpr int PER_IO = FULL ? PER_T : PER_T / 2;  // of them loaded from u / stored to y
@@ -105,7 +83,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   const int d = q / B, b = q % B;
   const size_t row = (size_t)b * D + d;
   const int c0 = tile * C;
-  typename In::T* Irow = I + (size_t)ql * M;
+  float2* Irow = I + (size_t)ql * M;
   auto tile_addr = [&](int p, int c) { return F::Col::addr(p, c); };
 
   if constexpr (MODE == 0) {
@@ -121,7 +99,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
     static_for<PER_T>([&](auto ii) {
       const int e = t + TC * ii.value;
       const int p = e / C, c = e % C;
-      lds[tile_addr(p, c)] = In::ld(Irow + (size_t)p * M2 + c0 + c);
+      lds[tile_addr(p, c)] = Irow[(size_t)p * M2 + c0 + c];
     });
     __syncthreads();
     F::Col::template inverse<!FULL>(lds, tw, t);
@@ -138,9 +116,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
         v = make_float2(v.x * g.x, v.y * g.y);
       }
       if constexpr (CHAIN) {
-        // the next order consumes the stored (rounded) value, as it would from memory
-        if constexpr (BF16) v = make_float2(bf16_to_f32(f32_to_bf16_rne(v.x)), bf16_to_f32(f32_to_bf16_rne(v.y)));
-        lds[tile_addr(p, c)] = v;
+        lds[tile_addr(p, c)] = v;             // the next order's input, kept in fp32
       } else {
         St::store2(yrow + 2 * j, v);
       }
@@ -152,7 +128,7 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   static_for<PER_T>([&](auto ii) {
     const int e = t + TC * ii.value;
     const int p = e / C, c = e % C;
-    In::st(Irow + (size_t)p * M2 + c0 + c, lds[tile_addr(p, c)]);
+    Irow[(size_t)p * M2 + c0 + c] = lds[tile_addr(p, c)];
   });
 }
 
@@ -192,14 +168,11 @@ k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
 // beta_A = t' of the first row and beta_B = NBLK-1-t' of the second (their bins mirror each other:
 // k <-> M-k pairs k1 with M1-k1 and complements every k2 digit); the g_glob = 0 pair instead uses
 // whole-row negation pairing on row 0 (threads < TP/2) and in-row complement pairing on row M1/2.
-template <int LOG2M, int MODE, bool IBF16>
+template <int LOG2M, int MODE>
 __global__ void __launch_bounds__(FS<LOG2M>::TR)
-k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __restrict__ Hs_out, int q0, int nq,
-          int B, int hsb, Twiddles tw) {
-  using HT = typename Inter<IBF16>::T;   // spectrum element: fp32 complex, or a bf16 pair word
-  const HT* __restrict__ Hs = static_cast<const HT*>(Hsv);
+k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq, int B, int hsb,
+          Twiddles tw) {
   using F = FS<LOG2M>;
-  using In = Inter<IBF16>;
   using Row = typename F::Row;
   using RL = typename F::RowRL;
   constexpr int M = F::M, M1 = F::M1, M2 = F::M2, G = F::G, TP = F::TP, TR = F::TR, RP = F::RP;
@@ -211,7 +184,7 @@ k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __r
   const int q = q0 + ql;
   // spectrum channel: d (one filter per channel, hsb = 0) or b * D + d (one per (b, d), hsb = D)
   const int d = (MODE == 0) ? q / B + (q % B) * hsb : q;
-  typename In::T* Irow = I + (size_t)ql * M;
+  float2* Irow = I + (size_t)ql * M;
 
   // bin row k1 of sub-row s (s = 2j: first of pair j, 2j+1: second)
   auto k1_of = [&](int s) {
@@ -227,12 +200,12 @@ k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __r
     int s, n;
     Row::first_input(t, i, s, n);
     const int k1 = k1_of(s);
-    const typename In::T* src = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
+    const float2* src = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
     // W_M^{(n + m PER0) k1} for m = 0..R0-1 as a running product from W_M^{n k1} by W_M^{PER0 k1}
     const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
     float2 w = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     static_for<R0>([&](auto m) {
-      const float2 v = In::ld(src + n + m.value * PER0);
+      const float2 v = src[n + m.value * PER0];
       x[i * R0 + m.value] = cmul(v, w);
       if constexpr (m.value + 1 < R0) w = cmul(w, ws);
     });
@@ -287,11 +260,11 @@ k_fs_rows(typename Inter<IBF16>::T* I, const void* __restrict__ Hsv, float2* __r
     int s, n;
     Row::first_input(t, i, s, n);
     const int k1 = k1_of(s);
-    typename In::T* dst = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
+    float2* dst = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
     const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
     float2 w = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     static_for<R0>([&](auto m) {
-      In::st(dst + n + m.value * PER0, cmulc(x[i * R0 + m.value], w));
+      dst[n + m.value * PER0] = cmulc(x[i * R0 + m.value], w);
       if constexpr (m.value + 1 < R0) w = cmul(w, ws);
     });
   });
@@ -334,12 +307,6 @@ __global__ void k_export1d_fs(const float2* __restrict__ Hs, float2* __restrict_
   out[k1 + M1 * (kap + (M2 / RP) * m)] = cscale(v, sc);
 }
 
-// fp32 spectrum -> bf16 copy (round to nearest even), one word per complex value
-__global__ void k_spectrum_bf16(const float2* __restrict__ Hs, uint32_t* __restrict__ Hb, size_t n) {
-  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) Inter<true>::st(Hb + i, Hs[i]);
-}
-
 // ------------------------------------------------------------------ host side
 namespace {
 
@@ -348,41 +315,28 @@ size_t fs_row_bytes() { return (size_t)(1 << LOG2M) * sizeof(float2); }
 
 template <int LOG2M, bool BF16, bool FULL>
 hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
-                          void* y, float2* I, int chunk, const Twiddles& tw, const void* mats, hipStream_t s, int hsb) {
-  // bf16 causal plans with 128-point columns run their column passes on the matrix cores
-  const bool mc = BF16 && !FULL && mats && fs_cols_mfma_supported(LOG2M);
+                          void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s, int hsb) {
   using F = FS<LOG2M>;
   using E = typename Store<BF16>::elem;
-  using IT = typename Inter<BF16>::T;
-  IT* Ib = reinterpret_cast<IT*>(I);
   const int rows = B * D;
   const int tiles = F::M2 / F::C;
   const int groups = (F::M1 / 2) / F::G;
   for (int q0 = 0; q0 < rows; q0 += chunk) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
-    if (mc)
-      (void)launch_fs_cols_mfma(LOG2M, 0, false, false, v, nullptr, nullptr, Ib, q0, nq, B, D, mats, s);
-    else
-      hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                         (const E*)v, (const E*)nullptr, (E*)nullptr, Ib, q0, nq, B, D, tw);
+    hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
+                       (const E*)v, (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
-      // bf16 plans read the bf16 copy stored after the fp32 spectrum
-      const size_t nch = hsb ? (size_t)B * D : (size_t)D;       // filters in the spectrum
-      const void* hs = BF16 ? (const void*)((const char*)spectra[i] + nch * F::M * sizeof(float2)) : spectra[i];
-      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0, BF16>), dim3(groups * nq), dim3(F::TR), 0, s, Ib, hs,
-                         (float2*)nullptr, q0, nq, B, hsb, tw);
-      if (mc)
-        (void)launch_fs_cols_mfma(LOG2M, 1, x[i] != nullptr, i + 1 < order, nullptr, x[i], y, Ib, q0, nq, B, D, mats,
-                                  s);
-      else if (i + 1 < order)
+      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0>), dim3(groups * nq), dim3(F::TR), 0, s, I,
+                         (const float2*)spectra[i], (float2*)nullptr, q0, nq, B, hsb, tw);
+      if (i + 1 < order)
         hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, true, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                           (const E*)nullptr, (const E*)x[i], (E*)nullptr, Ib, q0, nq, B, D, tw);
+                           (const E*)nullptr, (const E*)x[i], (E*)nullptr, I, q0, nq, B, D, tw);
       else if (x[i])
         hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                           (const E*)nullptr, (const E*)x[i], (E*)y, Ib, q0, nq, B, D, tw);
+                           (const E*)nullptr, (const E*)x[i], (E*)y, I, q0, nq, B, D, tw);
       else
         hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
-                           (const E*)nullptr, (const E*)nullptr, (E*)y, Ib, q0, nq, B, D, tw);
+                           (const E*)nullptr, (const E*)nullptr, (E*)y, I, q0, nq, B, D, tw);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -399,7 +353,7 @@ hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int 
   for (int q0 = 0; q0 < D; q0 += chunk) {
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
     hipLaunchKernelGGL((k_fs_cols_taps<LOG2M, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s, h, I, q0, nq, tw);
-    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1, false>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const void*)nullptr,
+    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const float2*)nullptr,
                        Hs, q0, nq, 1, 0, tw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -415,11 +369,6 @@ size_t fourstep_row_bytes(int log2L) { return (size_t)1 << log2L << 3; }
 
 #define HYENA_FS_CASES(X) X(15) X(16) X(17) X(18) X(19) X(20)
 
-hipError_t launch_spectrum_bf16_copy(const float2* Hs, void* Hb, size_t n, hipStream_t s) {
-  hipLaunchKernelGGL(k_spectrum_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Hs, (uint32_t*)Hb, n);
-  return hipGetLastError();
-}
-
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s) {
   switch (log2L) {
 #define X(n)                                                                                              \
@@ -434,15 +383,15 @@ hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int 
 
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, const void* mats, hipStream_t s, int full, int hsb) {
+                                  const Twiddles& tw, hipStream_t s, int full, int hsb) {
   switch (log2L) {
 #define X(n)                                                                                                   \
   case n:                                                                                                      \
     if (full)                                                                                                  \
-      return bf16 ? fs_conv_launch<n, true, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s, hsb)   \
-                  : fs_conv_launch<n, false, true>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s, hsb); \
-    return bf16 ? fs_conv_launch<n, true, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s, hsb)    \
-                : fs_conv_launch<n, false, false>(order, B, D, v, x, spectra, y, I, chunk, tw, mats, s, hsb);
+      return bf16 ? fs_conv_launch<n, true, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb)   \
+                  : fs_conv_launch<n, false, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb); \
+    return bf16 ? fs_conv_launch<n, true, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb)    \
+                : fs_conv_launch<n, false, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb);
     HYENA_FS_CASES(X)
 #undef X
   }

@@ -14,6 +14,16 @@ bool single_pass_supported(int log2L);
 // (b, d) in [B, D] order (input-dependent filters).
 hipError_t launch_conv1d_single(int log2L, int bf16, const void* u, const void* gate, void* y, const float2* Hs,
                                 int B, int D, const Twiddles& tw, hipStream_t s, int full = 0, int hsb = 0);
+// Orders 0..order-1 (order <= kConvMaxChain) in one launch, u_i kept on chip in fp32 between them.
+// gates[i] may be NULL only when order == 1.
+constexpr int kConvMaxChain = 8;
+struct ConvChain {
+  const void* gate[kConvMaxChain];
+  const float2* spectrum[kConvMaxChain];
+};
+hipError_t launch_conv1d_chain(int log2L, int bf16, const void* u, const void* const* gates,
+                               const float2* const* spectra, int order, void* y, int B, int D, const Twiddles& tw,
+                               hipStream_t s, int full = 0, int hsb = 0);
 hipError_t launch_spectrum1d_single(int log2L, const float* h, float2* Hs, int D, const Twiddles& tw,
                                     hipStream_t s, int full = 0);
 hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
@@ -23,15 +33,13 @@ hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D,
 // 2M samples.  x[i] may be NULL for the last order only (no gate).
 bool fourstep_supported(int log2L);
 size_t fourstep_row_bytes(int log2L);
-// mats: the matrix-core table (bf16 L = 2^15, 2^16 run their column passes on the matrix cores), or NULL.
+// The intermediate I is fp32 for either storage type; u_i stays fp32 between orders.
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, const void* mats, hipStream_t s, int full = 0, int hsb = 0);
+                                  const Twiddles& tw, hipStream_t s, int full = 0, int hsb = 0);
 hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
                                       const Twiddles& tw, hipStream_t s, int full = 0);
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
-// bf16 copy of a multi-pass spectrum (n complex values), read by the bf16 plans' row pass
-hipError_t launch_spectrum_bf16_copy(const float2* Hs, void* Hb, size_t n, hipStream_t s);
 
 // ---- 3-D, 64^3 grid: circ = 0 zero-padded to 128^3 (non-causal "same" convolution),
 //      circ = 1 periodic on the 64^3 grid itself
@@ -50,18 +58,13 @@ hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s, in
 // ---- matrix-core path: bf16 storage, L = 8192, rows in pairs of one channel (B even)
 bool mfma_pair_supported(int log2L, int B);
 size_t mfma_pair_spectrum_bytes_per_channel();
-size_t mfma_matrices_count();                    // bf16 values in the DFT-matrix table
+constexpr size_t kMfmaMatrixCount = (3 + 16 * 16) * 64 * 8;   // bf16 values in the DFT-matrix table
 void mfma_matrices_host(uint16_t* out);
 // Orders 1..order back to back in one launch (u_i stays on chip); spectra[i] = matrix-core copies.
 constexpr int kMfmaMaxChain = 8;
 hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void* const* spectra, int order,
                             void* y, const void* mats, int B, int D, const Twiddles& tw, hipStream_t s);
 hipError_t launch_pair_spectrum(const float2* Hnat, void* Hc, int D, hipStream_t s);
-// Matrix-core column passes of the multi-pass plan (bf16, L = 2^15, 2^16).  mode 0: pass A from u;
-// mode 1: pass C with gate (gated) then either the next order's pass A (chain) or the store of y.
-bool fs_cols_mfma_supported(int log2L);
-hipError_t launch_fs_cols_mfma(int log2L, int mode, bool gated, bool chain, const void* u, const void* gate, void* y,
-                               void* I, int q0, int nq, int B, int D, const void* mats, hipStream_t s);
 
 // ---- implicit filter taps
 struct FilterArgs {

@@ -23,10 +23,21 @@
  * Conventions for every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library never frees them.
  *   - Activations are channel-major and contiguous: [B, D, L] (1-D) or [B, D, nx, ny, nz] (3-D),
- *     element type given by hyena_dtype (math is always fp32; bf16 stores round to nearest even).
+ *     element type given by hyena_dtype.  bf16 is a storage type only: v, the gates and y are bf16 (stores
+ *     round to nearest even); the intermediates u_i of the recurrence and every transform intermediate
+ *     stay fp32.
+ *   - Arithmetic: fp32 on every path (radix butterflies on the vector units, fp32 twiddles, fp32 spectra and
+ *     spectral products), with one exception, the matrix-core path of hyena_fftconv / hyena_operator (bf16
+ *     storage, causal L = 8192, even B, order <= 2): its DFT steps are bf16 x bf16 matrix products with
+ *     fp32 accumulation -- the DFT matrices and the data entering each product are rounded to bf16 -- and
+ *     between its two orders u_1 is rounded to bf16; twiddles and the spectral product stay fp32.  Its
+ *     measured error against an fp64 evaluation is about 1.7e-2 (relative L2 per row, max over rows) at
+ *     order 2, against 2e-3 for the fp32 paths with bf16 storage.
  *   - Calls are asynchronous on the caller's HIP stream and never synchronise the host, except the
- *     first call on a device, which uploads the library's constant twiddle tables (about 512 KB) once.
- *   - The library holds no state across calls besides those immutable tables.
+ *     first call on a device, which uploads the library's constant tables (about 790 KB) once with a
+ *     blocking copy; hyena_init() does that upload ahead of time (for example before graph capture).
+ *   - The library holds no state across calls besides those immutable tables, which live in device arrays
+ *     of the library's code object (the library never calls hipMalloc).
  *   - Return value: HYENA_OK or a negative status (below); arguments are validated before anything
  *     is launched, so an error return means nothing was enqueued.  Device faults surface at the
  *     caller's next synchronisation.  hyena_status_str() names a status.
@@ -84,9 +95,9 @@ typedef struct {
 
 /* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array):
  * causal 8L bytes per channel (for L = 8192 followed by a bf16 copy laid out for the matrix-core
- * kernel, 36 KB per channel, except with HYENA_PER_SAMPLE; for L > 16384, 12L: a bf16 copy for the
- * bf16 plans follows); periodic 1-D 4L bytes per channel (6L for L > 32768); 3-D 128*128*65*8 bytes
- * per channel (zero-padded) or 64*64*33*8 (periodic).  With HYENA_PER_SAMPLE, D counts filters (B*D). */
+ * kernel, 36 KB per channel, except with HYENA_PER_SAMPLE); periodic 1-D 4L bytes per channel; 3-D
+ * 128*128*65*8 bytes per channel (zero-padded) or 64*64*33*8 (periodic).  With HYENA_PER_SAMPLE, D counts
+ * filters (B*D). */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
 
 /* Workspace bytes hyena_filter_gen needs: room for the taps (used when h_time is NULL) plus, for
@@ -139,8 +150,9 @@ int hyena_film_filter_gen(const hyena_film_params *p, int64_t B, int32_t R, cons
 
 /* One long convolution with optional gate: y = gate * (h conv u), or y = h conv u when gate == NULL.
  * u, gate, y: [B, D, points] of dtype.  spectrum: from hyena_filter_gen for the same dims and D.
- * bf16 storage with L = 8192, even B and 16-byte-aligned u, gate and y runs on the matrix cores (rows
- * b and b+1 of a channel transformed together); every other case runs the fp32 transform engine.
+ * bf16 storage with causal L = 8192, even B and 16-byte-aligned u, gate and y runs on the matrix cores
+ * (rows b and b+1 of a channel transformed together; bf16 operands, see the conventions above); every
+ * other case runs the fp32 transform engine.
  * y may equal u or gate exactly (in place); any other overlap returns HYENA_EALIAS. */
 int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *u,
                   const void *spectrum, const void *gate, void *y, void *ws, size_t ws_bytes,
@@ -149,9 +161,14 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
 /* The order-N operator y = x_N * (h_N conv (... x_1 * (h_1 conv v))).
  * x: host array of `order` device pointers (x[0] = x_1); spectra: host array of `order` spectra
  * (spectra[i] pairs with x[i]).  y doubles as the buffer between orders; y may equal v exactly but
- * must not overlap any x_i.  ws: hyena_workspace_bytes bytes.  On the matrix-core case (see
- * hyena_fftconv) up to 8 orders run in one launch with u_i kept on chip, rounded to bf16 exactly as a
- * store would round it, so the result equals `order` separate hyena_fftconv calls bit for bit. */
+ * must not overlap any x_i.  ws: hyena_workspace_bytes bytes.
+ * Engines: order <= 2 on the matrix-core case (see hyena_fftconv) runs both orders in one launch with u_1
+ * kept on chip, rounded to bf16 exactly as a store would round it, so the result equals `order` separate
+ * hyena_fftconv calls bit for bit.  Every other single-pass case (causal L <= 16384, periodic L <= 32768)
+ * runs up to 8 orders per launch of the fp32 engine with u_i kept on chip in fp32 (beyond 8 orders u passes
+ * through y, in the storage type, between launches); the multi-pass plans (longer rows, 3-D) chain the
+ * orders through the fp32 workspace.  Orders above 2 never take the matrix cores: their bf16 operands
+ * compound across orders past the bf16 tolerance. */
 int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *v,
                    const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,
                    hipStream_t stream);
@@ -196,7 +213,8 @@ int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D
  * bf16 before it is used, as hyena_operator rounds a stored intermediate. */
 int hyena_decode_state_bytes(int order, int64_t B, int64_t D, int64_t L, size_t *bytes);
 
-/* Clears the histories of a state buffer (enqueued on `stream`). */
+/* Clears a state buffer -- histories and prefix contributions -- before a new sequence (enqueued on
+ * `stream`). */
 int hyena_decode_reset(int order, int64_t B, int64_t D, int64_t L, void *state, size_t state_bytes,
                        hipStream_t stream);
 
@@ -215,7 +233,10 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
  * receives the operator's output on the prompt.  Each order runs the whole-row FFT convolution of its
  * history (the prompt, zero after it) and stores its gated output as the next order's history, so the next
  * call is hyena_decode_step at t = P, which starts a block.  spectra as for hyena_decode_step (no taps
- * needed).  y must not overlap the inputs or the state; the inputs must not overlap the state. */
+ * needed).  y must not overlap the inputs, the spectra or the state; the inputs and spectra must not overlap
+ * the state.  The steps that follow must pass the same `block` as the prefill (the state does not record it:
+ * with another block, t = P need not start a block and the step would read prefix contributions the prefill
+ * never wrote). */
 int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t block, int64_t P, int dtype, int mode,
                          const void *v, const void *const *x, const void *const *spectra, void *y, void *state,
                          size_t state_bytes, hipStream_t stream);
@@ -226,6 +247,11 @@ int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t blo
  * H[D, nx, ny, nz/2+1] (periodic). */
 int hyena_spectrum_export(hyena_dims dims, int mode, int64_t D, const void *spectrum, void *H,
                           hipStream_t stream);
+
+/* Uploads the library's constant tables to the current device (once per device; later calls return at
+ * once).  Optional: every other entry point does it on its first call on a device.  Call it before
+ * capturing library calls into a HIP graph, or to keep the first call free of the blocking upload. */
+int hyena_init(void);
 
 /* Static description of a status code. */
 const char *hyena_status_str(int status);

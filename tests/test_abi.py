@@ -72,9 +72,9 @@ def test_size_queries(lib):
     st, n = _size(lib.hyena_workspace_bytes, 2, 1, 3, L.dims_of([1 << 21]), L.F32, L.CIRCULAR)
     assert st == 0 and n == 3 * (1 << 20) * 8
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([1 << 16]), L.CIRCULAR, 2)
-    assert st == 0 and n == 2 * (1 << 15) * (8 + 4)        # fp32 spectrum + bf16 copy for the bf16 plans
+    assert st == 0 and n == 2 * (1 << 15) * 8               # fp32 spectrum (every plan keeps fp32 intermediates)
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([65536]), L.CAUSAL, 3)
-    assert st == 0 and n == 3 * 65536 * (8 + 4)
+    assert st == 0 and n == 3 * 65536 * 8
     # periodic 3-D: 64 x 64 x 33 bins per channel, intermediate 64 x-slabs of 64 x 33 per volume
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.CIRCULAR, 128)
     assert st == 0 and n == 128 * 64 * 64 * 33 * 8
@@ -150,7 +150,7 @@ def test_per_sample_sizes(lib):
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.LINEAR | L.PER_SAMPLE, 2 * 128)
     assert st == 0 and n == 2 * 128 * 128 * 128 * 65 * 8
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([65536]), L.CAUSAL | L.PER_SAMPLE, 6)
-    assert st == 0 and n == 6 * 65536 * (8 + 4)
+    assert st == 0 and n == 6 * 65536 * 8
     # workspace: FiLM vectors (B x 4 x 64 floats) and the transposed 64 x 64 and D x 64 weights (256-byte
     # rounded), taps of B*D filters, transform chunk
     scratch = lambda B, D: -(-(B * 4 * 64 + 64 * (64 + D)) * 4 // 256) * 256
@@ -253,6 +253,12 @@ def test_decode_sizes_and_rejects_before_launch(lib):
     assert prefill(block=3) == L.EUNSUPPORTED and prefill(dtype=9) == L.EINVAL
     assert prefill(st=state + 8) == L.EWORKSPACE
     assert prefill(yy=state + 1024) == L.EALIAS and prefill(yy=v + 8) == L.EALIAS
+    sp_in_state = (ctypes.c_void_p * 2)(1 << 47, state + 2048)
+    assert lib.hyena_decode_prefill(order, B, D, Lq, 64, 128, L.F32, L.CAUSAL, v, xs, sp_in_state, y, state, need,
+                                    None) == L.EALIAS             # a spectrum inside the state
+    y_in_sp = (ctypes.c_void_p * 2)(1 << 47, y - 64)
+    assert lib.hyena_decode_prefill(order, B, D, Lq, 64, 128, L.F32, L.CAUSAL, v, xs, y_in_sp, y, state, need,
+                                    None) == L.EALIAS             # the output inside a spectrum
     assert lib.hyena_decode_reset(order, B, D, Lq, state, need - 1, None) == L.EWORKSPACE
     assert lib.hyena_decode_reset(order, B, D, Lq, None, need, None) == L.EINVAL
 

@@ -4,7 +4,7 @@ import pytest
 
 import hyena_inputs as hi
 from oracle import hyena_oracle as orc
-from gpu_util import FP32_TOL, params_to_dev, rel_err_rows, say, to_dev
+from gpu_util import FP32_TOL, all_row_errors, params_to_dev, rel_err_rows, report_errors, say, to_dev
 
 pytestmark = pytest.mark.gpu
 N = 64
@@ -46,6 +46,26 @@ def test_filter3d_taps_and_spectrum(torch_cuda):
     Hg = H.cpu().numpy().astype(np.complex128)
     e = np.sqrt(np.sum(np.abs(Hg - Href) ** 2, axis=(1, 2, 3)) / np.sum(np.abs(Href) ** 2, axis=(1, 2, 3)))
     assert e.max() < 2e-5, e.max()
+
+
+def test_filter3d_taps_with_biases(torch_cuda):
+    """Non-zero hidden-layer and output biases (b1, b2): every 3-D tap against the oracle."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    D = 3
+    w = hi.WORKLOADS[4].with_(D=D)
+    p = hi.draw_filter_params(w, seed=43)[0]
+    rng = np.random.default_rng(43)
+    p["b1"] = rng.uniform(-1, 1, 64).astype(np.float32)
+    p["b2"] = rng.uniform(-1, 1, D).astype(np.float32)
+    say("3-D filter taps with biases, D=3")
+    h = torch.empty((D, 127, 127, 127), dtype=torch.float32, device="cuda")
+    hy.filter_gen(params_to_dev(p), (N, N, N), h_time=h)
+    torch.cuda.synchronize()
+    ref = orc.implicit_filter_3d(p, N)
+    e = rel_err_rows(h.cpu().numpy(), ref, point_axes=3)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < 1e-5, e.max()
 
 
 @pytest.mark.parametrize("gate", [False, True])
@@ -91,7 +111,9 @@ def test_conv3d_delta_filter(torch_cuda):
     assert e.max() < 1e-2, e.max()
 
 
-def test_operator3d_f32_D128_64cubed_sampled_channels(torch_cuda):
+@pytest.mark.timeout(600)
+def test_operator3d_f32_D128_64cubed_all_channels(torch_cuda):
+    """Workload 4 at full size: every one of the 128 volumes against the oracle."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
     w = hi.WORKLOADS[4]
@@ -102,11 +124,8 @@ def test_operator3d_f32_D128_64cubed_sampled_channels(torch_cuda):
     y = hy.operator(to_dev(v, torch.float32), [to_dev(x, torch.float32) for x in xs], spectra)
     torch.cuda.synchronize()
     y = y.cpu().numpy()
-    chans = [0, 37, 127]
-    say("  oracle on sampled channels")
-    hs = [orc.implicit_filter_3d(p, N, channels=chans) for p in params]
-    ref = orc.hyena_operator_3d(v[0, chans], [x[0, chans] for x in xs], hs)
-    e = rel_err_rows(y[0, chans], ref, point_axes=3)
-    say(f"  max rel err {e.max():.3e}")
-    assert e.max() < FP32_TOL
     assert np.all(np.isfinite(y))
+    say("  oracle on every volume")
+    e = all_row_errors(w, v, xs, params, y)
+    report_errors("workload 4", e)
+    assert e.max() < FP32_TOL

@@ -130,8 +130,8 @@ def test_decode_state_reuse_after_reset(torch_cuda):
 
 @pytest.mark.parametrize("order,B,D,L,block", [(2, 2, 8, 1024, 64), (3, 1, 4, 2048, 128)])
 def test_decode_bf16_tokens_match_oracle(torch_cuda, order, B, D, L, block):
-    """bf16 tokens (inputs rounded to bf16 once, as both sides see them; intermediates rounded like
-    stored ones on the GPU, not in the oracle)."""
+    """bf16 tokens (inputs rounded to bf16 once, as both sides see them; the GPU's intermediates u_i stay
+    fp32, only y_t is rounded)."""
     torch = torch_cuda
     w = hi.WORKLOADS[9].with_(order=order, B=B, D=D, dims=(L,), dtype="bf16")
     v, xs = hi.draw_activations(w, seed=L + block + 1)
@@ -170,7 +170,7 @@ def test_decode_bf16_layer_of_workload_1(torch_cuda):
     e2 = rel_err_rows(_rows(y), _rows(whole.float().cpu().numpy().astype(np.float64)))
     say(f"  every row vs the whole-sequence operator: max rel diff {e2.max():.3e}")
     # each path is held to BF16_TOL against the oracle (the operator's matrix-core transforms round their
-    # operands to bf16 and carry most of it), so their difference is bounded by the sum
+    # operands to bf16 and carry most of it), so their difference is bounded by the sum of the two
     assert e2.max() < 2 * BF16_TOL, e2.max()
 
 

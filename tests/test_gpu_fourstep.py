@@ -4,8 +4,8 @@ import pytest
 
 import hyena_inputs as hi
 from oracle import hyena_oracle as orc
-from gpu_util import (BF16_TOL, FP32_TOL, oracle_rows_1d, params_to_dev, rel_err_rows, run_hip_operator, say,
-                      to_dev)
+from gpu_util import (BF16_TOL, FP32_TOL, all_row_errors, oracle_rows_1d, params_to_dev, rel_err_rows,
+                      report_errors, run_hip_operator, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,38 +91,36 @@ def test_fourstep_no_gate_and_chunk_invariance(torch_cuda):
     assert rel_err_rows(c.cpu().numpy()[0], ref).max() < 5e-5
 
 
-def test_operator_bf16_order3_B2_D1024_L65536_sampled_rows(torch_cuda):
+@pytest.mark.timeout(600)
+def test_operator_bf16_order3_B2_D1024_L65536_all_rows(torch_cuda):
+    """Workload 2 at full size: every one of the 2048 (b, d) rows against the oracle."""
     w = hi.WORKLOADS[2]
     say("operator workload 2 (order 3, B=2 D=1024 L=65536, bf16): drawing inputs")
     v, xs = hi.draw_activations(w)
     params = hi.draw_filter_params(w)
     say("  running HIP operator")
-    y = run_hip_operator(w, v, xs, params)
-    rows = [tuple(r) for r in hi.sample_rows(w, 12)]
-    say("  oracle on sampled rows")
-    ref = oracle_rows_1d(w, v, xs, params, rows)
-    got = np.stack([y[b, d] for b, d in rows])
-    e = rel_err_rows(got, ref)
-    say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
-    assert e.max() < BF16_TOL
+    y = run_hip_operator(w, v, xs, params, host_dtype=np.float32)
     assert np.all(np.isfinite(y))
+    say("  oracle on every row")
+    e = all_row_errors(w, v, xs, params, y)
+    report_errors("workload 2", e)
+    assert e.max() < BF16_TOL
 
 
-def test_operator_f32_B1_D256_L1M_dna_sampled_rows(torch_cuda):
+@pytest.mark.timeout(600)
+def test_operator_f32_B1_D256_L1M_dna_all_rows(torch_cuda):
+    """Workload 3 at full size: every one of the 256 rows of 2^20 samples against the oracle."""
     w = hi.WORKLOADS[3]
     say("operator workload 3 (HyenaDNA order 2, B=1 D=256 L=1M, fp32): drawing inputs")
     v, xs = hi.draw_activations(w)
     params = hi.draw_filter_params(w)
     say("  running HIP operator")
-    y = run_hip_operator(w, v, xs, params)
-    rows = [tuple(r) for r in hi.sample_rows(w, 6)]
-    say("  oracle on sampled rows")
-    ref = oracle_rows_1d(w, v, xs, params, rows)
-    got = np.stack([y[b, d] for b, d in rows])
-    e = rel_err_rows(got, ref)
-    say(f"  max rel err {e.max():.3e} median {np.median(e):.3e}")
-    assert e.max() < FP32_TOL
+    y = run_hip_operator(w, v, xs, params, host_dtype=np.float32)
     assert np.all(np.isfinite(y))
+    say("  oracle on every row")
+    e = all_row_errors(w, v, xs, params, y)
+    report_errors("workload 3", e)
+    assert e.max() < FP32_TOL
 
 
 @pytest.mark.parametrize("L", [1 << 15, 1 << 16, 1 << 17, 1 << 20])

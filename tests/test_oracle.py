@@ -221,6 +221,49 @@ def test_filter_network_single_path():
             np.testing.assert_array_equal(h[other], np.full(L, b2[other]))
 
 
+def test_filter_network_hidden_bias_single_path():
+    """The hidden-layer bias b1 enters before the SiLU, one value per hidden unit: unit j carries a feature
+    plus its bias, unit m carries its bias alone (a constant SiLU(b1[m]) at every position), and channel d
+    reads both through W2.  A dropped b1, a b1 added after the SiLU, or a b1 indexed by channel instead of
+    by unit gives a different value."""
+    F = H = 64
+    D, L = 5, 64
+    j, m, k, d = 3, 17, 40, 2       # feature 40 = cos of frequency 9
+    W1 = np.zeros((H, F)); W1[j, k] = 1.5
+    b1 = np.linspace(-1.0, 1.0, H); b1[j] = 0.7; b1[m] = -1.2
+    W2 = np.zeros((D, H)); W2[d, j] = -2.0; W2[d, m] = 0.5
+    b2 = np.arange(D, dtype=float) * 0.25
+    p = dict(W1=W1, b1=b1, W2=W2, b2=b2, alpha=np.zeros(D))
+    h = orc.implicit_filter_1d(p, L)
+    t = np.arange(L)
+    zz = 1.5 * np.cos(2 * np.pi * 9 * t / L) + 0.7
+    const = 0.5 * (-1.2) / (1 + np.exp(1.2))
+    np.testing.assert_allclose(h[d], -2.0 * zz / (1 + np.exp(-zz)) + const + b2[d], atol=1e-13)
+    for other in range(D):
+        if other != d:
+            np.testing.assert_array_equal(h[other], np.full(L, b2[other]))
+    # at t = 0 the cosine feature is 1: a value checked by hand, SiLU(2.2) = 2.2 / (1 + e^-2.2)
+    assert h[d, 0] == pytest.approx(-2.0 * 2.2 / (1 + math.exp(-2.2)) + 0.5 * -1.2 / (1 + math.exp(1.2)) + 0.5,
+                                    abs=1e-13)
+
+
+def test_filter_network_hidden_bias_3d():
+    """The same hidden bias through the 3-D features: unit m with W1 row zero contributes W2[d, m] SiLU(b1[m])
+    at every offset, so the filter minus its window-free constant part is the single-feature path."""
+    n, D = 4, 3
+    F, H = 96, 64
+    W1 = np.zeros((H, F)); W1[5, 0] = 2.0             # unit 5 <- sin(2 pi r_x / n)
+    b1 = np.zeros(H); b1[5] = -0.3; b1[9] = 0.8
+    W2 = np.zeros((D, H)); W2[1, 5] = 1.0; W2[1, 9] = -1.0
+    p = dict(W1=W1, b1=b1, W2=W2, b2=np.zeros(D), alpha=np.zeros(D))
+    h = orc.implicit_filter_3d(p, n)                  # [D, 7, 7, 7]
+    rx = np.arange(-(n - 1), n)
+    zz = 2.0 * np.sin(2 * np.pi * rx / n) - 0.3       # depends on r_x only
+    ref = zz / (1 + np.exp(-zz)) - 0.8 / (1 + np.exp(-0.8))
+    np.testing.assert_allclose(h[1], np.broadcast_to(ref[:, None, None], h[1].shape), atol=1e-13)
+    np.testing.assert_array_equal(h[0], 0.0)
+
+
 def test_window_closed_form_and_channel_subset():
     rng = np.random.default_rng(15)
     p = _params(64, 64, 6, rng)
