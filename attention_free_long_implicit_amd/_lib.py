@@ -59,6 +59,8 @@ _SIG = {
     "hyena_operator": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, Dims, _c.c_int, _c.c_int, _c.c_void_p,
                                   _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p,
                                   _c.c_size_t, _c.c_void_p]),
+    "hyena_operator_noalloc": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, Dims, _c.c_int, _c.c_int, _c.c_void_p,
+                                          _c.POINTER(_c.c_void_p), _c.POINTER(_c.c_void_p), _c.c_void_p, _c.c_void_p]),
     "hyena_spectrum_export": (_c.c_int, [Dims, _c.c_int, _c.c_int64, _c.c_void_p, _c.c_void_p, _c.c_void_p]),
     "hyena_projection": (_c.c_int, [_c.c_int, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int64, _c.c_int, _c.c_void_p,
                                     _c.c_void_p, _c.c_void_p, _c.POINTER(_c.c_void_p), _c.c_void_p]),
@@ -314,6 +316,28 @@ def operator(v, xs: Sequence, spectra: Sequence, y=None, ws=None, mode: Optional
     sa = (ctypes.c_void_p * order)(*[_ptr(s) for s in spectra])
     _check(lib().hyena_operator(order, B, D, dims_of(pts), dt, mode, _ptr(v), xa, sa, _ptr(y), _ptr(ws),
                                 0 if ws is None else ws.numel(), _stream(v)), "hyena_operator")
+    return y
+
+
+def operator_noalloc(v, xs: Sequence, spectra: Sequence, y, mode: Optional[int] = None):
+    """The operator through hyena_operator_noalloc: no workspace, and nothing allocated here either, so y
+    (the output, shaped and typed like v) is required.  Calls on one device share the library's scratch:
+    order them on one stream."""
+    B, D = v.shape[:2]
+    pts = tuple(v.shape[2:])
+    order = len(xs)
+    if len(spectra) != order:
+        raise ValueError("need one spectrum per gate")
+    if y is None or y.shape != v.shape or y.dtype != v.dtype:
+        raise ValueError("y must be given, shaped and typed like v")
+    for x in xs:
+        if x.dtype != v.dtype or x.shape != v.shape:
+            raise ValueError("gates must match v in shape and dtype")
+    mode = mode_for(len(pts)) if mode is None else mode
+    xa = (ctypes.c_void_p * order)(*[_ptr(x) for x in xs])
+    sa = (ctypes.c_void_p * order)(*[_ptr(s) for s in spectra])
+    _check(lib().hyena_operator_noalloc(order, B, D, dims_of(pts), _dtype_code(v), mode, _ptr(v), xa, sa, _ptr(y),
+                                        _stream(v)), "hyena_operator_noalloc")
     return y
 
 

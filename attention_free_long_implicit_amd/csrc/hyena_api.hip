@@ -17,6 +17,8 @@ using namespace hyena;
 // uses that address.
 static __device__ __align__(256) float2 g_twiddle_table[kTwPow2Entries + kTwFine];
 static __device__ __align__(256) uint16_t g_matrix_table[kMfmaMatrixCount];
+// Workspace of hyena_operator_noalloc (the multi-pass intermediates), shared by every such call on a device.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -25,6 +27,7 @@ std::mutex g_mu;
 struct DeviceTables {
   Twiddles tw;
   const void* mats;       // DFT matrices of the matrix-core path (bf16, per lane)
+  void* scratch;          // this device's copy of `scratch`
   bool ready;
 };
 DeviceTables g_dev[kMaxDevices];
@@ -44,8 +47,10 @@ int init_current_device(DeviceTables** out) {
   if (!t.ready) {
     void* tw = nullptr;
     void* mats = nullptr;
+    void* scr = nullptr;
     if (hipGetSymbolAddress(&tw, HIP_SYMBOL(g_twiddle_table)) != hipSuccess || !tw) return HYENA_EHIP;
     if (hipGetSymbolAddress(&mats, HIP_SYMBOL(g_matrix_table)) != hipSuccess || !mats) return HYENA_EHIP;
+    if (hipGetSymbolAddress(&scr, HIP_SYMBOL(scratch)) != hipSuccess || !scr) return HYENA_EHIP;
     std::vector<float2> host(kTwPow2Entries + kTwFine);
     host[0] = make_float2(1.f, 0.f);
     for (int sz = 1; sz <= (1 << kTwPow2Log2); sz <<= 1)
@@ -60,6 +65,7 @@ int init_current_device(DeviceTables** out) {
     t.tw.pow2 = (const float2*)tw;
     t.tw.fine = (const float2*)tw + kTwPow2Entries;
     t.mats = mats;
+    t.scratch = scr;
     t.ready = true;
   }
   *out = &t;
@@ -293,6 +299,72 @@ int split_mode(int mode, bool* per_sample) {
   return mode & ~HYENA_PER_SAMPLE;
 }
 
+// hyena_operator with the workspace [ws, ws + ws_bytes); noalloc: the workspace is this device's `scratch`
+// (taken here, after validation), and a row whose intermediate does not fit it is rejected.
+int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void* v,
+                 const void* const* x, const void* const* spectra, void* y, void* ws, size_t ws_bytes,
+                 hipStream_t stream, bool noalloc) {
+  if (order < 1 || B <= 0 || D <= 0 || !v || !x || !spectra || !y || (dtype != HYENA_F32 && dtype != HYENA_BF16))
+    return HYENA_EINVAL;
+  for (int i = 0; i < order; ++i)
+    if (!x[i] || !spectra[i]) return HYENA_EINVAL;
+  if (B * D > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
+  bool ps = false;
+  mode = split_mode(mode, &ps);
+  const int hsb = ps ? (int)D : 0;
+  int64_t pts = 0;
+  int st = check_dims(dims, mode, &pts);
+  if (st) return st;
+  const int kind = kind_of(mode, dims);
+  const size_t tb = (size_t)B * D * pts * elem_bytes(dtype);
+  if (y != v && overlaps(y, tb, v, tb)) return HYENA_EALIAS;
+  for (int i = 0; i < order; ++i)
+    if (overlaps(y, tb, x[i], tb)) return HYENA_EALIAS;
+  int chunk = 0;
+  const size_t per = row_intermediate_bytes(kind, pts);
+  if (noalloc) {
+    if (per > kNoallocScratchBytes) return HYENA_EWORKSPACE;
+    DeviceTables* dt = nullptr;
+    if ((st = init_current_device(&dt))) return st;
+    ws = dt->scratch;
+    ws_bytes = kNoallocScratchBytes;
+  }
+  if (per) {
+    chunk = chunk_from_ws(per, B * D, ws, ws_bytes);
+    if (chunk < 1) return HYENA_EWORKSPACE;
+    if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
+    for (int i = 0; i < order; ++i)
+      if (overlaps(ws, ws_bytes, x[i], tb)) return HYENA_EALIAS;
+  }
+  Twiddles tw;
+  if ((st = get_twiddles(&tw))) return st;
+  if (chunk && is3d(kind))
+    return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws, chunk,
+                                    tw, stream, circ3(kind), hsb));
+  if (chunk)
+    return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
+                                             spectra, y, (float2*)ws, chunk, tw, stream,
+                                             kind == K_CIRC1 ? 1 : 0, hsb));
+  if (kind == K_CAUSAL && !hsb && order <= kMfmaMaxOrder && use_mfma(dtype, B, pts)) {
+    bool aligned = aligned16(v) && aligned16(y);
+    for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);
+    if (aligned) return conv_mfma_chain(B, D, pts, v, x, spectra, order, y, tw, stream);
+  }
+  // the single-pass fp32 engine: up to kConvMaxChain orders per launch with u_i on chip
+  const int lg = kind == K_CIRC1 ? circular_log2(pts) : log2i(pts);
+  const void* cur = v;
+  for (int i0 = 0; i0 < order; i0 += kConvMaxChain) {
+    const int n = order - i0 < kConvMaxChain ? order - i0 : kConvMaxChain;
+    const float2* sp[kConvMaxChain];
+    for (int k = 0; k < n; ++k) sp[k] = (const float2*)spectra[i0 + k];
+    if ((st = hip_status(launch_conv1d_chain(lg, dtype == HYENA_BF16, cur, x + i0, sp, n, y, (int)B, (int)D, tw,
+                                             stream, kind == K_CIRC1 ? 1 : 0, hsb))))
+      return st;
+    cur = y;
+  }
+  return HYENA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -489,58 +561,12 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
 int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void* v,
                    const void* const* x, const void* const* spectra, void* y, void* ws, size_t ws_bytes,
                    hipStream_t stream) {
-  if (order < 1 || B <= 0 || D <= 0 || !v || !x || !spectra || !y || (dtype != HYENA_F32 && dtype != HYENA_BF16))
-    return HYENA_EINVAL;
-  for (int i = 0; i < order; ++i)
-    if (!x[i] || !spectra[i]) return HYENA_EINVAL;
-  if (B * D > (int64_t)INT32_MAX) return HYENA_EUNSUPPORTED;
-  bool ps = false;
-  mode = split_mode(mode, &ps);
-  const int hsb = ps ? (int)D : 0;
-  int64_t pts = 0;
-  int st = check_dims(dims, mode, &pts);
-  if (st) return st;
-  const int kind = kind_of(mode, dims);
-  const size_t tb = (size_t)B * D * pts * elem_bytes(dtype);
-  if (y != v && overlaps(y, tb, v, tb)) return HYENA_EALIAS;
-  for (int i = 0; i < order; ++i)
-    if (overlaps(y, tb, x[i], tb)) return HYENA_EALIAS;
-  int chunk = 0;
-  const size_t per = row_intermediate_bytes(kind, pts);
-  if (per) {
-    chunk = chunk_from_ws(per, B * D, ws, ws_bytes);
-    if (chunk < 1) return HYENA_EWORKSPACE;
-    if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
-    for (int i = 0; i < order; ++i)
-      if (overlaps(ws, ws_bytes, x[i], tb)) return HYENA_EALIAS;
-  }
-  Twiddles tw;
-  if ((st = get_twiddles(&tw))) return st;
-  if (chunk && is3d(kind))
-    return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws, chunk,
-                                    tw, stream, circ3(kind), hsb));
-  if (chunk)
-    return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
-                                             spectra, y, (float2*)ws, chunk, tw, stream,
-                                             kind == K_CIRC1 ? 1 : 0, hsb));
-  if (kind == K_CAUSAL && !hsb && order <= kMfmaMaxOrder && use_mfma(dtype, B, pts)) {
-    bool aligned = aligned16(v) && aligned16(y);
-    for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);
-    if (aligned) return conv_mfma_chain(B, D, pts, v, x, spectra, order, y, tw, stream);
-  }
-  // the single-pass fp32 engine: up to kConvMaxChain orders per launch with u_i on chip
-  const int lg = kind == K_CIRC1 ? circular_log2(pts) : log2i(pts);
-  const void* cur = v;
-  for (int i0 = 0; i0 < order; i0 += kConvMaxChain) {
-    const int n = order - i0 < kConvMaxChain ? order - i0 : kConvMaxChain;
-    const float2* sp[kConvMaxChain];
-    for (int k = 0; k < n; ++k) sp[k] = (const float2*)spectra[i0 + k];
-    if ((st = hip_status(launch_conv1d_chain(lg, dtype == HYENA_BF16, cur, x + i0, sp, n, y, (int)B, (int)D, tw,
-                                             stream, kind == K_CIRC1 ? 1 : 0, hsb))))
-      return st;
-    cur = y;
-  }
-  return HYENA_OK;
+  return run_operator(order, B, D, dims, dtype, mode, v, x, spectra, y, ws, ws_bytes, stream, false);
+}
+
+int hyena_operator_noalloc(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void* v,
+                           const void* const* x, const void* const* spectra, void* y, hipStream_t stream) {
+  return run_operator(order, B, D, dims, dtype, mode, v, x, spectra, y, nullptr, 0, stream, true);
 }
 
 int hyena_projection(int order, int64_t B, int64_t L, int64_t d_model, int64_t D, int dtype, const void* x,

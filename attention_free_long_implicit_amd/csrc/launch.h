@@ -7,6 +7,9 @@
 
 namespace hyena {
 
+// Scratch of the entry point that allocates nothing (hyena_operator_noalloc): its multi-pass workspace.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+
 // ---- 1-D, one workgroup per row: an M = 2^log2L point packed transform, 10 <= log2L <= 14.
 // full = 0: causal, rows of M samples (zero-padded to 2M); full = 1: periodic, rows of 2M samples.
 bool single_pass_supported(int log2L);

@@ -173,6 +173,19 @@ int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, 
                    const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,
                    hipStream_t stream);
 
+/* hyena_operator without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the multi-pass
+ * intermediates go to a scratch array of 64 MiB that the library holds in every device's copy of its code
+ * object until the process ends; no call allocates (the first call on a device, unless hyena_init came
+ * first, uploads the constant tables with a blocking copy).  Same arguments, semantics and results as
+ * hyena_operator; the caller still owns v, x, spectra and y.  Rows whose intermediate exceeds the scratch
+ * return HYENA_EWORKSPACE (none of the supported sizes does: the largest is 8 MiB per row).  Every call
+ * on one device shares that device's scratch, which keeps the last call's contents: calls that overlap in
+ * time on one device (on different streams, or from different threads without ordering) race and give
+ * wrong results; calls ordered on one stream are safe. */
+int hyena_operator_noalloc(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *v,
+                           const void *const *x, const void *const *spectra, void *y, hipStream_t stream);
+
 /* The input projection (Hyena study note, step 1: v, x_1, ..., x_N = split(W_proj x); the listing
  * chunks the projected channels into N + 1 equal parts, v first):
  *   out[j][b, d, t] = sum_k W[j*D + d, k] * x[b, t, k] + bias[j*D + d],   j = 0..order

@@ -209,6 +209,18 @@ def test_projection_rejects_before_launch(lib):
     assert lib.hyena_projection(2, 2, 256, 64, 32, L.BF16, x, W, None, ox, None) == L.EALIAS
 
 
+def test_noalloc_rejects_before_launch(lib):
+    xs = (ctypes.c_void_p * 2)(1 << 43, 1 << 44)
+    sp = (ctypes.c_void_p * 2)(1 << 45, 1 << 46)
+    d1 = L.dims_of([1 << 17])
+    assert lib.hyena_operator_noalloc(0, 2, 8, d1, L.F32, L.CAUSAL, 1 << 41, xs, sp, 1 << 42, None) == L.EINVAL
+    assert lib.hyena_operator_noalloc(2, 2, 8, d1, 7, L.CAUSAL, 1 << 41, xs, sp, 1 << 42, None) == L.EINVAL
+    assert lib.hyena_operator_noalloc(2, 2, 8, L.dims_of([3000]), L.F32, L.CAUSAL, 1 << 41, xs, sp, 1 << 42,
+                                      None) == L.EUNSUPPORTED
+    assert lib.hyena_operator_noalloc(2, 2, 8, d1, L.F32, L.CAUSAL, 1 << 41, xs, sp, (1 << 41) + 64,
+                                      None) == L.EALIAS
+
+
 def test_decode_sizes_and_rejects_before_launch(lib):
     n = ctypes.c_size_t()
     # histories and prefix contributions, fp32, two planes per order; no workspace below 32768 points
