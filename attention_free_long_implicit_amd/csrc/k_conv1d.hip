@@ -79,6 +79,7 @@ k_conv1d(const typename Store<BF16>::elem* u, ConvChain ch, int order, typename 
     Twiddles tw = tw0;
     asm volatile("" : "+v"(t));
     asm volatile("" : "+s"(tw.pow2), "+s"(tw.fine));
+    t &= T - 1;                               // restores the range the index arithmetic is specialised on
     const auto P = C::NP::of(t);
     En::template forward_to_last<!FULL>(x, lds, tw, t);
     En::fwd_last(x, lds, P.betaA, P.betaB);
