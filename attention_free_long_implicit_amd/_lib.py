@@ -211,6 +211,66 @@ def filter_gen(params: dict, point_shape: Sequence[int], h_time=None, spectrum=N
     return spectrum
 
 
+class SpectrumCache:
+    """Filter spectra cached per (parameters, grid, mode): the implicit filter is a function of the position, so
+    one set of parameters gives one spectrum per grid size, which the operator reuses on every call at that size
+    (the Hyena study note's filter adapts to any sequence length; it need not be rebuilt per call).
+
+    The key holds, for every parameter tensor, its device, storage address, shape and version counter (torch
+    bumps the counter on every in-place change), so updating a parameter in place, or passing other tensors,
+    builds a new spectrum.  At most `max_entries` spectra are kept (least recently used dropped first).
+    `builder(params, point_shape, mode)` makes a spectrum (filter_gen by default)."""
+
+    def __init__(self, max_entries: int = 64, builder=None):
+        from collections import OrderedDict
+        self.max_entries = max_entries
+        self.builder = builder if builder is not None else (lambda p, shape, mode: filter_gen(p, shape, mode=mode))
+        self._d = OrderedDict()
+        self.builds = 0
+
+    @staticmethod
+    def key(params: dict, point_shape: Sequence[int], mode: int):
+        parts = tuple((k, str(t.device), t.data_ptr(), tuple(t.shape), t._version) for k, t in sorted(params.items()))
+        return parts, tuple(int(n) for n in point_shape), int(mode)
+
+    def get(self, params: dict, point_shape: Sequence[int], mode: Optional[int] = None):
+        mode = mode_for(len(point_shape)) if mode is None else mode
+        k = self.key(params, point_shape, mode)
+        sp = self._d.get(k)
+        if sp is None:
+            sp = self.builder(params, tuple(point_shape), mode)
+            self.builds += 1
+            self._d[k] = sp
+            while len(self._d) > self.max_entries:
+                self._d.popitem(last=False)
+        else:
+            self._d.move_to_end(k)
+        return sp
+
+    def clear(self):
+        self._d.clear()
+
+
+_default_cache = None
+
+
+def default_spectrum_cache() -> SpectrumCache:
+    global _default_cache
+    if _default_cache is None:
+        _default_cache = SpectrumCache()
+    return _default_cache
+
+
+def hyena(v, xs: Sequence, filter_params: Sequence[dict], y=None, mode: Optional[int] = None,
+          cache: Optional[SpectrumCache] = None):
+    """The order-N operator from filter parameters (one dict per order, as filter_gen takes): spectra come from
+    the cache (built on the first call at a grid size, reused afterwards), then operator()."""
+    cache = default_spectrum_cache() if cache is None else cache
+    pts = tuple(v.shape[2:])
+    spectra = [cache.get(p, pts, mode) for p in filter_params]
+    return operator(v, xs, spectra, y=y, mode=mode)
+
+
 def film_filter_workspace_bytes(B: int, point_shape: Sequence[int], D: int, mode: Optional[int] = None) -> int:
     n = ctypes.c_size_t()
     mode = mode_for(len(point_shape)) if mode is None else mode

@@ -110,18 +110,59 @@ def film_network_flops(w) -> float:
     return 2.0 * w.B * w.support * w.hidden * (w.ndim + w.hidden + w.D)
 
 
+def host_cores() -> int:
+    """Cores this process may run on (the GPU machine's own share)."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _pool_rows(work, rows, budget_s: float, cores: int):
+    """Run work(row) for rows on a pool of `cores` threads (numpy's FFTs release the interpreter lock, so the
+    threads run in parallel; BLAS is limited to one thread per call), in rounds of 4*cores rows until
+    budget_s of wall time has passed.  Returns (rows done, wall seconds)."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    done, wall = 0, 0.0
+    with threadpool_limits(1), ThreadPoolExecutor(cores) as ex:
+        for k in range(0, len(rows), 4 * cores):
+            batch = rows[k:k + 4 * cores]
+            t0 = time.perf_counter()
+            list(ex.map(work, batch))
+            wall += time.perf_counter() - t0
+            done += len(batch)
+            print(f"cpu baseline: {done} rows, {wall:.1f} s", file=sys.stderr, flush=True)
+            if wall >= budget_s:
+                break
+    return done, wall
+
+
+def _cpu_result(w, done, wall, cores, what):
+    return {"value": done * w.points / wall, "unit": "tokens·channels/s", "cores": cores, "kind": "oracle",
+            "cpu_model": host_cpu_model(),
+            "sample": f"{done} of {w.B * w.D} (b,d) rows of the same workload, order {w.order}, {what}; float64 numpy "
+                      f"FFT convolution on a pool of {cores} threads (one per core of this process's CPU set; numpy's "
+                      f"FFT releases the interpreter lock), {wall:.1f} s of wall time"}
+
+
 def cpu_baseline_film(w, v, xs, fparams, reg, budget_s: float):
     """The oracle on whole (b, d) volumes/rows of the input-dependent workload: per row, both orders'
     filters for that (b, d) (register summary, FiLM-SIREN on every tap, window) and then the operator,
     all inside the timed part, as the GPU step builds its filters per call."""
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(1):                  # one core: the matrix products would use every BLAS thread
-        return _cpu_baseline_film(w, v, xs, fparams, reg, budget_s)
-
-
-def _cpu_baseline_film(w, v, xs, fparams, reg, budget_s: float):
     from oracle import hyena_oracle as orc
-    rows = hi.sample_rows(w, 4096, seed=99)
+    rows = [tuple(r) for r in hi.sample_rows(w, 4096, seed=99)]
     circ = w.mode == "circular"
     if w.ndim == 1:
         offs = np.arange(w.dims[0])[:, None]
@@ -133,9 +174,9 @@ def _cpu_baseline_film(w, v, xs, fparams, reg, budget_s: float):
         c = offs.astype(np.float64) / n
         m = n if circ else 2 * n - 1
         shape = (1, m, m, m)
-    n_done, t_used = 0, 0.0
-    for b, d in rows:
-        t0 = time.perf_counter()
+
+    def work(bd):
+        b, d = bd
         hs = []
         for p in fparams:
             z = orc.register_summary(reg[b:b + 1], p["q"])[0]
@@ -151,66 +192,51 @@ def _cpu_baseline_film(w, v, xs, fparams, reg, budget_s: float):
             orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], hs, circular=circ)
         else:
             orc.hyena_operator_3d(v[b, d][None], [x[b, d][None] for x in xs], hs, circular=circ)
-        t_used += time.perf_counter() - t0
-        n_done += 1
-        print(f"cpu baseline: row {n_done} done ({t_used:.1f} s)", file=sys.stderr, flush=True)
-        if t_used >= budget_s:
-            break
-    return {"value": n_done * w.points / t_used, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_done} of {w.B * w.D} (b,d) rows of the same workload, order {w.order}, each with its "
-                      f"own input-dependent filters built inside the timed part (float64 numpy, FFT "
-                      f"convolution, BLAS limited to one thread); {t_used:.1f} s"}
+
+    cores = host_cores()
+    done, wall = _pool_rows(work, rows, budget_s, cores)
+    return _cpu_result(w, done, wall, cores, "each with its own input-dependent filters built inside the timed part")
 
 
 def cpu_baseline(w, v, xs, params, budget_s: float, proj_inputs=None):
-    """The oracle as it stands on whole (b, d) rows (volumes) of the same workload, until about
-    budget_s seconds of oracle time; the filters of the sampled channels are built outside the
-    timed part (as the GPU's spectra are), and building stops once it has taken 3 x budget_s.
-    With proj_inputs (x, W_proj, bias) each row's v, x_1..x_N come from the oracle's projection of the
-    token-major input, inside the timed part."""
-    from threadpoolctl import threadpool_limits
-    with threadpool_limits(1):                  # one core, also for the projection's matrix products
-        return _cpu_baseline(w, v, xs, params, budget_s, proj_inputs)
-
-
-def _cpu_baseline(w, v, xs, params, budget_s: float, proj_inputs):
+    """The oracle as it stands on whole (b, d) rows (volumes) of the same workload, on a thread pool over the
+    host's cores, until about budget_s seconds of wall time; the filters of the sampled channels are built
+    before the timed part (as the GPU's spectra are).  With proj_inputs (x, W_proj, bias) each row's v,
+    x_1..x_N come from the oracle's projection of the token-major input, inside the timed part."""
     from oracle import hyena_oracle as orc
-    rows = hi.sample_rows(w, 4096, seed=99)
+    from threadpoolctl import threadpool_limits
+    cores = host_cores()
+    rows = [tuple(r) for r in hi.sample_rows(w, 4096, seed=99)]
     circ = w.mode == "circular"
-    filt = {}
-    n_done, t_used, t_build = 0, 0.0, 0.0
-    for b, d in rows:
-        if d not in filt:
-            if t_build > 3 * budget_s and n_done > 0:
-                break
-            tb = time.perf_counter()
-            if w.ndim == 1:
-                filt[d] = [orc.implicit_filter_1d(p, w.dims[0], channels=[d]) for p in params]
-            elif circ:
-                filt[d] = [orc.implicit_filter_3d_circular(p, w.dims[0], channels=[d]) for p in params]
-            else:
-                filt[d] = [orc.implicit_filter_3d(p, w.dims[0], channels=[d]) for p in params]
-            t_build += time.perf_counter() - tb
-            print(f"cpu baseline: filters for channel {d} built ({t_build:.1f} s so far)", file=sys.stderr, flush=True)
-        t0 = time.perf_counter()
+    need = sorted({d for _, d in rows})
+    t0 = time.perf_counter()
+    with threadpool_limits(cores):
+        if w.ndim == 1:
+            built = [orc.implicit_filter_1d(p, w.dims[0], channels=need) for p in params]
+        elif circ:
+            built = [orc.implicit_filter_3d_circular(p, w.dims[0], channels=need) for p in params]
+        else:
+            built = [orc.implicit_filter_3d(p, w.dims[0], channels=need) for p in params]
+    print(f"cpu baseline: filters of {len(need)} channels built in {time.perf_counter() - t0:.1f} s",
+          file=sys.stderr, flush=True)
+    index = {d: k for k, d in enumerate(need)}
+
+    def work(bd):
+        b, d = bd
+        hs = [h[index[d]][None] for h in built]
         if proj_inputs is not None:
             xt, Wp, bp = proj_inputs
             sel = [j * w.D + d for j in range(w.order + 1)]
             rows_p = orc.input_projection(xt[b:b + 1], Wp[sel], bp[sel], w.order)     # each [1, 1, L]
-            orc.hyena_operator_rows(rows_p[0][0], [r[0] for r in rows_p[1:]], filt[d], circular=circ)
+            orc.hyena_operator_rows(rows_p[0][0], [r[0] for r in rows_p[1:]], hs, circular=circ)
         elif w.ndim == 1:
-            orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], filt[d], circular=circ)
+            orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], hs, circular=circ)
         else:
-            orc.hyena_operator_3d(v[b, d][None], [x[b, d][None] for x in xs], filt[d], circular=circ)
-        t_used += time.perf_counter() - t0
-        n_done += 1
-        if t_used >= budget_s:
-            break
-    return {"value": n_done * w.points / t_used, "unit": "tokens·channels/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_done} of {w.B * w.D} (b,d) rows of the same workload, order {w.order}, float64 numpy FFT "
-                      f"convolution on one core (numpy.fft is single-threaded, BLAS limited to one thread)"
-                      f"{', each row projected from the token-major input' if proj_inputs is not None else ''}"
-                      f", filters prebuilt; {t_used:.1f} s"}
+            orc.hyena_operator_3d(v[b, d][None], [x[b, d][None] for x in xs], hs, circular=circ)
+
+    done, wall = _pool_rows(work, rows, budget_s, cores)
+    what = "each row projected from the token-major input" if proj_inputs is not None else "filters prebuilt"
+    return _cpu_result(w, done, wall, cores, what)
 
 
 def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=10):
@@ -398,21 +424,211 @@ def run_decode(args, w, torch, hy, _lib):
     return out
 
 
+def build_step(w, torch, hy, _lib, dev):
+    """Device inputs of workload w and the step closure (one pass of the whole hot path over the batch).
+    Returns a dict: step, y, v, xs, params (host), filter_gen_ms, and the extra pieces of the input-dependent
+    and projection workloads."""
+    film = w.filter == "film"
+    proj = w.d_model > 0
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_film_params(w) if film else hi.draw_filter_params(w)
+    reg = hi.draw_registers(w) if film else None
+    vd = torch.from_numpy(v).to(dev).to(dt)
+    xd = [torch.from_numpy(x).to(dev).to(dt) for x in xs]
+    pd = [{k: torch.from_numpy(a).to(dev) for k, a in p.items()} for p in params]
+    y = torch.empty_like(vd)
+    mode = {"causal": _lib.CAUSAL, "linear": _lib.LINEAR, "circular": _lib.CIRCULAR}[w.mode]
+    ws_n = _lib.workspace_bytes(w.order, w.B, w.D, w.dims, _lib.BF16 if w.dtype == "bf16" else _lib.F32, mode)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
+    r = {"v": v, "xs": xs, "params": params, "reg": reg, "y": y, "vd": vd, "xd": xd, "pd": pd, "mode": mode,
+         "film": film, "proj": proj, "filter_gen_ms": None}
+    if proj:
+        xtok, Wp, bp = hi.draw_projection(w)
+        r["proj_inputs"] = (xtok, Wp, bp)
+        xtd = torch.from_numpy(xtok).to(dev).to(dt)
+        Wpd = torch.from_numpy(Wp).to(dev).to(dt)
+        bpd = torch.from_numpy(bp).to(dev)
+        pouts = [vd] + xd                       # the projection writes v, x_1..x_N in place of the drawn ones
+        r["projection"] = lambda: hy.projection(xtd, Wpd, w.order, bias=bpd, outs=pouts)
+    if film:
+        # per-sample filters: rebuilt inside every step into preallocated spectra and workspace
+        regd = torch.from_numpy(reg).to(dev)
+        op_mode = mode | _lib.PER_SAMPLE
+        spectra = [torch.empty(_lib.spectrum_bytes(w.dims, w.B * w.D, op_mode), dtype=torch.uint8, device=dev)
+                   for _ in pd]
+        fws = torch.empty(_lib.film_filter_workspace_bytes(w.B, w.dims, w.D, mode), dtype=torch.uint8, device=dev)
+        r["film_taps_only"] = lambda taps: hy.film_filter_gen(pd[0], regd, w.dims, h_time=taps, mode=mode, ws=fws,
+                                                              taps_only=True)
+
+        def step():
+            for p, sp in zip(pd, spectra):
+                hy.film_filter_gen(p, regd, w.dims, spectrum=sp, mode=mode, ws=fws)
+            hy.operator(vd, xd, spectra, y=y, ws=ws, mode=op_mode)
+    else:
+        # filter spectra (cached per grid): timed separately
+        spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
+        torch.cuda.synchronize()
+        fg = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
+            torch.cuda.synchronize()
+            fg.append(time.perf_counter() - t0)
+        r["filter_gen_ms"] = 1e3 * min(fg)
+        projection = r.get("projection")
+
+        def step():
+            if projection is not None:
+                projection()
+            hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
+    r["step"] = step
+    return r
+
+
+def time_back_to_back(torch, stream, step, n: int) -> float:
+    """ms per step over n steps launched back to back, bracketed by two events on the launch stream."""
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(n):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n
+
+
+def time_evicted(torch, stream, step, n: int, scratch, blocks: int = 5) -> list:
+    """ms per step with nothing of the step's working set cached: in each of `blocks` blocks, n/blocks steps
+    each launched right after a write of `scratch` (several times the 256 MB memory-side cache), timed as a
+    whole, minus the same number of scratch writes alone; both bracketed by two events on the launch stream,
+    so no event sits between a write and its step.  A step's cost includes the write-back of its outputs
+    that the next eviction forces.  Returns the per-block figures."""
+    per = max(1, n // blocks)
+    out = []
+    for k in range(-1, blocks):                 # block -1: untimed, settles the writes and the clocks
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(per):
+            scratch.fill_(float(i))
+            step()
+        ev[1].record(stream)
+        for i in range(per):
+            scratch.fill_(float(i))
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        if k >= 0:
+            out.append((ev[0].elapsed_time(ev[1]) - ev[1].elapsed_time(ev[2])) / per)
+    return out
+
+
+def sampled_parity(w, v, xs, params, y_host, rows):
+    """Per-row relative L2 error of the GPU output against the oracle on the given (b, d) rows (1-D workloads
+    with shared filters), computed on a thread pool: {"rows", "max", "median", "tolerance"}."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    from oracle import hyena_oracle as orc
+    circ = w.mode == "circular"
+    chans = sorted({int(d) for _, d in rows})
+    with threadpool_limits(host_cores()):
+        hs = [orc.implicit_filter_1d(p, w.dims[0], channels=chans) for p in params]
+    index = {d: k for k, d in enumerate(chans)}
+
+    def one(bd):
+        b, d = int(bd[0]), int(bd[1])
+        ref = orc.hyena_operator_rows(v[b, d][None], [x[b, d][None] for x in xs], [h[index[d]][None] for h in hs],
+                                      circular=circ)
+        return orc.rel_l2_per_row(np.asarray(y_host[b, d], np.float64)[None], ref)[0]
+    with threadpool_limits(1), ThreadPoolExecutor(host_cores()) as ex:
+        e = np.asarray(list(ex.map(one, rows)))
+    return {"rows": int(len(rows)), "of_rows": w.B * w.D, "max": float(e.max()), "median": float(np.median(e)),
+            "tolerance": 2e-2 if w.dtype == "bf16" else 1e-4,
+            "measure": "relative L2 error per (b, d) row against the float64 oracle"}
+
+
+TIMING_NOTE = ("ms_per_step: the timed steps run each right after a 1 GiB device write that evicts the 256 MB "
+               "memory-side cache, so every input comes from HBM; per block of steps, the time of the writes and "
+               "steps together minus that of the writes alone (two HIP events on the launch stream per block), "
+               "median over 5 blocks; warm: the same step launched back to back (its working set partly cached)")
+
+
+def measure(w, args, torch, hy, _lib, dev, stream, scratch, warm_steps: int, cold_steps: int, parity_rows=None):
+    """The timed part for one workload: W warm-up steps, cold_steps evicted steps (the headline), then
+    warm_steps back-to-back steps.  Returns (result dict, build dict)."""
+    r = build_step(w, torch, hy, _lib, dev)
+    step = r["step"]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    cold = time_evicted(torch, stream, step, cold_steps, scratch)
+    cold_ms = float(np.median(cold))
+    res_blocks = [float(c) for c in cold]
+    warm_ms = time_back_to_back(torch, stream, step, warm_steps) if warm_steps > 0 else None
+    T = w.tokens_channels
+    alg_step = algorithmic_bytes_per_order(w) * w.order
+    res = {"ms_per_step": cold_ms, "value": T / (cold_ms / 1e3),
+           "hbm_gbps_alg": alg_step / (cold_ms / 1e3) / 1e9,
+           "hbm_frac_alg": alg_step / (cold_ms / 1e3) / 1e9 / PEAK_HBM_GBPS,
+           "cold_ms_blocks": res_blocks}
+    if warm_ms is not None:
+        res["warm"] = {"ms_per_step": warm_ms, "steps": warm_steps, "value": T / (warm_ms / 1e3),
+                       "hbm_frac_alg": alg_step / (warm_ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+    if parity_rows is not None and not r["film"] and not r["proj"] and w.ndim == 1:
+        y_host = r["y"].float().cpu().numpy()
+        res["parity"] = sampled_parity(w, r["v"], r["xs"], r["params"], y_host, parity_rows)
+    return res, r
+
+
+def roofline_object(w, launch_ms: float, per_step: bool):
+    """HBM roofline of the dominant kernel (per_step: the whole step, when a step is several kernels)."""
+    key = kernel_key(w)
+    if per_step:
+        alg = algorithmic_bytes_per_order(w) * w.order
+        achieved = alg / (launch_ms / 1e3) / 1e9
+        return {"bound": "hbm", "kernel": key + " (whole step)", "achieved": achieved, "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": load_traffic(key),
+                "launch_ms": launch_ms, "alg_bytes_per_step": alg}
+    if uses_matrix_cores(w):
+        alg = algorithmic_bytes_per_order(w) * w.order        # one launch runs every order
+        floor = floor_bytes_per_step(w)
+        achieved = alg / (launch_ms / 1e3) / 1e9
+        return {"bound": "hbm", "kernel": key, "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBPS, "traffic": load_traffic(key), "launch_ms": launch_ms,
+                "alg_bytes_per_launch": alg, "floor_bytes_per_launch": floor,
+                "floor_frac": floor / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
+    alg = algorithmic_bytes_per_order(w) * w.order            # one fused launch runs every order
+    achieved = alg / (launch_ms / 1e3) / 1e9
+    return {"bound": "hbm", "kernel": key, "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS, "traffic": load_traffic(key), "launch_ms": launch_ms,
+            "alg_bytes_per_launch": alg}
+
+
+def config_block(w):
+    return {"workload": w.name, "order": w.order, "B": w.B, "D": w.D, "grid": list(w.dims), "boundary": w.mode,
+            "storage": w.dtype, "arithmetic": arithmetic(w), "alpha_range": [w.alpha_lo, w.alpha_hi],
+            "inputs": f"numpy default_rng([{w.index}, stream]): stream 0 activations, stream 1 filter parameters"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU reaches steady-state clocks only under sustained load: 0.1 s of warm-up and timed work
-    # (workload 1) measures that state; 50 steps after 5 read about 15 % slower
-    ap.add_argument("--steps", type=int, default=None, help="default 1000 (decode: one whole sequence, L tokens)")
-    ap.add_argument("--warmup", type=int, default=None, help="default 100 (decode: 512 tokens)")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps, each after a cache-evicting write (default 200; decode: one whole "
+                         "sequence, L tokens)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps first (default 100; decode: 512 tokens)")
+    ap.add_argument("--warm-steps", type=int, default=1000,
+                    help="back-to-back steps timed after the evicted ones (reported as warm; 0 skips them).  The "
+                         "GPU reaches steady clocks only under sustained load: 0.1 s of back-to-back work measures "
+                         "that state")
     ap.add_argument("--workload", type=int, default=1, help="index into hyena_inputs.WORKLOADS")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle wall time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device copy-bandwidth probe")
-    ap.add_argument("--cold-steps", type=int, default=50,
-                    help="after the timed region, this many more steps, each after a scratch write that evicts the "
-                         "256 MB memory-side cache, timed one by one (reported as cold_cache; 0 skips them)")
-    ap.add_argument("--evict-mb", type=int, default=1024, help="size of that scratch write")
+    ap.add_argument("--no-parity", action="store_true", help="skip the oracle check of the bench's own output")
+    ap.add_argument("--no-config3", action="store_true",
+                    help="skip the nested line of the 2^20-sample fp32 workload (the second target configuration)")
+    ap.add_argument("--evict-mb", type=int, default=1024, help="size of the cache-evicting write")
     ap.add_argument("--decode-block", type=int, default=0, help="decode workloads: tokens per prefix block "
                                                                "(0: the workload's own)")
     args = ap.parse_args()
@@ -429,131 +645,45 @@ def main():
 
     w = hi.WORKLOADS[args.workload]
     if args.steps is None:
-        args.steps = w.dims[0] if w.decode_block else 1000
+        args.steps = w.dims[0] if w.decode_block else 200
     if args.warmup is None:
         args.warmup = 512 if w.decode_block else 100
     if w.decode_block:
         out = run_decode(args, w, torch, hy, _lib)
         print(json.dumps(out), flush=True)
         return
-    film = w.filter == "film"
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    v, xs = hi.draw_activations(w)
-    params = hi.draw_film_params(w) if film else hi.draw_filter_params(w)
-    reg = hi.draw_registers(w) if film else None
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    vd = torch.from_numpy(v).to(dev).to(dt)
-    xd = [torch.from_numpy(x).to(dev).to(dt) for x in xs]
-    pd = [{k: torch.from_numpy(a).to(dev) for k, a in p.items()} for p in params]
-    y = torch.empty_like(vd)
-    mode = {"causal": _lib.CAUSAL, "linear": _lib.LINEAR, "circular": _lib.CIRCULAR}[w.mode]
-    ws_n = _lib.workspace_bytes(w.order, w.B, w.D, w.dims, _lib.BF16 if w.dtype == "bf16" else _lib.F32, mode)
-    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev) if ws_n else None
     stream = torch.cuda.current_stream(dev)
-
-    proj = w.d_model > 0
-    if proj:
-        xtok, Wp, bp = hi.draw_projection(w)
-        xtd = torch.from_numpy(xtok).to(dev).to(dt)
-        Wpd = torch.from_numpy(Wp).to(dev).to(dt)
-        bpd = torch.from_numpy(bp).to(dev)
-        pouts = [vd] + xd                       # the projection writes v, x_1..x_N in place of the drawn ones
-
-    if film:
-        # per-sample filters: rebuilt inside every step into preallocated spectra and workspace
-        regd = torch.from_numpy(reg).to(dev)
-        op_mode = mode | _lib.PER_SAMPLE
-        spectra = [torch.empty(_lib.spectrum_bytes(w.dims, w.B * w.D, op_mode), dtype=torch.uint8, device=dev)
-                   for _ in pd]
-        fws = torch.empty(_lib.film_filter_workspace_bytes(w.B, w.dims, w.D, mode), dtype=torch.uint8, device=dev)
-
-        def step():
-            for p, sp in zip(pd, spectra):
-                hy.film_filter_gen(p, regd, w.dims, spectrum=sp, mode=mode, ws=fws)
-            hy.operator(vd, xd, spectra, y=y, ws=ws, mode=op_mode)
-        filter_gen_ms = None
-    else:
-        # filter spectra (cached per grid): timed separately
-        spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
-        torch.cuda.synchronize()
-        fg = []
-        for _ in range(3):
-            t0 = time.perf_counter()
-            spectra = [hy.filter_gen(p, w.dims, mode=mode) for p in pd]
-            torch.cuda.synchronize()
-            fg.append(time.perf_counter() - t0)
-        filter_gen_ms = 1e3 * min(fg)
-
-        def step():
-            if proj:
-                hy.projection(xtd, Wpd, w.order, bias=bpd, outs=pouts)
-            hy.operator(vd, xd, spectra, y=y, ws=ws, mode=mode)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # two events on the launch stream bracket the timed region (an event after every step would add
-    # its own few microseconds to each step)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for k in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = np.full(args.steps, ev0.elapsed_time(ev1) / args.steps)
-    ms_per_step = 1e3 * wall / args.steps
-
-    # Back-to-back steps reread the same buffers, part of which the memory-side cache still holds.  The
-    # cold figure evicts it before every step (a scratch write several times its size) and times each
-    # step by its own events (which add a few microseconds per step).
-    cold = None
-    if args.cold_steps > 0:
-        scratch = torch.empty(args.evict_mb << 18, dtype=torch.float32, device=dev)
-        marks = []
-        torch.cuda.synchronize()
-        for k in range(args.cold_steps):
-            scratch.fill_(float(k))
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            step()
-            e1.record(stream)
-            marks.append((e0, e1))
-        torch.cuda.synchronize()
-        cold_ms = float(np.median([a.elapsed_time(b) for a, b in marks]))
-        del scratch
-        cold = {"ms_per_step": cold_ms, "steps": args.cold_steps, "evict_mb": args.evict_mb,
-                "value": w.tokens_channels / (cold_ms / 1e3),
-                "hbm_frac_alg": algorithmic_bytes_per_order(w) * w.order / (cold_ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
-    T = w.tokens_channels
-    value = T / (ms_per_step / 1e3)
-    alg_step = algorithmic_bytes_per_order(w) * w.order
+    scratch = torch.empty(args.evict_mb << 18, dtype=torch.float32, device=dev)
+    parity_rows = None
+    if not args.no_parity and w.ndim == 1 and w.filter != "film" and not w.d_model:
+        parity_rows = [tuple(r) for r in hi.sample_rows(w, 4096, seed=5)]      # every row up to 4096
+    t_wall = time.perf_counter()
+    res, r = measure(w, args, torch, hy, _lib, dev, stream, scratch, args.warm_steps, args.steps, parity_rows)
+    film, proj = r["film"], r["proj"]
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": res["value"],
         "unit": "tokens·channels/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": res["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded activations, Xavier-uniform filter networks; see hyena_inputs)",
-        "config": {"workload": w.name, "order": w.order, "B": w.B, "D": w.D, "grid": list(w.dims),
-                   "boundary": w.mode, "storage": w.dtype, "arithmetic": arithmetic(w),
-                   "alpha_range": [w.alpha_lo, w.alpha_hi],
-                   "inputs": f"numpy default_rng([{w.index}, stream]): stream 0 activations, stream 1 filter parameters"},
-        "hbm_gbps_alg": alg_step / (ms_per_step / 1e3) / 1e9,
-        "hbm_frac_alg": alg_step / (ms_per_step / 1e3) / 1e9 / PEAK_HBM_GBPS,
-        "event_ms_per_step": float(np.mean(step_ms)),
-        "filter_gen_ms": filter_gen_ms,
+        "config": config_block(w),
+        "timing": TIMING_NOTE,
+        "hbm_gbps_alg": res["hbm_gbps_alg"],
+        "hbm_frac_alg": res["hbm_frac_alg"],
+        "filter_gen_ms": r["filter_gen_ms"],
     }
+    for k in ("warm", "parity", "cold_ms_blocks"):
+        if k in res:
+            out[k] = res[k]
     if film:
         out["data"] = ("synthetic (seeded activations and register activations, SIREN/FiLM parameters drawn as in "
                        "hyena_inputs.draw_film_params)")
@@ -563,24 +693,10 @@ def main():
                               "sigma_range": [w.sigma_lo, w.sigma_hi],
                               "inputs": f"numpy default_rng([{w.index}, stream]): stream 0 activations, stream 1 "
                                         f"filter parameters, stream 2 register activations"})
-    if cold is not None:
-        out["cold_cache"] = cold
-    key = kernel_key(w)
-    if film:
         # dominant kernel: the filter network, timed alone (taps only: register summary + taps launch)
         taps = torch.empty((w.B, w.D, w.support), dtype=torch.float32, device=dev)
-        for _ in range(3):
-            hy.film_filter_gen(pd[0], regd, w.dims, h_time=taps, mode=mode, ws=fws, taps_only=True)
-        reps = 20
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            hy.film_filter_gen(pd[0], regd, w.dims, h_time=taps, mode=mode, ws=fws, taps_only=True)
-        e1.record(stream)
-        torch.cuda.synchronize()
+        launch_ms = time_back_to_back(torch, stream, lambda: r["film_taps_only"](taps), 20)
         del taps
-        launch_ms = e0.elapsed_time(e1) / reps
         flops = film_network_flops(w)
         tf = flops / (launch_ms / 1e3) / 1e12
         out["roofline"] = {"bound": "mfma", "kernel": f"k_film_tiles ({'3-D' if w.ndim == 3 else '1-D'} taps, "
@@ -590,26 +706,17 @@ def main():
                            "note": "peak: dense fp32 matrix-core 157.3 TFLOP/s (layer 2 and the read-out run on "
                                    "fp32 matrix cores; layer 1, the sines and the window on the vector units); "
                                    "the launch time includes the register-summary kernel"}
-        out["filter_share_of_step"] = w.order * launch_ms / float(np.mean(step_ms))
+        out["filter_share_of_step"] = w.order * launch_ms / res["ms_per_step"]
     else:
         # filter network (a GEMM pair per position) for all orders; the time includes the spectrum build
         net_flop = 2.0 * w.order * w.support * w.hidden * (w.features + w.D)
-        out["filter_gen"] = {"ms": filter_gen_ms, "network_gflop": net_flop / 1e9,
-                             "achieved_tflops": net_flop / (filter_gen_ms / 1e3) / 1e12, "peak_tflops": 157.3,
+        fg = r["filter_gen_ms"]
+        out["filter_gen"] = {"ms": fg, "network_gflop": net_flop / 1e9,
+                             "achieved_tflops": net_flop / (fg / 1e3) / 1e12, "peak_tflops": 157.3,
                              "note": "all orders; network flops over the whole filter build (spectra included)"}
     if proj:
         # dominant kernel of the new step part: the projection GEMM, timed alone
-        for _ in range(3):
-            hy.projection(xtd, Wpd, w.order, bias=bpd, outs=pouts)
-        reps = 50
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            hy.projection(xtd, Wpd, w.order, bias=bpd, outs=pouts)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        proj_ms = e0.elapsed_time(e1) / reps
+        proj_ms = time_back_to_back(torch, stream, r["projection"], 50)
         flops = 2.0 * w.B * w.points * w.d_model * (w.order + 1) * w.D
         peak = 2500.0 if w.dtype == "bf16" else 157.3
         tf = flops / (proj_ms / 1e3) / 1e12
@@ -618,41 +725,37 @@ def main():
                            "achieved": tf, "peak": peak, "unit": "TFLOP/s", "frac": tf / peak, "traffic": None,
                            "launch_ms": proj_ms, "alg_flops_per_launch": flops,
                            "note": f"dense {'bf16' if w.dtype == 'bf16' else 'fp32'} matrix-core peak"}
-        out["projection_share_of_step"] = proj_ms / float(np.mean(step_ms))
+        out["projection_share_of_step"] = proj_ms / res["ms_per_step"]
         out["config"]["d_model"] = w.d_model
         out["config"]["inputs"] += ", stream 3 token-major inputs and W_proj"
-    if film or proj:
-        pass                                # the roofline object above
-    elif uses_matrix_cores(w) and w.order <= 8:
-        # the whole step is one launch of the matrix-core kernel: all orders, u_i kept on chip
-        launch_ms = float(np.mean(step_ms))
-        achieved = alg_step / (launch_ms / 1e3) / 1e9
-        floor = floor_bytes_per_step(w)
-        out["roofline"] = {"bound": "hbm", "kernel": key, "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                           "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": load_traffic(key),
-                           "launch_ms": launch_ms, "alg_bytes_per_launch": alg_step,
-                           "floor_bytes_per_launch": floor,
-                           "floor_frac": floor / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBPS}
-    elif single_launch_per_order(w):
-        # the whole step is `order` launches of one fused kernel: its average launch duration
-        launch_ms = float(np.mean(step_ms)) / w.order
-        bytes_launch = algorithmic_bytes_per_order(w)
-        achieved = bytes_launch / (launch_ms / 1e3) / 1e9
-        out["roofline"] = {"bound": "hbm", "kernel": key, "achieved": achieved, "peak": PEAK_HBM_GBPS,
-                           "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS, "traffic": load_traffic(key),
-                           "launch_ms": launch_ms, "alg_bytes_per_launch": bytes_launch}
-    else:
-        # several kernels per order: the whole step against the algorithmic bytes of the step
-        achieved = alg_step / (float(np.mean(step_ms)) / 1e3) / 1e9
-        out["roofline"] = {"bound": "hbm", "kernel": key + " (whole step)", "achieved": achieved,
-                           "peak": PEAK_HBM_GBPS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBPS,
-                           "traffic": load_traffic(key), "alg_bytes_per_step": alg_step}
+    if not (film or proj):
+        one_launch = (uses_matrix_cores(w) or single_launch_per_order(w)) and w.order <= 8
+        out["roofline"] = roofline_for = roofline_object(w, res["ms_per_step"], per_step=not one_launch)
+        roofline_for["timing"] = ("cold step, one launch per step (see timing)" if one_launch else
+                                  "cold step (see timing)")
+    host = (r["v"], r["xs"], r["params"], r["reg"], r.get("proj_inputs"))
+    del r
+    if args.workload == 1 and not args.no_config3:
+        # the second target configuration: the 2^20-sample fp32 order-2 workload, in the same run
+        w3 = hi.WORKLOADS[3]
+        torch.cuda.empty_cache()
+        rows3 = [tuple(x) for x in hi.sample_rows(w3, 16, seed=5)] if not args.no_parity else None
+        res3, r3 = measure(w3, argparse.Namespace(warmup=3), torch, hy, _lib, dev, stream, scratch, 10, 10, rows3)
+        del r3
+        torch.cuda.empty_cache()
+        res3["steps"] = 10
+        res3["config"] = config_block(w3)
+        res3["roofline"] = roofline_object(w3, res3["ms_per_step"], per_step=True)
+        res3["tokens_channels_per_step"] = w3.tokens_channels
+        out["config3"] = res3
+    del scratch
     if not args.no_copy:
         out["copy_gbps"] = copy_bandwidth(torch, dev)
     if not args.no_cpu_baseline:
+        v, xs, params, reg, proj_inputs = host
         out["cpu_baseline"] = (cpu_baseline_film(w, v, xs, params, reg, args.cpu_budget) if film else
-                               cpu_baseline(w, v, xs, params, args.cpu_budget,
-                                            proj_inputs=(xtok, Wp, bp) if proj else None))
+                               cpu_baseline(w, v, xs, params, args.cpu_budget, proj_inputs=proj_inputs))
+    out["bench_wall_s"] = time.perf_counter() - t_wall
     print(json.dumps(out), flush=True)
 
 

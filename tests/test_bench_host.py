@@ -5,6 +5,8 @@ import os
 import subprocess
 import sys
 
+import numpy as np
+
 import hyena_inputs as hi
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -43,3 +45,30 @@ def test_decode_bytes_per_launch():
     # history values per row and n taps per channel
     want = 4 * (rows * (3 + 1 + 2 + 2) + N * 128 * (rows + D))
     assert bench.decode_bytes_per_launch(w, 128) == want == 4_030_464
+
+
+def test_cpu_baseline_runs_on_every_core_of_the_process():
+    """The oracle baseline runs on a thread pool over this process's CPU set and says so."""
+    w = hi.WORKLOADS[0].with_(B=2, D=8, dims=(1024,))
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    cb = bench.cpu_baseline(w, v, xs, params, budget_s=0.5)
+    assert cb["cores"] == len(os.sched_getaffinity(0)) and cb["kind"] == "oracle"
+    assert cb["value"] > 0 and isinstance(cb["cpu_model"], str) and cb["cpu_model"]
+    assert "rows of the same workload" in cb["sample"]
+
+
+def test_sampled_parity_of_an_exact_output_is_zero():
+    """The bench's own parity check: the oracle's output itself measures (numerically) zero error, and a
+    planted mistake in one row shows up in the maximum."""
+    from oracle import hyena_oracle as orc
+    w = hi.WORKLOADS[0].with_(B=2, D=4, dims=(2048,))
+    v, xs = hi.draw_activations(w)
+    params = hi.draw_filter_params(w)
+    hs = [orc.implicit_filter_1d(p, 2048) for p in params]
+    y = np.stack([orc.hyena_operator_rows(v[b], [x[b] for x in xs], hs) for b in range(2)])
+    rows = [(b, d) for b in range(2) for d in range(4)]
+    p = bench.sampled_parity(w, v, xs, params, y, rows)
+    assert p["rows"] == 8 and p["max"] < 1e-12
+    y[1, 2] *= 1.01
+    assert abs(bench.sampled_parity(w, v, xs, params, y, rows)["max"] - 1e-2) < 1e-9

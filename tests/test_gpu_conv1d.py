@@ -416,3 +416,26 @@ def test_no_decay_window(torch_cuda, L, B, dtype):
     e = rel_err_rows(got, ref)
     say(f"no decay L={L} {dtype}: max rel err {e.max():.3e}")
     assert e.max() < (1e-3 if dtype == "f32" else BF16_TOL)
+
+
+def test_operator_from_parameters_with_spectrum_cache(torch_cuda):
+    """hyena() builds each order's spectrum once per grid size and reuses it: equal to operator() with spectra
+    from filter_gen, two builds over two calls, a third after an in-place parameter update."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[0].with_(B=2, D=8, dims=(4096,))
+    v, xs = hi.draw_activations(w, seed=91)
+    params = [params_to_dev(p) for p in hi.draw_filter_params(w, seed=91)]
+    cache = hy.SpectrumCache()
+    vd = to_dev(v, torch.float32)
+    xd = [to_dev(x, torch.float32) for x in xs]
+    y1 = hy.hyena(vd, xd, params, cache=cache)
+    y2 = hy.hyena(vd, xd, params, cache=cache)
+    ref = hy.operator(vd, xd, [hy.filter_gen(p, w.dims) for p in params])
+    torch.cuda.synchronize()
+    assert cache.builds == 2
+    assert torch.equal(y1, ref) and torch.equal(y2, ref)
+    params[0]["alpha"].mul_(0.5)
+    y3 = hy.hyena(vd, xd, params, cache=cache)
+    torch.cuda.synchronize()
+    assert cache.builds == 3 and not torch.equal(y3, ref)
