@@ -193,12 +193,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // pointer 16-byte aligned.
 bool use_mfma(int dtype, int64_t B, int64_t L) { return dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B); }
 
-// Highest operator order sent to the matrix-core kernel.  Its bf16 transform operands cost about 5e-3 of
+// Highest operator order sent to the matrix-core kernel.  Its fp16 transform operands cost a few 1e-4 of
 // relative error per order, and later orders amplify what earlier ones leave: measured against the oracle
-// (max over rows) 1.7e-2 at order 2, but 3.4e-2 at order 3 with slowly decaying filters and 5.5e-2 at
-// order 4 with none -- beyond the 2e-2 that bf16 storage allows.  Higher orders take the fp32 engine, whose
-// only roundings are the bf16 stores.
-constexpr int kMfmaMaxOrder = 2;
+// (max over rows, with no decay window, the worst filter family) 2.6e-3 at order 2 and 5.7e-3 at order 3,
+// but already 1.2e-2 at order 4 and 4.1e-2 at order 6 against the 2e-2 that bf16 storage allows.  Higher
+// orders take the fp32 engine, whose only roundings are the bf16 stores.
+constexpr int kMfmaMaxOrder = 3;
 
 // Orders [0, order) through the matrix-core kernel, up to kMfmaMaxChain orders per launch with u_i on chip.
 int conv_mfma_chain(int64_t B, int64_t D, int64_t L, const void* u, const void* const* gates,

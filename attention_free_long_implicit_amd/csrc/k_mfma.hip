@@ -4,8 +4,17 @@
 // EulerStack "4. Hyena 상세", how it works 2 (FFT, elementwise product, inverse FFT); HyenaND summary,
 // boundary handling (zero-pad to twice the size) and nSubQ implementation (forward transform,
 // spectral product, inverse transform and output cut in one kernel, intermediates on chip).  The
-// transform steps are small dense DFT matrices, evaluated as bf16 matrix products with fp32
+// transform steps are small dense DFT matrices, evaluated as 16-bit matrix products with fp32
 // accumulation (a DFT as a dense matrix product is the remark in the SPECTRE digest's comments).
+//
+// Precision: every operand after the first product is fp16 (11-bit significand), not bf16 (8 bits):
+// the products cost the same on the matrix cores, and eight times finer rounding keeps the order-2
+// result well inside the bf16-storage tolerance even without a decay window (bf16 operands measured
+// up to 1.96e-2 of the 2e-2 allowed).  fp16's range is kept by exact power-of-two scaling: each order's
+// input is scaled so that its largest magnitude in the row pair lies in [0.5, 1), the filter spectrum
+// so that its largest bin does, and the inverse radix-32 matrices carry a factor 1/32 each, so no
+// intermediate exceeds 2^13; the output is scaled back in fp32 before the gate.  The first product of
+// the first order reads the bf16 inputs exactly, against a matrix split into two bf16 parts (hi + lo).
 //
 // Two rows b0, b1 of one channel (same filter) are transformed together as z = u_b0 + i u_b1:
 // since h is real, IDFT(DFT(z) H) = (h * u_b0) + i (h * u_b1), so no real-input split is needed.
@@ -21,9 +30,10 @@
 // Every factor that depends on the slab k1 and on one of a pass's own indices lives in that pass's
 // matrix (16 slabs x 4 matrices, a 256 KB table that stays in L2), so the only elementwise twiddle
 // left is W_1024^{n3 k2}, whose two indices are the row and the column of one product.  The filter
-// spectrum is stored for slabs 0..8 only (36 KB per channel); conjugate symmetry gives the rest.
+// spectrum is stored for slabs 0..8 only (36 KB per channel, plus its scale); conjugate symmetry gives the
+// rest.
 // A complex radix-R DFT is a real 2R x 2R matrix on (Re, Im); each MFMA (32x32x16) multiplies a 32-row
-// block of it by 32 columns (independent sub-transforms).  LDS holds one plane of complex bf16 words
+// block of it by 32 columns (independent sub-transforms).  LDS holds one plane of complex fp16 words
 // (re low, im high); rows hold 32 words plus one pad, so lanes reading one word each from 32
 // consecutive rows, or 32 consecutive words of one row, hit distinct banks.  Passes 2, 3, 3' and 2'
 // of slab k1 touch only that slab, which one wave owns, so only two barriers are needed.  Global
@@ -32,14 +42,18 @@
 #include <math.h>
 #include <string.h>
 
+#include <type_traits>
+
 #include "engine.h"
 #include "launch.h"
 
 namespace hyena {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 namespace mf {
 constexpr int L = 8192, N = 2 * L;
@@ -47,13 +61,18 @@ constexpr int ROW = 33;                     // 32 values + 1 pad
 constexpr int SLAB = 32 * ROW;              // one k1 (or n1-free) slab
 constexpr int PLANE = 16 * SLAB;            // 16 slabs
 constexpr int T = 256;                      // 4 waves
-// Matrix table, per lane 8 bf16 in the A-operand layout (row i = lane % 32, K = 8 (lane / 32) + e).
-// Fixed radix-16 matrices first, then per slab k1 four radix-32 matrices of four blocks each.
-enum { M1F = 0, M1I_R, M1I_I, NFIX };
+// Matrix table, per lane 8 16-bit values in the A-operand layout (row i = lane % 32, K = 8 (lane / 32) + e).
+// Fixed radix-16 matrices first -- the forward one as two bf16 parts (hi, and lo = the rest) and in fp16,
+// the two inverse blocks in fp16 -- then per slab k1 four fp16 radix-32 matrices of four blocks each (the
+// inverse ones, passes 3' and 2', scaled by 1/32).
+enum { M1F_HI = 0, M1F_LO, M1F_H, M1I_R, M1I_I, NFIX };
 enum { MF2 = 0, MF3, MI3, MI2, NSLABMAT };       // pass 2, pass 3, pass 3', pass 2'
 enum { B_CLO = 0, B_CHI, B_SLO, B_SHI, NBLK };   // cos / sin, K < 16 / K >= 16
-constexpr int SLAB_TABLE = NSLABMAT * NBLK;       // bf16x8 per lane per slab
+constexpr int SLAB_TABLE = NSLABMAT * NBLK;       // 16-byte entries per lane per slab
 constexpr int PAIR_SLABS = 9;                     // filter-spectrum slabs stored per channel (k1 = 0..8)
+constexpr int PAIR_WORDS = PAIR_SLABS * 16 * 64;  // fp16 complex words of one channel's spectrum copy
+constexpr int PAIR_STRIDE = PAIR_WORDS + 64;      // + one 256-byte tail: word 0 = the spectrum's scale back
+constexpr float INV_SCALE = 1024.0f;              // undoes the two 1/32 factors of the inverse matrices
 }  // namespace mf
 
 // Orders run back to back in one launch: gate and matrix-core spectrum copy of each order.
@@ -70,10 +89,34 @@ constexpr int kRawBufferWord3 = 0x00020000;
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ bf16x8 neg8(bf16x8 v) {   // flip the 8 sign bits, one XOR per dword
+__device__ __forceinline__ f32x16 mfma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f16x8 neg8(f16x8 v) {     // flip the 8 sign bits, one XOR per dword
   u32x4 r = __builtin_bit_cast(u32x4, v);
   r ^= 0x80008000u;
-  return __builtin_bit_cast(bf16x8, r);
+  return __builtin_bit_cast(f16x8, r);
+}
+__device__ __forceinline__ f16x8 as_h(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ bf16x8 as_b(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 2^-e with e the binary exponent of m (m = f 2^e, f in [0.5, 1)): the power of two that brings the
+// largest magnitude m into [0.5, 1); 1 for a zero or non-finite m.  The exponent is clamped to what an
+// fp32 power of two can hold.
+__device__ __forceinline__ float range_scale(float m) {
+  if (!(m > 0.0f) || !(m <= 3.0e38f)) return 1.0f;
+  int e = __builtin_amdgcn_frexp_expf(m);
+  e = e < -125 ? -125 : (e > 125 ? 125 : e);
+  return __builtin_ldexpf(1.0f, -e);
+}
+// largest value of v over the workgroup (4 waves); red: 4 floats of LDS; every thread returns the result.
+// The caller's next barrier must not be this one's: the slots are rewritten only after later barriers.
+__device__ __forceinline__ float block_max4(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // output row of accumulator register v for lane half h (32x32 MFMA layout)
@@ -87,13 +130,13 @@ __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 *
 // matrix row, lane = the data column.  DATA_A = true: data on A -> the transpose (lane = the matrix row,
 // registers = the data column), which puts the next contraction index in registers.
 template <bool INV, bool DATA_A>
-__device__ __forceinline__ void dft32(const bf16x8 (&M)[mf::NBLK], bf16x8 xr_lo, bf16x8 xr_hi, bf16x8 xi_lo,
-                                      bf16x8 xi_hi, f32x16& dr, f32x16& di) {
+__device__ __forceinline__ void dft32(const f16x8 (&M)[mf::NBLK], f16x8 xr_lo, f16x8 xr_hi, f16x8 xi_lo,
+                                      f16x8 xi_hi, f32x16& dr, f32x16& di) {
   using namespace mf;
-  auto mm = [](bf16x8 m, bf16x8 x, f32x16 c) { return DATA_A ? mfma(x, m, c) : mfma(m, x, c); };
+  auto mm = [](f16x8 m, f16x8 x, f32x16 c) { return DATA_A ? mfma(x, m, c) : mfma(m, x, c); };
   const f32x16 z = {};
-  const bf16x8 sxi_lo = INV ? neg8(xi_lo) : xi_lo, sxi_hi = INV ? neg8(xi_hi) : xi_hi;
-  const bf16x8 sxr_lo = INV ? xr_lo : neg8(xr_lo), sxr_hi = INV ? xr_hi : neg8(xr_hi);
+  const f16x8 sxi_lo = INV ? neg8(xi_lo) : xi_lo, sxi_hi = INV ? neg8(xi_hi) : xi_hi;
+  const f16x8 sxr_lo = INV ? xr_lo : neg8(xr_lo), sxr_hi = INV ? xr_hi : neg8(xr_hi);
   dr = mm(M[B_CLO], xr_lo, z);
   dr = mm(M[B_CHI], xr_hi, dr);
   dr = mm(M[B_SLO], sxi_lo, dr);
@@ -110,15 +153,24 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
   const bf16x2 v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
 }
+// two floats -> one dword of fp16 (round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t pack2h(float a, float b) {
+  const f16x2 v = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, v);
+}
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ float2 unpack_c(uint32_t w) { return make_float2(lo_f32(w), hi_f32(w)); }
+// one dword of fp16 (re low, im high) -> complex fp32
+__device__ __forceinline__ float2 unpack_h(uint32_t w) {
+  const f16x2 v = __builtin_bit_cast(f16x2, w);
+  return make_float2((float)v.x, (float)v.y);
+}
 
-// fp32 accumulators, each multiplied by a complex factor, -> bf16 operands in accumulator order
+// fp32 accumulators, each multiplied by a complex factor, -> fp16 operands in accumulator order
 // (block lo = registers 0..7, block hi = registers 8..15)
 template <class F>
-__device__ __forceinline__ void pack_operands(const f32x16& xr, const f32x16& xi, F&& factor, bf16x8& r_lo,
-                                              bf16x8& r_hi, bf16x8& i_lo, bf16x8& i_hi) {
+__device__ __forceinline__ void pack_operands(const f32x16& xr, const f32x16& xi, F&& factor, f16x8& r_lo,
+                                              f16x8& r_hi, f16x8& i_lo, f16x8& i_hi) {
   u32x4 rl, rh, il, ih;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -126,36 +178,36 @@ __device__ __forceinline__ void pack_operands(const f32x16& xr, const f32x16& xi
     const float2 a1 = factor(2 * m + 1, make_float2(xr[2 * m + 1], xi[2 * m + 1]));
     const float2 b0 = factor(8 + 2 * m, make_float2(xr[8 + 2 * m], xi[8 + 2 * m]));
     const float2 b1 = factor(9 + 2 * m, make_float2(xr[9 + 2 * m], xi[9 + 2 * m]));
-    rl[m] = pack2(a0.x, a1.x);
-    il[m] = pack2(a0.y, a1.y);
-    rh[m] = pack2(b0.x, b1.x);
-    ih[m] = pack2(b0.y, b1.y);
+    rl[m] = pack2h(a0.x, a1.x);
+    il[m] = pack2h(a0.y, a1.y);
+    rh[m] = pack2h(b0.x, b1.x);
+    ih[m] = pack2h(b0.y, b1.y);
   }
-  r_lo = __builtin_bit_cast(bf16x8, rl);
-  r_hi = __builtin_bit_cast(bf16x8, rh);
-  i_lo = __builtin_bit_cast(bf16x8, il);
-  i_hi = __builtin_bit_cast(bf16x8, ih);
+  r_lo = as_h(rl);
+  r_hi = as_h(rh);
+  i_lo = as_h(il);
+  i_hi = as_h(ih);
 }
 
-// 8 complex bf16 words (re low, im high) -> the 8 real parts and the 8 imaginary parts as MFMA operands
-__device__ __forceinline__ void split8(const uint32_t (&c)[8], bf16x8& re, bf16x8& im) {
+// 8 complex fp16 words (re low, im high) -> the 8 real parts and the 8 imaginary parts as MFMA operands
+__device__ __forceinline__ void split8(const uint32_t (&c)[8], f16x8& re, f16x8& im) {
   u32x4 r, i;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     r[m] = __builtin_amdgcn_perm(c[2 * m + 1], c[2 * m], 0x05040100u);
     i[m] = __builtin_amdgcn_perm(c[2 * m + 1], c[2 * m], 0x07060302u);
   }
-  re = __builtin_bit_cast(bf16x8, r);
-  im = __builtin_bit_cast(bf16x8, i);
+  re = as_h(r);
+  im = as_h(i);
 }
-// element t (compile-time) of each of 8 vectors of 8 bf16 -> one operand
+// element t (compile-time) of each of 8 vectors of 8 16-bit values -> one operand (its bits)
 template <int TT>
-__device__ __forceinline__ bf16x8 column8(const u32x4 (&V)[8]) {
+__device__ __forceinline__ u32x4 column8(const u32x4 (&V)[8]) {
   constexpr uint32_t sel = (TT & 1) ? 0x07060302u : 0x05040100u;
   u32x4 r;
 #pragma unroll
   for (int m = 0; m < 4; ++m) r[m] = __builtin_amdgcn_perm(V[2 * m + 1][TT >> 1], V[2 * m][TT >> 1], sel);
-  return __builtin_bit_cast(bf16x8, r);
+  return r;
 }
 template <int TT>
 __device__ __forceinline__ float elem_f32(const u32x4& g) {
@@ -167,10 +219,11 @@ __device__ __forceinline__ float elem_f32(const u32x4& g) {
 // (row, n1) in global memory.
 template <bool GATE>
 __global__ void __launch_bounds__(mf::T, 2)
-k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__ mats, int B, int D,
+k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ mats, int B, int D,
             Twiddles tw) {
   using namespace mf;
   __shared__ uint32_t S[PLANE];
+  __shared__ float red[4];
   const int npair = B >> 1;
   const int r = xcd_logical_block(blockIdx.x, D * npair);
   const int d = r / npair, p = r % npair;
@@ -188,10 +241,27 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   // would queue behind that order's spectrum loads): the fixed radix-16 matrices and the per-lane
   // twiddles W_1024^{j k(v)}, k(v) = row of accumulator v.
   const int l0 = threadIdx.x & 63;
-  const bf16x8 m1f = mats[M1F * 64 + l0], m1r = mats[M1I_R * 64 + l0], m1i = mats[M1I_I * 64 + l0];
+  // m1a, m1b: the forward radix-16 matrix of the next pass 1 (first order: its two bf16 parts; later
+  // orders: m1a in fp16, loaded at the end of the previous order)
+  u32x4 m1a = mats[M1F_HI * 64 + l0], m1b = mats[M1F_LO * 64 + l0];
+  const u32x4 m1r = mats[M1I_R * 64 + l0], m1i = mats[M1I_I * 64 + l0];
   float2 p2[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) p2[v] = twiddle<10>(tw, uint32_t((l0 & 31) * acc_row(v, l0 >> 5)));
+  // scale of the first order's input: the largest |u| of the row pair (bf16 magnitudes compare as
+  // integers), brought into [0.5, 1)
+  float s_in;
+  {
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = V[e][q] & 0x7fff7fffu;
+        m = max(m, max(w & 0xffffu, w >> 16));
+      }
+    s_in = range_scale(block_max4(__uint_as_float(m << 16), red));
+  }
 
   for (int ord = 0; ord < ch.order; ++ord) {
   // lane constants derived from an opaque copy of the thread id, so nothing is hoisted across orders
@@ -200,13 +270,15 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   const int t = tq, w = t >> 6, l = t & 63, j = l & 31, h = l >> 5;
   const int c0 = 256 * w + 8 * j;
   const int n2c = 8 * w + (j >> 2), n3c = 8 * (j & 3);   // tile t: n2 = n2c, n3 = n3c + t
-  const uint32_t* __restrict__ Hc = ch.spectrum[ord];
+  const uint32_t* __restrict__ Hc = ch.spectrum[ord] + (size_t)d * PAIR_STRIDE;
   const __bf16* gate = ch.gate[ord];
+  // scales back: the inverse matrices' 1/1024, the spectrum's normalisation, the input's scale
+  const float f_out = INV_SCALE * __builtin_bit_cast(float, Hc[PAIR_WORDS]) / s_in;
 
   // Slab matrices rotate through two buffers, each load issued one pass before its use:
   // Ma = pass 2, Mb = pass 3, then Ma = pass 3', Mb = pass 2', then the next slab's pass 2 and 3.
   // The first slab's matrices and filter spectrum are in flight during pass 1.
-  bf16x8 Ma[NBLK], Mb[NBLK];
+  f16x8 Ma[NBLK], Mb[NBLK];
   // The matrix table and the spectrum are read through buffer descriptors: the per-lane part of the
   // offset is fixed, the block / register part (and the mirror choice, uniform per wave) stays in
   // scalar registers, so a slab's 32 loads cost no vector instructions for their addresses.
@@ -214,18 +286,18 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
       (void*)(mats + NFIX * 64), (short)0, 16 * SLAB_TABLE * 64 * 16, kRawBufferWord3);
   const int mvo = l * 16;
   // blocks of matrix `which` of slab k1s (scalar) into M
-  auto load_mat = [&](int k1s_, int which, bf16x8 (&M)[NBLK]) {
+  auto load_mat = [&](int k1s_, int which, f16x8 (&M)[NBLK]) {
 #pragma unroll
     for (int b = 0; b < NBLK; ++b)
-      M[b] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                                            mrs, mvo, ((k1s_ * SLAB_TABLE + which * NBLK + b) * 64) * 16, 0));
+      M[b] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                           mrs, mvo, ((k1s_ * SLAB_TABLE + which * NBLK + b) * 64) * 16, 0));
   };
   // Filter spectrum: only slabs 0..8 are stored.  h is real, so H[N - k] = conj(H[k]); bin N - k of
   // slab k1 > 8 is register 15 - v of lane 63 - l in slab 16 - k1, read mirrored; the conjugation (sign
   // of the imaginary half) is applied where the value is used, so the load stays in flight until then.
   uint32_t hw[16];
-  const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(Hc + (size_t)d * PAIR_SLABS * 16 * 64), (short)0, PAIR_SLABS * 16 * 64 * 4, kRawBufferWord3);
+  const __amdgpu_buffer_rsrc_t hrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Hc, (short)0, PAIR_WORDS * 4, kRawBufferWord3);
   const int ws = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto load_spectrum = [&](int k1) {
     const bool mirror = k1 > 8;
@@ -238,16 +310,31 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
   load_mat(ws, MF2, Ma);
   load_mat(ws, MF3, Mb);
   load_spectrum(ws);
-  {
+  // pass 1.  First order: the bf16 inputs exactly, against the forward matrix in two bf16 parts; the
+  // accumulators are scaled into fp16's range as they are rounded.  Later orders: the scaled fp16 input
+  // against the fp16 matrix.
+  auto pass1 = [&](auto first) {
     static_for<8>([&](auto tt) {
       constexpr int TT = tt.value;
       const f32x16 z = {};
-      const f32x16 D1 = mfma(m1f, column8<TT>(V), z);
+      f32x16 D1;
+      float sc = 1.0f;
+      if constexpr (decltype(first)::value) {
+        const bf16x8 col = as_b(column8<TT>(V));
+        D1 = mfma(as_b(m1a), col, z);
+        D1 = mfma(as_b(m1b), col, D1);
+        sc = s_in;
+      } else {
+        D1 = mfma(as_h(m1a), as_h(column8<TT>(V)), z);
+      }
       // rows k1 = acc_row(e, h): real part in D1[e], imaginary part in D1[8 + e]
 #pragma unroll
-      for (int e = 0; e < 8; ++e) S[acc_row(e, h) * SLAB + n2c * ROW + n3c + TT] = pack2(D1[e], D1[8 + e]);
+      for (int e = 0; e < 8; ++e)
+        S[acc_row(e, h) * SLAB + n2c * ROW + n3c + TT] = pack2h(D1[e] * sc, D1[8 + e] * sc);
     });
-  }
+  };
+  if (ord == 0) pass1(std::true_type{});
+  else pass1(std::false_type{});
   __syncthreads();
 
   // ---------------- passes 2, 3, 3', 2' per slab k1 (wave w owns k1 = w, w+4, w+8, w+12)
@@ -267,7 +354,7 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
     const int k1 = w + 4 * it;
     const int k1s = ws + 4 * it;   // the same slab index, in a scalar register
     uint32_t* sl = S + k1 * SLAB;
-    bf16x8 xr_lo, xr_hi, xi_lo, xi_hi;
+    f16x8 xr_lo, xr_hi, xi_lo, xi_hi;
     f32x16 dr, di;
     // pass 2: data on A (rows n3 = j, K = n2 from LDS: element (n2, n3) at n2 * ROW + n3), matrix on B
     //   -> lane = k2, registers = n3 (row of v)
@@ -288,11 +375,11 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
     pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, p2[v]); }, xr_lo, xr_hi, xi_lo, xi_hi);
     dft32<false, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
     load_mat(k1s, MI2, Mb);
-    // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N in this exact order.
+    // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N (normalised) in this exact order.
     // pass 3': data on A (rows k2 = j, input k3 in accumulator order), matrix on B -> lane = n3,
     // registers = k2
     const uint32_t flip = k1s > 8 ? 0x80000000u : 0u;
-    pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, unpack_c(hw[v] ^ flip)); }, xr_lo, xr_hi, xi_lo,
+    pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, unpack_h(hw[v] ^ flip)); }, xr_lo, xr_hi, xi_lo,
                   xi_hi);
     if (it < 3) load_spectrum(k1s + 4);
     f32x16 er, ei;
@@ -304,7 +391,7 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
     dft32<true, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
     if (it < 3) load_mat(k1s + 4, MF3, Mb);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2(er[v], ei[v]);
+    for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2h(er[v], ei[v]);
   };
   // The gate for pass 1' is issued before the last slab, behind that slab's matrix and spectrum loads
   // (the vector-memory counter retires in order, so no earlier slab waits on it): lane keeps rows
@@ -317,81 +404,94 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const bf16x8* __restrict__
 
   // ---------------- pass 1': tiles t, column c = c0 + t, K = k1 (slab index), outputs n1 = 4h + e
   {
-    u32x4 Y[2][4];
-    float pa[4], pb[4];
+    const bool last = ord + 1 == ch.order;
+    float yv[2][4][8];   // [row][e][tile], fp32: the output, or the next order's input
+    float vmax = 0.0f;
     static_for<8>([&](auto tt) {
       constexpr int TT = tt.value;
       uint32_t cw[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) cw[e] = S[(8 * h + e) * SLAB + n2c * ROW + n3c + TT];
-      bf16x8 xr, xi;
+      f16x8 xr, xi;
       split8(cw, xr, xi);
       const f32x16 z = {};
-      f32x16 o = mfma(m1r, xr, z);
-      o = mfma(m1i, xi, o);
+      f32x16 o = mfma(as_h(m1r), xr, z);
+      o = mfma(as_h(m1i), xi, o);
       // rows 4h + e (e < 4): real part (row b0) in o[e], imaginary part (row b1) in o[8 + e]
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float a = o[e], b = o[8 + e];
+        float a = o[e] * f_out, b = o[8 + e] * f_out;
         if (GATE) {
           a *= elem_f32<TT>(G[0][e]);
           b *= elem_f32<TT>(G[1][e]);
         }
-        if constexpr (TT % 2 == 0) {
-          pa[e] = a;
-          pb[e] = b;
-        } else {
-          Y[0][e][TT >> 1] = pack2(pa[e], a);
-          Y[1][e][TT >> 1] = pack2(pb[e], b);
-        }
+        yv[0][e][TT] = a;
+        yv[1][e][TT] = b;
+        vmax = fmaxf(vmax, fmaxf(fabsf(a), fabsf(b)));
       }
     });
     __bf16* y0 = y + row0 * L + c0;
     __bf16* y1 = y + row1 * L + c0;
-    if (ord + 1 == ch.order) {
+    if (last) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        *reinterpret_cast<u32x4*>(y0 + 1024 * (4 * h + e)) = Y[0][e];
-        *reinterpret_cast<u32x4*>(y1 + 1024 * (4 * h + e)) = Y[1][e];
+        u32x4 Y0, Y1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          Y0[q] = pack2(yv[0][e][2 * q], yv[0][e][2 * q + 1]);
+          Y1[q] = pack2(yv[1][e][2 * q], yv[1][e][2 * q + 1]);
+        }
+        *reinterpret_cast<u32x4*>(y0 + 1024 * (4 * h + e)) = Y0;
+        *reinterpret_cast<u32x4*>(y1 + 1024 * (4 * h + e)) = Y1;
       }
     } else {
-      // u_i stays on chip, rounded to bf16 exactly as its store would be.  Pass 1' left lane (j, h) with
-      // rows b0, b1 at n1 = 4h + e; the next pass 1 wants row b_h at n1 = 0..7 in lane (j, h).  One
-      // cross-half swap per register does it: swapping the upper half of the row-b0 register with the
-      // lower half of the row-b1 register leaves [b0 from lanes 0..31, b1 from lanes 0..31] (n1 = e) in
-      // the first and [b0 from lanes 32..63, b1 from lanes 32..63] (n1 = 4 + e) in the second.
+      // u_i stays on chip: the next order's input, scaled into fp16's range by its own row-pair maximum
+      // (the barrier inside block_max4 also keeps the next pass 1 from writing LDS this pass still reads).
+      // Pass 1' left lane (j, h) with rows b0, b1 at n1 = 4h + e; the next pass 1 wants row b_h at
+      // n1 = 0..7 in lane (j, h).  One cross-half swap per register does it: swapping the upper half of the
+      // row-b0 register with the lower half of the row-b1 register leaves [b0 from lanes 0..31, b1 from
+      // lanes 0..31] (n1 = e) in the first and [b0 from lanes 32..63, b1 from lanes 32..63] (n1 = 4 + e) in
+      // the second.
+      m1a = mats[M1F_H * 64 + l0];
+      s_in = range_scale(block_max4(vmax, red));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const auto r = __builtin_amdgcn_permlane32_swap(Y[0][e][q], Y[1][e][q], false, false);
-          V[e][q] = r[0];
-          V[4 + e][q] = r[1];
+          const uint32_t a = pack2h(yv[0][e][2 * q] * s_in, yv[0][e][2 * q + 1] * s_in);
+          const uint32_t b = pack2h(yv[1][e][2 * q] * s_in, yv[1][e][2 * q + 1] * s_in);
+          const auto rr = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+          V[e][q] = rr[0];
+          V[4 + e][q] = rr[1];
         }
       }
-      __syncthreads();   // every wave is done reading LDS before the next order's pass 1 writes it
     }
   }
   }
 }
 
 
-// Pair-order spectrum: Hc[d][k1][v][lane] = H[k]/N as bf16 (re low, im high), k = k1 + 16 (lane%32)
-// + 512 k3(v, lane/32), for k1 = 0..8 (the convolution kernel mirrors slabs 9..15 from slabs 7..1);
-// H from the natural-order bins 0..L (upper bins by conjugate symmetry).
-__global__ void k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc) {
+// Pair-order spectrum of one channel per workgroup: Hc[d][k1][v][lane] = c_d H[k]/N as fp16 (re low, im
+// high), k = k1 + 16 (lane%32) + 512 k3(v, lane/32), for k1 = 0..8 (the convolution kernel mirrors slabs 9..15
+// from slabs 7..1), followed by the float 1/c_d; c_d is the power of two that brings the channel's largest
+// |H[k]|/N into [0.5, 1).  H from the natural-order bins 0..L (upper bins by conjugate symmetry).
+__global__ void __launch_bounds__(256) k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc) {
   using namespace mf;
-  const int d = blockIdx.y;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;    // (k1, v, lane)
-  if (idx >= PAIR_SLABS * 16 * 64) return;
-  const int k1 = idx / (16 * 64), v = (idx / 64) % 16, l = idx % 64;
-  const int jj = l & 31, h = l >> 5;
-  const int k = k1 + 16 * jj + 512 * acc_row(v, h);
+  __shared__ float red[4];
+  const int d = blockIdx.x;
   const float2* hn = Hnat + (size_t)d * (L + 1);
-  float2 hv = k <= L ? hn[k] : cconj(hn[N - k]);
-  hv = cscale(hv, 1.0f / N);
-  const uint32_t lo = (uint32_t)f32_to_bf16_rne(hv.x), hi = (uint32_t)f32_to_bf16_rne(hv.y);
-  Hc[(size_t)d * PAIR_SLABS * 16 * 64 + idx] = lo | (hi << 16);
+  float m = 0.0f;
+  for (int k = threadIdx.x; k <= L; k += 256) m = fmaxf(m, fmaxf(fabsf(hn[k].x), fabsf(hn[k].y)));
+  const float c = range_scale(block_max4(m * (1.0f / N), red));
+  const float sc = c * (1.0f / N);
+  uint32_t* out = Hc + (size_t)d * PAIR_STRIDE;
+  for (int idx = threadIdx.x; idx < PAIR_WORDS; idx += 256) {   // (k1, v, lane)
+    const int k1 = idx / (16 * 64), v = (idx / 64) % 16, l = idx % 64;
+    const int k = k1 + 16 * (l & 31) + 512 * acc_row(v, l >> 5);
+    const float2 hv = k <= L ? hn[k] : cconj(hn[N - k]);
+    out[idx] = pack2h(hv.x * sc, hv.y * sc);
+  }
+  if (threadIdx.x < 64) out[PAIR_WORDS + threadIdx.x] = threadIdx.x == 0 ? __float_as_uint(1.0f / c) : 0u;
 }
 
 // ------------------------------------------------------------------ host side
@@ -405,27 +505,27 @@ int perm_k3(int Kp) {
   return 16 * hi + (e < 4 ? 4 * hh + e : 8 + 4 * hh + e - 4);
 }
 
-// Radix-16 matrices, entry (row i, input K).
-float fixed_entry(int q, int i, int K) {
+// Radix-16 matrices, entry (row i, input K): q = 0 the forward one, q = 1 / 2 the inverse's blocks.
+double fixed_entry(int q, int i, int K) {
   auto c = [](int a, int b) { return cos(kTwoPi * (double)((a * b) % 16) / 16); };
   auto s = [](int a, int b) { return sin(kTwoPi * (double)((a * b) % 16) / 16); };
   switch (q) {
-    case mf::M1F: {   // forward, inputs m < 8: rows (Yr k | Yi k), cols (Xr m | Xi m)
+    case 0: {   // forward, inputs m < 8: rows (Yr k | Yi k), cols (Xr m | Xi m)
       const int k = i & 15, m = K & 7;
       const bool yi = i >= 16, xi = K >= 8;
-      if (!yi) return (float)(xi ? s(k, m) : c(k, m));
-      return (float)(xi ? c(k, m) : -s(k, m));
+      if (!yi) return xi ? s(k, m) : c(k, m);
+      return xi ? c(k, m) : -s(k, m);
     }
-    case mf::M1I_R: {  // inverse, Xr block: Yr = c, Yi = s
+    case 1: {   // inverse, Xr block: Yr = c, Yi = s
       const int n = i & 15;
-      return (float)(i < 16 ? c(n, K) : s(n, K));
+      return i < 16 ? c(n, K) : s(n, K);
     }
-    case mf::M1I_I: {  // inverse, Xi block: Yr = -s, Yi = c
+    case 2: {   // inverse, Xi block: Yr = -s, Yi = c
       const int n = i & 15;
-      return (float)(i < 16 ? -s(n, K) : c(n, K));
+      return i < 16 ? -s(n, K) : c(n, K);
     }
   }
-  return 0.f;
+  return 0.0;
 }
 
 // Angle (in turns) of the radix-32 entry (row i, input k) of slab matrix m for slab k1.
@@ -445,30 +545,53 @@ uint16_t bf16_rne(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
+double bf16_value(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+// fp16 bits of v, rounded to nearest even directly from double
+uint16_t f16_rne(double v) {
+  const _Float16 h = (_Float16)v;
+  uint16_t b;
+  memcpy(&b, &h, 2);
+  return b;
+}
 }  // namespace
 
 static_assert(kMfmaMatrixCount == ((size_t)mf::NFIX + 16 * mf::SLAB_TABLE) * 64 * 8, "matrix table size");
 
-// [NFIX][64][8], [16 slabs][4 mats][4 blocks][64][8] (bf16)
+// [NFIX][64][8], [16 slabs][4 mats][4 blocks][64][8] (16-bit values; see the table layout above)
 void mfma_matrices_host(uint16_t* out) {
-  for (int q = 0; q < mf::NFIX; ++q)
-    for (int l = 0; l < 64; ++l)
-      for (int e = 0; e < 8; ++e) out[(q * 64 + l) * 8 + e] = bf16_rne(fixed_entry(q, l % 32, 8 * (l / 32) + e));
+  for (int l = 0; l < 64; ++l)
+    for (int e = 0; e < 8; ++e) {
+      const int i = l % 32, K = 8 * (l / 32) + e;
+      const double f = fixed_entry(0, i, K);
+      const uint16_t hi = bf16_rne((float)f);
+      out[(mf::M1F_HI * 64 + l) * 8 + e] = hi;
+      out[(mf::M1F_LO * 64 + l) * 8 + e] = bf16_rne((float)(f - bf16_value(hi)));
+      out[(mf::M1F_H * 64 + l) * 8 + e] = f16_rne(f);
+      out[(mf::M1I_R * 64 + l) * 8 + e] = f16_rne(fixed_entry(1, i, K));
+      out[(mf::M1I_I * 64 + l) * 8 + e] = f16_rne(fixed_entry(2, i, K));
+    }
   uint16_t* o = out + (size_t)mf::NFIX * 64 * 8;
   for (int k1 = 0; k1 < 16; ++k1)
-    for (int m = 0; m < mf::NSLABMAT; ++m)
+    for (int m = 0; m < mf::NSLABMAT; ++m) {
+      const double scale = (m == mf::MI3 || m == mf::MI2) ? 1.0 / 32 : 1.0;
       for (int b = 0; b < mf::NBLK; ++b)
         for (int l = 0; l < 64; ++l)
           for (int e = 0; e < 8; ++e) {
             const int i = l % 32, k = 8 * (l / 32) + e + ((b == mf::B_CHI || b == mf::B_SHI) ? 16 : 0);
             const double a = kTwoPi * slab_angle(m, k1, i, k);
             const double val = (b == mf::B_CLO || b == mf::B_CHI) ? cos(a) : sin(a);
-            o[((((size_t)k1 * mf::NSLABMAT + m) * mf::NBLK + b) * 64 + l) * 8 + e] = bf16_rne((float)val);
+            o[((((size_t)k1 * mf::NSLABMAT + m) * mf::NBLK + b) * 64 + l) * 8 + e] = f16_rne(val * scale);
           }
+    }
 }
 
 bool mfma_pair_supported(int log2L, int B) { return log2L == 13 && B % 2 == 0; }
-size_t mfma_pair_spectrum_bytes_per_channel() { return (size_t)mf::PAIR_SLABS * 16 * 64 * 4; }
+size_t mfma_pair_spectrum_bytes_per_channel() { return (size_t)mf::PAIR_STRIDE * 4; }
 
 hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void* const* spectra, int order,
                             void* y, const void* mats, int B, int D, const Twiddles& tw, hipStream_t s) {
@@ -484,17 +607,16 @@ hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void*
   ch.order = order;
   const dim3 grid(D * (B / 2)), block(mf::T);
   if (gated)
-    hipLaunchKernelGGL((k_conv_mfma<true>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch, (const bf16x8*)mats,
+    hipLaunchKernelGGL((k_conv_mfma<true>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch, (const u32x4*)mats,
                        B, D, tw);
   else
     hipLaunchKernelGGL((k_conv_mfma<false>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch,
-                       (const bf16x8*)mats, B, D, tw);
+                       (const u32x4*)mats, B, D, tw);
   return hipGetLastError();
 }
 
 hipError_t launch_pair_spectrum(const float2* Hnat, void* Hc, int D, hipStream_t s) {
-  hipLaunchKernelGGL(k_pair_spectrum, dim3((mf::PAIR_SLABS * 16 * 64 + 255) / 256, D), dim3(256), 0, s, Hnat,
-                     (uint32_t*)Hc);
+  hipLaunchKernelGGL(k_pair_spectrum, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc);
   return hipGetLastError();
 }
 

@@ -53,10 +53,10 @@ def floor_bytes_per_step(w) -> int:
 
 
 def uses_matrix_cores(w) -> bool:
-    """Causal, bf16 storage, L = 8192, rows in pairs of one channel, order <= 2: the library's matrix-core
+    """Causal, bf16 storage, L = 8192, rows in pairs of one channel, order <= 3: the library's matrix-core
     kernel."""
     return (w.mode == "causal" and w.dtype == "bf16" and w.dims[0] == 8192 and w.B % 2 == 0
-            and w.filter != "film" and w.order <= 2)
+            and w.filter != "film" and w.order <= 3)
 
 
 def single_launch_per_order(w) -> bool:
@@ -76,8 +76,9 @@ def kernel_key(w) -> str:
 
 def arithmetic(w) -> str:
     if uses_matrix_cores(w):
-        return ("matrix-core DFT steps on bf16 operands (DFT matrices and transform data rounded to bf16), fp32 "
-                "accumulation, fp32 twiddles and spectral product; u_1 rounded to bf16 between the orders")
+        return ("matrix-core DFT steps on fp16 operands (DFT matrices, spectrum copy and transform data rounded to "
+                "fp16 after exact power-of-two range scaling; the first product reads the bf16 input exactly), "
+                "fp32 accumulation, fp32 twiddles and spectral product; u_1 passes between the orders in fp16")
     if w.dtype == "bf16":
         return "fp32 (bf16 only for the stored v, x_i and y)"
     return "fp32"

@@ -28,11 +28,14 @@
  *     stay fp32.
  *   - Arithmetic: fp32 on every path (radix butterflies on the vector units, fp32 twiddles, fp32 spectra and
  *     spectral products), with one exception, the matrix-core path of hyena_fftconv / hyena_operator (bf16
- *     storage, causal L = 8192, even B, order <= 2): its DFT steps are bf16 x bf16 matrix products with
- *     fp32 accumulation -- the DFT matrices and the data entering each product are rounded to bf16 -- and
- *     between its two orders u_1 is rounded to bf16; twiddles and the spectral product stay fp32.  Its
- *     measured error against an fp64 evaluation is about 1.7e-2 (relative L2 per row, max over rows) at
- *     order 2, against 2e-3 for the fp32 paths with bf16 storage.
+ *     storage, causal L = 8192, even B, order <= 3): its DFT steps are matrix products with fp32
+ *     accumulation whose operands are fp16 -- the DFT matrices, a copy of the filter spectrum and the data
+ *     entering each product are rounded to fp16 after an exact power-of-two scaling that keeps them in fp16's
+ *     range -- except the first product, which takes the bf16 inputs exactly against a matrix split into two
+ *     bf16 parts; u_i passes between orders in fp16 the same way; twiddles and the spectral product stay
+ *     fp32.  Its measured error against an fp64 evaluation (relative L2 per row, max over rows) is 2.4e-3 at
+ *     order 2 on the 8192-sample workload and at most 5.7e-3 at order 3, against 1.7e-3 to 2e-3 for the
+ *     fp32 paths with bf16 storage.
  *   - Calls are asynchronous on the caller's HIP stream and never synchronise the host, except the
  *     first call on a device, which uploads the library's constant tables (about 790 KB) once with a
  *     blocking copy; hyena_init() does that upload ahead of time (for example before graph capture).
@@ -94,8 +97,8 @@ typedef struct {
 } hyena_filter_params;
 
 /* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array):
- * causal 8L bytes per channel (for L = 8192 followed by a bf16 copy laid out for the matrix-core
- * kernel, 36 KB per channel, except with HYENA_PER_SAMPLE); periodic 1-D 4L bytes per channel; 3-D
+ * causal 8L bytes per channel (for L = 8192 followed by an fp16 copy laid out for the matrix-core
+ * kernel, 36.25 KB per channel, except with HYENA_PER_SAMPLE); periodic 1-D 4L bytes per channel; 3-D
  * 128*128*65*8 bytes per channel (zero-padded) or 64*64*33*8 (periodic).  With HYENA_PER_SAMPLE, D counts
  * filters (B*D). */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
@@ -162,13 +165,12 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
  * x: host array of `order` device pointers (x[0] = x_1); spectra: host array of `order` spectra
  * (spectra[i] pairs with x[i]).  y doubles as the buffer between orders; y may equal v exactly but
  * must not overlap any x_i.  ws: hyena_workspace_bytes bytes.
- * Engines: order <= 2 on the matrix-core case (see hyena_fftconv) runs both orders in one launch with u_1
- * kept on chip, rounded to bf16 exactly as a store would round it, so the result equals `order` separate
- * hyena_fftconv calls bit for bit.  Every other single-pass case (causal L <= 16384, periodic L <= 32768)
- * runs up to 8 orders per launch of the fp32 engine with u_i kept on chip in fp32 (beyond 8 orders u passes
- * through y, in the storage type, between launches); the multi-pass plans (longer rows, 3-D) chain the
- * orders through the fp32 workspace.  Orders above 2 never take the matrix cores: their bf16 operands
- * compound across orders past the bf16 tolerance. */
+ * Engines: order <= 3 on the matrix-core case (see hyena_fftconv) runs every order in one launch with u_i
+ * kept on chip (as fp16 operands, see the conventions above).  Every other single-pass case (causal
+ * L <= 16384, periodic L <= 32768) runs up to 8 orders per launch of the fp32 engine with u_i kept on chip in
+ * fp32 (beyond 8 orders u passes through y, in the storage type, between launches); the multi-pass plans
+ * (longer rows, 3-D) chain the orders through the fp32 workspace.  Orders above 3 never take the matrix
+ * cores: their 16-bit operands compound across orders towards the bf16 tolerance. */
 int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *v,
                    const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,
                    hipStream_t stream);

@@ -42,8 +42,9 @@ def _size(fn, *args):
 
 def test_size_queries(lib):
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([8192]), L.CAUSAL, 768)
-    # L = 8192 adds the matrix-core copy: 9 slabs x 16 registers x 64 lanes of bf16 pairs per channel
-    assert st == 0 and n == 768 * 8192 * 8 + 768 * 9 * 16 * 64 * 4
+    # L = 8192 adds the matrix-core copy: 9 slabs x 16 registers x 64 lanes of fp16 pairs per channel, then a
+    # 256-byte tail holding the copy's scale
+    assert st == 0 and n == 768 * 8192 * 8 + 768 * (9 * 16 * 64 * 4 + 256)
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([4096]), L.CAUSAL, 768)
     assert st == 0 and n == 768 * 4096 * 8
     st, n = _size(lib.hyena_filter_workspace_bytes, L.dims_of([1024]), L.CAUSAL, 16)
