@@ -28,8 +28,12 @@ struct DeviceTables {
   Twiddles tw;
   const void* mats;       // DFT matrices of the matrix-core path (bf16, per lane)
   void* scratch;          // this device's copy of `scratch`
+  SideStream side;        // the long-row plans' second stream (default priority) and its fork / join events
   bool ready;
 };
+// Held while a long-row plan forks onto a device's side stream, so that concurrent calls do not interleave
+// their fork and join events.
+std::mutex g_side_mu;
 DeviceTables g_dev[kMaxDevices];
 
 // W_N^j = exp(-2 pi i j / N) in double, rounded once to fp32.
@@ -64,6 +68,10 @@ int init_current_device(DeviceTables** out) {
       return HYENA_EHIP;
     t.tw.pow2 = (const float2*)tw;
     t.tw.fine = (const float2*)tw + kTwPow2Entries;
+    if (hipStreamCreateWithFlags(&t.side.s, hipStreamNonBlocking) != hipSuccess) return HYENA_EHIP;
+    if (hipEventCreateWithFlags(&t.side.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&t.side.join, hipEventDisableTiming) != hipSuccess)
+      return HYENA_EHIP;
     t.mats = mats;
     t.scratch = scr;
     t.ready = true;
@@ -169,13 +177,41 @@ size_t taps_per_channel(int kind, int64_t pts) { return is3d(kind) ? conv3d_taps
 bool has_pair_copy(int64_t L) { return mfma_pair_supported(log2i(L), 2); }
 size_t pair_copy_temp_bytes(int64_t L, int64_t D) { return (size_t)D * (size_t)(L + 1) * sizeof(float2); }
 
-// Rows per multi-pass chunk by default: about 160 MB of intermediate.  Smaller chunks (24-96 MB,
-// sized for the 256 MB memory-side cache) measured slower, from fewer workgroups per launch; larger
-// ones (up to whole workloads) measured the same.
+// Rows per multi-pass chunk by default on one stream: about 160 MB of intermediate (the decode state's
+// prefix convolutions and the 3-D plans).  Smaller chunks on one stream (24-96 MB, sized for the 256 MB
+// memory-side cache) measured slower, from fewer workgroups per launch; larger ones measured the same.
 int64_t default_chunk_rows(int64_t per, int64_t rows) {
   int64_t c = ((int64_t)160 << 20) / per;
   if (c < 1) c = 1;
   return c < rows ? c : rows;
+}
+
+// The 1-D long-row plans run chunks of about 64 MB of intermediate two at a time, on the caller's stream and
+// the library's side stream (32, 64 and 80 MB measured 5.12, 4.77 and 4.91 ms per step at L = 2^20, fp32,
+// 256 rows, against 5.37 ms for one stream of 160 MB chunks).  The workspace holds two chunks.
+int64_t pair_chunk_rows(int64_t per, int64_t rows) {
+  int64_t c = ((int64_t)64 << 20) / per;
+  if (c < 1) c = 1;
+  return c < rows ? c : rows;
+}
+size_t fourstep_ws_bytes(size_t per, int64_t rows) {
+  const int64_t c = pair_chunk_rows((int64_t)per, rows);
+  return (size_t)(rows > c ? 2 : 1) * (size_t)c * per;
+}
+// Chunk rows of a long-row plan within a workspace of ws_bytes, and whether it alternates two streams
+// (0: the workspace does not hold one row).
+int fourstep_chunk(size_t per, int64_t rows, size_t ws_bytes, bool* two) {
+  const int64_t cap = (int64_t)(ws_bytes / per);
+  *two = false;
+  if (cap < 1) return 0;
+  int64_t c = cap;
+  if (cap >= 2 && rows > 1) {
+    c = cap / 2;
+    const int64_t want = pair_chunk_rows((int64_t)per, rows);
+    if (c > want) c = want;
+    *two = rows > c;
+  }
+  return (int)(c < rows ? c : rows);
 }
 
 // Channels per chunk while building spectra from taps: about 1 GB of intermediate.  Nothing is reused
@@ -329,8 +365,10 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
     ws = dt->scratch;
     ws_bytes = kNoallocScratchBytes;
   }
+  bool two = false;
   if (per) {
-    chunk = chunk_from_ws(per, B * D, ws, ws_bytes);
+    chunk = is3d(kind) ? chunk_from_ws(per, B * D, ws, ws_bytes)
+                       : (ws && !((size_t)ws & 255u) ? fourstep_chunk(per, B * D, ws_bytes, &two) : 0);
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
     for (int i = 0; i < order; ++i)
@@ -341,10 +379,15 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
   if (chunk && is3d(kind))
     return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws, chunk,
                                     tw, stream, circ3(kind), hsb));
-  if (chunk)
+  if (chunk) {
+    DeviceTables* dt = nullptr;
+    if (two && (st = init_current_device(&dt))) return st;
+    std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
+    if (two) lk.lock();
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
-                                             spectra, y, (float2*)ws, chunk, tw, stream,
-                                             kind == K_CIRC1 ? 1 : 0, hsb));
+                                             spectra, y, (float2*)ws, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0, hsb,
+                                             two ? &dt->side : nullptr));
+  }
   if (kind == K_CAUSAL && !hsb && order <= kMfmaMaxOrder && use_mfma(dtype, B, pts)) {
     bool aligned = aligned16(v) && aligned16(y);
     for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);
@@ -426,7 +469,7 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   const int kind = kind_of(mode, dims);
   *bytes = 0;
   const size_t per = row_intermediate_bytes(kind, pts);
-  if (per) *bytes = (size_t)default_chunk_rows((int64_t)per, B * D) * per;
+  if (per) *bytes = is3d(kind) ? (size_t)default_chunk_rows((int64_t)per, B * D) * per : fourstep_ws_bytes(per, B * D);
   return HYENA_OK;
 }
 
@@ -534,8 +577,10 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   if (gate && y != gate && overlaps(y, tb, gate, tb)) return HYENA_EALIAS;
   int chunk = 0;
   const size_t per = row_intermediate_bytes(kind, pts);
+  bool two = false;
   if (per) {
-    chunk = chunk_from_ws(per, B * D, ws, ws_bytes);
+    chunk = is3d(kind) ? chunk_from_ws(per, B * D, ws, ws_bytes)
+                       : (ws && !((size_t)ws & 255u) ? fourstep_chunk(per, B * D, ws_bytes, &two) : 0);
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, u, tb) || (gate && overlaps(ws, ws_bytes, gate, tb)))
       return HYENA_EALIAS;
@@ -548,9 +593,13 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
     if (is3d(kind))
       return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
                                       stream, circ3(kind), hsb));
+    DeviceTables* dt = nullptr;
+    if (two && (st = init_current_device(&dt))) return st;
+    std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
+    if (two) lk.lock();
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs,
-                                             sp, y, (float2*)ws, chunk, tw, stream,
-                                             kind == K_CIRC1 ? 1 : 0, hsb));
+                                             sp, y, (float2*)ws, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0, hsb,
+                                             two ? &dt->side : nullptr));
   }
   if (kind == K_CIRC1)
     return hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, u, gate, y,

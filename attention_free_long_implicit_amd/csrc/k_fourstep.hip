@@ -313,16 +313,30 @@ namespace {
 template <int LOG2M>
 size_t fs_row_bytes() { return (size_t)(1 << LOG2M) * sizeof(float2); }
 
+// Chunks of rows run every pass of every order before the next chunk starts, so a chunk's intermediate is
+// reread while the memory-side cache may still hold it; with a side stream two chunks run at once, which keeps
+// the compute units busy while each chunk stays small (64 MB of intermediate measured best at L = 2^20:
+// 4.77 ms per step against 5.37 ms for one stream of 160 MB chunks).
 template <int LOG2M, bool BF16, bool FULL>
 hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
-                          void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s, int hsb) {
+                          void* y, float2* I0, int chunk, const Twiddles& tw, hipStream_t s0, int hsb,
+                          const SideStream* side) {
   using F = FS<LOG2M>;
   using E = typename Store<BF16>::elem;
   const int rows = B * D;
   const int tiles = F::M2 / F::C;
   const int groups = (F::M1 / 2) / F::G;
-  for (int q0 = 0; q0 < rows; q0 += chunk) {
+  const bool two = side != nullptr && rows > chunk;
+  if (two) {
+    hipError_t e = hipEventRecord(side->fork, s0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return e;
+  }
+  int k = 0;
+  for (int q0 = 0; q0 < rows; q0 += chunk, ++k) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
+    const hipStream_t s = (two && (k & 1)) ? side->s : s0;
+    float2* I = I0 + (two && (k & 1) ? (size_t)chunk * F::M : 0);
     hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
                        (const E*)v, (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
@@ -339,6 +353,11 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
                            (const E*)nullptr, (const E*)nullptr, (E*)y, I, q0, nq, B, D, tw);
     }
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (two) {
+    hipError_t e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s0, side->join, 0);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -383,15 +402,15 @@ hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int 
 
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, hipStream_t s, int full, int hsb) {
+                                  const Twiddles& tw, hipStream_t s, int full, int hsb, const SideStream* side) {
   switch (log2L) {
 #define X(n)                                                                                                   \
   case n:                                                                                                      \
     if (full)                                                                                                  \
-      return bf16 ? fs_conv_launch<n, true, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb)   \
-                  : fs_conv_launch<n, false, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb); \
-    return bf16 ? fs_conv_launch<n, true, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb)    \
-                : fs_conv_launch<n, false, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb);
+      return bf16 ? fs_conv_launch<n, true, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb, side)   \
+                  : fs_conv_launch<n, false, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb, side); \
+    return bf16 ? fs_conv_launch<n, true, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb, side)    \
+                : fs_conv_launch<n, false, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb, side);
     HYENA_FS_CASES(X)
 #undef X
   }

@@ -420,7 +420,7 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
       // rows 4h + e (e < 4): real part (row b0) in o[e], imaginary part (row b1) in o[8 + e]
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float a = o[e] * f_out, b = o[8 + e] * f_out;
+        float a = o[e], b = o[8 + e];   // times f_out (a power of two) is the result
         if (GATE) {
           a *= elem_f32<TT>(G[0][e]);
           b *= elem_f32<TT>(G[1][e]);
@@ -438,8 +438,8 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
         u32x4 Y0, Y1;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          Y0[q] = pack2(yv[0][e][2 * q], yv[0][e][2 * q + 1]);
-          Y1[q] = pack2(yv[1][e][2 * q], yv[1][e][2 * q + 1]);
+          Y0[q] = pack2(yv[0][e][2 * q] * f_out, yv[0][e][2 * q + 1] * f_out);
+          Y1[q] = pack2(yv[1][e][2 * q] * f_out, yv[1][e][2 * q + 1] * f_out);
         }
         *reinterpret_cast<u32x4*>(y0 + 1024 * (4 * h + e)) = Y0;
         *reinterpret_cast<u32x4*>(y1 + 1024 * (4 * h + e)) = Y1;
@@ -453,13 +453,14 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
       // lanes 0..31] (n1 = e) in the first and [b0 from lanes 32..63, b1 from lanes 32..63] (n1 = 4 + e) in
       // the second.
       m1a = mats[M1F_H * 64 + l0];
-      s_in = range_scale(block_max4(vmax, red));
+      s_in = range_scale(block_max4(vmax, red) * f_out);
+      const float c = f_out * s_in;    // a power of two: u_i scaled into [0.5, 1) in one exact product
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t a = pack2h(yv[0][e][2 * q] * s_in, yv[0][e][2 * q + 1] * s_in);
-          const uint32_t b = pack2h(yv[1][e][2 * q] * s_in, yv[1][e][2 * q + 1] * s_in);
+          const uint32_t a = pack2h(yv[0][e][2 * q] * c, yv[0][e][2 * q + 1] * c);
+          const uint32_t b = pack2h(yv[1][e][2 * q] * c, yv[1][e][2 * q + 1] * c);
           const auto rr = __builtin_amdgcn_permlane32_swap(a, b, false, false);
           V[e][q] = rr[0];
           V[4 + e][q] = rr[1];

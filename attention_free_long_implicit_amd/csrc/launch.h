@@ -37,9 +37,17 @@ hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D,
 bool fourstep_supported(int log2L);
 size_t fourstep_row_bytes(int log2L);
 // The intermediate I is fp32 for either storage type; u_i stays fp32 between orders.
+// side (optional): a second stream and two events; the chunks then alternate between the caller's stream and
+// that one (forked from and joined back into the caller's stream), each stream with its own half of I, which
+// must hold 2 * chunk rows.
+struct SideStream {
+  hipStream_t s;
+  hipEvent_t fork, join;
+};
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
-                                  const Twiddles& tw, hipStream_t s, int full = 0, int hsb = 0);
+                                  const Twiddles& tw, hipStream_t s, int full = 0, int hsb = 0,
+                                  const SideStream* side = nullptr);
 hipError_t launch_spectrum1d_fourstep(int log2L, const float* h, float2* Hs, int D, float2* I, int chunk,
                                       const Twiddles& tw, hipStream_t s, int full = 0);
 hipError_t launch_export1d_fourstep(int log2L, const float2* Hs, float2* H, int D, hipStream_t s);
