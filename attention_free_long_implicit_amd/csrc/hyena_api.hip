@@ -186,24 +186,29 @@ int64_t default_chunk_rows(int64_t per, int64_t rows) {
   return c < rows ? c : rows;
 }
 
-// The 1-D long-row plans run chunks of about 64 MB of intermediate two at a time, on the caller's stream and
-// the library's side stream (32, 64 and 80 MB measured 5.12, 4.77 and 4.91 ms per step at L = 2^20, fp32,
-// 256 rows, against 5.37 ms for one stream of 160 MB chunks).  The workspace holds two chunks.
+// The multi-pass plans (1-D long rows, 3-D volumes) run chunks of about 64 MB of intermediate two at a time,
+// on the caller's stream and the library's side stream (32, 48, 64, 72 and 80 MB measured 5.12, 4.86, 4.77-4.84,
+// 4.93 and 4.91 ms per step at L = 2^20, fp32, 256 rows, against 5.37 ms for one stream of 160 MB chunks;
+// 3-D 64^3 zero-padded, 128 volumes: 16, 32, 64, 128 MB 2.11, 1.63, 1.62, 1.77 ms against 1.79 ms for one
+// chunk).  A whole batch of at most 192 MB of intermediate runs as one chunk on one stream (periodic 64^3,
+// 138 MB: 0.41 ms, against 0.43 ms in 64 MB pairs).  The workspace holds two chunks.
 int64_t pair_chunk_rows(int64_t per, int64_t rows) {
+  if ((size_t)rows * (size_t)per <= ((size_t)192 << 20)) return rows;
   int64_t c = ((int64_t)64 << 20) / per;
   if (c < 1) c = 1;
   return c < rows ? c : rows;
 }
-size_t fourstep_ws_bytes(size_t per, int64_t rows) {
+size_t pair_ws_bytes(size_t per, int64_t rows) {
   const int64_t c = pair_chunk_rows((int64_t)per, rows);
   return (size_t)(rows > c ? 2 : 1) * (size_t)c * per;
 }
-// Chunk rows of a long-row plan within a workspace of ws_bytes, and whether it alternates two streams
+// Chunk rows of a multi-pass plan within a workspace of ws_bytes, and whether it alternates two streams
 // (0: the workspace does not hold one row).
-int fourstep_chunk(size_t per, int64_t rows, size_t ws_bytes, bool* two) {
+int pair_chunk(size_t per, int64_t rows, size_t ws_bytes, bool* two) {
   const int64_t cap = (int64_t)(ws_bytes / per);
   *two = false;
   if (cap < 1) return 0;
+  if (cap >= rows && pair_chunk_rows((int64_t)per, rows) >= rows) return (int)rows;   // one chunk
   int64_t c = cap;
   if (cap >= 2 && rows > 1) {
     c = cap / 2;
@@ -266,14 +271,6 @@ int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const v
   }
   return hip_status(launch_conv1d_single(log2i(L), dtype == HYENA_BF16, u, gate, y, (const float2*)spectrum,
                                          (int)B, (int)D, tw, s, 0, hsb));
-}
-
-// Multi-pass chunk rows that fit the caller's workspace (0 when it is too small).
-int chunk_from_ws(size_t per, int64_t rows, void* ws, size_t ws_bytes) {
-  if (!ws) return 0;
-  if ((size_t)ws & 255u) return 0;
-  const int64_t c = (int64_t)(ws_bytes / per);
-  return (int)(c < rows ? c : rows);
 }
 
 // Align a workspace cursor to 256 bytes; false when the remaining room is too small.
@@ -367,8 +364,7 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
   }
   bool two = false;
   if (per) {
-    chunk = is3d(kind) ? chunk_from_ws(per, B * D, ws, ws_bytes)
-                       : (ws && !((size_t)ws & 255u) ? fourstep_chunk(per, B * D, ws_bytes, &two) : 0);
+    chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &two) : 0;
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
     for (int i = 0; i < order; ++i)
@@ -376,14 +372,14 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
   }
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
-  if (chunk && is3d(kind))
-    return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws, chunk,
-                                    tw, stream, circ3(kind), hsb));
   if (chunk) {
     DeviceTables* dt = nullptr;
     if (two && (st = init_current_device(&dt))) return st;
     std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
     if (two) lk.lock();
+    if (is3d(kind))
+      return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws,
+                                      chunk, tw, stream, circ3(kind), hsb, two ? &dt->side : nullptr));
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
                                              spectra, y, (float2*)ws, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0, hsb,
                                              two ? &dt->side : nullptr));
@@ -469,7 +465,7 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   const int kind = kind_of(mode, dims);
   *bytes = 0;
   const size_t per = row_intermediate_bytes(kind, pts);
-  if (per) *bytes = is3d(kind) ? (size_t)default_chunk_rows((int64_t)per, B * D) * per : fourstep_ws_bytes(per, B * D);
+  if (per) *bytes = pair_ws_bytes(per, B * D);
   return HYENA_OK;
 }
 
@@ -579,8 +575,7 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   const size_t per = row_intermediate_bytes(kind, pts);
   bool two = false;
   if (per) {
-    chunk = is3d(kind) ? chunk_from_ws(per, B * D, ws, ws_bytes)
-                       : (ws && !((size_t)ws & 255u) ? fourstep_chunk(per, B * D, ws_bytes, &two) : 0);
+    chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &two) : 0;
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, u, tb) || (gate && overlaps(ws, ws_bytes, gate, tb)))
       return HYENA_EALIAS;
@@ -590,13 +585,13 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   if (chunk) {
     const void* xs[1] = {gate};
     const void* sp[1] = {spectrum};
-    if (is3d(kind))
-      return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
-                                      stream, circ3(kind), hsb));
     DeviceTables* dt = nullptr;
     if (two && (st = init_current_device(&dt))) return st;
     std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
     if (two) lk.lock();
+    if (is3d(kind))
+      return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
+                                      stream, circ3(kind), hsb, two ? &dt->side : nullptr));
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs,
                                              sp, y, (float2*)ws, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0, hsb,
                                              two ? &dt->side : nullptr));

@@ -320,13 +320,23 @@ size_t conv3d_taps_per_channel(int circ) {
 namespace {
 template <class G, bool BF16>
 hipError_t conv3d_launch_t(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
-                           void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s, int hsb) {
+                           void* y, float2* I0, int chunk, const Twiddles& tw, hipStream_t s0, int hsb,
+                           const SideStream* side) {
   using C = K3<G>;
   constexpr int N = C::N, T = C::T, TILES = C::TILES;
   using E = typename Store<BF16>::elem;
   const int rows = B * D;
-  for (int q0 = 0; q0 < rows; q0 += chunk) {
+  const bool two = side != nullptr && rows > chunk;
+  if (two) {
+    hipError_t e = hipEventRecord(side->fork, s0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+    if (e != hipSuccess) return e;
+  }
+  int k = 0;
+  for (int q0 = 0; q0 < rows; q0 += chunk, ++k) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
+    const hipStream_t s = (two && (k & 1)) ? side->s : s0;
+    float2* I = I0 + (two && (k & 1) ? (size_t)chunk * (conv3d_volume_bytes(G::PAD ? 0 : 1) / sizeof(float2)) : 0);
     hipLaunchKernelGGL((k3_planes<G, BF16, 0, false, false>), dim3(N * nq), dim3(T), 0, s, (const E*)v,
                        (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
@@ -343,6 +353,11 @@ hipError_t conv3d_launch_t(int order, int B, int D, const void* v, const void* c
                            (const E*)nullptr, (E*)y, I, q0, nq, B, D, tw);
     }
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (two) {
+    hipError_t e = hipEventRecord(side->join, side->s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s0, side->join, 0);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -374,12 +389,12 @@ hipError_t export3d_launch_t(const float2* Hs, float2* H, int D, hipStream_t s) 
 
 hipError_t launch_conv3d(int bf16, int order, int B, int D, const void* v, const void* const* x,
                          const void* const* spectra, void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s,
-                         int circ, int hsb) {
+                         int circ, int hsb, const SideStream* side) {
   if (circ)
-    return bf16 ? conv3d_launch_t<Geo3<true>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb)
-                : conv3d_launch_t<Geo3<true>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb);
-  return bf16 ? conv3d_launch_t<Geo3<false>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb)
-              : conv3d_launch_t<Geo3<false>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb);
+    return bf16 ? conv3d_launch_t<Geo3<true>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb, side)
+                : conv3d_launch_t<Geo3<true>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb, side);
+  return bf16 ? conv3d_launch_t<Geo3<false>, true>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb, side)
+              : conv3d_launch_t<Geo3<false>, false>(order, B, D, v, x, spectra, y, I, chunk, tw, s, hsb, side);
 }
 
 hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,

@@ -59,9 +59,10 @@ size_t conv3d_volume_bytes(int circ);                 // intermediate per (b, d)
 size_t conv3d_filter_volume_bytes(int circ);          // intermediate per channel while building a spectrum
 size_t conv3d_spectrum_bytes_per_channel(int circ);
 size_t conv3d_taps_per_channel(int circ);             // (2n-1)^3 or n^3
+// side (optional): as for launch_conv1d_fourstep; I then holds 2 * chunk volumes.
 hipError_t launch_conv3d(int bf16, int order, int B, int D, const void* v, const void* const* x,
                          const void* const* spectra, void* y, float2* I, int chunk, const Twiddles& tw, hipStream_t s,
-                         int circ, int hsb = 0);
+                         int circ, int hsb = 0, const SideStream* side = nullptr);
 hipError_t launch_spectrum3d(const float* h, float2* Hs, int D, float2* I, int chunk, const Twiddles& tw,
                              hipStream_t s, int circ);
 hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s, int circ);
