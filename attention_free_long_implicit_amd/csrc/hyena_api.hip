@@ -234,16 +234,16 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // pointer 16-byte aligned.
 bool use_mfma(int dtype, int64_t B, int64_t L) { return dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B); }
 
-// Highest operator order sent to the matrix-core kernel.  Its fp16 transform operands cost a few 1e-4 of
-// relative error per order, and later orders amplify what earlier ones leave: measured against the oracle
-// (max over rows, with no decay window, the worst filter family) 2.6e-3 at order 2 and 5.7e-3 at order 3,
-// but already 1.2e-2 at order 4 and 4.1e-2 at order 6 against the 2e-2 that bf16 storage allows.  Higher
-// orders take the fp32 engine, whose only roundings are the bf16 stores.
+// Highest operator order sent to the matrix-core kernel.  Its fp16 transform operands and products cost a
+// few 1e-4 of relative error per order, and later orders amplify what earlier ones leave: measured against
+// the oracle (max over rows, with no decay window, the worst filter family) 3.4e-3 at order 2, 6.8e-3 at
+// order 3 and 8.8e-3 at order 4, but 5.4e-2 at order 6 against the 2e-2 that bf16 storage allows.  Orders
+// above 3 take the fp32 engine, whose only roundings are the bf16 stores, keeping a margin of about 3x.
 constexpr int kMfmaMaxOrder = 3;
 
 // Orders [0, order) through the matrix-core kernel, up to kMfmaMaxChain orders per launch with u_i on chip.
 int conv_mfma_chain(int64_t B, int64_t D, int64_t L, const void* u, const void* const* gates,
-                    const void* const* spectra, int order, void* y, const Twiddles& tw, hipStream_t s) {
+                    const void* const* spectra, int order, void* y, hipStream_t s) {
   const void* mats = device_mats();
   if (!mats) return HYENA_EHIP;
   const void* cur = u;
@@ -255,7 +255,7 @@ int conv_mfma_chain(int64_t B, int64_t D, int64_t L, const void* u, const void* 
       g[k] = gates[i0 + k];
       sp[k] = (const char*)spectra[i0 + k] + (size_t)D * (size_t)L * sizeof(float2);
     }
-    const int st = hip_status(launch_conv_mfma(cur, g, sp, n, y, mats, (int)B, (int)D, tw, s));
+    const int st = hip_status(launch_conv_mfma(cur, g, sp, n, y, mats, (int)B, (int)D, s));
     if (st) return st;
     cur = y;
   }
@@ -267,7 +267,7 @@ int conv_once(int64_t B, int64_t D, int64_t L, int dtype, const void* u, const v
   if (!hsb && use_mfma(dtype, B, L) && aligned16(u) && aligned16(gate) && aligned16(y)) {
     const void* g[1] = {gate};
     const void* sp[1] = {spectrum};
-    return conv_mfma_chain(B, D, L, u, g, sp, 1, y, tw, s);
+    return conv_mfma_chain(B, D, L, u, g, sp, 1, y, s);
   }
   return hip_status(launch_conv1d_single(log2i(L), dtype == HYENA_BF16, u, gate, y, (const float2*)spectrum,
                                          (int)B, (int)D, tw, s, 0, hsb));
@@ -387,7 +387,7 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
   if (kind == K_CAUSAL && !hsb && order <= kMfmaMaxOrder && use_mfma(dtype, B, pts)) {
     bool aligned = aligned16(v) && aligned16(y);
     for (int i = 0; i < order; ++i) aligned = aligned && aligned16(x[i]);
-    if (aligned) return conv_mfma_chain(B, D, pts, v, x, spectra, order, y, tw, stream);
+    if (aligned) return conv_mfma_chain(B, D, pts, v, x, spectra, order, y, stream);
   }
   // the single-pass fp32 engine: up to kConvMaxChain orders per launch with u_i on chip
   const int lg = kind == K_CIRC1 ? circular_log2(pts) : log2i(pts);

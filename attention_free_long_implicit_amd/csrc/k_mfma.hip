@@ -15,6 +15,11 @@
 // so that its largest bin does, and the inverse radix-32 matrices carry a factor 1/32 each, so no
 // intermediate exceeds 2^13; the output is scaled back in fp32 before the gate.  The first product of
 // the first order reads the bf16 inputs exactly, against a matrix split into two bf16 parts (hi + lo).
+// The two elementwise steps between products (the twiddle W_1024 and the spectral product) take the
+// accumulators rounded to fp16 and multiply them in packed fp16 arithmetic, two complex values per
+// instruction, with twiddles and spectrum already stored as fp16 pairs; the result is the next product's
+// operand as it stands (two more roundings per step than an fp32 product, which moved the order-2 error on
+// the 8192-sample workload from 2.4e-3 to 2.8e-3, for a third fewer vector instructions).
 //
 // Two rows b0, b1 of one channel (same filter) are transformed together as z = u_b0 + i u_b1:
 // since h is real, IDFT(DFT(z) H) = (h * u_b0) + i (h * u_b1), so no real-input split is needed.
@@ -63,9 +68,10 @@ constexpr int PLANE = 16 * SLAB;            // 16 slabs
 constexpr int T = 256;                      // 4 waves
 // Matrix table, per lane 8 16-bit values in the A-operand layout (row i = lane % 32, K = 8 (lane / 32) + e).
 // Fixed radix-16 matrices first -- the forward one as two bf16 parts (hi, and lo = the rest) and in fp16,
-// the two inverse blocks in fp16 -- then per slab k1 four fp16 radix-32 matrices of four blocks each (the
-// inverse ones, passes 3' and 2', scaled by 1/32).
-enum { M1F_HI = 0, M1F_LO, M1F_H, M1I_R, M1I_I, NFIX };
+// the two inverse blocks in fp16 -- and the lane's twiddles W_1024^{j k(v)} as fp16 pairs (cos parts of
+// registers 0..7, 8..15, then the -sin parts) -- then per slab k1 four fp16 radix-32 matrices of four blocks each (cos
+// and sin, each for K < 16 and K >= 16; the inverse ones, passes 3' and 2', scaled by 1/32).
+enum { M1F_HI = 0, M1F_LO, M1F_H, M1I_R, M1I_I, TW_C0, TW_C1, TW_S0, TW_S1, NFIX };
 enum { MF2 = 0, MF3, MI3, MI2, NSLABMAT };       // pass 2, pass 3, pass 3', pass 2'
 enum { B_CLO = 0, B_CHI, B_SLO, B_SHI, NBLK };   // cos / sin, K < 16 / K >= 16
 constexpr int SLAB_TABLE = NSLABMAT * NBLK;       // 16-byte entries per lane per slab
@@ -125,6 +131,7 @@ __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 *
 // Complex radix-32 product of matrix blocks M (cos lo/hi, sin lo/hi) and data blocks (xr_lo, xr_hi, xi_lo,
 // xi_hi).  Forward (W = cos - i sin): Yr = C Xr + S Xi, Yi = C Xi - S Xr;
 // inverse (W = cos + i sin):           Yr = C Xr - S Xi, Yi = C Xi + S Xr.
+// (Storing -sin blocks instead of negating data costs more in matrix loads than the sign flips cost.)
 // A and B operands share one register layout (lane % 32 = row or column, K = 8 (lane / 32) + e), so the
 // same registers serve either side.  DATA_A = false: matrix on A, data columns on B -> output row = the
 // matrix row, lane = the data column.  DATA_A = true: data on A -> the transpose (lane = the matrix row,
@@ -160,28 +167,35 @@ __device__ __forceinline__ uint32_t pack2h(float a, float b) {
 }
 __device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-// one dword of fp16 (re low, im high) -> complex fp32
-__device__ __forceinline__ float2 unpack_h(uint32_t w) {
-  const f16x2 v = __builtin_bit_cast(f16x2, w);
-  return make_float2((float)v.x, (float)v.y);
+// fp32 accumulators -> fp16 pairs in accumulator order: pair q holds registers 2q (low half) and 2q + 1
+__device__ __forceinline__ void to_pairs(const f32x16& x, f16x2 (&p)[8]) {
+#pragma unroll
+  for (int q = 0; q < 8; ++q) p[q] = f16x2{(_Float16)x[2 * q], (_Float16)x[2 * q + 1]};
 }
-
-// fp32 accumulators, each multiplied by a complex factor, -> fp16 operands in accumulator order
-// (block lo = registers 0..7, block hi = registers 8..15)
-template <class F>
-__device__ __forceinline__ void pack_operands(const f32x16& xr, const f32x16& xi, F&& factor, f16x8& r_lo,
-                                              f16x8& r_hi, f16x8& i_lo, f16x8& i_hi) {
+// Complex product of fp16 pairs (a + i b) and (c + i s), or (c - i s) with CONJ, in packed fp16 arithmetic
+// (two complex values per instruction), written as MFMA operands (block lo = pairs 0..3, hi = pairs 4..7).
+template <bool CONJ>
+__device__ __forceinline__ void cmul_pairs(const f16x2 (&a)[8], const f16x2 (&b)[8], const f16x2 (&c)[8],
+                                           const f16x2 (&sn)[8], f16x8& r_lo, f16x8& r_hi, f16x8& i_lo,
+                                           f16x8& i_hi) {
   u32x4 rl, rh, il, ih;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const float2 a0 = factor(2 * m, make_float2(xr[2 * m], xi[2 * m]));
-    const float2 a1 = factor(2 * m + 1, make_float2(xr[2 * m + 1], xi[2 * m + 1]));
-    const float2 b0 = factor(8 + 2 * m, make_float2(xr[8 + 2 * m], xi[8 + 2 * m]));
-    const float2 b1 = factor(9 + 2 * m, make_float2(xr[9 + 2 * m], xi[9 + 2 * m]));
-    rl[m] = pack2h(a0.x, a1.x);
-    il[m] = pack2h(a0.y, a1.y);
-    rh[m] = pack2h(b0.x, b1.x);
-    ih[m] = pack2h(b0.y, b1.y);
+  for (int q = 0; q < 8; ++q) {
+    f16x2 re, im;
+    if (CONJ) {
+      re = __builtin_elementwise_fma(a[q], c[q], b[q] * sn[q]);
+      im = __builtin_elementwise_fma(b[q], c[q], -(a[q] * sn[q]));
+    } else {
+      re = __builtin_elementwise_fma(a[q], c[q], -(b[q] * sn[q]));
+      im = __builtin_elementwise_fma(a[q], sn[q], b[q] * c[q]);
+    }
+    if (q < 4) {
+      rl[q] = __builtin_bit_cast(uint32_t, re);
+      il[q] = __builtin_bit_cast(uint32_t, im);
+    } else {
+      rh[q - 4] = __builtin_bit_cast(uint32_t, re);
+      ih[q - 4] = __builtin_bit_cast(uint32_t, im);
+    }
   }
   r_lo = as_h(rl);
   r_hi = as_h(rh);
@@ -219,8 +233,7 @@ __device__ __forceinline__ float elem_f32(const u32x4& g) {
 // (row, n1) in global memory.
 template <bool GATE>
 __global__ void __launch_bounds__(mf::T, 2)
-k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ mats, int B, int D,
-            Twiddles tw) {
+k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ mats, int B, int D) {
   using namespace mf;
   __shared__ uint32_t S[PLANE];
   __shared__ float red[4];
@@ -245,9 +258,22 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
   // orders: m1a in fp16, loaded at the end of the previous order)
   u32x4 m1a = mats[M1F_HI * 64 + l0], m1b = mats[M1F_LO * 64 + l0];
   const u32x4 m1r = mats[M1I_R * 64 + l0], m1i = mats[M1I_I * 64 + l0];
-  float2 p2[16];
+  // as fp16 pairs (real parts, imaginary parts) in accumulator order
+  f16x2 pc[8], ps[8];
+  {
+    const u32x4 c0 = mats[TW_C0 * 64 + l0], c1 = mats[TW_C1 * 64 + l0];
+    const u32x4 s0 = mats[TW_S0 * 64 + l0], s1 = mats[TW_S1 * 64 + l0];
+    // (each element goes through a scalar: this compiler's __builtin_bit_cast of a subscripted vector
+    // element reads element 0 whatever the subscript)
 #pragma unroll
-  for (int v = 0; v < 16; ++v) p2[v] = twiddle<10>(tw, uint32_t((l0 & 31) * acc_row(v, l0 >> 5)));
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = c0[q], b = c1[q], e = s0[q], f = s1[q];
+      pc[q] = __builtin_bit_cast(f16x2, a);
+      pc[4 + q] = __builtin_bit_cast(f16x2, b);
+      ps[q] = __builtin_bit_cast(f16x2, e);
+      ps[4 + q] = __builtin_bit_cast(f16x2, f);
+    }
+  }
   // scale of the first order's input: the largest |u| of the row pair (bf16 magnitudes compare as
   // integers), brought into [0.5, 1)
   float s_in;
@@ -292,9 +318,11 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
       M[b] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                            mrs, mvo, ((k1s_ * SLAB_TABLE + which * NBLK + b) * 64) * 16, 0));
   };
-  // Filter spectrum: only slabs 0..8 are stored.  h is real, so H[N - k] = conj(H[k]); bin N - k of
-  // slab k1 > 8 is register 15 - v of lane 63 - l in slab 16 - k1, read mirrored; the conjugation (sign
-  // of the imaginary half) is applied where the value is used, so the load stays in flight until then.
+  // Filter spectrum: only slabs 0..8 are stored, as fp16 pairs in accumulator order (word q < 8: the real
+  // parts of registers 2q, 2q + 1; word 8 + q: their imaginary parts).  h is real, so H[N - k] = conj(H[k]);
+  // bin N - k of slab k1 > 8 is register 15 - v of lane 63 - l in slab 16 - k1: pair q of a mirrored slab
+  // is pair 7 - q of lane 63 - l with its halves swapped and the imaginary parts negated; the swap and
+  // the sign are applied where the value is used, so the load stays in flight until then.
   uint32_t hw[16];
   const __amdgpu_buffer_rsrc_t hrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)Hc, (short)0, PAIR_WORDS * 4, kRawBufferWord3);
@@ -304,8 +332,8 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
     const int slab = (mirror ? 16 - k1 : k1) * (16 * 64 * 4);
     const int vo = (mirror ? 63 - l : l) * 4;
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      hw[v] = __builtin_amdgcn_raw_buffer_load_b32(hrs, vo, slab + (mirror ? 15 - v : v) * 256, 0);
+    for (int k = 0; k < 16; ++k)
+      hw[k] = __builtin_amdgcn_raw_buffer_load_b32(hrs, vo, slab + (mirror ? (k < 8 ? 7 - k : 23 - k) : k) * 256, 0);
   };
   load_mat(ws, MF2, Ma);
   load_mat(ws, MF3, Mb);
@@ -372,22 +400,49 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
     }
     // twiddle W_1024^{n3 k2} (k2 = j, n3 = row of v); pass 3: matrix on A (rows k3, input n3 in accumulator
     // order), data on B -> lane = k2, registers = k3
-    pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, p2[v]); }, xr_lo, xr_hi, xi_lo, xi_hi);
+    {
+      f16x2 ar[8], ai[8];
+      to_pairs(dr, ar);
+      to_pairs(di, ai);
+      cmul_pairs<false>(ar, ai, pc, ps, xr_lo, xr_hi, xi_lo, xi_hi);
+    }
     dft32<false, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
     load_mat(k1s, MI2, Mb);
     // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N (normalised) in this exact order.
     // pass 3': data on A (rows k2 = j, input k3 in accumulator order), matrix on B -> lane = n3,
     // registers = k2
-    const uint32_t flip = k1s > 8 ? 0x80000000u : 0u;
-    pack_operands(dr, di, [&](int v, float2 x) { return cmul(x, unpack_h(hw[v] ^ flip)); }, xr_lo, xr_hi, xi_lo,
-                  xi_hi);
+    {
+      f16x2 ar[8], ai[8], hr[8], hi[8];
+      to_pairs(dr, ar);
+      to_pairs(di, ai);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        hr[q] = __builtin_bit_cast(f16x2, hw[q]);
+        hi[q] = __builtin_bit_cast(f16x2, hw[8 + q]);
+      }
+      if (k1s > 8) {   // wave-uniform: mirrored slab, conj(H) with the pair halves swapped
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          hr[q] = hr[q].yx;
+          hi[q] = hi[q].yx;
+        }
+        cmul_pairs<true>(ar, ai, hr, hi, xr_lo, xr_hi, xi_lo, xi_hi);
+      } else {
+        cmul_pairs<false>(ar, ai, hr, hi, xr_lo, xr_hi, xi_lo, xi_hi);
+      }
+    }
     if (it < 3) load_spectrum(k1s + 4);
     f32x16 er, ei;
     dft32<true, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
     if (it < 3) load_mat(k1s + 4, MF2, Ma);
     // conj twiddle W_1024^{n3 k2} (n3 = j, k2 = row of v); pass 2': matrix on A (rows n2, input k2 in
     // accumulator order), data on B -> lane = n3, registers = n2; store (n2, n3) at n2 * ROW + n3
-    pack_operands(er, ei, [&](int v, float2 x) { return cmulc(x, p2[v]); }, xr_lo, xr_hi, xi_lo, xi_hi);
+    {
+      f16x2 ar[8], ai[8];
+      to_pairs(er, ar);
+      to_pairs(ei, ai);
+      cmul_pairs<true>(ar, ai, pc, ps, xr_lo, xr_hi, xi_lo, xi_hi);
+    }
     dft32<true, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
     if (it < 3) load_mat(k1s + 4, MF3, Mb);
 #pragma unroll
@@ -472,10 +527,11 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
 }
 
 
-// Pair-order spectrum of one channel per workgroup: Hc[d][k1][v][lane] = c_d H[k]/N as fp16 (re low, im
-// high), k = k1 + 16 (lane%32) + 512 k3(v, lane/32), for k1 = 0..8 (the convolution kernel mirrors slabs 9..15
-// from slabs 7..1), followed by the float 1/c_d; c_d is the power of two that brings the channel's largest
-// |H[k]|/N into [0.5, 1).  H from the natural-order bins 0..L (upper bins by conjugate symmetry).
+// Pair-order spectrum of one channel per workgroup: for k1 = 0..8 (the convolution kernel mirrors slabs
+// 9..15 from slabs 7..1), Hc[d][k1][q][lane] = the real parts of c_d H[k(2q)]/N and c_d H[k(2q + 1)]/N as fp16
+// (register 2q low), Hc[d][k1][8 + q][lane] their imaginary parts, k(v) = k1 + 16 (lane%32) + 512 k3(v, lane/32);
+// then the float 1/c_d.  c_d is the power of two that brings the channel's largest |H[k]|/N into [0.5, 1).
+// H from the natural-order bins 0..L (upper bins by conjugate symmetry).
 __global__ void __launch_bounds__(256) k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc) {
   using namespace mf;
   __shared__ float red[4];
@@ -486,11 +542,13 @@ __global__ void __launch_bounds__(256) k_pair_spectrum(const float2* __restrict_
   const float c = range_scale(block_max4(m * (1.0f / N), red));
   const float sc = c * (1.0f / N);
   uint32_t* out = Hc + (size_t)d * PAIR_STRIDE;
-  for (int idx = threadIdx.x; idx < PAIR_WORDS; idx += 256) {   // (k1, v, lane)
-    const int k1 = idx / (16 * 64), v = (idx / 64) % 16, l = idx % 64;
-    const int k = k1 + 16 * (l & 31) + 512 * acc_row(v, l >> 5);
-    const float2 hv = k <= L ? hn[k] : cconj(hn[N - k]);
-    out[idx] = pack2h(hv.x * sc, hv.y * sc);
+  auto bin = [&](int k) { return k <= L ? hn[k] : cconj(hn[N - k]); };
+  for (int idx = threadIdx.x; idx < PAIR_WORDS; idx += 256) {   // (k1, word, lane)
+    const int k1 = idx / (16 * 64), wd = (idx / 64) % 16, l = idx % 64;
+    const int q = wd & 7;
+    const float2 a = bin(k1 + 16 * (l & 31) + 512 * acc_row(2 * q, l >> 5));
+    const float2 b = bin(k1 + 16 * (l & 31) + 512 * acc_row(2 * q + 1, l >> 5));
+    out[idx] = wd < 8 ? pack2h(a.x * sc, b.x * sc) : pack2h(a.y * sc, b.y * sc);
   }
   if (threadIdx.x < 64) out[PAIR_WORDS + threadIdx.x] = threadIdx.x == 0 ? __float_as_uint(1.0f / c) : 0u;
 }
@@ -575,6 +633,15 @@ void mfma_matrices_host(uint16_t* out) {
       out[(mf::M1F_H * 64 + l) * 8 + e] = f16_rne(f);
       out[(mf::M1I_R * 64 + l) * 8 + e] = f16_rne(fixed_entry(1, i, K));
       out[(mf::M1I_I * 64 + l) * 8 + e] = f16_rne(fixed_entry(2, i, K));
+      // twiddle pairs: dword m of block TW_C0 / TW_C1 holds registers 2m, 2m + 1 (resp. 8 + 2m, 9 + 2m)
+      const int h = l / 32, j = l % 32;
+      for (int blk = 0; blk < 2; ++blk) {
+        const int v = 8 * blk + e;
+        const int rowk = 8 * (v >> 2) + 4 * h + (v & 3);   // accumulator row of register v
+        const double a = kTwoPi * (double)((j * rowk) % 1024) / 1024;
+        out[((mf::TW_C0 + blk) * 64 + l) * 8 + e] = f16_rne(cos(a));
+        out[((mf::TW_S0 + blk) * 64 + l) * 8 + e] = f16_rne(-sin(a));
+      }
     }
   uint16_t* o = out + (size_t)mf::NFIX * 64 * 8;
   for (int k1 = 0; k1 < 16; ++k1)
@@ -595,7 +662,7 @@ bool mfma_pair_supported(int log2L, int B) { return log2L == 13 && B % 2 == 0; }
 size_t mfma_pair_spectrum_bytes_per_channel() { return (size_t)mf::PAIR_STRIDE * 4; }
 
 hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void* const* spectra, int order,
-                            void* y, const void* mats, int B, int D, const Twiddles& tw, hipStream_t s) {
+                            void* y, const void* mats, int B, int D, hipStream_t s) {
   if (order < 1 || order > kMfmaMaxChain) return hipErrorInvalidValue;
   MfmaChain ch{};
   bool gated = true;
@@ -609,10 +676,10 @@ hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void*
   const dim3 grid(D * (B / 2)), block(mf::T);
   if (gated)
     hipLaunchKernelGGL((k_conv_mfma<true>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch, (const u32x4*)mats,
-                       B, D, tw);
+                       B, D);
   else
     hipLaunchKernelGGL((k_conv_mfma<false>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch,
-                       (const u32x4*)mats, B, D, tw);
+                       (const u32x4*)mats, B, D);
   return hipGetLastError();
 }
 

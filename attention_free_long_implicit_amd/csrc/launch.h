@@ -70,12 +70,12 @@ hipError_t launch_export3d(const float2* Hs, float2* H, int D, hipStream_t s, in
 // ---- matrix-core path: bf16 storage, L = 8192, rows in pairs of one channel (B even)
 bool mfma_pair_supported(int log2L, int B);
 size_t mfma_pair_spectrum_bytes_per_channel();
-constexpr size_t kMfmaMatrixCount = (5 + 16 * 16) * 64 * 8;   // 16-bit values in the DFT-matrix table
+constexpr size_t kMfmaMatrixCount = (9 + 16 * 16) * 64 * 8;   // 16-bit values in the DFT-matrix table
 void mfma_matrices_host(uint16_t* out);
 // Orders 1..order back to back in one launch (u_i stays on chip); spectra[i] = matrix-core copies.
 constexpr int kMfmaMaxChain = 8;
 hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void* const* spectra, int order,
-                            void* y, const void* mats, int B, int D, const Twiddles& tw, hipStream_t s);
+                            void* y, const void* mats, int B, int D, hipStream_t s);
 hipError_t launch_pair_spectrum(const float2* Hnat, void* Hc, int D, hipStream_t s);
 
 // ---- implicit filter taps

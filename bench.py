@@ -78,7 +78,7 @@ def arithmetic(w) -> str:
     if uses_matrix_cores(w):
         return ("matrix-core DFT steps on fp16 operands (DFT matrices, spectrum copy and transform data rounded to "
                 "fp16 after exact power-of-two range scaling; the first product reads the bf16 input exactly), "
-                "fp32 accumulation, fp32 twiddles and spectral product; u_1 passes between the orders in fp16")
+                "fp32 accumulation; twiddle and spectral products in packed fp16; u_1 passes between the orders in fp16")
     if w.dtype == "bf16":
         return "fp32 (bf16 only for the stored v, x_i and y)"
     return "fp32"

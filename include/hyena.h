@@ -32,10 +32,10 @@
  *     accumulation whose operands are fp16 -- the DFT matrices, a copy of the filter spectrum and the data
  *     entering each product are rounded to fp16 after an exact power-of-two scaling that keeps them in fp16's
  *     range -- except the first product, which takes the bf16 inputs exactly against a matrix split into two
- *     bf16 parts; u_i passes between orders in fp16 the same way; twiddles and the spectral product stay
- *     fp32.  Its measured error against an fp64 evaluation (relative L2 per row, max over rows) is 2.4e-3 at
- *     order 2 on the 8192-sample workload and at most 5.7e-3 at order 3, against 1.7e-3 to 2e-3 for the
- *     fp32 paths with bf16 storage.
+ *     bf16 parts; u_i passes between orders in fp16 the same way; the twiddle and spectral products between
+ *     the matrix products are packed fp16 multiplies.  Its measured error against an fp64 evaluation
+ *     (relative L2 per row, max over rows) is 2.8e-3 at order 2 on the 8192-sample workload and at most
+ *     4.9e-3 at order 3, against 1.7e-3 to 2e-3 for the fp32 paths with bf16 storage.
  *   - Calls are asynchronous on the caller's HIP stream and never synchronise the host, except the
  *     first call on a device, which uploads the library's constant tables (about 790 KB) once with a
  *     blocking copy; hyena_init() does that upload ahead of time (for example before graph capture).
