@@ -115,14 +115,16 @@ __device__ __forceinline__ float range_scale(float m) {
   e = e < -125 ? -125 : (e > 125 ? 125 : e);
   return __builtin_ldexpf(1.0f, -e);
 }
-// largest value of v over the workgroup (4 waves); red: 4 floats of LDS; every thread returns the result.
-// The caller's next barrier must not be this one's: the slots are rewritten only after later barriers.
+// largest value of v over this thread's group of four waves (waves 4g..4g+3); red: one float of LDS per
+// wave of the workgroup; every thread returns its group's result.  The caller's next barrier must not be
+// this one's: the slots are rewritten only after later barriers.
 __device__ __forceinline__ float block_max4(float v, float* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
-  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float* g = red + 4 * (threadIdx.x >> 8);
+  return fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
 }
 
 // output row of accumulator register v for lane half h (32x32 MFMA layout)
@@ -228,24 +230,32 @@ __device__ __forceinline__ float elem_f32(const u32x4& g) {
   return (TT & 1) ? hi_f32(g[TT >> 1]) : lo_f32(g[TT >> 1]);
 }
 
-// Pass 1 / pass 1' column mapping: wave w, lane j (= lane % 32), tile t handle column c = 256 w + 8 j + t
-// (n3 = c % 32, n2 = c / 32), so each lane's 8 tiles cover 8 consecutive samples: one 16-byte access per
-// (row, n1) in global memory.
-template <bool GATE>
-__global__ void __launch_bounds__(mf::T, 2)
+// Workgroups of NP x 4 waves take NP row pairs of one channel (NP = 2 when a channel has an even number of
+// row pairs): each wave's passes 1 and 1' serve its own pair, and in passes 2..2' a wave transforms its
+// slabs for every pair of the workgroup with one set of matrix and spectrum loads.
+// Pass 1 / pass 1' column mapping: wave w (of its pair's four), lane j (= lane % 32), tile t handle column
+// c = 256 w + 8 j + t (n3 = c % 32, n2 = c / 32), so each lane's 8 tiles cover 8 consecutive samples: one
+// 16-byte access per (row, n1) in global memory.
+template <bool GATE, int NP>
+__global__ void __launch_bounds__(mf::T * NP, 2 / NP)
 k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ mats, int B, int D) {
   using namespace mf;
-  __shared__ uint32_t S[PLANE];
-  __shared__ float red[4];
-  const int npair = B >> 1;
-  const int r = xcd_logical_block(blockIdx.x, D * npair);
-  const int d = r / npair, p = r % npair;
+  static_assert(NP == 1 || NP == 2, "one or two row pairs per workgroup");
+  constexpr int NW = 4 * NP;        // waves; wave w owns slabs k1 = w + NW it, it < NIT
+  constexpr int NIT = 16 / NW;
+  __shared__ uint32_t S[NP * PLANE];
+  __shared__ float red[NW];
+  const int ngrp = (B >> 1) / NP;   // workgroups per channel
+  const int r = xcd_logical_block(blockIdx.x, D * ngrp);
+  const int d = r / ngrp;
+  const int mine = (int)(threadIdx.x >> 8);   // this wave's pair (passes 1 and 1')
+  const int p = (r % ngrp) * NP + mine;
   const size_t row0 = (size_t)(2 * p) * D + d, row1 = (size_t)(2 * p + 1) * D + d;
 
   // pass 1 input of the first order: lanes h = 0 / 1 carry row b0 / b1 (real / imaginary input), n1 = e
   u32x4 V[8];
   {
-    const int l = threadIdx.x & 63, c0 = 256 * (threadIdx.x >> 6) + 8 * (l & 31);
+    const int l = threadIdx.x & 63, c0 = 256 * ((threadIdx.x >> 6) & 3) + 8 * (l & 31);
     const __bf16* src = ((l >> 5) == 0 ? u + row0 * L : u + row1 * L) + c0;
 #pragma unroll
     for (int e = 0; e < 8; ++e) V[e] = *reinterpret_cast<const u32x4*>(src + 1024 * e);
@@ -293,9 +303,10 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
   // lane constants derived from an opaque copy of the thread id, so nothing is hoisted across orders
   int tq = threadIdx.x;
   asm volatile("" : "+v"(tq));
-  const int t = tq, w = t >> 6, l = t & 63, j = l & 31, h = l >> 5;
-  const int c0 = 256 * w + 8 * j;
-  const int n2c = 8 * w + (j >> 2), n3c = 8 * (j & 3);   // tile t: n2 = n2c, n3 = n3c + t
+  const int t = tq, w = t >> 6, wq = w & 3, l = t & 63, j = l & 31, h = l >> 5;
+  const int c0 = 256 * wq + 8 * j;
+  const int n2c = 8 * wq + (j >> 2), n3c = 8 * (j & 3);   // tile t: n2 = n2c, n3 = n3c + t
+  uint32_t* const Sm = S + (w >> 2) * PLANE;                // this wave's pair's plane
   const uint32_t* __restrict__ Hc = ch.spectrum[ord] + (size_t)d * PAIR_STRIDE;
   const __bf16* gate = ch.gate[ord];
   // scales back: the inverse matrices' 1/1024, the spectrum's normalisation, the input's scale
@@ -358,14 +369,14 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
       // rows k1 = acc_row(e, h): real part in D1[e], imaginary part in D1[8 + e]
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        S[acc_row(e, h) * SLAB + n2c * ROW + n3c + TT] = pack2h(D1[e] * sc, D1[8 + e] * sc);
+        Sm[acc_row(e, h) * SLAB + n2c * ROW + n3c + TT] = pack2h(D1[e] * sc, D1[8 + e] * sc);
     });
   };
   if (ord == 0) pass1(std::true_type{});
   else pass1(std::false_type{});
   __syncthreads();
 
-  // ---------------- passes 2, 3, 3', 2' per slab k1 (wave w owns k1 = w, w+4, w+8, w+12)
+  // ---------------- passes 2, 3, 3', 2' per slab k1, for each pair of the workgroup
   u32x4 G[2][4];
   auto load_gate = [&]() {
     if (GATE) {
@@ -378,82 +389,99 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
       }
     }
   };
-  auto slab_step = [&](int it) {
-    const int k1 = w + 4 * it;
-    const int k1s = ws + 4 * it;   // the same slab index, in a scalar register
-    uint32_t* sl = S + k1 * SLAB;
-    f16x8 xr_lo, xr_hi, xi_lo, xi_hi;
-    f32x16 dr, di;
+  auto slab_step = [&](auto itc) {
+    constexpr int it = decltype(itc)::value;
+    const int k1 = w + NW * it;
+    const int k1s = ws + NW * it;   // the same slab index, in a scalar register
+    f16x8 xr_lo[NP], xr_hi[NP], xi_lo[NP], xi_hi[NP];
+    f32x16 dr[NP], di[NP];
     // pass 2: data on A (rows n3 = j, K = n2 from LDS: element (n2, n3) at n2 * ROW + n3), matrix on B
     //   -> lane = k2, registers = n3 (row of v)
-    {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const uint32_t* sl = S + q * PLANE + k1 * SLAB;
       uint32_t clo[8], chi[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         clo[e] = sl[(8 * h + e) * ROW + j];
         chi[e] = sl[(16 + 8 * h + e) * ROW + j];
       }
-      split8(clo, xr_lo, xi_lo);
-      split8(chi, xr_hi, xi_hi);
-      dft32<false, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
-      load_mat(k1s, MI3, Ma);
+      split8(clo, xr_lo[q], xi_lo[q]);
+      split8(chi, xr_hi[q], xi_hi[q]);
+      dft32<false, true>(Ma, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q], dr[q], di[q]);
     }
+    load_mat(k1s, MI3, Ma);
     // twiddle W_1024^{n3 k2} (k2 = j, n3 = row of v); pass 3: matrix on A (rows k3, input n3 in accumulator
     // order), data on B -> lane = k2, registers = k3
-    {
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
       f16x2 ar[8], ai[8];
-      to_pairs(dr, ar);
-      to_pairs(di, ai);
-      cmul_pairs<false>(ar, ai, pc, ps, xr_lo, xr_hi, xi_lo, xi_hi);
+      to_pairs(dr[q], ar);
+      to_pairs(di[q], ai);
+      cmul_pairs<false>(ar, ai, pc, ps, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q]);
+      dft32<false, false>(Mb, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q], dr[q], di[q]);
     }
-    dft32<false, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, dr, di);
     load_mat(k1s, MI2, Mb);
     // spectral product: bin k1 + 16 j + 512 k3(v); Hc holds H/N (normalised) in this exact order.
-    // pass 3': data on A (rows k2 = j, input k3 in accumulator order), matrix on B -> lane = n3,
-    // registers = k2
     {
-      f16x2 ar[8], ai[8], hr[8], hi[8];
-      to_pairs(dr, ar);
-      to_pairs(di, ai);
+      f16x2 hr[8], hi[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         hr[q] = __builtin_bit_cast(f16x2, hw[q]);
         hi[q] = __builtin_bit_cast(f16x2, hw[8 + q]);
       }
+      auto product = [&](auto conj) {
+#pragma unroll
+        for (int q = 0; q < NP; ++q) {
+          f16x2 ar[8], ai[8];
+          to_pairs(dr[q], ar);
+          to_pairs(di[q], ai);
+          cmul_pairs<decltype(conj)::value>(ar, ai, hr, hi, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q]);
+        }
+      };
       if (k1s > 8) {   // wave-uniform: mirrored slab, conj(H) with the pair halves swapped
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           hr[q] = hr[q].yx;
           hi[q] = hi[q].yx;
         }
-        cmul_pairs<true>(ar, ai, hr, hi, xr_lo, xr_hi, xi_lo, xi_hi);
+        product(std::true_type{});
       } else {
-        cmul_pairs<false>(ar, ai, hr, hi, xr_lo, xr_hi, xi_lo, xi_hi);
+        product(std::false_type{});
       }
     }
-    if (it < 3) load_spectrum(k1s + 4);
-    f32x16 er, ei;
-    dft32<true, true>(Ma, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
-    if (it < 3) load_mat(k1s + 4, MF2, Ma);
+    if (it + 1 < NIT) load_spectrum(k1s + NW);
+    else if (NP == 2) load_gate();   // (two pairs leave no registers for it before the spectrum is used)
+    // pass 3': data on A (rows k2 = j, input k3 in accumulator order), matrix on B -> lane = n3,
+    // registers = k2
+#pragma unroll
+    for (int q = 0; q < NP; ++q) dft32<true, true>(Ma, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q], dr[q], di[q]);
+    if (it + 1 < NIT) load_mat(k1s + NW, MF2, Ma);
     // conj twiddle W_1024^{n3 k2} (n3 = j, k2 = row of v); pass 2': matrix on A (rows n2, input k2 in
     // accumulator order), data on B -> lane = n3, registers = n2; store (n2, n3) at n2 * ROW + n3
-    {
-      f16x2 ar[8], ai[8];
-      to_pairs(er, ar);
-      to_pairs(ei, ai);
-      cmul_pairs<true>(ar, ai, pc, ps, xr_lo, xr_hi, xi_lo, xi_hi);
-    }
-    dft32<true, false>(Mb, xr_lo, xr_hi, xi_lo, xi_hi, er, ei);
-    if (it < 3) load_mat(k1s + 4, MF3, Mb);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2h(er[v], ei[v]);
+    for (int q = 0; q < NP; ++q) {
+      f16x2 ar[8], ai[8];
+      to_pairs(dr[q], ar);
+      to_pairs(di[q], ai);
+      cmul_pairs<true>(ar, ai, pc, ps, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q]);
+      dft32<true, false>(Mb, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q], dr[q], di[q]);
+    }
+    if (it + 1 < NIT) load_mat(k1s + NW, MF3, Mb);
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      uint32_t* sl = S + q * PLANE + k1 * SLAB;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2h(dr[q][v], di[q][v]);
+    }
   };
   // The gate for pass 1' is issued before the last slab, behind that slab's matrix and spectrum loads
   // (the vector-memory counter retires in order, so no earlier slab waits on it): lane keeps rows
   // b0 / b1 at n1 = 4h + e (e < 4), 8 consecutive samples each.
-  for (int it = 0; it < 3; ++it) slab_step(it);
-  load_gate();
-  slab_step(3);
+  static_for<NIT>([&](auto itc) {
+    if constexpr (decltype(itc)::value == NIT - 1 && NP == 1) load_gate();
+    slab_step(itc);
+  });
 
   __syncthreads();
 
@@ -466,7 +494,7 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
       constexpr int TT = tt.value;
       uint32_t cw[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) cw[e] = S[(8 * h + e) * SLAB + n2c * ROW + n3c + TT];
+      for (int e = 0; e < 8; ++e) cw[e] = Sm[(8 * h + e) * SLAB + n2c * ROW + n3c + TT];
       f16x8 xr, xi;
       split8(cw, xr, xi);
       const f32x16 z = {};
@@ -673,13 +701,14 @@ hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void*
   }
   if (!gated && (order != 1 || gates[0])) return hipErrorInvalidValue;   // only a single order may go ungated
   ch.order = order;
-  const dim3 grid(D * (B / 2)), block(mf::T);
-  if (gated)
-    hipLaunchKernelGGL((k_conv_mfma<true>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch, (const u32x4*)mats,
-                       B, D);
-  else
-    hipLaunchKernelGGL((k_conv_mfma<false>), grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch,
-                       (const u32x4*)mats, B, D);
+  // two row pairs per workgroup when a channel has an even number of them
+  const int np = (B / 2) % 2 == 0 ? 2 : 1;
+  const dim3 grid(D * (B / 2) / np), block(mf::T * np);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, block, 0, s, (const __bf16*)u, (__bf16*)y, ch, (const u32x4*)mats, B, D);
+  };
+  if (gated) np == 2 ? go(k_conv_mfma<true, 2>) : go(k_conv_mfma<true, 1>);
+  else np == 2 ? go(k_conv_mfma<false, 2>) : go(k_conv_mfma<false, 1>);
   return hipGetLastError();
 }
 
