@@ -490,6 +490,8 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
     const bool last = ord + 1 == ch.order;
     float yv[2][4][8];   // [row][e][tile], fp32: the output, or the next order's input
     float vmax = 0.0f;
+    // the tiles, and (when another order follows) the largest |value| for its input scale
+    auto tiles = [&](auto chain) {
     static_for<8>([&](auto tt) {
       constexpr int TT = tt.value;
       uint32_t cw[8];
@@ -510,12 +512,14 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
         }
         yv[0][e][TT] = a;
         yv[1][e][TT] = b;
-        vmax = fmaxf(vmax, fmaxf(fabsf(a), fabsf(b)));
+        if constexpr (decltype(chain)::value) vmax = fmaxf(vmax, fmaxf(fabsf(a), fabsf(b)));
       }
     });
+    };
     __bf16* y0 = y + row0 * L + c0;
     __bf16* y1 = y + row1 * L + c0;
     if (last) {
+      tiles(std::false_type{});
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         u32x4 Y0, Y1;
@@ -528,6 +532,7 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
         *reinterpret_cast<u32x4*>(y1 + 1024 * (4 * h + e)) = Y1;
       }
     } else {
+      tiles(std::true_type{});
       // u_i stays on chip: the next order's input, scaled into fp16's range by its own row-pair maximum
       // (the barrier inside block_max4 also keeps the next pass 1 from writing LDS this pass still reads).
       // Pass 1' left lane (j, h) with rows b0, b1 at n1 = 4h + e; the next pass 1 wants row b_h at
