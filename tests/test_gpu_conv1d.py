@@ -298,6 +298,33 @@ def test_matrix_core_order2_fused_against_oracle(torch_cuda):
     assert e2.max() < BF16_TOL
 
 
+@pytest.mark.parametrize("order,B", [(1, 4), (3, 4), (2, 8), (3, 6)])
+def test_matrix_core_workgroup_forms(torch_cuda, order, B):
+    """The matrix-core kernel takes two row pairs of a channel per workgroup when B / 2 is even (B = 4, 8) and
+    one otherwise (B = 6): every row against the oracle, and each row pair bitwise equal to the same pair run
+    alone (B = 2, one pair per workgroup), which checks the pair / channel mapping and the per-pair scale
+    reductions of the two-pair form."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    w = hi.WORKLOADS[1].with_(B=B, D=12, order=order)
+    v, xs = hi.draw_activations(w, seed=80 + 10 * order + B)
+    params = hi.draw_filter_params(w, seed=80 + 10 * order + B)
+    say(f"matrix-core workgroup forms: order {order} B={B} D=12 L=8192 bf16")
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
+    vd = to_dev(v, torch.bfloat16)
+    xd = [to_dev(x, torch.bfloat16) for x in xs]
+    y = hy.operator(vd, xd, spectra)
+    torch.cuda.synchronize()
+    e = all_row_errors(w, v, xs, params, y.float().cpu().numpy())
+    report_errors(f"order {order} B={B}", e)
+    assert e.max() < BF16_TOL
+    for p in range(B // 2):
+        sl = slice(2 * p, 2 * p + 2)
+        yp = hy.operator(vd[sl], [x[sl] for x in xd], spectra)
+        torch.cuda.synchronize()
+        assert torch.equal(yp, y[sl]), f"row pair {p}"
+
+
 @pytest.mark.parametrize("order", [3, 4, 5, 8])
 @pytest.mark.parametrize("decay", ["none", "slow"])
 def test_high_orders_bf16_L8192_against_oracle(torch_cuda, order, decay):
