@@ -162,14 +162,15 @@ int circular_log2(int64_t L) { return log2i(L) - 1; }
 int engine_log2(int kind, int64_t L) { return kind == K_CIRC1 ? circular_log2(L) : log2i(L); }
 bool multipass1d(int kind, int64_t L) { return !single_pass_supported(engine_log2(kind, L)); }
 
-// Intermediate bytes per (b, d) row / volume for the multi-pass plans (0: single pass).
-size_t row_intermediate_bytes(int kind, int64_t pts) {
+// Intermediate bytes per (b, d) row / volume for the multi-pass plans (0: single pass); the 1-D rows of bf16
+// storage keep their intermediate in block-scaled fp16.
+size_t row_intermediate_bytes(int kind, int64_t pts, int dtype) {
   if (is3d(kind)) return conv3d_volume_bytes(circ3(kind));
-  return multipass1d(kind, pts) ? fourstep_row_bytes(engine_log2(kind, pts)) : 0;
+  return multipass1d(kind, pts) ? fourstep_row_bytes(engine_log2(kind, pts), dtype == HYENA_BF16) : 0;
 }
 size_t filter_intermediate_bytes(int kind, int64_t pts) {
   if (is3d(kind)) return conv3d_filter_volume_bytes(circ3(kind));
-  return multipass1d(kind, pts) ? fourstep_row_bytes(engine_log2(kind, pts)) : 0;
+  return multipass1d(kind, pts) ? fourstep_row_bytes(engine_log2(kind, pts), 0) : 0;
 }
 size_t taps_per_channel(int kind, int64_t pts) { return is3d(kind) ? conv3d_taps_per_channel(circ3(kind)) : (size_t)pts; }
 
@@ -354,7 +355,7 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
   for (int i = 0; i < order; ++i)
     if (overlaps(y, tb, x[i], tb)) return HYENA_EALIAS;
   int chunk = 0;
-  const size_t per = row_intermediate_bytes(kind, pts);
+  const size_t per = row_intermediate_bytes(kind, pts, dtype);
   if (noalloc) {
     if (per > kNoallocScratchBytes) return HYENA_EWORKSPACE;
     DeviceTables* dt = nullptr;
@@ -464,7 +465,7 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   if (st) return st;
   const int kind = kind_of(mode, dims);
   *bytes = 0;
-  const size_t per = row_intermediate_bytes(kind, pts);
+  const size_t per = row_intermediate_bytes(kind, pts, dtype);
   if (per) *bytes = pair_ws_bytes(per, B * D);
   return HYENA_OK;
 }
@@ -572,7 +573,7 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   if (y != u && overlaps(y, tb, u, tb)) return HYENA_EALIAS;
   if (gate && y != gate && overlaps(y, tb, gate, tb)) return HYENA_EALIAS;
   int chunk = 0;
-  const size_t per = row_intermediate_bytes(kind, pts);
+  const size_t per = row_intermediate_bytes(kind, pts, dtype);
   bool two = false;
   if (per) {
     chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &two) : 0;
@@ -656,7 +657,7 @@ int decode_check(int order, int64_t B, int64_t D, int64_t L, int64_t* rows) {
 }
 size_t decode_plane_bytes(int64_t rows, int64_t L) { return (size_t)rows * (size_t)L * sizeof(float); }
 size_t decode_ws_bytes(int64_t rows, int64_t L) {
-  const size_t per = row_intermediate_bytes(K_CAUSAL, L);
+  const size_t per = row_intermediate_bytes(K_CAUSAL, L, HYENA_F32);   // decode convolutions run in fp32
   return per ? (size_t)default_chunk_rows((int64_t)per, rows) * per : 0;
 }
 }  // namespace
@@ -725,7 +726,7 @@ int hyena_decode_step(int order, int64_t B, int64_t D, int64_t L, int64_t block,
     Twiddles tw;
     if ((st = get_twiddles(&tw))) return st;
     const int lg = log2i(L);
-    const size_t per = row_intermediate_bytes(K_CAUSAL, L);
+    const size_t per = row_intermediate_bytes(K_CAUSAL, L, HYENA_F32);   // decode convolutions run in fp32
     const int chunk = per ? (int)default_chunk_rows((int64_t)per, rows) : 0;
     for (int i = 0; i < order; ++i) {
       float* h_i = hist + (size_t)i * plane;
@@ -782,7 +783,7 @@ int hyena_decode_prefill(int order, int64_t B, int64_t D, int64_t L, int64_t blo
   float* fut = hist + (size_t)order * plane;
   const int bf = dtype == HYENA_BF16;
   const int lg = log2i(L);
-  const size_t per = row_intermediate_bytes(K_CAUSAL, L);
+  const size_t per = row_intermediate_bytes(K_CAUSAL, L, HYENA_F32);   // decode convolutions run in fp32
   const int chunk = per ? (int)default_chunk_rows((int64_t)per, rows) : 0;
   // the prompt through the orders on the whole-row FFT path, each order's input kept as its history
   if ((st = hip_status(launch_decode_prefill(0, bf, v, nullptr, hist, nullptr, (int)rows, (int)L, (int)P, stream))))

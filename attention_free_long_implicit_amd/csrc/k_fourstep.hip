@@ -16,11 +16,15 @@
 // row of L = 2M samples fills all M packed values, pass A loads every n1 and pass C keeps every n1,
 // so the same passes compute the L-point circular convolution (the row pass is unchanged).
 //
-// The intermediate is one complex fp32 M-vector per row, for either storage type: with bf16 activations only
-// v, the gates and y are bf16, and u_i stays fp32 from one order to the next (rounding the intermediate or
-// u_i to bf16 compounds across orders into errors beyond what bf16 storage is allowed).  Rows are processed
-// in chunks whose intermediates stay resident in L2 / the memory-side cache.  Rows are visited channel-major
-// (q = d*B + b) so the B rows of a channel read its filter spectrum back to back.
+// The intermediate is one complex M-vector per row.  fp32 storage keeps it in fp32.  With bf16 storage (only v,
+// the gates and y are bf16) it is held in fp16 with block scaling: every block of values written by one
+// workgroup is scaled by a power of two that brings its largest component into [2^14, 2^15) and rounded to
+// fp16 (11-bit significand, half the bytes of fp32), its exponent stored beside the row; the reader scales
+// back in fp32.  Rounding to bf16 instead (8 bits) compounds across passes and orders into errors beyond what
+// bf16 storage is allowed; u_i itself stays fp32 from one order to the next (it lives in LDS between pass C
+// and the next pass A).  Rows are processed in chunks whose intermediates stay resident in L2 / the
+// memory-side cache.  Rows are visited channel-major (q = d*B + b) so the B rows of a channel read its filter
+// spectrum back to back.
 //
 // Spectrum layout per channel: Hs[g][slot][t'] for row-pair group g < M1/2, slot < 2 RP, thread t'
 // of the pair (see k_fs_rows); g = 0 holds rows k1 = 0 and k1 = M1/2.  Hs = H / (4M).
@@ -37,6 +41,44 @@ template <> struct FourStepPlan<17> { using Col = Radices<16, 16>;   using Row =
 template <> struct FourStepPlan<18> { using Col = Radices<16, 16>;   using Row = Radices<16, 8, 8>;  static constexpr int G = 1; };
 template <> struct FourStepPlan<19> { using Col = Radices<8, 8, 8>;  using Row = Radices<16, 8, 8>;  static constexpr int G = 1; };
 template <> struct FourStepPlan<20> { using Col = Radices<8, 8, 8>;  using Row = Radices<16, 16, 8>; static constexpr int G = 1; };
+
+// Block-scaled fp16 intermediate: a row's region of M + 1024 32-bit words holds the M values as fp16 pairs
+// (real low, imaginary high) in [0, M), the exponents of pass A's column tiles (M / 8192 <= 128 of them) from
+// word M + EA, and the exponents of pass B's workgroups, one per bin-row position (M1 <= 512), from M + EB.
+struct H16Row {
+  static constexpr int EA = 0, EB = 128;   // offsets from word M
+  static constexpr int EXTRA = 1024;       // words after the values
+};
+// e such that m * 2^-e has its largest component in [2^14, 2^15); 0 for a zero or non-finite m (which then
+// passes through unscaled).  e >= -112 keeps 2^-e finite.
+__device__ __forceinline__ int h16_exponent(float m) {
+  if (!(m > 0.0f) || !(m <= 3.0e38f)) return 0;
+  const int e = __builtin_amdgcn_frexp_expf(m) - 15;
+  return e < -112 ? -112 : e;
+}
+__device__ __forceinline__ uint32_t h16_pack(float2 v, float s) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 r = {(_Float16)(v.x * s), (_Float16)(v.y * s)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ float2 h16_unpack(uint32_t w, float s) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  const h2 r = __builtin_bit_cast(h2, w);
+  return make_float2((float)r.x * s, (float)r.y * s);
+}
+// largest value of v over the NT threads of the workgroup (red: NT / 64 floats of LDS); every thread returns it.
+// The caller's next barrier must not be this one's.
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float m = red[0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k) m = fmaxf(m, red[k]);
+  return m;
+}
 
 template <int LOG2M>
 struct FS {
@@ -83,7 +125,11 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   const int d = q / B, b = q % B;
   const size_t row = (size_t)b * D + d;
   const int c0 = tile * C;
+  constexpr bool H16 = BF16;
   float2* Irow = I + (size_t)ql * M;
+  // the fp16 form (bf16 storage): rows of M + EXTRA words
+  uint32_t* const Wrow = reinterpret_cast<uint32_t*>(I) + (size_t)ql * (M + H16Row::EXTRA);
+  static_assert(!H16 || M / 8192 <= 128, "tile exponents");
   auto tile_addr = [&](int p, int c) { return F::Col::addr(p, c); };
 
   if constexpr (MODE == 0) {
@@ -96,11 +142,22 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
     });
     __syncthreads();
   } else {
-    static_for<PER_T>([&](auto ii) {
-      const int e = t + TC * ii.value;
-      const int p = e / C, c = e % C;
-      lds[tile_addr(p, c)] = Irow[(size_t)p * M2 + c0 + c];
-    });
+    if constexpr (H16) {
+      __shared__ float rsc[M1];   // 2^e of pass B's block that wrote bin-row position p
+      for (int p = t; p < M1; p += TC) rsc[p] = __builtin_ldexpf(1.0f, (int)Wrow[M + H16Row::EB + p]);
+      __syncthreads();
+      static_for<PER_T>([&](auto ii) {
+        const int e = t + TC * ii.value;
+        const int p = e / C, c = e % C;
+        lds[tile_addr(p, c)] = h16_unpack(Wrow[(size_t)p * M2 + c0 + c], rsc[p]);
+      });
+    } else {
+      static_for<PER_T>([&](auto ii) {
+        const int e = t + TC * ii.value;
+        const int p = e / C, c = e % C;
+        lds[tile_addr(p, c)] = Irow[(size_t)p * M2 + c0 + c];
+      });
+    }
     __syncthreads();
     F::Col::template inverse<!FULL>(lds, tw, t);
     // gate the causal half (positions n1 < M1/2 are z'[n2 + M2 n1]), or every position (FULL)
@@ -125,11 +182,31 @@ k_fs_cols(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
     __syncthreads();
   }
   F::Col::template forward<!FULL>(lds, tw, t);
-  static_for<PER_T>([&](auto ii) {
-    const int e = t + TC * ii.value;
-    const int p = e / C, c = e % C;
-    Irow[(size_t)p * M2 + c0 + c] = lds[tile_addr(p, c)];
-  });
+  if constexpr (H16) {
+    // the tile's values, their largest component over the workgroup, then the scaled fp16 store
+    __shared__ float red[TC / 64];
+    float2 vals[PER_T];
+    float m = 0.0f;
+    static_for<PER_T>([&](auto ii) {
+      const int e = t + TC * ii.value;
+      vals[ii.value] = lds[tile_addr(e / C, e % C)];
+      m = fmaxf(m, fmaxf(fabsf(vals[ii.value].x), fabsf(vals[ii.value].y)));
+    });
+    const int ex = h16_exponent(block_max<TC>(m, red));
+    const float sc = __builtin_ldexpf(1.0f, -ex);
+    static_for<PER_T>([&](auto ii) {
+      const int e = t + TC * ii.value;
+      const int p = e / C, c = e % C;
+      Wrow[(size_t)p * M2 + c0 + c] = h16_pack(vals[ii.value], sc);
+    });
+    if (t == 0) Wrow[M + H16Row::EA + tile] = (uint32_t)ex;
+  } else {
+    static_for<PER_T>([&](auto ii) {
+      const int e = t + TC * ii.value;
+      const int p = e / C, c = e % C;
+      Irow[(size_t)p * M2 + c0 + c] = lds[tile_addr(p, c)];
+    });
+  }
 }
 
 // Spectrum pass A: fp32 taps h[d, 0:M) zero-padded, or h[d, 0:2M) (FULL; one "row" per channel, B = 1).
@@ -168,7 +245,8 @@ k_fs_cols_taps(const float* h, float2* I, int q0, int nq, Twiddles tw) {
 // beta_A = t' of the first row and beta_B = NBLK-1-t' of the second (their bins mirror each other:
 // k <-> M-k pairs k1 with M1-k1 and complements every k2 digit); the g_glob = 0 pair instead uses
 // whole-row negation pairing on row 0 (threads < TP/2) and in-row complement pairing on row M1/2.
-template <int LOG2M, int MODE>
+// H16: the intermediate is block-scaled fp16 (bf16 storage, MODE 0 only).
+template <int LOG2M, int MODE, bool H16>
 __global__ void __launch_bounds__(FS<LOG2M>::TR)
 k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out, int q0, int nq, int B, int hsb,
           Twiddles tw) {
@@ -185,6 +263,14 @@ k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out,
   // spectrum channel: d (one filter per channel, hsb = 0) or b * D + d (one per (b, d), hsb = D)
   const int d = (MODE == 0) ? q / B + (q % B) * hsb : q;
   float2* Irow = I + (size_t)ql * M;
+  uint32_t* const Wrow = reinterpret_cast<uint32_t*>(I) + (size_t)ql * (M + H16Row::EXTRA);
+  static_assert(!H16 || MODE == 0, "fp16 intermediate in the convolution only");
+  constexpr int NTILE = M / 8192, TCOL = M2 / NTILE;   // pass A's column tiles: TCOL columns each
+  __shared__ float tsc[H16 ? NTILE : 1];               // 2^e of pass A's tiles
+  if constexpr (H16) {
+    for (int k = t; k < NTILE; k += TR) tsc[k] = __builtin_ldexpf(1.0f, (int)Wrow[M + H16Row::EA + k]);
+    __syncthreads();
+  }
 
   // bin row k1 of sub-row s (s = 2j: first of pair j, 2j+1: second)
   auto k1_of = [&](int s) {
@@ -200,12 +286,13 @@ k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out,
     int s, n;
     Row::first_input(t, i, s, n);
     const int k1 = k1_of(s);
-    const float2* src = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
+    const size_t roff = (size_t)F::ColRL::position_of_bin(k1) * M2;
     // W_M^{(n + m PER0) k1} for m = 0..R0-1 as a running product from W_M^{n k1} by W_M^{PER0 k1}
     const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
     float2 w = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     static_for<R0>([&](auto m) {
-      const float2 v = src[n + m.value * PER0];
+      const int col = n + m.value * PER0;
+      const float2 v = H16 ? h16_unpack(Wrow[roff + col], tsc[col / TCOL]) : Irow[roff + col];
       x[i * R0 + m.value] = cmul(v, w);
       if constexpr (m.value + 1 < R0) w = cmul(w, ws);
     });
@@ -254,17 +341,31 @@ k_fs_rows(float2* I, const float2* __restrict__ Hs, float2* __restrict__ Hs_out,
 
   Row::inv_last(x, lds, bA, bB);
   Row::template inverse_from_last<false>(x, lds, tw, t);
+  // fp16 form: one power of two for the workgroup's rows (the twiddle below keeps magnitudes), recorded at
+  // each of its bin-row positions
+  float sc = 1.0f;
+  if constexpr (H16) {
+    __shared__ float red[TR / 64 > 0 ? TR / 64 : 1];
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < E; ++k) m = fmaxf(m, fmaxf(fabsf(x[k].x), fabsf(x[k].y)));
+    const int ex = h16_exponent(block_max<TR>(m, red));
+    sc = __builtin_ldexpf(1.0f, -ex);
+    if (t < 2 * G) Wrow[M + H16Row::EB + F::ColRL::position_of_bin(k1_of(t))] = (uint32_t)ex;
+  }
   // conjugate twiddle and store back
   static_for<E / R0>([&](auto ii) {
     constexpr int i = ii.value;
     int s, n;
     Row::first_input(t, i, s, n);
     const int k1 = k1_of(s);
-    float2* dst = Irow + (size_t)F::ColRL::position_of_bin(k1) * M2;
+    const size_t roff = (size_t)F::ColRL::position_of_bin(k1) * M2;
     const float2 ws = twiddle<LOG2M>(tw, uint32_t(PER0) * uint32_t(k1));
     float2 w = twiddle<LOG2M>(tw, uint32_t(n) * uint32_t(k1));
     static_for<R0>([&](auto m) {
-      dst[n + m.value * PER0] = cmulc(x[i * R0 + m.value], w);
+      const float2 r = cmulc(x[i * R0 + m.value], w);
+      if constexpr (H16) Wrow[roff + n + m.value * PER0] = h16_pack(r, sc);
+      else Irow[roff + n + m.value * PER0] = r;
       if constexpr (m.value + 1 < R0) w = cmul(w, ws);
     });
   });
@@ -336,11 +437,12 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
   for (int q0 = 0; q0 < rows; q0 += chunk, ++k) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
     const hipStream_t s = (two && (k & 1)) ? side->s : s0;
-    float2* I = I0 + (two && (k & 1) ? (size_t)chunk * F::M : 0);
+    // rows of M float2 (fp32 intermediate) or of M + EXTRA words (fp16, bf16 storage)
+    float2* I = I0 + (two && (k & 1) ? (size_t)chunk * (BF16 ? (F::M + H16Row::EXTRA) / 2 : F::M) : 0);
     hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
                        (const E*)v, (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
-      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0>), dim3(groups * nq), dim3(F::TR), 0, s, I,
+      hipLaunchKernelGGL((k_fs_rows<LOG2M, 0, BF16>), dim3(groups * nq), dim3(F::TR), 0, s, I,
                          (const float2*)spectra[i], (float2*)nullptr, q0, nq, B, hsb, tw);
       if (i + 1 < order)
         hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 1, true, true, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
@@ -372,7 +474,7 @@ hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int 
   for (int q0 = 0; q0 < D; q0 += chunk) {
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
     hipLaunchKernelGGL((k_fs_cols_taps<LOG2M, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s, h, I, q0, nq, tw);
-    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const float2*)nullptr,
+    hipLaunchKernelGGL((k_fs_rows<LOG2M, 1, false>), dim3(groups * nq), dim3(F::TR), 0, s, I, (const float2*)nullptr,
                        Hs, q0, nq, 1, 0, tw);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -384,7 +486,9 @@ hipError_t fs_spectrum_launch(const float* h, float2* Hs, int D, float2* I, int 
 
 bool fourstep_supported(int log2L) { return log2L >= 15 && log2L <= 20; }
 
-size_t fourstep_row_bytes(int log2L) { return (size_t)1 << log2L << 3; }
+size_t fourstep_row_bytes(int log2L, int bf16) {
+  return bf16 ? (((size_t)1 << log2L) + H16Row::EXTRA) * 4 : (size_t)1 << log2L << 3;
+}
 
 #define HYENA_FS_CASES(X) X(15) X(16) X(17) X(18) X(19) X(20)
 

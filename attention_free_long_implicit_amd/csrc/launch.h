@@ -35,8 +35,9 @@ hipError_t launch_export1d_single(int log2L, const float2* Hs, float2* H, int D,
 // `chunk` rows of M complex values.  full = 0: causal, rows of M samples; full = 1: periodic, rows of
 // 2M samples.  x[i] may be NULL for the last order only (no gate).
 bool fourstep_supported(int log2L);
-size_t fourstep_row_bytes(int log2L);
-// The intermediate I is fp32 for either storage type; u_i stays fp32 between orders.
+// Workspace bytes per row: the fp32 intermediate (M complex fp32), or with bf16 storage its block-scaled fp16
+// form (M fp16 pairs and 1024 words of block exponents).  u_i stays fp32 between orders either way.
+size_t fourstep_row_bytes(int log2L, int bf16);
 // side (optional): a second stream and two events; the chunks then alternate between the caller's stream and
 // that one (forked from and joined back into the caller's stream), each stream with its own half of I, which
 // must hold 2 * chunk rows.

@@ -24,8 +24,10 @@
  *   - Tensor pointers are DEVICE pointers owned by the caller; the library never frees them.
  *   - Activations are channel-major and contiguous: [B, D, L] (1-D) or [B, D, nx, ny, nz] (3-D),
  *     element type given by hyena_dtype.  bf16 is a storage type only: v, the gates and y are bf16 (stores
- *     round to nearest even); the intermediates u_i of the recurrence and every transform intermediate
- *     stay fp32.
+ *     round to nearest even); the intermediates u_i of the recurrence stay fp32, and so does every transform
+ *     intermediate except two: the matrix-core path's operands (below) and, with bf16 storage, the
+ *     multi-pass 1-D plans' workspace, held as fp16 with a power-of-two scale per block of values (each
+ *     block's largest component in [2^14, 2^15); 1.7e-3 -> 2.6e-3 on the order-3, 65536-sample workload).
  *   - Arithmetic: fp32 on every path (radix butterflies on the vector units, fp32 twiddles, fp32 spectra and
  *     spectral products), with one exception, the matrix-core path of hyena_fftconv / hyena_operator (bf16
  *     storage, causal L = 8192, even B, order <= 3): its DFT steps are matrix products with fp32
@@ -37,7 +39,7 @@
  *     (relative L2 per row, max over rows) is 2.8e-3 at order 2 on the 8192-sample workload and at most
  *     4.9e-3 at order 3, against 1.7e-3 to 2e-3 for the fp32 paths with bf16 storage.
  *   - Calls are asynchronous on the caller's HIP stream and never synchronise the host, except the
- *     first call on a device, which uploads the library's constant tables (about 790 KB) once with a
+ *     first call on a device, which uploads the library's constant tables (about 800 KB) once with a
  *     blocking copy; hyena_init() does that upload ahead of time (for example before graph capture).
  *   - The library holds no state across calls besides those immutable tables, which live in device arrays
  *     of the library's code object (the library never calls hipMalloc).
@@ -154,7 +156,7 @@ int hyena_film_filter_gen(const hyena_film_params *p, int64_t B, int32_t R, cons
 /* One long convolution with optional gate: y = gate * (h conv u), or y = h conv u when gate == NULL.
  * u, gate, y: [B, D, points] of dtype.  spectrum: from hyena_filter_gen for the same dims and D.
  * bf16 storage with causal L = 8192, even B and 16-byte-aligned u, gate and y runs on the matrix cores
- * (rows b and b+1 of a channel transformed together; bf16 operands, see the conventions above); every
+ * (rows b and b+1 of a channel transformed together; fp16 operands, see the conventions above); every
  * other case runs the fp32 transform engine.
  * y may equal u or gate exactly (in place); any other overlap returns HYENA_EALIAS. */
 int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *u,
@@ -169,7 +171,7 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
  * kept on chip (as fp16 operands, see the conventions above).  Every other single-pass case (causal
  * L <= 16384, periodic L <= 32768) runs up to 8 orders per launch of the fp32 engine with u_i kept on chip in
  * fp32 (beyond 8 orders u passes through y, in the storage type, between launches); the multi-pass plans
- * (longer rows, 3-D) chain the orders through the fp32 workspace.  Orders above 3 never take the matrix
+ * (longer rows, 3-D) chain the orders through the workspace (u_i itself fp32).  Orders above 3 never take the matrix
  * cores: their 16-bit operands compound across orders towards the bf16 tolerance. */
 int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *v,
                    const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,

@@ -51,9 +51,12 @@ def test_size_queries(lib):
     assert st == 0 and n == 16 * 1024 * 4
     st, n = _size(lib.hyena_workspace_bytes, 2, 4, 768, L.dims_of([8192]), L.BF16, L.CAUSAL)
     assert st == 0 and n == 0
-    # multi-pass lengths need a workspace of whole rows of L complex fp32 values
+    # multi-pass lengths need a workspace of whole rows: L complex fp32 values, or with bf16 storage L fp16
+    # pairs and 1024 words of block exponents
     st, n = _size(lib.hyena_workspace_bytes, 3, 2, 1024, L.dims_of([65536]), L.BF16, L.CAUSAL)
-    assert st == 0 and n > 0 and n % (65536 * 8) == 0
+    assert st == 0 and n > 0 and n % (65536 * 4 + 4096) == 0
+    st, n = _size(lib.hyena_workspace_bytes, 1, 1, 3, L.dims_of([65536]), L.BF16, L.CAUSAL)
+    assert st == 0 and n == 3 * (65536 * 4 + 4096)
     st, n = _size(lib.hyena_workspace_bytes, 2, 1, 3, L.dims_of([1 << 20]), L.F32, L.CAUSAL)
     assert st == 0 and n == 3 * (1 << 20) * 8          # never more rows than there are
     # 3-D: spectrum 128 x 128 x 65 bins per channel; intermediate 64 x 128 x 65 per volume
