@@ -125,7 +125,7 @@ def test_operator_f32_B1_D256_L1M_dna_all_rows(torch_cuda):
 
 @pytest.mark.parametrize("L", [1 << 15, 1 << 16, 1 << 17, 1 << 20])
 def test_fourstep_fftconv_bf16_chunked(torch_cuda, L):
-    """bf16 storage (the intermediate is bf16 too), two chunks of which one is ragged, every
+    """bf16 storage (the intermediate is block-scaled fp16), two chunks of which one is ragged, every
     multi-pass plan family; against the oracle on the bf16-rounded inputs."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
@@ -162,3 +162,42 @@ def test_fourstep_zero_input_gives_exact_zero(torch_cuda, dtype):
     y = hy.operator(v, xs, spectra)
     torch.cuda.synchronize()
     assert torch.count_nonzero(y).item() == 0
+
+
+@pytest.mark.parametrize("L", [1 << 16, 1 << 20])
+def test_fourstep_bf16_block_scales_per_row(torch_cuda, L):
+    """The bf16-storage plans keep their intermediate in fp16 with one power-of-two scale per block, and every
+    block belongs to one (b, d) row: rows whose magnitudes differ by 2^100 (a single impulse among them, the
+    widest spread within a row) each stay within the bf16 tolerance of the oracle, and a NaN row leaves the
+    others bitwise unchanged."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    B, D = 1, 6
+    w = hi.WORKLOADS[2].with_(B=B, D=D, dims=(L,), order=2)
+    rng = np.random.default_rng(L % 997)
+    v = rng.standard_normal((B, D, L)).astype(np.float32)
+    v[0, 0] *= 2.0 ** -60
+    v[0, 1] *= 2.0 ** -20
+    v[0, 3] *= 2.0 ** 40
+    v[0, 4] = 0.0
+    v[0, 4, L // 3] = 3.0
+    xs = [rng.standard_normal((B, D, L)).astype(np.float32) for _ in range(2)]
+    params = hi.draw_filter_params(w, seed=11)
+    say(f"four-step bf16 block scales, rows 2^-60 .. 2^40 and an impulse, L={L}")
+    spectra = [hy.filter_gen(params_to_dev(q), (L,)) for q in params]
+    vd = torch.from_numpy(v).to(torch.bfloat16).cuda()
+    xd = [torch.from_numpy(x).to(torch.bfloat16).cuda() for x in xs]
+    y = hy.operator(vd, xd, spectra)
+    torch.cuda.synchronize()
+    vr = vd.float().cpu().numpy()
+    xr = [x.float().cpu().numpy() for x in xd]
+    e = all_row_errors(w, vr, xr, params, y.float().cpu().numpy())
+    report_errors("block scales", e)
+    assert e.max() < BF16_TOL
+    vn = vd.clone()
+    vn[0, 2, L // 2] = float("nan")
+    yn = hy.operator(vn, xd, spectra)
+    torch.cuda.synchronize()
+    assert torch.isnan(yn[0, 2]).any()
+    keep = [0, 1, 3, 4, 5]
+    assert torch.equal(yn[0, keep], y[0, keep])
