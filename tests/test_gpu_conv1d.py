@@ -298,6 +298,34 @@ def test_matrix_core_order2_fused_against_oracle(torch_cuda):
     assert e2.max() < BF16_TOL
 
 
+@pytest.mark.parametrize("B", [2, 4])
+@pytest.mark.parametrize("gate", [False, True])
+def test_matrix_core_fftconv(torch_cuda, B, gate):
+    """hyena_fftconv on the matrix cores (bf16, L = 8192), with and without a gate, in both workgroup forms
+    (B = 2: one row pair per workgroup; B = 4: two): every row against the oracle's gated causal
+    convolution of the bf16-rounded inputs."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L, D = 8192, 10
+    w = hi.WORKLOADS[1].with_(B=B, D=D, order=1)
+    rng = np.random.default_rng(90 + B + 2 * gate)
+    u = torch.from_numpy(rng.standard_normal((B, D, L)).astype(np.float32)).to(torch.bfloat16)
+    g = torch.from_numpy(rng.standard_normal((B, D, L)).astype(np.float32)).to(torch.bfloat16)
+    p = hi.draw_filter_params(w, seed=13)[0]
+    say(f"matrix-core fftconv B={B} gate={gate}")
+    spec = hy.filter_gen(params_to_dev(p), (L,))
+    y = hy.fftconv(u.cuda(), spec, gate=g.cuda() if gate else None)
+    torch.cuda.synchronize()
+    h = orc.implicit_filter_1d(p, L)
+    un = u.float().numpy().astype(np.float64).reshape(-1, L)
+    ref = orc.causal_conv_fft(un, np.tile(h, (B, 1)))
+    if gate:
+        ref = ref * g.float().numpy().astype(np.float64).reshape(-1, L)
+    e = rel_err_rows(y.float().cpu().numpy().reshape(-1, L), ref)
+    say(f"  max rel err {e.max():.3e}")
+    assert e.max() < BF16_TOL
+
+
 @pytest.mark.parametrize("order,B", [(1, 4), (3, 4), (2, 8), (3, 6)])
 def test_matrix_core_workgroup_forms(torch_cuda, order, B):
     """The matrix-core kernel takes two row pairs of a channel per workgroup when B / 2 is even (B = 4, 8) and
