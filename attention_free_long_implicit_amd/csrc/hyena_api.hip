@@ -23,12 +23,17 @@ static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 namespace {
 
 constexpr int kMaxDevices = 64;
+// Multi-pass plans: chunks of about kChunkMB of intermediate cycle over kChunkWays streams (the caller's and
+// kChunkWays - 1 side streams); see pair_chunk_rows.
+constexpr int kChunkWays = 2;      // streams the chunks cycle over (the caller's and kChunkWays - 1 side streams)
+constexpr int kChunkMB = 64;
+static_assert(kChunkWays >= 2 && kChunkWays <= kSideStreams + 1, "side streams");
 std::mutex g_mu;
 struct DeviceTables {
   Twiddles tw;
   const void* mats;       // DFT matrices of the matrix-core path (bf16, per lane)
   void* scratch;          // this device's copy of `scratch`
-  SideStream side;        // the long-row plans' second stream (default priority) and its fork / join events
+  SideStream side;        // the long-row plans' side streams (default priority) and their fork / join events
   bool ready;
 };
 // Held while a long-row plan forks onto a device's side stream, so that concurrent calls do not interleave
@@ -68,10 +73,12 @@ int init_current_device(DeviceTables** out) {
       return HYENA_EHIP;
     t.tw.pow2 = (const float2*)tw;
     t.tw.fine = (const float2*)tw + kTwPow2Entries;
-    if (hipStreamCreateWithFlags(&t.side.s, hipStreamNonBlocking) != hipSuccess) return HYENA_EHIP;
-    if (hipEventCreateWithFlags(&t.side.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&t.side.join, hipEventDisableTiming) != hipSuccess)
-      return HYENA_EHIP;
+    for (int j = 0; j < kSideStreams; ++j)
+      if (hipStreamCreateWithFlags(&t.side.s[j], hipStreamNonBlocking) != hipSuccess ||
+          hipEventCreateWithFlags(&t.side.join[j], hipEventDisableTiming) != hipSuccess)
+        return HYENA_EHIP;
+    if (hipEventCreateWithFlags(&t.side.fork, hipEventDisableTiming) != hipSuccess) return HYENA_EHIP;
+    t.side.ways = kChunkWays;
     t.mats = mats;
     t.scratch = scr;
     t.ready = true;
@@ -192,30 +199,33 @@ int64_t default_chunk_rows(int64_t per, int64_t rows) {
 // 4.93 and 4.91 ms per step at L = 2^20, fp32, 256 rows, against 5.37 ms for one stream of 160 MB chunks;
 // 3-D 64^3 zero-padded, 128 volumes: 16, 32, 64, 128 MB 2.11, 1.63, 1.62, 1.77 ms against 1.79 ms for one
 // chunk).  A whole batch of at most 192 MB of intermediate runs as one chunk on one stream (periodic 64^3,
-// 138 MB: 0.41 ms, against 0.43 ms in 64 MB pairs).  The workspace holds two chunks.
+// 138 MB: 0.41 ms, against 0.43 ms in 64 MB pairs).  Three streams measured slower (64 / 44 MB chunks: 5.28 /
+// 4.96 ms at L = 2^20 against 4.83, 2.95 / 2.90 ms against 2.85 for the order-3 L = 65536 bf16 workload,
+// 1.70 / 1.63 ms against 1.61 for 3-D).  The workspace holds kChunkWays chunks.
 int64_t pair_chunk_rows(int64_t per, int64_t rows) {
   if ((size_t)rows * (size_t)per <= ((size_t)192 << 20)) return rows;
-  int64_t c = ((int64_t)64 << 20) / per;
+  int64_t c = ((int64_t)kChunkMB << 20) / per;
   if (c < 1) c = 1;
   return c < rows ? c : rows;
 }
 size_t pair_ws_bytes(size_t per, int64_t rows) {
   const int64_t c = pair_chunk_rows((int64_t)per, rows);
-  return (size_t)(rows > c ? 2 : 1) * (size_t)c * per;
+  return (size_t)(rows > c ? kChunkWays : 1) * (size_t)c * per;
 }
-// Chunk rows of a multi-pass plan within a workspace of ws_bytes, and whether it alternates two streams
+// Chunk rows of a multi-pass plan within a workspace of ws_bytes, and how many streams its chunks cycle over
 // (0: the workspace does not hold one row).
-int pair_chunk(size_t per, int64_t rows, size_t ws_bytes, bool* two) {
+int pair_chunk(size_t per, int64_t rows, size_t ws_bytes, int* ways) {
   const int64_t cap = (int64_t)(ws_bytes / per);
-  *two = false;
+  *ways = 1;
   if (cap < 1) return 0;
   if (cap >= rows && pair_chunk_rows((int64_t)per, rows) >= rows) return (int)rows;   // one chunk
   int64_t c = cap;
   if (cap >= 2 && rows > 1) {
-    c = cap / 2;
+    const int w = cap >= kChunkWays ? kChunkWays : (int)cap;
+    c = cap / w;
     const int64_t want = pair_chunk_rows((int64_t)per, rows);
     if (c > want) c = want;
-    *two = rows > c;
+    if (rows > c) *ways = w;
   }
   return (int)(c < rows ? c : rows);
 }
@@ -363,9 +373,9 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
     ws = dt->scratch;
     ws_bytes = kNoallocScratchBytes;
   }
-  bool two = false;
+  int ways = 1;
   if (per) {
-    chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &two) : 0;
+    chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
     for (int i = 0; i < order; ++i)
@@ -375,15 +385,20 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
   if ((st = get_twiddles(&tw))) return st;
   if (chunk) {
     DeviceTables* dt = nullptr;
-    if (two && (st = init_current_device(&dt))) return st;
+    if (ways > 1 && (st = init_current_device(&dt))) return st;
     std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
-    if (two) lk.lock();
+    SideStream sd{};
+    if (ways > 1) {
+      lk.lock();
+      sd = dt->side;
+      sd.ways = ways;
+    }
     if (is3d(kind))
       return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws,
-                                      chunk, tw, stream, circ3(kind), hsb, two ? &dt->side : nullptr));
+                                      chunk, tw, stream, circ3(kind), hsb, ways > 1 ? &sd : nullptr));
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
                                              spectra, y, (float2*)ws, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0, hsb,
-                                             two ? &dt->side : nullptr));
+                                             ways > 1 ? &sd : nullptr));
   }
   if (kind == K_CAUSAL && !hsb && order <= kMfmaMaxOrder && use_mfma(dtype, B, pts)) {
     bool aligned = aligned16(v) && aligned16(y);
@@ -574,9 +589,9 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   if (gate && y != gate && overlaps(y, tb, gate, tb)) return HYENA_EALIAS;
   int chunk = 0;
   const size_t per = row_intermediate_bytes(kind, pts, dtype);
-  bool two = false;
+  int ways = 1;
   if (per) {
-    chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &two) : 0;
+    chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, u, tb) || (gate && overlaps(ws, ws_bytes, gate, tb)))
       return HYENA_EALIAS;
@@ -587,15 +602,20 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
     const void* xs[1] = {gate};
     const void* sp[1] = {spectrum};
     DeviceTables* dt = nullptr;
-    if (two && (st = init_current_device(&dt))) return st;
+    if (ways > 1 && (st = init_current_device(&dt))) return st;
     std::unique_lock<std::mutex> lk(g_side_mu, std::defer_lock);
-    if (two) lk.lock();
+    SideStream sd{};
+    if (ways > 1) {
+      lk.lock();
+      sd = dt->side;
+      sd.ways = ways;
+    }
     if (is3d(kind))
       return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
-                                      stream, circ3(kind), hsb, two ? &dt->side : nullptr));
+                                      stream, circ3(kind), hsb, ways > 1 ? &sd : nullptr));
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs,
                                              sp, y, (float2*)ws, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0, hsb,
-                                             two ? &dt->side : nullptr));
+                                             ways > 1 ? &sd : nullptr));
   }
   if (kind == K_CIRC1)
     return hip_status(launch_conv1d_single(circular_log2(pts), dtype == HYENA_BF16, u, gate, y,

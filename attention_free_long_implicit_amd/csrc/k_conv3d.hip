@@ -326,17 +326,17 @@ hipError_t conv3d_launch_t(int order, int B, int D, const void* v, const void* c
   constexpr int N = C::N, T = C::T, TILES = C::TILES;
   using E = typename Store<BF16>::elem;
   const int rows = B * D;
-  const bool two = side != nullptr && rows > chunk;
-  if (two) {
-    hipError_t e = hipEventRecord(side->fork, s0);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+  const int ways = (side != nullptr && rows > chunk) ? side->ways : 1;
+  if (ways > 1) {
+    const hipError_t e = side_fork(side, s0);
     if (e != hipSuccess) return e;
   }
   int k = 0;
   for (int q0 = 0; q0 < rows; q0 += chunk, ++k) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
-    const hipStream_t s = (two && (k & 1)) ? side->s : s0;
-    float2* I = I0 + (two && (k & 1) ? (size_t)chunk * (conv3d_volume_bytes(G::PAD ? 0 : 1) / sizeof(float2)) : 0);
+    const int j = k % ways;
+    const hipStream_t s = j ? side->s[j - 1] : s0;
+    float2* I = I0 + (size_t)j * chunk * (conv3d_volume_bytes(G::PAD ? 0 : 1) / sizeof(float2));
     hipLaunchKernelGGL((k3_planes<G, BF16, 0, false, false>), dim3(N * nq), dim3(T), 0, s, (const E*)v,
                        (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
@@ -355,12 +355,7 @@ hipError_t conv3d_launch_t(int order, int B, int D, const void* v, const void* c
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (two) {
-    hipError_t e = hipEventRecord(side->join, side->s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s0, side->join, 0);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return ways > 1 ? side_join(side, s0) : hipSuccess;
 }
 
 template <class G>

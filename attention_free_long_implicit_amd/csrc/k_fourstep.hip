@@ -415,9 +415,9 @@ template <int LOG2M>
 size_t fs_row_bytes() { return (size_t)(1 << LOG2M) * sizeof(float2); }
 
 // Chunks of rows run every pass of every order before the next chunk starts, so a chunk's intermediate is
-// reread while the memory-side cache may still hold it; with a side stream two chunks run at once, which keeps
-// the compute units busy while each chunk stays small (64 MB of intermediate measured best at L = 2^20:
-// 4.77 ms per step against 5.37 ms for one stream of 160 MB chunks).
+// reread while the memory-side cache may still hold it; with side streams several chunks run at once, which
+// keeps the compute units busy while each chunk stays small (two streams of 64 MB of intermediate measured
+// best at L = 2^20: 4.77 ms per step against 5.37 ms for one stream of 160 MB chunks).
 template <int LOG2M, bool BF16, bool FULL>
 hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* const* x, const void* const* spectra,
                           void* y, float2* I0, int chunk, const Twiddles& tw, hipStream_t s0, int hsb,
@@ -427,18 +427,18 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
   const int rows = B * D;
   const int tiles = F::M2 / F::C;
   const int groups = (F::M1 / 2) / F::G;
-  const bool two = side != nullptr && rows > chunk;
-  if (two) {
-    hipError_t e = hipEventRecord(side->fork, s0);
-    if (e == hipSuccess) e = hipStreamWaitEvent(side->s, side->fork, 0);
+  const int ways = (side != nullptr && rows > chunk) ? side->ways : 1;
+  if (ways > 1) {
+    const hipError_t e = side_fork(side, s0);
     if (e != hipSuccess) return e;
   }
   int k = 0;
   for (int q0 = 0; q0 < rows; q0 += chunk, ++k) {
     const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
-    const hipStream_t s = (two && (k & 1)) ? side->s : s0;
+    const int j = k % ways;
+    const hipStream_t s = j ? side->s[j - 1] : s0;
     // rows of M float2 (fp32 intermediate) or of M + EXTRA words (fp16, bf16 storage)
-    float2* I = I0 + (two && (k & 1) ? (size_t)chunk * (BF16 ? (F::M + H16Row::EXTRA) / 2 : F::M) : 0);
+    float2* I = I0 + (size_t)j * chunk * (BF16 ? (F::M + H16Row::EXTRA) / 2 : F::M);
     hipLaunchKernelGGL((k_fs_cols<LOG2M, BF16, 0, false, false, FULL>), dim3(tiles * nq), dim3(F::TC), 0, s,
                        (const E*)v, (const E*)nullptr, (E*)nullptr, I, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
@@ -457,12 +457,7 @@ hipError_t fs_conv_launch(int order, int B, int D, const void* v, const void* co
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (two) {
-    hipError_t e = hipEventRecord(side->join, side->s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(s0, side->join, 0);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  return ways > 1 ? side_join(side, s0) : hipSuccess;
 }
 
 template <int LOG2M, bool FULL>

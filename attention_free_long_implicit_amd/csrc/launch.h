@@ -38,13 +38,30 @@ bool fourstep_supported(int log2L);
 // Workspace bytes per row: the fp32 intermediate (M complex fp32), or with bf16 storage its block-scaled fp16
 // form (M fp16 pairs and 1024 words of block exponents).  u_i stays fp32 between orders either way.
 size_t fourstep_row_bytes(int log2L, int bf16);
-// side (optional): a second stream and two events; the chunks then alternate between the caller's stream and
-// that one (forked from and joined back into the caller's stream), each stream with its own half of I, which
-// must hold 2 * chunk rows.
+// side (optional): side streams and their events; the chunks then cycle over the caller's stream and
+// ways - 1 side streams (forked from and joined back into the caller's stream), each stream with its own
+// part of I, which must hold ways * chunk rows.
+constexpr int kSideStreams = 2;
 struct SideStream {
-  hipStream_t s;
-  hipEvent_t fork, join;
+  hipStream_t s[kSideStreams];
+  hipEvent_t fork, join[kSideStreams];
+  int ways;                      // streams the chunks cycle over, the caller's included (2 .. kSideStreams + 1)
 };
+// the side streams start after the caller's work so far
+inline hipError_t side_fork(const SideStream* sd, hipStream_t s0) {
+  hipError_t e = hipEventRecord(sd->fork, s0);
+  for (int j = 0; j + 1 < sd->ways && e == hipSuccess; ++j) e = hipStreamWaitEvent(sd->s[j], sd->fork, 0);
+  return e;
+}
+// the caller's stream continues after the side streams' work
+inline hipError_t side_join(const SideStream* sd, hipStream_t s0) {
+  hipError_t e = hipSuccess;
+  for (int j = 0; j + 1 < sd->ways && e == hipSuccess; ++j) {
+    e = hipEventRecord(sd->join[j], sd->s[j]);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s0, sd->join[j], 0);
+  }
+  return e;
+}
 hipError_t launch_conv1d_fourstep(int log2L, int bf16, int order, int B, int D, const void* v,
                                   const void* const* x, const void* const* spectra, void* y, float2* I, int chunk,
                                   const Twiddles& tw, hipStream_t s, int full = 0, int hsb = 0,
