@@ -36,7 +36,7 @@ struct DeviceTables {
   SideStream side;        // the long-row plans' side streams (default priority) and their fork / join events
   bool ready;
 };
-// Held while a long-row plan forks onto a device's side stream, so that concurrent calls do not interleave
+// Held while a long-row plan forks onto a device's side streams, so that concurrent calls do not interleave
 // their fork and join events.
 std::mutex g_side_mu;
 DeviceTables g_dev[kMaxDevices];

@@ -118,7 +118,7 @@ def test_film_spectrum_matches_fft_of_taps(torch_cuda):
     ("causal", 1024, "f32", 3, 8),          # one workgroup per row
     ("causal", 8192, "bf16", 2, 6),         # bf16, even B: still the fp32 engine (filters differ per row)
     ("causal", 32768, "f32", 2, 3),         # multi-pass
-    ("causal", 65536, "bf16", 2, 3),        # multi-pass bf16: the bf16 spectrum copy of B*D filters
+    ("causal", 65536, "bf16", 2, 3),        # multi-pass bf16: fp16 intermediate, fp32 spectra of B*D filters
     ("circular", 4096, "f32", 2, 5),
     ("circular", 65536, "f32", 3, 2),       # periodic multi-pass
 ])
