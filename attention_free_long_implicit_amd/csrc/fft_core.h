@@ -250,6 +250,14 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+// Block scaling of fp16 intermediates: e such that m * 2^-e lies in [2^14, 2^15) (fp16 holds up to 65504);
+// 0 for a zero or non-finite m (which then passes through unscaled).  e >= -112 keeps 2^-e finite.
+__device__ __forceinline__ int h16_exponent(float m) {
+  if (!(m > 0.0f) || !(m <= 3.0e38f)) return 0;
+  const int e = __builtin_amdgcn_frexp_expf(m) - 15;
+  return e < -112 ? -112 : e;
+}
+
 // Two consecutive stored elements (one packed complex sample) <-> float2.
 template <bool BF16> struct Store;
 template <> struct Store<false> {

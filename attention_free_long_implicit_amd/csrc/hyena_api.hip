@@ -181,9 +181,16 @@ size_t filter_intermediate_bytes(int kind, int64_t pts) {
 }
 size_t taps_per_channel(int kind, int64_t pts) { return is3d(kind) ? conv3d_taps_per_channel(circ3(kind)) : (size_t)pts; }
 
-// Lengths whose spectrum also carries the matrix-core (row-pair, bf16) copy after the fp32 one.
+// Lengths whose spectrum also carries the matrix-core (row-pair, bf16) copy after the fp32 one: the
+// single-workgroup kernel's (L = 8192) and the long-row kernel's (L = 2^15, 2^16).
 bool has_pair_copy(int64_t L) { return mfma_pair_supported(log2i(L), 2); }
+bool has_long_pair_copy(int64_t L) { return is_pow2(L) && mfl_supported(log2i(L), 2); }
 size_t pair_copy_temp_bytes(int64_t L, int64_t D) { return (size_t)D * (size_t)(L + 1) * sizeof(float2); }
+size_t pair_copy_bytes_per_channel(int64_t L) {
+  if (has_pair_copy(L)) return mfma_pair_spectrum_bytes_per_channel();
+  if (has_long_pair_copy(L)) return mfl_spectrum_bytes_per_channel(log2i(L));
+  return 0;
+}
 
 // Rows per multi-pass chunk by default on one stream: about 160 MB of intermediate (the decode state's
 // prefix convolutions and the 3-D plans).  Smaller chunks on one stream (24-96 MB, sized for the 256 MB
@@ -244,6 +251,24 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // The matrix-core kernel: bf16, L = 8192, rows in pairs, and (16-byte vector accesses) every activation
 // pointer 16-byte aligned.
 bool use_mfma(int dtype, int64_t B, int64_t L) { return dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B); }
+
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+// Highest operator order sent to the long-row matrix-core kernels (same budget as kMfmaMaxOrder: fp16
+// transform operands, plus the fp16 planes between passes).
+constexpr int kMflMaxOrder = 3;
+
+// Whether a causal bf16 call of B rows per channel at length L, with these activation pointers, takes the
+// long-row matrix-core kernels (8-byte vector accesses to every activation).
+bool use_mfl(int kind, int dtype, int64_t B, int64_t L, int hsb, int order, const void* v, const void* const* x,
+             const void* y) {
+  if (kind != K_CAUSAL || hsb || dtype != HYENA_BF16 || order > kMflMaxOrder || !is_pow2(L) ||
+      !mfl_supported(log2i(L), (int)B))
+    return false;
+  bool ok = aligned8(v) && aligned8(y);
+  for (int i = 0; i < order; ++i) ok = ok && (!x[i] || aligned8(x[i]));
+  return ok;
+}
 
 // Highest operator order sent to the matrix-core kernel.  Its fp16 transform operands and products cost a
 // few 1e-4 of relative error per order, and later orders amplify what earlier ones leave: measured against
@@ -311,9 +336,28 @@ int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* sp
   }
   if (is3d(kind))
     return hip_status(launch_spectrum3d(h, (float2*)spectrum, (int)nch, (float2*)wsp, chunk, tw, stream, circ3(kind)));
-  if (row_b)
-    return hip_status(launch_spectrum1d_fourstep(engine_log2(kind, L), h, (float2*)spectrum, (int)nch, (float2*)wsp,
-                                                 chunk, tw, stream, kind == K_CIRC1 ? 1 : 0));
+  if (row_b) {
+    if ((st = hip_status(launch_spectrum1d_fourstep(engine_log2(kind, L), h, (float2*)spectrum, (int)nch,
+                                                    (float2*)wsp, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0))))
+      return st;
+    if (!pair_copy || kind != K_CAUSAL || !has_long_pair_copy(L)) return HYENA_OK;
+    // the long-row matrix-core copy after the fp32 spectra: natural-order bins of as many channels as the
+    // workspace holds (free again: the same stream has finished with the intermediate), then their copy
+    const size_t nat = pair_copy_temp_bytes(L, 1);
+    const int64_t c = (int64_t)(wsn / nat);
+    if (c < 1) return HYENA_EWORKSPACE;
+    const size_t pb = mfl_spectrum_bytes_per_channel(log2i(L));
+    char* pair = (char*)spectrum + (size_t)nch * (size_t)L * sizeof(float2);
+    for (int64_t d0 = 0; d0 < nch; d0 += c) {
+      const int n = (int)(nch - d0 < c ? nch - d0 : c);
+      if ((st = hip_status(launch_export1d_fourstep(log2i(L), (const float2*)spectrum + (size_t)d0 * (size_t)L,
+                                                    (float2*)wsp, n, stream))))
+        return st;
+      if ((st = hip_status(launch_mfl_spectrum(log2i(L), (const float2*)wsp, pair + (size_t)d0 * pb, n, stream))))
+        return st;
+    }
+    return HYENA_OK;
+  }
   if (kind == K_CIRC1)
     return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, (int)nch, tw, stream, 1));
   if ((st = hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, (int)nch, tw, stream)))) return st;
@@ -331,7 +375,9 @@ int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* sp
 // Whether spectra_from_taps finds the room it needs in [wsp, wsp + wsn) (checked before any launch).
 bool spectra_ws_ok(int kind, int64_t L, int64_t nch, char* wsp, size_t wsn, bool pair_copy) {
   const size_t row_b = filter_intermediate_bytes(kind, L);
-  if (row_b) return ws_align256(wsp, wsn) && wsn >= row_b;
+  if (row_b)
+    return ws_align256(wsp, wsn) && wsn >= row_b &&
+           (!pair_copy || kind != K_CAUSAL || !has_long_pair_copy(L) || wsn >= pair_copy_temp_bytes(L, 1));
   if (pair_copy && kind == K_CAUSAL && has_pair_copy(L))
     return ws_align256(wsp, wsn) && wsn >= pair_copy_temp_bytes(L, nch);
   return true;
@@ -374,8 +420,14 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
     ws_bytes = kNoallocScratchBytes;
   }
   int ways = 1;
+  bool mfl = false;   // the long-row matrix-core kernels (chunks of row pairs)
   if (per) {
-    chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
+    const bool ws_ok = ws && !((size_t)ws & 255u);
+    if (ws_ok && use_mfl(kind, dtype, B, pts, hsb, order, v, x, y)) {
+      chunk = pair_chunk(mfl_pair_bytes(log2i(pts)), B * D / 2, ws_bytes, &ways);
+      mfl = chunk >= 1;
+    }
+    if (!mfl) chunk = ws_ok ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
     for (int i = 0; i < order; ++i)
@@ -396,6 +448,14 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
     if (is3d(kind))
       return hip_status(launch_conv3d(dtype == HYENA_BF16, order, (int)B, (int)D, v, x, spectra, y, (float2*)ws,
                                       chunk, tw, stream, circ3(kind), hsb, ways > 1 ? &sd : nullptr));
+    if (mfl) {
+      const void* mats = device_mats();
+      if (!mats) return HYENA_EHIP;
+      std::vector<const void*> sp(order);
+      for (int i = 0; i < order; ++i) sp[i] = (const char*)spectra[i] + (size_t)D * (size_t)pts * sizeof(float2);
+      return hip_status(launch_conv_mfl(log2i(pts), order, (int)B, (int)D, v, x, sp.data(), y, ws, chunk, mats, tw,
+                                        stream, ways > 1 ? &sd : nullptr));
+    }
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, order, (int)B, (int)D, v, x,
                                              spectra, y, (float2*)ws, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0, hsb,
                                              ways > 1 ? &sd : nullptr));
@@ -453,8 +513,7 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   const int kind = kind_of(mode, dims);
   if (is3d(kind)) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel(circ3(kind));
   else if (kind == K_CIRC1) *bytes = (size_t)D * (size_t)(pts / 2) * sizeof(float2);
-  else *bytes = (size_t)D * (size_t)pts * sizeof(float2) +
-                (has_pair_copy(pts) && !ps ? (size_t)D * mfma_pair_spectrum_bytes_per_channel() : 0);
+  else *bytes = (size_t)D * (size_t)pts * sizeof(float2) + (ps ? 0 : (size_t)D * pair_copy_bytes_per_channel(pts));
   return HYENA_OK;
 }
 
@@ -467,7 +526,12 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* b
   *bytes = (size_t)D * taps_per_channel(kind, pts) * sizeof(float);
   if (kind == K_CAUSAL && has_pair_copy(pts)) *bytes += 256 + pair_copy_temp_bytes(pts, D);
   const size_t per = filter_intermediate_bytes(kind, pts);
-  if (per) *bytes += 256 + (size_t)filter_chunk_rows((int64_t)per, D) * per;
+  if (per) {
+    size_t room = (size_t)filter_chunk_rows((int64_t)per, D) * per;
+    if (kind == K_CAUSAL && has_long_pair_copy(pts) && room < pair_copy_temp_bytes(pts, 1))
+      room = pair_copy_temp_bytes(pts, 1);
+    *bytes += 256 + room;
+  }
   return HYENA_OK;
 }
 
@@ -482,6 +546,12 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   *bytes = 0;
   const size_t per = row_intermediate_bytes(kind, pts, dtype);
   if (per) *bytes = pair_ws_bytes(per, B * D);
+  // the long-row matrix-core kernels' pairs (the per-row plan stays possible, for misaligned activations)
+  if (per && kind == K_CAUSAL && !ps && dtype == HYENA_BF16 && order <= kMflMaxOrder &&
+      mfl_supported(log2i(pts), (int)B)) {
+    const size_t m = pair_ws_bytes(mfl_pair_bytes(log2i(pts)), B * D / 2);
+    if (m > *bytes) *bytes = m;
+  }
   return HYENA_OK;
 }
 
@@ -590,8 +660,15 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   int chunk = 0;
   const size_t per = row_intermediate_bytes(kind, pts, dtype);
   int ways = 1;
+  bool mfl = false;   // the long-row matrix-core kernels (chunks of row pairs)
+  const void* xs[1] = {gate};
   if (per) {
-    chunk = ws && !((size_t)ws & 255u) ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
+    const bool ws_ok = ws && !((size_t)ws & 255u);
+    if (ws_ok && use_mfl(kind, dtype, B, pts, hsb, 1, u, xs, y)) {
+      chunk = pair_chunk(mfl_pair_bytes(log2i(pts)), B * D / 2, ws_bytes, &ways);
+      mfl = chunk >= 1;
+    }
+    if (!mfl) chunk = ws_ok ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, u, tb) || (gate && overlaps(ws, ws_bytes, gate, tb)))
       return HYENA_EALIAS;
@@ -599,7 +676,6 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   Twiddles tw;
   if ((st = get_twiddles(&tw))) return st;
   if (chunk) {
-    const void* xs[1] = {gate};
     const void* sp[1] = {spectrum};
     DeviceTables* dt = nullptr;
     if (ways > 1 && (st = init_current_device(&dt))) return st;
@@ -613,6 +689,13 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
     if (is3d(kind))
       return hip_status(launch_conv3d(dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs, sp, y, (float2*)ws, chunk, tw,
                                       stream, circ3(kind), hsb, ways > 1 ? &sd : nullptr));
+    if (mfl) {
+      const void* mats = device_mats();
+      if (!mats) return HYENA_EHIP;
+      const void* mp[1] = {(const char*)spectrum + (size_t)D * (size_t)pts * sizeof(float2)};
+      return hip_status(launch_conv_mfl(log2i(pts), 1, (int)B, (int)D, u, xs, mp, y, ws, chunk, mats, tw, stream,
+                                        ways > 1 ? &sd : nullptr));
+    }
     return hip_status(launch_conv1d_fourstep(engine_log2(kind, pts), dtype == HYENA_BF16, 1, (int)B, (int)D, u, xs,
                                              sp, y, (float2*)ws, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0, hsb,
                                              ways > 1 ? &sd : nullptr));

@@ -49,13 +49,6 @@ struct H16Row {
   static constexpr int EA = 0, EB = 128;   // offsets from word M
   static constexpr int EXTRA = 1024;       // words after the values
 };
-// e such that m * 2^-e has its largest component in [2^14, 2^15); 0 for a zero or non-finite m (which then
-// passes through unscaled).  e >= -112 keeps 2^-e finite.
-__device__ __forceinline__ int h16_exponent(float m) {
-  if (!(m > 0.0f) || !(m <= 3.0e38f)) return 0;
-  const int e = __builtin_amdgcn_frexp_expf(m) - 15;
-  return e < -112 ? -112 : e;
-}
 __device__ __forceinline__ uint32_t h16_pack(float2 v, float s) {
   typedef _Float16 h2 __attribute__((ext_vector_type(2)));
   const h2 r = {(_Float16)(v.x * s), (_Float16)(v.y * s)};

@@ -77,7 +77,9 @@ def test_fourstep_no_gate_and_chunk_invariance(torch_cuda):
     vd = to_dev(v, torch.bfloat16)
     xd = [to_dev(x, torch.bfloat16) for x in xs]
     y_big = hy.operator(vd, xd, spectra)
-    y_one = hy.operator(vd, xd, spectra, ws=torch.empty(L * 8, dtype=torch.uint8, device="cuda"))
+    # a workspace sized for one channel's rows: one chunk per channel
+    one = hy.workspace_bytes(3, B, 1, (L,), hy.BF16)
+    y_one = hy.operator(vd, xd, spectra, ws=torch.empty(one, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(y_big, y_one)
     # no-gate fftconv of one channel == order-1 oracle convolution
@@ -148,11 +150,12 @@ def test_fourstep_fftconv_bf16_chunked(torch_cuda, L):
     assert e.max() < BF16_TOL, e.max()
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_fourstep_zero_input_gives_exact_zero(torch_cuda, dtype):
+@pytest.mark.parametrize("dtype,B", [("f32", 1), ("bf16", 1), ("bf16", 2)])
+def test_fourstep_zero_input_gives_exact_zero(torch_cuda, dtype, B):
+    """v = 0 gives y = 0 exactly on the multi-pass plans (per row, and the long-row matrix cores for B = 2)."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
-    L, B, D = 1 << 15, 1, 3
+    L, D = 1 << 15, 3
     w = hi.WORKLOADS[0].with_(B=B, D=D, dims=(L,))
     p = hi.draw_filter_params(w, seed=9)
     tdt = torch.float32 if dtype == "f32" else torch.bfloat16
