@@ -181,10 +181,11 @@ size_t filter_intermediate_bytes(int kind, int64_t pts) {
 }
 size_t taps_per_channel(int kind, int64_t pts) { return is3d(kind) ? conv3d_taps_per_channel(circ3(kind)) : (size_t)pts; }
 
-// Lengths whose spectrum also carries the matrix-core (row-pair, bf16) copy after the fp32 one: the
-// single-workgroup kernel's (L = 8192) and the long-row kernel's (L = 2^15, 2^16).
+// Lengths whose spectrum also carries a matrix-core (bf16 storage) copy after the fp32 one: the row-pair
+// copy of the single-workgroup kernel (L = 8192) and the split coefficients of the long-row kernels
+// (L = 2^15 .. 2^17).
 bool has_pair_copy(int64_t L) { return mfma_pair_supported(log2i(L), 2); }
-bool has_long_pair_copy(int64_t L) { return is_pow2(L) && mfl_supported(log2i(L), 2); }
+bool has_long_pair_copy(int64_t L) { return is_pow2(L) && mfl_supported(log2i(L)); }
 size_t pair_copy_temp_bytes(int64_t L, int64_t D) { return (size_t)D * (size_t)(L + 1) * sizeof(float2); }
 size_t pair_copy_bytes_per_channel(int64_t L) {
   if (has_pair_copy(L)) return mfma_pair_spectrum_bytes_per_channel();
@@ -252,21 +253,18 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // pointer 16-byte aligned.
 bool use_mfma(int dtype, int64_t B, int64_t L) { return dtype == HYENA_BF16 && mfma_pair_supported(log2i(L), (int)B); }
 
-bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
-
 // Highest operator order sent to the long-row matrix-core kernels (same budget as kMfmaMaxOrder: fp16
 // transform operands, plus the fp16 planes between passes).
 constexpr int kMflMaxOrder = 3;
 
-// Whether a causal bf16 call of B rows per channel at length L, with these activation pointers, takes the
-// long-row matrix-core kernels (8-byte vector accesses to every activation).
-bool use_mfl(int kind, int dtype, int64_t B, int64_t L, int hsb, int order, const void* v, const void* const* x,
-             const void* y) {
+// Whether a causal bf16 call at length L, with these activation pointers, takes the long-row matrix-core
+// kernels (16-byte vector accesses to every activation).
+bool use_mfl(int kind, int dtype, int64_t L, int hsb, int order, const void* v, const void* const* x, const void* y) {
   if (kind != K_CAUSAL || hsb || dtype != HYENA_BF16 || order > kMflMaxOrder || !is_pow2(L) ||
-      !mfl_supported(log2i(L), (int)B))
+      !mfl_supported(log2i(L)))
     return false;
-  bool ok = aligned8(v) && aligned8(y);
-  for (int i = 0; i < order; ++i) ok = ok && (!x[i] || aligned8(x[i]));
+  bool ok = aligned16(v) && aligned16(y);
+  for (int i = 0; i < order; ++i) ok = ok && (!x[i] || aligned16(x[i]));
   return ok;
 }
 
@@ -353,7 +351,7 @@ int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* sp
       if ((st = hip_status(launch_export1d_fourstep(log2i(L), (const float2*)spectrum + (size_t)d0 * (size_t)L,
                                                     (float2*)wsp, n, stream))))
         return st;
-      if ((st = hip_status(launch_mfl_spectrum(log2i(L), (const float2*)wsp, pair + (size_t)d0 * pb, n, stream))))
+      if ((st = hip_status(launch_mfl_spectrum(log2i(L), (const float2*)wsp, pair + (size_t)d0 * pb, n, tw, stream))))
         return st;
     }
     return HYENA_OK;
@@ -420,11 +418,11 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
     ws_bytes = kNoallocScratchBytes;
   }
   int ways = 1;
-  bool mfl = false;   // the long-row matrix-core kernels (chunks of row pairs)
+  bool mfl = false;   // the long-row matrix-core kernels
   if (per) {
     const bool ws_ok = ws && !((size_t)ws & 255u);
-    if (ws_ok && use_mfl(kind, dtype, B, pts, hsb, order, v, x, y)) {
-      chunk = pair_chunk(mfl_pair_bytes(log2i(pts)), B * D / 2, ws_bytes, &ways);
+    if (ws_ok && use_mfl(kind, dtype, pts, hsb, order, v, x, y)) {
+      chunk = pair_chunk(mfl_row_bytes(log2i(pts)), B * D, ws_bytes, &ways);
       mfl = chunk >= 1;
     }
     if (!mfl) chunk = ws_ok ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
@@ -546,12 +544,8 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   *bytes = 0;
   const size_t per = row_intermediate_bytes(kind, pts, dtype);
   if (per) *bytes = pair_ws_bytes(per, B * D);
-  // the long-row matrix-core kernels' pairs (the per-row plan stays possible, for misaligned activations)
-  if (per && kind == K_CAUSAL && !ps && dtype == HYENA_BF16 && order <= kMflMaxOrder &&
-      mfl_supported(log2i(pts), (int)B)) {
-    const size_t m = pair_ws_bytes(mfl_pair_bytes(log2i(pts)), B * D / 2);
-    if (m > *bytes) *bytes = m;
-  }
+  // (the long-row matrix-core kernels need less per row than the per-row plan, which stays possible for
+  // misaligned activations)
   return HYENA_OK;
 }
 
@@ -660,12 +654,12 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   int chunk = 0;
   const size_t per = row_intermediate_bytes(kind, pts, dtype);
   int ways = 1;
-  bool mfl = false;   // the long-row matrix-core kernels (chunks of row pairs)
+  bool mfl = false;   // the long-row matrix-core kernels
   const void* xs[1] = {gate};
   if (per) {
     const bool ws_ok = ws && !((size_t)ws & 255u);
-    if (ws_ok && use_mfl(kind, dtype, B, pts, hsb, 1, u, xs, y)) {
-      chunk = pair_chunk(mfl_pair_bytes(log2i(pts)), B * D / 2, ws_bytes, &ways);
+    if (ws_ok && use_mfl(kind, dtype, pts, hsb, 1, u, xs, y)) {
+      chunk = pair_chunk(mfl_row_bytes(log2i(pts)), B * D, ws_bytes, &ways);
       mfl = chunk >= 1;
     }
     if (!mfl) chunk = ws_ok ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;

@@ -1,29 +1,35 @@
-// Matrix-core causal long convolution for bf16 storage and long rows (L = 2^15, 2^16), rows taken in pairs.
+// Matrix-core causal long convolution for bf16 storage and long rows (L = 2^15, 2^16, 2^17), one row at a time.
 //
 // Operation: Hyena study note, steps 2-3 (long convolution with the implicit filter, gate); EulerStack
 // "4. Hyena 상세", how it works 2 (FFT, elementwise product, inverse FFT); HyenaND summary, boundary handling
-// (zero-pad to twice the size).  A row of 2L samples is too long for one workgroup, so the transform is split
-// four-step style, N = 2L = N1 x N2 with N2 = 16384 the matrix-core transform of the 8192-sample kernel:
+// (zero-pad to twice the size).  The real row u of L samples, zero-padded to 2L, is packed into M = L complex
+// points z[n] = u[2n] + i u[2n+1] (zero for n >= M/2).  With Z = DFT_M(z) and H the 2L-point DFT of the filter,
+// the packed spectrum of the padded product is
 //
-//   n = m + N2 n0 (n0 < N1, only n0 < N1/2 non-zero: the zero padding), k = k0 + N1 kappa,
-//   W_N^{nk} = W_N1^{n0 k0} . W_N^{m k0} . W_N2^{m kappa}.
+//   Z'[k] = A[k] Z[k] + B[k] conj(Z[M - k]),   A = Hs - Hd sin(pi k / M),  B = i Hd cos(pi k / M),
+//   Hs = (H[k] + H[k + M]) / 2,  Hd = (H[k] - H[k + M]) / 2,
 //
-//   column pass (k_mfl_cols): for every column m, the N1-point DFT over n0 and the twiddle W_N^{m k0}
-//       -> plane k0, X[k0][m]; in fp32, one thread per four consecutive columns.
-//   plane pass  (k_mfl_planes): every plane k0 is an N2-point sequence: forward transform on the matrix
-//       cores, product with the filter spectrum at bins k0 + N1 kappa (scaled by 1/N), inverse transform;
-//       the passes and the slab decomposition are those of the 8192-sample kernel (16 x 32 x 32), with all
-//       16 inputs of the first radix-16 product non-zero and all 16 outputs of the last one kept.
-//   column pass again: conjugate twiddle, inverse N1-point DFT over k0, keep n0 < N1/2 (the causal half),
-//       gate; for every order but the last the same workgroup then runs the next order's forward column
-//       pass on the gated values, so u_i never goes to memory.
+// (the usual split of a real transform into the transforms of its even and odd samples, the product, and the
+// re-packing, folded into two coefficients per bin), and the inverse transform of Z' gives (h * u)[2n] +
+// i (h * u)[2n+1].  A row is too long for one workgroup, so the transform is split four-step style,
+// M = N1 x N2 with N2 = 16384 the matrix-core transform of the 8192-sample kernel:
 //
-// Rows are paired as in the 8192-sample kernel: z = u_b0 + i u_b1 for two rows of one channel (h is real, so
-// the inverse transform of DFT(z) H is (h * u_b0) + i (h * u_b1)).  A pair's planes live in the workspace as
-// fp16 (11-bit significand), real parts and imaginary parts in separate planes, each block of values written
-// by one workgroup scaled by a power of two (its exponent stored beside the planes; the reader scales back
-// exactly).  Each workgroup of the plane pass takes the two planes k0 and N1 - k0 (0 and N1/2 together), whose
-// filter-spectrum bins mirror each other (H[N - k] = conj H[k]), so one stored half serves both.
+//   n = m + N2 n0 (only n0 < N1/2 non-zero), k = k0 + N1 kappa,  W_M^{nk} = W_N1^{n0 k0} W_M^{m k0} W_N2^{m kappa}.
+//
+//   column pass (k_mfl_cols): for every column m, the N1-point DFT over n0 and the twiddle W_M^{m k0} -> plane
+//       k0; in fp32, one thread per four consecutive columns.
+//   plane pass (k_mfl_planes): every plane k0 is an N2-point sequence, transformed on the matrix cores with the
+//       slab decomposition of the 8192-sample kernel (16 x 32 x 32; all 16 inputs of the first radix-16
+//       product non-zero, all 16 outputs of the last one kept); the split above needs bin M - k, which lies in
+//       plane N1 - k0 (mod N1), so a workgroup takes the planes k0 and N1 - k0 (0 and N1/2 together) and
+//       exchanges the bins through LDS.
+//   column pass again: conjugate twiddle, inverse N1-point DFT, keep n0 < N1/2 (the causal half), gate; for
+//       every order but the last the same workgroup then runs the next order's forward column pass on the
+//       gated values, so u_i never goes to memory.
+//
+// A row's planes live in the workspace as fp16 (11-bit significand), real and imaginary parts in separate
+// planes, each block of values written by one workgroup scaled by a power of two (its exponent stored beside
+// the planes; the reader scales back exactly), so every row keeps its own scale.
 #include "engine.h"
 #include "launch.h"
 #include "mfma_core.h"
@@ -33,54 +39,26 @@ namespace hyena {
 namespace mfl {
 constexpr int N2 = 16384;                 // plane length
 constexpr int TILE_C = 64;                // column pass: columns c .. c + 63 (mod 1024) for all 16 n1
-constexpr int NTILE = 1024 / TILE_C;      // column tiles per pair
+constexpr int NTILE = 1024 / TILE_C;      // column tiles per row
 constexpr int TC = 256;                   // column-pass threads: four consecutive columns each
 constexpr int TP = 512;                   // plane-pass threads: two planes of four waves
-// Per pair: N1 planes of N2 fp16 real parts then N2 fp16 imaginary parts (N 32-bit words), then a header of
-// HDR 32-bit words: the column pass's tile exponents (H_EA + tile); its per-tile "row is non-zero" bits in two
-// slots by order parity (H_NZ + 32 slot + 2 tile + row: the column pass of order i reads slot i % 2 while
-// writing slot (i + 1) % 2 for the next order); the plane pass's plane exponents (H_EB + k0).
-enum { H_EA = 0, H_NZ = 32, H_EB = 128, HDR = 256 };
+// Per row: N1 planes of N2 fp16 real parts then N2 fp16 imaginary parts (M 32-bit words), then a header of
+// HDR words: the column pass's tile exponents (H_EA + tile), the plane pass's plane exponents (H_EB + k0).
+enum { H_EA = 0, H_EB = 32, HDR = 64 };
+// tile exponent of an all-zero tile: below any real one (2^kNoExponent is 0 in fp32)
+constexpr int kNoExponent = -4096;
 template <int N1>
 struct Plan {
-  static_assert(N1 == 4 || N1 == 8, "L = 2^15 or 2^16");
-  static constexpr int N = N1 * N2;
-  static constexpr int L = N / 2;
-  static constexpr int LOG2N = N1 == 4 ? 16 : 17;
-  static constexpr size_t PAIR_WORDS = (size_t)N + HDR;
-  // spectrum slots of 16 words x 64 lanes: plane 0 slabs 0..8, plane N1/2 slabs 0..7, planes 1..N1/2-1
-  // slabs 0..15; then a 64-word tail (word 0: the exponent of the table's scale back)
-  static constexpr int SLOTS = 8 * N1 + 1;
-  static constexpr int SPEC_WORDS = SLOTS * 1024 + 64;
+  static_assert(N1 == 2 || N1 == 4 || N1 == 8, "L = 2^15, 2^16 or 2^17");
+  static constexpr int M = N1 * N2;       // packed points per row = samples per row
+  static constexpr int LOG2M = N1 == 2 ? 15 : (N1 == 4 ? 16 : 17);
+  static constexpr size_t ROW_WORDS = (size_t)M + HDR;
+  // split coefficients per channel: [plane][slab][32 words][64 lanes] (words 0..15: A, 16..31: B; in each,
+  // 8 real-part pairs then 8 imaginary-part pairs), then a 64-word tail (word 0: log2 of the scale back)
+  static constexpr int COEF_WORDS = N1 * 16 * 32 * 64;
+  static constexpr int SPEC_WORDS = COEF_WORDS + 64;
 };
 }  // namespace mfl
-
-// Largest value of a and of b, and the OR of c and of d, over the 256 threads (4 waves) of the workgroup;
-// red: 16 words of LDS.  The caller's next barrier must not be this one's.
-__device__ __forceinline__ void block_reduce4(float& a, float& b, uint32_t& c, uint32_t& d, uint32_t* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    a = fmaxf(a, __shfl_xor(a, o));
-    b = fmaxf(b, __shfl_xor(b, o));
-    c |= __shfl_xor(c, o);
-    d |= __shfl_xor(d, o);
-  }
-  if ((threadIdx.x & 63) == 0) {
-    uint32_t* r = red + 4 * (threadIdx.x >> 6);
-    r[0] = __float_as_uint(a);
-    r[1] = __float_as_uint(b);
-    r[2] = c;
-    r[3] = d;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    a = fmaxf(a, __uint_as_float(red[4 * w]));
-    b = fmaxf(b, __uint_as_float(red[4 * w + 1]));
-    c |= red[4 * w + 2];
-    d |= red[4 * w + 3];
-  }
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -88,38 +66,35 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // ----------------------------------------------------------------------------------------------
 // Column pass.  MODE 0: forward from the bf16 input u (first order).  MODE 1: inverse of the planes, gate
 // (GATE), then store y, or (CHAIN) the forward column pass of the next order on the gated values.
-// grid.x = NTILE * nq (pair fastest); thread t: n1 = t / 16, columns m = 64 tile + 4 (t % 16) + i + 1024 n1,
-// i < 4, so each access of a plane or a row is 8 bytes, 16 threads per 128-byte segment.
+// grid.x = NTILE * nq (row fastest); thread t: n1 = t / 16, columns m = 64 tile + 4 (t % 16) + i + 1024 n1,
+// i < 4: 8 consecutive samples of a row (16 bytes) and 4 consecutive values of a plane (8 bytes) per access.
 template <int N1, int MODE, bool GATE, bool CHAIN>
 __global__ void __launch_bounds__(mfl::TC)
 k_mfl_cols(const uint16_t* u, const uint16_t* gate, uint16_t* y, uint32_t* W, int q0, int nq, int B, int D,
-           int par, Twiddles tw) {
+           Twiddles tw) {
   using namespace mfl;
   using P = Plan<N1>;
-  constexpr int N = P::N, L = P::L, H = N1 / 2;
-  __shared__ uint32_t red[16];
+  constexpr int M = P::M, H = N1 / 2;
+  __shared__ float red[TC / 64];
   const int t = threadIdx.x;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int pl = lb % nq, tile = lb / nq;
-  const int q = q0 + pl;
-  const int np = B >> 1;
-  const int d = q / np, bp = q % np;
-  const size_t r0 = (size_t)(2 * bp) * D + d, r1 = r0 + D;
-  uint32_t* const Wp = W + (size_t)pl * P::PAIR_WORDS;
+  const int rl = lb % nq, tile = lb / nq;
+  const int q = q0 + rl;                     // rows visited channel-major: q = d B + b
+  const size_t row = (size_t)(q % B) * D + q / B;
+  uint32_t* const Wp = W + (size_t)rl * P::ROW_WORDS;
   uint16_t* const planes = reinterpret_cast<uint16_t*>(Wp);
-  uint32_t* const hdr = Wp + N;
+  uint32_t* const hdr = Wp + M;
   const int m0 = TILE_C * tile + 4 * (t & 15) + 1024 * (t >> 4);
 
-  float2 z[4][H];   // [column][n0]: row b0 in x, row b1 in y
+  float2 z[4][H];   // [column][n0]: samples 2n and 2n + 1 of the row
   if constexpr (MODE == 0) {
 #pragma unroll
     for (int n0 = 0; n0 < H; ++n0) {
-      const uint2 a = *reinterpret_cast<const uint2*>(u + r0 * L + m0 + N2 * n0);
-      const uint2 b = *reinterpret_cast<const uint2*>(u + r1 * L + m0 + N2 * n0);
-      z[0][n0] = make_float2(bf16_lo(a.x), bf16_lo(b.x));
-      z[1][n0] = make_float2(bf16_hi(a.x), bf16_hi(b.x));
-      z[2][n0] = make_float2(bf16_lo(a.y), bf16_lo(b.y));
-      z[3][n0] = make_float2(bf16_hi(a.y), bf16_hi(b.y));
+      const uint4 a = *reinterpret_cast<const uint4*>(u + row * M + 2 * (m0 + N2 * n0));
+      z[0][n0] = make_float2(bf16_lo(a.x), bf16_hi(a.x));
+      z[1][n0] = make_float2(bf16_lo(a.y), bf16_hi(a.y));
+      z[2][n0] = make_float2(bf16_lo(a.z), bf16_hi(a.z));
+      z[3][n0] = make_float2(bf16_lo(a.w), bf16_hi(a.w));
     }
   } else {
     uint2 re[N1], im[N1];
@@ -128,28 +103,17 @@ k_mfl_cols(const uint16_t* u, const uint16_t* gate, uint16_t* y, uint32_t* W, in
       re[k0] = *reinterpret_cast<const uint2*>(planes + (size_t)k0 * 2 * N2 + m0);
       im[k0] = *reinterpret_cast<const uint2*>(planes + (size_t)k0 * 2 * N2 + N2 + m0);
     }
-    uint2 g0[H], g1[H];
+    uint4 g[H];
     if constexpr (GATE) {
 #pragma unroll
-      for (int n0 = 0; n0 < H; ++n0) {
-        g0[n0] = *reinterpret_cast<const uint2*>(gate + r0 * L + m0 + N2 * n0);
-        g1[n0] = *reinterpret_cast<const uint2*>(gate + r1 * L + m0 + N2 * n0);
-      }
+      for (int n0 = 0; n0 < H; ++n0) g[n0] = *reinterpret_cast<const uint4*>(gate + row * M + 2 * (m0 + N2 * n0));
     }
-    // exponents of the plane pass's blocks; a row whose input to this order was all zeros gives exact zeros
-    float eb[N1];
+    float eb[N1];   // the plane pass's scales back
 #pragma unroll
     for (int k0 = 0; k0 < N1; ++k0) eb[k0] = __builtin_ldexpf(1.0f, (int)hdr[H_EB + k0]);
-    uint32_t nz0 = 0, nz1 = 0;
-#pragma unroll
-    for (int k = 0; k < NTILE; ++k) {
-      nz0 |= hdr[H_NZ + 32 * par + 2 * k];
-      nz1 |= hdr[H_NZ + 32 * par + 2 * k + 1];
-    }
-    const float keep0 = nz0 ? 1.0f : 0.0f, keep1 = nz1 ? 1.0f : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float2 w = twiddle<P::LOG2N>(tw, uint32_t(m0 + i));
+      const float2 w = twiddle<P::LOG2M>(tw, uint32_t(m0 + i));
       float2 p[N1];
       twiddle_powers<N1>(w, p);
       float2 x[N1];
@@ -163,11 +127,11 @@ k_mfl_cols(const uint16_t* u, const uint16_t* gate, uint16_t* y, uint32_t* W, in
       dft<N1, true, false, true>(x);
 #pragma unroll
       for (int n0 = 0; n0 < H; ++n0) {
-        float a = x[n0].x * keep0, b = x[n0].y * keep1;
+        float a = x[n0].x, b = x[n0].y;
         if constexpr (GATE) {
-          const uint32_t ga = (i < 2) ? g0[n0].x : g0[n0].y, gb = (i < 2) ? g1[n0].x : g1[n0].y;
-          a *= (i & 1) ? bf16_hi(ga) : bf16_lo(ga);
-          b *= (i & 1) ? bf16_hi(gb) : bf16_lo(gb);
+          const uint32_t gw = i == 0 ? g[n0].x : (i == 1 ? g[n0].y : (i == 2 ? g[n0].z : g[n0].w));
+          a *= bf16_lo(gw);
+          b *= bf16_hi(gw);
         }
         z[i][n0] = make_float2(a, b);
       }
@@ -175,44 +139,38 @@ k_mfl_cols(const uint16_t* u, const uint16_t* gate, uint16_t* y, uint32_t* W, in
     if constexpr (!CHAIN) {
 #pragma unroll
       for (int n0 = 0; n0 < H; ++n0) {
-        uint2 ya, yb;
-        ya.x = f32x2_to_bf16x2_rne(z[0][n0].x, z[1][n0].x);
-        ya.y = f32x2_to_bf16x2_rne(z[2][n0].x, z[3][n0].x);
-        yb.x = f32x2_to_bf16x2_rne(z[0][n0].y, z[1][n0].y);
-        yb.y = f32x2_to_bf16x2_rne(z[2][n0].y, z[3][n0].y);
-        *reinterpret_cast<uint2*>(y + r0 * L + m0 + N2 * n0) = ya;
-        *reinterpret_cast<uint2*>(y + r1 * L + m0 + N2 * n0) = yb;
+        uint4 o;
+        o.x = f32x2_to_bf16x2_rne(z[0][n0].x, z[0][n0].y);
+        o.y = f32x2_to_bf16x2_rne(z[1][n0].x, z[1][n0].y);
+        o.z = f32x2_to_bf16x2_rne(z[2][n0].x, z[2][n0].y);
+        o.w = f32x2_to_bf16x2_rne(z[3][n0].x, z[3][n0].y);
+        *reinterpret_cast<uint4*>(y + row * M + 2 * (m0 + N2 * n0)) = o;
       }
       return;
     }
   }
 
-  // forward column pass: the tile's scale from a bound (each output component is at most N1 times the largest
-  // input component), and per row whether any input is non-zero
-  float a0 = 0.0f, a1 = 0.0f;
-  uint32_t o0 = 0, o1 = 0;
+  // forward column pass; the tile's scale from a bound: each output component is at most N1 times the largest
+  // input component (N1 / 2 inputs, each component of a product with a unit twiddle at most twice as large)
+  float a = 0.0f;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int n0 = 0; n0 < H; ++n0) {
-      a0 = fmaxf(a0, fabsf(z[i][n0].x));
-      a1 = fmaxf(a1, fabsf(z[i][n0].y));
-      o0 |= __float_as_uint(z[i][n0].x) & 0x7fffffffu;
-      o1 |= __float_as_uint(z[i][n0].y) & 0x7fffffffu;
-    }
-  block_reduce4(a0, a1, o0, o1, red);
-  const int ex = h16_exponent((float)N1 * fmaxf(a0, a1));
+    for (int n0 = 0; n0 < H; ++n0) a = fmaxf(a, fmaxf(fabsf(z[i][n0].x), fabsf(z[i][n0].y)));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) a = fmaxf(a, __shfl_xor(a, o));
+  if ((t & 63) == 0) red[t >> 6] = a;
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < TC / 64; ++k) a = fmaxf(a, red[k]);
+  const int ex = h16_exponent((float)N1 * a);
   const float sc = __builtin_ldexpf(1.0f, -ex);
-  if (t == 0) {
-    const int slot = MODE == 0 ? par : par ^ 1;
-    hdr[H_EA + tile] = (uint32_t)ex;
-    hdr[H_NZ + 32 * slot + 2 * tile] = o0;
-    hdr[H_NZ + 32 * slot + 2 * tile + 1] = o1;
-  }
+  // an all-zero tile records kNoExponent, so that it cannot set the row's common scale in the plane pass
+  if (t == 0) hdr[H_EA + tile] = (uint32_t)(a > 0.0f ? ex : kNoExponent);
   uint32_t rw[N1][2], iw[N1][2];   // fp16 pairs of columns (0, 1) and (2, 3)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float2 w = twiddle<P::LOG2N>(tw, uint32_t(m0 + i));
+    const float2 w = twiddle<P::LOG2M>(tw, uint32_t(m0 + i));
     float2 p[N1];
     twiddle_powers<N1>(w, p);
     float2 x[N1];
@@ -222,8 +180,8 @@ k_mfl_cols(const uint16_t* u, const uint16_t* gate, uint16_t* y, uint32_t* W, in
 #pragma unroll
     for (int k0 = 0; k0 < N1; ++k0) {
       const float2 v = cmul(x[k0], p[k0]);
-      const _Float16 vr = (_Float16)(v.x * sc), vi = (_Float16)(v.y * sc);
-      const uint32_t br = __builtin_bit_cast(uint16_t, vr), bi = __builtin_bit_cast(uint16_t, vi);
+      const uint32_t br = __builtin_bit_cast(uint16_t, (_Float16)(v.x * sc));
+      const uint32_t bi = __builtin_bit_cast(uint16_t, (_Float16)(v.y * sc));
       if (i & 1) {
         rw[k0][i >> 1] |= br << 16;
         iw[k0][i >> 1] |= bi << 16;
@@ -241,32 +199,40 @@ k_mfl_cols(const uint16_t* u, const uint16_t* gate, uint16_t* y, uint32_t* W, in
 }
 
 // ----------------------------------------------------------------------------------------------
-// Plane pass: workgroup = planes k0 = g and N1 - g of one pair (g = 0: planes 0 and N1/2), 8 waves, one LDS
-// plane each.  Waves 4q..4q+3 run pass 1 and pass 1' of plane q; in passes 2..2' wave w owns slabs w and
-// w + 8 of both planes, with one set of matrix loads.  The transform steps are those of k_conv_mfma (the
-// 8192-sample kernel): pass 1 radix 16 over n1 (all 16 inputs), pass 2 radix 32 with the slab's matrix,
-// twiddle W_1024, pass 3 radix 32 -> bins kappa = k1 + 16 k2 + 512 k3; product; passes 3', 2', 1' inverse.
+// Plane pass: workgroup = planes k0 = g and N1 - g of one row (g = 0: planes 0 and N1/2), 8 waves, one LDS
+// plane each.  Waves 4q..4q+3 run pass 1 and pass 1' of plane q; in the slab passes wave w owns slabs w and
+// w + 8 of both planes, with one set of matrix loads.  Steps (as in k_conv_mfma, the 8192-sample kernel):
+//   pass 1   radix 16 over n1 (all 16 inputs) -> slab k1                                    | barrier
+//   forward  pass 2 (radix 32, the slab's matrix), twiddle W_1024, pass 3 -> bins
+//            kappa = k1 + 16 k2 + 512 k3, written back over the slab (k3 row, k2 column)  | barrier
+//   split    Z' = A Z + B conj(Z[M - k]) for the wave's four slab units, the mirrored bins read from LDS
+//            (plane N1 - k0, slab 15 - k1, k2 -> 31 - k2, k3 -> 31 - k3; in plane 0, slab 16 - k1, and
+//            for its slab 0, k2 -> 32 - k2 and, where k2 = 0, k3 -> 32 - k3, all mod 32); kept in registers
+//                                                                                         | barrier
+//   inverse  pass 3', conjugate twiddle, pass 2' -> slab                                   | barrier
+//   pass 1'  radix 16 over k1, all 16 outputs, stored as fp16.
 //
-// Scaling (all exact powers of two): the column pass's tiles have exponents e_A; the plane's input is read
-// as fp16 and its first product's accumulators are scaled by 2^(e_A - E - 16), E = max e_A, which puts every
-// input component below 1/2 (with all 16 inputs non-zero, no intermediate then exceeds 2^14.5); the spectrum
-// table holds c H / N; the output block is stored as fp16 scaled by 2^-e', e' chosen from a bound (each
-// output component is at most 32 times the largest value pass 2' leaves), with
-// e_B = e' + 10 + log2(1/c) + E + 16 recorded for the column pass.
+// Scaling (all exact powers of two): the column pass's tiles have exponents e_A (kNoExponent for an all-zero
+// tile); the plane's input is read as fp16 and its first product's accumulators are scaled by
+// 2^(e_A - E - 17), E = max e_A, which keeps every
+// input component below 1/4, the bins' magnitudes below 2^12.5 and the split's below 2^14 (fp16 holds 65504); the
+// coefficient table holds c A / M and c B / M; the output block is stored as fp16 scaled by 2^-e', e' chosen
+// from a bound (each output component is at most 32 times the largest value pass 2' leaves), with
+// e_B = e' + 10 + log2(1/c) + E + 17 recorded for the column pass (the 10: the inverse matrices' 1/32 each).
 template <int N1>
 __global__ void __launch_bounds__(mfl::TP, 1)
 k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __restrict__ mats, int q0, int nq, int B) {
   using namespace mf;
   using P = mfl::Plan<N1>;
-  constexpr int N2 = mfl::N2, NW = 8, NIT = 2, G = N1 / 2;
+  constexpr int N2 = mfl::N2, NW = 8, G = N1 / 2;
   __shared__ uint32_t S[2 * PLANE];
   __shared__ float red[2 * NW];
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int pl = lb / G, g = lb % G;
-  const int d = (q0 + pl) / (B >> 1);
-  uint32_t* const Wp = W + (size_t)pl * P::PAIR_WORDS;
+  const int rl = lb / G, g = lb % G;
+  const int d = (q0 + rl) / B;
+  uint32_t* const Wp = W + (size_t)rl * P::ROW_WORDS;
   uint16_t* const planes = reinterpret_cast<uint16_t*>(Wp);
-  uint32_t* const hdr = Wp + P::N;
+  uint32_t* const hdr = Wp + P::M;
   const int mine = (int)(threadIdx.x >> 8);
   auto plane_of = [&](int qq) { return qq == 0 ? g : (g == 0 ? N1 / 2 : N1 - g); };
 
@@ -276,8 +242,8 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
   uint32_t* const Sm = S + mine * PLANE;
   uint16_t* const Pm = planes + (size_t)plane_of(mine) * 2 * N2;   // this group's plane (real parts first)
 
-  // pass 1 input: lanes h = 0 / 1 carry the real / imaginary parts, n1 = e, 8 consecutive columns each
-  u32x4 VA[8], VB[8];   // n1 = e, n1 = 8 + e
+  // pass 1 input: lanes h = 0 / 1 carry the real / imaginary parts, n1 = e and 8 + e, 8 consecutive columns
+  u32x4 VA[8], VB[8];
   {
     const uint16_t* src = Pm + h * N2 + c0;
 #pragma unroll
@@ -302,12 +268,12 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
       ps[4 + q] = __builtin_bit_cast(f16x2, f);
     }
   }
-  int E = -1000;
+  int E = mfl::kNoExponent;
 #pragma unroll
   for (int k = 0; k < mfl::NTILE; ++k) E = max(E, (int)hdr[mfl::H_EA + k]);
-  const float f_in = __builtin_ldexpf(1.0f, (int)hdr[mfl::H_EA + (c0 >> 6)] - E - 16);
+  const float f_in = __builtin_ldexpf(1.0f, (int)hdr[mfl::H_EA + (c0 >> 6)] - E - 17);
   const uint32_t* __restrict__ Hc = spec + (size_t)d * P::SPEC_WORDS;
-  const int eH = (int)Hc[P::SLOTS * 1024];
+  const int eH = (int)Hc[P::COEF_WORDS];
 
   f16x8 Ma[NBLK], Mb[NBLK];
   const __amdgpu_buffer_rsrc_t mrs = __builtin_amdgcn_make_buffer_rsrc(
@@ -319,41 +285,18 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
       M[b] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(
                                            mrs, mvo, ((k1s_ * SLAB_TABLE + which * NBLK + b) * 64) * 16, 0));
   };
-  // Spectrum slot of plane qq's slab k1 and whether it is read mirrored.  Bin N - k of (plane k0, slab k1,
-  // lane l, register v) is register 15 - v of lane 63 - l in plane N1 - k0, slab 15 - k1 (slab 16 - k1 for
-  // plane 0, whose mirror is itself): a mirrored read takes word 7 - q / 23 - q of lane 63 - l and uses it
-  // with the halves swapped and conjugated.  All wave-uniform.
-  auto slot_of = [&](int qq, int k1, bool& mir) {
-    if (g == 0) {
-      if (qq == 0) {
-        mir = k1 > 8;
-        return mir ? 16 - k1 : k1;
-      }
-      mir = k1 > 7;
-      return 9 + (mir ? 15 - k1 : k1);
-    }
-    mir = qq == 1;
-    return 17 + 16 * (g - 1) + (mir ? 15 - k1 : k1);
+  const __amdgpu_buffer_rsrc_t crs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Hc, (short)0, P::COEF_WORDS * 4, kRawBufferWord3);
+  // the 32 coefficient words of plane qq's slab k1 (scalar) for this lane
+  auto load_coef = [&](int qq, int k1s_, uint32_t (&c)[32]) {
+    const int base = (plane_of(qq) * 16 + k1s_) * 32;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) c[k] = __builtin_amdgcn_raw_buffer_load_b32(crs, l * 4, (base + k) * 256, 0);
   };
-  uint32_t hw[2][16];
-  const __amdgpu_buffer_rsrc_t hrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Hc, (short)0, P::SLOTS * 1024 * 4, kRawBufferWord3);
   const int ws = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  auto load_spectrum = [&](int k1s) {
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) {
-      bool mir;
-      const int slot = slot_of(qq, k1s, mir);
-      const int vo = (mir ? 63 - l : l) * 4;
-#pragma unroll
-      for (int k = 0; k < 16; ++k)
-        hw[qq][k] = __builtin_amdgcn_raw_buffer_load_b32(hrs, vo, slot * 4096 + (mir ? (k < 8 ? 7 - k : 23 - k) : k) * 256, 0);
-    }
-  };
   load_mat(ws, MF2, Ma);
   load_mat(ws, MF3, Mb);
-  load_spectrum(ws);
-  // pass 1: both halves of the radix-16 input (n1 < 8, n1 >= 8), accumulators scaled into range
+  // pass 1: both halves of the radix-16 input, accumulators scaled into range
   static_for<8>([&](auto tt) {
     constexpr int TT = tt.value;
     const f32x16 z = {};
@@ -365,8 +308,9 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
   });
   __syncthreads();
 
-  float vm[2] = {0.0f, 0.0f};   // largest |value| pass 2' leaves, per plane
-  auto slab_step = [&](auto itc) {
+  // ---------------- forward: passes 2 and 3 of the wave's slabs, bins written back over each slab
+  uint32_t cf[32];   // coefficients of the next split unit
+  static_for<2>([&](auto itc) {
     constexpr int it = decltype(itc)::value;
     const int k1 = w + NW * it;
     const int k1s = ws + NW * it;
@@ -385,7 +329,8 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
       split8(chi, xr_hi[q], xi_hi[q]);
       dft32<false, true>(Ma, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q], dr[q], di[q]);
     }
-    load_mat(k1s, MI3, Ma);
+    if (it == 0) load_mat(k1s + NW, MF2, Ma);
+    else load_mat(ws, MI3, Ma);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       f16x2 ar[8], ai[8];
@@ -394,36 +339,88 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
       cmul_pairs<false>(ar, ai, pc, ps, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q]);
       dft32<false, false>(Mb, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q], dr[q], di[q]);
     }
-    load_mat(k1s, MI2, Mb);
-    // spectral product, plane by plane (bin k0 + N1 (k1 + 16 j + 512 k3(v)))
+    if (it == 0) {
+      load_mat(k1s + NW, MF3, Mb);
+    } else {
+      load_mat(ws, MI2, Mb);
+      load_coef(0, ws, cf);
+    }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      f16x2 hr[8], hi[8];
+      uint32_t* sl = S + q * PLANE + k1 * SLAB;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        hr[k] = __builtin_bit_cast(f16x2, hw[q][k]);
-        hi[k] = __builtin_bit_cast(f16x2, hw[q][8 + k]);
-      }
-      f16x2 ar[8], ai[8];
-      to_pairs(dr[q], ar);
-      to_pairs(di[q], ai);
-      bool mir;
-      slot_of(q, k1s, mir);
-      if (mir) {
+      for (int v = 0; v < 16; ++v) sl[acc_row(v, h) * ROW + j] = pack2h(dr[q][v], di[q][v]);
+    }
+  });
+  __syncthreads();
+
+  // ---------------- split: units (it, q) = plane q, slab w + 8 it; results kept as pass 3' operands
+  f16x8 zr_lo[2][2], zr_hi[2][2], zi_lo[2][2], zi_hi[2][2];
+  static_for<4>([&](auto uc) {
+    constexpr int U = uc.value, it = U >> 1, q = U & 1;
+    const int k1 = w + NW * it;
+    const int qm = g == 0 ? q : 1 - q;                  // the plane holding the mirrored bins
+    const bool p0 = plane_of(q) == 0, s0 = p0 && k1 == 0;   // (wave-uniform)
+    const int k1m = p0 ? (16 - k1) & 15 : 15 - k1;
+    const int k2m = s0 ? (32 - j) & 31 : 31 - j;
+    const uint32_t* own = S + q * PLANE + k1 * SLAB + j;
+    const uint32_t* mir = S + qm * PLANE + k1m * SLAB + k2m;
+    uint32_t zw[16], mw[16];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          hr[k] = hr[k].yx;
-          hi[k] = hi[k].yx;
-        }
-        cmul_pairs<true>(ar, ai, hr, hi, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q]);
+    for (int v = 0; v < 16; ++v) {
+      const int k3 = acc_row(v, h);
+      const int k3m = (s0 && j == 0) ? (32 - k3) & 31 : 31 - k3;
+      zw[v] = own[k3 * ROW];
+      mw[v] = mir[k3m * ROW];
+    }
+    uint32_t c[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) c[k] = cf[k];
+    if constexpr (U + 1 < 4) load_coef((U + 1) & 1, ws + NW * ((U + 1) >> 1), cf);
+    // pairs of registers (2p, 2p + 1): real parts, imaginary parts
+    u32x4 rl_, rh_, il_, ih_;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const f16x2 zr = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(zw[2 * p + 1], zw[2 * p], 0x05040100u));
+      const f16x2 zi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(zw[2 * p + 1], zw[2 * p], 0x07060302u));
+      const f16x2 mr = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(mw[2 * p + 1], mw[2 * p], 0x05040100u));
+      const f16x2 mi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(mw[2 * p + 1], mw[2 * p], 0x07060302u));
+      const uint32_t c0_ = c[p], c1_ = c[8 + p], c2_ = c[16 + p], c3_ = c[24 + p];
+      const f16x2 ar = __builtin_bit_cast(f16x2, c0_), ai = __builtin_bit_cast(f16x2, c1_);
+      const f16x2 br = __builtin_bit_cast(f16x2, c2_), bi = __builtin_bit_cast(f16x2, c3_);
+      // A Z + B conj(Zm)
+      const f16x2 re = __builtin_elementwise_fma(ar, zr, __builtin_elementwise_fma(-ai, zi,
+                           __builtin_elementwise_fma(br, mr, bi * mi)));
+      const f16x2 im = __builtin_elementwise_fma(ar, zi, __builtin_elementwise_fma(ai, zr,
+                           __builtin_elementwise_fma(bi, mr, -(br * mi))));
+      const uint32_t rb = __builtin_bit_cast(uint32_t, re), ib = __builtin_bit_cast(uint32_t, im);
+      if (p < 4) {
+        rl_[p] = rb;
+        il_[p] = ib;
       } else {
-        cmul_pairs<false>(ar, ai, hr, hi, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q]);
+        rh_[p - 4] = rb;
+        ih_[p - 4] = ib;
       }
     }
-    if (it + 1 < NIT) load_spectrum(k1s + NW);
+    zr_lo[it][q] = as_h(rl_);
+    zr_hi[it][q] = as_h(rh_);
+    zi_lo[it][q] = as_h(il_);
+    zi_hi[it][q] = as_h(ih_);
+  });
+  __syncthreads();
+
+  // ---------------- inverse: passes 3' and 2' of the wave's slabs
+  float vm[2] = {0.0f, 0.0f};   // largest |value| pass 2' leaves, per plane
+  static_for<2>([&](auto itc) {
+    constexpr int it = decltype(itc)::value;
+    const int k1 = w + NW * it;
+    const int k1s = ws + NW * it;
+    f16x8 xr_lo[2], xr_hi[2], xi_lo[2], xi_hi[2];
+    f32x16 dr[2], di[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) dft32<true, true>(Ma, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q], dr[q], di[q]);
-    if (it + 1 < NIT) load_mat(k1s + NW, MF2, Ma);
+    for (int q = 0; q < 2; ++q)
+      dft32<true, true>(Ma, zr_lo[it][q], zr_hi[it][q], zi_lo[it][q], zi_hi[it][q], dr[q], di[q]);
+    if (it == 0) load_mat(k1s + NW, MI3, Ma);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       f16x2 ar[8], ai[8];
@@ -432,7 +429,7 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
       cmul_pairs<true>(ar, ai, pc, ps, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q]);
       dft32<true, false>(Mb, xr_lo[q], xr_hi[q], xi_lo[q], xi_hi[q], dr[q], di[q]);
     }
-    if (it + 1 < NIT) load_mat(k1s + NW, MF3, Mb);
+    if (it == 0) load_mat(k1s + NW, MI2, Mb);
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       uint32_t* sl = S + q * PLANE + k1 * SLAB;
@@ -442,8 +439,7 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
         sl[acc_row(v, h) * ROW + j] = pack2h(dr[q][v], di[q][v]);
       }
     }
-  };
-  static_for<NIT>([&](auto itc) { slab_step(itc); });
+  });
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
 #pragma unroll
@@ -490,50 +486,56 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
     *reinterpret_cast<u32x4*>(Pm + c0 + 1024 * n1) = outR[s];
     *reinterpret_cast<u32x4*>(Pm + N2 + c0 + 1024 * n1) = outI[s];
   }
-  if ((threadIdx.x & 255) == 0) hdr[mfl::H_EB + plane_of(mine)] = (uint32_t)(eo + 10 + eH + E + 16);
+  if ((threadIdx.x & 255) == 0) hdr[mfl::H_EB + plane_of(mine)] = (uint32_t)(eo + 10 + eH + E + 17);
 }
 
-// Spectrum copy of one channel per workgroup from the natural-order bins 0..L of the 2L-point DFT (upper bins
-// by conjugate symmetry): slot s (see Plan) of plane k0, slab k1: word q < 8 of lane l holds the real parts of
-// c H[k(2q)] / N and c H[k(2q + 1)] / N as fp16 (register 2q low), word 8 + q their imaginary parts,
-// k(v) = k0 + N1 (k1 + 16 (l % 32) + 512 k3(v, l / 32)); then the tail, word 0 = log2(1/c).  c is the power of
-// two that brings the channel's largest |H[k]| / N into [0.5, 1).
+// Split coefficients of one channel per workgroup from the natural-order bins 0..L of the 2L-point filter
+// spectrum: for plane k0, slab k1, word wd, lane l: words 0..15 hold A, 16..31 B; word 8 r + p of either
+// holds the real (r = 0) or imaginary (r = 1) parts of c X[k(2p)] / M and c X[k(2p + 1)] / M as fp16 (register
+// 2p low), k(v) = k0 + N1 (k1 + 16 (l % 32) + 512 k3(v, l / 32)); then the tail, word 0 = log2(1/c).  c is the
+// power of two that brings the largest component of A / M and B / M into [0.5, 1).
 template <int N1>
-__global__ void __launch_bounds__(256) k_mfl_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc) {
+__global__ void __launch_bounds__(256) k_mfl_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc,
+                                                      Twiddles tw) {
   using namespace mf;
   using P = mfl::Plan<N1>;
-  constexpr int L = P::L, N = P::N;
+  constexpr int M = P::M;
   __shared__ float red[4];
   const int d = blockIdx.x;
-  const float2* hn = Hnat + (size_t)d * (L + 1);
+  const float2* hn = Hnat + (size_t)d * (M + 1);
+  // A[k], B[k] from H[k] and H[k + M] = conj(H[M - k]) (k >= 1; H[M] itself for k = 0)
+  auto coef = [&](int k, float2& A, float2& Bc) {
+    const float2 h0 = hn[k];
+    const float2 h1 = k == 0 ? hn[M] : cconj(hn[M - k]);
+    const float2 hs = make_float2(0.5f * (h0.x + h1.x), 0.5f * (h0.y + h1.y));
+    const float2 hd = make_float2(0.5f * (h0.x - h1.x), 0.5f * (h0.y - h1.y));
+    const float2 wk = twiddle<P::LOG2M + 1>(tw, uint32_t(k));   // cos(pi k / M) - i sin(pi k / M)
+    const float cs = wk.x, sn = -wk.y;
+    A = make_float2(hs.x - hd.x * sn, hs.y - hd.y * sn);
+    Bc = make_float2(-hd.y * cs, hd.x * cs);
+  };
   float m = 0.0f;
-  for (int k = threadIdx.x; k <= L; k += 256) m = fmaxf(m, fmaxf(fabsf(hn[k].x), fabsf(hn[k].y)));
-  const float c = range_scale(block_max4(m * (1.0f / N), red));
-  const float sc = c * (1.0f / N);
+  for (int k = threadIdx.x; k < M; k += 256) {
+    float2 A, Bc;
+    coef(k, A, Bc);
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(A.x), fabsf(A.y)), fmaxf(fabsf(Bc.x), fabsf(Bc.y))));
+  }
+  const float c = range_scale(block_max4(m * (1.0f / M), red));
+  const float sc = c * (1.0f / M);
   uint32_t* out = Hc + (size_t)d * P::SPEC_WORDS;
-  auto bin = [&](int k) { return k <= L ? hn[k] : cconj(hn[N - k]); };
-  for (int idx = threadIdx.x; idx < P::SLOTS * 1024; idx += 256) {   // (slot, word, lane)
-    const int slot = idx / 1024, wd = (idx / 64) % 16, l = idx % 64;
-    int k0, k1;
-    if (slot < 9) {
-      k0 = 0;
-      k1 = slot;
-    } else if (slot < 17) {
-      k0 = N1 / 2;
-      k1 = slot - 9;
-    } else {
-      k0 = 1 + (slot - 17) / 16;
-      k1 = (slot - 17) % 16;
-    }
-    const int q = wd & 7;
+  for (int idx = threadIdx.x; idx < P::COEF_WORDS; idx += 256) {   // (plane, slab, word, lane)
+    const int l = idx & 63, wd = (idx >> 6) & 31, unit = idx >> 11;
+    const int k0 = unit >> 4, k1 = unit & 15;
+    const int p = wd & 7;
     const int base = k0 + N1 * (k1 + 16 * (l & 31));
-    const float2 a = bin(base + N1 * 512 * acc_row(2 * q, l >> 5));
-    const float2 b = bin(base + N1 * 512 * acc_row(2 * q + 1, l >> 5));
-    out[idx] = wd < 8 ? pack2h(a.x * sc, b.x * sc) : pack2h(a.y * sc, b.y * sc);
+    float2 a0, b0, a1, b1;
+    coef(base + N1 * 512 * acc_row(2 * p, l >> 5), a0, b0);
+    coef(base + N1 * 512 * acc_row(2 * p + 1, l >> 5), a1, b1);
+    const float2 x0 = wd < 16 ? a0 : b0, x1 = wd < 16 ? a1 : b1;
+    out[idx] = (wd & 8) ? pack2h(x0.y * sc, x1.y * sc) : pack2h(x0.x * sc, x1.x * sc);
   }
   if (threadIdx.x < 64)
-    out[P::SLOTS * 1024 + threadIdx.x] =
-        threadIdx.x == 0 ? (uint32_t)(__builtin_amdgcn_frexp_expf(1.0f / c) - 1) : 0u;
+    out[P::COEF_WORDS + threadIdx.x] = threadIdx.x == 0 ? (uint32_t)(__builtin_amdgcn_frexp_expf(1.0f / c) - 1) : 0u;
 }
 
 // ------------------------------------------------------------------ host side
@@ -544,8 +546,8 @@ hipError_t mfl_conv_launch(int order, int B, int D, const void* v, const void* c
                            void* y, uint32_t* W0, int chunk, const void* mats, const Twiddles& tw, hipStream_t s0,
                            const SideStream* side) {
   using P = mfl::Plan<N1>;
-  const int pairs = (B / 2) * D;
-  const int ways = (side != nullptr && pairs > chunk) ? side->ways : 1;
+  const int rows = B * D;
+  const int ways = (side != nullptr && rows > chunk) ? side->ways : 1;
   if (ways > 1) {
     const hipError_t e = side_fork(side, s0);
     if (e != hipSuccess) return e;
@@ -554,26 +556,26 @@ hipError_t mfl_conv_launch(int order, int B, int D, const void* v, const void* c
   const uint16_t* vv = (const uint16_t*)v;
   uint16_t* yy = (uint16_t*)y;
   int k = 0;
-  for (int q0 = 0; q0 < pairs; q0 += chunk, ++k) {
-    const int nq = (pairs - q0 < chunk) ? pairs - q0 : chunk;
+  for (int q0 = 0; q0 < rows; q0 += chunk, ++k) {
+    const int nq = (rows - q0 < chunk) ? rows - q0 : chunk;
     const int j = k % ways;
     const hipStream_t s = j ? side->s[j - 1] : s0;
-    uint32_t* W = W0 + (size_t)j * chunk * P::PAIR_WORDS;
+    uint32_t* W = W0 + (size_t)j * chunk * P::ROW_WORDS;
     const dim3 gc(mfl::NTILE * nq), gp((N1 / 2) * nq);
     hipLaunchKernelGGL((k_mfl_cols<N1, 0, false, false>), gc, dim3(mfl::TC), 0, s, vv, (const uint16_t*)nullptr,
-                       (uint16_t*)nullptr, W, q0, nq, B, D, 0, tw);
+                       (uint16_t*)nullptr, W, q0, nq, B, D, tw);
     for (int i = 0; i < order; ++i) {
       hipLaunchKernelGGL((k_mfl_planes<N1>), gp, dim3(mfl::TP), 0, s, W, (const uint32_t*)spectra[i], mt, q0, nq, B);
       const uint16_t* g = (const uint16_t*)x[i];
       if (i + 1 < order)
         hipLaunchKernelGGL((k_mfl_cols<N1, 1, true, true>), gc, dim3(mfl::TC), 0, s, (const uint16_t*)nullptr, g,
-                           (uint16_t*)nullptr, W, q0, nq, B, D, i & 1, tw);
+                           (uint16_t*)nullptr, W, q0, nq, B, D, tw);
       else if (g)
         hipLaunchKernelGGL((k_mfl_cols<N1, 1, true, false>), gc, dim3(mfl::TC), 0, s, (const uint16_t*)nullptr, g,
-                           yy, W, q0, nq, B, D, i & 1, tw);
+                           yy, W, q0, nq, B, D, tw);
       else
         hipLaunchKernelGGL((k_mfl_cols<N1, 1, false, false>), gc, dim3(mfl::TC), 0, s, (const uint16_t*)nullptr,
-                           (const uint16_t*)nullptr, yy, W, q0, nq, B, D, i & 1, tw);
+                           (const uint16_t*)nullptr, yy, W, q0, nq, B, D, tw);
     }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -583,32 +585,38 @@ hipError_t mfl_conv_launch(int order, int B, int D, const void* v, const void* c
 
 }  // namespace
 
-bool mfl_supported(int log2L, int B) { return (log2L == 15 || log2L == 16) && B % 2 == 0; }
+bool mfl_supported(int log2L) { return log2L >= 15 && log2L <= 17; }
 
-size_t mfl_pair_bytes(int log2L) {
-  return ((size_t)2 << log2L) * 4 + (size_t)mfl::HDR * 4;
-}
+size_t mfl_row_bytes(int log2L) { return (((size_t)1 << log2L) + mfl::HDR) * 4; }
 
 size_t mfl_spectrum_bytes_per_channel(int log2L) {
-  return log2L == 15 ? (size_t)mfl::Plan<4>::SPEC_WORDS * 4 : (size_t)mfl::Plan<8>::SPEC_WORDS * 4;
+  switch (log2L) {
+    case 15: return (size_t)mfl::Plan<2>::SPEC_WORDS * 4;
+    case 16: return (size_t)mfl::Plan<4>::SPEC_WORDS * 4;
+    case 17: return (size_t)mfl::Plan<8>::SPEC_WORDS * 4;
+  }
+  return 0;
 }
 
 hipError_t launch_conv_mfl(int log2L, int order, int B, int D, const void* v, const void* const* x,
-                           const void* const* spectra, void* y, void* ws, int chunk_pairs, const void* mats,
+                           const void* const* spectra, void* y, void* ws, int chunk_rows, const void* mats,
                            const Twiddles& tw, hipStream_t s, const SideStream* side) {
-  if (!mfl_supported(log2L, B) || order < 1 || chunk_pairs < 1) return hipErrorInvalidValue;
-  if (log2L == 15)
-    return mfl_conv_launch<4>(order, B, D, v, x, spectra, y, (uint32_t*)ws, chunk_pairs, mats, tw, s, side);
-  return mfl_conv_launch<8>(order, B, D, v, x, spectra, y, (uint32_t*)ws, chunk_pairs, mats, tw, s, side);
+  if (!mfl_supported(log2L) || order < 1 || chunk_rows < 1) return hipErrorInvalidValue;
+  uint32_t* W = (uint32_t*)ws;
+  switch (log2L) {
+    case 15: return mfl_conv_launch<2>(order, B, D, v, x, spectra, y, W, chunk_rows, mats, tw, s, side);
+    case 16: return mfl_conv_launch<4>(order, B, D, v, x, spectra, y, W, chunk_rows, mats, tw, s, side);
+    default: return mfl_conv_launch<8>(order, B, D, v, x, spectra, y, W, chunk_rows, mats, tw, s, side);
+  }
 }
 
-hipError_t launch_mfl_spectrum(int log2L, const float2* Hnat, void* Hc, int D, hipStream_t s) {
-  if (log2L == 15)
-    hipLaunchKernelGGL(k_mfl_spectrum<4>, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc);
-  else if (log2L == 16)
-    hipLaunchKernelGGL(k_mfl_spectrum<8>, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc);
-  else
-    return hipErrorInvalidValue;
+hipError_t launch_mfl_spectrum(int log2L, const float2* Hnat, void* Hc, int D, const Twiddles& tw, hipStream_t s) {
+  switch (log2L) {
+    case 15: hipLaunchKernelGGL(k_mfl_spectrum<2>, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc, tw); break;
+    case 16: hipLaunchKernelGGL(k_mfl_spectrum<4>, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc, tw); break;
+    case 17: hipLaunchKernelGGL(k_mfl_spectrum<8>, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc, tw); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -96,17 +96,17 @@ hipError_t launch_conv_mfma(const void* u, const void* const* gates, const void*
                             void* y, const void* mats, int B, int D, hipStream_t s);
 hipError_t launch_pair_spectrum(const float2* Hnat, void* Hc, int D, hipStream_t s);
 
-// ---- matrix-core path for long rows: bf16 storage, L = 2^15 or 2^16, rows in pairs of one channel (B even).
-// The workspace holds chunk_pairs pairs of mfl_pair_bytes each (ways * chunk_pairs with side streams);
-// spectra[i] = the long-row matrix-core copies (mfl_spectrum_bytes_per_channel per channel).
-bool mfl_supported(int log2L, int B);
-size_t mfl_pair_bytes(int log2L);
+// ---- matrix-core path for long rows: bf16 storage, L = 2^15, 2^16 or 2^17, each row alone (any B).
+// The workspace holds chunk_rows rows of mfl_row_bytes each (ways * chunk_rows with side streams);
+// spectra[i] = the long-row split-coefficient copies (mfl_spectrum_bytes_per_channel per channel).
+bool mfl_supported(int log2L);
+size_t mfl_row_bytes(int log2L);
 size_t mfl_spectrum_bytes_per_channel(int log2L);
 hipError_t launch_conv_mfl(int log2L, int order, int B, int D, const void* v, const void* const* x,
-                           const void* const* spectra, void* y, void* ws, int chunk_pairs, const void* mats,
+                           const void* const* spectra, void* y, void* ws, int chunk_rows, const void* mats,
                            const Twiddles& tw, hipStream_t s, const SideStream* side = nullptr);
 // from the natural-order bins 0..L of each channel's 2L-point spectrum ([D][L + 1])
-hipError_t launch_mfl_spectrum(int log2L, const float2* Hnat, void* Hc, int D, hipStream_t s);
+hipError_t launch_mfl_spectrum(int log2L, const float2* Hnat, void* Hc, int D, const Twiddles& tw, hipStream_t s);
 
 // ---- implicit filter taps
 struct FilterArgs {

@@ -78,12 +78,13 @@ def test_size_queries(lib):
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([1 << 16]), L.CIRCULAR, 2)
     assert st == 0 and n == 2 * (1 << 15) * 8               # fp32 spectrum (every plan keeps fp32 intermediates)
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([65536]), L.CAUSAL, 3)
-    # fp32 spectrum, then the long-row matrix-core copy: 65 slots of 4 KB and a 256-byte tail per channel
-    assert st == 0 and n == 3 * 65536 * 8 + 3 * (65 * 4096 + 256)
-    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([32768]), L.CAUSAL, 3)
-    assert st == 0 and n == 3 * 32768 * 8 + 3 * (33 * 4096 + 256)
-    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([1 << 17]), L.CAUSAL, 3)
-    assert st == 0 and n == 3 * (1 << 17) * 8
+    # fp32 spectrum, then the long-row matrix-core split coefficients: two fp16 complex values per packed
+    # bin (L of them) and a 256-byte tail per channel
+    for Lc in (1 << 15, 1 << 16, 1 << 17):
+        st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([Lc]), L.CAUSAL, 3)
+        assert st == 0 and n == 3 * Lc * 8 + 3 * (Lc * 8 + 256)
+    st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([1 << 18]), L.CAUSAL, 3)
+    assert st == 0 and n == 3 * (1 << 18) * 8
     # periodic 3-D: 64 x 64 x 33 bins per channel, intermediate 64 x-slabs of 64 x 33 per volume
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.CIRCULAR, 128)
     assert st == 0 and n == 128 * 64 * 64 * 33 * 8

@@ -127,8 +127,9 @@ def test_operator_f32_B1_D256_L1M_dna_all_rows(torch_cuda):
 
 @pytest.mark.parametrize("L", [1 << 15, 1 << 16, 1 << 17, 1 << 20])
 def test_fourstep_fftconv_bf16_chunked(torch_cuda, L):
-    """bf16 storage (the intermediate is block-scaled fp16), two chunks of which one is ragged, every
-    multi-pass plan family; against the oracle on the bf16-rounded inputs."""
+    """bf16 storage (the intermediate is block-scaled fp16), five rows in chunks of two, two and one on two
+    streams (a workspace sized for four rows), every multi-pass plan family (the long-row matrix-core kernels up
+    to 2^17 samples, the vector-unit plan above); against the oracle on the bf16-rounded inputs."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
     B, D = 1, 5
@@ -139,7 +140,7 @@ def test_fourstep_fftconv_bf16_chunked(torch_cuda, L):
     p = hi.draw_filter_params(w, seed=5)[0]
     say(f"four-step fftconv bf16 L={L}")
     spec = hy.filter_gen(params_to_dev(p), (L,))
-    ws = torch.empty(3 * L * 8, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(hy.workspace_bytes(1, 1, 4, (L,), hy.BF16), dtype=torch.uint8, device="cuda")
     y = hy.operator(u.cuda(), [g.cuda()], [spec], ws=ws)
     torch.cuda.synchronize()
     h = orc.implicit_filter_1d(p, L)

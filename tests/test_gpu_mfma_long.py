@@ -1,5 +1,5 @@
-"""The long-row matrix-core kernels (bf16 storage, L = 2^15 and 2^16, rows of one channel in pairs): against
-the oracle, chunking and streams, routing, zero rows, the allocation-free entry point."""
+"""The long-row matrix-core kernels (bf16 storage, L = 2^15 .. 2^17, every row packed on its own): against the
+oracle, rows of very different magnitudes, chunking and streams, routing, the allocation-free entry point."""
 import numpy as np
 import pytest
 
@@ -23,12 +23,12 @@ def _bf16_inputs(torch, rng, shape):
     return torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(torch.bfloat16)
 
 
-@pytest.mark.parametrize("L", [1 << 15, 1 << 16])
-@pytest.mark.parametrize("B", [2, 4])
+@pytest.mark.parametrize("L", [1 << 15, 1 << 16, 1 << 17])
+@pytest.mark.parametrize("B", [1, 2, 3])
 @pytest.mark.parametrize("gate", [False, True])
 def test_long_fftconv(torch_cuda, L, B, gate):
     """hyena_fftconv, one order, with and without a gate: every row against the oracle's causal convolution of
-    the bf16-rounded inputs (several row pairs of a channel when B = 4)."""
+    the bf16-rounded inputs."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
     D = 3
@@ -51,7 +51,7 @@ def test_long_fftconv(torch_cuda, L, B, gate):
     assert e.max() < BF16_TOL
 
 
-@pytest.mark.parametrize("L", [1 << 15, 1 << 16])
+@pytest.mark.parametrize("L", [1 << 15, 1 << 16, 1 << 17])
 @pytest.mark.parametrize("order", [2, 3])
 @pytest.mark.parametrize("decay", ["none", "slow"])
 def test_long_operator_orders(torch_cuda, L, order, decay):
@@ -71,9 +71,9 @@ def test_long_operator_orders(torch_cuda, L, order, decay):
 
 
 def test_long_chunks_and_streams(torch_cuda):
-    """Five row pairs run as one chunk, as five chunks of one pair (a workspace that holds one), and as chunks
-    of two, two and one pair cycling over two streams (a workspace that holds four): bitwise equal, since no
-    pair's arithmetic depends on its chunk."""
+    """Ten rows run as one chunk, as chunks of one row cycling over two streams (a workspace sized for two
+    rows), and as chunks of four, four and two rows over two streams (a workspace sized for eight): bitwise
+    equal, since no row's arithmetic depends on its chunk."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
     L, B, D, order = 1 << 15, 2, 5, 3
@@ -98,37 +98,50 @@ def test_long_chunks_and_streams(torch_cuda):
     assert e.max() < BF16_TOL
 
 
-def test_long_zero_rows_in_pairs(torch_cuda):
-    """A row whose input is all zeros gives exact zeros even though its pair partner is not zero (the column
-    pass keeps per row whether any input is non-zero); the partners stay within the tolerance."""
+def test_long_rows_of_very_different_magnitudes(torch_cuda):
+    """Every row is transformed on its own with its own power-of-two block scales: in one channel, rows scaled
+    by 2^-50 and 2^40, a single impulse and an all-zero row each stay within the tolerance of the oracle (the
+    zero row gives exact zeros), and a NaN in one row leaves every other row bitwise unchanged."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
-    L, B, D = 1 << 16, 2, 3
+    L, B, D = 1 << 16, 5, 2
     w = hi.WORKLOADS[2].with_(B=B, D=D, dims=(L,), order=2)
     v, xs = hi.draw_activations(w, seed=61)
-    v[1, 1] = 0.0
-    v[0, 2] = 0.0
+    v[0, 1] *= 2.0 ** -50
+    v[1, 1] *= 2.0 ** 40
+    v[2, 1] = 0.0
+    v[2, 1, L // 3] = 3.0
+    v[3, 1] = 0.0
     params = hi.draw_filter_params(w, seed=61)
-    say("long-row matrix cores: zero rows paired with non-zero rows")
+    say("long-row matrix cores: rows 2^-50 .. 2^40, an impulse and a zero row in one channel")
     spectra = [hy.filter_gen(params_to_dev(p), (L,)) for p in params]
     vd = to_dev(v, torch.bfloat16)
     xd = [to_dev(x, torch.bfloat16) for x in xs]
     y = hy.operator(vd, xd, spectra)
     torch.cuda.synchronize()
-    assert torch.count_nonzero(y[1, 1]).item() == 0
-    assert torch.count_nonzero(y[0, 2]).item() == 0
-    yh = y.float().cpu().numpy()
-    e = all_row_errors(w, v, xs, params, yh)
-    keep = [i for i in range(B * D) if i not in (1 * D + 1, 0 * D + 2)]
-    report_errors("zero rows' partners", e[keep])
+    assert torch.count_nonzero(y[3, 1]).item() == 0
+    vr = vd.float().cpu().numpy()
+    xr = [x.float().cpu().numpy() for x in xd]
+    e = all_row_errors(w, vr, xr, params, y.float().cpu().numpy())
+    zero = 3 * D + 1
+    keep = [i for i in range(B * D) if i != zero]
+    report_errors("rows of very different magnitudes", e[keep])
     assert e[keep].max() < BF16_TOL
+    vn = vd.clone()
+    vn[4, 0, L // 2] = float("nan")
+    yn = hy.operator(vn, xd, spectra)
+    torch.cuda.synchronize()
+    assert torch.isnan(yn[4, 0]).any()
+    yf, ynf = y.reshape(B * D, L), yn.reshape(B * D, L)
+    others = [i for i in range(B * D) if i != 4 * D + 0]
+    assert torch.equal(ynf[others], yf[others])
 
 
 def test_long_routing(torch_cuda):
-    """Which plan a bf16 call at L = 65536 with B = 2 takes: orders up to 3 with 8-byte-aligned activations take
-    the long-row matrix-core kernels, so they differ from the same call with a misaligned v (the per-row plan),
-    both within the tolerance of each other; order 4 takes the per-row plan whatever the alignment (bitwise
-    equal)."""
+    """Which plan a bf16 call at L = 65536 takes: orders up to 3 with 16-byte-aligned activations take the
+    long-row matrix-core kernels, so they differ from the same call with a misaligned v (the vector-unit
+    multi-pass plan), both within the tolerance of each other; order 4 takes the vector-unit plan whatever
+    the alignment (bitwise equal)."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
     L = 1 << 16
@@ -143,7 +156,7 @@ def test_long_routing(torch_cuda):
         buf = torch.empty(v.size + 1, dtype=torch.bfloat16, device="cuda")
         vm = buf[1:].view(v.shape)
         vm.copy_(vd)
-        assert vm.data_ptr() % 8 != 0
+        assert vm.data_ptr() % 16 != 0
         ym = hy.operator(vm, xd, spectra)
         torch.cuda.synchronize()
         say(f"routing order {order}")
