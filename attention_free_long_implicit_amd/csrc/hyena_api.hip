@@ -235,7 +235,12 @@ int pair_chunk(size_t per, int64_t rows, size_t ws_bytes, int* ways) {
     if (c > want) c = want;
     if (rows > c) *ways = w;
   }
-  return (int)(c < rows ? c : rows);
+  if (c >= rows) return (int)rows;
+  // equal chunks, their number a multiple of the streams (never larger than c): no nearly empty last
+  // chunk running alone at the end
+  int64_t n = (rows + c - 1) / c;
+  n = (n + *ways - 1) / *ways * *ways;
+  return (int)((rows + n - 1) / n);
 }
 
 // Channels per chunk while building spectra from taps: about 1 GB of intermediate.  Nothing is reused

@@ -10,11 +10,13 @@
 // Precision: every operand after the first product is fp16 (11-bit significand), not bf16 (8 bits):
 // the products cost the same on the matrix cores, and eight times finer rounding keeps the order-2
 // result well inside the bf16-storage tolerance even without a decay window (bf16 operands measured
-// up to 1.96e-2 of the 2e-2 allowed).  fp16's range is kept by exact power-of-two scaling: each order's
-// input is scaled so that its largest magnitude in the row pair lies in [0.5, 1), the filter spectrum
-// so that its largest bin does, and the inverse radix-32 matrices carry a factor 1/32 each, so no
-// intermediate exceeds 2^13; the output is scaled back in fp32 before the gate.  The first product of
-// the first order reads the bf16 inputs exactly, against a matrix split into two bf16 parts (hi + lo).
+// up to 1.96e-2 of the 2e-2 allowed).  fp16's range is kept by exact power-of-two scaling: each row of each
+// order's input is scaled so that its largest magnitude lies in [0.5, 1) (one scale per row, not per pair:
+// the transform mixes the two rows, and a row far smaller than its partner would otherwise be resolved only
+// to the partner's rounding level), the filter spectrum so that its largest bin does, and the inverse
+// radix-32 matrices carry a factor 1/32 each, so no intermediate exceeds 2^13; the output is scaled back in
+// fp32 before the gate, and a row that is all zeros gives exact zeros.  The first product of the first order
+// reads the bf16 inputs exactly, against a matrix split into two bf16 parts (hi + lo) times the row scales.
 // The two elementwise steps between products (the twiddle W_1024 and the spectral product) take the
 // accumulators rounded to fp16 and multiply them in packed fp16 arithmetic, two complex values per
 // instruction, with twiddles and spectrum already stored as fp16 pairs; the result is the next product's
@@ -76,7 +78,7 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
   constexpr int NW = 4 * NP;        // waves; wave w owns slabs k1 = w + NW it, it < NIT
   constexpr int NIT = 16 / NW;
   __shared__ uint32_t S[NP * PLANE];
-  __shared__ float red[NW];
+  __shared__ float red[2 * NW];
   const int ngrp = (B >> 1) / NP;   // workgroups per channel
   const int r = xcd_logical_block(blockIdx.x, D * ngrp);
   const int d = r / ngrp;
@@ -116,9 +118,13 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
       ps[4 + q] = __builtin_bit_cast(f16x2, f);
     }
   }
-  // scale of the first order's input: the largest |u| of the row pair (bf16 magnitudes compare as
-  // integers), brought into [0.5, 1)
-  float s_in;
+  // Scales of the first order's input, one per row: each row's largest |u| (bf16 magnitudes compare as
+  // integers) brought into [0.5, 1), so that each row of the pair keeps its own range (the transform mixes
+  // the two rows: with one scale for both, a row much smaller than its partner would be resolved only to
+  // the partner's rounding level).  The row scale of lane half h goes into the first product's matrix: its
+  // lanes h carry the inputs K = 8h .. 8h + 7 of row h, and the bf16 parts times a power of two stay exact.
+  // A row that is all zeros gives exact zeros (its scale back is 0).
+  float s0, s1, k0, k1;   // row scales; 1, or 0 for a row that is all zeros
   {
     uint32_t m = 0;
 #pragma unroll
@@ -128,7 +134,18 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
         const uint32_t w = V[e][q] & 0x7fff7fffu;
         m = max(m, max(w & 0xffffu, w >> 16));
       }
-    s_in = range_scale(block_max4(__uint_as_float(m << 16), red));
+    float m0, m1;
+    block_max4_rows(__uint_as_float(m << 16), red, m0, m1);
+    s0 = range_scale(m0);
+    s1 = range_scale(m1);
+    k0 = m0 != 0.0f ? 1.0f : 0.0f;
+    k1 = m1 != 0.0f ? 1.0f : 0.0f;
+    const float sl = (l0 >> 5) ? s1 : s0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      m1a[q] = pack2(lo_f32(m1a[q]) * sl, hi_f32(m1a[q]) * sl);
+      m1b[q] = pack2(lo_f32(m1b[q]) * sl, hi_f32(m1b[q]) * sl);
+    }
   }
 
   for (int ord = 0; ord < ch.order; ++ord) {
@@ -142,7 +159,8 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
   const uint32_t* __restrict__ Hc = ch.spectrum[ord] + (size_t)d * PAIR_STRIDE;
   const __bf16* gate = ch.gate[ord];
   // scales back: the inverse matrices' 1/1024, the spectrum's normalisation, the input's scale
-  const float f_out = INV_SCALE * __builtin_bit_cast(float, Hc[PAIR_WORDS]) / s_in;
+  const float f_h = INV_SCALE * __builtin_bit_cast(float, Hc[PAIR_WORDS]);
+  const float f_out0 = f_h * k0 / s0, f_out1 = f_h * k1 / s1;
 
   // Slab matrices rotate through two buffers, each load issued one pass before its use:
   // Ma = pass 2, Mb = pass 3, then Ma = pass 3', Mb = pass 2', then the next slab's pass 2 and 3.
@@ -181,27 +199,24 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
   load_mat(ws, MF2, Ma);
   load_mat(ws, MF3, Mb);
   load_spectrum(ws);
-  // pass 1.  First order: the bf16 inputs exactly, against the forward matrix in two bf16 parts; the
-  // accumulators are scaled into fp16's range as they are rounded.  Later orders: the scaled fp16 input
-  // against the fp16 matrix.
+  // pass 1.  First order: the bf16 inputs exactly, against the forward matrix in two bf16 parts (scaled by
+  // the row scales).  Later orders: the scaled fp16 input against the fp16 matrix.
   auto pass1 = [&](auto first) {
     static_for<8>([&](auto tt) {
       constexpr int TT = tt.value;
       const f32x16 z = {};
       f32x16 D1;
-      float sc = 1.0f;
       if constexpr (decltype(first)::value) {
         const bf16x8 col = as_b(column8<TT>(V));
         D1 = mfma(as_b(m1a), col, z);
         D1 = mfma(as_b(m1b), col, D1);
-        sc = s_in;
       } else {
         D1 = mfma(as_h(m1a), as_h(column8<TT>(V)), z);
       }
       // rows k1 = acc_row(e, h): real part in D1[e], imaginary part in D1[8 + e]
 #pragma unroll
       for (int e = 0; e < 8; ++e)
-        Sm[acc_row(e, h) * SLAB + n2c * ROW + n3c + TT] = pack2h(D1[e] * sc, D1[8 + e] * sc);
+        Sm[acc_row(e, h) * SLAB + n2c * ROW + n3c + TT] = pack2h(D1[e], D1[8 + e]);
     });
   };
   if (ord == 0) pass1(std::true_type{});
@@ -321,7 +336,7 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
   {
     const bool last = ord + 1 == ch.order;
     float yv[2][4][8];   // [row][e][tile], fp32: the output, or the next order's input
-    float vmax = 0.0f;
+    float vmax0 = 0.0f, vmax1 = 0.0f;
     // the tiles, and (when another order follows) the largest |value| for its input scale
     auto tiles = [&](auto chain) {
     static_for<8>([&](auto tt) {
@@ -337,14 +352,17 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
       // rows 4h + e (e < 4): real part (row b0) in o[e], imaginary part (row b1) in o[8 + e]
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        float a = o[e], b = o[8 + e];   // times f_out (a power of two) is the result
+        float a = o[e], b = o[8 + e];   // times f_out0 / f_out1 (powers of two, or 0) is the result
         if (GATE) {
           a *= elem_f32<TT>(G[0][e]);
           b *= elem_f32<TT>(G[1][e]);
         }
         yv[0][e][TT] = a;
         yv[1][e][TT] = b;
-        if constexpr (decltype(chain)::value) vmax = fmaxf(vmax, fmaxf(fabsf(a), fabsf(b)));
+        if constexpr (decltype(chain)::value) {
+          vmax0 = fmaxf(vmax0, fabsf(a));
+          vmax1 = fmaxf(vmax1, fabsf(b));
+        }
       }
     });
     };
@@ -357,30 +375,36 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
         u32x4 Y0, Y1;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          Y0[q] = pack2(yv[0][e][2 * q] * f_out, yv[0][e][2 * q + 1] * f_out);
-          Y1[q] = pack2(yv[1][e][2 * q] * f_out, yv[1][e][2 * q + 1] * f_out);
+          Y0[q] = pack2(yv[0][e][2 * q] * f_out0, yv[0][e][2 * q + 1] * f_out0);
+          Y1[q] = pack2(yv[1][e][2 * q] * f_out1, yv[1][e][2 * q + 1] * f_out1);
         }
         *reinterpret_cast<u32x4*>(y0 + 1024 * (4 * h + e)) = Y0;
         *reinterpret_cast<u32x4*>(y1 + 1024 * (4 * h + e)) = Y1;
       }
     } else {
       tiles(std::true_type{});
-      // u_i stays on chip: the next order's input, scaled into fp16's range by its own row-pair maximum
-      // (the barrier inside block_max4 also keeps the next pass 1 from writing LDS this pass still reads).
+      // u_i stays on chip: the next order's input, each row scaled into fp16's range by its own maximum
+      // (the barrier inside block_max4x2 also keeps the next pass 1 from writing LDS this pass still reads).
       // Pass 1' left lane (j, h) with rows b0, b1 at n1 = 4h + e; the next pass 1 wants row b_h at
       // n1 = 0..7 in lane (j, h).  One cross-half swap per register does it: swapping the upper half of the
       // row-b0 register with the lower half of the row-b1 register leaves [b0 from lanes 0..31, b1 from
       // lanes 0..31] (n1 = e) in the first and [b0 from lanes 32..63, b1 from lanes 32..63] (n1 = 4 + e) in
       // the second.
       m1a = mats[M1F_H * 64 + l0];
-      s_in = range_scale(block_max4(vmax, red) * f_out);
-      const float c = f_out * s_in;    // a power of two: u_i scaled into [0.5, 1) in one exact product
+      float m0, m1;
+      block_max4x2(vmax0 * f_out0, vmax1 * f_out1, red, m0, m1);
+      s0 = range_scale(m0);
+      s1 = range_scale(m1);
+      k0 = m0 != 0.0f ? 1.0f : 0.0f;
+      k1 = m1 != 0.0f ? 1.0f : 0.0f;
+      // powers of two: each row of u_i scaled into [0.5, 1) in one exact product
+      const float c0 = f_out0 * s0, c1 = f_out1 * s1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t a = pack2h(yv[0][e][2 * q] * c, yv[0][e][2 * q + 1] * c);
-          const uint32_t b = pack2h(yv[1][e][2 * q] * c, yv[1][e][2 * q + 1] * c);
+          const uint32_t a = pack2h(yv[0][e][2 * q] * c0, yv[0][e][2 * q + 1] * c0);
+          const uint32_t b = pack2h(yv[1][e][2 * q] * c1, yv[1][e][2 * q + 1] * c1);
           const auto rr = __builtin_amdgcn_permlane32_swap(a, b, false, false);
           V[e][q] = rr[0];
           V[4 + e][q] = rr[1];

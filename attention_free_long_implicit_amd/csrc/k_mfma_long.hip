@@ -523,16 +523,19 @@ __global__ void __launch_bounds__(256) k_mfl_spectrum(const float2* __restrict__
   const float c = range_scale(block_max4(m * (1.0f / M), red));
   const float sc = c * (1.0f / M);
   uint32_t* out = Hc + (size_t)d * P::SPEC_WORDS;
-  for (int idx = threadIdx.x; idx < P::COEF_WORDS; idx += 256) {   // (plane, slab, word, lane)
-    const int l = idx & 63, wd = (idx >> 6) & 31, unit = idx >> 11;
+  // one thread per (plane and slab, register pair p, lane): the two bins' A and B, four words
+  for (int idx = threadIdx.x; idx < N1 * 16 * 8 * 64; idx += 256) {
+    const int l = idx & 63, p = (idx >> 6) & 7, unit = idx >> 9;
     const int k0 = unit >> 4, k1 = unit & 15;
-    const int p = wd & 7;
     const int base = k0 + N1 * (k1 + 16 * (l & 31));
     float2 a0, b0, a1, b1;
     coef(base + N1 * 512 * acc_row(2 * p, l >> 5), a0, b0);
     coef(base + N1 * 512 * acc_row(2 * p + 1, l >> 5), a1, b1);
-    const float2 x0 = wd < 16 ? a0 : b0, x1 = wd < 16 ? a1 : b1;
-    out[idx] = (wd & 8) ? pack2h(x0.y * sc, x1.y * sc) : pack2h(x0.x * sc, x1.x * sc);
+    uint32_t* o = out + (size_t)unit * 2048 + l;
+    o[p * 64] = pack2h(a0.x * sc, a1.x * sc);
+    o[(8 + p) * 64] = pack2h(a0.y * sc, a1.y * sc);
+    o[(16 + p) * 64] = pack2h(b0.x * sc, b1.x * sc);
+    o[(24 + p) * 64] = pack2h(b0.y * sc, b1.y * sc);
   }
   if (threadIdx.x < 64)
     out[P::COEF_WORDS + threadIdx.x] = threadIdx.x == 0 ? (uint32_t)(__builtin_amdgcn_frexp_expf(1.0f / c) - 1) : 0u;

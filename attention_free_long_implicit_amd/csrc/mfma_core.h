@@ -78,6 +78,34 @@ __device__ __forceinline__ float block_max4(float v, float* red) {
   return fmaxf(fmaxf(g[0], g[1]), fmaxf(g[2], g[3]));
 }
 
+// Largest values per row over this thread's group of four waves (waves 4g..4g+3), for data whose lanes
+// carry row h = lane / 32 (v) or both rows (v0, v1); red: two floats of LDS per wave of the workgroup.
+// Every thread receives both rows' results.  The caller's next barrier must not be this one's.
+__device__ __forceinline__ void block_max4_rows(float v, float* red, float& m0, float& m1) {
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  if ((threadIdx.x & 31) == 0) red[2 * (threadIdx.x >> 6) + ((threadIdx.x >> 5) & 1)] = v;
+  __syncthreads();
+  const float* g = red + 8 * (threadIdx.x >> 8);
+  m0 = fmaxf(fmaxf(g[0], g[2]), fmaxf(g[4], g[6]));
+  m1 = fmaxf(fmaxf(g[1], g[3]), fmaxf(g[5], g[7]));
+}
+__device__ __forceinline__ void block_max4x2(float v0, float v1, float* red, float& m0, float& m1) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    v0 = fmaxf(v0, __shfl_xor(v0, o));
+    v1 = fmaxf(v1, __shfl_xor(v1, o));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[2 * (threadIdx.x >> 6)] = v0;
+    red[2 * (threadIdx.x >> 6) + 1] = v1;
+  }
+  __syncthreads();
+  const float* g = red + 8 * (threadIdx.x >> 8);
+  m0 = fmaxf(fmaxf(g[0], g[2]), fmaxf(g[4], g[6]));
+  m1 = fmaxf(fmaxf(g[1], g[3]), fmaxf(g[5], g[7]));
+}
+
 // output row of accumulator register v for lane half h (32x32 MFMA layout)
 __device__ __forceinline__ int acc_row(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
 

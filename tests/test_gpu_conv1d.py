@@ -326,6 +326,37 @@ def test_matrix_core_fftconv(torch_cuda, B, gate):
     assert e.max() < BF16_TOL
 
 
+@pytest.mark.parametrize("B", [2, 4])
+def test_matrix_core_rows_of_very_different_magnitudes(torch_cuda, B):
+    """The matrix-core kernel transforms two rows of a channel together, each with its own power-of-two scale:
+    rows 2^-50 and 2^40 in one pair, a zero row paired with a normal one (exact zeros), and a normal row paired
+    with a single impulse each stay within the tolerance of the oracle."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L, D = 8192, 4
+    w = hi.WORKLOADS[1].with_(B=B, D=D, order=2)
+    v, xs = hi.draw_activations(w, seed=44 + B)
+    v[0, 0] *= 2.0 ** -50
+    v[1, 0] *= 2.0 ** 40
+    v[0, 1] = 0.0
+    v[1, 2] = 0.0
+    v[1, 2, L // 3] = 3.0
+    params = hi.draw_filter_params(w, seed=44 + B)
+    say(f"matrix cores, rows of very different magnitudes in a pair, B={B}")
+    spectra = [hy.filter_gen(params_to_dev(p), w.dims) for p in params]
+    vd = to_dev(v, torch.bfloat16)
+    xd = [to_dev(x, torch.bfloat16) for x in xs]
+    y = hy.operator(vd, xd, spectra)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y[0, 1]).item() == 0
+    vr = vd.float().cpu().numpy()
+    xr = [x.float().cpu().numpy() for x in xd]
+    e = all_row_errors(w, vr, xr, params, y.float().cpu().numpy())
+    keep = [i for i in range(B * D) if i != 1]
+    report_errors("rows of very different magnitudes", e[keep])
+    assert e[keep].max() < BF16_TOL
+
+
 @pytest.mark.parametrize("order,B", [(1, 4), (3, 4), (2, 8), (3, 6)])
 def test_matrix_core_workgroup_forms(torch_cuda, order, B):
     """The matrix-core kernel takes two row pairs of a channel per workgroup when B / 2 is even (B = 4, 8) and
