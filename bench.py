@@ -59,6 +59,13 @@ def uses_matrix_cores(w) -> bool:
             and w.filter != "film" and w.order <= 3)
 
 
+def uses_long_matrix_cores(w) -> bool:
+    """Causal, bf16 storage, L = 2^15 .. 2^17, order <= 3: the library's long-row matrix-core kernels (column
+    passes on the vector units, 16384-point planes on the matrix cores)."""
+    return (w.ndim == 1 and w.mode == "causal" and w.dtype == "bf16" and w.dims[0] in (1 << 15, 1 << 16, 1 << 17)
+            and w.filter != "film" and w.order <= 3)
+
+
 def single_launch_per_order(w) -> bool:
     """1-D lengths whose transform fits one workgroup: one fused kernel per order."""
     return w.ndim == 1 and (w.dims[0] <= 16384 or w.mode == "circular")
@@ -71,6 +78,8 @@ def kernel_key(w) -> str:
     L = w.dims[0]
     if uses_matrix_cores(w):
         return f"conv_mfma_L{L}_bf16_pairs"
+    if uses_long_matrix_cores(w):
+        return f"mfma_long_L{L}_bf16"
     return f"conv1d_L{L}_{w.dtype}_gate{circ}" if single_launch_per_order(w) else f"fourstep_L{L}_{w.dtype}"
 
 
@@ -79,6 +88,12 @@ def arithmetic(w) -> str:
         return ("matrix-core DFT steps on fp16 operands (DFT matrices, spectrum copy and transform data rounded to "
                 "fp16 after exact power-of-two range scaling; the first product reads the bf16 input exactly), "
                 "fp32 accumulation; twiddle and spectral products in packed fp16; u_1 passes between the orders in fp16")
+    if uses_long_matrix_cores(w):
+        return ("column passes in fp32; 16384-point plane transforms on the matrix cores with fp16 operands and "
+                "fp32 accumulation; planes stored between passes as fp16 with power-of-two block scales; split "
+                "coefficients fp16, twiddle / split / spectral products in packed fp16; u_i between orders in fp32")
+    if w.dtype == "bf16" and not single_launch_per_order(w) and w.ndim == 1:
+        return "fp32; transform intermediate stored between passes as fp16 with power-of-two block scales"
     if w.dtype == "bf16":
         return "fp32 (bf16 only for the stored v, x_i and y)"
     return "fp32"

@@ -25,19 +25,26 @@
  *   - Activations are channel-major and contiguous: [B, D, L] (1-D) or [B, D, nx, ny, nz] (3-D),
  *     element type given by hyena_dtype.  bf16 is a storage type only: v, the gates and y are bf16 (stores
  *     round to nearest even); the intermediates u_i of the recurrence stay fp32, and so does every transform
- *     intermediate except two: the matrix-core path's operands (below) and, with bf16 storage, the
+ *     intermediate except two: the matrix-core paths' operands (below) and, with bf16 storage, the
  *     multi-pass 1-D plans' workspace, held as fp16 with a power-of-two scale per block of values (each
- *     block's largest component in [2^14, 2^15); 1.7e-3 -> 2.6e-3 on the order-3, 65536-sample workload).
+ *     block's largest component at most 2^15; 1.7e-3 -> 2.6e-3 on the order-3, 65536-sample workload with the
+ *     fp32 transforms).
  *   - Arithmetic: fp32 on every path (radix butterflies on the vector units, fp32 twiddles, fp32 spectra and
- *     spectral products), with one exception, the matrix-core path of hyena_fftconv / hyena_operator (bf16
- *     storage, causal L = 8192, even B, order <= 3): its DFT steps are matrix products with fp32
- *     accumulation whose operands are fp16 -- the DFT matrices, a copy of the filter spectrum and the data
- *     entering each product are rounded to fp16 after an exact power-of-two scaling that keeps them in fp16's
- *     range -- except the first product, which takes the bf16 inputs exactly against a matrix split into two
- *     bf16 parts; u_i passes between orders in fp16 the same way; the twiddle and spectral products between
- *     the matrix products are packed fp16 multiplies.  Its measured error against an fp64 evaluation
- *     (relative L2 per row, max over rows) is 2.8e-3 at order 2 on the 8192-sample workload and at most
- *     4.9e-3 at order 3, against 1.7e-3 to 2e-3 for the fp32 paths with bf16 storage.
+ *     spectral products), with two exceptions, the matrix-core paths of hyena_fftconv / hyena_operator with
+ *     bf16 storage and order <= 3: causal L = 8192 with even B (rows b and b+1 of a channel transformed
+ *     together, each with its own scale), and causal L = 2^15, 2^16, 2^17 (each row on its own; column
+ *     passes in fp32, 16384-point plane transforms on the matrix cores).  Their DFT steps are matrix products
+ *     with fp32 accumulation whose operands are fp16 -- the DFT matrices, a copy of the filter spectrum (for
+ *     the long rows, two split coefficients per bin) and the data entering each product are rounded to fp16
+ *     after an exact power-of-two scaling that keeps them in fp16's range -- except the first product at
+ *     L = 8192, which takes the bf16 inputs exactly against a matrix split into two bf16 parts; at L = 8192
+ *     u_i passes between orders in fp16 the same way; the twiddle, split and spectral products between the
+ *     matrix products are packed fp16 multiplies.  Measured error against an fp64 evaluation (relative L2
+ *     per row, max over rows): 3.2e-3 at order 2 on the 8192-sample workload, 4.9e-3 at order 3 on the
+ *     65536-sample workload, at most 4.9e-3 at order 3 without a decay window, against 1.7e-3 to 2e-3 for the
+ *     fp32 paths with bf16 storage.  At L = 8192 the two rows of a pair share the transform's rounding: a row
+ *     holding a single impulse beside a full row measured 1.0e-2, and a non-finite value in one row makes
+ *     its partner's output non-finite too.
  *   - Calls are asynchronous on the caller's HIP stream and never synchronise the host, except the
  *     first call on a device, which uploads the library's constant tables (about 800 KB) once with a
  *     blocking copy; hyena_init() does that upload ahead of time (for example before graph capture).
@@ -99,8 +106,9 @@ typedef struct {
 } hyena_filter_params;
 
 /* Size in bytes of one order's filter spectrum for D channels (an opaque, engine-ordered array):
- * causal 8L bytes per channel (for L = 8192 followed by an fp16 copy laid out for the matrix-core
- * kernel, 36.25 KB per channel, except with HYENA_PER_SAMPLE); periodic 1-D 4L bytes per channel; 3-D
+ * causal 8L bytes per channel (except with HYENA_PER_SAMPLE, followed for L = 8192 by an fp16 copy laid out
+ * for the matrix-core kernel, 36.25 KB per channel, and for L = 2^15 .. 2^17 by the long-row matrix-core
+ * kernels' fp16 split coefficients, 8L + 256 bytes per channel); periodic 1-D 4L bytes per channel; 3-D
  * 128*128*65*8 bytes per channel (zero-padded) or 64*64*33*8 (periodic).  With HYENA_PER_SAMPLE, D counts
  * filters (B*D). */
 int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t *bytes);
@@ -118,7 +126,8 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
  * offset + n/2) when h_time is not NULL, and the filter spectrum into `spectrum`
  * (hyena_spectrum_bytes bytes).  ws/ws_bytes: scratch of hyena_filter_workspace_bytes bytes (may be
  * NULL/0 when h_time is given and the length runs in one pass, L <= 16384, except causal L = 8192,
- * whose matrix-core copy is staged there; HYENA_EWORKSPACE when too small).  The spectrum depends
+ * whose matrix-core copy is staged there, as is the long-row copy of causal L = 2^15 .. 2^17 after the
+ * multi-pass intermediate; HYENA_EWORKSPACE when too small).  The spectrum depends
  * only on (params, dims), so callers cache it per length. */
 int hyena_filter_gen(const hyena_filter_params *p, hyena_dims dims, int mode, float *h_time, void *spectrum,
                      void *ws, size_t ws_bytes, hipStream_t stream);
@@ -155,9 +164,9 @@ int hyena_film_filter_gen(const hyena_film_params *p, int64_t B, int32_t R, cons
 
 /* One long convolution with optional gate: y = gate * (h conv u), or y = h conv u when gate == NULL.
  * u, gate, y: [B, D, points] of dtype.  spectrum: from hyena_filter_gen for the same dims and D.
- * bf16 storage with causal L = 8192, even B and 16-byte-aligned u, gate and y runs on the matrix cores
- * (rows b and b+1 of a channel transformed together; fp16 operands, see the conventions above); every
- * other case runs the fp32 transform engine.
+ * bf16 storage with 16-byte-aligned u, gate and y runs on the matrix cores for causal L = 8192 with even B
+ * (rows b and b+1 of a channel transformed together) and for causal L = 2^15 .. 2^17 (fp16 operands, see
+ * the conventions above); every other case runs the fp32 transform engines.
  * y may equal u or gate exactly (in place); any other overlap returns HYENA_EALIAS. */
 int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *u,
                   const void *spectrum, const void *gate, void *y, void *ws, size_t ws_bytes,
@@ -171,8 +180,9 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
  * kept on chip (as fp16 operands, see the conventions above).  Every other single-pass case (causal
  * L <= 16384, periodic L <= 32768) runs up to 8 orders per launch of the fp32 engine with u_i kept on chip in
  * fp32 (beyond 8 orders u passes through y, in the storage type, between launches); the multi-pass plans
- * (longer rows, 3-D) chain the orders through the workspace (u_i itself fp32).  Orders above 3 never take the matrix
- * cores: their 16-bit operands compound across orders towards the bf16 tolerance. */
+ * (longer rows, 3-D; the long-row matrix-core case for orders <= 3) chain the orders through the workspace
+ * (u_i itself fp32).  Orders above 3 never take the matrix cores: their 16-bit operands compound across
+ * orders towards the bf16 tolerance. */
 int hyena_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, const void *v,
                    const void *const *x, const void *const *spectra, void *y, void *ws, size_t ws_bytes,
                    hipStream_t stream);
