@@ -187,3 +187,33 @@ def test_long_noalloc_matches_operator(torch_cuda):
         hy.operator_noalloc(vd, xd, spectra, y2)
         torch.cuda.synchronize()
         assert torch.equal(y, y2)
+
+
+def test_long_inplace_and_determinism(torch_cuda):
+    """The operator with y = v, and fftconv with y = u and with y = gate, on the long-row matrix-core kernels
+    (several chunks on two streams): bitwise equal to the out-of-place calls, which repeat bitwise."""
+    torch = torch_cuda
+    import attention_free_long_implicit_amd as hy
+    L, B, D, order = 1 << 16, 2, 5, 2
+    w = hi.WORKLOADS[2].with_(B=B, D=D, dims=(L,), order=order)
+    v, xs = hi.draw_activations(w, seed=97)
+    params = hi.draw_filter_params(w, seed=97)
+    say("long-row matrix cores: in place and determinism")
+    spectra = [hy.filter_gen(params_to_dev(p), (L,)) for p in params]
+    vd = to_dev(v, torch.bfloat16)
+    xd = [to_dev(x, torch.bfloat16) for x in xs]
+    ws = torch.empty(hy.workspace_bytes(order, B, 2, (L,), hy.BF16), dtype=torch.uint8, device="cuda")
+    y1 = hy.operator(vd, xd, spectra, ws=ws)
+    y2 = hy.operator(vd, xd, spectra, ws=ws)
+    vi = vd.clone()
+    hy.operator(vi, xd, spectra, y=vi, ws=ws)
+    c1 = hy.fftconv(vd, spectra[0], gate=xd[0])
+    ui = vd.clone()
+    hy.fftconv(ui, spectra[0], gate=xd[0], y=ui)
+    gi = xd[0].clone()
+    hy.fftconv(vd, spectra[0], gate=gi, y=gi)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert torch.equal(y1, vi)
+    assert torch.equal(c1, ui)
+    assert torch.equal(c1, gi)
