@@ -185,11 +185,11 @@ size_t taps_per_channel(int kind, int64_t pts) { return is3d(kind) ? conv3d_taps
 // copy of the single-workgroup kernel (L = 8192) and the split coefficients of the long-row kernels
 // (L = 2^15 .. 2^17).
 bool has_pair_copy(int64_t L) { return mfma_pair_supported(log2i(L), 2); }
-bool has_long_pair_copy(int64_t L) { return is_pow2(L) && mfl_supported(log2i(L)); }
-size_t pair_copy_temp_bytes(int64_t L, int64_t D) { return (size_t)D * (size_t)(L + 1) * sizeof(float2); }
-size_t pair_copy_bytes_per_channel(int64_t L) {
+bool has_long_row_copy(int64_t L) { return is_pow2(L) && mfl_supported(log2i(L)); }
+size_t natural_bins_bytes(int64_t L, int64_t D) { return (size_t)D * (size_t)(L + 1) * sizeof(float2); }
+size_t mfma_copy_bytes_per_channel(int64_t L) {
   if (has_pair_copy(L)) return mfma_pair_spectrum_bytes_per_channel();
-  if (has_long_pair_copy(L)) return mfl_spectrum_bytes_per_channel(log2i(L));
+  if (has_long_row_copy(L)) return mfl_spectrum_bytes_per_channel(log2i(L));
   return 0;
 }
 
@@ -324,10 +324,11 @@ bool ws_align256(char*& p, size_t& n) {
 }
 
 // Filter spectra of `nch` channels from their taps h [nch, taps] (the workspace [wsp, wsp + wsn) holds the
-// multi-pass intermediate or the matrix-core copy's staging).  pair_copy: also write the bf16 row-pair
-// copy (L = 8192 causal, one filter per channel).
+// multi-pass intermediate or the matrix-core copy's staging).  mfma_copy: also write the matrix-core copy of
+// bf16 storage after the fp32 spectra (causal L = 8192: the row-pair copy; causal L = 2^15 .. 2^17: the
+// long-row split coefficients; one filter per channel).
 int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* spectrum, char* wsp, size_t wsn,
-                      bool pair_copy, const Twiddles& tw, hipStream_t stream) {
+                      bool mfma_copy, const Twiddles& tw, hipStream_t stream) {
   int st;
   const size_t row_b = filter_intermediate_bytes(kind, L);
   int chunk = 0;
@@ -343,20 +344,20 @@ int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* sp
     if ((st = hip_status(launch_spectrum1d_fourstep(engine_log2(kind, L), h, (float2*)spectrum, (int)nch,
                                                     (float2*)wsp, chunk, tw, stream, kind == K_CIRC1 ? 1 : 0))))
       return st;
-    if (!pair_copy || kind != K_CAUSAL || !has_long_pair_copy(L)) return HYENA_OK;
+    if (!mfma_copy || kind != K_CAUSAL || !has_long_row_copy(L)) return HYENA_OK;
     // the long-row matrix-core copy after the fp32 spectra: natural-order bins of as many channels as the
     // workspace holds (free again: the same stream has finished with the intermediate), then their copy
-    const size_t nat = pair_copy_temp_bytes(L, 1);
+    const size_t nat = natural_bins_bytes(L, 1);
     const int64_t c = (int64_t)(wsn / nat);
     if (c < 1) return HYENA_EWORKSPACE;
     const size_t pb = mfl_spectrum_bytes_per_channel(log2i(L));
-    char* pair = (char*)spectrum + (size_t)nch * (size_t)L * sizeof(float2);
+    char* copy = (char*)spectrum + (size_t)nch * (size_t)L * sizeof(float2);
     for (int64_t d0 = 0; d0 < nch; d0 += c) {
       const int n = (int)(nch - d0 < c ? nch - d0 : c);
       if ((st = hip_status(launch_export1d_fourstep(log2i(L), (const float2*)spectrum + (size_t)d0 * (size_t)L,
                                                     (float2*)wsp, n, stream))))
         return st;
-      if ((st = hip_status(launch_mfl_spectrum(log2i(L), (const float2*)wsp, pair + (size_t)d0 * pb, n, tw, stream))))
+      if ((st = hip_status(launch_mfl_spectrum(log2i(L), (const float2*)wsp, copy + (size_t)d0 * pb, n, tw, stream))))
         return st;
     }
     return HYENA_OK;
@@ -364,9 +365,9 @@ int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* sp
   if (kind == K_CIRC1)
     return hip_status(launch_spectrum1d_single(circular_log2(L), h, (float2*)spectrum, (int)nch, tw, stream, 1));
   if ((st = hip_status(launch_spectrum1d_single(log2i(L), h, (float2*)spectrum, (int)nch, tw, stream)))) return st;
-  if (pair_copy && has_pair_copy(L)) {
+  if (mfma_copy && has_pair_copy(L)) {
     // natural-order bins into the workspace, then the pair-order bf16 copy after the fp32 spectrum
-    if (!ws_align256(wsp, wsn) || wsn < pair_copy_temp_bytes(L, nch)) return HYENA_EWORKSPACE;
+    if (!ws_align256(wsp, wsn) || wsn < natural_bins_bytes(L, nch)) return HYENA_EWORKSPACE;
     float2* nat = (float2*)wsp;
     if ((st = hip_status(launch_export1d_single(log2i(L), (const float2*)spectrum, nat, (int)nch, stream)))) return st;
     void* pair = (char*)spectrum + (size_t)nch * (size_t)L * sizeof(float2);
@@ -376,13 +377,13 @@ int spectra_from_taps(int kind, int64_t L, const float* h, int64_t nch, void* sp
 }
 
 // Whether spectra_from_taps finds the room it needs in [wsp, wsp + wsn) (checked before any launch).
-bool spectra_ws_ok(int kind, int64_t L, int64_t nch, char* wsp, size_t wsn, bool pair_copy) {
+bool spectra_ws_ok(int kind, int64_t L, int64_t nch, char* wsp, size_t wsn, bool mfma_copy) {
   const size_t row_b = filter_intermediate_bytes(kind, L);
   if (row_b)
     return ws_align256(wsp, wsn) && wsn >= row_b &&
-           (!pair_copy || kind != K_CAUSAL || !has_long_pair_copy(L) || wsn >= pair_copy_temp_bytes(L, 1));
-  if (pair_copy && kind == K_CAUSAL && has_pair_copy(L))
-    return ws_align256(wsp, wsn) && wsn >= pair_copy_temp_bytes(L, nch);
+           (!mfma_copy || kind != K_CAUSAL || !has_long_row_copy(L) || wsn >= natural_bins_bytes(L, 1));
+  if (mfma_copy && kind == K_CAUSAL && has_pair_copy(L))
+    return ws_align256(wsp, wsn) && wsn >= natural_bins_bytes(L, nch);
   return true;
 }
 
@@ -516,7 +517,7 @@ int hyena_spectrum_bytes(hyena_dims dims, int mode, int64_t D, size_t* bytes) {
   const int kind = kind_of(mode, dims);
   if (is3d(kind)) *bytes = (size_t)D * conv3d_spectrum_bytes_per_channel(circ3(kind));
   else if (kind == K_CIRC1) *bytes = (size_t)D * (size_t)(pts / 2) * sizeof(float2);
-  else *bytes = (size_t)D * (size_t)pts * sizeof(float2) + (ps ? 0 : (size_t)D * pair_copy_bytes_per_channel(pts));
+  else *bytes = (size_t)D * (size_t)pts * sizeof(float2) + (ps ? 0 : (size_t)D * mfma_copy_bytes_per_channel(pts));
   return HYENA_OK;
 }
 
@@ -527,12 +528,12 @@ int hyena_filter_workspace_bytes(hyena_dims dims, int mode, int64_t D, size_t* b
   if (st) return st;
   const int kind = kind_of(mode, dims);
   *bytes = (size_t)D * taps_per_channel(kind, pts) * sizeof(float);
-  if (kind == K_CAUSAL && has_pair_copy(pts)) *bytes += 256 + pair_copy_temp_bytes(pts, D);
+  if (kind == K_CAUSAL && has_pair_copy(pts)) *bytes += 256 + natural_bins_bytes(pts, D);
   const size_t per = filter_intermediate_bytes(kind, pts);
   if (per) {
     size_t room = (size_t)filter_chunk_rows((int64_t)per, D) * per;
-    if (kind == K_CAUSAL && has_long_pair_copy(pts) && room < pair_copy_temp_bytes(pts, 1))
-      room = pair_copy_temp_bytes(pts, 1);
+    if (kind == K_CAUSAL && has_long_row_copy(pts) && room < natural_bins_bytes(pts, 1))
+      room = natural_bins_bytes(pts, 1);
     *bytes += 256 + room;
   }
   return HYENA_OK;
