@@ -596,6 +596,36 @@ def measure(w, args, torch, hy, _lib, dev, stream, scratch, warm_steps: int, col
     return res, r
 
 
+def torch_fft_context(w, r, torch, hy, stream, ours_warm_ms):
+    """Context only, not a code path of the library: the same operator written with torch.fft (the platform's
+    FFT library) on the same GPU -- rfft of the zero-padded rows, product with the 2L-point filter spectra,
+    irfft, cut to L, gate, every order, fp32 -- timed back to back like `warm`.  The filter taps come from
+    hyena_filter_gen, their spectra from torch.fft (not timed)."""
+    L = w.dims[0]
+    n = 2 * L
+    spec = []
+    for p in r["pd"]:
+        taps = torch.empty((w.D, L), dtype=torch.float32, device=r["vd"].device)
+        hy.filter_gen(p, w.dims, h_time=taps)
+        spec.append(torch.fft.rfft(taps, n=n))
+    vd, xd = r["vd"], r["xd"]
+
+    def step():
+        u = vd.float()
+        for H, x in zip(spec, xd):
+            u = torch.fft.irfft(torch.fft.rfft(u, n=n) * H, n=n)[..., :L] * x.float()
+        return u.to(vd.dtype)
+    for _ in range(3):
+        step()
+    ms = time_back_to_back(torch, stream, step, 10)
+    del spec
+    torch.cuda.empty_cache()
+    return {"ms_per_step": ms, "ours_warm_ms_per_step": ours_warm_ms,
+            "ratio": ms / ours_warm_ms if ours_warm_ms else None,
+            "note": "context only: torch.fft rfft / product / irfft / gate in fp32 per order on the same GPU, "
+                    "back to back (10 steps); not a code path of the library and not a target"}
+
+
 def roofline_object(w, launch_ms: float, per_step: bool):
     """HBM roofline of the dominant kernel (per_step: the whole step, when a step is several kernels)."""
     key = kernel_key(w)
@@ -641,6 +671,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle wall time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the device copy-bandwidth probe")
+    ap.add_argument("--no-torch-fft", action="store_true",
+                    help="skip the torch.fft context line (1-D causal workloads with shared filters)")
     ap.add_argument("--no-parity", action="store_true", help="skip the oracle check of the bench's own output")
     ap.add_argument("--no-config3", action="store_true",
                     help="skip the nested line of the 2^20-sample fp32 workload (the second target configuration)")
@@ -749,6 +781,9 @@ def main():
         out["roofline"] = roofline_for = roofline_object(w, res["ms_per_step"], per_step=not one_launch)
         roofline_for["timing"] = ("cold step, one launch per step (see timing)" if one_launch else
                                   "cold step (see timing)")
+    if (not args.no_torch_fft and w.ndim == 1 and w.mode == "causal" and not (film or proj)
+            and res.get("warm") is not None):
+        out["torch_fft_context"] = torch_fft_context(w, r, torch, hy, stream, res["warm"]["ms_per_step"])
     host = (r["v"], r["xs"], r["params"], r["reg"], r.get("proj_inputs"))
     del r
     if args.workload == 1 and not args.no_config3:
