@@ -85,6 +85,11 @@ def test_size_queries(lib):
         assert st == 0 and n == 3 * Lc * 8 + 3 * (Lc * 8 + 256)
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([1 << 18]), L.CAUSAL, 3)
     assert st == 0 and n == 3 * (1 << 18) * 8
+    # one channel: the filter workspace holds the taps and the L + 1 natural-order bins staged for the
+    # long-row copy (8 bytes more than the multi-pass intermediate of one channel)
+    for Lc in (1 << 15, 1 << 17):
+        st, n = _size(lib.hyena_filter_workspace_bytes, L.dims_of([Lc]), L.CAUSAL, 1)
+        assert st == 0 and n >= Lc * 4 + 256 + (Lc + 1) * 8
     # periodic 3-D: 64 x 64 x 33 bins per channel, intermediate 64 x-slabs of 64 x 33 per volume
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.CIRCULAR, 128)
     assert st == 0 and n == 128 * 64 * 64 * 33 * 8

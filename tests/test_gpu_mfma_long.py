@@ -217,3 +217,18 @@ def test_long_inplace_and_determinism(torch_cuda):
     assert torch.equal(y1, vi)
     assert torch.equal(c1, ui)
     assert torch.equal(c1, gi)
+
+
+@pytest.mark.parametrize("L", [1 << 15, 1 << 17])
+def test_long_single_row(torch_cuda, L):
+    """B = D = 1: one row, one channel (the filter build stages one channel's L + 1 natural-order bins, which
+    the workspace query sizes for); order 2 against the oracle."""
+    w = hi.WORKLOADS[2].with_(B=1, D=1, dims=(L,), order=2)
+    v, xs = hi.draw_activations(w, seed=3)
+    params = hi.draw_filter_params(w, seed=3)
+    say(f"long-row matrix cores: one row, L={L}")
+    from gpu_util import run_hip_operator
+    y = run_hip_operator(w, v, xs, params, host_dtype=np.float32)
+    e = all_row_errors(w, v, xs, params, y)
+    report_errors(f"one row L={L}", e)
+    assert e.max() < BF16_TOL
