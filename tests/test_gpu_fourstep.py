@@ -168,12 +168,13 @@ def test_fourstep_zero_input_gives_exact_zero(torch_cuda, dtype, B):
     assert torch.count_nonzero(y).item() == 0
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("L", [1 << 16, 1 << 20])
-def test_fourstep_bf16_block_scales_per_row(torch_cuda, L):
-    """The bf16-storage plans keep their intermediate in fp16 with one power-of-two scale per block, and every
-    block belongs to one (b, d) row: rows whose magnitudes differ by 2^100 (a single impulse among them, the
-    widest spread within a row) each stay within the bf16 tolerance of the oracle, and a NaN row leaves the
-    others bitwise unchanged."""
+def test_fourstep_block_scales_per_row(torch_cuda, L, dtype):
+    """Rows whose magnitudes differ by 2^100 (a single impulse among them, the widest spread within a row) each
+    stay within the storage type's tolerance of the oracle, and a NaN row turns NaN and leaves the others
+    bitwise unchanged.  With bf16 storage the intermediate is fp16 with one power-of-two scale per block, and
+    every block belongs to one (b, d) row; with fp32 storage it is fp32."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
     B, D = 1, 6
@@ -187,17 +188,18 @@ def test_fourstep_bf16_block_scales_per_row(torch_cuda, L):
     v[0, 4, L // 3] = 3.0
     xs = [rng.standard_normal((B, D, L)).astype(np.float32) for _ in range(2)]
     params = hi.draw_filter_params(w, seed=11)
-    say(f"four-step bf16 block scales, rows 2^-60 .. 2^40 and an impulse, L={L}")
+    say(f"four-step {dtype} block scales, rows 2^-60 .. 2^40 and an impulse, L={L}")
     spectra = [hy.filter_gen(params_to_dev(q), (L,)) for q in params]
-    vd = torch.from_numpy(v).to(torch.bfloat16).cuda()
-    xd = [torch.from_numpy(x).to(torch.bfloat16).cuda() for x in xs]
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    vd = torch.from_numpy(v).to(tdt).cuda()
+    xd = [torch.from_numpy(x).to(tdt).cuda() for x in xs]
     y = hy.operator(vd, xd, spectra)
     torch.cuda.synchronize()
     vr = vd.float().cpu().numpy()
     xr = [x.float().cpu().numpy() for x in xd]
     e = all_row_errors(w, vr, xr, params, y.float().cpu().numpy())
     report_errors("block scales", e)
-    assert e.max() < BF16_TOL
+    assert e.max() < (BF16_TOL if dtype == "bf16" else FP32_TOL)
     vn = vd.clone()
     vn[0, 2, L // 2] = float("nan")
     yn = hy.operator(vn, xd, spectra)
