@@ -59,11 +59,12 @@ def test_size_queries(lib):
     assert st == 0 and n == 3 * (65536 * 4 + 4096)
     st, n = _size(lib.hyena_workspace_bytes, 2, 1, 3, L.dims_of([1 << 20]), L.F32, L.CAUSAL)
     assert st == 0 and n == 3 * (1 << 20) * 8          # never more rows than there are
-    # 3-D: spectrum 128 x 128 x 65 bins per channel; intermediate 64 x 128 x 65 per volume
+    # 3-D: spectrum 128 x 128 x 65 bins per channel; intermediate 65 x 64 x 64 per volume (after the
+    # z transform only)
     st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([64, 64, 64]), L.LINEAR, 128)
     assert st == 0 and n == 128 * 128 * 128 * 65 * 8
     st, n = _size(lib.hyena_workspace_bytes, 2, 1, 2, L.dims_of([64, 64, 64]), L.F32, L.LINEAR)
-    assert st == 0 and n == 2 * 64 * 128 * 65 * 8
+    assert st == 0 and n == 2 * 65 * 64 * 64 * 8
     # periodic 1-D: L/2 packed bins per channel, no workspace, taps only for the filter
     for Lc in (2048, 8192, 32768):
         st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([Lc]), L.CIRCULAR, 16)
