@@ -70,27 +70,32 @@ def test_filter3d_taps_with_biases(torch_cuda):
 
 @pytest.mark.parametrize("gate", [False, True])
 def test_fftconv3d_fp32_matches_oracle(torch_cuda, gate):
+    """B = 2, D = 2 (volumes (b, d) with the filter of channel d); the gated case through a workspace of two
+    volumes: four chunks of one volume alternating over two streams."""
     torch = torch_cuda
     import attention_free_long_implicit_amd as hy
-    B, D = 1, 3
+    B, D = 2, 2
     w = hi.WORKLOADS[4].with_(B=B, D=D)
     rng = np.random.default_rng(42)
     u = rng.standard_normal((B, D, N, N, N)).astype(np.float32)
     g = rng.standard_normal((B, D, N, N, N)).astype(np.float32)
     p = hi.draw_filter_params(w, seed=42)[0]
-    say(f"3-D fftconv fp32 gate={gate}")
+    say(f"3-D fftconv fp32 B=2 D=2 gate={gate}")
     spec = hy.filter_gen(params_to_dev(p), (N, N, N))
-    ws = torch.empty(2 * N * 8320 * 8, dtype=torch.uint8, device="cuda")   # two volumes per chunk: 2 chunks
+    vol = 65 * N * N * 8                    # intermediate per volume: [65 kz][64 x][64 y] complex fp32
+    ws = torch.empty(2 * vol, dtype=torch.uint8, device="cuda")
     y = hy.operator(to_dev(u, torch.float32), [to_dev(g, torch.float32)], [spec], ws=ws) if gate else \
         hy.fftconv(to_dev(u, torch.float32), spec)
     torch.cuda.synchronize()
     h = orc.implicit_filter_3d(p, N)
-    ref = orc.linear_conv3d_fft(u[0].astype(np.float64), h)
-    if gate:
-        ref = ref * g[0]
-    e = rel_err_rows(y.cpu().numpy()[0], ref, point_axes=3)
-    say(f"  max rel err {e.max():.3e}")
-    assert e.max() < 2e-5, e.max()
+    got = y.cpu().numpy()
+    for b in range(B):
+        ref = orc.linear_conv3d_fft(u[b].astype(np.float64), h)
+        if gate:
+            ref = ref * g[b]
+        e = rel_err_rows(got[b], ref, point_axes=3)
+        say(f"  b={b}: max rel err {e.max():.3e}")
+        assert e.max() < 2e-5, e.max()
 
 
 def test_conv3d_delta_filter(torch_cuda):
