@@ -27,6 +27,7 @@ constexpr int kMaxDevices = 64;
 // kChunkWays - 1 side streams); see pair_chunk_rows.
 constexpr int kChunkWays = 2;      // streams the chunks cycle over (the caller's and kChunkWays - 1 side streams)
 constexpr int kChunkMB = 64;
+constexpr int kChunk3dMB = 96;    // the zero-padded 3-D plan (see pair_chunk_rows)
 static_assert(kChunkWays >= 2 && kChunkWays <= kSideStreams + 1, "side streams");
 std::mutex g_mu;
 struct DeviceTables {
@@ -204,34 +205,35 @@ int64_t default_chunk_rows(int64_t per, int64_t rows) {
 
 // The multi-pass plans (1-D long rows, 3-D volumes) run chunks of about 64 MB of intermediate two at a time,
 // on the caller's stream and the library's side stream (32, 48, 64, 72 and 80 MB measured 5.12, 4.86, 4.77-4.84,
-// 4.93 and 4.91 ms per step at L = 2^20, fp32, 256 rows, against 5.37 ms for one stream of 160 MB chunks;
-// 3-D 64^3 zero-padded, 128 volumes: 16, 32, 64, 128 MB 2.11, 1.63, 1.62, 1.77 ms against 1.79 ms for one
-// chunk).  A whole batch of at most 192 MB of intermediate runs as one chunk on one stream (periodic 64^3,
-// 138 MB: 0.41 ms, against 0.43 ms in 64 MB pairs).  Three streams measured slower (64 / 44 MB chunks: 5.28 /
-// 4.96 ms at L = 2^20 against 4.83, 2.95 / 2.90 ms against 2.85 for the order-3 L = 65536 bf16 workload,
-// 1.70 / 1.63 ms against 1.61 for 3-D).  The workspace holds kChunkWays chunks.
-int64_t pair_chunk_rows(int64_t per, int64_t rows) {
+// 4.93 and 4.91 ms per step at L = 2^20, fp32, 256 rows, against 5.37 ms for one stream of 160 MB chunks).
+// The zero-padded 3-D plan takes chunks of about 96 MB (128 volumes of 2.13 MB: ten, six and four equal
+// chunks measured 1.437, 1.405 and 1.384 ms per step).  A whole batch of at most 192 MB of intermediate runs
+// as one chunk on one stream (periodic 64^3, 138 MB: 0.41 ms, against 0.43 ms in 64 MB pairs).  Three streams
+// measured slower (64 / 44 MB chunks: 5.28 / 4.96 ms at L = 2^20 against 4.83, 2.95 / 2.90 ms against 2.85
+// for the order-3 L = 65536 bf16 workload).  The workspace holds kChunkWays chunks.
+int chunk_mb(int kind) { return is3d(kind) && !circ3(kind) ? kChunk3dMB : kChunkMB; }
+int64_t pair_chunk_rows(int64_t per, int64_t rows, int mb) {
   if ((size_t)rows * (size_t)per <= ((size_t)192 << 20)) return rows;
-  int64_t c = ((int64_t)kChunkMB << 20) / per;
+  int64_t c = ((int64_t)mb << 20) / per;
   if (c < 1) c = 1;
   return c < rows ? c : rows;
 }
-size_t pair_ws_bytes(size_t per, int64_t rows) {
-  const int64_t c = pair_chunk_rows((int64_t)per, rows);
+size_t pair_ws_bytes(size_t per, int64_t rows, int mb) {
+  const int64_t c = pair_chunk_rows((int64_t)per, rows, mb);
   return (size_t)(rows > c ? kChunkWays : 1) * (size_t)c * per;
 }
 // Chunk rows of a multi-pass plan within a workspace of ws_bytes, and how many streams its chunks cycle over
 // (0: the workspace does not hold one row).
-int pair_chunk(size_t per, int64_t rows, size_t ws_bytes, int* ways) {
+int pair_chunk(size_t per, int64_t rows, size_t ws_bytes, int* ways, int mb) {
   const int64_t cap = (int64_t)(ws_bytes / per);
   *ways = 1;
   if (cap < 1) return 0;
-  if (cap >= rows && pair_chunk_rows((int64_t)per, rows) >= rows) return (int)rows;   // one chunk
+  if (cap >= rows && pair_chunk_rows((int64_t)per, rows, mb) >= rows) return (int)rows;   // one chunk
   int64_t c = cap;
   if (cap >= 2 && rows > 1) {
     const int w = cap >= kChunkWays ? kChunkWays : (int)cap;
     c = cap / w;
-    const int64_t want = pair_chunk_rows((int64_t)per, rows);
+    const int64_t want = pair_chunk_rows((int64_t)per, rows, mb);
     if (c > want) c = want;
     if (rows > c) *ways = w;
   }
@@ -428,10 +430,10 @@ int run_operator(int order, int64_t B, int64_t D, hyena_dims dims, int dtype, in
   if (per) {
     const bool ws_ok = ws && !((size_t)ws & 255u);
     if (ws_ok && use_mfl(kind, dtype, pts, hsb, order, v, x, y)) {
-      chunk = pair_chunk(mfl_row_bytes(log2i(pts)), B * D, ws_bytes, &ways);
+      chunk = pair_chunk(mfl_row_bytes(log2i(pts)), B * D, ws_bytes, &ways, kChunkMB);
       mfl = chunk >= 1;
     }
-    if (!mfl) chunk = ws_ok ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
+    if (!mfl) chunk = ws_ok ? pair_chunk(per, B * D, ws_bytes, &ways, chunk_mb(kind)) : 0;
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, v, tb)) return HYENA_EALIAS;
     for (int i = 0; i < order; ++i)
@@ -549,7 +551,7 @@ int hyena_workspace_bytes(int order, int64_t B, int64_t D, hyena_dims dims, int 
   const int kind = kind_of(mode, dims);
   *bytes = 0;
   const size_t per = row_intermediate_bytes(kind, pts, dtype);
-  if (per) *bytes = pair_ws_bytes(per, B * D);
+  if (per) *bytes = pair_ws_bytes(per, B * D, chunk_mb(kind));
   // (the long-row matrix-core kernels need less per row than the per-row plan, which stays possible for
   // misaligned activations)
   return HYENA_OK;
@@ -665,10 +667,10 @@ int hyena_fftconv(int64_t B, int64_t D, hyena_dims dims, int dtype, int mode, co
   if (per) {
     const bool ws_ok = ws && !((size_t)ws & 255u);
     if (ws_ok && use_mfl(kind, dtype, pts, hsb, 1, u, xs, y)) {
-      chunk = pair_chunk(mfl_row_bytes(log2i(pts)), B * D, ws_bytes, &ways);
+      chunk = pair_chunk(mfl_row_bytes(log2i(pts)), B * D, ws_bytes, &ways, kChunkMB);
       mfl = chunk >= 1;
     }
-    if (!mfl) chunk = ws_ok ? pair_chunk(per, B * D, ws_bytes, &ways) : 0;
+    if (!mfl) chunk = ws_ok ? pair_chunk(per, B * D, ws_bytes, &ways, chunk_mb(kind)) : 0;
     if (chunk < 1) return HYENA_EWORKSPACE;
     if (overlaps(ws, ws_bytes, y, tb) || overlaps(ws, ws_bytes, u, tb) || (gate && overlaps(ws, ws_bytes, gate, tb)))
       return HYENA_EALIAS;

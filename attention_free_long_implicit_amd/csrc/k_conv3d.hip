@@ -299,18 +299,18 @@ __global__ void k3_export(const float2* __restrict__ Hs, float2* __restrict__ H)
 }
 
 // ------------------------------------------------------------------ zero-padded plan: z alone, then (x, y)
-// Padding doubles the data along each axis it is applied to.  Passes A-C above store the volume after the
-// z and y transforms (4x the activations).  The plan below stores it after the z transform only (2x): its
-// middle pass transforms x and y together in one LDS plane [128 x][128 y] per z-bin, where both paddings
-// happen on chip.  Passes per (b, d) volume:
+// Padding doubles the data along each axis it is applied to.  Run on the padded grid, passes A-C would
+// store the volume after its z and y transforms (4x the activations).  This plan stores it after the z
+// transform only (2x): its middle pass transforms x and y together in one LDS plane [128 x][128 y] per
+// z-bin, where both paddings happen on chip.  Passes per (b, d) volume:
 //   Z   k3z_lines   one x-slab: z-transform + split on [64 y][65 kz]; stored as J[kz][x][y] (x, y < 64)
 //   XY  k3z_planes  one kz: J[kz] (32 KB) into the plane, y- and x-transforms (zero upper halves),
 //                   product with the filter spectrum, inverse x and y keeping x, y < 64, back to J[kz]
 //   Z'  k3z_lines   one x-slab: re-pack, inverse z (keep z < 64), gate; for every order but the last the
 //                   same workgroup then runs the next order's pass Z
 // Intermediate per volume: [65 kz][64 x][64 y] complex fp32 (2.13 MB).  Filter spectrum per channel:
-// Hz[kz][x-position][y-position] (65 x 128 x 128), scaled like the A-C plan's (H / 2^22), built by the same
-// two steps over all 128^3 placed taps.
+// Hz[kz][x-position][y-position] (65 x 128 x 128), Hz = H / 2^22 where H is the 128^3 real-input DFT of the
+// placed filter, built by the same two steps over all 128^3 placed taps.
 namespace k3z {
 constexpr int N = 64, MP = 128, NKZ = 65, T = 512;
 constexpr int TXY = 1024;                      // pass XY: one workgroup per CU (its plane takes 129 KB)

@@ -65,6 +65,9 @@ def test_size_queries(lib):
     assert st == 0 and n == 128 * 128 * 128 * 65 * 8
     st, n = _size(lib.hyena_workspace_bytes, 2, 1, 2, L.dims_of([64, 64, 64]), L.F32, L.LINEAR)
     assert st == 0 and n == 2 * 65 * 64 * 64 * 8
+    # 128 volumes (272 MB of intermediate): two chunks of about 96 MB (47 volumes each) in the workspace
+    st, n = _size(lib.hyena_workspace_bytes, 2, 1, 128, L.dims_of([64, 64, 64]), L.F32, L.LINEAR)
+    assert st == 0 and n == 2 * 47 * 65 * 64 * 64 * 8
     # periodic 1-D: L/2 packed bins per channel, no workspace, taps only for the filter
     for Lc in (2048, 8192, 32768):
         st, n = _size(lib.hyena_spectrum_bytes, L.dims_of([Lc]), L.CIRCULAR, 16)
