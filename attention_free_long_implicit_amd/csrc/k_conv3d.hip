@@ -94,7 +94,7 @@ __device__ __forceinline__ void k3_zline_pairs(float2* plane, const Twiddles& tw
   static_for<PER>([&](auto ii) {
     const int it = t + T * ii.value;
     if (it >= ITEMS) return;
-    const int y = it / (HZ + 1), k = it % (HZ + 1);
+    const int y = it % NLINES, k = it / NLINES;   // lanes on consecutive lines: distinct banks
     const int kp = (NZC - k) % NZC;
     float2* line = plane + y * NKZ;
     const float2 w = twiddle<ilog2(2 * NZC)>(tw, uint32_t(k));
@@ -115,7 +115,7 @@ __device__ __forceinline__ void k3_zline_pairs(float2* plane, const Twiddles& tw
   static_for<PER>([&](auto ii) {
     const int it = t + T * ii.value;
     if (it >= ITEMS) return;
-    const int y = it / (HZ + 1), k = it % (HZ + 1);
+    const int y = it % NLINES, k = it / NLINES;   // lanes on consecutive lines: distinct banks
     float2* line = plane + y * NKZ;
     if constexpr (SPLIT) {
       line[k] = a[ii.value];
