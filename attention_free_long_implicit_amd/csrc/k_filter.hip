@@ -267,10 +267,11 @@ k_film_prep(FilmArgs a, const float* __restrict__ reg, int B, int R, float* __re
 
 namespace film {
 constexpr int H = 64, TP = 64, CB = 128, T = 256;
-constexpr int SK = TP + 4;        // row stride of the [k][position] and [k][unit] tiles
-constexpr int SC = CB + 4;        // row stride of the [k][channel] read-out tile
+constexpr int SK = TP + 4;        // row stride of the [k][position] layer-1 output
 constexpr int SH = H + 1;         // row stride of the [position][unit] layer-2 output
 constexpr int SP = TP + 1;        // row stride of the [channel][position] output staging
+// one LDS region, reused: layer-1 output, then layer-2 output, then the output staging
+constexpr int RS = (CB * SP > H * SK ? (CB * SP > TP * SH ? CB * SP : TP * SH) : (H * SK > TP * SH ? H * SK : TP * SH));
 }  // namespace film
 
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float film_f32x16;
@@ -291,19 +292,17 @@ __device__ __forceinline__ float siren_sin(float x) {
 // Taps of sample blockIdx.z: 64 positions x 128 channels per workgroup, four waves.  Layer 1 (n inputs)
 // is evaluated directly into LDS; layer 2 (64 x 64 x 64) and the read-out (64 x 128 x 64) run on the
 // matrix cores in fp32 (v_mfma_f32_32x32x2f32): layer 2 one 32 x 32 block per wave (two accumulators
-// over alternate k), the read-out two.  The read-out weights are staged at the start, so their loads
-// overlap layers 1 and 2; the output tile leaves through LDS as [channel][position] rows, so the
-// stores run along positions.
+// over alternate k), the read-out two.  The weight operands of both products (the same for every
+// workgroup of a sample) are read straight from global memory, where they stay in L2; LDS holds only
+// the activations, one 33 KB region that is reused by each phase, so four workgroups share a CU.  The
+// output tile leaves through LDS as [channel][position] rows, so the stores run along positions.
 template <class G>
 __global__ void __launch_bounds__(film::T)
 k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict__ a2t_g,
              const float* __restrict__ a3t_g, G geo, float* __restrict__ h) {
   using namespace film;
   constexpr int NC = G::NC;
-  constexpr int R0 = H * SC;                            // a3t [k][c]; later the output staging [c][p]
-  constexpr int R1 = 2 * H * SK;                        // a2t [k][j], h1T [k][p]; later h2 [p][j]
-  static_assert(CB * SP <= R0 && TP * SH <= R1, "LDS regions");
-  __shared__ __align__(16) float lds[R0 + R1];
+  __shared__ __align__(16) float lds[RS];              // h1T [k][p], then h2 [p][j], then the staging [c][p]
   __shared__ float gm[4 * H];                           // gamma_1, beta_1, gamma_2, beta_2
   __shared__ float w1[H][NC + 2];                       // A1 row, a1, omega0 of each first-layer unit
   __shared__ float crd[NC][TP];
@@ -314,14 +313,7 @@ k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict_
   const int npos = geo.count();
   const int p0 = blockIdx.x * TP, c0 = blockIdx.y * CB;
 
-  float* a3t = lds;
-  float* a2t = lds + R0;
-  float* h1T = a2t + H * SK;
-  for (int i = tid; i < H * CB; i += T) {
-    const int k = i / CB, c = i % CB;
-    a3t[k * SC + c] = (c0 + c < a.D) ? a3t_g[(size_t)k * a.D + c0 + c] : 0.0f;
-  }
-  for (int i = tid; i < H * H; i += T) a2t[(i / H) * SK + i % H] = a2t_g[i];
+  float* h1T = lds;
   gm[tid] = mod[(size_t)b * 4 * H + tid];
   if (tid < H) {
 #pragma unroll
@@ -361,7 +353,7 @@ k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict_
 #pragma unroll 8
   for (int s = 0; s < H / 2; ++s) {
     const int k = 2 * s + hk;
-    acc2[s & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(h1T[k * SK + 32 * pb + l32], a2t[k * SK + 32 * jb + l32],
+    acc2[s & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(h1T[k * SK + 32 * pb + l32], a2t_g[k * H + 32 * jb + l32],
                                                        acc2[s & 1], 0, 0, 0);
   }
   // register v holds position 32 pb + 8 (v / 4) + 4 hk + (v mod 4) of unit j = 32 jb + l32
@@ -372,9 +364,9 @@ k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict_
 #pragma unroll
     for (int v = 0; v < 16; ++v) h2v[v] = siren_sin(fmaf(g2, acc2[0][v] + acc2[1][v] + bj, be2));
   }
-  __syncthreads();                                      // every wave is done with a2t and h1T
+  __syncthreads();                                      // every wave is done with h1T
 
-  float* h2 = lds + R0;
+  float* h2 = lds;
   {
     const int j = 32 * jb + l32;
 #pragma unroll
@@ -384,6 +376,11 @@ k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict_
 
   // read-out: wave owns positions 32 pb .. + 31 x channels 64 cq .. + 63 (two 32-column blocks)
   const int cq = wave >> 1;
+  // this lane's read-out weight columns (channels past D read as zero)
+  const int ca = c0 + 64 * cq + l32, cb = ca + 32;
+  const float* w3a = a3t_g + (ca < a.D ? ca : 0);
+  const float* w3b = a3t_g + (cb < a.D ? cb : 0);
+  const float ma = ca < a.D ? 1.0f : 0.0f, mb = cb < a.D ? 1.0f : 0.0f;
   film_f32x16 acc3[2];
 #pragma unroll
   for (int u = 0; u < 2; ++u)
@@ -393,13 +390,12 @@ k_film_tiles(FilmArgs a, const float* __restrict__ mod, const float* __restrict_
   for (int s = 0; s < H / 2; ++s) {
     const int k = 2 * s + hk;
     const float av = h2[(32 * pb + l32) * SH + k];
-#pragma unroll
-    for (int u = 0; u < 2; ++u)
-      acc3[u] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, a3t[k * SC + 64 * cq + 32 * u + l32], acc3[u], 0, 0, 0);
+    acc3[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, ma * w3a[(size_t)k * a.D], acc3[0], 0, 0, 0);
+    acc3[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, mb * w3b[(size_t)k * a.D], acc3[1], 0, 0, 0);
   }
 
   // bias and window; register v holds position 32 pb + 8 (v / 4) + 4 hk + (v mod 4) of channel d
-  __syncthreads();                                      // every wave is done with a3t and h2
+  __syncthreads();                                      // every wave is done with h2
   float* st = lds;                                      // [CB][SP]
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
