@@ -392,22 +392,24 @@ k3z_lines(const typename Store<BF16>::elem* u, const typename Store<BF16>::elem*
   k3z_store_slab<N>(plane, Jv, x, t);
 }
 
-// Pass Z for the filter: taps placed at r mod 128 on all 128 x-slabs and y-lines.
-// grid.x = 128 slabs * nq (channel fastest).
+// Pass Z for the filter: taps placed at r mod 128 on all 128 x-slabs and y-lines, half an x-slab (64
+// y-lines, a 33 KB plane) per workgroup so that four share a CU.  grid.x = 2 * 128 half-slabs * nq
+// (channel fastest).
 __global__ void __launch_bounds__(k3z::T)
 k3z_taps(const float* __restrict__ h, float2* J, int q0, int nq, Twiddles tw) {
   using namespace k3z;
-  constexpr int NZC = C::NZC, W = C::W;
-  __shared__ float2 plane[MP * NKZ];
+  constexpr int NZC = C::NZC, W = C::W, NL = MP / 2;
+  __shared__ float2 plane[NL * NKZ];
   const int t = threadIdx.x;
   const int lb = xcd_logical_block(blockIdx.x, gridDim.x);
-  const int ql = lb % nq, x = lb / nq;
+  const int ql = lb % nq, hs = lb / nq;
+  const int x = hs >> 1, y0 = NL * (hs & 1);
   const int d = q0 + ql;
   const float* hd = h + (size_t)d * W * W * W;
   const int rx = C::offset(x);
-  static_for<(MP * NZC) / T>([&](auto ii) {
+  static_for<(NL * NZC) / T>([&](auto ii) {
     const int e = t + T * ii.value;
-    const int yy = e / NZC, m = e % NZC;
+    const int yl = e / NZC, m = e % NZC, yy = y0 + yl;
     const int ry = C::offset(yy);
     float2 v = make_float2(0.f, 0.f);
     if (C::in_filter(x) && C::in_filter(yy)) {
@@ -416,12 +418,17 @@ k3z_taps(const float* __restrict__ h, float2* J, int q0, int nq, Twiddles tw) {
       if (C::in_filter(z0)) v.x = line[C::tap(C::offset(z0))];
       if (C::in_filter(z1)) v.y = line[C::tap(C::offset(z1))];
     }
-    plane[yy * NKZ + m] = v;
+    plane[yl * NKZ + m] = v;
   });
   __syncthreads();
-  C::template ZEng<MP>::template forward<false>(plane, tw, t);
-  k3_zline_pairs<G, MP, true>(plane, tw, t);
-  k3z_store_slab<MP>(plane, J + (size_t)ql * FVOL, x, t);
+  C::template ZEng<NL>::template forward<false>(plane, tw, t);
+  k3_zline_pairs<G, NL, true>(plane, tw, t);
+  // J[kz][x][y] (128 x 128 per z-bin): this half-slab's 64 y values of row (kz, x)
+  float2* Jv = J + (size_t)ql * FVOL;
+  for (int e = t; e < NKZ * NL; e += T) {
+    const int kz = e / NL, yl = e % NL;
+    Jv[((size_t)kz * MP + x) * MP + y0 + yl] = plane[yl * NKZ + kz];
+  }
 }
 
 // Pass XY.  MODE 0: y- and x-transforms of J[kz] (x, y < 64; upper halves zero), product with Hz,
@@ -609,7 +616,7 @@ hipError_t spectrum3d_pad_launch(const float* h, float2* Hs, int D, float2* I, i
   using namespace k3z;
   for (int q0 = 0; q0 < D; q0 += chunk) {
     const int nq = (D - q0 < chunk) ? D - q0 : chunk;
-    hipLaunchKernelGGL(k3z_taps, dim3(MP * nq), dim3(T), 0, s, h, I, q0, nq, tw);
+    hipLaunchKernelGGL(k3z_taps, dim3(2 * MP * nq), dim3(T), 0, s, h, I, q0, nq, tw);
     hipLaunchKernelGGL((k3z_planes<1>), dim3(NKZ * nq), dim3(TXY), 0, s, I, (const float2*)nullptr, Hs, q0, nq, 1, 0,
                        tw);
     hipError_t e = hipGetLastError();
