@@ -424,14 +424,19 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
 __global__ void __launch_bounds__(256) k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc) {
   using namespace mf;
   __shared__ float red[4];
+  __shared__ float2 hb[L + 1];   // the channel's bins, read once, coalesced; the copy below gathers from LDS
   const int d = blockIdx.x;
   const float2* hn = Hnat + (size_t)d * (L + 1);
   float m = 0.0f;
-  for (int k = threadIdx.x; k <= L; k += 256) m = fmaxf(m, fmaxf(fabsf(hn[k].x), fabsf(hn[k].y)));
-  const float c = range_scale(block_max4(m * (1.0f / N), red));
+  for (int k = threadIdx.x; k <= L; k += 256) {
+    const float2 v = hn[k];
+    hb[k] = v;
+    m = fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y)));
+  }
+  const float c = range_scale(block_max4(m * (1.0f / N), red));   // (its barrier also publishes hb)
   const float sc = c * (1.0f / N);
   uint32_t* out = Hc + (size_t)d * PAIR_STRIDE;
-  auto bin = [&](int k) { return k <= L ? hn[k] : cconj(hn[N - k]); };
+  auto bin = [&](int k) { return k <= L ? hb[k] : cconj(hb[N - k]); };
   for (int idx = threadIdx.x; idx < PAIR_WORDS; idx += 256) {   // (k1, word, lane)
     const int k1 = idx / (16 * 64), wd = (idx / 64) % 16, l = idx % 64;
     const int q = wd & 7;
