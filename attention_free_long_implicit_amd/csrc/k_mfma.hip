@@ -424,19 +424,25 @@ k_conv_mfma(const __bf16* u, __bf16* y, MfmaChain ch, const u32x4* __restrict__ 
 __global__ void __launch_bounds__(256) k_pair_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc) {
   using namespace mf;
   __shared__ float red[4];
-  __shared__ float2 hb[L + 1];   // the channel's bins, read once, coalesced; the copy below gathers from LDS
+  // the channel's bins, read once, coalesced; the copy below gathers them from LDS.  Bin k sits at
+  // k + k / 16: the gather's lanes step 16 bins apart, which the padding spreads over distinct banks.
+  __shared__ float2 hb[L + 1 + (L >> 4) + 1];
   const int d = blockIdx.x;
   const float2* hn = Hnat + (size_t)d * (L + 1);
   float m = 0.0f;
   for (int k = threadIdx.x; k <= L; k += 256) {
     const float2 v = hn[k];
-    hb[k] = v;
+    hb[k + (k >> 4)] = v;
     m = fmaxf(m, fmaxf(fabsf(v.x), fabsf(v.y)));
   }
   const float c = range_scale(block_max4(m * (1.0f / N), red));   // (its barrier also publishes hb)
   const float sc = c * (1.0f / N);
   uint32_t* out = Hc + (size_t)d * PAIR_STRIDE;
-  auto bin = [&](int k) { return k <= L ? hb[k] : cconj(hb[N - k]); };
+  auto bin = [&](int k) {
+    const int j = k <= L ? k : N - k;
+    const float2 v = hb[j + (j >> 4)];
+    return k <= L ? v : cconj(v);
+  };
   for (int idx = threadIdx.x; idx < PAIR_WORDS; idx += 256) {   // (k1, word, lane)
     const int k1 = idx / (16 * 64), wd = (idx / 64) % 16, l = idx % 64;
     const int q = wd & 7;
