@@ -489,56 +489,87 @@ k_mfl_planes(uint32_t* W, const uint32_t* __restrict__ spec, const u32x4* __rest
   if ((threadIdx.x & 255) == 0) hdr[mfl::H_EB + plane_of(mine)] = (uint32_t)(eo + 10 + eH + E + 17);
 }
 
-// Split coefficients of one channel per workgroup from the natural-order bins 0..L of the 2L-point filter
-// spectrum: for plane k0, slab k1, word wd, lane l: words 0..15 hold A, 16..31 B; word 8 r + p of either
-// holds the real (r = 0) or imaginary (r = 1) parts of c X[k(2p)] / M and c X[k(2p + 1)] / M as fp16 (register
-// 2p low), k(v) = k0 + N1 (k1 + 16 (l % 32) + 512 k3(v, l / 32)); then the tail, word 0 = log2(1/c).  c is the
-// power of two that brings the largest component of A / M and B / M into [0.5, 1).
+// Split coefficients of the natural-order bins 0..L of the 2L-point filter spectrum: for plane k0, slab k1,
+// word wd, lane l: words 0..15 hold A, 16..31 B; word 8 r + p of either holds the real (r = 0) or imaginary
+// (r = 1) parts of c X[k(2p)] / M and c X[k(2p + 1)] / M as fp16 (register 2p low), k(v) = k0 + N1 (k1 + 16
+// (l % 32) + 512 k3(v, l / 32)); then the tail, word 0 = log2(1/c).  c is the power of two that brings the
+// largest component of A / M and B / M into [0.5, 1).
+// A[k], B[k] from H[k] and H[k + M] = conj(H[M - k]) (k >= 1; H[M] itself for k = 0).
 template <int N1>
-__global__ void __launch_bounds__(256) k_mfl_spectrum(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc,
-                                                      Twiddles tw) {
+__device__ __forceinline__ void mfl_coef(const float2* hn, const Twiddles& tw, int k, float2& A, float2& Bc) {
+  constexpr int M = mfl::Plan<N1>::M;
+  const float2 h0 = hn[k];
+  const float2 h1 = k == 0 ? hn[M] : cconj(hn[M - k]);
+  const float2 hs = make_float2(0.5f * (h0.x + h1.x), 0.5f * (h0.y + h1.y));
+  const float2 hd = make_float2(0.5f * (h0.x - h1.x), 0.5f * (h0.y - h1.y));
+  const float2 wk = twiddle<mfl::Plan<N1>::LOG2M + 1>(tw, uint32_t(k));   // cos(pi k / M) - i sin(pi k / M)
+  const float cs = wk.x, sn = -wk.y;
+  A = make_float2(hs.x - hd.x * sn, hs.y - hd.y * sn);
+  Bc = make_float2(-hd.y * cs, hd.x * cs);
+}
+
+// The scale c of one channel per workgroup: the largest component over every bin's A and B (bins read in
+// order); writes the tail.
+template <int N1>
+__global__ void __launch_bounds__(256) k_mfl_spec_scale(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc,
+                                                        Twiddles tw) {
   using namespace mf;
   using P = mfl::Plan<N1>;
   constexpr int M = P::M;
   __shared__ float red[4];
   const int d = blockIdx.x;
   const float2* hn = Hnat + (size_t)d * (M + 1);
-  // A[k], B[k] from H[k] and H[k + M] = conj(H[M - k]) (k >= 1; H[M] itself for k = 0)
-  auto coef = [&](int k, float2& A, float2& Bc) {
-    const float2 h0 = hn[k];
-    const float2 h1 = k == 0 ? hn[M] : cconj(hn[M - k]);
-    const float2 hs = make_float2(0.5f * (h0.x + h1.x), 0.5f * (h0.y + h1.y));
-    const float2 hd = make_float2(0.5f * (h0.x - h1.x), 0.5f * (h0.y - h1.y));
-    const float2 wk = twiddle<P::LOG2M + 1>(tw, uint32_t(k));   // cos(pi k / M) - i sin(pi k / M)
-    const float cs = wk.x, sn = -wk.y;
-    A = make_float2(hs.x - hd.x * sn, hs.y - hd.y * sn);
-    Bc = make_float2(-hd.y * cs, hd.x * cs);
-  };
   float m = 0.0f;
   for (int k = threadIdx.x; k < M; k += 256) {
     float2 A, Bc;
-    coef(k, A, Bc);
+    mfl_coef<N1>(hn, tw, k, A, Bc);
     m = fmaxf(m, fmaxf(fmaxf(fabsf(A.x), fabsf(A.y)), fmaxf(fabsf(Bc.x), fabsf(Bc.y))));
   }
   const float c = range_scale(block_max4(m * (1.0f / M), red));
-  const float sc = c * (1.0f / M);
   uint32_t* out = Hc + (size_t)d * P::SPEC_WORDS;
-  // one thread per (plane and slab, register pair p, lane): the two bins' A and B, four words
-  for (int idx = threadIdx.x; idx < N1 * 16 * 8 * 64; idx += 256) {
-    const int l = idx & 63, p = (idx >> 6) & 7, unit = idx >> 9;
+  if (threadIdx.x < 64)
+    out[P::COEF_WORDS + threadIdx.x] = threadIdx.x == 0 ? (uint32_t)(__builtin_amdgcn_frexp_expf(1.0f / c) - 1) : 0u;
+}
+
+// The coefficient words of one channel and one pair of accumulator rows (r, r + 1) per workgroup (sixteen per
+// channel: rows 0..31).  Their bins k0 + N1 (k1 + 16 l' + 512 r'), r' = r, r + 1, fill one window of 1024 N1 consecutive
+// bins, whose A and B go to LDS first (bins, their mirrors and twiddles read in order); the words then gather
+// from LDS, the window padded by one element per 16 N1 so that the lanes, 16 N1 bins apart, hit distinct banks.
+// Rows r, r + 1 are registers 2p, 2p + 1 of lane half h (r = 8 (p >> 1) + 4 h + 2 (p & 1)): words p, 8 + p,
+// 16 + p and 24 + p of lanes 32 h .. 32 h + 31, every plane and slab.  Runs after k_mfl_spec_scale (reads c
+// from the tail).
+template <int N1>
+__global__ void __launch_bounds__(256) k_mfl_spec_coef(const float2* __restrict__ Hnat, uint32_t* __restrict__ Hc,
+                                                       Twiddles tw) {
+  using namespace mf;
+  using P = mfl::Plan<N1>;
+  constexpr int M = P::M, NW = 1024 * N1, S = 16 * N1, NWP = NW + NW / S + 1;
+  __shared__ float2 cA[NWP], cB[NWP];
+  const int d = blockIdx.x >> 4, r = 2 * (blockIdx.x & 15);
+  const int p = 2 * (r >> 3) + ((r >> 1) & 1), h = (r >> 2) & 1;
+  const int W0 = 512 * N1 * r;
+  const float2* hn = Hnat + (size_t)d * (M + 1);
+  uint32_t* out = Hc + (size_t)d * P::SPEC_WORDS;
+  for (int i = threadIdx.x; i < NW; i += 256) {
+    float2 A, Bc;
+    mfl_coef<N1>(hn, tw, W0 + i, A, Bc);
+    cA[i + i / S] = A;
+    cB[i + i / S] = Bc;
+  }
+  const int e = (int)out[P::COEF_WORDS];                  // log2(1/c), from k_mfl_spec_scale
+  const float sc = ldexpf(1.0f, -e) * (1.0f / M);
+  __syncthreads();
+  for (int it = threadIdx.x; it < N1 * 16 * 32; it += 256) {
+    const int lq = it & 31, unit = it >> 5;
     const int k0 = unit >> 4, k1 = unit & 15;
-    const int base = k0 + N1 * (k1 + 16 * (l & 31));
-    float2 a0, b0, a1, b1;
-    coef(base + N1 * 512 * acc_row(2 * p, l >> 5), a0, b0);
-    coef(base + N1 * 512 * acc_row(2 * p + 1, l >> 5), a1, b1);
-    uint32_t* o = out + (size_t)unit * 2048 + l;
+    const int i0 = k0 + N1 * (k1 + 16 * lq), i1 = i0 + 512 * N1;
+    const float2 a0 = cA[i0 + i0 / S], b0 = cB[i0 + i0 / S], a1 = cA[i1 + i1 / S], b1 = cB[i1 + i1 / S];
+    uint32_t* o = out + (size_t)unit * 2048 + 32 * h + lq;
     o[p * 64] = pack2h(a0.x * sc, a1.x * sc);
     o[(8 + p) * 64] = pack2h(a0.y * sc, a1.y * sc);
     o[(16 + p) * 64] = pack2h(b0.x * sc, b1.x * sc);
     o[(24 + p) * 64] = pack2h(b0.y * sc, b1.y * sc);
   }
-  if (threadIdx.x < 64)
-    out[P::COEF_WORDS + threadIdx.x] = threadIdx.x == 0 ? (uint32_t)(__builtin_amdgcn_frexp_expf(1.0f / c) - 1) : 0u;
 }
 
 // ------------------------------------------------------------------ host side
@@ -614,10 +645,14 @@ hipError_t launch_conv_mfl(int log2L, int order, int B, int D, const void* v, co
 }
 
 hipError_t launch_mfl_spectrum(int log2L, const float2* Hnat, void* Hc, int D, const Twiddles& tw, hipStream_t s) {
+  auto go = [&](auto scale, auto coef) {
+    hipLaunchKernelGGL(scale, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc, tw);
+    hipLaunchKernelGGL(coef, dim3(16 * D), dim3(256), 0, s, Hnat, (uint32_t*)Hc, tw);
+  };
   switch (log2L) {
-    case 15: hipLaunchKernelGGL(k_mfl_spectrum<2>, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc, tw); break;
-    case 16: hipLaunchKernelGGL(k_mfl_spectrum<4>, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc, tw); break;
-    case 17: hipLaunchKernelGGL(k_mfl_spectrum<8>, dim3(D), dim3(256), 0, s, Hnat, (uint32_t*)Hc, tw); break;
+    case 15: go(k_mfl_spec_scale<2>, k_mfl_spec_coef<2>); break;
+    case 16: go(k_mfl_spec_scale<4>, k_mfl_spec_coef<4>); break;
+    case 17: go(k_mfl_spec_scale<8>, k_mfl_spec_coef<8>); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
